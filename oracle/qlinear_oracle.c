@@ -1,0 +1,423 @@
+/*
+ * CPU oracle for the quantized linear layer: TEST INFRASTRUCTURE ONLY.
+ *
+ * Plain, slow, obviously correct loops that state what the layer computes.
+ * Only the test suite, the smoke check and the benchmark's CPU-baseline leg
+ * call this file; the GPU library never links or includes it, and this file
+ * includes nothing of the GPU library.  Floating point is fp64 unless the
+ * definition fixes a single fp32 operation (written fl32 below); those are
+ * plain C float operations, compiled with -ffp-contract=off so each one is a
+ * single IEEE round-to-nearest-even operation.
+ *
+ * Sources (web pages, cited by title and section):
+ *   [Q4]  bitorch-engine API docs, "Q4LinearFunction" - forward.
+ *   [BL]  LLaMA-BitNet utils.py, "Class BitLinear" - forward docstring
+ *         steps 1-5 and the forward body.
+ *   [PT]  Ascend CANN ATB docs, "Per-token Quantization for Matmul" -
+ *         Parameters, Input, Output and Example.
+ *   [CA]  frankenstein-transformer docs, "Common Attention Utilities" -
+ *         activation_quant, weight_quant, BitLinear.bake_ternary_weights.
+ *   [L4]  docs.rs vyre-libs 0.7.2, "linear_4bit/mod.rs" - module doc
+ *         comment and the QuantizedLinear4BitPlannerEvidence fields.
+ *
+ * Every function returns 0 on success and a negative value when an integer
+ * accumulator would not fit in int32 (the definition asserts that it does).
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+/* ------------------------------------------------------------------ */
+/* O1: per-token absmax int8 activation quantization.                  */
+/* ------------------------------------------------------------------ */
+/*
+ * [BL] forward steps 1-2 (parameter-free RMSNorm, then 8-bit per-token
+ * quantization) and step 5 (the activation scale multiplies the output);
+ * [CA] activation_quant (scale the last dimension into [-128, 127], round,
+ * rescale).
+ *
+ * For each token row m of X[m, k] (fp32 values, exact copies of the bf16 /
+ * fp16 input):
+ *   a   = max_k |X|                       (exact)
+ *   a'  = max(a, eps_q)                   (division guard)
+ *   s   = fl32(127 / a')
+ *   q   = clamp(rne(fl32(X * s)), -128, 127)
+ *   r   = 1                               without RMSNorm
+ *   r   = 1 / sqrt(sum_k X^2 / K + eps_n) with RMSNorm (fp64)
+ *   pts = fp32(a' * r / 127)              (fp64, one final rounding)
+ *   rowsum = sum_k q                      (int32)
+ * RMSNorm multiplies the whole row by r > 0 and absmax quantization is
+ * invariant under a positive per-row factor, so the codes are those of X
+ * and the norm survives only as the factor r in the dequant scale.
+ */
+int oracle_quant_act(const float *x, int64_t m, int64_t k, int rmsnorm,
+                     double eps_norm, float eps_q, int8_t *q, float *pts,
+                     int32_t *rowsum)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < m; i++) {
+        const float *row = x + i * k;
+        float a = 0.0f;
+        for (int64_t j = 0; j < k; j++) {
+            float v = fabsf(row[j]);
+            if (v > a) a = v;
+        }
+        float ap = a > eps_q ? a : eps_q;
+        float s = 127.0f / ap;
+        int64_t sum = 0;
+        for (int64_t j = 0; j < k; j++) {
+            float v = row[j] * s;
+            float r = nearbyintf(v);
+            if (r > 127.0f) r = 127.0f;
+            if (r < -128.0f) r = -128.0f;
+            int8_t c = (int8_t)r;
+            q[i * k + j] = c;
+            sum += c;
+        }
+        double rr = 1.0;
+        if (rmsnorm) {
+            double ss = 0.0;
+            for (int64_t j = 0; j < k; j++) ss += (double)row[j] * (double)row[j];
+            rr = 1.0 / sqrt(ss / (double)k + eps_norm);
+        }
+        pts[i] = (float)((double)ap * rr / 127.0);
+        if (rowsum) rowsum[i] = (int32_t)sum;
+    }
+    return 0;
+}
+
+/* ------------------------------------------------------------------ */
+/* O2: absmean ternary weight quantization and its 2-bit packing.      */
+/* ------------------------------------------------------------------ */
+/*
+ * [BL] forward step 3 (ternary {-1, 0, +1} via absmean) and step 5 (a
+ * scalar weight scale); [CA] weight_quant (scale by the inverse mean
+ * absolute value, round to the nearest integer in [-1, 1]).
+ *
+ *   gamma  = sum |W| / count              (fp64, sequential)
+ *   gamma' = max(gamma, eps)
+ *   q      = sign(W) if |W| > gamma'/2 else 0
+ * The comparison is exact in fp64 (halving is exact); |W| == gamma'/2
+ * gives 0, which is round-half-to-even of W/gamma' = +-0.5.  Values whose
+ * quotient is 1.5 or more clamp to +-1, so this equals
+ * clamp(rne(W / gamma'), -1, 1) in exact arithmetic.
+ *
+ * w is read in its stored layout: layout 1 = [n][k] (nn.Linear weight),
+ * layout 0 = [k][n].  codes are always written [n][k].
+ */
+int oracle_ternary_quant(const float *w, int layout, int64_t n, int64_t k,
+                         double eps, int8_t *codes, double *gamma_out)
+{
+    int64_t count = n * k;
+    double sum = 0.0;
+    for (int64_t i = 0; i < count; i++) sum += fabs((double)w[i]);
+    double g = sum / (double)count;
+    if (g < eps) g = eps;
+    double half = g / 2.0;
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < n; r++) {
+        for (int64_t c = 0; c < k; c++) {
+            float v = layout == 1 ? w[r * k + c] : w[c * n + r];
+            double av = fabs((double)v);
+            int8_t t = 0;
+            if (av > half) t = v > 0.0f ? 1 : -1;
+            codes[r * k + c] = t;
+        }
+    }
+    *gamma_out = g;
+    return 0;
+}
+
+/*
+ * Count of weights within rel * gamma' of the rounding threshold gamma'/2:
+ * the only weights whose code could depend on the summation order of the
+ * absmean.
+ */
+int64_t oracle_ternary_tie_band(const float *w, int64_t count, double gamma,
+                                double rel)
+{
+    int64_t c = 0;
+    for (int64_t i = 0; i < count; i++)
+        if (fabs(fabs((double)w[i]) - gamma / 2.0) <= rel * gamma) c++;
+    return c;
+}
+
+/*
+ * Ternary pack layout version 1 (our definition; the pages fix only that
+ * codes are ternary and BitNet stores them in 2 bits).  Requires
+ * n % 16 == 0 and k % 256 == 0.
+ *   The [n][k] code matrix is cut into blocks of 16 columns x 256 k; block
+ *   (nb, kb) is 256 consecutive u32 words starting at word
+ *   (nb * (k / 256) + kb) * 256.
+ *   Word 4*l + t of a block (l in [0, 64), t in [0, 4)) holds column
+ *   16*nb + l % 16 and the 16 consecutive k starting at
+ *   k0 = 256*kb + 64*(l / 16) + 16*t.
+ *   Element k0 + 4*a + b (a, b in [0, 4)) sits in bits [8b + 2a, 8b + 2a + 1]
+ *   as the code c = q + 1 in {0, 1, 2}.
+ */
+static int64_t tern_word_index(int64_t n, int64_t k, int64_t col, int64_t kk,
+                               int *bitpos)
+{
+    int64_t nb = col / 16, kb = kk / 256;
+    int64_t within = kk % 256;
+    int64_t lgrp = within / 64;          /* l / 16 */
+    int64_t t = (within % 64) / 16;
+    int64_t e = within % 16;             /* 4a + b */
+    int64_t a = e / 4, b = e % 4;
+    int64_t l = lgrp * 16 + col % 16;
+    (void)n;
+    *bitpos = (int)(8 * b + 2 * a);
+    return (nb * (k / 256) + kb) * 256 + 4 * l + t;
+}
+
+int oracle_pack_ternary_v1(const int8_t *codes, int64_t n, int64_t k,
+                           uint32_t *packed)
+{
+    if (n % 16 || k % 256) return -2;
+    memset(packed, 0, (size_t)(n * k / 16) * sizeof(uint32_t));
+    for (int64_t r = 0; r < n; r++)
+        for (int64_t c = 0; c < k; c++) {
+            int bit;
+            int64_t wi = tern_word_index(n, k, r, c, &bit);
+            uint32_t code = (uint32_t)(codes[r * k + c] + 1);
+            packed[wi] |= code << bit;
+        }
+    return 0;
+}
+
+int oracle_unpack_ternary_v1(const uint32_t *packed, int64_t n, int64_t k,
+                             int8_t *codes)
+{
+    if (n % 16 || k % 256) return -2;
+    for (int64_t r = 0; r < n; r++)
+        for (int64_t c = 0; c < k; c++) {
+            int bit;
+            int64_t wi = tern_word_index(n, k, r, c, &bit);
+            codes[r * k + c] = (int8_t)((int)((packed[wi] >> bit) & 3u) - 1);
+        }
+    return 0;
+}
+
+/* ------------------------------------------------------------------ */
+/* O3: 4-bit packing and the grouped affine INT4 product.              */
+/* ------------------------------------------------------------------ */
+/*
+ * [L4] module doc: the packed weight is u32 words holding eight nibbles;
+ * the grouped path applies a per-group scale and zero-point (the
+ * "scale plus zero-point sidecar").
+ *
+ * Weight layout version 1 (our definition).  Requires n % 16 == 0 and
+ * k % 128 == 0.  Blocks of 16 columns x 128 k; block (nb, kb) is 256 words
+ * from word (nb * (k / 128) + kb) * 256.  Word 4*l + t holds column
+ * 16*nb + l % 16 and the 8 k starting at k0 = 128*kb + 32*(l / 16) + 8*t.
+ * Nibble p (bits [4p, 4p + 3]) holds k-offset 2p for p < 4 and 2(p - 4) + 1
+ * for p >= 4.  Only the low nibble of each input code is used.
+ */
+static int64_t int4_word_index(int64_t k, int64_t col, int64_t kk, int *bitpos)
+{
+    int64_t nb = col / 16, kb = kk / 128;
+    int64_t within = kk % 128;
+    int64_t lgrp = within / 32;
+    int64_t t = (within % 32) / 8;
+    int64_t off = within % 8;
+    int64_t p = (off % 2 == 0) ? off / 2 : off / 2 + 4;
+    int64_t l = lgrp * 16 + col % 16;
+    *bitpos = (int)(4 * p);
+    return (nb * (k / 128) + kb) * 256 + 4 * l + t;
+}
+
+int oracle_pack_int4_v1(const uint8_t *q, int64_t n, int64_t k,
+                        uint32_t *packed)
+{
+    if (n % 16 || k % 128) return -2;
+    memset(packed, 0, (size_t)(n * k / 8) * sizeof(uint32_t));
+    for (int64_t r = 0; r < n; r++)
+        for (int64_t c = 0; c < k; c++) {
+            int bit;
+            int64_t wi = int4_word_index(k, r, c, &bit);
+            packed[wi] |= ((uint32_t)(q[r * k + c] & 15u)) << bit;
+        }
+    return 0;
+}
+
+int oracle_unpack_int4_v1(const uint32_t *packed, int64_t n, int64_t k,
+                          uint8_t *q)
+{
+    if (n % 16 || k % 128) return -2;
+    for (int64_t r = 0; r < n; r++)
+        for (int64_t c = 0; c < k; c++) {
+            int bit;
+            int64_t wi = int4_word_index(k, r, c, &bit);
+            q[r * k + c] = (uint8_t)((packed[wi] >> bit) & 15u);
+        }
+    return 0;
+}
+
+/*
+ * Zero-points z[n][g] (g = number of groups) are stored group-major:
+ * word (gi, col / 8) of a [g][n / 8] array, column col in nibble col % 8.
+ * Requires n % 8 == 0.
+ */
+int oracle_pack_int4_zeros(const uint8_t *z, int64_t n, int64_t g,
+                           uint32_t *packed)
+{
+    if (n % 8) return -2;
+    memset(packed, 0, (size_t)(g * n / 8) * sizeof(uint32_t));
+    for (int64_t r = 0; r < n; r++)
+        for (int64_t gi = 0; gi < g; gi++)
+            packed[gi * (n / 8) + r / 8] |= ((uint32_t)(z[r * g + gi] & 15u))
+                                            << (4 * (r % 8));
+    return 0;
+}
+
+/*
+ * y[m][n] = sum_g s[n][g] * sum_{k in g} x[m][k] * (q[n][k] - z[n][g])
+ * in fp64; also bound[m][n] = sum_k |x[m][k] * w[n][k]| with the dequantized
+ * weight w = s * (q - z), the scale of the error allowed for this path.
+ * x and s hold the fp16 input values widened exactly to fp64.
+ */
+int oracle_grouped_int4(const double *x, const uint8_t *q, const double *s,
+                        const uint8_t *z, int64_t group_size, int64_t m,
+                        int64_t n, int64_t k, double *y, double *bound)
+{
+    int64_t ng = k / group_size;
+#pragma omp parallel for schedule(static)
+    for (int64_t c = 0; c < n; c++) {
+        for (int64_t r = 0; r < m; r++) {
+            double acc = 0.0, ab = 0.0;
+            for (int64_t gi = 0; gi < ng; gi++) {
+                double sg = s[c * ng + gi];
+                int zg = z[c * ng + gi] & 15;
+                double part = 0.0;
+                for (int64_t j = gi * group_size; j < (gi + 1) * group_size; j++) {
+                    int d = (int)(q[c * k + j] & 15) - zg;
+                    part += x[r * k + j] * (double)d;
+                    ab += fabs(x[r * k + j] * sg * (double)d);
+                }
+                acc += sg * part;
+            }
+            y[r * n + c] = acc;
+            if (bound) bound[r * n + c] = ab;
+        }
+    }
+    return 0;
+}
+
+/* ------------------------------------------------------------------ */
+/* O4: integer GEMM and the per-token dequant epilogue.                */
+/* ------------------------------------------------------------------ */
+/*
+ * [PT] Input (x int8 [m,k], weight int8 [k,n], deqScale [n],
+ * perTokenScale [m]), Parameters (transposeB), Output ([m,n] fp16 / bf16)
+ * and Example: out[m][n] = (sum_k x[m][k] * w[k][n]) * deqScale[n] *
+ * perTokenScale[m].
+ * acc is accumulated in int64 and must fit int32.
+ * layout 0: w is [k][n]; layout 1: w is [n][k] (transposeB).
+ */
+int oracle_gemm_i8(const int8_t *x, const int8_t *w, int layout, int64_t m,
+                   int64_t n, int64_t k, int32_t *acc)
+{
+    int bad = 0;
+#pragma omp parallel for schedule(static) reduction(| : bad)
+    for (int64_t r = 0; r < m; r++) {
+        for (int64_t c = 0; c < n; c++) {
+            int64_t s = 0;
+            for (int64_t j = 0; j < k; j++) {
+                int64_t wv = layout == 1 ? w[c * k + j] : w[j * n + c];
+                s += (int64_t)x[r * k + j] * wv;
+            }
+            if (s > INT32_MAX || s < INT32_MIN) bad = 1;
+            acc[r * n + c] = (int32_t)s;
+        }
+    }
+    return bad ? -1 : 0;
+}
+
+/* y[m][n] = acc[m][n] * pts[m] * deq[n] in fp64 ([PT] Example; [BL] step 5). */
+int oracle_dequant(const int32_t *acc, const float *pts, const float *deq,
+                   int64_t m, int64_t n, double *y)
+{
+    for (int64_t r = 0; r < m; r++)
+        for (int64_t c = 0; c < n; c++)
+            y[r * n + c] = (double)acc[r * n + c] * (double)pts[r] * (double)deq[c];
+    return 0;
+}
+
+/* ------------------------------------------------------------------ */
+/* O5: A4W4 per-tensor 4-bit quantization ([Q4] forward).             */
+/* ------------------------------------------------------------------ */
+/*
+ * [Q4] forward: inputs and weights are quantized to 4 bits with the given
+ * scale factors; eps avoids division by zero.
+ *   s' = max(scale, eps)
+ *   q  = clamp(rne(fl32(X / s')), -8, 7)
+ * The product is then oracle_gemm_i8 (layout [n][k]) and the dequant is
+ * acc * s'_a * s'_w in fp64.
+ */
+int oracle_quant_int4_tensor(const float *x, int64_t count, float scale,
+                             float eps, int8_t *q)
+{
+    float sp = scale > eps ? scale : eps;
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < count; i++) {
+        float v = x[i] / sp;
+        float r = nearbyintf(v);
+        if (r > 7.0f) r = 7.0f;
+        if (r < -8.0f) r = -8.0f;
+        q[i] = (int8_t)r;
+    }
+    return 0;
+}
+
+/* ------------------------------------------------------------------ */
+/* Output rounding: fp64 -> fp16 / bf16, round to nearest, ties to even. */
+/* ------------------------------------------------------------------ */
+/*
+ * [PT] Parameters / Output: the result is written as float16 or bf16.
+ * Direct single rounding from fp64 (no fp32 intermediate).  fp16 overflow
+ * gives +-inf as in IEEE.  Returns the 16-bit pattern.
+ */
+static uint16_t round_to_16(double v, int mant_bits, int exp_bits)
+{
+    int bias = (1 << (exp_bits - 1)) - 1;
+    uint16_t sign = (uint16_t)(signbit(v) ? 1u << 15 : 0u);
+    double a = fabs(v);
+    uint16_t expmask = (uint16_t)(((1u << exp_bits) - 1u) << mant_bits);
+    if (isnan(v)) return (uint16_t)(expmask | (1u << (mant_bits - 1)));
+    if (isinf(v)) return (uint16_t)(sign | expmask);
+    if (a == 0.0) return sign;
+    int e;
+    frexp(a, &e);                 /* a = f * 2^e, f in [0.5, 1) */
+    int ue = e - 1;               /* a in [2^ue, 2^(ue+1)) */
+    int emin = 1 - bias;
+    if (ue < emin) ue = emin;     /* subnormal range uses the minimum exponent */
+    double quantum = ldexp(1.0, ue - mant_bits);
+    double units = nearbyint(a / quantum);   /* exact scaling by a power of 2 */
+    if (units == 0.0) return sign;           /* rounds to a signed zero */
+    /* units may have carried into the next binade; recompose. */
+    double r = units * quantum;
+    int e2;
+    frexp(r, &e2);
+    int rexp = e2 - 1;
+    uint32_t bits;
+    if (r >= ldexp(1.0, bias + 1)) return (uint16_t)(sign | expmask);  /* overflow */
+    if (rexp < emin) {
+        bits = (uint32_t)units;                  /* subnormal */
+    } else {
+        uint32_t biased = (uint32_t)(rexp + bias);
+        uint32_t mant = (uint32_t)(r / ldexp(1.0, rexp - mant_bits)) - (1u << mant_bits);
+        bits = (biased << mant_bits) | mant;
+    }
+    return (uint16_t)(sign | bits);
+}
+
+void oracle_round_f16(const double *v, int64_t count, uint16_t *out)
+{
+    for (int64_t i = 0; i < count; i++) out[i] = round_to_16(v[i], 10, 5);
+}
+
+void oracle_round_bf16(const double *v, int64_t count, uint16_t *out)
+{
+    for (int64_t i = 0; i < count; i++) out[i] = round_to_16(v[i], 7, 8);
+}

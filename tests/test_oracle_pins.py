@@ -1,0 +1,371 @@
+"""Pins of the CPU oracle against what the pages and the mathematics fix.
+
+Each test checks the oracle against something other than itself: values
+printed on the pages (``tests/golden``), textbook results computed by a
+library routine the oracle does not use (numpy integer / fp64 matmul), exact
+rational arithmetic (``fractions.Fraction``) on tiny inputs, closed forms and
+invariants.  A dropped term, a wrong sign or index, or a transposed operand
+in the oracle fails at least one of them.
+"""
+import json
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synthetic
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _bf16_values(x: torch.Tensor) -> np.ndarray:
+    return x.float().numpy()
+
+
+# ---------------------------------------------------------------------------
+# O4: integer GEMM + per-token epilogue
+# ---------------------------------------------------------------------------
+def test_worked_example_exact():
+    """"Per-token Quantization for Matmul", Example: printed output and sums."""
+    with open(os.path.join(GOLDEN, "per_token_example.json")) as f:
+        ex = json.load(f)
+    x = np.array(ex["x"], np.int8)
+    w = np.array(ex["weight_kn"], np.int8)
+    acc, y = oracle.w8a8(x, w, False, np.array(ex["perTokenScale"], np.float32),
+                         np.array(ex["deqScale"], np.float32))
+    assert acc.tolist() == ex["acc"]
+    assert y.tolist() == ex["output"]
+    # every printed output is exactly representable in fp16 and bf16
+    out = np.array(ex["output"], np.float64)
+    assert np.array_equal(oracle.round_f16(y).view(np.float16).astype(np.float64), out)
+    bf = (oracle.round_bf16(y).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    assert np.array_equal(bf, out)
+
+
+@pytest.mark.parametrize("m,n,k,layout_nk", [(1, 1, 1, True), (5, 7, 3, False), (17, 33, 65, True),
+                                             (33, 18, 300, False), (64, 48, 512, True)])
+def test_gemm_unit_scales_is_textbook_matmul(m, n, k, layout_nk):
+    """pts = deq = 1 reduces to integer matmul (numpy int64 ``@``)."""
+    d = synthetic.w8a8(m, n, k, layout_nk, seed=7 + m)
+    x, w = d["x"].numpy(), d["w"].numpy()
+    ones_m, ones_n = np.ones(m, np.float32), np.ones(n, np.float32)
+    acc, y = oracle.w8a8(x, w, layout_nk, ones_m, ones_n)
+    wk = w.T if layout_nk else w  # [k, n]
+    ref = x.astype(np.int64) @ wk.astype(np.int64)
+    assert np.array_equal(acc.astype(np.int64), ref)
+    assert np.array_equal(y, ref.astype(np.float64))
+
+
+@pytest.mark.parametrize("layout_nk", [False, True])
+def test_dequant_brute_force_fp64(layout_nk):
+    """y equals the fp64 matmul of the dequantized operands (x*pts) @ (w*deq)."""
+    d = synthetic.w8a8(19, 23, 77, layout_nk, seed=11)
+    x, w, pts, deq = (d[k].numpy() for k in ("x", "w", "pts", "deq"))
+    _, y = oracle.w8a8(x, w, layout_nk, pts, deq)
+    wk = (w.T if layout_nk else w).astype(np.float64)
+    ref = (x.astype(np.float64) * pts.astype(np.float64)[:, None]) @ (wk * deq.astype(np.float64)[None, :])
+    np.testing.assert_allclose(y, ref, rtol=1e-12, atol=1e-300)
+
+
+def test_gemm_int32_overflow_is_reported():
+    """The definition asserts the accumulator fits int32: (-128)^2 * 2^17 = 2^31 does not."""
+    k = 1 << 17
+    x = np.full((1, k), -128, np.int8)
+    with pytest.raises(ValueError):
+        oracle.gemm_i8(x, x, True)
+    # one fewer term fits
+    acc = oracle.gemm_i8(x[:, :k - 1], x[:, :k - 1], True)
+    assert int(acc[0, 0]) == 128 * 128 * (k - 1)
+
+
+# ---------------------------------------------------------------------------
+# O1: per-token absmax int8 quantization
+# ---------------------------------------------------------------------------
+def _act_rows(seed=3, m=24, k=257):
+    return _bf16_values(synthetic.activations(m, k, seed, outliers=0.01))
+
+
+def test_quant_act_invariants():
+    """"Common Attention Utilities" activation_quant: range [-128,127], per-token scale."""
+    x = _act_rows()
+    q, pts, rs = oracle.quant_act(x)
+    assert q.min() >= -127 and q.max() <= 127          # 127/absmax scaling never reaches -128
+    a = np.abs(x).max(axis=1)
+    ap = np.maximum(a, np.float32(1e-5))
+    for i in range(x.shape[0]):
+        j = int(np.argmax(np.abs(x[i])))
+        assert abs(int(q[i, j])) == 127 and np.sign(q[i, j]) == np.sign(x[i, j])
+    # reconstruction within half a step (plus fp32 slack)
+    step = ap.astype(np.float64) / 127.0
+    err = np.abs(x.astype(np.float64) - q.astype(np.float64) * step[:, None])
+    assert np.all(err <= step[:, None] * (0.5 + 1e-6))
+    assert np.array_equal(rs, q.astype(np.int64).sum(axis=1).astype(np.int32))
+    # pts without RMSNorm is the correctly rounded fp32 of a'/127
+    assert np.array_equal(pts, (ap.astype(np.float64) / 127.0).astype(np.float32))
+
+
+def test_quant_act_idempotent():
+    """Re-quantizing the dequantized codes returns the same codes."""
+    x = _act_rows(seed=5)
+    q, pts, _ = oracle.quant_act(x)
+    xr = q.astype(np.float32) * pts[:, None]
+    q2, _, _ = oracle.quant_act(xr)
+    assert np.array_equal(q, q2)
+
+
+def test_quant_act_exact_rational_brute_force():
+    """Codes from exact arithmetic: s = RN32(127/a'), v = RN32(x*s), q = round-half-even(v).
+
+    fp64 carries each fp32 step exactly (products of two fp32 values are exact
+    in fp64; fp64 division rounded to fp32 is the correctly rounded fp32
+    quotient), and Python's ``round`` on Fraction is round-half-to-even.
+    """
+    x = _act_rows(seed=9, m=6, k=64)
+    q, _, _ = oracle.quant_act(x)
+    for i in range(x.shape[0]):
+        a = max(abs(float(v)) for v in x[i])
+        ap = max(a, float(np.float32(1e-5)))
+        s = float(np.float32(127.0 / ap))
+        for j in range(x.shape[1]):
+            v = float(np.float32(float(x[i, j]) * s))
+            c = round(Fraction(v))
+            c = max(-128, min(127, c))
+            assert int(q[i, j]) == c
+
+
+def test_quant_act_rmsnorm_folding():
+    """"Class BitLinear" steps 1-2: RMSNorm leaves codes unchanged and scales pts by r."""
+    x = _act_rows(seed=13)
+    q0, p0, r0 = oracle.quant_act(x, rmsnorm=False)
+    q1, p1, r1 = oracle.quant_act(x, rmsnorm=True, eps_norm=1e-6)
+    assert np.array_equal(q0, q1) and np.array_equal(r0, r1)
+    xd = x.astype(np.float64)
+    r = 1.0 / np.sqrt((xd * xd).mean(axis=1) + 1e-6)
+    np.testing.assert_allclose(p1.astype(np.float64) / p0.astype(np.float64), r, rtol=2e-7)
+    # literal pipeline: normalize in fp64, then absmax-quantize the normalized row
+    lit = np.rint(np.clip((xd * r[:, None]) * (127.0 / np.abs(xd * r[:, None]).max(axis=1))[:, None],
+                          -128, 127))
+    assert np.mean(lit != q1) < 1e-3
+
+
+def test_quant_act_degenerate_rows():
+    x = np.zeros((3, 40), np.float32)
+    x[1, 7] = -3.5          # one-hot
+    x[2, :] = 2.0           # constant
+    q, pts, rs = oracle.quant_act(x)
+    assert np.all(q[0] == 0) and pts[0] == np.float32(np.float64(np.float32(1e-5)) / 127.0)
+    assert q[1, 7] == -127 and np.count_nonzero(q[1]) == 1
+    assert np.all(q[2] == 127) and rs[2] == 127 * 40
+
+
+# ---------------------------------------------------------------------------
+# O2: absmean ternary
+# ---------------------------------------------------------------------------
+def test_ternary_exact_rational_brute_force():
+    """Codes equal clamp(round-half-even(W / gamma), -1, 1) with exact rational gamma."""
+    w = synthetic.master_weight(16, 48, seed=21).numpy()
+    codes, g = oracle.ternary_quant(w)
+    gx = sum(Fraction(abs(float(v))) for v in w.ravel()) / w.size
+    assert abs(Fraction(g) - gx) <= gx * Fraction(1, 10 ** 14)
+    assert oracle.ternary_tie_band(w, g) == 0
+    for (i, j), v in np.ndenumerate(w):
+        c = max(-1, min(1, round(Fraction(float(v)) / gx)))
+        assert int(codes[i, j]) == c
+
+
+def test_ternary_half_tie_rounds_to_zero():
+    """A weight exactly at gamma'/2 rounds half-to-even to 0; just above gives +-1."""
+    w = np.array([[1.0, -1.0, 0.5, -0.5, 3.0, 0.0, -3.0, 2.0]], np.float32)  # mean|w| = 1.375
+    w = np.repeat(w, 16, axis=0)
+    codes, g = oracle.ternary_quant(w)
+    assert g == 1.375
+    assert codes[0].tolist() == [1, -1, 0, 0, 1, 0, -1, 1]
+    # mean|w| = 2, so +-1 sit exactly on gamma'/2: W/gamma' = +-0.5 rounds to 0,
+    # 2/2 = 1 stays 1 and 5/2 = 2.5 clamps to 1
+    w2 = np.repeat(np.array([[5.0, -5.0, 1.0, -1.0, 2.0, 0.0, -1.0, 1.0]], np.float32), 16, axis=0)
+    codes2, g2 = oracle.ternary_quant(w2)
+    assert g2 == 2.0
+    exp = [max(-1, min(1, round(Fraction(float(v)) / Fraction(g2)))) for v in w2[0]]
+    assert codes2[0].tolist() == exp == [1, -1, 0, 0, 1, 0, 0, 0]
+    assert oracle.ternary_tie_band(w2, g2) == 4 * 16
+
+
+def test_ternary_eps_guard_and_layouts():
+    w = synthetic.master_weight(32, 64, seed=22).numpy()
+    c_nk, g1 = oracle.ternary_quant(w, layout_nk=True)
+    c_kn, g2 = oracle.ternary_quant(np.ascontiguousarray(w.T), layout_nk=False)
+    assert np.array_equal(c_nk, c_kn) and abs(g1 - g2) <= 1e-15 * g1
+    z = np.zeros((16, 16), np.float32)
+    cz, gz = oracle.ternary_quant(z, eps=1e-5)
+    assert gz == 1e-5 and not cz.any()
+
+
+def test_ternary_sign_and_bake_idempotence():
+    """"Common Attention Utilities" bake_ternary_weights: re-baking changes no code."""
+    w = synthetic.master_weight(64, 256, seed=23).numpy()
+    codes, g = oracle.ternary_quant(w)
+    nz = codes != 0
+    assert np.all(np.sign(w[nz]) == codes[nz])
+    assert np.all(np.abs(w[~nz]) <= g / 2) and np.all(np.abs(w[nz]) > g / 2)
+    baked = codes.astype(np.float32) * np.float32(g)
+    codes2, g2 = oracle.ternary_quant(baked)
+    assert np.array_equal(codes, codes2)
+    # the scale drifts to p * fp32(gamma'), p = nonzero fraction: why baking is guarded
+    p = nz.mean()
+    assert abs(g2 - p * float(np.float32(g))) <= 1e-12 * g2
+
+
+def test_ternary_gaussian_zero_fraction():
+    """For Gaussian weights the zero fraction is erf(0.5*sqrt(2/pi)/sqrt(2)) ~ 0.310."""
+    w = synthetic.master_weight(256, 4096, seed=24).numpy()
+    codes, _ = oracle.ternary_quant(w)
+    expect = math.erf(0.5 * math.sqrt(2 / math.pi) / math.sqrt(2))
+    assert abs((codes == 0).mean() - expect) < 3e-3
+
+
+def test_ternary_pack_round_trip_and_fragments():
+    w = synthetic.master_weight(48, 768, seed=25).numpy()
+    codes, _ = oracle.ternary_quant(w)
+    packed = oracle.pack_ternary(codes)
+    assert packed.size == 48 * 768 // 16
+    assert np.array_equal(oracle.unpack_ternary(packed, 48, 768), codes)
+    # no 2-bit field ever holds 3
+    fields = np.stack([(packed >> s) & 3 for s in range(0, 32, 2)])
+    assert not np.any(fields == 3)
+    # each word unpacks to 16 consecutive k of one column: bytes of (word >> 2a) & 0x03030303
+    kblocks = 768 // 256
+    for nb, kb, l, t in [(0, 0, 0, 0), (2, 1, 37, 3), (1, 2, 63, 2)]:
+        word = int(packed[(nb * kblocks + kb) * 256 + 4 * l + t])
+        col = 16 * nb + l % 16
+        k0 = 256 * kb + 64 * (l // 16) + 16 * t
+        got = [((word >> (2 * a)) >> (8 * b)) & 3 for a in range(4) for b in range(4)]
+        assert got == [int(c) + 1 for c in codes[col, k0:k0 + 16]]
+
+
+# ---------------------------------------------------------------------------
+# O3: grouped affine INT4
+# ---------------------------------------------------------------------------
+def _grouped(m=5, n=32, k=256, g=64, seed=31):
+    d = synthetic.grouped_int4(m, n, k, g, seed=seed)
+    return (d["x"].float().numpy().astype(np.float64), d["q"].numpy(),
+            d["s"].float().numpy().astype(np.float64), d["z"].numpy(), g)
+
+
+def test_grouped_zero_when_zero_point_equals_code():
+    x, q, s, z, g = _grouped()
+    zq = np.ascontiguousarray(np.repeat(q[:, ::g][:, :, None], 1, axis=2)[:, :, 0])
+    qq = np.repeat(zq, g, axis=1)  # every code equals its group's zero
+    y, _ = oracle.grouped_int4(x, qq, s, zq, g)
+    assert np.all(y == 0.0)
+
+
+def test_grouped_unit_scale_zero_offset_is_matmul():
+    x, q, s, z, g = _grouped()
+    y, _ = oracle.grouped_int4(x, q, np.ones_like(s), np.zeros_like(z), g)
+    np.testing.assert_allclose(y, x @ q.astype(np.float64).T, rtol=1e-13)
+
+
+@pytest.mark.parametrize("g", [32, 128, 256])
+def test_grouped_brute_force_dequant_then_matmul(g):
+    x, q, s, z, _ = _grouped(g=g, seed=33)
+    w = np.repeat(s, g, axis=1) * (q.astype(np.float64) - np.repeat(z.astype(np.float64), g, axis=1))
+    y, bound = oracle.grouped_int4(x, q, s, z, g)
+    ref = x @ w.T
+    assert np.all(np.abs(y - ref) <= 1e-12 * bound + 1e-300)
+    np.testing.assert_allclose(bound, np.abs(x) @ np.abs(w).T, rtol=1e-12)
+    # linearity in x (scaling by 2 is exact)
+    y2, _ = oracle.grouped_int4(2 * x, q, s, z, g)
+    assert np.array_equal(y2, 2 * y)
+
+
+def test_int4_pack_round_trip_and_pairs():
+    _, q, _, z, g = _grouped(n=48, k=384, g=128)
+    packed = oracle.pack_int4(q)
+    assert np.array_equal(oracle.unpack_int4(packed, 48, 384), q)
+    # high nibbles of the codes are ignored
+    assert np.array_equal(oracle.pack_int4(q | 0xF0), packed)
+    # (word >> 4i) & 0x000F000F holds the pair (k0 + 2i, k0 + 2i + 1)
+    kb_per = 384 // 128
+    for nb, kb, l, t in [(0, 0, 0, 0), (2, 2, 45, 3), (1, 1, 18, 1)]:
+        word = int(packed[(nb * kb_per + kb) * 256 + 4 * l + t])
+        col = 16 * nb + l % 16
+        k0 = 128 * kb + 32 * (l // 16) + 8 * t
+        for i in range(4):
+            pair = (word >> (4 * i)) & 0x000F000F
+            assert (pair & 0xF, pair >> 16) == (int(q[col, k0 + 2 * i]), int(q[col, k0 + 2 * i + 1]))
+    zp = oracle.pack_int4_zeros(z)
+    ng = z.shape[1]
+    for c in (0, 7, 8, 47):
+        for gi in range(ng):
+            assert (int(zp[gi * 6 + c // 8]) >> (4 * (c % 8))) & 15 == int(z[c, gi])
+
+
+def test_int4_evidence_bytes():
+    """"linear_4bit/mod.rs" module doc: the fused path avoids an 8x expansion (f32 vs 4-bit)."""
+    b = oracle.int4_evidence_bytes(32, 11008, 4096, 128)
+    assert b["packed_weight_bytes"] == 22_544_384
+    assert b["dequantized_weight_bytes"] == 180_355_072
+    assert b["dequantized_weight_bytes"] == 8 * b["packed_weight_bytes"]
+    assert b["sidecar_bytes"] == 704_512 + 176_128
+    assert b["output_bytes"] == 704_512
+
+
+# ---------------------------------------------------------------------------
+# O5: A4W4
+# ---------------------------------------------------------------------------
+def test_a4w4_integer_inputs_are_their_own_codes():
+    g = synthetic.rng(41)
+    x = g.integers(-8, 8, (9, 70)).astype(np.float32)
+    q = oracle.quant_int4_tensor(x, 1.0, 1e-5)
+    assert np.array_equal(q, x.astype(np.int8))
+
+
+def test_a4w4_quant_brute_force_and_saturation():
+    d = synthetic.a4w4(40, 24, 96, seed=42)
+    x = d["x"].float().numpy()
+    for scale in (d["scale_a"], d["scale_a"] / 4, 0.0):
+        q = oracle.quant_int4_tensor(x, scale, 1e-5)
+        sp = float(max(np.float32(scale), np.float32(1e-5)))
+        quo = (x.astype(np.float64) / sp).astype(np.float32)  # correctly rounded fp32 quotient
+        ref = np.clip([round(Fraction(float(v))) for v in quo.ravel()], -8, 7).reshape(x.shape)
+        assert np.array_equal(q, ref)
+    q_small = oracle.quant_int4_tensor(x, d["scale_a"] / 4, 1e-5)
+    assert (q_small == -8).any() and (q_small == 7).any()
+
+
+def test_a4w4_dequant_brute_force():
+    d = synthetic.a4w4(33, 20, 130, seed=43)
+    x, w = d["x"].float().numpy(), d["w"].float().numpy()
+    qa, qw, acc, y = oracle.a4w4(x, w, d["scale_a"], d["scale_w"], d["eps"])
+    sa = float(oracle.effective_scale(d["scale_a"], d["eps"]))
+    sw = float(oracle.effective_scale(d["scale_w"], d["eps"]))
+    ref = (qa.astype(np.float64) * sa) @ (qw.astype(np.float64) * sw).T
+    np.testing.assert_allclose(y, ref, rtol=1e-12)
+    assert np.array_equal(acc.astype(np.int64), qa.astype(np.int64) @ qw.astype(np.int64).T)
+
+
+# ---------------------------------------------------------------------------
+# Output rounding
+# ---------------------------------------------------------------------------
+def test_round_f16_matches_numpy():
+    g = synthetic.rng(51)
+    v = np.concatenate([g.standard_normal(20000) * 10.0 ** g.integers(-9, 6, 20000),
+                        [0.0, -0.0, 65504.0, 65519.99, 65520.0, -70000.0, 2.0 ** -24, 2.0 ** -25,
+                         3 * 2.0 ** -26, 1 + 2.0 ** -11, 1 + 3 * 2.0 ** -11]])
+    got = oracle.round_f16(v)
+    assert np.array_equal(got, v.astype(np.float16).view(np.uint16))
+
+
+def test_round_bf16_matches_torch_on_fp32_values():
+    g = synthetic.rng(52)
+    v32 = (g.standard_normal(20000) * 10.0 ** g.integers(-30, 30, 20000)).astype(np.float32)
+    ties = np.array([1 + 2.0 ** -8, 1 + 3 * 2.0 ** -8, -(1 + 2.0 ** -8), 3.0e38, 1e-40], np.float32)
+    v32 = np.concatenate([v32, ties])
+    got = oracle.round_bf16(v32.astype(np.float64))
+    ref = torch.from_numpy(v32).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(got, ref)
+    assert got[-5] == 0x3F80 and got[-4] == 0x3F82   # ties go to the even mantissa
