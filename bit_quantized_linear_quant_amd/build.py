@@ -1,0 +1,72 @@
+"""Build ``libqlinear.so`` (the gfx950 HIP kernels and their C ABI) in-tree.
+
+Usage: ``python -m bit_quantized_linear_quant_amd.build`` (or call
+``build()``).  Every source is compiled with hipcc for gfx950 only; objects go
+to ``_build/`` next to this file and the shared library next to it.
+"""
+from __future__ import annotations
+
+import concurrent.futures as cf
+import os
+import shutil
+import subprocess
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+CSRC = os.path.join(HERE, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+BUILD = os.path.join(HERE, "_build")
+LIB = os.path.join(HERE, "libqlinear.so")
+SOURCES = ["api.hip", "quant.hip", "pack.hip", "gemm_i8.hip", "gemm_w2a8.hip", "gemm_int4.hip"]
+ARCH = "gfx950"
+
+
+def hipcc() -> str:
+    for cand in (shutil.which("hipcc"), "/opt/rocm/bin/hipcc"):
+        if cand and os.path.exists(cand):
+            return cand
+    raise RuntimeError("hipcc not found (ROCm is required to build libqlinear)")
+
+
+def compile_flags() -> list[str]:
+    return [
+        f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
+        # packed fp32 VALU ops are kept out of every kernel
+        "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+        # IEEE fp32 division and square root (the quantizers divide)
+        "-fhip-fp32-correctly-rounded-divide-sqrt",
+        "-Wno-unused-command-line-argument",
+        f"-I{INCLUDE}", f"-I{CSRC}",
+    ]
+
+
+def _compile(src: str) -> str:
+    obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
+    cmd = [hipcc(), *compile_flags(), "-c", os.path.join(CSRC, src), "-o", obj]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"hipcc failed for {src}:\n{res.stderr}")
+    return obj
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every kernel source for gfx950 and link ``libqlinear.so``."""
+    os.makedirs(BUILD, exist_ok=True)
+    jobs = min(len(SOURCES), max(1, min(8, os.cpu_count() or 1)))
+    with cf.ThreadPoolExecutor(jobs) as ex:
+        objs = list(ex.map(_compile, SOURCES))
+    tmp = LIB + ".tmp"
+    cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"link failed:\n{res.stderr}")
+    os.replace(tmp, LIB)
+    if verbose:
+        print(f"built {LIB}")
+    return LIB
+
+
+if __name__ == "__main__":
+    build(verbose=True)
+    sys.exit(0)

@@ -1,0 +1,259 @@
+// BitLinear product on 2-bit packed ternary weights, gfx950
+// ("Class BitLinear" forward steps 4-5: integer codes times ternary codes,
+// then the per-token activation scale and the scalar weight scale).
+//
+// The packed layout (16 columns x 256 k per 1 KB block, 16 bytes per lane)
+// is fragment-ordered: word t of lane l is exactly the 16-k B operand of
+// lane l in v_mfma_i32_16x16x64_i8 step t, so weights go straight from HBM
+// into registers and are unpacked there -- (word >> 2a) & 0x03030303 is four
+// consecutive k as bytes code+1 in {0,1,2} -- with no dequantized weight in
+// memory.  The A operand of lane l in step t is the 16 bytes of its token
+// row at k = 256kb + 64(l/16) + 16t, the same k assignment, so the matrix
+// core sums matching terms.  The accumulator holds sum x*(code+1); the
+// epilogue subtracts the token's code sum: acc = sum x*code exactly.
+//
+// m > 16: 128 x 128 tiles, 2 x 2 waves of 64 x 64, A staged in LDS per
+//         256-k step (rows padded to 272 bytes), B loaded per wave.
+// m <= 16: decode GEMV.  The m rows fill one 16-row MFMA block (missing rows
+//         are zero and cost no memory traffic); each workgroup owns NBLK
+//         column blocks and its waves split k; int32 partials are summed
+//         in LDS in a fixed order (exact, hence deterministic).
+#include "ql_device.hpp"
+#include "ql_launch.hpp"
+
+namespace ql {
+
+namespace {
+
+__device__ __forceinline__ v4i unpack_tern(uint32_t w) {
+    return v4i{(int)(w & 0x03030303u), (int)((w >> 2) & 0x03030303u), (int)((w >> 4) & 0x03030303u),
+               (int)((w >> 6) & 0x03030303u)};
+}
+
+__device__ __forceinline__ uint32_t word_of(const uint4 &v, int t) {
+    return t == 0 ? v.x : (t == 1 ? v.y : (t == 2 ? v.z : v.w));
+}
+
+template <int OUT>
+__device__ __forceinline__ void epilogue_store(void *out, int64_t idx, int32_t acc, int32_t rs,
+                                               float pts, float g) {
+    const int32_t v = acc - rs;
+    if (OUT == OUT_I32) static_cast<int32_t *>(out)[idx] = v;
+    else store_out<OUT>(out, idx, __fmul_rn(__fmul_rn((float)v, pts), g));
+}
+
+// ---------------------------------------------------------------------------
+// m > 16: tiled GEMM
+// ---------------------------------------------------------------------------
+constexpr int GBM = 128, GBN = 128, GBK = 256;
+constexpr int kGRow = GBK + 16;  // LDS row stride (bytes)
+constexpr int kGThreads = 256;
+
+template <int OUT>
+__global__ __launch_bounds__(kGThreads) void w2a8_gemm_kernel(const int8_t *__restrict__ xq,
+                                                              const float *__restrict__ pts,
+                                                              const int32_t *__restrict__ rowsum,
+                                                              const uint32_t *__restrict__ packed,
+                                                              const double *__restrict__ gamma,
+                                                              int64_t m, int64_t n, int64_t k,
+                                                              void *__restrict__ out) {
+    __shared__ __attribute__((aligned(16))) int8_t As[GBM * kGRow];
+    const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+    const int wm = wave / 2, wn = wave % 2;
+    const int64_t m0 = (int64_t)blockIdx.y * GBM;
+    const int64_t nbase = (int64_t)blockIdx.x * (GBN / 16) + wn * 4;  // first column block of the wave
+    const int64_t nblocks = n / 16, kblocks = k / GBK;
+
+    uint4 ra[8];
+    uint4 rb[4];
+    auto gload = [&](int64_t kb) {
+#pragma unroll
+        for (int c = 0; c < 8; c++) {
+            const int chunk = tid + c * kGThreads;
+            const int row = chunk / 16, c16 = chunk % 16;
+            const int64_t gr = m0 + row;
+            ra[c] = gr < m ? *reinterpret_cast<const uint4 *>(xq + gr * k + kb * GBK + 16 * c16)
+                           : make_uint4(0, 0, 0, 0);
+        }
+#pragma unroll
+        for (int j = 0; j < 4; j++) {
+            const int64_t nb = nbase + j;
+            rb[j] = nb < nblocks
+                        ? *reinterpret_cast<const uint4 *>(packed + (nb * kblocks + kb) * 256 + 4 * lane)
+                        : make_uint4(0x55555555u, 0x55555555u, 0x55555555u, 0x55555555u);
+        }
+    };
+    auto sstore = [&]() {
+#pragma unroll
+        for (int c = 0; c < 8; c++) {
+            const int chunk = tid + c * kGThreads;
+            const int row = chunk / 16, c16 = chunk % 16;
+            *reinterpret_cast<uint4 *>(As + row * kGRow + 16 * c16) = ra[c];
+        }
+    };
+
+    v4i acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; i++)
+#pragma unroll
+        for (int j = 0; j < 4; j++) acc[i][j] = v4i{0, 0, 0, 0};
+
+    gload(0);
+    sstore();
+    __syncthreads();
+    const int fr = lane % 16, fk = 64 * (lane / 16);
+    for (int64_t kb = 0; kb < kblocks; kb++) {
+        uint4 cb[4];
+#pragma unroll
+        for (int j = 0; j < 4; j++) cb[j] = rb[j];
+        if (kb + 1 < kblocks) gload(kb + 1);
+#pragma unroll
+        for (int t = 0; t < 4; t++) {
+            v4i a[4];
+#pragma unroll
+            for (int i = 0; i < 4; i++)
+                a[i] = *reinterpret_cast<const v4i *>(As + (wm * 64 + i * 16 + fr) * kGRow + fk + 16 * t);
+#pragma unroll
+            for (int j = 0; j < 4; j++) {
+                const v4i b = unpack_tern(word_of(cb[j], t));
+#pragma unroll
+                for (int i = 0; i < 4; i++)
+                    acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[i], b, acc[i][j], 0, 0, 0);
+            }
+        }
+        __syncthreads();
+        if (kb + 1 < kblocks) {
+            sstore();
+            __syncthreads();
+        }
+    }
+
+    const float g = OUT == OUT_I32 ? 0.0f : (float)gamma[0];  // gamma may be NULL for int32 output
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+        const int64_t nb = nbase + j;
+        if (nb >= nblocks) continue;
+        const int64_t col = nb * 16 + fr;
+#pragma unroll
+        for (int i = 0; i < 4; i++)
+#pragma unroll
+            for (int r = 0; r < 4; r++) {
+                const int64_t row = m0 + wm * 64 + i * 16 + 4 * (lane / 16) + r;
+                if (row < m)
+                    epilogue_store<OUT>(out, row * n + col, acc[i][j][r], rowsum[row],
+                                        OUT == OUT_I32 ? 0.0f : pts[row], g);
+            }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// m <= 16: split-K decode GEMV
+// ---------------------------------------------------------------------------
+template <int NBLK, int WAVES, int U, int OUT>
+__global__ __launch_bounds__(WAVES * 64) void w2a8_gemv_kernel(const int8_t *__restrict__ xq,
+                                                               const float *__restrict__ pts,
+                                                               const int32_t *__restrict__ rowsum,
+                                                               const uint32_t *__restrict__ packed,
+                                                               const double *__restrict__ gamma,
+                                                               int64_t m, int64_t n, int64_t k,
+                                                               void *__restrict__ out) {
+    __shared__ v4i red[WAVES][NBLK][kWave];
+    const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+    const int64_t nb0 = (int64_t)blockIdx.x * NBLK;
+    const int64_t nblocks = n / 16, kblocks = k / 256;
+    const int fr = lane % 16;
+    const bool row_ok = fr < m;
+    const int8_t *xrow = xq + (int64_t)fr * k + 64 * (lane / 16);
+
+    v4i acc[NBLK];
+#pragma unroll
+    for (int j = 0; j < NBLK; j++) acc[j] = v4i{0, 0, 0, 0};
+
+    for (int64_t kb0 = wave; kb0 < kblocks; kb0 += (int64_t)WAVES * U) {
+        uint4 bw[U][NBLK];
+        v4i af[U][4];
+#pragma unroll
+        for (int u = 0; u < U; u++) {
+            const int64_t kb = kb0 + (int64_t)u * WAVES;
+            const bool kb_ok = kb < kblocks;
+#pragma unroll
+            for (int j = 0; j < NBLK; j++) {
+                const int64_t nb = nb0 + j;
+                bw[u][j] = (kb_ok && nb < nblocks)
+                               ? *reinterpret_cast<const uint4 *>(packed + (nb * kblocks + kb) * 256 + 4 * lane)
+                               : make_uint4(0x55555555u, 0x55555555u, 0x55555555u, 0x55555555u);
+            }
+#pragma unroll
+            for (int t = 0; t < 4; t++)
+                af[u][t] = (kb_ok && row_ok) ? *reinterpret_cast<const v4i *>(xrow + kb * 256 + 16 * t)
+                                             : v4i{0, 0, 0, 0};
+        }
+#pragma unroll
+        for (int u = 0; u < U; u++)
+#pragma unroll
+            for (int t = 0; t < 4; t++)
+#pragma unroll
+                for (int j = 0; j < NBLK; j++)
+                    acc[j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(af[u][t], unpack_tern(word_of(bw[u][j], t)),
+                                                                   acc[j], 0, 0, 0);
+    }
+
+#pragma unroll
+    for (int j = 0; j < NBLK; j++) red[wave][j][lane] = acc[j];
+    __syncthreads();
+    const float g = OUT == OUT_I32 ? 0.0f : (float)gamma[0];  // gamma may be NULL for int32 output
+    for (int j = wave; j < NBLK; j += WAVES) {
+        const int64_t nb = nb0 + j;
+        if (nb >= nblocks) continue;
+        v4i s = red[0][j][lane];
+#pragma unroll
+        for (int w = 1; w < WAVES; w++) s += red[w][j][lane];
+        const int64_t col = nb * 16 + fr;
+#pragma unroll
+        for (int r = 0; r < 4; r++) {
+            const int64_t row = 4 * (lane / 16) + r;
+            if (row < m)
+                epilogue_store<OUT>(out, row * n + col, s[r], rowsum[row],
+                                    OUT == OUT_I32 ? 0.0f : pts[row], g);
+        }
+    }
+}
+
+template <int NBLK, int OUT>
+hipError_t launch_gemv(const int8_t *xq, const float *pts, const int32_t *rowsum, const uint32_t *packed,
+                       const double *gamma, int64_t m, int64_t n, int64_t k, void *out, hipStream_t st) {
+    constexpr int WAVES = 4, U = 2;
+    const int64_t nblocks = n / 16;
+    const unsigned grid = (unsigned)((nblocks + NBLK - 1) / NBLK);
+    hipLaunchKernelGGL((w2a8_gemv_kernel<NBLK, WAVES, U, OUT>), dim3(grid), dim3(WAVES * 64), 0, st, xq,
+                       pts, rowsum, packed, gamma, m, n, k, out);
+    return hipGetLastError();
+}
+
+template <int OUT>
+hipError_t launch_out(const int8_t *xq, const float *pts, const int32_t *rowsum, const uint32_t *packed,
+                      const double *gamma, int64_t m, int64_t n, int64_t k, void *out, hipStream_t st) {
+    if (m <= 16) {
+        if (m <= 4) return launch_gemv<2, OUT>(xq, pts, rowsum, packed, gamma, m, n, k, out, st);
+        return launch_gemv<4, OUT>(xq, pts, rowsum, packed, gamma, m, n, k, out, st);
+    }
+    dim3 grid((unsigned)((n + GBN - 1) / GBN), (unsigned)((m + GBM - 1) / GBM));
+    hipLaunchKernelGGL((w2a8_gemm_kernel<OUT>), grid, dim3(kGThreads), 0, st, xq, pts, rowsum, packed,
+                       gamma, m, n, k, out);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_gemm_w2a8(const int8_t *xq, const float *pts, const int32_t *rowsum,
+                            const uint32_t *packed, const double *gamma, int64_t m, int64_t n,
+                            int64_t k, int out_kind, void *out, hipStream_t st) {
+    if (m > (int64_t)GBM * 65535) return hipErrorInvalidValue;
+    switch (out_kind) {
+        case OUT_F16: return launch_out<OUT_F16>(xq, pts, rowsum, packed, gamma, m, n, k, out, st);
+        case OUT_BF16: return launch_out<OUT_BF16>(xq, pts, rowsum, packed, gamma, m, n, k, out, st);
+        default: return launch_out<OUT_I32>(xq, pts, rowsum, packed, gamma, m, n, k, out, st);
+    }
+}
+
+}  // namespace ql

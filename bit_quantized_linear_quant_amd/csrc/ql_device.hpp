@@ -1,0 +1,106 @@
+// Device helpers shared by the gfx950 kernels of libqlinear: vector types,
+// element conversions, wave64 reductions and the rounding stores of the
+// dequant epilogue.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ql {
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef _Float16 v8h __attribute__((ext_vector_type(8)));
+typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+
+constexpr int kWave = 64;
+
+// Output element kinds of the epilogue.
+enum OutKind : int { OUT_F16 = 0, OUT_BF16 = 1, OUT_I32 = 2, OUT_F32 = 3 };
+
+// Input element kinds of the quantizers.
+enum InKind : int { IN_F32 = 0, IN_F16 = 1, IN_BF16 = 2 };
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) {
+    return __uint_as_float(b << 16);
+}
+
+__device__ __forceinline__ float f16_bits_to_f32(uint32_t b) {
+    _Float16 h = __builtin_bit_cast(_Float16, (uint16_t)b);
+    return (float)h;
+}
+
+// fp32 -> bf16, round to nearest, ties to even; NaN stays a quiet NaN and
+// values past the largest finite bf16 become +-inf.
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
+}
+
+// fp32 -> fp16, round to nearest, ties to even (v_cvt_f16_f32 under the
+// default rounding mode); overflow gives +-inf.
+__device__ __forceinline__ uint16_t f32_to_f16_rne(float f) {
+    return __builtin_bit_cast(uint16_t, (_Float16)f);
+}
+
+// Load element i of a row of kind K as fp32 (exact for all three kinds).
+template <int K>
+__device__ __forceinline__ float load_elem(const void *p, int64_t i) {
+    if constexpr (K == IN_F32) return static_cast<const float *>(p)[i];
+    else if constexpr (K == IN_F16) return f16_bits_to_f32(static_cast<const uint16_t *>(p)[i]);
+    else return bf16_bits_to_f32(static_cast<const uint16_t *>(p)[i]);
+}
+
+// Load 8 consecutive elements starting at element i (16-byte aligned for
+// 16-bit kinds, 32-byte aligned for fp32) as fp32.
+template <int K>
+__device__ __forceinline__ void load8_vec(const void *p, int64_t i, float v[8]) {
+    if constexpr (K == IN_F32) {
+        const float4 *q = reinterpret_cast<const float4 *>(static_cast<const float *>(p) + i);
+        float4 a = q[0], b = q[1];
+        v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+        v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+    } else {
+        uint4 u = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(p) + i);
+        uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+        for (int j = 0; j < 4; j++) {
+            if constexpr (K == IN_F16) {
+                v[2 * j] = f16_bits_to_f32(w[j] & 0xffffu);
+                v[2 * j + 1] = f16_bits_to_f32(w[j] >> 16);
+            } else {
+                v[2 * j] = __uint_as_float(w[j] << 16);
+                v[2 * j + 1] = __uint_as_float(w[j] & 0xffff0000u);
+            }
+        }
+    }
+}
+
+template <typename T>
+__device__ __forceinline__ T wave_max(T v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+        T u = __shfl_xor(v, o, kWave);
+        v = u > v ? u : v;
+    }
+    return v;
+}
+
+template <typename T>
+__device__ __forceinline__ T wave_sum(T v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+    return v;
+}
+
+// Store one epilogue value.  For OUT_I32 the caller passes the integer.
+template <int OUT>
+__device__ __forceinline__ void store_out(void *out, int64_t idx, float y) {
+    if constexpr (OUT == OUT_F16) static_cast<uint16_t *>(out)[idx] = f32_to_f16_rne(y);
+    else if constexpr (OUT == OUT_BF16) static_cast<uint16_t *>(out)[idx] = f32_to_bf16_rne(y);
+    else static_cast<float *>(out)[idx] = y;
+}
+
+}  // namespace ql

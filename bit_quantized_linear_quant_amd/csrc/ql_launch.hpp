@@ -1,0 +1,57 @@
+// Internal launchers of libqlinear: one per kernel family.  The C ABI in
+// api.hip validates arguments, then calls these; each enqueues its kernels
+// on the given stream and returns hipGetLastError().
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace ql {
+
+// quant.hip
+hipError_t launch_quant_act(int in_kind, const void *x, int64_t m, int64_t k, bool rmsnorm,
+                            float eps_norm, float eps_q, int8_t *q, float *pts, int32_t *rowsum,
+                            hipStream_t st);
+hipError_t launch_quant_int4_tensor(int in_kind, const void *x, int64_t count, const float *scale,
+                                    float eps, int8_t *q, hipStream_t st);
+
+// pack.hip
+size_t absmean_partial_count(int64_t count);
+hipError_t launch_pack_ternary(const float *w, bool layout_nk, int64_t n, int64_t k, double eps,
+                               uint32_t *packed, double *gamma, double *partials, hipStream_t st);
+hipError_t launch_pack_int4_weight(const uint8_t *codes, int64_t n, int64_t k, uint32_t *packed,
+                                   hipStream_t st);
+hipError_t launch_pack_int4_zeros(const uint8_t *z, int64_t n, int64_t groups, uint32_t *packed,
+                                  hipStream_t st);
+
+// gemm_i8.hip: int8 x int8 -> int32 tiled MFMA GEMM with a fused epilogue.
+enum EpiKind : int { EPI_ROWCOL = 0, EPI_SCALARS = 1 };
+struct GemmI8Args {
+    const int8_t *x;     // [m, k]
+    const int8_t *w;     // [n, k] (nk) or [k, n]
+    bool w_nk;
+    int epi;             // EpiKind
+    const float *pts;    // EPI_ROWCOL: [m]
+    const float *deq;    // EPI_ROWCOL: [n]
+    const float *sa;     // EPI_SCALARS: device scalar
+    const float *sw;     // EPI_SCALARS: device scalar
+    float eps;           // EPI_SCALARS: guard of both scalars
+    int64_t m, n, k;
+    int out_kind;        // OutKind
+    void *out;           // [m, n]
+};
+hipError_t launch_gemm_i8(const GemmI8Args &a, hipStream_t st);
+
+// gemm_w2a8.hip: packed ternary weights.
+hipError_t launch_gemm_w2a8(const int8_t *xq, const float *pts, const int32_t *rowsum,
+                            const uint32_t *packed, const double *gamma, int64_t m, int64_t n,
+                            int64_t k, int out_kind, void *out, hipStream_t st);
+
+// gemm_int4.hip: grouped affine INT4 with fp16 activations.
+hipError_t launch_gemm_int4_grouped(const uint16_t *x, const uint32_t *packed_w,
+                                    const uint16_t *scales, const uint32_t *packed_zeros,
+                                    int64_t group_size, int64_t m, int64_t n, int64_t k,
+                                    int out_kind, void *out, hipStream_t st);
+
+}  // namespace ql

@@ -1,0 +1,254 @@
+// Activation quantizers for gfx950.
+//
+// quant_act: per-token absmax int8 codes with an optional parameter-free
+// RMSNorm folded into the per-token scale ("Class BitLinear" forward steps
+// 1-2 and 5; "Common Attention Utilities" activation_quant).  One 256-thread
+// workgroup per token row; the row is read from HBM once and kept in
+// registers (up to 8192 elements), the absmax / sum of squares are wave64
+// shuffle reductions, and the codes are written with 8-byte stores.
+//
+// quant_int4_tensor: per-tensor 4-bit codes of "Q4LinearFunction" forward,
+// q = clamp(rne(x / max(scale, eps)), -8, 7) with IEEE division.
+#include "ql_device.hpp"
+#include "ql_launch.hpp"
+
+namespace ql {
+
+namespace {
+
+constexpr int kQThreads = 256;
+constexpr int kQCache = 4;  // chunks of 8 elements per thread held in registers
+
+template <int K, bool VEC>
+__device__ __forceinline__ void load_chunk(const void *row, int64_t ch, int64_t k, float v[8]) {
+    const int64_t base = ch * 8;
+    if (VEC && base + 8 <= k) {
+        load8_vec<K>(row, base, v);
+    } else {
+#pragma unroll
+        for (int j = 0; j < 8; j++) v[j] = (base + j < k) ? load_elem<K>(row, base + j) : 0.0f;
+    }
+}
+
+__device__ __forceinline__ int code_i8(float v, float s) {
+    float t = __builtin_rintf(__fmul_rn(v, s));
+    t = fminf(fmaxf(t, -128.0f), 127.0f);
+    return (int)t;
+}
+
+template <bool VEC>
+__device__ __forceinline__ int store_chunk(int8_t *qrow, int64_t ch, int64_t k, const float v[8], float s) {
+    const int64_t base = ch * 8;
+    int sum = 0;
+    if (VEC && base + 8 <= k) {
+        uint32_t lo = 0, hi = 0;
+#pragma unroll
+        for (int j = 0; j < 4; j++) {
+            int c0 = code_i8(v[j], s), c1 = code_i8(v[j + 4], s);
+            sum += c0 + c1;
+            lo |= (uint32_t)(c0 & 0xff) << (8 * j);
+            hi |= (uint32_t)(c1 & 0xff) << (8 * j);
+        }
+        *reinterpret_cast<uint2 *>(qrow + base) = make_uint2(lo, hi);
+    } else {
+#pragma unroll
+        for (int j = 0; j < 8; j++) {
+            if (base + j < k) {
+                int c = code_i8(v[j], s);
+                sum += c;
+                qrow[base + j] = (int8_t)c;
+            }
+        }
+    }
+    return sum;
+}
+
+// Block-wide reduction of one value through LDS after a wave reduction; the
+// four wave results are combined in a fixed order, so the result does not
+// depend on scheduling.
+template <typename T, bool MAX>
+__device__ __forceinline__ T block_reduce(T v, T *lds) {
+    v = MAX ? wave_max(v) : wave_sum(v);
+    const int w = threadIdx.x / kWave;
+    if ((threadIdx.x % kWave) == 0) lds[w] = v;
+    __syncthreads();
+    T r = lds[0];
+#pragma unroll
+    for (int i = 1; i < kQThreads / kWave; i++) r = MAX ? (lds[i] > r ? lds[i] : r) : r + lds[i];
+    __syncthreads();
+    return r;
+}
+
+template <int K, bool VEC, bool RMS>
+__global__ __launch_bounds__(kQThreads) void quant_act_kernel(const void *__restrict__ x, int64_t k,
+                                                              float eps_norm, float eps_q,
+                                                              int8_t *__restrict__ q,
+                                                              float *__restrict__ pts,
+                                                              int32_t *__restrict__ rowsum) {
+    __shared__ float red_f[kQThreads / kWave];
+    __shared__ int red_i[kQThreads / kWave];
+    const int64_t row = blockIdx.x;
+    const int esz = K == IN_F32 ? 4 : 2;
+    const void *xr = static_cast<const char *>(x) + row * k * esz;
+    int8_t *qr = q + row * k;
+    const int64_t nchunk = (k + 7) / 8;
+    const int tid = threadIdx.x;
+
+    float cache[kQCache][8];
+    float amax = 0.0f, ss = 0.0f;
+#pragma unroll
+    for (int c = 0; c < kQCache; c++) {
+        const int64_t ch = (int64_t)c * kQThreads + tid;
+        if (ch < nchunk) {
+            load_chunk<K, VEC>(xr, ch, k, cache[c]);
+#pragma unroll
+            for (int j = 0; j < 8; j++) {
+                amax = fmaxf(amax, fabsf(cache[c][j]));
+                if (RMS) ss += cache[c][j] * cache[c][j];
+            }
+        }
+    }
+    for (int64_t ch = (int64_t)kQCache * kQThreads + tid; ch < nchunk; ch += kQThreads) {
+        float v[8];
+        load_chunk<K, VEC>(xr, ch, k, v);
+#pragma unroll
+        for (int j = 0; j < 8; j++) {
+            amax = fmaxf(amax, fabsf(v[j]));
+            if (RMS) ss += v[j] * v[j];
+        }
+    }
+    amax = block_reduce<float, true>(amax, red_f);
+    if (RMS) ss = block_reduce<float, false>(ss, red_f);
+
+    const float ap = amax > eps_q ? amax : eps_q;
+    const float s = __fdiv_rn(127.0f, ap);
+
+    int rs = 0;
+#pragma unroll
+    for (int c = 0; c < kQCache; c++) {
+        const int64_t ch = (int64_t)c * kQThreads + tid;
+        if (ch < nchunk) rs += store_chunk<VEC>(qr, ch, k, cache[c], s);
+    }
+    for (int64_t ch = (int64_t)kQCache * kQThreads + tid; ch < nchunk; ch += kQThreads) {
+        float v[8];
+        load_chunk<K, VEC>(xr, ch, k, v);
+        rs += store_chunk<VEC>(qr, ch, k, v, s);
+    }
+    rs = block_reduce<int, false>(rs, red_i);
+
+    if (tid == 0) {
+        float p;
+        if (RMS) {
+            const float r = 1.0f / sqrtf(ss / (float)k + eps_norm);
+            p = ap * r / 127.0f;
+        } else {
+            p = __fdiv_rn(ap, 127.0f);
+        }
+        pts[row] = p;
+        if (rowsum) rowsum[row] = rs;
+    }
+}
+
+constexpr int kI4Threads = 256;
+
+__device__ __forceinline__ uint32_t code_i4(float v, float sp) {
+    float t = __builtin_rintf(__fdiv_rn(v, sp));
+    t = fminf(fmaxf(t, -8.0f), 7.0f);
+    return (uint32_t)((int)t) & 0xffu;
+}
+
+template <int K, bool VEC>
+__global__ __launch_bounds__(kI4Threads) void quant_int4_tensor_kernel(const void *__restrict__ x,
+                                                                       int64_t count,
+                                                                       const float *__restrict__ scale,
+                                                                       float eps,
+                                                                       int8_t *__restrict__ q) {
+    const float sc = *scale;
+    const float sp = sc > eps ? sc : eps;
+    const int64_t nchunk = (count + 7) / 8;
+    const int64_t stride = (int64_t)gridDim.x * kI4Threads;
+    for (int64_t ch = (int64_t)blockIdx.x * kI4Threads + threadIdx.x; ch < nchunk; ch += stride) {
+        const int64_t base = ch * 8;
+        if (VEC && base + 8 <= count) {
+            float v[8];
+            load8_vec<K>(x, base, v);
+            uint32_t lo = 0, hi = 0;
+#pragma unroll
+            for (int j = 0; j < 4; j++) {
+                lo |= code_i4(v[j], sp) << (8 * j);
+                hi |= code_i4(v[j + 4], sp) << (8 * j);
+            }
+            *reinterpret_cast<uint2 *>(q + base) = make_uint2(lo, hi);
+        } else {
+            for (int j = 0; j < 8 && base + j < count; j++)
+                q[base + j] = (int8_t)code_i4(load_elem<K>(x, base + j), sp);
+        }
+    }
+}
+
+template <int K, bool VEC, bool RMS>
+hipError_t launch_quant_act_t(const void *x, int64_t m, int64_t k, float eps_norm, float eps_q,
+                              int8_t *q, float *pts, int32_t *rowsum, hipStream_t st) {
+    hipLaunchKernelGGL((quant_act_kernel<K, VEC, RMS>), dim3((unsigned)m), dim3(kQThreads), 0, st,
+                       x, k, eps_norm, eps_q, q, pts, rowsum);
+    return hipGetLastError();
+}
+
+template <int K, bool VEC>
+hipError_t launch_quant_act_k(bool rms, const void *x, int64_t m, int64_t k, float eps_norm,
+                              float eps_q, int8_t *q, float *pts, int32_t *rowsum, hipStream_t st) {
+    return rms ? launch_quant_act_t<K, VEC, true>(x, m, k, eps_norm, eps_q, q, pts, rowsum, st)
+               : launch_quant_act_t<K, VEC, false>(x, m, k, eps_norm, eps_q, q, pts, rowsum, st);
+}
+
+template <int K>
+hipError_t launch_quant_act_v(bool vec, bool rms, const void *x, int64_t m, int64_t k,
+                              float eps_norm, float eps_q, int8_t *q, float *pts, int32_t *rowsum,
+                              hipStream_t st) {
+    return vec ? launch_quant_act_k<K, true>(rms, x, m, k, eps_norm, eps_q, q, pts, rowsum, st)
+               : launch_quant_act_k<K, false>(rms, x, m, k, eps_norm, eps_q, q, pts, rowsum, st);
+}
+
+template <int K>
+hipError_t launch_i4_v(bool vec, const void *x, int64_t count, const float *scale, float eps,
+                       int8_t *q, hipStream_t st) {
+    const int64_t nchunk = (count + 7) / 8;
+    int64_t blocks = (nchunk + kI4Threads - 1) / kI4Threads;
+    if (blocks > 256 * 64) blocks = 256 * 64;
+    if (vec)
+        hipLaunchKernelGGL((quant_int4_tensor_kernel<K, true>), dim3((unsigned)blocks),
+                           dim3(kI4Threads), 0, st, x, count, scale, eps, q);
+    else
+        hipLaunchKernelGGL((quant_int4_tensor_kernel<K, false>), dim3((unsigned)blocks),
+                           dim3(kI4Threads), 0, st, x, count, scale, eps, q);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_quant_act(int in_kind, const void *x, int64_t m, int64_t k, bool rmsnorm,
+                            float eps_norm, float eps_q, int8_t *q, float *pts, int32_t *rowsum,
+                            hipStream_t st) {
+    // Vector path: every row starts 16-byte aligned and holds whole 8-element
+    // chunks, and the int8 code row is 8-byte aligned.
+    const bool vec = (k % 8) == 0;
+    switch (in_kind) {
+        case IN_F32: return launch_quant_act_v<IN_F32>(vec, rmsnorm, x, m, k, eps_norm, eps_q, q, pts, rowsum, st);
+        case IN_F16: return launch_quant_act_v<IN_F16>(vec, rmsnorm, x, m, k, eps_norm, eps_q, q, pts, rowsum, st);
+        default: return launch_quant_act_v<IN_BF16>(vec, rmsnorm, x, m, k, eps_norm, eps_q, q, pts, rowsum, st);
+    }
+}
+
+hipError_t launch_quant_int4_tensor(int in_kind, const void *x, int64_t count, const float *scale,
+                                    float eps, int8_t *q, hipStream_t st) {
+    // base pointers are 16-byte aligned; chunk starts are multiples of 8
+    // elements, so the vector path is always aligned.
+    const bool vec = true;
+    switch (in_kind) {
+        case IN_F32: return launch_i4_v<IN_F32>(vec, x, count, scale, eps, q, st);
+        case IN_F16: return launch_i4_v<IN_F16>(vec, x, count, scale, eps, q, st);
+        default: return launch_i4_v<IN_BF16>(vec, x, count, scale, eps, q, st);
+    }
+}
+
+}  // namespace ql

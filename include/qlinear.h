@@ -1,0 +1,266 @@
+/*
+ * qlinear.h - C ABI of the MI355X (gfx950) quantized linear layer library
+ * (libqlinear.so).
+ *
+ * The layer: activations quantized per token to int8 (absmax, optionally
+ * after a parameter-free RMSNorm), weights that are ternary (absmean),
+ * int8, 4-bit grouped affine, or 4-bit per-tensor, and an integer-
+ * accumulated product with a dequant epilogue
+ *     out[m][n] = acc[m][n] * perTokenScale[m] * deqScale[n].
+ *
+ * Sources (web pages, cited by title and section):
+ *   [Q4] bitorch-engine API docs, "Q4LinearFunction": forward.
+ *   [BL] LLaMA-BitNet utils.py, "Class BitLinear": forward docstring steps
+ *        1-5 and the forward body.
+ *   [PT] Ascend CANN ATB docs, "Per-token Quantization for Matmul":
+ *        Parameters, Input, Output, Example.
+ *   [CA] frankenstein-transformer docs, "Common Attention Utilities":
+ *        activation_quant, weight_quant, BitLinear.forward and
+ *        bake_ternary_weights.
+ *   [L4] docs.rs vyre-libs 0.7.2, "linear_4bit/mod.rs": module doc comment,
+ *        QuantizedLinear4BitSpec, QuantizedLinear4BitPlannerEvidence.
+ *
+ * Conventions for every entry point:
+ *   - Tensor pointers are DEVICE pointers, owned and allocated by the caller.
+ *     The library never allocates, frees or synchronizes; it keeps no mutable
+ *     global state and may be called from several threads.
+ *   - Matrices are dense row-major.  Leading dimensions of a "(..., k)"
+ *     activation are flattened into m by the caller ([CA] BitLinear.forward
+ *     takes shape (..., in_features)).
+ *   - Every tensor pointer must be 16-byte aligned ([PT] Input asks 32 bytes
+ *     for deqScale; 32 is recommended, 16 is required).
+ *   - `stream` is a hipStream_t passed as void*; NULL is the null stream.
+ *     Work is enqueued asynchronously: a kernel fault surfaces at the
+ *     caller's next synchronization, not as a return code.
+ *   - Arguments are validated on the host before any launch.  An invalid
+ *     call returns a negative ql_status and enqueues nothing.  A launch
+ *     failure returns QL_ERR_HIP.  No C++ exception crosses the boundary.
+ *   - NaN or Inf inputs give unspecified (but memory-safe) outputs.
+ */
+#ifndef QLINEAR_H
+#define QLINEAR_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define QL_ABI_VERSION 1
+/* Version of the 2-bit ternary weight layout written by qlinear_pack_ternary. */
+#define QL_TERNARY_PACK_V1 1
+/* Version of the 4-bit weight layout written by qlinear_pack_int4. */
+#define QL_INT4_PACK_V1 1
+
+typedef enum ql_status {
+    QL_OK = 0,
+    QL_ERR_NULL = -1,        /* a required pointer is NULL */
+    QL_ERR_SHAPE = -2,       /* a size is out of range or breaks a divisibility rule */
+    QL_ERR_DTYPE = -3,       /* a dtype this entry point does not accept */
+    QL_ERR_ALIGN = -4,       /* a pointer is not 16-byte aligned */
+    QL_ERR_WORKSPACE = -5,   /* workspace NULL or smaller than qlinear_workspace_bytes */
+    QL_ERR_UNSUPPORTED = -6, /* a valid but not implemented combination */
+    QL_ERR_HIP = -7          /* the HIP runtime reported an error */
+} ql_status;
+
+/* Element types.  QL_I32 as an output dtype exposes the raw int32
+ * accumulator; QL_F32 exposes the fp32 value before the final rounding. */
+typedef enum ql_dtype {
+    QL_F32 = 0,
+    QL_F16 = 1,
+    QL_BF16 = 2,
+    QL_I8 = 3,
+    QL_U8 = 4,
+    QL_I32 = 5
+} ql_dtype;
+
+/* Weight layouts: [PT] Input gives weight [k, n]; [PT] Parameters
+ * transposeB=true, and the nn.Linear weight of [BL], give [n, k]. */
+typedef enum ql_wlayout {
+    QL_W_KN = 0,
+    QL_W_NK = 1
+} ql_wlayout;
+
+/* Flags of qlinear_quant_act. */
+#define QL_RMSNORM 1u
+
+/* What qlinear_pack_int4 packs. */
+typedef enum ql_int4_what {
+    QL_INT4_WEIGHT = 0,
+    QL_INT4_ZEROS = 1
+} ql_int4_what;
+
+/* Operations that take a workspace (qlinear_workspace_bytes). */
+typedef enum ql_op {
+    QL_OP_PACK_TERNARY = 0,
+    QL_OP_GEMM_A4W4 = 1
+} ql_op;
+
+/* Returns QL_ABI_VERSION of the built library. */
+int qlinear_abi_version(void);
+
+/* Static, never-NULL description of a status code. */
+const char *qlinear_status_string(ql_status s);
+
+/* Bytes of workspace the operation needs for these sizes (0 if none).
+ *   QL_OP_PACK_TERNARY: fp64 partial sums of the absmean; m is ignored.
+ *   QL_OP_GEMM_A4W4:    int8 codes of x [m,k] then w [n,k], m*k + n*k bytes
+ *                       rounded up to 256-byte boundaries. */
+size_t qlinear_workspace_bytes(ql_op op, int64_t m, int64_t n, int64_t k);
+
+/*
+ * Per-token int8 activation quantization.
+ * [BL] forward steps 1-2 (parameter-free RMSNorm, then 8-bit per-token
+ * quantization) and step 5; [CA] activation_quant (the last dimension is
+ * scaled into [-128, 127] per token, rounded, and rescaled).
+ *
+ *   x       [m, k] QL_BF16, QL_F16 or QL_F32.
+ *   flags   0 or QL_RMSNORM.
+ *   q       [m, k] int8 out: clamp(rne(fl32(x * fl32(127 / a'))), -128, 127),
+ *           a' = max(max_k |x|, eps_q).  Codes do not depend on the RMSNorm:
+ *           it multiplies a row by r > 0 and absmax codes are invariant.
+ *   per_token_scale [m] fp32 out: a' * r / 127, r = 1/sqrt(mean(x^2) + eps_norm)
+ *           with QL_RMSNORM (computed in fp32), else r = 1 (correctly rounded).
+ *   rowsum  [m] int32 out, may be NULL: sum_k q[m, k].
+ * m, k >= 1.  Errors: QL_ERR_NULL, QL_ERR_SHAPE, QL_ERR_DTYPE, QL_ERR_ALIGN.
+ */
+ql_status qlinear_quant_act(const void *x, ql_dtype x_dtype, int64_t m, int64_t k,
+                            uint32_t flags, float eps_norm, float eps_q,
+                            int8_t *q, float *per_token_scale, int32_t *rowsum,
+                            void *stream);
+
+/*
+ * Per-tensor 4-bit quantization of [Q4] forward ("quantizes inputs and
+ * weights to 4-bits using specified scale factors"; eps avoids division by
+ * zero):  q = clamp(rne(fl32(x / max(*scale, eps))), -8, 7), stored in int8.
+ *   x      [count] QL_F16, QL_BF16 or QL_F32.
+ *   scale  device fp32 scalar.
+ * count >= 1.  Errors: QL_ERR_NULL, QL_ERR_SHAPE, QL_ERR_DTYPE, QL_ERR_ALIGN.
+ */
+ql_status qlinear_quant_int4_tensor(const void *x, ql_dtype x_dtype, int64_t count,
+                                    const float *scale, float eps, int8_t *q,
+                                    void *stream);
+
+/*
+ * Absmean ternary weight quantization and 2-bit pack (one-time, like
+ * [CA] bake_ternary_weights).  [BL] forward step 3; [CA] weight_quant.
+ *   w       fp32, [n, k] for QL_W_NK or [k, n] for QL_W_KN.
+ *   gamma'  = max(sum|w| / (n*k), eps), summed in fp64 with a fixed order.
+ *   code    = sign(w) if |w| > gamma'/2 else 0  (= clamp(rne(w/gamma'), -1, 1)).
+ *   packed  [n*k/16] u32 out, layout QL_TERNARY_PACK_V1:
+ *           blocks of 16 columns x 256 k, block (nb, kb) = 256 words from
+ *           word (nb*(k/256) + kb)*256; word 4l+t (l < 64, t < 4) holds column
+ *           16nb + l%16 and the 16 k from k0 = 256kb + 64(l/16) + 16t; element
+ *           k0 + 4a + b is at bits [8b+2a, 8b+2a+1] as code+1 in {0, 1, 2}.
+ *   gamma   device fp64 scalar out: gamma'.
+ *   workspace >= qlinear_workspace_bytes(QL_OP_PACK_TERNARY, 0, n, k).
+ * n % 16 == 0, k % 256 == 0.  Deterministic: the same input gives the same
+ * gamma' and words on every call.
+ */
+ql_status qlinear_pack_ternary(const float *w, ql_wlayout layout, int64_t n, int64_t k,
+                               double eps, uint32_t *packed, double *gamma,
+                               void *workspace, size_t ws_bytes, void *stream);
+
+/*
+ * 4-bit pack ([L4] module doc: eight nibbles per u32 word).  Only the low
+ * nibble of each input byte is used.
+ *   QL_INT4_WEIGHT: codes [rows=n, cols=k] -> packed [n*k/8] u32, layout
+ *       QL_INT4_PACK_V1: blocks of 16 columns x 128 k, block (nb, kb) = 256
+ *       words from word (nb*(k/128) + kb)*256; word 4l+t holds column
+ *       16nb + l%16 and the 8 k from k0 = 128kb + 32(l/16) + 8t; nibble p
+ *       holds k-offset 2p for p < 4 and 2(p-4)+1 for p >= 4.
+ *       Requires n % 16 == 0, k % 128 == 0.
+ *   QL_INT4_ZEROS: zero-points [rows=n, cols=groups] -> packed [groups][n/8]
+ *       u32, column c in nibble c % 8.  Requires n % 8 == 0.
+ */
+ql_status qlinear_pack_int4(const uint8_t *codes, int64_t rows, int64_t cols,
+                            ql_int4_what what, uint32_t *packed, void *stream);
+
+/*
+ * Per-token W8A8 linear ([PT] Input, Parameters, Output, Example):
+ *   out[m][n] = (sum_k x[m][k] * w[k][n]) * per_token_scale[m] * deq_scale[n]
+ * computed as an exact int32 accumulation, then fl32(fl32(acc * pts) * deq),
+ * rounded to nearest even in the output type.
+ *   x [m, k] int8; w [k, n] (QL_W_KN) or [n, k] (QL_W_NK) int8;
+ *   deq_scale [n] fp32; per_token_scale [m] fp32;
+ *   out [m, n] QL_F16 / QL_BF16, or QL_I32 for the raw accumulator (the
+ *   scale pointers may then be NULL).
+ * m, n, k >= 1 (any sizes; edge tiles are masked); k <= 131071 so the int32
+ * accumulator cannot overflow.
+ */
+ql_status qlinear_gemm_w8a8(const int8_t *x, const int8_t *w, ql_wlayout layout,
+                            const float *deq_scale, const float *per_token_scale,
+                            int64_t m, int64_t n, int64_t k, ql_dtype out_dtype, void *out,
+                            void *stream);
+
+/*
+ * BitLinear product on packed ternary weights ([BL] forward steps 4-5):
+ *   acc[m][n] = sum_k xq[m][k] * code[n][k]
+ *   out[m][n] = fl32(fl32(acc * per_token_scale[m]) * fp32(*gamma))
+ *   xq [m, k] int8 codes and rowsum [m] from qlinear_quant_act;
+ *   packed / gamma from qlinear_pack_ternary;
+ *   out [m, n] QL_BF16 / QL_F16, or QL_I32 for acc.
+ * The kernel multiplies by code+1 in {0, 1, 2} and subtracts rowsum.
+ * m <= 16 takes the split-K decode GEMV path, larger m the tiled GEMM path.
+ * n % 16 == 0, k % 256 == 0, k <= 131071.
+ */
+ql_status qlinear_gemm_w2a8(const int8_t *xq, const float *per_token_scale,
+                            const int32_t *rowsum, const uint32_t *packed,
+                            const double *gamma, int64_t m, int64_t n, int64_t k,
+                            ql_dtype out_dtype, void *out, void *stream);
+
+/*
+ * Grouped affine INT4 linear ([L4] module doc: the packed u32 weight is
+ * unpacked inside the k loop with its per-group scale and zero-point; no
+ * dequantized weight buffer is written):
+ *   out[m][n] = sum_g s[n][g] * sum_{k in g} x[m][k] * (q[n][k] - z[n][g])
+ *   x [m, k] QL_F16 (x_dtype; QL_I8 activations are not implemented and
+ *     return QL_ERR_UNSUPPORTED; per_token_scale is reserved for them);
+ *   packed_w from qlinear_pack_int4(QL_INT4_WEIGHT);
+ *   scales [n, k/group_size] fp16 (row-major, one per column and group);
+ *   packed_zeros from qlinear_pack_int4(QL_INT4_ZEROS) of z [n, groups];
+ *   bias must be NULL (not implemented);
+ *   out [m, n] QL_F16, or QL_F32 for the value before rounding.
+ * (q - z) is formed exactly in fp16, products accumulate in fp32 per group
+ * and each group's partial sum is scaled once.
+ * n % 16 == 0, k % 128 == 0, group_size % 128 == 0, k % group_size == 0.
+ */
+ql_status qlinear_gemm_w4a8_grouped(const void *x, ql_dtype x_dtype,
+                                    const float *per_token_scale,
+                                    const uint32_t *packed_w, const uint16_t *scales,
+                                    const uint32_t *packed_zeros, int64_t group_size,
+                                    int64_t m, int64_t n, int64_t k, const void *bias,
+                                    ql_dtype out_dtype, void *out, void *stream);
+
+/*
+ * A4W4 product on 4-bit codes held in int8 ([Q4] forward, second half):
+ *   out[m][n] = fl32(fl32(acc * s'_a) * s'_w),  acc = sum_k xq[m][k] * wq[n][k],
+ *   s'_a = max(*scale_a, eps), s'_w = max(*scale_w, eps) (device fp32 scalars).
+ *   xq [m, k], wq [n, k] int8 (codes in [-8, 7] from qlinear_quant_int4_tensor;
+ *   any int8 values are multiplied exactly); out QL_F16 / QL_BF16 / QL_I32.
+ * m, n, k >= 1; k <= 131071.
+ */
+ql_status qlinear_gemm_a4w4_codes(const int8_t *xq, const int8_t *wq,
+                                  const float *scale_a, const float *scale_w, float eps,
+                                  int64_t m, int64_t n, int64_t k, ql_dtype out_dtype,
+                                  void *out, void *stream);
+
+/*
+ * Q4Linear forward ([Q4] forward): quantizes x [m, k] and w [n, k] (both
+ * in_dtype: QL_F16, QL_BF16 or QL_F32) per tensor to 4 bits with
+ * qlinear_quant_int4_tensor into the workspace (xq at offset 0, wq at
+ * offset round_up(m*k, 256)), then runs qlinear_gemm_a4w4_codes.
+ * workspace >= qlinear_workspace_bytes(QL_OP_GEMM_A4W4, m, n, k); on return
+ * it holds the codes.
+ */
+ql_status qlinear_gemm_a4w4(const void *x, const void *w, ql_dtype in_dtype,
+                            const float *scale_a, const float *scale_w, float eps,
+                            int64_t m, int64_t n, int64_t k, ql_dtype out_dtype, void *out,
+                            void *workspace, size_t ws_bytes, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QLINEAR_H */

@@ -1,0 +1,54 @@
+"""Shared helpers of the GPU parity tests: tolerances and conversions.
+
+Tolerances (relative to the oracle's fp64 value y):
+  bf16 output: |gpu - y| <= 2^-7 |y| + 1e-6
+  fp16 output: |gpu - y| <= 2^-10 |y| + 1e-6
+  grouped INT4 (fp16 activations): |gpu - y| <= 1e-3 * sum_k |x_k * w_k|
+Integer results (codes, packed words, int32 accumulators) must be identical.
+"""
+import numpy as np
+import torch
+
+TOL_REL = {torch.bfloat16: 2.0 ** -7, torch.float16: 2.0 ** -10}
+TOL_ABS = 1e-6
+
+
+def to_np(t: torch.Tensor) -> np.ndarray:
+    t = t.detach().cpu()
+    if t.dtype in (torch.bfloat16, torch.float16):
+        t = t.float()
+    return t.numpy()
+
+
+def words(t: torch.Tensor) -> np.ndarray:
+    """Packed u32 words held in an int32 tensor."""
+    return t.detach().cpu().numpy().view(np.uint32)
+
+
+def assert_float_close(gpu: torch.Tensor, y: np.ndarray, what: str = "out") -> None:
+    rel = TOL_REL[gpu.dtype]
+    g = to_np(gpu).astype(np.float64)
+    assert g.shape == y.shape, (g.shape, y.shape)
+    err = np.abs(g - y)
+    tol = rel * np.abs(y) + TOL_ABS
+    bad = ~(err <= tol)  # NaN counts as bad
+    if bad.any():
+        idx = np.unravel_index(np.argmax(np.where(bad, err / tol, -1)), y.shape)
+        raise AssertionError(f"{what}: {int(bad.sum())} of {y.size} outside tolerance; worst at {idx}: "
+                             f"gpu={g[idx]!r} oracle={y[idx]!r}")
+
+
+def assert_equal(gpu, ref: np.ndarray, what: str) -> None:
+    g = gpu if isinstance(gpu, np.ndarray) else gpu.detach().cpu().numpy()
+    assert g.shape == ref.shape, (what, g.shape, ref.shape)
+    if not np.array_equal(g, ref):
+        bad = np.argwhere(g != ref)
+        i = tuple(bad[0])
+        raise AssertionError(f"{what}: {len(bad)} of {ref.size} differ; first at {i}: gpu={g[i]} oracle={ref[i]}")
+
+
+def poison(shape, dtype, device="cuda:0") -> torch.Tensor:
+    """Output buffer filled with 0xFF bytes (NaN for floats, -1 for ints) to catch unwritten elements."""
+    t = torch.empty(shape, dtype=dtype, device=device)
+    t.view(torch.uint8).fill_(0xFF)
+    return t

@@ -1,0 +1,297 @@
+"""GPU tier: every C entry point against the CPU oracle, element by element.
+
+Sizes are ones the oracle finishes in seconds while still spanning several
+kernel tiles and a ragged tail; edge cases cover the smallest shapes, k not a
+multiple of the vector width, the largest k the int32 accumulator allows, and
+the degenerate inputs of each quantizer.  Every call goes through the C ABI
+(ctypes) of libqlinear; outputs are poisoned first so an unwritten element
+fails.
+"""
+import numpy as np
+import pytest
+import torch
+
+import bit_quantized_linear_quant_amd as ql
+import oracle
+import synthetic
+from parity_util import assert_equal, assert_float_close, poison, to_np, words
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _library():
+    ql.lib()  # raises if libqlinear.so is missing: no silent fallback
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+
+
+def _cuda(t):
+    return t.to(DEV).contiguous()
+
+
+def _sync():
+    torch.cuda.synchronize()
+
+
+# ---------------------------------------------------------------------------
+# W8A8 per-token product
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("out_dtype", [torch.float16, torch.bfloat16, torch.int32])
+def test_worked_example(out_dtype):
+    ex = synthetic.worked_example()
+    out = poison((2, 3), out_dtype)
+    ql.qlinear_gemm_w8a8(_cuda(ex["x"]), _cuda(ex["w"]), ql.QL_W_KN, _cuda(ex["deq"]), _cuda(ex["pts"]),
+                         out_dtype=out_dtype, out=out)
+    _sync()
+    want = [[9, 12, 15], [19, 26, 33]] if out_dtype == torch.int32 else [[9, 24, 45], [38, 104, 198]]
+    assert to_np(out).tolist() == want
+
+
+W8A8_SHAPES = [
+    (16, 128, 256, False),     # the per-token W8A8 workload
+    (1, 1, 1, False),
+    (2, 3, 2, True),
+    (300, 270, 200, True),
+    (129, 257, 1000, False),
+    (77, 45, 77, True),        # k not a multiple of 16: byte loads
+    (33, 50, 77, False),
+    (256, 256, 64, True),
+    (130, 131, 4096, True),
+]
+
+
+@pytest.mark.parametrize("m,n,k,nk", W8A8_SHAPES)
+def test_w8a8_parity(m, n, k, nk):
+    d = synthetic.w8a8(m, n, k, nk, seed=100 + m + n + k)
+    x, w, deq, pts = (d[key] for key in ("x", "w", "deq", "pts"))
+    acc, y = oracle.w8a8(x.numpy(), w.numpy(), nk, pts.numpy(), deq.numpy())
+    layout = ql.QL_W_NK if nk else ql.QL_W_KN
+    xg, wg, dg, pg = _cuda(x), _cuda(w), _cuda(deq), _cuda(pts)
+    oi = poison((m, n), torch.int32)
+    ql.qlinear_gemm_w8a8(xg, wg, layout, None, None, out_dtype=torch.int32, out=oi)
+    for dt in (torch.float16, torch.bfloat16):
+        o = poison((m, n), dt)
+        ql.qlinear_gemm_w8a8(xg, wg, layout, dg, pg, out_dtype=dt, out=o)
+        _sync()
+        assert_float_close(o, y, f"w8a8 {dt}")
+    assert_equal(oi, acc, "w8a8 int32 accumulator")
+
+
+def test_w8a8_max_k_extremes():
+    """k = 131071 with every operand -128: the largest accumulator the ABI allows."""
+    m, n, k = 3, 5, 131071
+    x = torch.full((m, k), -128, dtype=torch.int8)
+    w = torch.full((n, k), -128, dtype=torch.int8)
+    w[1, ::2] = 127
+    acc = oracle.gemm_i8(x.numpy(), w.numpy(), True)
+    assert int(acc[0, 0]) == 128 * 128 * k
+    o = poison((m, n), torch.int32)
+    ql.qlinear_gemm_w8a8(_cuda(x), _cuda(w), ql.QL_W_NK, None, None, out_dtype=torch.int32, out=o)
+    _sync()
+    assert_equal(o, acc, "w8a8 max-k accumulator")
+
+
+def test_w8a8_deterministic():
+    d = synthetic.w8a8(200, 300, 512, True, seed=5)
+    args = [_cuda(d[key]) for key in ("x", "w")]
+    o1 = ql.qlinear_gemm_w8a8(*args, ql.QL_W_NK, _cuda(d["deq"]), _cuda(d["pts"]))
+    o2 = ql.qlinear_gemm_w8a8(*args, ql.QL_W_NK, _cuda(d["deq"]), _cuda(d["pts"]))
+    _sync()
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
+
+
+# ---------------------------------------------------------------------------
+# Per-token activation quantization
+# ---------------------------------------------------------------------------
+QUANT_SHAPES = [(1, 8192), (16, 8192), (7, 4097), (33, 77), (5, 1), (3, 20000), (64, 4096), (2, 8)]
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16, torch.float32])
+@pytest.mark.parametrize("rms", [False, True])
+@pytest.mark.parametrize("m,k", QUANT_SHAPES)
+def test_quant_act_parity(dtype, rms, m, k):
+    x = synthetic.activations(m, k, seed=200 + m * 7 + k, outliers=0.01, dtype=dtype)
+    q_ref, pts_ref, rs_ref = oracle.quant_act(x.float().numpy(), rmsnorm=rms, eps_norm=1e-6, eps_q=1e-5)
+    q = poison((m, k), torch.int8)
+    pts = poison((m,), torch.float32)
+    rs = poison((m,), torch.int32)
+    ql.qlinear_quant_act(_cuda(x), rmsnorm=rms, eps_norm=1e-6, eps_q=1e-5, q=q, per_token_scale=pts,
+                         rowsum=rs)
+    _sync()
+    assert_equal(q, q_ref, "codes")
+    assert_equal(rs, rs_ref, "rowsum")
+    if rms:
+        np.testing.assert_allclose(to_np(pts), pts_ref, rtol=1e-5)
+    else:
+        assert_equal(pts, pts_ref, "per-token scale")
+
+
+def test_quant_act_degenerate_rows():
+    x = torch.zeros(4, 300, dtype=torch.bfloat16)
+    x[1, 17] = -3.5
+    x[2, :] = 2.0
+    x[3, 5] = 1e-30  # below eps_q: scale guarded
+    q_ref, pts_ref, rs_ref = oracle.quant_act(x.float().numpy())
+    q, pts, rs = ql.qlinear_quant_act(_cuda(x))
+    _sync()
+    assert_equal(q, q_ref, "codes")
+    assert_equal(pts, pts_ref, "pts")
+    assert_equal(rs, rs_ref, "rowsum")
+
+
+@pytest.mark.parametrize("dtype", [torch.float16, torch.bfloat16, torch.float32])
+@pytest.mark.parametrize("count", [1, 7, 8, 1000, 65537])
+@pytest.mark.parametrize("scale_mul", [1.0, 0.25, 0.0])
+def test_quant_int4_tensor_parity(dtype, count, scale_mul):
+    x = synthetic.activations(1, count, seed=300 + count, dtype=dtype).reshape(count)
+    scale = float(np.float32(x.abs().max().float().item()) / np.float32(7.0)) * scale_mul
+    ref = oracle.quant_int4_tensor(x.float().numpy(), scale, 1e-5)
+    q = poison((count,), torch.int8)
+    ql.qlinear_quant_int4_tensor(_cuda(x), torch.tensor([scale], dtype=torch.float32, device=DEV), 1e-5, q=q)
+    _sync()
+    assert_equal(q, ref, "int4 codes")
+
+
+# ---------------------------------------------------------------------------
+# Packs
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("n,k", [(16, 256), (48, 768), (400, 512)])
+@pytest.mark.parametrize("nk", [True, False])
+def test_pack_ternary_parity(n, k, nk):
+    w = synthetic.master_weight(n, k, seed=400 + n + k)
+    wl = w if nk else w.t().contiguous()
+    codes, gamma = oracle.ternary_quant(wl.numpy(), layout_nk=nk)
+    assert oracle.ternary_tie_band(w.numpy(), gamma) == 0
+    ref = oracle.pack_ternary(codes)
+    layout = ql.QL_W_NK if nk else ql.QL_W_KN
+    packed = poison((n * k // 16,), torch.int32)
+    wg = _cuda(wl)
+    p1, g1 = ql.qlinear_pack_ternary(wg, layout, packed=packed)
+    p2, g2 = ql.qlinear_pack_ternary(wg, layout)
+    _sync()
+    assert_equal(words(p1), ref, "ternary words")
+    assert abs(g1.item() - gamma) <= 1e-12 * gamma
+    assert torch.equal(p1, p2) and torch.equal(g1.view(torch.int64), g2.view(torch.int64))
+
+
+def test_pack_ternary_eps_guard():
+    w = torch.zeros(32, 256)
+    packed, g = ql.qlinear_pack_ternary(_cuda(w), ql.QL_W_NK, eps=1e-5)
+    _sync()
+    assert g.item() == 1e-5
+    assert_equal(words(packed), oracle.pack_ternary(np.zeros((32, 256), np.int8)), "zero weight words")
+
+
+@pytest.mark.parametrize("n,k", [(16, 128), (48, 384), (400, 512)])
+def test_pack_int4_parity(n, k):
+    d = synthetic.grouped_int4(1, n, k, 128, seed=500 + n)
+    q = d["q"] | torch.randint(0, 16, d["q"].shape, dtype=torch.uint8) * 16  # high nibbles are ignored
+    ref = oracle.pack_int4(q.numpy())
+    out = poison((n * k // 8,), torch.int32)
+    ql.qlinear_pack_int4(_cuda(q), ql.QL_INT4_WEIGHT, packed=out)
+    zref = oracle.pack_int4_zeros(d["z"].numpy())
+    zout = ql.qlinear_pack_int4(_cuda(d["z"]), ql.QL_INT4_ZEROS)
+    _sync()
+    assert_equal(words(out), ref, "int4 weight words")
+    assert_equal(words(zout), zref, "int4 zero words")
+
+
+# ---------------------------------------------------------------------------
+# BitLinear: quant_act -> pack_ternary -> w2a8
+# ---------------------------------------------------------------------------
+W2A8_SHAPES = [(1, 400, 512), (2, 256, 768), (4, 400, 512), (5, 64, 256), (16, 400, 768), (17, 400, 512),
+               (130, 256, 768), (300, 400, 512)]
+
+
+@pytest.mark.parametrize("m,n,k", W2A8_SHAPES)
+def test_w2a8_parity(m, n, k):
+    d = synthetic.bitlinear(m, n, k, seed=600 + m + n)
+    x, w = d["x"], d["w"]
+    xq_ref, pts_ref, rs_ref = oracle.quant_act(x.float().numpy(), rmsnorm=True)
+    codes, gamma = oracle.ternary_quant(w.numpy())
+    acc_ref, y_ref = oracle.w2a8(xq_ref, pts_ref, codes, gamma)
+    xq, pts, rs = ql.qlinear_quant_act(_cuda(x), rmsnorm=True)
+    packed, g = ql.qlinear_pack_ternary(_cuda(w), ql.QL_W_NK)
+    oi = poison((m, n), torch.int32)
+    ql.qlinear_gemm_w2a8(xq, pts, rs, packed, g, n, out_dtype=torch.int32, out=oi)
+    ob = poison((m, n), torch.bfloat16)
+    ql.qlinear_gemm_w2a8(xq, pts, rs, packed, g, n, out_dtype=torch.bfloat16, out=ob)
+    of = poison((m, n), torch.float16)
+    ql.qlinear_gemm_w2a8(xq, pts, rs, packed, g, n, out_dtype=torch.float16, out=of)
+    _sync()
+    assert_equal(xq, xq_ref, "activation codes")
+    assert_equal(words(packed), oracle.pack_ternary(codes), "ternary words")
+    assert_equal(oi, acc_ref, "w2a8 accumulator")
+    assert_float_close(ob, y_ref, "w2a8 bf16")
+    assert_float_close(of, y_ref, "w2a8 fp16")
+
+
+def test_w2a8_gemv_deterministic():
+    d = synthetic.bitlinear(16, 512, 1024, seed=7)
+    xq, pts, rs = ql.qlinear_quant_act(_cuda(d["x"]), rmsnorm=True)
+    packed, g = ql.qlinear_pack_ternary(_cuda(d["w"]), ql.QL_W_NK)
+    a = ql.qlinear_gemm_w2a8(xq, pts, rs, packed, g, 512)
+    b = ql.qlinear_gemm_w2a8(xq, pts, rs, packed, g, 512)
+    _sync()
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+# ---------------------------------------------------------------------------
+# Grouped affine INT4
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("m,n,k,g", [(1, 48, 256, 128), (5, 400, 512, 128), (32, 400, 512, 256),
+                                     (40, 64, 384, 128), (32, 16, 128, 128), (3, 32, 1024, 1024)])
+def test_grouped_int4_parity(m, n, k, g):
+    d = synthetic.grouped_int4(m, n, k, g, seed=700 + m + n + k)
+    x, q, s, z = d["x"], d["q"], d["s"], d["z"]
+    y, bound = oracle.grouped_int4(x.float().numpy(), q.numpy(), s.float().numpy(), z.numpy(), g)
+    pw = ql.qlinear_pack_int4(_cuda(q), ql.QL_INT4_WEIGHT)
+    pz = ql.qlinear_pack_int4(_cuda(z), ql.QL_INT4_ZEROS)
+    o32 = poison((m, n), torch.float32)
+    ql.qlinear_gemm_w4a8_grouped(_cuda(x), pw, _cuda(s), pz, g, n, out_dtype=torch.float32, out=o32)
+    o16 = poison((m, n), torch.float16)
+    ql.qlinear_gemm_w4a8_grouped(_cuda(x), pw, _cuda(s), pz, g, n, out_dtype=torch.float16, out=o16)
+    _sync()
+    for o, name in ((o32, "fp32"), (o16, "fp16")):
+        err = np.abs(to_np(o).astype(np.float64) - y)
+        assert np.all(err <= 1e-3 * bound), f"grouped {name}: max err/bound {np.max(err / bound)}"
+    # the fp16 output is the fp32 output rounded once to nearest even
+    assert torch.equal(o16, o32.to(torch.float16))
+
+
+def test_grouped_int4_zero_point_equals_code_gives_zero():
+    m, n, k, g = 4, 32, 256, 128
+    d = synthetic.grouped_int4(m, n, k, g, seed=9)
+    z = d["z"]
+    q = torch.repeat_interleave(z, g, dim=1).contiguous()
+    pw = ql.qlinear_pack_int4(_cuda(q), ql.QL_INT4_WEIGHT)
+    pz = ql.qlinear_pack_int4(_cuda(z), ql.QL_INT4_ZEROS)
+    o = ql.qlinear_gemm_w4a8_grouped(_cuda(d["x"]), pw, _cuda(d["s"]), pz, g, n, out_dtype=torch.float32)
+    _sync()
+    assert torch.count_nonzero(o).item() == 0
+
+
+# ---------------------------------------------------------------------------
+# A4W4
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("m,n,k", [(33, 20, 130), (256, 256, 512), (129, 65, 1000), (1, 1, 1)])
+@pytest.mark.parametrize("scale_mul", [1.0, 0.25])
+def test_a4w4_parity(m, n, k, scale_mul):
+    d = synthetic.a4w4(m, n, k, seed=800 + m + n + k)
+    sa, sw = d["scale_a"] * scale_mul, d["scale_w"] * scale_mul
+    qa, qw, acc, y = oracle.a4w4(d["x"].float().numpy(), d["w"].float().numpy(), sa, sw, d["eps"])
+    sag = torch.tensor([sa], dtype=torch.float32, device=DEV)
+    swg = torch.tensor([sw], dtype=torch.float32, device=DEV)
+    out = poison((m, n), torch.float16)
+    out, ws = ql.qlinear_gemm_a4w4(_cuda(d["x"]), _cuda(d["w"]), sag, swg, d["eps"], out=out)
+    xq, wq = ql.a4w4_codes_from_workspace(ws, m, n, k)
+    oi = poison((m, n), torch.int32)
+    ql.qlinear_gemm_a4w4_codes(xq, wq, sag, swg, d["eps"], out_dtype=torch.int32, out=oi)
+    ob = ql.qlinear_gemm_a4w4_codes(xq, wq, sag, swg, d["eps"], out_dtype=torch.bfloat16)
+    _sync()
+    assert_equal(xq, qa, "x codes")
+    assert_equal(wq, qw, "w codes")
+    assert_equal(oi, acc, "a4w4 accumulator")
+    assert_float_close(out, y, "a4w4 fp16")
+    assert_float_close(ob, y, "a4w4 bf16")
