@@ -1,0 +1,243 @@
+"""Benchmark of the quantized linear layer on one MI355X.
+
+Step: one Q4Linear (A4W4) forward on the 8192^3 workload -- per-tensor 4-bit
+quantization of x[8192,8192] and w[8192,8192] (fp16), then the int8 matrix-
+core product with the fused fp16 epilogue -- the large-M GEMM that the
+metric's int8 TOPS figure is quoted on.  Inputs are resident in HBM before the
+timed region; W untimed warm-up steps precede exactly K timed steps bracketed
+by device synchronization.
+
+The same JSON line carries:
+  roofline      the int8 GEMM kernel: algorithmic ops per launch / its mean
+                duration from HIP events recorded around it in the timed
+                region, against the 5.0 POP/s dense int8 peak; `traffic` is
+                the HBM bytes per launch measured by rocprofv3 counters for
+                the current kernel source, else null.
+  cpu_baseline  the CPU oracle timed on this host on a bounded row sample of
+                the same forward, scaled to TOPS.
+  decode_gemv   the metric's second figure: packed-ternary-weight HBM GB/s of
+                the M<=16 decode GEMV (K=8192, N=28672) for M in {1,4,16},
+                with the packed weight rotated over copies larger than the
+                256 MB last-level cache, launches replayed from a HIP graph.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "int8 TOPS (large-M GEMM) + packed-weight HBM GB/s (M≤16 GEMV), % roofline"
+PEAK_INT8_TOPS = 5000.0      # MI355X dense int8 MFMA, 5.0 POP/s
+PEAK_HBM_GBS = 8000.0        # MI355X HBM3E, 8 TB/s
+GEMM_KERNEL_SOURCES = ["gemm_i8.hip", "ql_device.hpp"]
+GEMV_KERNEL_SOURCES = ["gemm_w2a8.hip", "ql_device.hpp"]
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.txt")
+
+
+def kernel_source_hash(files) -> str:
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(ROOT, "bit_quantized_linear_quant_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def recorded_traffic(name: str, src_hash: str):
+    """HBM bytes per launch measured by rocprofv3 for this kernel source, else None."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    with open(TRAFFIC_FILE) as f:
+        for line in f:
+            parts = dict(p.split("=", 1) for p in line.split() if "=" in p)
+            if parts.get("kernel") == name and parts.get("src") == src_hash:
+                return int(parts["fetch_bytes"]) + int(parts["write_bytes"])
+    return None
+
+
+def cpu_baseline(d, target_s: float = 12.0):
+    """The CPU oracle on a row sample of the same forward, scaled to TOPS."""
+    import numpy as np
+    import oracle
+
+    x = d["x"].float().numpy()
+    w = d["w"].float().numpy()
+    m, k = x.shape
+    n = w.shape[0]
+    threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+
+    def run(rows):
+        t0 = time.perf_counter()
+        qa = oracle.quant_int4_tensor(x[:rows], d["scale_a"], d["eps"])
+        qw = oracle.quant_int4_tensor(w, d["scale_w"], d["eps"])
+        acc = oracle.gemm_i8(qa, qw, True)
+        sa = float(oracle.effective_scale(d["scale_a"], d["eps"]))
+        sw = float(oracle.effective_scale(d["scale_w"], d["eps"]))
+        y = acc.astype(np.float64) * sa * sw
+        oracle.round_f16(y)
+        return time.perf_counter() - t0
+
+    # calibrate: a fixed part (quantizing all of w) plus a per-row part
+    t8, t24 = run(8), run(24)
+    per_row = max((t24 - t8) / 16, 1e-6)
+    fixed = max(t8 - 8 * per_row, 0.0)
+    rows = int(min(m, max(8, (target_s - fixed) / per_row)))
+    rows = max(8, rows // 8 * 8)
+    t = run(rows)
+    return {"value": 2.0 * rows * n * k / t / 1e12, "unit": "TOPS", "cores": threads, "kind": "oracle",
+            "sample": f"{rows} of {m} token rows of the A4W4 forward (x-row and full-w 4-bit quantization, "
+                      f"integer product over k={k} for all n={n} columns, fp64 dequant, fp16 rounding); "
+                      f"{t:.1f} s on {threads} threads"}
+
+
+def bench_a4w4(args, ql, torch, synthetic):
+    dev = "cuda:0"
+    m = n = k = 8192
+    d = synthetic.a4w4(m, n, k, seed=1005)
+    x = d["x"].to(dev)
+    w = d["w"].to(dev)
+    sa = torch.tensor([d["scale_a"]], dtype=torch.float32, device=dev)
+    sw = torch.tensor([d["scale_w"]], dtype=torch.float32, device=dev)
+    eps = d["eps"]
+    out = torch.empty((m, n), dtype=torch.float16, device=dev)
+    ws = torch.empty((ql.qlinear_workspace_bytes(ql.QL_OP_GEMM_A4W4, m, n, k),), dtype=torch.uint8, device=dev)
+    xq, wq = ql.a4w4_codes_from_workspace(ws, m, n, k)
+
+    # A plain device copy of known size: the byte counters' calibration kernel.
+    cal_src = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
+    cal_dst = torch.empty_like(cal_src)
+    cal_dst.copy_(cal_src)
+
+    def step(ev=None):
+        # the three launches of qlinear_gemm_a4w4, with events between them
+        if ev is not None:
+            ev[0].record()
+        ql.qlinear_quant_int4_tensor(x.view(-1), sa, eps, q=xq.view(-1))
+        if ev is not None:
+            ev[1].record()
+        ql.qlinear_quant_int4_tensor(w.view(-1), sw, eps, q=wq.view(-1))
+        if ev is not None:
+            ev[2].record()
+        ql.qlinear_gemm_a4w4_codes(xq, wq, sa, sw, eps, out_dtype=torch.float16, out=out)
+        if ev is not None:
+            ev[3].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    qx = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps
+    qw = sum(e[1].elapsed_time(e[2]) for e in evs) / args.steps
+    gm = sum(e[2].elapsed_time(e[3]) for e in evs) / args.steps
+    ops = 2.0 * m * n * k
+    ms_per_step = wall * 1e3 / args.steps
+    res = {"m": m, "n": n, "k": k, "ops": ops, "ms_per_step": ms_per_step,
+           "value": ops / (ms_per_step * 1e-3) / 1e12,
+           "kernel_ms": {"quant_x": qx, "quant_w": qw, "gemm": gm}, "gemm_tops": ops / (gm * 1e-3) / 1e12}
+    return res, d
+
+
+def bench_decode(ql, torch, synthetic, reps: int = 10):
+    """Packed-weight GB/s of the M<=16 decode GEMV, weights rotated past the last-level cache."""
+    dev = "cuda:0"
+    n, k = 28672, 8192
+    dd = synthetic.decode((1, 4, 16), n, k, seed=1003)
+    packed, gamma = ql.qlinear_pack_ternary(dd["w"].to(dev), ql.QL_W_NK)
+    copies = [packed] + [packed.clone() for _ in range(5)]     # 6 x 58.7 MB > 256 MB cache
+    packed_bytes = n * k // 4
+    res = {}
+    for m, x in dd["x"].items():
+        xq, pts, rs = ql.qlinear_quant_act(x.to(dev), rmsnorm=True)
+        out = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
+        launches = 4 * len(copies)
+        for c in copies:   # warm-up outside capture
+            ql.qlinear_gemm_w2a8(xq, pts, rs, c, gamma, n, out=out)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(launches):
+                ql.qlinear_gemm_w2a8(xq, pts, rs, copies[i % len(copies)], gamma, n, out=out)
+        g.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / (reps * launches)
+        gbs = packed_bytes / (us * 1e-6) / 1e9
+        res[str(m)] = {"us_per_launch": round(us, 3), "packed_weight_GBps": round(gbs, 1),
+                       "frac_hbm": round(gbs / PEAK_HBM_GBS, 4)}
+        del g
+    return {"unit": "GB/s", "n": n, "k": k, "packed_weight_bytes": packed_bytes,
+            "timing": "per launch, mean over HIP-graph replays of 24 back-to-back launches rotating 6 "
+                      "copies of the packed weight (352 MB)",
+            "by_m": res}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import bit_quantized_linear_quant_amd as ql
+    import synthetic
+
+    ql.lib()
+    res, d = bench_a4w4(args, ql, torch, synthetic)
+    gemv = bench_decode(ql, torch, synthetic)
+    gemm_src = kernel_source_hash(GEMM_KERNEL_SOURCES)
+    traffic = recorded_traffic("gemm_i8_a4w4_8192", gemm_src)
+    achieved = res["gemm_tops"]
+    line = {
+        "metric": METRIC,
+        "value": round(res["value"], 2),
+        "unit": "TOPS",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(res["ms_per_step"], 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int8",
+        "data": "synthetic",
+        "config": {"workload": "A4W4 Q4Linear forward: fp16 x[8192,8192] N(0,1), fp16 w[8192,8192] "
+                               "N(0,0.02^2), per-tensor scales max|t|/7, eps 1e-5, 4-bit codes in int8, "
+                               "int8 MFMA product, fp16 out",
+                   "m": res["m"], "n": res["n"], "k": res["k"], "global_batch": res["m"],
+                   "parallelism": "single GPU"},
+        "kernel_ms": {key: round(v, 4) for key, v in res["kernel_ms"].items()},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_INT8_TOPS, "unit": "TOPS",
+                     "frac": round(achieved / PEAK_INT8_TOPS, 4), "traffic": traffic,
+                     "kernel": "gemm_i8_kernel (qlinear_gemm_a4w4_codes)",
+                     "work_per_launch": f"2*m*n*k = {int(res['ops'])} int8 ops"},
+        "decode_gemv": gemv,
+    }
+    torch.cuda.synchronize()
+    line["cpu_baseline"] = cpu_baseline(d)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()
