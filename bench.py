@@ -230,7 +230,7 @@ def main():
         "kernel_ms": {key: round(v, 4) for key, v in res["kernel_ms"].items()},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_INT8_TOPS, "unit": "TOPS",
                      "frac": round(achieved / PEAK_INT8_TOPS, 4), "traffic": traffic,
-                     "kernel": "gemm_i8_kernel (qlinear_gemm_a4w4_codes)",
+                     "kernel": "gemm_i8_big_kernel (qlinear_gemm_a4w4_codes)",
                      "work_per_launch": f"2*m*n*k = {int(res['ops'])} int8 ops"},
         "decode_gemv": gemv,
     }

@@ -2,20 +2,27 @@
 // epilogue fused ("Per-token Quantization for Matmul": Input, Output and
 // Example; "Q4LinearFunction" forward for the per-tensor scale pair).
 //
-// Tiling: a 256-thread workgroup computes a 128 x 128 output tile as a 2 x 2
-// grid of waves, each wave a 64 x 64 sub-tile of 4 x 4
-// v_mfma_i32_16x16x64_i8 blocks (64 int32 accumulators per lane).  Each
-// 64-byte k-step stages the A (activation rows) and B (weight columns) tiles
-// in LDS with k contiguous; rows are padded to 80 bytes so the 16-byte
-// fragment reads of 16 consecutive rows fall in distinct bank groups.  The
-// next k-step's tiles are prefetched into registers while the matrix cores
-// work on the current one.
+// Two kernels share the epilogue:
 //
-// Weights stored [k][n] (the layout of the worked example) are transposed in
-// registers, 4 k x 4 n bytes at a time, on their way into LDS.
-// Edge tiles in m, n and k are zero-filled on load and masked on store, so
-// any m, n, k >= 1 works; the 16-byte vector loads need k % 16 == 0 (rows of
-// [n][k] and [m][k] operands) and fall back to byte loads otherwise.
+// gemm_i8_big_kernel -- large products with [n][k] weights and k % 128 == 0
+//   (the 8192^3 A4W4 product).  A 256-thread workgroup owns a 256 x 256
+//   output tile, each wave a 128 x 128 quarter held as 4 x 4 blocks of
+//   v_mfma_i32_32x32x32_i8 (256 int32 accumulators per lane, one wave per
+//   SIMD).  A and B k-slices move from HBM straight into LDS with
+//   global_load_lds_dwordx4 (no register staging), double-buffered so the
+//   next slice streams in while the matrix cores consume the current one;
+//   one barrier per slice.  In LDS each 16-byte chunk c of row r sits at
+//   chunk position c ^ swz(r), which puts the 16 rows read together by a
+//   fragment load in distinct bank groups.  Tiles are ordered so that each
+//   XCD (workgroup id mod 8) walks its own band of tile rows, four rows at a
+//   time, so concurrently running tiles share A and B slices in that XCD's
+//   L2.  Rows past m or n are loaded clamped and never stored.
+//
+// gemm_i8_kernel -- everything else (any m, n, k >= 1, weights [k][n] or
+//   [n][k]): 128 x 128 tiles, 2 x 2 waves of 64 x 64 in 16x16x64 MFMA blocks,
+//   register-staged loads with zero fill at the edges, LDS rows padded to
+//   80 bytes; [k][n] weights are transposed 4 x 4 bytes at a time in
+//   registers on their way into LDS.
 #include "ql_device.hpp"
 #include "ql_launch.hpp"
 
@@ -23,11 +30,9 @@ namespace ql {
 
 namespace {
 
-constexpr int BM = 128, BN = 128, BK = 64;
-constexpr int kLdsRow = BK + 16;  // padded row stride in bytes
-constexpr int kThreads = 256;
-constexpr int WM = 64, WN = 64;   // wave sub-tile
-constexpr int TM = WM / 16, TN = WN / 16;
+typedef int v16i __attribute__((ext_vector_type(16)));
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(1))) void glb_void;
 
 struct Params {
     const int8_t *x;
@@ -40,6 +45,193 @@ struct Params {
     int64_t m, n, k;
     void *out;
 };
+
+// Per-row and per-column epilogue factors: (acc * row) * col, rounded once
+// per multiply in fp32, then to the output type.
+template <int EPI, int OUT>
+struct Epilogue {
+    float sa = 0.f, sw = 0.f;
+    __device__ __forceinline__ void init(const Params &p) {
+        if (EPI == EPI_SCALARS && OUT != OUT_I32) {
+            const float a = *p.sa, w = *p.sw;
+            sa = a > p.eps ? a : p.eps;
+            sw = w > p.eps ? w : p.eps;
+        }
+    }
+    __device__ __forceinline__ float col_factor(const Params &p, int64_t col) const {
+        if (OUT == OUT_I32) return 0.f;
+        return EPI == EPI_ROWCOL ? p.deq[col] : sw;
+    }
+    __device__ __forceinline__ float row_factor(const Params &p, int64_t row) const {
+        if (OUT == OUT_I32) return 0.f;
+        return EPI == EPI_ROWCOL ? p.pts[row] : sa;
+    }
+    __device__ __forceinline__ void store(const Params &p, int64_t row, int64_t col, int32_t v, float rf,
+                                          float cf) const {
+        const int64_t idx = row * p.n + col;
+        if (OUT == OUT_I32) static_cast<int32_t *>(p.out)[idx] = v;
+        else store_out<OUT>(p.out, idx, __fmul_rn(__fmul_rn((float)v, rf), cf));
+    }
+};
+
+// ---------------------------------------------------------------------------
+// Large-tile kernel
+// ---------------------------------------------------------------------------
+constexpr int LB = 256;        // tile rows and columns
+constexpr int LThreads = 256;
+constexpr int kGroupM = 4;     // tile rows walked together per XCD
+
+template <int CH>
+__device__ __forceinline__ int swz(int r) {
+    if constexpr (CH == 4) return ((r >> 1) ^ (r >> 2)) & 3;
+    else return (r & 7) ^ ((r >> 3) & 3);
+}
+
+// Workgroup id -> (tile row, tile column).  Hardware hands consecutive ids to
+// the 8 XCDs in turn; ids are first regrouped so each XCD receives a
+// contiguous range of tiles, then each range is walked kGroupM tile rows at a
+// time, column by column.
+__device__ __forceinline__ void tile_of(int b, int tiles_m, int tiles_n, int &tm, int &tn) {
+    const int total = tiles_m * tiles_n;
+    int t = b;
+    if (total % 8 == 0) t = (b % 8) * (total / 8) + b / 8;
+    const int group = t / (kGroupM * tiles_n);
+    const int first = group * kGroupM;
+    const int rows = min(tiles_m - first, kGroupM);
+    const int within = t - group * kGroupM * tiles_n;
+    tm = first + within % rows;
+    tn = within / rows;
+}
+
+template <int BK, int EPI, int OUT>
+__global__ __launch_bounds__(LThreads, 1) void gemm_i8_big_kernel(Params p, int tiles_m, int tiles_n) {
+    constexpr int CH = BK / 16;                 // 16-byte chunks per LDS row
+    constexpr int TILE = LB * BK;               // bytes of one A or B slice
+    constexpr int PER_WAVE = TILE / 1024 / 4;   // 1 KB direct loads per wave per slice and operand
+    constexpr int S = BK / 32;                  // 32-k MFMA steps per slice
+    static_assert(S % 2 == 0, "fragment double buffer assumes an even step count");
+    __shared__ __attribute__((aligned(1024))) int8_t smem[2 * 2 * TILE];
+
+    const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+    const int wm = wave / 2, wn = wave % 2;
+    int tm, tn;
+    tile_of(blockIdx.x, tiles_m, tiles_n, tm, tn);
+    const int64_t m0 = (int64_t)tm * LB, n0 = (int64_t)tn * LB;
+    const int64_t K = p.k;
+    const int64_t nk = K / BK;
+
+    // Global source of each direct load issued by this lane.
+    const int8_t *srcA[PER_WAVE];
+    const int8_t *srcB[PER_WAVE];
+#pragma unroll
+    for (int ii = 0; ii < PER_WAVE; ii++) {
+        const int pos = 64 * (wave * PER_WAVE + ii) + lane;   // chunk position in the slice
+        const int row = pos / CH;
+        const int c = (pos % CH) ^ swz<CH>(row);
+        const int64_t ra = min(m0 + row, p.m - 1), rb = min(n0 + row, p.n - 1);
+        srcA[ii] = p.x + ra * K + 16 * c;
+        srcB[ii] = p.w + rb * K + 16 * c;
+    }
+    auto issue = [&](int buf, int64_t k0) {
+        int8_t *As = smem + buf * 2 * TILE;
+        int8_t *Bs = As + TILE;
+#pragma unroll
+        for (int ii = 0; ii < PER_WAVE; ii++) {
+            const int inst = wave * PER_WAVE + ii;
+            __builtin_amdgcn_global_load_lds((glb_void *)(srcA[ii] + k0), (lds_void *)(As + 1024 * inst), 16, 0, 0);
+            __builtin_amdgcn_global_load_lds((glb_void *)(srcB[ii] + k0), (lds_void *)(Bs + 1024 * inst), 16, 0, 0);
+        }
+    };
+
+    // LDS byte offsets of this lane's fragments: block row 32i + lane%32,
+    // chunk 2s + lane/32.  swz depends only on the low 5 row bits, so the
+    // offset of block i is that of block 0 plus 32 rows.
+    const int fr = lane % 32;
+    int offA[S], offB[S];
+#pragma unroll
+    for (int s = 0; s < S; s++) {
+        const int c = 2 * s + lane / 32;
+        const int ra = wm * 128 + fr, rb = wn * 128 + fr;
+        offA[s] = 16 * (CH * ra + (c ^ swz<CH>(ra)));
+        offB[s] = 16 * (CH * rb + (c ^ swz<CH>(rb)));
+    }
+    auto frags = [&](v4i (&a)[4], v4i (&b)[4], const int8_t *As, int s) {
+        const int8_t *Bs = As + TILE;
+#pragma unroll
+        for (int i = 0; i < 4; i++) a[i] = *reinterpret_cast<const v4i *>(As + offA[s] + i * 32 * CH * 16);
+#pragma unroll
+        for (int j = 0; j < 4; j++) b[j] = *reinterpret_cast<const v4i *>(Bs + offB[s] + j * 32 * CH * 16);
+    };
+
+    v16i acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; i++)
+#pragma unroll
+        for (int j = 0; j < 4; j++) acc[i][j] = v16i{};
+
+    v4i fa[2][4], fb[2][4];
+    issue(0, 0);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    frags(fa[0], fb[0], smem, 0);
+    for (int64_t kt = 0; kt < nk; kt++) {
+        const int cur = (int)(kt & 1);
+        const int8_t *As = smem + cur * 2 * TILE;
+        // Next slice (the last step reloads its own slice into the idle
+        // buffer, keeping the loop body free of branches).
+        issue(cur ^ 1, min(kt + 1, nk - 1) * BK);
+#pragma unroll
+        for (int s = 0; s < S; s++) {
+            if (s + 1 < S) frags(fa[(s + 1) & 1], fb[(s + 1) & 1], As, s + 1);
+#pragma unroll
+            for (int i = 0; i < 4; i++)
+#pragma unroll
+                for (int j = 0; j < 4; j++)
+                    acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fa[s & 1][i], fb[s & 1][j], acc[i][j], 0, 0, 0);
+            // Matrix-core issue interleaved with the next fragments' LDS reads
+            // (and, in the first step, with the next slice's direct loads).
+            if (s + 1 < S) {
+#pragma unroll
+                for (int q = 0; q < 8; q++) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                    if (s == 0) __builtin_amdgcn_sched_group_barrier(0x010, 2 * PER_WAVE / 8, 0);
+                }
+                __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+            }
+        }
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        frags(fa[0], fb[0], smem + (cur ^ 1) * 2 * TILE, 0);
+    }
+
+    // Epilogue: lane holds column lane%32 of each 32x32 block and rows
+    // 8*(r/4) + 4*(lane/32) + r%4 of register r.
+    Epilogue<EPI, OUT> ep;
+    ep.init(p);
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+        const int64_t col = n0 + wn * 128 + 32 * j + fr;
+        if (col >= p.n) continue;
+        const float cf = ep.col_factor(p, col);
+#pragma unroll
+        for (int i = 0; i < 4; i++)
+#pragma unroll
+            for (int r = 0; r < 16; r++) {
+                const int64_t row = m0 + wm * 128 + 32 * i + 8 * (r / 4) + 4 * (lane / 32) + (r % 4);
+                if (row < p.m) ep.store(p, row, col, acc[i][j][r], ep.row_factor(p, row), cf);
+            }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// General kernel
+// ---------------------------------------------------------------------------
+constexpr int BM = 128, BN = 128, BK = 64;
+constexpr int kLdsRow = BK + 16;  // padded row stride in bytes
+constexpr int kThreads = 256;
+constexpr int WM = 64, WN = 64;   // wave sub-tile
+constexpr int TM = WM / 16, TN = WN / 16;
 
 // 16 bytes of row `row` of a [rows][k] int8 matrix at column kk, zero-filled
 // outside [0, rows) x [0, k).
@@ -95,8 +287,8 @@ __global__ __launch_bounds__(kThreads) void gemm_i8_kernel(Params p) {
     const int64_t n0 = (int64_t)blockIdx.x * BN;
     const int64_t nk = (p.k + BK - 1) / BK;
 
-    // Register staging of one k-step: A as 2 x 16 bytes, B likewise (NK) or
-    // two 4x4 transposed blocks (KN).
+    // Register staging of one k-step: A as 2 x 16 bytes, B likewise ([n][k])
+    // or two 4x4 transposed blocks ([k][n]).
     uint4 ra[2];
     uint4 rb[2];
     uint32_t rbt[2][4];
@@ -166,43 +358,20 @@ __global__ __launch_bounds__(kThreads) void gemm_i8_kernel(Params p) {
     }
 
     // Epilogue: lane holds column fr of each 16x16 block and rows 4*(lane/16)+r.
-    float s_scalar = 0.0f;
-    if (EPI == EPI_SCALARS && OUT != OUT_I32) {
-        const float sa = *p.sa, sw = *p.sw;
-        const float a1 = sa > p.eps ? sa : p.eps;
-        const float w1 = sw > p.eps ? sw : p.eps;
-        s_scalar = a1;  // applied as (acc * s'_a) * s'_w
-        (void)w1;
-    }
+    Epilogue<EPI, OUT> ep;
+    ep.init(p);
 #pragma unroll
     for (int j = 0; j < TN; j++) {
         const int64_t col = n0 + wn * WN + j * 16 + fr;
         if (col >= p.n) continue;
-        float cs = 1.0f;
-        if (OUT != OUT_I32) {
-            if (EPI == EPI_ROWCOL) cs = p.deq[col];
-            else {
-                const float sw = *p.sw;
-                cs = sw > p.eps ? sw : p.eps;
-            }
-        }
+        const float cf = ep.col_factor(p, col);
 #pragma unroll
-        for (int i = 0; i < TM; i++) {
+        for (int i = 0; i < TM; i++)
 #pragma unroll
             for (int r = 0; r < 4; r++) {
                 const int64_t row = m0 + wm * WM + i * 16 + 4 * (lane / 16) + r;
-                if (row >= p.m) continue;
-                const int32_t v = acc[i][j][r];
-                const int64_t idx = row * p.n + col;
-                if (OUT == OUT_I32) {
-                    static_cast<int32_t *>(p.out)[idx] = v;
-                } else {
-                    const float rs = EPI == EPI_ROWCOL ? p.pts[row] : s_scalar;
-                    const float y = __fmul_rn(__fmul_rn((float)v, rs), cs);
-                    store_out<OUT>(p.out, idx, y);
-                }
+                if (row < p.m) ep.store(p, row, col, acc[i][j][r], ep.row_factor(p, row), cf);
             }
-        }
     }
 }
 
@@ -210,6 +379,16 @@ template <bool NK, bool VEC, int EPI, int OUT>
 hipError_t launch_t(const Params &p, hipStream_t st) {
     dim3 grid((unsigned)((p.n + BN - 1) / BN), (unsigned)((p.m + BM - 1) / BM));
     hipLaunchKernelGGL((gemm_i8_kernel<NK, VEC, EPI, OUT>), grid, dim3(kThreads), 0, st, p);
+    return hipGetLastError();
+}
+
+constexpr int kBigBK = 128;
+
+template <int EPI, int OUT>
+hipError_t launch_big(const Params &p, hipStream_t st) {
+    const int tiles_m = (int)((p.m + LB - 1) / LB), tiles_n = (int)((p.n + LB - 1) / LB);
+    hipLaunchKernelGGL((gemm_i8_big_kernel<kBigBK, EPI, OUT>), dim3((unsigned)(tiles_m * tiles_n)),
+                       dim3(LThreads), 0, st, p, tiles_m, tiles_n);
     return hipGetLastError();
 }
 
@@ -222,6 +401,15 @@ hipError_t launch_out(int out_kind, const Params &p, hipStream_t st) {
     }
 }
 
+template <int EPI>
+hipError_t launch_big_out(int out_kind, const Params &p, hipStream_t st) {
+    switch (out_kind) {
+        case OUT_F16: return launch_big<EPI, OUT_F16>(p, st);
+        case OUT_BF16: return launch_big<EPI, OUT_BF16>(p, st);
+        default: return launch_big<EPI, OUT_I32>(p, st);
+    }
+}
+
 template <bool NK, bool VEC>
 hipError_t launch_epi(int epi, int out_kind, const Params &p, hipStream_t st) {
     return epi == EPI_ROWCOL ? launch_out<NK, VEC, EPI_ROWCOL>(out_kind, p, st)
@@ -230,8 +418,16 @@ hipError_t launch_epi(int epi, int out_kind, const Params &p, hipStream_t st) {
 
 }  // namespace
 
+bool gemm_i8_uses_big_tiles(bool w_nk, int64_t m, int64_t n, int64_t k) {
+    return w_nk && (k % kBigBK) == 0 && m >= 2 * LB && n >= 2 * LB &&
+           ((m + LB - 1) / LB) * ((n + LB - 1) / LB) <= 0x7fffffff;
+}
+
 hipError_t launch_gemm_i8(const GemmI8Args &a, hipStream_t st) {
     Params p{a.x, a.w, a.pts, a.deq, a.sa, a.sw, a.eps, a.m, a.n, a.k, a.out};
+    if (gemm_i8_uses_big_tiles(a.w_nk, a.m, a.n, a.k))
+        return a.epi == EPI_ROWCOL ? launch_big_out<EPI_ROWCOL>(a.out_kind, p, st)
+                                   : launch_big_out<EPI_SCALARS>(a.out_kind, p, st);
     if (a.m > (int64_t)BM * 65535) return hipErrorInvalidValue;
     const bool vec = (a.k % 16) == 0;
     if (a.w_nk)

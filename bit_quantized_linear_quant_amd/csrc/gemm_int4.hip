@@ -74,8 +74,7 @@ __global__ __launch_bounds__(WAVES * 64) void int4_grouped_kernel(const uint16_t
             const int64_t nb = nb0 + j;
             const bool ok = nb < nblocks;
             const int64_t col = nb * 16 + fr;
-            bw[j] = ok ? *reinterpret_cast<const uint4 *>(packed_w + (nb * kblocks + kb) * 256 + 4 * lane)
-                       : make_uint4(0, 0, 0, 0);
+            bw[j] = ok ? load16_stream(packed_w + (nb * kblocks + kb) * 256 + 4 * lane) : make_uint4(0, 0, 0, 0);
             sc[j] = ok ? f16_bits_to_f32(scales[col * groups + g]) : 0.0f;
             zq[j] = ok ? (packed_z[g * (n / 8) + col / 8] >> (4 * (col % 8))) & 15u : 0u;
         }

@@ -17,7 +17,8 @@
 // m <= 16: decode GEMV.  The m rows fill one 16-row MFMA block (missing rows
 //         are zero and cost no memory traffic); each workgroup owns NBLK
 //         column blocks and its waves split k; int32 partials are summed
-//         in LDS in a fixed order (exact, hence deterministic).
+//         in LDS in a fixed order (exact, hence deterministic).  Weights are
+//         read with non-temporal loads: each byte is used exactly once.
 #include "ql_device.hpp"
 #include "ql_launch.hpp"
 
@@ -180,7 +181,7 @@ __global__ __launch_bounds__(WAVES * 64) void w2a8_gemv_kernel(const int8_t *__r
             for (int j = 0; j < NBLK; j++) {
                 const int64_t nb = nb0 + j;
                 bw[u][j] = (kb_ok && nb < nblocks)
-                               ? *reinterpret_cast<const uint4 *>(packed + (nb * kblocks + kb) * 256 + 4 * lane)
+                               ? load16_stream(packed + (nb * kblocks + kb) * 256 + 4 * lane)
                                : make_uint4(0x55555555u, 0x55555555u, 0x55555555u, 0x55555555u);
             }
 #pragma unroll
@@ -219,10 +220,9 @@ __global__ __launch_bounds__(WAVES * 64) void w2a8_gemv_kernel(const int8_t *__r
     }
 }
 
-template <int NBLK, int OUT>
+template <int NBLK, int WAVES, int U, int OUT>
 hipError_t launch_gemv(const int8_t *xq, const float *pts, const int32_t *rowsum, const uint32_t *packed,
                        const double *gamma, int64_t m, int64_t n, int64_t k, void *out, hipStream_t st) {
-    constexpr int WAVES = 4, U = 2;
     const int64_t nblocks = n / 16;
     const unsigned grid = (unsigned)((nblocks + NBLK - 1) / NBLK);
     hipLaunchKernelGGL((w2a8_gemv_kernel<NBLK, WAVES, U, OUT>), dim3(grid), dim3(WAVES * 64), 0, st, xq,
@@ -234,8 +234,11 @@ template <int OUT>
 hipError_t launch_out(const int8_t *xq, const float *pts, const int32_t *rowsum, const uint32_t *packed,
                       const double *gamma, int64_t m, int64_t n, int64_t k, void *out, hipStream_t st) {
     if (m <= 16) {
-        if (m <= 4) return launch_gemv<2, OUT>(xq, pts, rowsum, packed, gamma, m, n, k, out, st);
-        return launch_gemv<4, OUT>(xq, pts, rowsum, packed, gamma, m, n, k, out, st);
+        // Measured on MI355X at k=8192, n=28672 (weights streamed from HBM): m <= 4 is best with
+        // 4 column blocks over 4 waves, 4 k-blocks in flight per wave; larger m with 8 column
+        // blocks per workgroup so each activation fragment load serves more weight blocks.
+        if (m <= 4) return launch_gemv<4, 4, 4, OUT>(xq, pts, rowsum, packed, gamma, m, n, k, out, st);
+        return launch_gemv<8, 8, 2, OUT>(xq, pts, rowsum, packed, gamma, m, n, k, out, st);
     }
     dim3 grid((unsigned)((n + GBN - 1) / GBN), (unsigned)((m + GBM - 1) / GBM));
     hipLaunchKernelGGL((w2a8_gemm_kernel<OUT>), grid, dim3(kGThreads), 0, st, xq, pts, rowsum, packed,

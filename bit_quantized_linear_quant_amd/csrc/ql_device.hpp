@@ -15,6 +15,15 @@ typedef _Float16 h2 __attribute__((ext_vector_type(2)));
 
 constexpr int kWave = 64;
 
+typedef unsigned v4u __attribute__((ext_vector_type(4)));
+
+// 16-byte streaming load (non-temporal: the data is read once and should not
+// displace reused lines from the caches).  p must be 16-byte aligned.
+__device__ __forceinline__ uint4 load16_stream(const void *p) {
+    const v4u t = __builtin_nontemporal_load(reinterpret_cast<const v4u *>(p));
+    return make_uint4(t[0], t[1], t[2], t[3]);
+}
+
 // Output element kinds of the epilogue.
 enum OutKind : int { OUT_F16 = 0, OUT_BF16 = 1, OUT_I32 = 2, OUT_F32 = 3 };
 

@@ -42,6 +42,8 @@ struct GemmI8Args {
     void *out;           // [m, n]
 };
 hipError_t launch_gemm_i8(const GemmI8Args &a, hipStream_t st);
+// True when the product runs on the 256 x 256 direct-to-LDS kernel.
+bool gemm_i8_uses_big_tiles(bool w_nk, int64_t m, int64_t n, int64_t k);
 
 // gemm_w2a8.hip: packed ternary weights.
 hipError_t launch_gemm_w2a8(const int8_t *xq, const float *pts, const int32_t *rowsum,

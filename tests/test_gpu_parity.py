@@ -58,6 +58,10 @@ W8A8_SHAPES = [
     (33, 50, 77, False),
     (256, 256, 64, True),
     (130, 131, 4096, True),
+    (512, 512, 64, True),      # 256 x 256 direct-to-LDS tiles from here on
+    (520, 777, 192, True),     # ragged m and n
+    (1024, 768, 1024, True),
+    (700, 600, 120, True),     # k % 64 != 0: general kernel at large m, n
 ]
 
 
@@ -275,7 +279,8 @@ def test_grouped_int4_zero_point_equals_code_gives_zero():
 # ---------------------------------------------------------------------------
 # A4W4
 # ---------------------------------------------------------------------------
-@pytest.mark.parametrize("m,n,k", [(33, 20, 130), (256, 256, 512), (129, 65, 1000), (1, 1, 1)])
+@pytest.mark.parametrize("m,n,k", [(33, 20, 130), (256, 256, 512), (129, 65, 1000), (1, 1, 1), (600, 520, 640),
+                                   (1024, 1024, 256)])
 @pytest.mark.parametrize("scale_mul", [1.0, 0.25])
 def test_a4w4_parity(m, n, k, scale_mul):
     d = synthetic.a4w4(m, n, k, seed=800 + m + n + k)
