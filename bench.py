@@ -206,6 +206,10 @@ def main():
     ql.lib()
     res, d = bench_a4w4(args, ql, torch, synthetic)
     gemv = bench_decode(ql, torch, synthetic)
+    gemv_src = kernel_source_hash(GEMV_KERNEL_SOURCES)
+    for m_str, key in (("1", "w2a8_gemv_m1_m4_28672x8192"), ("4", "w2a8_gemv_m1_m4_28672x8192"),
+                       ("16", "w2a8_gemv_m16_28672x8192")):
+        gemv["by_m"][m_str]["traffic"] = recorded_traffic(key, gemv_src)
     gemm_src = kernel_source_hash(GEMM_KERNEL_SOURCES)
     traffic = recorded_traffic("gemm_i8_a4w4_8192", gemm_src)
     achieved = res["gemm_tops"]
