@@ -95,7 +95,8 @@ int oracle_quant_act(const float *x, int64_t m, int64_t k, int rmsnorm,
  * scalar weight scale); [CA] weight_quant (scale by the inverse mean
  * absolute value, round to the nearest integer in [-1, 1]).
  *
- *   gamma  = sum |W| / count              (fp64, sequential)
+ *   S      = sum |W|                      (exact, then rounded once to fp64)
+ *   gamma  = S / count                    (one fp64 division)
  *   gamma' = max(gamma, eps)
  *   q      = sign(W) if |W| > gamma'/2 else 0
  * The comparison is exact in fp64 (halving is exact); |W| == gamma'/2
@@ -106,13 +107,67 @@ int oracle_quant_act(const float *x, int64_t m, int64_t k, int rmsnorm,
  * w is read in its stored layout: layout 1 = [n][k] (nn.Linear weight),
  * layout 0 = [k][n].  codes are always written [n][k].
  */
+/*
+ * Exact sum of |w| over fp32 values.  A finite fp32 magnitude is
+ * mant * 2^(e - 149) with mant < 2^24 and e = max(biased exponent - 1, 0)
+ * in [0, 253], so it is an integer below 2^277 in units of 2^-149, and a sum
+ * of fewer than 2^40 of them is an integer below 2^317: five 64-bit limbs
+ * hold it with no rounding at all.  Non-finite inputs are not summed.
+ */
+typedef struct { uint64_t limb[5]; } exact_sum;
+
+static void exact_add_limb(exact_sum *a, int i, uint64_t v)
+{
+    for (; i < 5 && v; i++) {
+        uint64_t old = a->limb[i];
+        a->limb[i] = old + v;
+        v = a->limb[i] < old ? 1u : 0u;   /* carry into the next limb */
+    }
+}
+
+static void exact_add_abs(exact_sum *a, float v)
+{
+    uint32_t bits;
+    memcpy(&bits, &v, sizeof bits);
+    bits &= 0x7fffffffu;
+    uint32_t be = bits >> 23, frac = bits & 0x7fffffu;
+    if (be == 255) return;
+    uint64_t mant = be ? (frac | 0x800000u) : frac;
+    int e = be ? (int)be - 1 : 0;
+    int i = e / 64, off = e % 64;
+    exact_add_limb(a, i, mant << off);
+    if (off > 40) exact_add_limb(a, i + 1, mant >> (64 - off));
+}
+
+/* The exact sum rounded to the nearest fp64, ties to even. */
+static double exact_to_double(const exact_sum *a)
+{
+    int top = -1;
+    for (int b = 319; b >= 0; b--)
+        if ((a->limb[b / 64] >> (b % 64)) & 1u) { top = b; break; }
+    if (top < 0) return 0.0;
+    if (top < 53) {
+        /* below 2^53 units: the integer itself is exact in fp64 */
+        return ldexp((double)a->limb[0], -149);
+    }
+    /* keep bits [top-52, top]; round on bit top-53 and the bits below it */
+    int low = top - 52;
+    uint64_t m = 0;
+    for (int b = top; b >= low; b--) m = (m << 1) | ((a->limb[b / 64] >> (b % 64)) & 1u);
+    int guard = (int)((a->limb[(low - 1) / 64] >> ((low - 1) % 64)) & 1u);
+    int sticky = 0;
+    for (int b = low - 2; b >= 0 && !sticky; b--) sticky = (int)((a->limb[b / 64] >> (b % 64)) & 1u);
+    if (guard && (sticky || (m & 1u))) m++;   /* m may become 2^53: still exact */
+    return ldexp((double)m, low - 149);
+}
+
 int oracle_ternary_quant(const float *w, int layout, int64_t n, int64_t k,
                          double eps, int8_t *codes, double *gamma_out)
 {
     int64_t count = n * k;
-    double sum = 0.0;
-    for (int64_t i = 0; i < count; i++) sum += fabs((double)w[i]);
-    double g = sum / (double)count;
+    exact_sum acc = {{0, 0, 0, 0, 0}};
+    for (int64_t i = 0; i < count; i++) exact_add_abs(&acc, w[i]);
+    double g = exact_to_double(&acc) / (double)count;
     if (g < eps) g = eps;
     double half = g / 2.0;
 #pragma omp parallel for schedule(static)

@@ -13,6 +13,22 @@ TOL_REL = {torch.bfloat16: 2.0 ** -7, torch.float16: 2.0 ** -10}
 TOL_ABS = 1e-6
 
 
+def absmean_rel_tol(count: int) -> float:
+    """Relative bound on |gamma_gpu - gamma_oracle| for the ternary absmean.
+
+    The oracle's gamma is the exact sum of |W| rounded once, divided once
+    (2 roundings).  The kernel sums |W| in fp64 along paths of at most
+    64 sequential adds per thread (16384-element chunks over 256 threads),
+    8 tree levels per workgroup, ceil(chunks / 256) sequential adds per thread
+    of the final workgroup and 8 more tree levels, then divides once; a sum of
+    non-negative terms along a path of d adds is off by at most d units of
+    2^-53 relative.
+    """
+    chunks = -(-count // 16384)
+    depth = 64 + 8 + -(-chunks // 256) + 8 + 1
+    return (depth + 2) * 2.0 ** -53
+
+
 def to_np(t: torch.Tensor) -> np.ndarray:
     t = t.detach().cpu()
     if t.dtype in (torch.bfloat16, torch.float16):

@@ -14,7 +14,7 @@ import torch
 import bit_quantized_linear_quant_amd as ql
 import oracle
 import synthetic
-from parity_util import assert_equal, assert_float_close, poison, to_np, words
+from parity_util import absmean_rel_tol, assert_equal, assert_float_close, poison, to_np, words
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
@@ -166,7 +166,8 @@ def test_pack_ternary_parity(n, k, nk):
     w = synthetic.master_weight(n, k, seed=400 + n + k)
     wl = w if nk else w.t().contiguous()
     codes, gamma = oracle.ternary_quant(wl.numpy(), layout_nk=nk)
-    assert oracle.ternary_tie_band(w.numpy(), gamma) == 0
+    tol = absmean_rel_tol(n * k)
+    assert oracle.ternary_tie_band(w.numpy(), gamma, tol) == 0
     ref = oracle.pack_ternary(codes)
     layout = ql.QL_W_NK if nk else ql.QL_W_KN
     packed = poison((n * k // 16,), torch.int32)
@@ -175,7 +176,7 @@ def test_pack_ternary_parity(n, k, nk):
     p2, g2 = ql.qlinear_pack_ternary(wg, layout)
     _sync()
     assert_equal(words(p1), ref, "ternary words")
-    assert abs(g1.item() - gamma) <= 1e-12 * gamma
+    assert abs(g1.item() - gamma) <= tol * gamma
     assert torch.equal(p1, p2) and torch.equal(g1.view(torch.int64), g2.view(torch.int64))
 
 
@@ -190,7 +191,8 @@ def test_pack_ternary_eps_guard():
 @pytest.mark.parametrize("n,k", [(16, 128), (48, 384), (400, 512)])
 def test_pack_int4_parity(n, k):
     d = synthetic.grouped_int4(1, n, k, 128, seed=500 + n)
-    q = d["q"] | torch.randint(0, 16, d["q"].shape, dtype=torch.uint8) * 16  # high nibbles are ignored
+    hi = torch.from_numpy(synthetic.rng(501 + n).integers(0, 16, tuple(d["q"].shape), dtype=np.uint8))
+    q = d["q"] | hi * 16  # high nibbles are ignored
     ref = oracle.pack_int4(q.numpy())
     out = poison((n * k // 8,), torch.int32)
     ql.qlinear_pack_int4(_cuda(q), ql.QL_INT4_WEIGHT, packed=out)

@@ -169,12 +169,38 @@ def test_ternary_exact_rational_brute_force():
     """Codes equal clamp(round-half-even(W / gamma), -1, 1) with exact rational gamma."""
     w = synthetic.master_weight(16, 48, seed=21).numpy()
     codes, g = oracle.ternary_quant(w)
-    gx = sum(Fraction(abs(float(v))) for v in w.ravel()) / w.size
-    assert abs(Fraction(g) - gx) <= gx * Fraction(1, 10 ** 14)
+    sx = sum(Fraction(abs(float(v))) for v in w.ravel())
+    gx = sx / w.size
+    # gamma = fl64(fl64(exact sum) / count): Python's int / int division rounds correctly
+    assert g == float(sx) / w.size
+    assert abs(Fraction(g) - gx) <= gx * Fraction(1, 2 ** 51)
     assert oracle.ternary_tie_band(w, g) == 0
     for (i, j), v in np.ndenumerate(w):
         c = max(-1, min(1, round(Fraction(float(v)) / gx)))
         assert int(codes[i, j]) == c
+
+
+def test_ternary_absmean_sum_is_exact():
+    """The mean comes from the exact sum of |W|, rounded once: inputs on which
+    a running fp64 sum rounds differently, spanning denormals to 2^127."""
+    cases = [
+        [1.0] + [2.0 ** -53] * 15,          # a running sum stays at 1.0; exactly 1 + 15 * 2^-53
+        [2.0 ** 127, 2.0 ** -149, 1.0, 3.0 ** 20] + [-(2.0 ** 70)] * 12,
+        [2.0 ** -149] * 8 + [1.5 * 2.0 ** -126] * 8,
+        [float(np.float32(v)) for v in synthetic.rng(25).standard_normal(16) * 1e30],
+    ]
+    for vals in cases:
+        w = np.repeat(np.array([vals], np.float32), 16, axis=0)
+        assert np.all(np.isfinite(w))
+        _, g = oracle.ternary_quant(w, eps=0.0)
+        exact = sum(Fraction(abs(float(v))) for v in w.ravel())
+        assert g == float(exact) / w.size, vals
+    # the first case is one a running fp64 sum gets wrong
+    w = np.repeat(np.array([cases[0]], np.float32), 16, axis=0)
+    running = 0.0
+    for v in w.ravel():
+        running += abs(float(v))
+    assert running / w.size != oracle.ternary_quant(w, eps=0.0)[1]
 
 
 def test_ternary_half_tie_rounds_to_zero():
