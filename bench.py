@@ -188,6 +188,172 @@ def bench_decode(ql, torch, synthetic, reps: int = 10):
             "by_m": res}
 
 
+def _events(torch):
+    return torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+
+def time_graph(torch, launch, count: int, reps: int = 10) -> float:
+    """Mean us per launch: `count` launches captured in one HIP graph, replayed `reps` times."""
+    launch(0)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(count):
+            launch(i)
+    g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = _events(torch)
+    e0.record()
+    for _ in range(reps):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    del g
+    return e0.elapsed_time(e1) * 1e3 / (reps * count)
+
+
+def time_eager(torch, launch, count: int) -> float:
+    """Mean us per call of `count` back-to-back calls on the current stream."""
+    launch(0)
+    torch.cuda.synchronize()
+    e0, e1 = _events(torch)
+    e0.record()
+    for i in range(count):
+        launch(i)
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e3 / count
+
+
+def time_cpu(fn, min_s: float = 1.0) -> float:
+    """Seconds per call of fn (repeated until min_s has passed)."""
+    fn()
+    n, t0 = 0, time.perf_counter()
+    while True:
+        fn()
+        n += 1
+        t = time.perf_counter() - t0
+        if t >= min_s:
+            return t / n
+
+
+def _row(us, work, unit, peak, bound, what, oracle_rate=None, oracle_sample=None):
+    rate = work / (us * 1e-6) / (1e9 if unit == "GB/s" else 1e12)
+    r = {"us_per_launch": round(us, 3), "achieved": round(rate, 1), "unit": unit, "bound": bound,
+         "work_per_launch": what}
+    if peak is not None:
+        r["peak"] = peak
+        r["frac"] = round(rate / peak, 4)
+    if oracle_rate is not None:
+        r["oracle"] = {"value": round(oracle_rate, 4), "unit": unit, "sample": oracle_sample}
+    return r
+
+
+def bench_rows(ql, torch, synthetic):
+    """Every step of the path on its own workload, against the roofline that bounds it.
+
+    HBM-bound rows rotate enough input copies (>= 384 MB) that no launch finds its
+    input in the 256 MB last-level cache; launch-bound rows replay a HIP graph.
+    Each row carries the CPU oracle's rate on a sample of the same work.
+    """
+    import numpy as np
+    import oracle
+
+    dev = "cuda:0"
+    rows = {}
+    threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+
+    # a4: per-token W8A8, 16x256x128, fp16 out (launch-bound; no roofline claim).
+    d = synthetic.w8a8()
+    x, w = d["x"].to(dev), d["w"].to(dev)
+    deq, pts = d["deq"].to(dev), d["pts"].to(dev)
+    out = torch.empty((16, 128), dtype=torch.float16, device=dev)
+    us = time_graph(torch, lambda i: ql.qlinear_gemm_w8a8(x, w, ql.QL_W_KN, deq, pts, out=out), 100)
+    xn, wn, dn, pn = (d[key].numpy() for key in ("x", "w", "deq", "pts"))
+    t = time_cpu(lambda: oracle.w8a8(xn, wn, False, pn, dn))
+    rows["a4_w8a8_16x256x128"] = _row(us, 2.0 * 16 * 256 * 128, "TOPS", None, "launch",
+                                      "2*m*n*k ops; HIP-graph replay of 100 launches",
+                                      2.0 * 16 * 256 * 128 / t / 1e12, "the whole product")
+
+    # a1 + a5: BitLinear forward, x bf16 [2048,4096] (1% outliers), w [4096,4096] -> bf16.
+    m, n, k = 2048, 4096, 4096
+    d = synthetic.bitlinear(m, n, k)
+    xs = [d["x"].to(dev)] + [d["x"].to(dev) for _ in range(23)]            # 24 x 16.8 MB
+    q = torch.empty((m, k), dtype=torch.int8, device=dev)
+    pts = torch.empty((m,), dtype=torch.float32, device=dev)
+    rs = torch.empty((m,), dtype=torch.int32, device=dev)
+    us = time_graph(torch, lambda i: ql.qlinear_quant_act(xs[i % len(xs)], rmsnorm=True, q=q,
+                                                          per_token_scale=pts, rowsum=rs), 48)
+    qbytes = m * k * 2 + m * k + 8 * m
+    xf = d["x"].float().numpy()
+    sample = 256
+    t = time_cpu(lambda: oracle.quant_act(xf[:sample], rmsnorm=True))
+    rows["a1_quant_act_2048x4096_bf16_rmsnorm"] = _row(
+        us, qbytes, "GB/s", PEAK_HBM_GBS, "hbm", f"{qbytes} B (bf16 read, int8 codes, scale and rowsum)",
+        sample * (k * 3 + 8) / t / 1e9, f"{sample} of {m} rows")
+    del xs
+    packed, gamma = ql.qlinear_pack_ternary(d["w"].to(dev), ql.QL_W_NK)
+    xq, pts, rs = ql.qlinear_quant_act(d["x"].to(dev), rmsnorm=True)
+    out = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
+    us = time_graph(torch, lambda i: ql.qlinear_gemm_w2a8(xq, pts, rs, packed, gamma, n, out=out), 20)
+    ops = 2.0 * m * n * k
+    codes, g = oracle.ternary_quant(d["w"].numpy())
+    xqn, ptsn, _ = oracle.quant_act(xf[:32], rmsnorm=True)
+    t = time_cpu(lambda: oracle.w2a8(xqn, ptsn, codes, g))
+    rows["a5_w2a8_gemm_2048x4096x4096"] = _row(us, ops, "TOPS", PEAK_INT8_TOPS, "mfma", "2*m*n*k int8 ops",
+                                               2.0 * 32 * n * k / t / 1e12, f"32 of {m} rows")
+
+    # a2: absmean ternary pack of the decode weight fp32 [28672,8192] (one-time).
+    n, k = 28672, 8192
+    wd = synthetic.master_weight(n, k, 1003 + 100_000)
+    wdev = wd.to(dev)
+    pk = torch.empty((n * k // 16,), dtype=torch.int32, device=dev)
+    gm = torch.empty((1,), dtype=torch.float64, device=dev)
+    ws = torch.empty((ql.qlinear_workspace_bytes(ql.QL_OP_PACK_TERNARY, 0, n, k),), dtype=torch.uint8,
+                     device=dev)
+    us = time_eager(torch, lambda i: ql.qlinear_pack_ternary(wdev, ql.QL_W_NK, packed=pk, gamma=gm,
+                                                             workspace=ws), 5)
+    pbytes = 2 * n * k * 4 + n * k // 4
+    wn = wd.numpy()
+    sample = 2048
+    t = time_cpu(lambda: oracle.pack_ternary(oracle.ternary_quant(wn[:sample])[0]))
+    rows["a2_pack_ternary_28672x8192_fp32"] = _row(
+        us, pbytes, "GB/s", PEAK_HBM_GBS, "hbm",
+        f"{pbytes} B (fp32 weight read twice: absmean, then threshold; 2-bit words written)",
+        sample * k * (8 + 0.25) / t / 1e9, f"{sample} of {n} rows (their own absmean)")
+    del wdev, pk, ws
+
+    # a3 + a7: grouped affine INT4, x fp16 [32,4096], uint4 w [11008,4096], g=128 -> fp16.
+    dg = synthetic.grouped_int4()
+    m, n, k, gs = 32, 11008, 4096, dg["group_size"]
+    qdev = dg["q"].to(dev)
+    pw = torch.empty((n * k // 8,), dtype=torch.int32, device=dev)
+    us = time_eager(torch, lambda i: ql.qlinear_pack_int4(qdev, ql.QL_INT4_WEIGHT, packed=pw), 20)
+    i4bytes = n * k + n * k // 2
+    qn = dg["q"].numpy()
+    t = time_cpu(lambda: oracle.pack_int4(qn[:1024]))
+    rows["a3_pack_int4_11008x4096"] = _row(us, i4bytes, "GB/s", PEAK_HBM_GBS, "hbm",
+                                           f"{i4bytes} B (one code byte read, half a byte written per weight)",
+                                           1024 * k * 1.5 / t / 1e9, f"1024 of {n} rows")
+    pws = [pw] + [pw.clone() for _ in range(15)]                           # 16 x 22.5 MB
+    xg = dg["x"].to(dev)
+    sc = dg["s"].to(dev)
+    pz = ql.qlinear_pack_int4(dg["z"].to(dev), ql.QL_INT4_ZEROS)
+    outg = torch.empty((m, n), dtype=torch.float16, device=dev)
+    us = time_graph(torch, lambda i: ql.qlinear_gemm_w4a8_grouped(xg, pws[i % len(pws)], sc, pz, gs, n,
+                                                                  out=outg), 48)
+    gbytes = n * k // 2 + n * (k // gs) * 2 + n * (k // gs) // 2 + m * k * 2 + m * n * 2
+    xgn, sn = dg["x"].float().numpy(), dg["s"].float().numpy()
+    zn = dg["z"].numpy()
+    t = time_cpu(lambda: oracle.grouped_int4(xgn, qn[:512], sn[:512], zn[:512], gs))
+    rows["a7_grouped_int4_32x4096x11008_g128"] = _row(
+        us, gbytes, "GB/s", PEAK_HBM_GBS, "hbm",
+        f"{gbytes} B (packed weight, fp16 scales, packed zeros, fp16 x, fp16 out)",
+        (512 * k // 2 + 512 * (k // gs) * 2.5 + m * k * 2 + m * 512 * 2) / t / 1e9, f"512 of {n} columns")
+    del pws
+    return {"threads_oracle": threads, "rows": rows}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -238,6 +404,7 @@ def main():
                      "work_per_launch": f"2*m*n*k = {int(res['ops'])} int8 ops"},
         "decode_gemv": gemv,
     }
+    line["path_rows"] = bench_rows(ql, torch, synthetic)
     torch.cuda.synchronize()
     line["cpu_baseline"] = cpu_baseline(d)
     print(json.dumps(line), flush=True)

@@ -103,6 +103,13 @@ def _gpu(t: torch.Tensor, name: str, dtype=None):
     return t
 
 
+def _need(t, nbytes: int, name: str):
+    """Reject a buffer smaller than the call reads or writes (the C ABI takes bare pointers)."""
+    if t is not None and t.numel() * t.element_size() < nbytes:
+        raise ValueError(f"{name} holds {t.numel() * t.element_size()} bytes, the call needs {nbytes}")
+    return t
+
+
 def _check(fn: str, rc: int) -> None:
     if rc != QL_OK:
         raise QLinearError(fn, rc)
@@ -133,6 +140,9 @@ def qlinear_quant_act(x, rmsnorm=False, eps_norm=1e-6, eps_q=1e-5, q=None, per_t
     pts = _empty((m,), torch.float32, x) if per_token_scale is None else _gpu(per_token_scale, "pts",
                                                                                torch.float32)
     rs = _empty((m,), torch.int32, x) if rowsum is None else _gpu(rowsum, "rowsum", torch.int32)
+    _need(q, m * k, "q")
+    _need(pts, 4 * m, "per_token_scale")
+    _need(rs, 4 * m, "rowsum")
     _check("qlinear_quant_act", lib().qlinear_quant_act(
         _ptr(x), _TORCH_TO_QL[x.dtype], m, k, QL_RMSNORM if rmsnorm else 0, float(eps_norm), float(eps_q),
         _ptr(q), _ptr(pts), _ptr(rs), _stream(x)))
@@ -144,6 +154,7 @@ def qlinear_quant_int4_tensor(x, scale, eps=1e-5, q=None):
     _gpu(x, "x")
     _gpu(scale, "scale", torch.float32)
     q = _empty(x.shape, torch.int8, x) if q is None else _gpu(q, "q", torch.int8)
+    _need(q, x.numel(), "q")
     _check("qlinear_quant_int4_tensor", lib().qlinear_quant_int4_tensor(
         _ptr(x), _TORCH_TO_QL[x.dtype], x.numel(), _ptr(scale), float(eps), _ptr(q), _stream(x)))
     return q
@@ -155,6 +166,7 @@ def qlinear_pack_ternary(w, layout=QL_W_NK, eps=1e-5, packed=None, gamma=None, w
     n, k = (w.shape if layout == QL_W_NK else (w.shape[1], w.shape[0]))
     packed = _empty((n * k // 16,), torch.int32, w) if packed is None else _gpu(packed, "packed")
     gamma = _empty((1,), torch.float64, w) if gamma is None else _gpu(gamma, "gamma", torch.float64)
+    _need(packed, n * k // 4, "packed")
     ws_bytes = qlinear_workspace_bytes(QL_OP_PACK_TERNARY, 0, n, k)
     if workspace is None:
         workspace = _empty((max(ws_bytes, 1),), torch.uint8, w)
@@ -169,6 +181,7 @@ def qlinear_pack_int4(codes, what=QL_INT4_WEIGHT, packed=None):
     _gpu(codes, "codes", torch.uint8)
     rows, cols = codes.shape
     packed = _empty((rows * cols // 8,), torch.int32, codes) if packed is None else _gpu(packed, "packed")
+    _need(packed, rows * cols // 2, "packed")
     _check("qlinear_pack_int4", lib().qlinear_pack_int4(_ptr(codes), rows, cols, what, _ptr(packed),
                                                         _stream(codes)))
     return packed
@@ -180,10 +193,13 @@ def qlinear_gemm_w8a8(x, w, layout, deq_scale, per_token_scale, out_dtype=torch.
     _gpu(w, "w", torch.int8)
     m, k = x.shape
     n = w.shape[1] if layout == QL_W_KN else w.shape[0]
+    if (w.shape[0] if layout == QL_W_KN else w.shape[1]) != k:
+        raise ValueError(f"w {tuple(w.shape)} does not match x {tuple(x.shape)}")
     if out_dtype != torch.int32:
-        _gpu(deq_scale, "deq_scale", torch.float32)
-        _gpu(per_token_scale, "per_token_scale", torch.float32)
+        _need(_gpu(deq_scale, "deq_scale", torch.float32), 4 * n, "deq_scale")
+        _need(_gpu(per_token_scale, "per_token_scale", torch.float32), 4 * m, "per_token_scale")
     out = _empty((m, n), out_dtype, x) if out is None else _gpu(out, "out", out_dtype)
+    _need(out, m * n * out.element_size(), "out")
     _check("qlinear_gemm_w8a8", lib().qlinear_gemm_w8a8(
         _ptr(x), _ptr(w), layout, _ptr(deq_scale), _ptr(per_token_scale), m, n, k,
         _TORCH_TO_QL[out_dtype], _ptr(out), _stream(x)))
@@ -196,10 +212,13 @@ def qlinear_gemm_w2a8(xq, per_token_scale, rowsum, packed, gamma, n, out_dtype=t
     _gpu(rowsum, "rowsum", torch.int32)
     _gpu(packed, "packed")
     m, k = xq.shape
+    _need(rowsum, 4 * m, "rowsum")
+    _need(packed, n * k // 4, "packed")
     if out_dtype != torch.int32:
-        _gpu(per_token_scale, "per_token_scale", torch.float32)
+        _need(_gpu(per_token_scale, "per_token_scale", torch.float32), 4 * m, "per_token_scale")
         _gpu(gamma, "gamma", torch.float64)
     out = _empty((m, n), out_dtype, xq) if out is None else _gpu(out, "out", out_dtype)
+    _need(out, m * n * out.element_size(), "out")
     _check("qlinear_gemm_w2a8", lib().qlinear_gemm_w2a8(
         _ptr(xq), _ptr(per_token_scale), _ptr(rowsum), _ptr(packed), _ptr(gamma), m, n, k,
         _TORCH_TO_QL[out_dtype], _ptr(out), _stream(xq)))
@@ -214,7 +233,12 @@ def qlinear_gemm_w4a8_grouped(x, packed_w, scales, packed_zeros, group_size, n, 
     _gpu(scales, "scales", torch.float16)
     _gpu(packed_zeros, "packed_zeros")
     m, k = x.shape
+    if group_size > 0 and k % group_size == 0:
+        _need(packed_w, n * k // 2, "packed_w")
+        _need(scales, 2 * n * (k // group_size), "scales")
+        _need(packed_zeros, n * (k // group_size) // 2, "packed_zeros")
     out = _empty((m, n), out_dtype, x) if out is None else _gpu(out, "out", out_dtype)
+    _need(out, m * n * out.element_size(), "out")
     _check("qlinear_gemm_w4a8_grouped", lib().qlinear_gemm_w4a8_grouped(
         _ptr(x), _TORCH_TO_QL[x.dtype], _ptr(per_token_scale), _ptr(packed_w), _ptr(scales),
         _ptr(packed_zeros), group_size, m, n, k, _ptr(bias), _TORCH_TO_QL[out_dtype], _ptr(out),
@@ -228,10 +252,13 @@ def qlinear_gemm_a4w4_codes(xq, wq, scale_a, scale_w, eps=1e-5, out_dtype=torch.
     _gpu(wq, "wq", torch.int8)
     m, k = xq.shape
     n = wq.shape[0]
+    if wq.shape[1] != k:
+        raise ValueError(f"wq {tuple(wq.shape)} does not match xq {tuple(xq.shape)}")
     if out_dtype != torch.int32:
         _gpu(scale_a, "scale_a", torch.float32)
         _gpu(scale_w, "scale_w", torch.float32)
     out = _empty((m, n), out_dtype, xq) if out is None else _gpu(out, "out", out_dtype)
+    _need(out, m * n * out.element_size(), "out")
     _check("qlinear_gemm_a4w4_codes", lib().qlinear_gemm_a4w4_codes(
         _ptr(xq), _ptr(wq), _ptr(scale_a), _ptr(scale_w), float(eps), m, n, k, _TORCH_TO_QL[out_dtype],
         _ptr(out), _stream(xq)))
@@ -246,13 +273,16 @@ def qlinear_gemm_a4w4(x, w, scale_a, scale_w, eps=1e-5, out_dtype=torch.float16,
     _gpu(scale_w, "scale_w", torch.float32)
     m, k = x.shape
     n = w.shape[0]
+    if w.shape[1] != k:
+        raise ValueError(f"w {tuple(w.shape)} does not match x {tuple(x.shape)}")
     ws_bytes = qlinear_workspace_bytes(QL_OP_GEMM_A4W4, m, n, k)
     if workspace is None:
         workspace = _empty((ws_bytes,), torch.uint8, x)
     out = _empty((m, n), out_dtype, x) if out is None else _gpu(out, "out", out_dtype)
+    _need(out, m * n * out.element_size(), "out")
     _check("qlinear_gemm_a4w4", lib().qlinear_gemm_a4w4(
         _ptr(x), _ptr(w), _TORCH_TO_QL[x.dtype], _ptr(scale_a), _ptr(scale_w), float(eps), m, n, k,
-        _TORCH_TO_QL[out_dtype], _ptr(out), _ptr(workspace), workspace.numel(), _stream(x)))
+        _TORCH_TO_QL[out_dtype], _ptr(out), _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(x)))
     return out, workspace
 
 
