@@ -14,8 +14,12 @@
 // the group scale multiplies it once (group_size is a multiple of 128).
 //
 // Workgroup: WAVES waves split the k blocks of NBLK column blocks for one
-// 32-row slice of x (two 16-row MFMA blocks share every unpacked weight
-// fragment); fp32 partials are added in LDS in a fixed wave order.
+// slice of RB 16-row blocks of x (with RB = 2 every unpacked weight fragment
+// feeds two MFMA row blocks; m <= 16 uses RB = 1).  Each wave keeps two
+// register stages: while the matrix cores consume one k block, the weight
+// fragments (non-temporal: read once), scales, zero-points and x fragments
+// of its next k block are in flight.  The fp32 partials of the waves are
+// added in LDS in a fixed wave order.
 #include "ql_device.hpp"
 #include "ql_launch.hpp"
 
@@ -40,7 +44,68 @@ __device__ __forceinline__ v8h unpack_int4(uint32_t w, h2 zz) {
     return r;
 }
 
-template <int NBLK, int WAVES, int OUT>
+// One k block's operands for the NBLK column blocks of a wave: packed
+// weight fragments, raw fp16 scales, zero-point words and the x fragments of
+// RB 16-row blocks.
+template <int NBLK, int RB>
+struct Stage {
+    uint4 w[NBLK];
+    uint32_t s[NBLK], z[NBLK];
+    v8h a[RB][4];
+};
+
+// Issue every load of k block kb (clamped into range; the caller masks a
+// block past the end).  All loads are unconditional, so none of them waits
+// for another.
+template <int NBLK, int RB>
+__device__ __forceinline__ void load_stage(Stage<NBLK, RB> &st, const uint16_t *const xrow[RB],
+                                           const uint32_t *__restrict__ packed_w,
+                                           const uint16_t *__restrict__ scales,
+                                           const uint32_t *__restrict__ packed_z, int64_t kb,
+                                           int64_t nb0, int64_t nblocks, int64_t kblocks,
+                                           int64_t group_size, int64_t groups, int64_t n, int lane) {
+    const int fr = lane % 16;
+    const int64_t kbc = kb < kblocks ? kb : kblocks - 1;
+    const int64_t g = kbc * 128 / group_size;
+#pragma unroll
+    for (int j = 0; j < NBLK; j++) {
+        const int64_t nbc = nb0 + j < nblocks ? nb0 + j : nblocks - 1;
+        const int64_t col = nbc * 16 + fr;
+        st.w[j] = load16_stream(packed_w + (nbc * kblocks + kbc) * 256 + 4 * lane);
+        st.s[j] = scales[col * groups + g];
+        st.z[j] = packed_z[g * (n / 8) + col / 8] >> (4 * (col % 8));
+    }
+#pragma unroll
+    for (int b = 0; b < RB; b++)
+#pragma unroll
+        for (int t = 0; t < 4; t++) st.a[b][t] = *reinterpret_cast<const v8h *>(xrow[b] + kbc * 128 + 8 * t);
+}
+
+// Accumulate one k block: per column block, four MFMA steps per row block
+// into a fresh fp32 partial, then one multiply by the group scale.
+template <int NBLK, int RB>
+__device__ __forceinline__ void compute_stage(const Stage<NBLK, RB> &st, v4f (&acc)[RB][NBLK], bool kb_ok,
+                                              int64_t nb0, int64_t nblocks) {
+#pragma unroll
+    for (int j = 0; j < NBLK; j++) {
+        const bool ok = kb_ok && nb0 + j < nblocks;
+        const float sc = ok ? f16_bits_to_f32(st.s[j]) : 0.0f;
+        const h2 zz = __builtin_bit_cast(h2, (0x6400u | (st.z[j] & 15u)) * 0x00010001u);
+        v4f p[RB];
+#pragma unroll
+        for (int b = 0; b < RB; b++) p[b] = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int t = 0; t < 4; t++) {
+            const v8h wv = unpack_int4(word_of(st.w[j], t), zz);
+#pragma unroll
+            for (int b = 0; b < RB; b++) p[b] = __builtin_amdgcn_mfma_f32_16x16x32_f16(st.a[b][t], wv, p[b], 0, 0, 0);
+        }
+#pragma unroll
+        for (int b = 0; b < RB; b++) acc[b][j] += sc * p[b];
+    }
+}
+
+template <int NBLK, int WAVES, int RB, int OUT>
 __global__ __launch_bounds__(WAVES * 64) void int4_grouped_kernel(const uint16_t *__restrict__ x,
                                                                   const uint32_t *__restrict__ packed_w,
                                                                   const uint16_t *__restrict__ scales,
@@ -48,65 +113,54 @@ __global__ __launch_bounds__(WAVES * 64) void int4_grouped_kernel(const uint16_t
                                                                   int64_t group_size, int64_t m,
                                                                   int64_t n, int64_t k,
                                                                   void *__restrict__ out) {
-    __shared__ v4f red[WAVES][2 * NBLK][kWave];
-    const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+    __shared__ v4f red[WAVES][RB * NBLK][kWave];
+    const int lane = threadIdx.x % kWave, wave = wave_id();
     const int64_t nb0 = (int64_t)blockIdx.x * NBLK;
-    const int64_t row0 = (int64_t)blockIdx.y * 32;
+    const int64_t row0 = (int64_t)blockIdx.y * 16 * RB;
     const int64_t nblocks = n / 16, kblocks = k / 128, groups = k / group_size;
     const int fr = lane % 16;
-    const int64_t r0 = row0 + fr, r1 = row0 + 16 + fr;
-    const bool ok0 = r0 < m, ok1 = r1 < m;
-    const int koff = 32 * (lane / 16);
-
-    v4f acc[2][NBLK];
+    // Rows past m read row 0: an MFMA row only feeds its own output row,
+    // which is never stored.
+    const uint16_t *xrow[RB];
 #pragma unroll
-    for (int b = 0; b < 2; b++)
+    for (int b = 0; b < RB; b++) {
+        const int64_t r = row0 + 16 * b + fr;
+        xrow[b] = x + (r < m ? r : 0) * k + 32 * (lane / 16);
+    }
+
+    v4f acc[RB][NBLK];
+#pragma unroll
+    for (int b = 0; b < RB; b++)
 #pragma unroll
         for (int j = 0; j < NBLK; j++) acc[b][j] = v4f{0.f, 0.f, 0.f, 0.f};
 
-    for (int64_t kb = wave; kb < kblocks; kb += WAVES) {
-        const int64_t g = kb * 128 / group_size;
-        uint4 bw[NBLK];
-        float sc[NBLK];
-        uint32_t zq[NBLK];
-#pragma unroll
-        for (int j = 0; j < NBLK; j++) {
-            const int64_t nb = nb0 + j;
-            const bool ok = nb < nblocks;
-            const int64_t col = nb * 16 + fr;
-            bw[j] = ok ? load16_stream(packed_w + (nb * kblocks + kb) * 256 + 4 * lane) : make_uint4(0, 0, 0, 0);
-            sc[j] = ok ? f16_bits_to_f32(scales[col * groups + g]) : 0.0f;
-            zq[j] = ok ? (packed_z[g * (n / 8) + col / 8] >> (4 * (col % 8))) & 15u : 0u;
-        }
-        v8h a0[4], a1[4];
-#pragma unroll
-        for (int t = 0; t < 4; t++) {
-            const int64_t kk = kb * 128 + koff + 8 * t;
-            a0[t] = ok0 ? *reinterpret_cast<const v8h *>(x + r0 * k + kk) : v8h{};
-            a1[t] = ok1 ? *reinterpret_cast<const v8h *>(x + r1 * k + kk) : v8h{};
-        }
-#pragma unroll
-        for (int j = 0; j < NBLK; j++) {
-            const uint32_t zpair = (0x6400u | zq[j]) * 0x00010001u;
-            const h2 zz = __builtin_bit_cast(h2, zpair);
-            v4f p0 = {0.f, 0.f, 0.f, 0.f}, p1 = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int t = 0; t < 4; t++) {
-                const v8h b = unpack_int4(word_of(bw[j], t), zz);
-                p0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0[t], b, p0, 0, 0, 0);
-                p1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1[t], b, p1, 0, 0, 0);
-            }
-            acc[0][j] += sc[j] * p0;
-            acc[1][j] += sc[j] * p1;
-        }
+    // The wave owns k blocks wave, wave + WAVES, ...  Two register stages:
+    // the loads of the next k block are in flight while the matrix cores
+    // work on the current one.
+    Stage<NBLK, RB> s0, s1;
+    int64_t kb = wave;
+    load_stage(s0, xrow, packed_w, scales, packed_z, kb, nb0, nblocks, kblocks, group_size, groups, n, lane);
+    while (kb < kblocks) {
+        const int64_t kb1 = kb + WAVES;
+        if (kb1 < kblocks)
+            load_stage(s1, xrow, packed_w, scales, packed_z, kb1, nb0, nblocks, kblocks, group_size, groups, n,
+                       lane);
+        compute_stage(s0, acc, true, nb0, nblocks);
+        if (kb1 >= kblocks) break;
+        const int64_t kb2 = kb1 + WAVES;
+        if (kb2 < kblocks)
+            load_stage(s0, xrow, packed_w, scales, packed_z, kb2, nb0, nblocks, kblocks, group_size, groups, n,
+                       lane);
+        compute_stage(s1, acc, true, nb0, nblocks);
+        kb = kb2;
     }
 
 #pragma unroll
-    for (int b = 0; b < 2; b++)
+    for (int b = 0; b < RB; b++)
 #pragma unroll
         for (int j = 0; j < NBLK; j++) red[wave][b * NBLK + j][lane] = acc[b][j];
     __syncthreads();
-    for (int e = wave; e < 2 * NBLK; e += WAVES) {
+    for (int e = wave; e < RB * NBLK; e += WAVES) {
         const int b = e / NBLK, j = e % NBLK;
         const int64_t nb = nb0 + j;
         if (nb >= nblocks) continue;
@@ -122,16 +176,25 @@ __global__ __launch_bounds__(WAVES * 64) void int4_grouped_kernel(const uint16_t
     }
 }
 
+template <int NBLK, int WAVES, int RB, int OUT>
+hipError_t launch_cfg(const uint16_t *x, const uint32_t *packed_w, const uint16_t *scales,
+                      const uint32_t *packed_z, int64_t group_size, int64_t m, int64_t n, int64_t k,
+                      void *out, hipStream_t st) {
+    const int64_t nblocks = n / 16;
+    dim3 grid((unsigned)((nblocks + NBLK - 1) / NBLK), (unsigned)((m + 16 * RB - 1) / (16 * RB)));
+    hipLaunchKernelGGL((int4_grouped_kernel<NBLK, WAVES, RB, OUT>), grid, dim3(WAVES * 64), 0, st, x,
+                       packed_w, scales, packed_z, group_size, m, n, k, out);
+    return hipGetLastError();
+}
+
 template <int OUT>
 hipError_t launch_t(const uint16_t *x, const uint32_t *packed_w, const uint16_t *scales,
                     const uint32_t *packed_z, int64_t group_size, int64_t m, int64_t n, int64_t k,
                     void *out, hipStream_t st) {
-    constexpr int NBLK = 4, WAVES = 8;
-    const int64_t nblocks = n / 16;
-    dim3 grid((unsigned)((nblocks + NBLK - 1) / NBLK), (unsigned)((m + 31) / 32));
-    hipLaunchKernelGGL((int4_grouped_kernel<NBLK, WAVES, OUT>), grid, dim3(WAVES * 64), 0, st, x, packed_w,
-                       scales, packed_z, group_size, m, n, k, out);
-    return hipGetLastError();
+    // m <= 16 needs one 16-row MFMA block; larger m takes 32-row slices so
+    // every unpacked weight fragment serves two row blocks.
+    if (m <= 16) return launch_cfg<3, 8, 1, OUT>(x, packed_w, scales, packed_z, group_size, m, n, k, out, st);
+    return launch_cfg<3, 8, 2, OUT>(x, packed_w, scales, packed_z, group_size, m, n, k, out, st);
 }
 
 }  // namespace

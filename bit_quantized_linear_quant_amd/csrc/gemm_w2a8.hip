@@ -159,7 +159,7 @@ __global__ __launch_bounds__(WAVES * 64) void w2a8_gemv_kernel(const int8_t *__r
                                                                int64_t m, int64_t n, int64_t k,
                                                                void *__restrict__ out) {
     __shared__ v4i red[WAVES][NBLK][kWave];
-    const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+    const int lane = threadIdx.x % kWave, wave = wave_id();
     const int64_t nb0 = (int64_t)blockIdx.x * NBLK;
     const int64_t nblocks = n / 16, kblocks = k / 256;
     const int fr = lane % 16;

@@ -17,6 +17,12 @@ constexpr int kWave = 64;
 
 typedef unsigned v4u __attribute__((ext_vector_type(4)));
 
+// Index of the calling wave in its workgroup, as a wave-uniform (scalar)
+// value, so that arithmetic on it runs on the scalar unit.
+__device__ __forceinline__ int wave_id() {
+    return __builtin_amdgcn_readfirstlane((int)(threadIdx.x / kWave));
+}
+
 // 16-byte streaming load (non-temporal: the data is read once and should not
 // displace reused lines from the caches).  p must be 16-byte aligned.
 __device__ __forceinline__ uint4 load16_stream(const void *p) {
