@@ -14,11 +14,13 @@
 //
 // m > 16: 128 x 128 tiles, 2 x 2 waves of 64 x 64, A staged in LDS per
 //         256-k step (rows padded to 272 bytes), B loaded per wave.
-// m <= 16: decode GEMV.  The m rows fill one 16-row MFMA block (missing rows
-//         are zero and cost no memory traffic); each workgroup owns NBLK
-//         column blocks and its waves split k; int32 partials are summed
-//         in LDS in a fixed order (exact, hence deterministic).  Weights are
-//         read with non-temporal loads: each byte is used exactly once.
+// m <= 16: decode GEMV.  The m rows fill one 16-row MFMA block (rows past m
+//         repeat row 0 and are never stored); each workgroup owns NBLK
+//         column blocks and its waves split k, each wave keeping two
+//         register stages so the next k block's weights are in flight while
+//         the current one is multiplied; int32 partials are summed in LDS in
+//         a fixed order (exact, hence deterministic).  Weights are read with
+//         non-temporal loads: each byte is used exactly once.
 #include "ql_device.hpp"
 #include "ql_launch.hpp"
 
@@ -150,6 +152,52 @@ __global__ __launch_bounds__(kGThreads) void w2a8_gemm_kernel(const int8_t *__re
 // ---------------------------------------------------------------------------
 // m <= 16: split-K decode GEMV
 // ---------------------------------------------------------------------------
+// U k blocks of operands for the NBLK column blocks of one wave.
+template <int NBLK, int U>
+struct GemvStage {
+    uint4 w[U][NBLK];
+    v4i a[U][4];
+};
+
+// Issue every load of the k blocks kb0, kb0 + WAVES, ... (U of them) from
+// clamped, in-bounds addresses; nothing is conditional, so no load waits for
+// another.  A k block past the end is masked at compute time.
+template <int NBLK, int WAVES, int U>
+__device__ __forceinline__ void gemv_load(GemvStage<NBLK, U> &st, const int8_t *xrow,
+                                          const uint32_t *__restrict__ packed, int64_t kb0, int64_t nb0,
+                                          int64_t nblocks, int64_t kblocks, int lane) {
+#pragma unroll
+    for (int u = 0; u < U; u++) {
+        const int64_t kb = kb0 + (int64_t)u * WAVES;
+        const int64_t kbc = kb < kblocks ? kb : kblocks - 1;
+#pragma unroll
+        for (int j = 0; j < NBLK; j++) {
+            const int64_t nbc = nb0 + j < nblocks ? nb0 + j : nblocks - 1;
+            st.w[u][j] = load16_stream(packed + (nbc * kblocks + kbc) * 256 + 4 * lane);
+        }
+#pragma unroll
+        for (int t = 0; t < 4; t++) st.a[u][t] = *reinterpret_cast<const v4i *>(xrow + kbc * 256 + 16 * t);
+    }
+}
+
+template <int NBLK, int WAVES, int U>
+__device__ __forceinline__ void gemv_compute(const GemvStage<NBLK, U> &st, v4i (&acc)[NBLK], int64_t kb0,
+                                             int64_t kblocks) {
+#pragma unroll
+    for (int u = 0; u < U; u++) {
+        // a zero activation fragment removes a k block past the end exactly
+        const bool ok = kb0 + (int64_t)u * WAVES < kblocks;
+#pragma unroll
+        for (int t = 0; t < 4; t++) {
+            const v4i a = ok ? st.a[u][t] : v4i{0, 0, 0, 0};
+#pragma unroll
+            for (int j = 0; j < NBLK; j++)
+                acc[j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, unpack_tern(word_of(st.w[u][j], t)), acc[j], 0,
+                                                               0, 0);
+        }
+    }
+}
+
 template <int NBLK, int WAVES, int U, int OUT>
 __global__ __launch_bounds__(WAVES * 64) void w2a8_gemv_kernel(const int8_t *__restrict__ xq,
                                                                const float *__restrict__ pts,
@@ -163,40 +211,30 @@ __global__ __launch_bounds__(WAVES * 64) void w2a8_gemv_kernel(const int8_t *__r
     const int64_t nb0 = (int64_t)blockIdx.x * NBLK;
     const int64_t nblocks = n / 16, kblocks = k / 256;
     const int fr = lane % 16;
-    const bool row_ok = fr < m;
-    const int8_t *xrow = xq + (int64_t)fr * k + 64 * (lane / 16);
+    // Rows past m read row 0: an MFMA row only feeds its own output row,
+    // which is never stored.  Column blocks past n likewise repeat the last.
+    const int8_t *xrow = xq + (int64_t)(fr < m ? fr : 0) * k + 64 * (lane / 16);
 
     v4i acc[NBLK];
 #pragma unroll
     for (int j = 0; j < NBLK; j++) acc[j] = v4i{0, 0, 0, 0};
 
-    for (int64_t kb0 = wave; kb0 < kblocks; kb0 += (int64_t)WAVES * U) {
-        uint4 bw[U][NBLK];
-        v4i af[U][4];
-#pragma unroll
-        for (int u = 0; u < U; u++) {
-            const int64_t kb = kb0 + (int64_t)u * WAVES;
-            const bool kb_ok = kb < kblocks;
-#pragma unroll
-            for (int j = 0; j < NBLK; j++) {
-                const int64_t nb = nb0 + j;
-                bw[u][j] = (kb_ok && nb < nblocks)
-                               ? load16_stream(packed + (nb * kblocks + kb) * 256 + 4 * lane)
-                               : make_uint4(0x55555555u, 0x55555555u, 0x55555555u, 0x55555555u);
-            }
-#pragma unroll
-            for (int t = 0; t < 4; t++)
-                af[u][t] = (kb_ok && row_ok) ? *reinterpret_cast<const v4i *>(xrow + kb * 256 + 16 * t)
-                                             : v4i{0, 0, 0, 0};
-        }
-#pragma unroll
-        for (int u = 0; u < U; u++)
-#pragma unroll
-            for (int t = 0; t < 4; t++)
-#pragma unroll
-                for (int j = 0; j < NBLK; j++)
-                    acc[j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(af[u][t], unpack_tern(word_of(bw[u][j], t)),
-                                                                   acc[j], 0, 0, 0);
+    // Two register stages of U k blocks each: the loads of the next stage are
+    // in flight while the matrix cores consume the current one.
+    constexpr int64_t step = (int64_t)WAVES * U;
+    GemvStage<NBLK, U> s0, s1;
+    int64_t kb = wave;
+    gemv_load<NBLK, WAVES, U>(s0, xrow, packed, kb, nb0, nblocks, kblocks, lane);
+    while (true) {
+        const int64_t kb1 = kb + step;
+        if (kb1 < kblocks) gemv_load<NBLK, WAVES, U>(s1, xrow, packed, kb1, nb0, nblocks, kblocks, lane);
+        gemv_compute<NBLK, WAVES, U>(s0, acc, kb, kblocks);
+        if (kb1 >= kblocks) break;
+        const int64_t kb2 = kb1 + step;
+        if (kb2 < kblocks) gemv_load<NBLK, WAVES, U>(s0, xrow, packed, kb2, nb0, nblocks, kblocks, lane);
+        gemv_compute<NBLK, WAVES, U>(s1, acc, kb1, kblocks);
+        if (kb2 >= kblocks) break;
+        kb = kb2;
     }
 
 #pragma unroll
@@ -234,11 +272,10 @@ template <int OUT>
 hipError_t launch_out(const int8_t *xq, const float *pts, const int32_t *rowsum, const uint32_t *packed,
                       const double *gamma, int64_t m, int64_t n, int64_t k, void *out, hipStream_t st) {
     if (m <= 16) {
-        // Measured on MI355X at k=8192, n=28672 (weights streamed from HBM): m <= 4 is best with
-        // 4 column blocks over 4 waves, 4 k-blocks in flight per wave; larger m with 8 column
-        // blocks per workgroup so each activation fragment load serves more weight blocks.
-        if (m <= 4) return launch_gemv<4, 4, 4, OUT>(xq, pts, rowsum, packed, gamma, m, n, k, out, st);
-        return launch_gemv<8, 8, 2, OUT>(xq, pts, rowsum, packed, gamma, m, n, k, out, st);
+        // Measured on MI355X at k=8192, n=28672 with the weights streamed from
+        // HBM: 4 column blocks per workgroup over 8 waves, one k block per
+        // register stage, is the fastest for every m from 1 to 16.
+        return launch_gemv<4, 8, 1, OUT>(xq, pts, rowsum, packed, gamma, m, n, k, out, st);
     }
     dim3 grid((unsigned)((n + GBN - 1) / GBN), (unsigned)((m + GBM - 1) / GBM));
     hipLaunchKernelGGL((w2a8_gemm_kernel<OUT>), grid, dim3(kGThreads), 0, st, xq, pts, rowsum, packed,

@@ -2,10 +2,12 @@
 //
 // quant_act: per-token absmax int8 codes with an optional parameter-free
 // RMSNorm folded into the per-token scale ("Class BitLinear" forward steps
-// 1-2 and 5; "Common Attention Utilities" activation_quant).  One 256-thread
-// workgroup per token row; the row is read from HBM once and kept in
-// registers (up to 8192 elements), the absmax / sum of squares are wave64
-// shuffle reductions, and the codes are written with 8-byte stores.
+// 1-2 and 5; "Common Attention Utilities" activation_quant).  Rows of up to
+// 8192 elements in whole 8-element chunks: one wave per row, the row held in
+// registers, all of a lane's loads in flight at once, wave64 shuffle
+// reductions only.  Other rows: one 256-thread workgroup per row, the row
+// read from HBM once and kept in registers (up to 8192 elements), wave
+// reductions combined through LDS.  Codes are written with 8-byte stores.
 //
 // quant_int4_tensor: per-tensor 4-bit codes of "Q4LinearFunction" forward,
 // q = clamp(rne(x / max(scale, eps)), -8, 7) with IEEE division.
@@ -149,6 +151,107 @@ __global__ __launch_bounds__(kQThreads) void quant_act_kernel(const void *__rest
     }
 }
 
+// One wave per token row for rows of at most 64 * NCH whole 8-element
+// chunks: lane l holds chunks l, l + 64, ... in registers.  Every load is
+// unconditional (a chunk index past the row is clamped to the last chunk and
+// its values are masked to zero), so all of a lane's loads are in flight
+// together; absmax, sum of squares and the code sum are wave64 shuffle
+// reductions, with no LDS and no barrier.
+constexpr int kQWaveRows = 4;  // rows (waves) per workgroup
+
+template <int K, int NCH, bool RMS>
+__global__ __launch_bounds__(kQWaveRows * kWave) void quant_act_wave_kernel(const void *__restrict__ x,
+                                                                            int64_t m, int64_t k,
+                                                                            float eps_norm, float eps_q,
+                                                                            int8_t *__restrict__ q,
+                                                                            float *__restrict__ pts,
+                                                                            int32_t *__restrict__ rowsum) {
+    const int lane = threadIdx.x % kWave;
+    const int64_t row = (int64_t)blockIdx.x * kQWaveRows + wave_id();
+    if (row >= m) return;
+    const int esz = K == IN_F32 ? 4 : 2;
+    const void *xr = static_cast<const char *>(x) + row * k * esz;
+    int8_t *qr = q + row * k;
+    const int64_t nchunk = k / 8;
+
+    float v[NCH][8];
+#pragma unroll
+    for (int c = 0; c < NCH; c++) {
+        const int64_t ch = (int64_t)c * kWave + lane;
+        load8_vec<K>(xr, (ch < nchunk ? ch : nchunk - 1) * 8, v[c]);
+    }
+    float amax = 0.0f, ss = 0.0f;
+#pragma unroll
+    for (int c = 0; c < NCH; c++) {
+        const bool in = (int64_t)c * kWave + lane < nchunk;
+#pragma unroll
+        for (int j = 0; j < 8; j++) {
+            const float e = in ? v[c][j] : 0.0f;
+            v[c][j] = e;
+            amax = fmaxf(amax, fabsf(e));
+            if (RMS) ss += e * e;
+        }
+    }
+    amax = wave_max(amax);
+    if (RMS) ss = wave_sum(ss);
+
+    const float ap = amax > eps_q ? amax : eps_q;
+    const float s = __fdiv_rn(127.0f, ap);
+    int rs = 0;
+#pragma unroll
+    for (int c = 0; c < NCH; c++) {
+        const int64_t ch = (int64_t)c * kWave + lane;
+        uint32_t lo = 0, hi = 0;
+#pragma unroll
+        for (int j = 0; j < 4; j++) {
+            const int c0 = code_i8(v[c][j], s), c1 = code_i8(v[c][j + 4], s);
+            rs += c0 + c1;
+            lo |= (uint32_t)(c0 & 0xff) << (8 * j);
+            hi |= (uint32_t)(c1 & 0xff) << (8 * j);
+        }
+        if (ch < nchunk) *reinterpret_cast<uint2 *>(qr + ch * 8) = make_uint2(lo, hi);
+    }
+    rs = wave_sum(rs);
+    if (lane == 0) {
+        float p;
+        if (RMS) {
+            const float r = 1.0f / sqrtf(ss / (float)k + eps_norm);
+            p = ap * r / 127.0f;
+        } else {
+            p = __fdiv_rn(ap, 127.0f);
+        }
+        pts[row] = p;
+        if (rowsum) rowsum[row] = rs;
+    }
+}
+
+template <int K, int NCH>
+hipError_t launch_wave_rows(bool rms, const void *x, int64_t m, int64_t k, float eps_norm, float eps_q,
+                            int8_t *q, float *pts, int32_t *rowsum, hipStream_t st) {
+    const unsigned grid = (unsigned)((m + kQWaveRows - 1) / kQWaveRows);
+    if (rms)
+        hipLaunchKernelGGL((quant_act_wave_kernel<K, NCH, true>), dim3(grid), dim3(kQWaveRows * kWave), 0, st, x,
+                           m, k, eps_norm, eps_q, q, pts, rowsum);
+    else
+        hipLaunchKernelGGL((quant_act_wave_kernel<K, NCH, false>), dim3(grid), dim3(kQWaveRows * kWave), 0, st,
+                           x, m, k, eps_norm, eps_q, q, pts, rowsum);
+    return hipGetLastError();
+}
+
+// Rows of whole 8-element chunks up to 8192 elements take the wave-per-row
+// kernel, sized to the row; anything else the workgroup-per-row kernel.
+template <int K>
+bool try_wave_rows(hipError_t &err, bool rms, const void *x, int64_t m, int64_t k, float eps_norm,
+                   float eps_q, int8_t *q, float *pts, int32_t *rowsum, hipStream_t st) {
+    if (k % 8 != 0 || k > 8192) return false;
+    const int64_t per_lane = (k / 8 + kWave - 1) / kWave;
+    if (per_lane <= 2) err = launch_wave_rows<K, 2>(rms, x, m, k, eps_norm, eps_q, q, pts, rowsum, st);
+    else if (per_lane <= 4) err = launch_wave_rows<K, 4>(rms, x, m, k, eps_norm, eps_q, q, pts, rowsum, st);
+    else if (per_lane <= 8) err = launch_wave_rows<K, 8>(rms, x, m, k, eps_norm, eps_q, q, pts, rowsum, st);
+    else err = launch_wave_rows<K, 16>(rms, x, m, k, eps_norm, eps_q, q, pts, rowsum, st);
+    return true;
+}
+
 constexpr int kI4Threads = 256;
 
 __device__ __forceinline__ uint32_t code_i4(float v, float sp) {
@@ -232,6 +335,13 @@ hipError_t launch_quant_act(int in_kind, const void *x, int64_t m, int64_t k, bo
     // Vector path: every row starts 16-byte aligned and holds whole 8-element
     // chunks, and the int8 code row is 8-byte aligned.
     const bool vec = (k % 8) == 0;
+    hipError_t err = hipSuccess;
+    const bool done = in_kind == IN_F32
+                          ? try_wave_rows<IN_F32>(err, rmsnorm, x, m, k, eps_norm, eps_q, q, pts, rowsum, st)
+                          : in_kind == IN_F16
+                                ? try_wave_rows<IN_F16>(err, rmsnorm, x, m, k, eps_norm, eps_q, q, pts, rowsum, st)
+                                : try_wave_rows<IN_BF16>(err, rmsnorm, x, m, k, eps_norm, eps_q, q, pts, rowsum, st);
+    if (done) return err;
     switch (in_kind) {
         case IN_F32: return launch_quant_act_v<IN_F32>(vec, rmsnorm, x, m, k, eps_norm, eps_q, q, pts, rowsum, st);
         case IN_F16: return launch_quant_act_v<IN_F16>(vec, rmsnorm, x, m, k, eps_norm, eps_q, q, pts, rowsum, st);
