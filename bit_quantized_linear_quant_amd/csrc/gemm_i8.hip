@@ -47,10 +47,13 @@ struct Params {
 };
 
 // Per-row and per-column epilogue factors: (acc * row) * col, rounded once
-// per multiply in fp32, then to the output type.
+// per multiply in fp32, then to the output type.  Per-row factors of a tile
+// are staged in LDS and per-column factors loaded before the store loops, so
+// no output element waits on a global load of its own.
 template <int EPI, int OUT>
 struct Epilogue {
     float sa = 0.f, sw = 0.f;
+    const float *rowf = nullptr;  // LDS copy of the tile's per-row factors
     __device__ __forceinline__ void init(const Params &p) {
         if (EPI == EPI_SCALARS && OUT != OUT_I32) {
             const float a = *p.sa, w = *p.sw;
@@ -58,13 +61,22 @@ struct Epilogue {
             sw = w > p.eps ? w : p.eps;
         }
     }
+    // Called by every thread of the workgroup, after the last read of `lds`
+    // by the main loop; a barrier must follow before row_factor is used.
+    __device__ __forceinline__ void stage_rows(const Params &p, int64_t m0, int rows, float *lds) {
+        if (EPI == EPI_ROWCOL && OUT != OUT_I32) {
+            for (int r = threadIdx.x; r < rows; r += blockDim.x) lds[r] = p.pts[m0 + r < p.m ? m0 + r : p.m - 1];
+            rowf = lds;
+        }
+    }
     __device__ __forceinline__ float col_factor(const Params &p, int64_t col) const {
         if (OUT == OUT_I32) return 0.f;
-        return EPI == EPI_ROWCOL ? p.deq[col] : sw;
+        return EPI == EPI_ROWCOL ? p.deq[col < p.n ? col : p.n - 1] : sw;
     }
-    __device__ __forceinline__ float row_factor(const Params &p, int64_t row) const {
+    // `local` is the row's index within the staged tile.
+    __device__ __forceinline__ float row_factor(int local) const {
         if (OUT == OUT_I32) return 0.f;
-        return EPI == EPI_ROWCOL ? p.pts[row] : sa;
+        return EPI == EPI_ROWCOL ? rowf[local] : sa;
     }
     __device__ __forceinline__ void store(const Params &p, int64_t row, int64_t col, int32_t v, float rf,
                                           float cf) const {
@@ -87,22 +99,6 @@ __device__ __forceinline__ int swz(int r) {
     else return (r & 7) ^ ((r >> 3) & 3);
 }
 
-// Workgroup id -> (tile row, tile column).  Hardware hands consecutive ids to
-// the 8 XCDs in turn; ids are first regrouped so each XCD receives a
-// contiguous range of tiles, then each range is walked kGroupM tile rows at a
-// time, column by column.
-__device__ __forceinline__ void tile_of(int b, int tiles_m, int tiles_n, int &tm, int &tn) {
-    const int total = tiles_m * tiles_n;
-    int t = b;
-    if (total % 8 == 0) t = (b % 8) * (total / 8) + b / 8;
-    const int group = t / (kGroupM * tiles_n);
-    const int first = group * kGroupM;
-    const int rows = min(tiles_m - first, kGroupM);
-    const int within = t - group * kGroupM * tiles_n;
-    tm = first + within % rows;
-    tn = within / rows;
-}
-
 template <int BK, int EPI, int OUT>
 __global__ __launch_bounds__(LThreads, 1) void gemm_i8_big_kernel(Params p, int tiles_m, int tiles_n) {
     constexpr int CH = BK / 16;                 // 16-byte chunks per LDS row
@@ -110,12 +106,16 @@ __global__ __launch_bounds__(LThreads, 1) void gemm_i8_big_kernel(Params p, int 
     constexpr int PER_WAVE = TILE / 1024 / 4;   // 1 KB direct loads per wave per slice and operand
     constexpr int S = BK / 32;                  // 32-k MFMA steps per slice
     static_assert(S % 2 == 0, "fragment double buffer assumes an even step count");
-    __shared__ __attribute__((aligned(1024))) int8_t smem[2 * 2 * TILE];
+    // main loop: two A and two B slices; epilogue: 1 KB of row factors, then
+    // one padded 128 x 128 output sub-tile per wave (2-byte outputs)
+    constexpr int EPITCH = 128 * 2 + 16;
+    constexpr int SMEM = 2 * 2 * TILE > 1024 + 4 * 128 * EPITCH ? 2 * 2 * TILE : 1024 + 4 * 128 * EPITCH;
+    __shared__ __attribute__((aligned(1024))) int8_t smem[SMEM];
 
     const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
     const int wm = wave / 2, wn = wave % 2;
     int tm, tn;
-    tile_of(blockIdx.x, tiles_m, tiles_n, tm, tn);
+    xcd_tile(blockIdx.x, tiles_m, tiles_n, kGroupM, tm, tn);
     const int64_t m0 = (int64_t)tm * LB, n0 = (int64_t)tn * LB;
     const int64_t K = p.k;
     const int64_t nk = K / BK;
@@ -209,17 +209,62 @@ __global__ __launch_bounds__(LThreads, 1) void gemm_i8_big_kernel(Params p, int 
     // 8*(r/4) + 4*(lane/32) + r%4 of register r.
     Epilogue<EPI, OUT> ep;
     ep.init(p);
+    ep.stage_rows(p, m0, LB, reinterpret_cast<float *>(smem));
+    __syncthreads();
+    float cf[4];
 #pragma unroll
-    for (int j = 0; j < 4; j++) {
-        const int64_t col = n0 + wn * 128 + 32 * j + fr;
-        if (col >= p.n) continue;
-        const float cf = ep.col_factor(p, col);
+    for (int j = 0; j < 4; j++) cf[j] = ep.col_factor(p, n0 + wn * 128 + 32 * j + fr);
+    if constexpr (OUT == OUT_F16 || OUT == OUT_BF16) {
+        // Through LDS: the wave rounds its 128 x 128 sub-tile into a padded
+        // LDS tile (the two row groups of one write land 16 banks apart), then
+        // writes whole 256-byte row segments, 16 bytes per lane.
+        int8_t *tile = smem + 1024 + wave * 128 * EPITCH;
 #pragma unroll
         for (int i = 0; i < 4; i++)
 #pragma unroll
             for (int r = 0; r < 16; r++) {
-                const int64_t row = m0 + wm * 128 + 32 * i + 8 * (r / 4) + 4 * (lane / 32) + (r % 4);
-                if (row < p.m) ep.store(p, row, col, acc[i][j][r], ep.row_factor(p, row), cf);
+                const int lr = 32 * i + 8 * (r / 4) + 4 * (lane / 32) + (r % 4);
+                const float rf = ep.row_factor(wm * 128 + lr);
+#pragma unroll
+                for (int j = 0; j < 4; j++) {
+                    const float y = __fmul_rn(__fmul_rn((float)acc[i][j][r], rf), cf[j]);
+                    *reinterpret_cast<uint16_t *>(tile + lr * EPITCH + 2 * (32 * j + fr)) =
+                        OUT == OUT_F16 ? f32_to_f16_rne(y) : f32_to_bf16_rne(y);
+                }
+            }
+        // each wave reads back only its own sub-tile
+        __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0)
+        __builtin_amdgcn_wave_barrier();
+#pragma unroll
+        for (int q = 0; q < 32; q++) {
+            const int lr = 4 * q + lane / 16, piece = lane % 16;
+            const uint4 v = *reinterpret_cast<const uint4 *>(tile + lr * EPITCH + 16 * piece);
+            const int64_t row = m0 + wm * 128 + lr, col = n0 + wn * 128 + 8 * piece;
+            if (row < p.m) {
+                uint16_t *dst = static_cast<uint16_t *>(p.out) + row * p.n + col;
+                if (col + 8 <= p.n && (p.n % 8) == 0) {
+                    *reinterpret_cast<uint4 *>(dst) = v;
+                } else {
+                    const uint16_t h[8] = {(uint16_t)v.x, (uint16_t)(v.x >> 16), (uint16_t)v.y, (uint16_t)(v.y >> 16),
+                                           (uint16_t)v.z, (uint16_t)(v.z >> 16), (uint16_t)v.w, (uint16_t)(v.w >> 16)};
+#pragma unroll
+                    for (int e = 0; e < 8; e++)
+                        if (col + e < p.n) dst[e] = h[e];
+                }
+            }
+        }
+        return;
+    }
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+        const int64_t col = n0 + wn * 128 + 32 * j + fr;
+        if (col >= p.n) continue;
+#pragma unroll
+        for (int i = 0; i < 4; i++)
+#pragma unroll
+            for (int r = 0; r < 16; r++) {
+                const int local = wm * 128 + 32 * i + 8 * (r / 4) + 4 * (lane / 32) + (r % 4);
+                if (m0 + local < p.m) ep.store(p, m0 + local, col, acc[i][j][r], ep.row_factor(local), cf[j]);
             }
     }
 }
@@ -360,17 +405,21 @@ __global__ __launch_bounds__(kThreads) void gemm_i8_kernel(Params p) {
     // Epilogue: lane holds column fr of each 16x16 block and rows 4*(lane/16)+r.
     Epilogue<EPI, OUT> ep;
     ep.init(p);
+    ep.stage_rows(p, m0, BM, reinterpret_cast<float *>(As));
+    __syncthreads();
+    float cf[TN];
+#pragma unroll
+    for (int j = 0; j < TN; j++) cf[j] = ep.col_factor(p, n0 + wn * WN + j * 16 + fr);
 #pragma unroll
     for (int j = 0; j < TN; j++) {
         const int64_t col = n0 + wn * WN + j * 16 + fr;
         if (col >= p.n) continue;
-        const float cf = ep.col_factor(p, col);
 #pragma unroll
         for (int i = 0; i < TM; i++)
 #pragma unroll
             for (int r = 0; r < 4; r++) {
-                const int64_t row = m0 + wm * WM + i * 16 + 4 * (lane / 16) + r;
-                if (row < p.m) ep.store(p, row, col, acc[i][j][r], ep.row_factor(p, row), cf);
+                const int local = wm * WM + i * 16 + 4 * (lane / 16) + r;
+                if (m0 + local < p.m) ep.store(p, m0 + local, col, acc[i][j][r], ep.row_factor(local), cf[j]);
             }
     }
 }

@@ -45,6 +45,19 @@ __device__ __forceinline__ void epilogue_store(void *out, int64_t idx, int32_t a
     else store_out<OUT>(out, idx, __fmul_rn(__fmul_rn((float)v, pts), g));
 }
 
+// Code sums and per-token scales of a tile's rows, staged in LDS after the
+// main loop (every thread of the workgroup calls this; a barrier must follow)
+// so no output element waits on a global load of its own.
+template <int OUT>
+__device__ __forceinline__ void stage_rows(const float *__restrict__ pts, const int32_t *__restrict__ rowsum,
+                                           int64_t m, int64_t m0, int rows, int32_t *rs_lds, float *pts_lds) {
+    for (int r = threadIdx.x; r < rows; r += blockDim.x) {
+        const int64_t row = m0 + r < m ? m0 + r : m - 1;
+        rs_lds[r] = rowsum[row];
+        if (OUT != OUT_I32) pts_lds[r] = pts[row];
+    }
+}
+
 // ---------------------------------------------------------------------------
 // m > 16: tiled GEMM
 // ---------------------------------------------------------------------------
@@ -131,6 +144,10 @@ __global__ __launch_bounds__(kGThreads) void w2a8_gemm_kernel(const int8_t *__re
         }
     }
 
+    int32_t *rs_lds = reinterpret_cast<int32_t *>(As);
+    float *pts_lds = reinterpret_cast<float *>(As) + GBM;
+    stage_rows<OUT>(pts, rowsum, m, m0, GBM, rs_lds, pts_lds);
+    __syncthreads();
     const float g = OUT == OUT_I32 ? 0.0f : (float)gamma[0];  // gamma may be NULL for int32 output
 #pragma unroll
     for (int j = 0; j < 4; j++) {
@@ -141,11 +158,183 @@ __global__ __launch_bounds__(kGThreads) void w2a8_gemm_kernel(const int8_t *__re
         for (int i = 0; i < 4; i++)
 #pragma unroll
             for (int r = 0; r < 4; r++) {
-                const int64_t row = m0 + wm * 64 + i * 16 + 4 * (lane / 16) + r;
-                if (row < m)
-                    epilogue_store<OUT>(out, row * n + col, acc[i][j][r], rowsum[row],
-                                        OUT == OUT_I32 ? 0.0f : pts[row], g);
+                const int local = wm * 64 + i * 16 + 4 * (lane / 16) + r;
+                if (m0 + local < m)
+                    epilogue_store<OUT>(out, (m0 + local) * n + col, acc[i][j][r], rs_lds[local],
+                                        OUT == OUT_I32 ? 0.0f : pts_lds[local], g);
             }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// m >= 256: large-tile GEMM
+// ---------------------------------------------------------------------------
+// A 256-thread workgroup owns a 256 x 128 output tile; wave (wm, wn) owns
+// 128 x 64 as 8 x 4 blocks of v_mfma_i32_16x16x64_i8.  Per 256-k block:
+//   * the A slice (256 token rows x 256 code bytes, 64 KB) goes HBM -> LDS
+//     with global_load_lds_dwordx4, double-buffered; 16-byte chunk c of row r
+//     is stored at chunk position c ^ (r & 15), so the 16 rows read by one
+//     fragment load sit in distinct bank groups;
+//   * the tile's eight packed weight fragment blocks (1 KB each, already in
+//     lane order) go HBM -> LDS the same way; each wave reads its four and
+//     unpacks them in registers.
+// Step t of a block uses, for lane l, k = 64(l/16) + 16t: chunk 4(l/16) + t
+// of the A row and word t of the weight fragment.
+constexpr int XBM = 256, XBN = 128, XBK = 256;
+constexpr int kXThreads = 256;
+constexpr int kXGroupM = 4;
+constexpr int kXSlice = XBM * XBK;                     // bytes of one A slice
+constexpr int kXBSlice = XBN / 16 * 1024;              // bytes of one B slice (8 fragment blocks)
+constexpr int kXStage = kXSlice + kXBSlice;
+constexpr int kXLoads = kXSlice / 1024 / (kXThreads / kWave);   // 1 KB A loads per wave per slice
+constexpr int kXBLoads = kXBSlice / 1024 / (kXThreads / kWave); // 1 KB B loads per wave per slice
+
+__device__ __forceinline__ void xs_wait_all() { __builtin_amdgcn_s_waitcnt(0); }
+
+// One 256-k block: the loads of the next block go to `nxt` while the matrix
+// cores consume `cur`.  The two slices are distinct restrict pointers, so the
+// compiler knows the LDS reads of `cur` do not depend on the loads into `nxt`
+// and does not make them wait for those loads.
+__device__ __forceinline__ void w2a8_big_step(v4i (&acc)[8][4], const int8_t *__restrict__ cur,
+                                              int8_t *__restrict__ nxt, const int8_t *const (&srca)[kXLoads],
+                                              const uint32_t *const (&srcb)[kXBLoads], int64_t koff_a,
+                                              int64_t koff_b, int wave, int wn, int lane, int aoff0) {
+#pragma unroll
+    for (int ii = 0; ii < kXLoads; ii++) lds_load16(srca[ii] + koff_a, nxt + 1024 * (kXLoads * wave + ii));
+#pragma unroll
+    for (int jj = 0; jj < kXBLoads; jj++)
+        lds_load16(srcb[jj] + koff_b, nxt + kXSlice + 1024 * (kXBLoads * wave + jj));
+    uint4 bw[4];
+#pragma unroll
+    for (int j = 0; j < 4; j++) bw[j] = *reinterpret_cast<const uint4 *>(cur + kXSlice + 1024 * (4 * wn + j) + 16 * lane);
+    const int fr = lane % 16, g4 = 4 * (lane / 16);
+    v4i fa[2][8];
+#pragma unroll
+    for (int t = 0; t < 4; t++) {
+        const int off = aoff0 + 16 * ((g4 + t) ^ fr);
+#pragma unroll
+        for (int i = 0; i < 8; i++) fa[t & 1][i] = *reinterpret_cast<const v4i *>(cur + off + i * 16 * XBK);
+#pragma unroll
+        for (int j = 0; j < 4; j++) {
+            const v4i b = unpack_tern(word_of(bw[j], t));
+#pragma unroll
+            for (int i = 0; i < 8; i++)
+                acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(fa[t & 1][i], b, acc[i][j], 0, 0, 0);
+        }
+    }
+}
+
+template <int OUT>
+__global__ __launch_bounds__(kXThreads, 1) void w2a8_big_kernel(const int8_t *__restrict__ xq,
+                                                                const float *__restrict__ pts,
+                                                                const int32_t *__restrict__ rowsum,
+                                                                const uint32_t *__restrict__ packed,
+                                                                const double *__restrict__ gamma,
+                                                                int64_t m, int64_t n, int64_t k,
+                                                                void *__restrict__ out, int tiles_m,
+                                                                int tiles_n) {
+    __shared__ __attribute__((aligned(1024))) int8_t smem[2 * kXStage];
+    const int lane = threadIdx.x % kWave, wave = wave_id();
+    const int wm = wave / 2, wn = wave % 2;
+    int tm, tn;
+    xcd_tile(blockIdx.x, tiles_m, tiles_n, kXGroupM, tm, tn);
+    const int64_t m0 = (int64_t)tm * XBM, n0 = (int64_t)tn * XBN;
+    const int64_t kblocks = k / XBK, nblocks = n / 16;
+
+    // A load ii of this wave fills LDS bytes [1024 (16 wave + ii), +1024) of
+    // the slice: chunk position lane % 16 of row 64 wave + 4 ii + lane / 16.
+    // B load jj fills fragment block 2 wave + jj of the tile's 8 column
+    // blocks, which is 1 KB of the packed weight in lane order.  Sources are
+    // given for k block 0; block kb adds kb * 256 bytes (A) or kb * 256 words (B).
+    const int8_t *srca[kXLoads];
+#pragma unroll
+    for (int ii = 0; ii < kXLoads; ii++) {
+        const int row = 64 * wave + 4 * ii + lane / 16;
+        const int c = (lane % 16) ^ (row & 15);
+        const int64_t r = m0 + row < m ? m0 + row : m - 1;
+        srca[ii] = xq + r * k + 16 * c;
+    }
+    const uint32_t *srcb[kXBLoads];
+#pragma unroll
+    for (int jj = 0; jj < kXBLoads; jj++) {
+        const int blk = kXBLoads * wave + jj;
+        const int64_t nb = n0 / 16 + blk < nblocks ? n0 / 16 + blk : nblocks - 1;
+        srcb[jj] = packed + nb * kblocks * 256 + 4 * lane;
+    }
+    // A fragment of step t, row block i: row 128 wm + 16 i + lane % 16,
+    // chunk 4 (lane / 16) + t, stored at chunk position ^ (lane % 16).
+    const int aoff0 = (128 * wm + lane % 16) * XBK;
+
+    v4i acc[8][4];
+#pragma unroll
+    for (int i = 0; i < 8; i++)
+#pragma unroll
+        for (int j = 0; j < 4; j++) acc[i][j] = v4i{0, 0, 0, 0};
+
+#pragma unroll
+    for (int ii = 0; ii < kXLoads; ii++) lds_load16(srca[ii], smem + 1024 * (kXLoads * wave + ii));
+#pragma unroll
+    for (int jj = 0; jj < kXBLoads; jj++) lds_load16(srcb[jj], smem + kXSlice + 1024 * (kXBLoads * wave + jj));
+    xs_wait_all();
+    __syncthreads();
+    for (int64_t kb = 0; kb < kblocks; kb++) {
+        const int cur = (int)(kb & 1);
+        // block kb + 1 streams into the other buffer (the last block reloads
+        // its own slice there, keeping the loop body free of branches)
+        const int64_t nxt = kb + 1 < kblocks ? kb + 1 : kb;
+        w2a8_big_step(acc, smem + cur * kXStage, smem + (cur ^ 1) * kXStage, srca, srcb, nxt * XBK, nxt * 256,
+                      wave, wn, lane, aoff0);
+        xs_wait_all();
+        __syncthreads();
+    }
+
+    // Epilogue through LDS: each wave converts its 128 x 64 sub-tile into an
+    // LDS tile (rows padded by 16 bytes, so the four row groups of one write
+    // fall in distinct banks), then writes whole 128- or 256-byte row segments
+    // to global memory, 16 bytes per lane.
+    int32_t *rs_lds = reinterpret_cast<int32_t *>(smem);
+    float *pts_lds = reinterpret_cast<float *>(smem) + XBM;
+    stage_rows<OUT>(pts, rowsum, m, m0, XBM, rs_lds, pts_lds);
+    __syncthreads();
+    constexpr int ES = OUT == OUT_I32 || OUT == OUT_F32 ? 4 : 2;   // output element bytes
+    constexpr int ROWB = 64 * ES;                                  // bytes of a sub-tile row
+    constexpr int PITCH = ROWB + 16;
+    int8_t *tile = smem + 2 * XBM * 4 + wave * 128 * PITCH;
+    const float g = OUT == OUT_I32 ? 0.0f : (float)gamma[0];  // gamma may be NULL for int32 output
+    // Lane l holds column l % 16 and rows 4(l/16) + r of each 16 x 16 block.
+#pragma unroll
+    for (int i = 0; i < 8; i++)
+#pragma unroll
+        for (int r = 0; r < 4; r++) {
+            const int lr = 16 * i + 4 * (lane / 16) + r;          // row within the sub-tile
+            const int local = 128 * wm + lr;
+            const float rf = OUT == OUT_I32 ? 0.0f : pts_lds[local];
+            const int32_t rsv = rs_lds[local];
+#pragma unroll
+            for (int j = 0; j < 4; j++) {
+                const int c = 16 * j + lane % 16;
+                const int32_t v = acc[i][j][r] - rsv;
+                int8_t *dst = tile + lr * PITCH + c * ES;
+                if constexpr (OUT == OUT_I32) *reinterpret_cast<int32_t *>(dst) = v;
+                else if constexpr (OUT == OUT_F32) *reinterpret_cast<float *>(dst) = __fmul_rn(__fmul_rn((float)v, rf), g);
+                else if constexpr (OUT == OUT_F16) *reinterpret_cast<uint16_t *>(dst) = f32_to_f16_rne(__fmul_rn(__fmul_rn((float)v, rf), g));
+                else *reinterpret_cast<uint16_t *>(dst) = f32_to_bf16_rne(__fmul_rn(__fmul_rn((float)v, rf), g));
+            }
+        }
+    // the wave reads back only its own sub-tile: a wave-local LDS ordering
+    // (all lanes' writes complete) is enough
+    __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0)
+    __builtin_amdgcn_wave_barrier();
+    constexpr int SEG = ROWB / 16;                 // 16-byte pieces per sub-tile row
+    constexpr int ROWS_PER = 64 / SEG;             // sub-tile rows per wave store
+    const int64_t col0 = n0 + 64 * wn;
+#pragma unroll
+    for (int q = 0; q < 128 / ROWS_PER; q++) {
+        const int lr = q * ROWS_PER + lane / SEG, piece = lane % SEG;
+        const uint4 v = *reinterpret_cast<const uint4 *>(tile + lr * PITCH + 16 * piece);
+        const int64_t row = m0 + 128 * wm + lr;
+        const int64_t col = col0 + piece * (16 / ES);
+        if (row < m && col < n) *reinterpret_cast<uint4 *>(static_cast<int8_t *>(out) + (row * n + col) * ES) = v;
     }
 }
 
@@ -214,6 +403,16 @@ __global__ __launch_bounds__(WAVES * 64) void w2a8_gemv_kernel(const int8_t *__r
     // Rows past m read row 0: an MFMA row only feeds its own output row,
     // which is never stored.  Column blocks past n likewise repeat the last.
     const int8_t *xrow = xq + (int64_t)(fr < m ? fr : 0) * k + 64 * (lane / 16);
+    // this lane's output rows 4(lane/16) + r: their code sums and scales are
+    // loaded now, so their latency hides behind the k loop
+    int32_t rsr[4];
+    float ptr[4];
+#pragma unroll
+    for (int r = 0; r < 4; r++) {
+        const int64_t row = 4 * (lane / 16) + r < m ? 4 * (lane / 16) + r : m - 1;
+        rsr[r] = rowsum[row];
+        ptr[r] = OUT == OUT_I32 ? 0.0f : pts[row];
+    }
 
     v4i acc[NBLK];
 #pragma unroll
@@ -251,9 +450,7 @@ __global__ __launch_bounds__(WAVES * 64) void w2a8_gemv_kernel(const int8_t *__r
 #pragma unroll
         for (int r = 0; r < 4; r++) {
             const int64_t row = 4 * (lane / 16) + r;
-            if (row < m)
-                epilogue_store<OUT>(out, row * n + col, s[r], rowsum[row],
-                                    OUT == OUT_I32 ? 0.0f : pts[row], g);
+            if (row < m) epilogue_store<OUT>(out, row * n + col, s[r], rsr[r], ptr[r], g);
         }
     }
 }
@@ -276,6 +473,12 @@ hipError_t launch_out(const int8_t *xq, const float *pts, const int32_t *rowsum,
         // HBM: 4 column blocks per workgroup over 8 waves, one k block per
         // register stage, is the fastest for every m from 1 to 16.
         return launch_gemv<4, 8, 1, OUT>(xq, pts, rowsum, packed, gamma, m, n, k, out, st);
+    }
+    if (m >= XBM) {
+        const int tiles_m = (int)((m + XBM - 1) / XBM), tiles_n = (int)((n + XBN - 1) / XBN);
+        hipLaunchKernelGGL((w2a8_big_kernel<OUT>), dim3((unsigned)(tiles_m * tiles_n)), dim3(kXThreads), 0, st, xq,
+                           pts, rowsum, packed, gamma, m, n, k, out, tiles_m, tiles_n);
+        return hipGetLastError();
     }
     dim3 grid((unsigned)((n + GBN - 1) / GBN), (unsigned)((m + GBM - 1) / GBM));
     hipLaunchKernelGGL((w2a8_gemm_kernel<OUT>), grid, dim3(kGThreads), 0, st, xq, pts, rowsum, packed,

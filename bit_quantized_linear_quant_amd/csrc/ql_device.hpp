@@ -17,6 +17,15 @@ constexpr int kWave = 64;
 
 typedef unsigned v4u __attribute__((ext_vector_type(4)));
 
+// 16 bytes per lane from global memory straight into LDS
+// (global_load_lds_dwordx4): lane l of the wave writes lds_base + 16 l.
+// lds_base must be the same for every lane of the wave.
+__device__ __forceinline__ void lds_load16(const void *src, void *lds_base) {
+    typedef __attribute__((address_space(1))) void gvoid;
+    typedef __attribute__((address_space(3))) void lvoid;
+    __builtin_amdgcn_global_load_lds((gvoid *)src, (lvoid *)lds_base, 16, 0, 0);
+}
+
 // Index of the calling wave in its workgroup, as a wave-uniform (scalar)
 // value, so that arithmetic on it runs on the scalar unit.
 __device__ __forceinline__ int wave_id() {
@@ -28,6 +37,23 @@ __device__ __forceinline__ int wave_id() {
 __device__ __forceinline__ uint4 load16_stream(const void *p) {
     const v4u t = __builtin_nontemporal_load(reinterpret_cast<const v4u *>(p));
     return make_uint4(t[0], t[1], t[2], t[3]);
+}
+
+// Workgroup id -> (tile row, tile column) for a grid of tiles_m x tiles_n
+// output tiles.  The hardware hands consecutive workgroup ids to the 8 XCDs in
+// turn; ids are first regrouped so each XCD receives a contiguous range of
+// tiles, then each range is walked group_m tile rows at a time, column by
+// column, so tiles running together on one XCD share A and B slices in its L2.
+__device__ __forceinline__ void xcd_tile(int b, int tiles_m, int tiles_n, int group_m, int &tm, int &tn) {
+    const int total = tiles_m * tiles_n;
+    int t = b;
+    if (total % 8 == 0) t = (b % 8) * (total / 8) + b / 8;
+    const int group = t / (group_m * tiles_n);
+    const int first = group * group_m;
+    const int rows = min(tiles_m - first, group_m);
+    const int within = t - group * group_m * tiles_n;
+    tm = first + within % rows;
+    tn = within / rows;
 }
 
 // Output element kinds of the epilogue.
