@@ -3,8 +3,9 @@
 // Ternary ("Class BitLinear" forward step 3; "Common Attention Utilities"
 // weight_quant and bake_ternary_weights): gamma' = max(mean|W|, eps) is an
 // fp64 sum over fixed 16384-element chunks (one workgroup each, fixed
-// per-thread order and a fixed shuffle tree), then a single workgroup sums
-// the chunk partials in a fixed order, so gamma' is identical on every call.
+// per-thread order and a fixed shuffle tree), then one 1024-thread workgroup
+// sums the chunk partials in a fixed order, so gamma' is identical on every
+// call.
 // The pack kernel compares |W| with gamma'/2 exactly in fp64 and writes one
 // 16-byte lane slice (four words) of the 2-bit layout per thread.
 //
@@ -38,6 +39,28 @@ __global__ __launch_bounds__(kPThreads) void absmean_partial_kernel(const float 
     __shared__ double red[kPThreads / kWave];
     const int64_t base = (int64_t)blockIdx.x * kChunk;
     double acc = 0.0;
+    if (base + kChunk <= count) {
+        // whole chunk: every load first (non-temporal: read once), then the
+        // adds in the same order as the ragged path below
+        float4 v[kChunkIters];
+#pragma unroll
+        for (int it = 0; it < kChunkIters; it++) {
+            const v4u t = __builtin_nontemporal_load(
+                reinterpret_cast<const v4u *>(w + base + ((int64_t)it * kPThreads + threadIdx.x) * 4));
+            v[it] = make_float4(__uint_as_float(t[0]), __uint_as_float(t[1]), __uint_as_float(t[2]),
+                                __uint_as_float(t[3]));
+        }
+#pragma unroll
+        for (int it = 0; it < kChunkIters; it++) {
+            acc += fabs((double)v[it].x);
+            acc += fabs((double)v[it].y);
+            acc += fabs((double)v[it].z);
+            acc += fabs((double)v[it].w);
+        }
+        const double s = block_sum_f64(acc, red);
+        if (threadIdx.x == 0) partial[blockIdx.x] = s;
+        return;
+    }
 #pragma unroll 4
     for (int it = 0; it < kChunkIters; it++) {
         const int64_t idx = base + ((int64_t)it * kPThreads + threadIdx.x) * 4;
@@ -56,15 +79,35 @@ __global__ __launch_bounds__(kPThreads) void absmean_partial_kernel(const float 
     if (threadIdx.x == 0) partial[blockIdx.x] = s;
 }
 
-__global__ __launch_bounds__(kPThreads) void absmean_final_kernel(const double *__restrict__ partial,
+// Sum of the chunk partials by one 1024-thread workgroup: thread t adds
+// partials t, t + 1024, ... in order (loaded 16 at a time, so the loads are in
+// flight together), then the 16 wave sums are added in wave order.
+constexpr int kFThreads = 1024;
+constexpr int kFBatch = 16;
+
+__global__ __launch_bounds__(kFThreads) void absmean_final_kernel(const double *__restrict__ partial,
                                                                   int64_t nparts, int64_t count,
                                                                   double eps,
                                                                   double *__restrict__ gamma) {
-    __shared__ double red[kPThreads / kWave];
+    __shared__ double red[kFThreads / kWave];
     double acc = 0.0;
-    for (int64_t i = threadIdx.x; i < nparts; i += kPThreads) acc += partial[i];
-    const double s = block_sum_f64(acc, red);
+    for (int64_t base = threadIdx.x; base < nparts; base += (int64_t)kFThreads * kFBatch) {
+        double v[kFBatch];
+#pragma unroll
+        for (int j = 0; j < kFBatch; j++) {
+            const int64_t i = base + (int64_t)j * kFThreads;
+            v[j] = i < nparts ? partial[i] : 0.0;
+        }
+#pragma unroll
+        for (int j = 0; j < kFBatch; j++) acc += v[j];
+    }
+    acc = wave_sum(acc);
+    if ((threadIdx.x % kWave) == 0) red[threadIdx.x / kWave] = acc;
+    __syncthreads();
     if (threadIdx.x == 0) {
+        double s = red[0];
+#pragma unroll
+        for (int i = 1; i < kFThreads / kWave; i++) s += red[i];
         const double g = s / (double)count;
         gamma[0] = g < eps ? eps : g;
     }
@@ -178,7 +221,7 @@ hipError_t launch_pack_ternary(const float *w, bool layout_nk, int64_t n, int64_
     const int64_t nparts = (int64_t)absmean_partial_count(count);
     hipLaunchKernelGGL(absmean_partial_kernel, dim3((unsigned)nparts), dim3(kPThreads), 0, st, w,
                        count, partials);
-    hipLaunchKernelGGL(absmean_final_kernel, dim3(1), dim3(kPThreads), 0, st, partials, nparts,
+    hipLaunchKernelGGL(absmean_final_kernel, dim3(1), dim3(kFThreads), 0, st, partials, nparts,
                        count, eps, gamma);
     const int64_t nslices = (n / 16) * (k / 256) * 64;
     if (layout_nk)

@@ -19,13 +19,13 @@ def absmean_rel_tol(count: int) -> float:
     The oracle's gamma is the exact sum of |W| rounded once, divided once
     (2 roundings).  The kernel sums |W| in fp64 along paths of at most
     64 sequential adds per thread (16384-element chunks over 256 threads),
-    8 tree levels per workgroup, ceil(chunks / 256) sequential adds per thread
-    of the final workgroup and 8 more tree levels, then divides once; a sum of
-    non-negative terms along a path of d adds is off by at most d units of
-    2^-53 relative.
+    6 shuffle levels and 3 wave adds per workgroup, then in one 1024-thread
+    workgroup ceil(chunks / 1024) sequential adds per thread, 6 shuffle levels
+    and 15 wave adds, then divides once; a sum of non-negative terms along a
+    path of d adds is off by at most d units of 2^-53 relative.
     """
     chunks = -(-count // 16384)
-    depth = 64 + 8 + -(-chunks // 256) + 8 + 1
+    depth = 64 + 6 + 3 + -(-chunks // 1024) + 6 + 15 + 1
     return (depth + 2) * 2.0 ** -53
 
 
