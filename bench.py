@@ -373,7 +373,7 @@ def main():
     res, d = bench_a4w4(args, ql, torch, synthetic)
     gemv = bench_decode(ql, torch, synthetic)
     gemv_src = kernel_source_hash(GEMV_KERNEL_SOURCES)
-    for m_str, key in (("1", "w2a8_gemv_m1_m4_28672x8192"), ("4", "w2a8_gemv_m1_m4_28672x8192"),
+    for m_str, key in (("1", "w2a8_gemv_m1_28672x8192"), ("4", "w2a8_gemv_m4_28672x8192"),
                        ("16", "w2a8_gemv_m16_28672x8192")):
         gemv["by_m"][m_str]["traffic"] = recorded_traffic(key, gemv_src)
     gemm_src = kernel_source_hash(GEMM_KERNEL_SOURCES)
