@@ -68,6 +68,7 @@ def _load():
             "oracle_unpack_int4_v1": (i32, [vp, i64, i64, vp]),
             "oracle_pack_int4_zeros": (i32, [vp, i64, i64, vp]),
             "oracle_grouped_int4": (i32, [vp, vp, vp, vp, i64, i64, i64, i64, vp, vp]),
+            "oracle_grouped_int4_i8": (i32, [vp, vp, vp, vp, vp, i64, i64, i64, i64, vp, vp]),
             "oracle_gemm_i8": (i32, [vp, vp, i32, i64, i64, i64, vp]),
             "oracle_dequant": (i32, [vp, vp, vp, i64, i64, vp]),
             "oracle_quant_int4_tensor": (i32, [vp, i64, f32, f32, vp]),
@@ -206,6 +207,29 @@ def grouped_int4(x, q, s, z, group_size: int):
     b = np.empty((m, n), np.float64)
     _check(_load().oracle_grouped_int4(_p(x), _p(q), _p(s), _p(z), group_size, m, n, k,
                                        _p(y), _p(b)), "grouped_int4")
+    return y, b
+
+
+def grouped_int4_i8(xq, pts, q, s, z, group_size: int):
+    """fp64 ``y[m,n] = pts[m] * sum_g s[n,g] * sum_{k in g} xq[m,k] * (q[n,k] - z[n,g])``.
+
+    "linear_4bit/mod.rs" module doc for the weights; the per-token int8
+    activation codes of "Class BitLinear" steps 2 and 5.  Group inner sums
+    are exact integers.  Also returns ``bound[m,n] = |pts[m]| * sum_k
+    |xq * s * (q - z)|``.
+    """
+    xq = _c(xq, np.int8)
+    pts = _c(pts, np.float32)
+    q = _c(q, np.uint8)
+    s = _c(s, np.float64)
+    z = _c(z, np.uint8)
+    m, k = xq.shape
+    n = q.shape[0]
+    assert q.shape == (n, k) and s.shape == z.shape == (n, k // group_size) and pts.shape == (m,)
+    y = np.empty((m, n), np.float64)
+    b = np.empty((m, n), np.float64)
+    _check(_load().oracle_grouped_int4_i8(_p(xq), _p(pts), _p(q), _p(s), _p(z), group_size, m, n, k,
+                                          _p(y), _p(b)), "grouped_int4_i8")
     return y, b
 
 

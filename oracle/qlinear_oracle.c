@@ -359,6 +359,42 @@ int oracle_grouped_int4(const double *x, const uint8_t *q, const double *s,
     return 0;
 }
 
+/*
+ * The same grouped affine INT4 linear with int8 activation codes and their
+ * per-token scale ([L4] module doc for the weight side; the per-token int8
+ * activation of [BL] steps 2 and 5 for the input side):
+ *   y[m][n] = pts[m] * sum_g s[n][g] * sum_{k in g} xq[m][k] * (q[n][k] - z[n][g])
+ * The inner sums are exact integers (int64); the rest is fp64.
+ *   bound[m][n] = |pts[m]| * sum_k |xq[m][k] * s[n][g(k)] * (q[n][k] - z[n][g(k)])|
+ */
+int oracle_grouped_int4_i8(const int8_t *xq, const float *pts, const uint8_t *q,
+                           const double *s, const uint8_t *z, int64_t group_size,
+                           int64_t m, int64_t n, int64_t k, double *y, double *bound)
+{
+    int64_t ng = k / group_size;
+#pragma omp parallel for schedule(static)
+    for (int64_t c = 0; c < n; c++) {
+        for (int64_t r = 0; r < m; r++) {
+            double acc = 0.0, ab = 0.0;
+            for (int64_t gi = 0; gi < ng; gi++) {
+                double sg = s[c * ng + gi];
+                int zg = z[c * ng + gi] & 15;
+                int64_t part = 0, apart = 0;
+                for (int64_t j = gi * group_size; j < (gi + 1) * group_size; j++) {
+                    int64_t d = (int64_t)xq[r * k + j] * ((int)(q[c * k + j] & 15) - zg);
+                    part += d;
+                    apart += d < 0 ? -d : d;
+                }
+                acc += sg * (double)part;
+                ab += fabs(sg) * (double)apart;
+            }
+            y[r * n + c] = (double)pts[r] * acc;
+            if (bound) bound[r * n + c] = fabs((double)pts[r]) * ab;
+        }
+    }
+    return 0;
+}
+
 /* ------------------------------------------------------------------ */
 /* O4: integer GEMM and the per-token dequant epilogue.                */
 /* ------------------------------------------------------------------ */

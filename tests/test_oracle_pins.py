@@ -308,6 +308,46 @@ def test_grouped_brute_force_dequant_then_matmul(g):
     assert np.array_equal(y2, 2 * y)
 
 
+def _grouped_i8_case(m, n, k, g, seed):
+    r = synthetic.rng(seed)
+    xq = r.integers(-127, 128, (m, k), dtype=np.int8)
+    pts = r.uniform(1e-3, 1e-2, m).astype(np.float32)
+    d = synthetic.grouped_int4(m, n, k, g, seed=seed)
+    return xq, pts, d["q"].numpy(), d["s"].float().numpy().astype(np.float64), d["z"].numpy()
+
+
+def test_grouped_i8_equals_fp_grouped_on_dequantized_activations():
+    """int8 codes times their per-token scale, fed to the fp64 grouped oracle, give the same y."""
+    xq, pts, q, s, z = _grouped_i8_case(5, 48, 256, 128, seed=41)
+    y, bound = oracle.grouped_int4_i8(xq, pts, q, s, z, 128)
+    x = xq.astype(np.float64) * pts.astype(np.float64)[:, None]
+    y2, bound2 = oracle.grouped_int4(x, q, s, z, 128)
+    assert np.all(np.abs(y - y2) <= 1e-12 * bound + 1e-300)
+    np.testing.assert_allclose(bound, bound2, rtol=1e-12)
+
+
+def test_grouped_i8_unit_scale_zero_offset_is_integer_matmul():
+    xq, _, q, s, z = _grouped_i8_case(4, 32, 256, 128, seed=42)
+    y, _ = oracle.grouped_int4_i8(xq, np.ones(4, np.float32), q, np.ones_like(s), np.zeros_like(z), 128)
+    assert np.array_equal(y, (xq.astype(np.int64) @ q.astype(np.int64).T).astype(np.float64))
+
+
+def test_grouped_i8_zero_point_equal_to_code_gives_zero():
+    xq, pts, _, s, z = _grouped_i8_case(3, 16, 256, 128, seed=43)
+    q = np.repeat(z, 128, axis=1)
+    y, _ = oracle.grouped_int4_i8(xq, pts, q, s, z, 128)
+    assert not y.any()
+
+
+@pytest.mark.parametrize("g", [128, 256])
+def test_grouped_i8_brute_force(g):
+    xq, pts, q, s, z = _grouped_i8_case(3, 16, 512, g, seed=44 + g)
+    y, _ = oracle.grouped_int4_i8(xq, pts, q, s, z, g)
+    w = np.repeat(s, g, axis=1) * (q.astype(np.float64) - np.repeat(z, g, axis=1))
+    ref = (xq.astype(np.float64) * pts.astype(np.float64)[:, None]) @ w.T
+    np.testing.assert_allclose(y, ref, rtol=1e-12, atol=1e-15)
+
+
 def test_int4_pack_round_trip_and_pairs():
     _, q, _, z, g = _grouped(n=48, k=384, g=128)
     packed = oracle.pack_int4(q)
