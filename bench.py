@@ -350,6 +350,16 @@ def bench_rows(ql, torch, synthetic):
         us, gbytes, "GB/s", PEAK_HBM_GBS, "hbm",
         f"{gbytes} B (packed weight, fp16 scales, packed zeros, fp16 x, fp16 out)",
         (512 * k // 2 + 512 * (k // gs) * 2.5 + m * k * 2 + m * 512 * 2) / t / 1e9, f"512 of {n} columns")
+    xqg, ptsg, _ = ql.qlinear_quant_act(xg)
+    us = time_graph(torch, lambda i: ql.qlinear_gemm_w4a8_grouped(xqg, pws[i % len(pws)], sc, pz, gs, n, out=outg,
+                                                                  per_token_scale=ptsg), 48)
+    gbytes8 = n * k // 2 + n * (k // gs) * 2 + n * (k // gs) // 2 + m * k + 4 * m + m * n * 2
+    xqn, ptsn, _ = oracle.quant_act(xgn)
+    t = time_cpu(lambda: oracle.grouped_int4_i8(xqn, ptsn, qn[:512], sn[:512], zn[:512], gs))
+    rows["a7i8_grouped_int4_int8_act_32x4096x11008_g128"] = _row(
+        us, gbytes8, "GB/s", PEAK_HBM_GBS, "hbm",
+        f"{gbytes8} B (packed weight, fp16 scales, packed zeros, int8 x codes and scales, fp16 out)",
+        (512 * k // 2 + 512 * (k // gs) * 2.5 + m * k + m * 512 * 2) / t / 1e9, f"512 of {n} columns")
     del pws
     return {"threads_oracle": threads, "rows": rows}
 

@@ -227,8 +227,14 @@ def qlinear_gemm_w2a8(xq, per_token_scale, rowsum, packed, gamma, n, out_dtype=t
 
 def qlinear_gemm_w4a8_grouped(x, packed_w, scales, packed_zeros, group_size, n, out_dtype=torch.float16,
                               out=None, per_token_scale=None, bias=None):
-    """Grouped affine INT4 linear with fp16 ``x[m,k]``; ``scales`` fp16 ``[n, k/group_size]``."""
+    """Grouped affine INT4 linear; ``scales`` fp16 ``[n, k/group_size]``.
+
+    ``x[m,k]`` is fp16 activations, or int8 activation codes with their fp32
+    ``per_token_scale[m]`` (from ``qlinear_quant_act``).
+    """
     _gpu(x, "x")
+    if x.dtype == torch.int8:
+        _need(_gpu(per_token_scale, "per_token_scale", torch.float32), 4 * x.shape[0], "per_token_scale")
     _gpu(packed_w, "packed_w")
     _gpu(scales, "scales", torch.float16)
     _gpu(packed_zeros, "packed_zeros")

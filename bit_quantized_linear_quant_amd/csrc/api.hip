@@ -159,21 +159,25 @@ ql_status qlinear_gemm_w4a8_grouped(const void *x, ql_dtype x_dtype, const float
                                     const uint32_t *packed_zeros, int64_t group_size, int64_t m, int64_t n,
                                     int64_t k, const void *bias, ql_dtype out_dtype, void *out,
                                     void *stream) {
-    (void)per_token_scale;
     if (!x || !packed_w || !scales || !packed_zeros || !out) return QL_ERR_NULL;
-    if (x_dtype == QL_I8) return QL_ERR_UNSUPPORTED;
-    if (x_dtype != QL_F16) return QL_ERR_DTYPE;
-    if (out_dtype != QL_F16 && out_dtype != QL_F32) return QL_ERR_DTYPE;
+    if (x_dtype != QL_F16 && x_dtype != QL_I8) return QL_ERR_DTYPE;
+    if (x_dtype == QL_I8 && !per_token_scale) return QL_ERR_NULL;
+    if (out_dtype != QL_F16 && out_dtype != QL_F32 && !(x_dtype == QL_I8 && out_dtype == QL_BF16))
+        return QL_ERR_DTYPE;
     if (bias) return QL_ERR_UNSUPPORTED;
     if (m < 1 || n < 16 || k < 128 || n % 16 || k % 128 || group_size < 128 || group_size % 128 ||
         k % group_size)
         return QL_ERR_SHAPE;
     if (!aligned16(x) || !aligned16(packed_w) || !aligned16(scales) || !aligned16(packed_zeros) ||
-        !aligned16(out))
+        !aligned16(out) || (per_token_scale && !aligned16(per_token_scale)))
         return QL_ERR_ALIGN;
+    const int ok = out_dtype == QL_F32 ? ql::OUT_F32 : out_dtype == QL_BF16 ? ql::OUT_BF16 : ql::OUT_F16;
+    if (x_dtype == QL_I8)
+        return hip_status(ql::launch_gemm_int4_grouped_i8(static_cast<const int8_t *>(x), per_token_scale,
+                                                          packed_w, scales, packed_zeros, group_size, m, n, k, ok,
+                                                          out, as_stream(stream)));
     return hip_status(ql::launch_gemm_int4_grouped(static_cast<const uint16_t *>(x), packed_w, scales,
-                                                   packed_zeros, group_size, m, n, k,
-                                                   out_dtype == QL_F32 ? ql::OUT_F32 : ql::OUT_F16, out,
+                                                   packed_zeros, group_size, m, n, k, ok, out,
                                                    as_stream(stream)));
 }
 

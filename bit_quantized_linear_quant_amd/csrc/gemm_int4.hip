@@ -101,7 +101,9 @@ __device__ __forceinline__ void compute_stage(const Stage<NBLK, RB> &st, v4f (&a
             for (int b = 0; b < RB; b++) p[b] = __builtin_amdgcn_mfma_f32_16x16x32_f16(st.a[b][t], wv, p[b], 0, 0, 0);
         }
 #pragma unroll
-        for (int b = 0; b < RB; b++) acc[b][j] += sc * p[b];
+        for (int b = 0; b < RB; b++)
+#pragma unroll
+            for (int r = 0; r < 4; r++) acc[b][j][r] = __builtin_fmaf(sc, p[b][r], acc[b][j][r]);
     }
 }
 
@@ -197,6 +199,181 @@ hipError_t launch_t(const uint16_t *x, const uint32_t *packed_w, const uint16_t 
     return launch_cfg<3, 8, 2, OUT>(x, packed_w, scales, packed_z, group_size, m, n, k, out, st);
 }
 
+// ---------------------------------------------------------------------------
+// int8 activation codes
+// ---------------------------------------------------------------------------
+// The same packed weights feed v_mfma_i32_16x16x64_i8.  Step s (0, 1) of a
+// 128-k block gives lane l the 16 k from 32(l/16) + 16s: the activation codes
+// are 16 contiguous bytes of its row, the weight operand is words 2s and
+// 2s + 1 of its fragment with the nibbles (codes 0..15) restored to k order
+// by two byte permutes per word.  The zero-point is applied afterwards:
+// sum x (q - z) = sum x q - z sum x, with sum x from one more MFMA against an
+// all-ones operand.  The block's exact int32 result is scaled by the group
+// scale in fp32; the per-token scale multiplies the final sum.
+
+// Natural-order int8 codes of the 8 k of one packed word.
+__device__ __forceinline__ void nibbles_to_bytes(uint32_t w, int &lo_k, int &hi_k) {
+    const uint32_t lo = w & 0x0F0F0F0Fu, hi = (w >> 4) & 0x0F0F0F0Fu;
+    lo_k = (int)__builtin_amdgcn_perm(hi, lo, 0x06040200u);   // k0 .. k0+3
+    hi_k = (int)__builtin_amdgcn_perm(hi, lo, 0x07050301u);   // k0+4 .. k0+7
+}
+
+__device__ __forceinline__ v4i weight_step(const uint4 &w, int s) {
+    int b0, b1, b2, b3;
+    nibbles_to_bytes(s == 0 ? w.x : w.z, b0, b1);
+    nibbles_to_bytes(s == 0 ? w.y : w.w, b2, b3);
+    return v4i{b0, b1, b2, b3};
+}
+
+template <int NBLK, int RB>
+struct StageI8 {
+    uint4 w[NBLK];
+    uint32_t s[NBLK], z[NBLK];
+    v4i a[RB][2];
+};
+
+template <int NBLK, int RB>
+__device__ __forceinline__ void load_stage_i8(StageI8<NBLK, RB> &st, const int8_t *const xrow[RB],
+                                              const uint32_t *__restrict__ packed_w,
+                                              const uint16_t *__restrict__ scales,
+                                              const uint32_t *__restrict__ packed_z, int64_t kb, int64_t nb0,
+                                              int64_t nblocks, int64_t kblocks, int64_t group_size,
+                                              int64_t groups, int64_t n, int lane) {
+    const int fr = lane % 16;
+    const int64_t kbc = kb < kblocks ? kb : kblocks - 1;
+    const int64_t g = kbc * 128 / group_size;
+#pragma unroll
+    for (int j = 0; j < NBLK; j++) {
+        const int64_t nbc = nb0 + j < nblocks ? nb0 + j : nblocks - 1;
+        const int64_t col = nbc * 16 + fr;
+        st.w[j] = load16_stream(packed_w + (nbc * kblocks + kbc) * 256 + 4 * lane);
+        st.s[j] = scales[col * groups + g];
+        st.z[j] = packed_z[g * (n / 8) + col / 8] >> (4 * (col % 8));
+    }
+#pragma unroll
+    for (int b = 0; b < RB; b++)
+#pragma unroll
+        for (int s = 0; s < 2; s++) st.a[b][s] = *reinterpret_cast<const v4i *>(xrow[b] + kbc * 128 + 16 * s);
+}
+
+template <int NBLK, int RB>
+__device__ __forceinline__ void compute_stage_i8(const StageI8<NBLK, RB> &st, v4f (&acc)[RB][NBLK], int64_t nb0,
+                                                 int64_t nblocks) {
+    const v4i ones = v4i{0x01010101, 0x01010101, 0x01010101, 0x01010101};
+    v4i sx[RB];
+#pragma unroll
+    for (int b = 0; b < RB; b++) {
+        sx[b] = __builtin_amdgcn_mfma_i32_16x16x64_i8(st.a[b][0], ones, v4i{0, 0, 0, 0}, 0, 0, 0);
+        sx[b] = __builtin_amdgcn_mfma_i32_16x16x64_i8(st.a[b][1], ones, sx[b], 0, 0, 0);
+    }
+#pragma unroll
+    for (int j = 0; j < NBLK; j++) {
+        const float sc = nb0 + j < nblocks ? f16_bits_to_f32(st.s[j]) : 0.0f;
+        const int z = (int)(st.z[j] & 15u);
+        const v4i w0 = weight_step(st.w[j], 0), w1 = weight_step(st.w[j], 1);
+#pragma unroll
+        for (int b = 0; b < RB; b++) {
+            v4i p = __builtin_amdgcn_mfma_i32_16x16x64_i8(st.a[b][0], w0, v4i{0, 0, 0, 0}, 0, 0, 0);
+            p = __builtin_amdgcn_mfma_i32_16x16x64_i8(st.a[b][1], w1, p, 0, 0, 0);
+#pragma unroll
+            for (int r = 0; r < 4; r++) acc[b][j][r] = __builtin_fmaf(sc, (float)(p[r] - z * sx[b][r]), acc[b][j][r]);
+        }
+    }
+}
+
+template <int NBLK, int WAVES, int RB, int OUT>
+__global__ __launch_bounds__(WAVES * 64) void int4_grouped_i8_kernel(const int8_t *__restrict__ xq,
+                                                                     const float *__restrict__ pts,
+                                                                     const uint32_t *__restrict__ packed_w,
+                                                                     const uint16_t *__restrict__ scales,
+                                                                     const uint32_t *__restrict__ packed_z,
+                                                                     int64_t group_size, int64_t m, int64_t n,
+                                                                     int64_t k, void *__restrict__ out) {
+    __shared__ v4f red[WAVES][RB * NBLK][kWave];
+    const int lane = threadIdx.x % kWave, wave = wave_id();
+    const int64_t nb0 = (int64_t)blockIdx.x * NBLK;
+    const int64_t row0 = (int64_t)blockIdx.y * 16 * RB;
+    const int64_t nblocks = n / 16, kblocks = k / 128, groups = k / group_size;
+    const int fr = lane % 16;
+    // Rows past m read row 0: an MFMA row only feeds its own output row.
+    const int8_t *xrow[RB];
+    float prow[RB][4];
+#pragma unroll
+    for (int b = 0; b < RB; b++) {
+        const int64_t r = row0 + 16 * b + fr;
+        xrow[b] = xq + (r < m ? r : 0) * k + 32 * (lane / 16);
+#pragma unroll
+        for (int q = 0; q < 4; q++) {
+            const int64_t orow = row0 + 16 * b + 4 * (lane / 16) + q;
+            prow[b][q] = pts[orow < m ? orow : m - 1];
+        }
+    }
+
+    v4f acc[RB][NBLK];
+#pragma unroll
+    for (int b = 0; b < RB; b++)
+#pragma unroll
+        for (int j = 0; j < NBLK; j++) acc[b][j] = v4f{0.f, 0.f, 0.f, 0.f};
+
+    StageI8<NBLK, RB> s0, s1;
+    int64_t kb = wave;
+    load_stage_i8(s0, xrow, packed_w, scales, packed_z, kb, nb0, nblocks, kblocks, group_size, groups, n, lane);
+    while (kb < kblocks) {
+        const int64_t kb1 = kb + WAVES;
+        if (kb1 < kblocks)
+            load_stage_i8(s1, xrow, packed_w, scales, packed_z, kb1, nb0, nblocks, kblocks, group_size, groups,
+                          n, lane);
+        compute_stage_i8(s0, acc, nb0, nblocks);
+        if (kb1 >= kblocks) break;
+        const int64_t kb2 = kb1 + WAVES;
+        if (kb2 < kblocks)
+            load_stage_i8(s0, xrow, packed_w, scales, packed_z, kb2, nb0, nblocks, kblocks, group_size, groups,
+                          n, lane);
+        compute_stage_i8(s1, acc, nb0, nblocks);
+        kb = kb2;
+    }
+
+#pragma unroll
+    for (int b = 0; b < RB; b++)
+#pragma unroll
+        for (int j = 0; j < NBLK; j++) red[wave][b * NBLK + j][lane] = acc[b][j];
+    __syncthreads();
+    for (int e = wave; e < RB * NBLK; e += WAVES) {
+        const int b = e / NBLK, j = e % NBLK;
+        const int64_t nb = nb0 + j;
+        if (nb >= nblocks) continue;
+        v4f s = red[0][e][lane];
+#pragma unroll
+        for (int w = 1; w < WAVES; w++) s += red[w][e][lane];
+        const int64_t col = nb * 16 + fr;
+#pragma unroll
+        for (int r = 0; r < 4; r++) {
+            const int64_t row = row0 + b * 16 + 4 * (lane / 16) + r;
+            if (row < m) store_out<OUT>(out, row * n + col, __fmul_rn(s[r], prow[b][r]));
+        }
+    }
+}
+
+template <int NBLK, int WAVES, int RB, int OUT>
+hipError_t launch_cfg_i8(const int8_t *xq, const float *pts, const uint32_t *packed_w, const uint16_t *scales,
+                         const uint32_t *packed_z, int64_t group_size, int64_t m, int64_t n, int64_t k, void *out,
+                         hipStream_t st) {
+    const int64_t nblocks = n / 16;
+    dim3 grid((unsigned)((nblocks + NBLK - 1) / NBLK), (unsigned)((m + 16 * RB - 1) / (16 * RB)));
+    hipLaunchKernelGGL((int4_grouped_i8_kernel<NBLK, WAVES, RB, OUT>), grid, dim3(WAVES * 64), 0, st, xq, pts,
+                       packed_w, scales, packed_z, group_size, m, n, k, out);
+    return hipGetLastError();
+}
+
+template <int OUT>
+hipError_t launch_i8_t(const int8_t *xq, const float *pts, const uint32_t *packed_w, const uint16_t *scales,
+                       const uint32_t *packed_z, int64_t group_size, int64_t m, int64_t n, int64_t k, void *out,
+                       hipStream_t st) {
+    if (m <= 16)
+        return launch_cfg_i8<3, 8, 1, OUT>(xq, pts, packed_w, scales, packed_z, group_size, m, n, k, out, st);
+    return launch_cfg_i8<3, 8, 2, OUT>(xq, pts, packed_w, scales, packed_z, group_size, m, n, k, out, st);
+}
+
 }  // namespace
 
 hipError_t launch_gemm_int4_grouped(const uint16_t *x, const uint32_t *packed_w, const uint16_t *scales,
@@ -206,6 +383,21 @@ hipError_t launch_gemm_int4_grouped(const uint16_t *x, const uint32_t *packed_w,
     if (out_kind == OUT_F32)
         return launch_t<OUT_F32>(x, packed_w, scales, packed_zeros, group_size, m, n, k, out, st);
     return launch_t<OUT_F16>(x, packed_w, scales, packed_zeros, group_size, m, n, k, out, st);
+}
+
+}  // namespace ql
+
+namespace ql {
+
+hipError_t launch_gemm_int4_grouped_i8(const int8_t *xq, const float *pts, const uint32_t *packed_w,
+                                       const uint16_t *scales, const uint32_t *packed_zeros, int64_t group_size,
+                                       int64_t m, int64_t n, int64_t k, int out_kind, void *out, hipStream_t st) {
+    if ((m + 31) / 32 > 65535) return hipErrorInvalidValue;
+    switch (out_kind) {
+        case OUT_F32: return launch_i8_t<OUT_F32>(xq, pts, packed_w, scales, packed_zeros, group_size, m, n, k, out, st);
+        case OUT_BF16: return launch_i8_t<OUT_BF16>(xq, pts, packed_w, scales, packed_zeros, group_size, m, n, k, out, st);
+        default: return launch_i8_t<OUT_F16>(xq, pts, packed_w, scales, packed_zeros, group_size, m, n, k, out, st);
+    }
 }
 
 }  // namespace ql

@@ -81,8 +81,12 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
 }
 
 // fp32 -> fp16, round to nearest, ties to even (v_cvt_f16_f32 under the
-// default rounding mode); overflow gives +-inf.
+// default rounding mode); overflow gives +-inf.  The empty asm makes `f` an
+// fp32 value in a register first, so the compiler cannot fold the product
+// that produced it into a mixed-precision multiply that rounds once to fp16:
+// the output is exactly the fp32 result rounded once more.
 __device__ __forceinline__ uint16_t f32_to_f16_rne(float f) {
+    asm volatile("" : "+v"(f));
     return __builtin_bit_cast(uint16_t, (_Float16)f);
 }
 

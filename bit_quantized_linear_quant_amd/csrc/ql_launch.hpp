@@ -55,5 +55,8 @@ hipError_t launch_gemm_int4_grouped(const uint16_t *x, const uint32_t *packed_w,
                                     const uint16_t *scales, const uint32_t *packed_zeros,
                                     int64_t group_size, int64_t m, int64_t n, int64_t k,
                                     int out_kind, void *out, hipStream_t st);
+hipError_t launch_gemm_int4_grouped_i8(const int8_t *xq, const float *pts, const uint32_t *packed_w,
+                                       const uint16_t *scales, const uint32_t *packed_zeros, int64_t group_size,
+                                       int64_t m, int64_t n, int64_t k, int out_kind, void *out, hipStream_t st);
 
 }  // namespace ql

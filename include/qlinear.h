@@ -213,17 +213,22 @@ ql_status qlinear_gemm_w2a8(const int8_t *xq, const float *per_token_scale,
 /*
  * Grouped affine INT4 linear ([L4] module doc: the packed u32 weight is
  * unpacked inside the k loop with its per-group scale and zero-point; no
- * dequantized weight buffer is written):
- *   out[m][n] = sum_g s[n][g] * sum_{k in g} x[m][k] * (q[n][k] - z[n][g])
- *   x [m, k] QL_F16 (x_dtype; QL_I8 activations are not implemented and
- *     return QL_ERR_UNSUPPORTED; per_token_scale is reserved for them);
+ * dequantized weight buffer is written).  Two activation kinds:
+ *   x_dtype QL_F16: x [m, k] fp16 activations,
+ *     out[m][n] = sum_g s[n][g] * sum_{k in g} x[m][k] * (q[n][k] - z[n][g]);
+ *     (q - z) is formed exactly in fp16, products accumulate in fp32 per
+ *     128-k block and each block's partial sum is scaled once.
+ *     per_token_scale is ignored.  out QL_F16, or QL_F32 for the value before
+ *     rounding.
+ *   x_dtype QL_I8: x [m, k] int8 activation codes with per_token_scale [m]
+ *     fp32 (qlinear_quant_act; [BL] steps 2 and 5),
+ *     out[m][n] = pts[m] * sum_g s[n][g] * sum_{k in g} xq[m][k] * (q[n][k] - z[n][g]);
+ *     each 128-k block's integer sum is exact (int32), scaled by s in fp32;
+ *     pts multiplies the final sum.  out QL_F16, QL_BF16 or QL_F32.
  *   packed_w from qlinear_pack_int4(QL_INT4_WEIGHT);
  *   scales [n, k/group_size] fp16 (row-major, one per column and group);
  *   packed_zeros from qlinear_pack_int4(QL_INT4_ZEROS) of z [n, groups];
- *   bias must be NULL (not implemented);
- *   out [m, n] QL_F16, or QL_F32 for the value before rounding.
- * (q - z) is formed exactly in fp16, products accumulate in fp32 per group
- * and each group's partial sum is scaled once.
+ *   bias must be NULL (not implemented: QL_ERR_UNSUPPORTED).
  * n % 16 == 0, k % 128 == 0, group_size % 128 == 0, k % group_size == 0.
  */
 ql_status qlinear_gemm_w4a8_grouped(const void *x, ql_dtype x_dtype,

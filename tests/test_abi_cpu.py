@@ -104,7 +104,10 @@ def test_gemm_validation(L):
     assert w2(A, A, A, A, A, 1, 16, 128, ql.QL_BF16, A, NULL) == -2
     assert w2(A, A, A, U, A, 1, 16, 256, ql.QL_BF16, A, NULL) == -4
     g4 = L.qlinear_gemm_w4a8_grouped
-    assert g4(A, ql.QL_I8, A, A, A, A, 128, 1, 16, 128, NULL, ql.QL_F16, A, NULL) == -6
+    assert g4(A, ql.QL_I8, NULL, A, A, A, 128, 1, 16, 128, NULL, ql.QL_F16, A, NULL) == -1  # needs pts
+    assert g4(A, ql.QL_I8, U, A, A, A, 128, 1, 16, 128, NULL, ql.QL_F16, A, NULL) == -4
+    assert g4(A, ql.QL_I8, A, A, A, A, 128, 1, 16, 128, NULL, ql.QL_I32, A, NULL) == -3
+    assert g4(A, ql.QL_U8, A, A, A, A, 128, 1, 16, 128, NULL, ql.QL_F16, A, NULL) == -3
     assert g4(A, ql.QL_F16, NULL, A, A, A, 64, 1, 16, 128, NULL, ql.QL_F16, A, NULL) == -2
     assert g4(A, ql.QL_F16, NULL, A, A, A, 256, 1, 16, 384, NULL, ql.QL_F16, A, NULL) == -2
     assert g4(A, ql.QL_F16, NULL, A, A, A, 128, 1, 16, 128, A, ql.QL_F16, A, NULL) == -6  # bias

@@ -137,6 +137,24 @@ def test_grouped_int4_full_workload():
     assert torch.equal(o16, o32.to(torch.float16))
 
 
+def test_grouped_int4_i8_full_shape():
+    """The grouped INT4 weights with int8 activation codes (quantized from the fp16
+    activations of the same workload) at 32x4096x11008, g = 128."""
+    d = synthetic.grouped_int4()
+    m, n, k, gs = 32, 11008, 4096, d["group_size"]
+    xq_ref, pts_ref, _ = oracle.quant_act(d["x"].float().numpy())
+    y, bound = oracle.grouped_int4_i8(xq_ref, pts_ref, d["q"].numpy(), d["s"].float().numpy(), d["z"].numpy(), gs)
+    xq, pts, _ = ql.qlinear_quant_act(_cuda(d["x"]))
+    pw = ql.qlinear_pack_int4(_cuda(d["q"]), ql.QL_INT4_WEIGHT)
+    pz = ql.qlinear_pack_int4(_cuda(d["z"]), ql.QL_INT4_ZEROS)
+    o16 = poison((m, n), torch.float16)
+    ql.qlinear_gemm_w4a8_grouped(xq, pw, _cuda(d["s"]), pz, gs, n, out=o16, per_token_scale=pts)
+    torch.cuda.synchronize()
+    assert_equal(xq, xq_ref, "activation codes")
+    err = np.abs(to_np(o16).astype(np.float64) - y)
+    assert np.all(err <= 1e-3 * bound), f"grouped int8 fp16: max err/bound {np.max(err / bound)}"
+
+
 def test_a4w4_full_workload():
     m = n = k = 8192
     d = synthetic.a4w4(m, n, k)

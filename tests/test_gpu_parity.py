@@ -278,6 +278,71 @@ def test_grouped_int4_zero_point_equals_code_gives_zero():
     assert torch.count_nonzero(o).item() == 0
 
 
+def _grouped_i8_inputs(m, n, k, g, seed):
+    d = synthetic.grouped_int4(m, n, k, g, seed=seed)
+    r = synthetic.rng(seed + 17)
+    xq = torch.from_numpy(r.integers(-127, 128, (m, k), dtype=np.int8))
+    pts = torch.from_numpy(r.uniform(1e-3, 1e-2, m).astype(np.float32))
+    return xq, pts, d["q"], d["s"], d["z"]
+
+
+@pytest.mark.parametrize("m,n,k,g", [(1, 48, 256, 128), (5, 400, 512, 128), (16, 64, 256, 128),
+                                     (17, 400, 512, 256), (32, 400, 512, 128), (40, 64, 384, 128),
+                                     (3, 32, 1024, 1024)])
+def test_grouped_int4_i8_parity(m, n, k, g):
+    """int8 activation codes: fp32 output within the arithmetic's bound, 16-bit outputs
+    within the grouped bar and equal to the fp32 output rounded once."""
+    xq, pts, q, s, z = _grouped_i8_inputs(m, n, k, g, seed=900 + m + n + k)
+    y, bound = oracle.grouped_int4_i8(xq.numpy(), pts.numpy(), q.numpy(), s.float().numpy(), z.numpy(), g)
+    pw = ql.qlinear_pack_int4(_cuda(q), ql.QL_INT4_WEIGHT)
+    pz = ql.qlinear_pack_int4(_cuda(z), ql.QL_INT4_ZEROS)
+    outs = {}
+    for dt in (torch.float32, torch.float16, torch.bfloat16):
+        o = poison((m, n), dt)
+        ql.qlinear_gemm_w4a8_grouped(_cuda(xq), pw, _cuda(s), pz, g, n, out_dtype=dt, out=o,
+                                     per_token_scale=_cuda(pts))
+        outs[dt] = o
+    _sync()
+    # exact int32 block sums; at most k/128 + 2 fp32 roundings of partial sums bounded by `bound`
+    err32 = np.abs(to_np(outs[torch.float32]).astype(np.float64) - y)
+    assert np.all(err32 <= 2.0 ** -18 * bound + 1e-30), f"fp32: max err/bound {np.max(err32 / bound)}"
+    for dt in (torch.float16, torch.bfloat16):
+        err = np.abs(to_np(outs[dt]).astype(np.float64) - y)
+        assert np.all(err <= 1e-3 * bound), f"{dt}: max err/bound {np.max(err / bound)}"
+        assert torch.equal(outs[dt], outs[torch.float32].to(dt))
+
+
+def test_grouped_int4_i8_zero_point_equals_code_gives_zero():
+    m, n, k, g = 4, 32, 256, 128
+    xq, pts, _, s, z = _grouped_i8_inputs(m, n, k, g, seed=19)
+    q = torch.repeat_interleave(z, g, dim=1).contiguous()
+    pw = ql.qlinear_pack_int4(_cuda(q), ql.QL_INT4_WEIGHT)
+    pz = ql.qlinear_pack_int4(_cuda(z), ql.QL_INT4_ZEROS)
+    o = ql.qlinear_gemm_w4a8_grouped(_cuda(xq), pw, _cuda(s), pz, g, n, out_dtype=torch.float32,
+                                     per_token_scale=_cuda(pts))
+    _sync()
+    assert torch.count_nonzero(o).item() == 0
+
+
+def test_grouped_int4_i8_extreme_codes():
+    """All activation codes -127 or 127 and all weight codes 0 or 15 with zero-point 0 or 15."""
+    m, n, k, g = 16, 32, 512, 128
+    r = synthetic.rng(23)
+    xq = torch.from_numpy(np.where(r.random((m, k)) < 0.5, -127, 127).astype(np.int8))
+    q = torch.from_numpy(np.where(r.random((n, k)) < 0.5, 0, 15).astype(np.uint8))
+    z = torch.from_numpy(np.where(r.random((n, k // g)) < 0.5, 0, 15).astype(np.uint8))
+    s = torch.ones((n, k // g), dtype=torch.float16)
+    pts = torch.ones(m, dtype=torch.float32)
+    y, _ = oracle.grouped_int4_i8(xq.numpy(), pts.numpy(), q.numpy(), s.float().numpy(), z.numpy(), g)
+    pw = ql.qlinear_pack_int4(_cuda(q), ql.QL_INT4_WEIGHT)
+    pz = ql.qlinear_pack_int4(_cuda(z), ql.QL_INT4_ZEROS)
+    o = ql.qlinear_gemm_w4a8_grouped(_cuda(xq), pw, _cuda(s), pz, g, n, out_dtype=torch.float32,
+                                     per_token_scale=_cuda(pts))
+    _sync()
+    # every term is an integer and the sums stay below 2^24: exact in fp32
+    assert np.array_equal(to_np(o).astype(np.float64), y)
+
+
 # ---------------------------------------------------------------------------
 # A4W4
 # ---------------------------------------------------------------------------
