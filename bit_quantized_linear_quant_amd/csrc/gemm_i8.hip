@@ -4,19 +4,21 @@
 //
 // Two kernels share the epilogue:
 //
-// gemm_i8_big_kernel -- large products with [n][k] weights and k % 128 == 0
+// gemm_i8_big_kernel -- large products with [n][k] weights and k % 64 == 0
 //   (the 8192^3 A4W4 product).  A 256-thread workgroup owns a 256 x 256
 //   output tile, each wave a 128 x 128 quarter held as 4 x 4 blocks of
 //   v_mfma_i32_32x32x32_i8 (256 int32 accumulators per lane, one wave per
-//   SIMD).  A and B k-slices move from HBM straight into LDS with
-//   global_load_lds_dwordx4 (no register staging), double-buffered so the
-//   next slice streams in while the matrix cores consume the current one;
-//   one barrier per slice.  In LDS each 16-byte chunk c of row r sits at
-//   chunk position c ^ swz(r), which puts the 16 rows read together by a
-//   fragment load in distinct bank groups.  Tiles are ordered so that each
-//   XCD (workgroup id mod 8) walks its own band of tile rows, four rows at a
-//   time, so concurrently running tiles share A and B slices in that XCD's
-//   L2.  Rows past m or n are loaded clamped and never stored.
+//   SIMD).  64-byte k-slices of A and B move from HBM straight into LDS with
+//   global_load_lds_dwordx4 (no register staging) through a ring of three
+//   slices, so two slices stream in while the matrix cores consume the
+//   third; one explicit vmcnt wait and one barrier per slice.  In LDS each
+//   16-byte chunk c of row r sits at chunk position c ^ swz(r), which puts
+//   the 16 rows read together by a fragment load in distinct bank groups.
+//   Tiles are ordered so that each XCD (workgroup id mod 8) walks its own
+//   band of tile rows, four rows at a time, so concurrently running tiles
+//   share A and B slices in that XCD's L2.  Rows past m or n are loaded
+//   clamped and never stored.  16-bit outputs leave through a padded LDS
+//   tile as whole row segments.
 //
 // gemm_i8_kernel -- everything else (any m, n, k >= 1, weights [k][n] or
 //   [n][k]): 128 x 128 tiles, 2 x 2 waves of 64 x 64 in 16x16x64 MFMA blocks,
@@ -99,20 +101,72 @@ __device__ __forceinline__ int swz(int r) {
     else return (r & 7) ^ ((r >> 3) & 3);
 }
 
-template <int BK, int EPI, int OUT>
+template <int BK>
+struct BigTile {
+    static constexpr int CH = BK / 16;                // 16-byte chunks per LDS row
+    static constexpr int TILE = LB * BK;              // bytes of one A or B slice
+    static constexpr int PER_WAVE = TILE / 1024 / 4;  // 1 KB direct loads per wave per slice and operand
+    static constexpr int S = BK / 32;                 // 32-k MFMA steps per slice
+};
+
+// One k-slice: the direct loads of a later slice into `nxt`, then the MFMAs of
+// `cur`, each step's fragments read from LDS while the previous step's
+// MFMAs issue.  `cur` and `nxt` are distinct restrict pointers, so the
+// compiler does not make the LDS reads of `cur` wait for the loads into `nxt`.
+template <int BK>
+__device__ __forceinline__ void big_slice(v16i (&acc)[4][4], const int8_t *__restrict__ cur,
+                                          int8_t *__restrict__ nxt, const int8_t *const (&srcA)[BigTile<BK>::PER_WAVE],
+                                          const int8_t *const (&srcB)[BigTile<BK>::PER_WAVE], int64_t nxt_k0,
+                                          const int (&offA)[BigTile<BK>::S], const int (&offB)[BigTile<BK>::S],
+                                          int wave) {
+    constexpr int CH = BigTile<BK>::CH, TILE = BigTile<BK>::TILE, PER_WAVE = BigTile<BK>::PER_WAVE;
+    constexpr int S = BigTile<BK>::S;
+#pragma unroll
+    for (int ii = 0; ii < PER_WAVE; ii++) {
+        const int inst = wave * PER_WAVE + ii;
+        lds_load16(srcA[ii] + nxt_k0, nxt + 1024 * inst);
+        lds_load16(srcB[ii] + nxt_k0, nxt + TILE + 1024 * inst);
+    }
+    v4i fa[2][4], fb[2][4];
+    auto frags = [&](int s) {
+#pragma unroll
+        for (int i = 0; i < 4; i++) fa[s & 1][i] = *reinterpret_cast<const v4i *>(cur + offA[s] + i * 32 * CH * 16);
+#pragma unroll
+        for (int j = 0; j < 4; j++) fb[s & 1][j] = *reinterpret_cast<const v4i *>(cur + TILE + offB[s] + j * 32 * CH * 16);
+    };
+    frags(0);
+#pragma unroll
+    for (int s = 0; s < S; s++) {
+        if (s + 1 < S) frags(s + 1);
+#pragma unroll
+        for (int i = 0; i < 4; i++)
+#pragma unroll
+            for (int j = 0; j < 4; j++)
+                acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fa[s & 1][i], fb[s & 1][j], acc[i][j], 0, 0, 0);
+        // matrix-core issue interleaved with the next step's LDS reads
+        if (s + 1 < S) {
+#pragma unroll
+            for (int q = 0; q < 8; q++) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            }
+            __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+        }
+    }
+}
+
+template <int BK, int NBUF, int EPI, int OUT>
 __global__ __launch_bounds__(LThreads, 1) void gemm_i8_big_kernel(Params p, int tiles_m, int tiles_n) {
-    constexpr int CH = BK / 16;                 // 16-byte chunks per LDS row
-    constexpr int TILE = LB * BK;               // bytes of one A or B slice
-    constexpr int PER_WAVE = TILE / 1024 / 4;   // 1 KB direct loads per wave per slice and operand
-    constexpr int S = BK / 32;                  // 32-k MFMA steps per slice
-    static_assert(S % 2 == 0, "fragment double buffer assumes an even step count");
-    // main loop: two A and two B slices; epilogue: 1 KB of row factors, then
-    // one padded 128 x 128 output sub-tile per wave (2-byte outputs)
+    constexpr int CH = BigTile<BK>::CH, TILE = BigTile<BK>::TILE, PER_WAVE = BigTile<BK>::PER_WAVE;
+    constexpr int S = BigTile<BK>::S;
+    constexpr int STAGE = 2 * TILE;
+    // main loop: a ring of NBUF (A, B) slices; epilogue: 1 KB of row factors,
+    // then one padded 128 x 128 output sub-tile per wave (2-byte outputs)
     constexpr int EPITCH = 128 * 2 + 16;
-    constexpr int SMEM = 2 * 2 * TILE > 1024 + 4 * 128 * EPITCH ? 2 * 2 * TILE : 1024 + 4 * 128 * EPITCH;
+    constexpr int SMEM = NBUF * STAGE > 1024 + 4 * 128 * EPITCH ? NBUF * STAGE : 1024 + 4 * 128 * EPITCH;
     __shared__ __attribute__((aligned(1024))) int8_t smem[SMEM];
 
-    const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+    const int lane = threadIdx.x % kWave, wave = wave_id();
     const int wm = wave / 2, wn = wave % 2;
     int tm, tn;
     xcd_tile(blockIdx.x, tiles_m, tiles_n, kGroupM, tm, tn);
@@ -120,7 +174,7 @@ __global__ __launch_bounds__(LThreads, 1) void gemm_i8_big_kernel(Params p, int 
     const int64_t K = p.k;
     const int64_t nk = K / BK;
 
-    // Global source of each direct load issued by this lane.
+    // Global source of each direct load issued by this lane (for k = 0).
     const int8_t *srcA[PER_WAVE];
     const int8_t *srcB[PER_WAVE];
 #pragma unroll
@@ -132,17 +186,6 @@ __global__ __launch_bounds__(LThreads, 1) void gemm_i8_big_kernel(Params p, int 
         srcA[ii] = p.x + ra * K + 16 * c;
         srcB[ii] = p.w + rb * K + 16 * c;
     }
-    auto issue = [&](int buf, int64_t k0) {
-        int8_t *As = smem + buf * 2 * TILE;
-        int8_t *Bs = As + TILE;
-#pragma unroll
-        for (int ii = 0; ii < PER_WAVE; ii++) {
-            const int inst = wave * PER_WAVE + ii;
-            __builtin_amdgcn_global_load_lds((glb_void *)(srcA[ii] + k0), (lds_void *)(As + 1024 * inst), 16, 0, 0);
-            __builtin_amdgcn_global_load_lds((glb_void *)(srcB[ii] + k0), (lds_void *)(Bs + 1024 * inst), 16, 0, 0);
-        }
-    };
-
     // LDS byte offsets of this lane's fragments: block row 32i + lane%32,
     // chunk 2s + lane/32.  swz depends only on the low 5 row bits, so the
     // offset of block i is that of block 0 plus 32 rows.
@@ -155,13 +198,6 @@ __global__ __launch_bounds__(LThreads, 1) void gemm_i8_big_kernel(Params p, int 
         offA[s] = 16 * (CH * ra + (c ^ swz<CH>(ra)));
         offB[s] = 16 * (CH * rb + (c ^ swz<CH>(rb)));
     }
-    auto frags = [&](v4i (&a)[4], v4i (&b)[4], const int8_t *As, int s) {
-        const int8_t *Bs = As + TILE;
-#pragma unroll
-        for (int i = 0; i < 4; i++) a[i] = *reinterpret_cast<const v4i *>(As + offA[s] + i * 32 * CH * 16);
-#pragma unroll
-        for (int j = 0; j < 4; j++) b[j] = *reinterpret_cast<const v4i *>(Bs + offB[s] + j * 32 * CH * 16);
-    };
 
     v16i acc[4][4];
 #pragma unroll
@@ -169,41 +205,32 @@ __global__ __launch_bounds__(LThreads, 1) void gemm_i8_big_kernel(Params p, int 
 #pragma unroll
         for (int j = 0; j < 4; j++) acc[i][j] = v16i{};
 
-    v4i fa[2][4], fb[2][4];
-    issue(0, 0);
+    // Slices 0 .. NBUF-2 in flight before the loop; iteration kt consumes
+    // slice kt and starts slice kt + NBUF - 1 (clamped: the last iterations
+    // reload the final slice, keeping the loop body free of branches) into
+    // the buffer that iteration kt - 1 consumed.
+#pragma unroll
+    for (int b = 0; b < NBUF - 1; b++) {
+        const int64_t k0 = (int64_t)(b < nk ? b : nk - 1) * BK;
+#pragma unroll
+        for (int ii = 0; ii < PER_WAVE; ii++) {
+            const int inst = wave * PER_WAVE + ii;
+            lds_load16(srcA[ii] + k0, smem + b * STAGE + 1024 * inst);
+            lds_load16(srcB[ii] + k0, smem + b * STAGE + TILE + 1024 * inst);
+        }
+    }
+    for (int64_t kt = 0; kt < nk; kt++) {
+        // this wave's loads of slice kt are done (the NBUF - 2 newer slices
+        // may still be in flight); after the barrier every wave's are, and
+        // every wave has finished reading the buffer refilled below
+        wait_vmcnt<(NBUF - 2) * 2 * PER_WAVE>();
+        barrier_only();
+        const int cur = (int)(kt % NBUF), nxt = (int)((kt + NBUF - 1) % NBUF);
+        const int64_t nxt_k0 = (kt + NBUF - 1 < nk ? kt + NBUF - 1 : nk - 1) * BK;
+        big_slice<BK>(acc, smem + cur * STAGE, smem + nxt * STAGE, srcA, srcB, nxt_k0, offA, offB, wave);
+    }
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    frags(fa[0], fb[0], smem, 0);
-    for (int64_t kt = 0; kt < nk; kt++) {
-        const int cur = (int)(kt & 1);
-        const int8_t *As = smem + cur * 2 * TILE;
-        // Next slice (the last step reloads its own slice into the idle
-        // buffer, keeping the loop body free of branches).
-        issue(cur ^ 1, min(kt + 1, nk - 1) * BK);
-#pragma unroll
-        for (int s = 0; s < S; s++) {
-            if (s + 1 < S) frags(fa[(s + 1) & 1], fb[(s + 1) & 1], As, s + 1);
-#pragma unroll
-            for (int i = 0; i < 4; i++)
-#pragma unroll
-                for (int j = 0; j < 4; j++)
-                    acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fa[s & 1][i], fb[s & 1][j], acc[i][j], 0, 0, 0);
-            // Matrix-core issue interleaved with the next fragments' LDS reads
-            // (and, in the first step, with the next slice's direct loads).
-            if (s + 1 < S) {
-#pragma unroll
-                for (int q = 0; q < 8; q++) {
-                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-                    if (s == 0) __builtin_amdgcn_sched_group_barrier(0x010, 2 * PER_WAVE / 8, 0);
-                }
-                __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
-            }
-        }
-        __builtin_amdgcn_s_waitcnt(0);
-        __syncthreads();
-        frags(fa[0], fb[0], smem + (cur ^ 1) * 2 * TILE, 0);
-    }
 
     // Epilogue: lane holds column lane%32 of each 32x32 block and rows
     // 8*(r/4) + 4*(lane/32) + r%4 of register r.
@@ -431,12 +458,13 @@ hipError_t launch_t(const Params &p, hipStream_t st) {
     return hipGetLastError();
 }
 
-constexpr int kBigBK = 128;
+constexpr int kBigBK = 64;     // k bytes per slice
+constexpr int kBigBuf = 3;     // slices in the LDS ring (two in flight ahead)
 
 template <int EPI, int OUT>
 hipError_t launch_big(const Params &p, hipStream_t st) {
     const int tiles_m = (int)((p.m + LB - 1) / LB), tiles_n = (int)((p.n + LB - 1) / LB);
-    hipLaunchKernelGGL((gemm_i8_big_kernel<kBigBK, EPI, OUT>), dim3((unsigned)(tiles_m * tiles_n)),
+    hipLaunchKernelGGL((gemm_i8_big_kernel<kBigBK, kBigBuf, EPI, OUT>), dim3((unsigned)(tiles_m * tiles_n)),
                        dim3(LThreads), 0, st, p, tiles_m, tiles_n);
     return hipGetLastError();
 }

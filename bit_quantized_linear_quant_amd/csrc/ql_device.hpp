@@ -26,6 +26,23 @@ __device__ __forceinline__ void lds_load16(const void *src, void *lds_base) {
     __builtin_amdgcn_global_load_lds((gvoid *)src, (lvoid *)lds_base, 16, 0, 0);
 }
 
+// s_waitcnt vmcnt(N), leaving expcnt and lgkmcnt at their maximum: waits until
+// at most N of this wave's vector-memory operations (LDS-DMA loads included)
+// are outstanding.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
+    __builtin_amdgcn_s_waitcnt(((N >> 4) << 14) | (N & 15) | (7 << 4) | (15 << 8));
+}
+
+// Workgroup barrier without the full memory wait __syncthreads() implies
+// (which drains every outstanding LDS-DMA load); callers wait explicitly.
+__device__ __forceinline__ void barrier_only() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
 // Index of the calling wave in its workgroup, as a wave-uniform (scalar)
 // value, so that arithmetic on it runs on the scalar unit.
 __device__ __forceinline__ int wave_id() {
