@@ -354,7 +354,7 @@ struct GemvStage {
 template <int NBLK, int WAVES, int U>
 __device__ __forceinline__ void gemv_load(GemvStage<NBLK, U> &st, const int8_t *xrow,
                                           const uint32_t *__restrict__ packed, int64_t kb0, int64_t nb0,
-                                          int64_t nblocks, int64_t kblocks, int lane) {
+                                          int64_t nblocks, int64_t kblocks, int lane, bool row_live) {
 #pragma unroll
     for (int u = 0; u < U; u++) {
         const int64_t kb = kb0 + (int64_t)u * WAVES;
@@ -365,7 +365,9 @@ __device__ __forceinline__ void gemv_load(GemvStage<NBLK, U> &st, const int8_t *
             st.w[u][j] = load16_stream(packed + (nbc * kblocks + kbc) * 256 + 4 * lane);
         }
 #pragma unroll
-        for (int t = 0; t < 4; t++) st.a[u][t] = *reinterpret_cast<const v4i *>(xrow + kbc * 256 + 16 * t);
+        // lanes of rows past m load nothing (their rows are never stored)
+        for (int t = 0; t < 4; t++)
+            st.a[u][t] = row_live ? *reinterpret_cast<const v4i *>(xrow + kbc * 256 + 16 * t) : v4i{0, 0, 0, 0};
     }
 }
 
@@ -423,14 +425,14 @@ __global__ __launch_bounds__(WAVES * 64) void w2a8_gemv_kernel(const int8_t *__r
     constexpr int64_t step = (int64_t)WAVES * U;
     GemvStage<NBLK, U> s0, s1;
     int64_t kb = wave;
-    gemv_load<NBLK, WAVES, U>(s0, xrow, packed, kb, nb0, nblocks, kblocks, lane);
+    gemv_load<NBLK, WAVES, U>(s0, xrow, packed, kb, nb0, nblocks, kblocks, lane, fr < m);
     while (true) {
         const int64_t kb1 = kb + step;
-        if (kb1 < kblocks) gemv_load<NBLK, WAVES, U>(s1, xrow, packed, kb1, nb0, nblocks, kblocks, lane);
+        if (kb1 < kblocks) gemv_load<NBLK, WAVES, U>(s1, xrow, packed, kb1, nb0, nblocks, kblocks, lane, fr < m);
         gemv_compute<NBLK, WAVES, U>(s0, acc, kb, kblocks);
         if (kb1 >= kblocks) break;
         const int64_t kb2 = kb1 + step;
-        if (kb2 < kblocks) gemv_load<NBLK, WAVES, U>(s0, xrow, packed, kb2, nb0, nblocks, kblocks, lane);
+        if (kb2 < kblocks) gemv_load<NBLK, WAVES, U>(s0, xrow, packed, kb2, nb0, nblocks, kblocks, lane, fr < m);
         gemv_compute<NBLK, WAVES, U>(s1, acc, kb1, kblocks);
         if (kb2 >= kblocks) break;
         kb = kb2;
@@ -470,9 +472,10 @@ hipError_t launch_out(const int8_t *xq, const float *pts, const int32_t *rowsum,
                       const double *gamma, int64_t m, int64_t n, int64_t k, void *out, hipStream_t st) {
     if (m <= 16) {
         // Measured on MI355X at k=8192, n=28672 with the weights streamed from
-        // HBM: 4 column blocks per workgroup over 8 waves, one k block per
-        // register stage, is the fastest for every m from 1 to 16.
-        return launch_gemv<4, 8, 1, OUT>(xq, pts, rowsum, packed, gamma, m, n, k, out, st);
+        // HBM, 8 waves and one k block per register stage: 4 column blocks per
+        // workgroup up to m = 4, 7 above (1792 column blocks = 256 workgroups).
+        if (m <= 4) return launch_gemv<4, 8, 1, OUT>(xq, pts, rowsum, packed, gamma, m, n, k, out, st);
+        return launch_gemv<7, 8, 1, OUT>(xq, pts, rowsum, packed, gamma, m, n, k, out, st);
     }
     if (m >= XBM) {
         const int tiles_m = (int)((m + XBM - 1) / XBM), tiles_n = (int)((n + XBN - 1) / XBN);
