@@ -39,6 +39,10 @@ _QL_TO_TORCH = {v: k for k, v in _TORCH_TO_QL.items()}
 _lib = None
 
 
+# QL_ABI_VERSION of include/qlinear.h that the argument lists below follow.
+ABI_VERSION = 2
+
+
 class QLinearError(RuntimeError):
     def __init__(self, fn: str, status: int):
         self.status = status
@@ -70,8 +74,8 @@ def lib() -> ctypes.CDLL:
             "qlinear_quant_int4_tensor": (i32, [vp, i32, i64, vp, f32, vp, vp]),
             "qlinear_pack_ternary": (i32, [vp, i32, i64, i64, f64, vp, vp, vp, sz, vp]),
             "qlinear_pack_int4": (i32, [vp, i64, i64, i32, vp, vp]),
-            "qlinear_gemm_w8a8": (i32, [vp, vp, i32, vp, vp, i64, i64, i64, i32, vp, vp]),
-            "qlinear_gemm_w2a8": (i32, [vp, vp, vp, vp, vp, i64, i64, i64, i32, vp, vp]),
+            "qlinear_gemm_w8a8": (i32, [vp, vp, i32, vp, vp, vp, i64, i64, i64, i32, vp, vp]),
+            "qlinear_gemm_w2a8": (i32, [vp, vp, vp, vp, vp, vp, i64, i64, i64, i32, vp, vp]),
             "qlinear_gemm_w4a8_grouped": (i32, [vp, i32, vp, vp, vp, vp, i64, i64, i64, i64, vp, i32, vp,
                                                 vp]),
             "qlinear_gemm_a4w4_codes": (i32, [vp, vp, vp, vp, f32, i64, i64, i64, i32, vp, vp]),
@@ -81,6 +85,9 @@ def lib() -> ctypes.CDLL:
             fn = getattr(L, name)
             fn.restype = res
             fn.argtypes = args
+        built = L.qlinear_abi_version()
+        if built != ABI_VERSION:
+            raise ImportError(f"{LIB_PATH} has ABI version {built}, this binding needs {ABI_VERSION}: rebuild it")
         _lib = L
     return _lib
 
@@ -108,6 +115,15 @@ def _need(t, nbytes: int, name: str):
     if t is not None and t.numel() * t.element_size() < nbytes:
         raise ValueError(f"{name} holds {t.numel() * t.element_size()} bytes, the call needs {nbytes}")
     return t
+
+
+def _bias(bias, n: int, out_dtype):
+    """Validate an optional fp32 bias ``[n]`` (added after the dequant, before the output rounding)."""
+    if bias is None:
+        return None
+    if out_dtype == torch.int32:
+        raise ValueError("a bias needs a floating-point output (int32 output is the raw accumulator)")
+    return _need(_gpu(bias, "bias", torch.float32), 4 * n, "bias")
 
 
 def _check(fn: str, rc: int) -> None:
@@ -187,8 +203,8 @@ def qlinear_pack_int4(codes, what=QL_INT4_WEIGHT, packed=None):
     return packed
 
 
-def qlinear_gemm_w8a8(x, w, layout, deq_scale, per_token_scale, out_dtype=torch.float16, out=None):
-    """Per-token W8A8 linear: int8 ``x[m,k]`` times int8 ``w`` ([k,n] or [n,k])."""
+def qlinear_gemm_w8a8(x, w, layout, deq_scale, per_token_scale, out_dtype=torch.float16, out=None, bias=None):
+    """Per-token W8A8 linear: int8 ``x[m,k]`` times int8 ``w`` ([k,n] or [n,k]), optional fp32 ``bias[n]``."""
     _gpu(x, "x", torch.int8)
     _gpu(w, "w", torch.int8)
     m, k = x.shape
@@ -198,16 +214,18 @@ def qlinear_gemm_w8a8(x, w, layout, deq_scale, per_token_scale, out_dtype=torch.
     if out_dtype != torch.int32:
         _need(_gpu(deq_scale, "deq_scale", torch.float32), 4 * n, "deq_scale")
         _need(_gpu(per_token_scale, "per_token_scale", torch.float32), 4 * m, "per_token_scale")
+    _bias(bias, n, out_dtype)
     out = _empty((m, n), out_dtype, x) if out is None else _gpu(out, "out", out_dtype)
     _need(out, m * n * out.element_size(), "out")
     _check("qlinear_gemm_w8a8", lib().qlinear_gemm_w8a8(
-        _ptr(x), _ptr(w), layout, _ptr(deq_scale), _ptr(per_token_scale), m, n, k,
+        _ptr(x), _ptr(w), layout, _ptr(deq_scale), _ptr(per_token_scale), _ptr(bias), m, n, k,
         _TORCH_TO_QL[out_dtype], _ptr(out), _stream(x)))
     return out
 
 
-def qlinear_gemm_w2a8(xq, per_token_scale, rowsum, packed, gamma, n, out_dtype=torch.bfloat16, out=None):
-    """BitLinear product of int8 codes ``xq[m,k]`` and packed ternary weights (``n`` columns)."""
+def qlinear_gemm_w2a8(xq, per_token_scale, rowsum, packed, gamma, n, out_dtype=torch.bfloat16, out=None,
+                      bias=None):
+    """BitLinear product of int8 codes ``xq[m,k]`` and packed ternary weights (``n`` columns), optional bias."""
     _gpu(xq, "xq", torch.int8)
     _gpu(rowsum, "rowsum", torch.int32)
     _gpu(packed, "packed")
@@ -217,10 +235,11 @@ def qlinear_gemm_w2a8(xq, per_token_scale, rowsum, packed, gamma, n, out_dtype=t
     if out_dtype != torch.int32:
         _need(_gpu(per_token_scale, "per_token_scale", torch.float32), 4 * m, "per_token_scale")
         _gpu(gamma, "gamma", torch.float64)
+    _bias(bias, n, out_dtype)
     out = _empty((m, n), out_dtype, xq) if out is None else _gpu(out, "out", out_dtype)
     _need(out, m * n * out.element_size(), "out")
     _check("qlinear_gemm_w2a8", lib().qlinear_gemm_w2a8(
-        _ptr(xq), _ptr(per_token_scale), _ptr(rowsum), _ptr(packed), _ptr(gamma), m, n, k,
+        _ptr(xq), _ptr(per_token_scale), _ptr(rowsum), _ptr(packed), _ptr(gamma), _ptr(bias), m, n, k,
         _TORCH_TO_QL[out_dtype], _ptr(out), _stream(xq)))
     return out
 
@@ -230,7 +249,8 @@ def qlinear_gemm_w4a8_grouped(x, packed_w, scales, packed_zeros, group_size, n, 
     """Grouped affine INT4 linear; ``scales`` fp16 ``[n, k/group_size]``.
 
     ``x[m,k]`` is fp16 activations, or int8 activation codes with their fp32
-    ``per_token_scale[m]`` (from ``qlinear_quant_act``).
+    ``per_token_scale[m]`` (from ``qlinear_quant_act``).  ``bias`` is an
+    optional fp32 ``[n]``.
     """
     _gpu(x, "x")
     if x.dtype == torch.int8:
@@ -243,6 +263,7 @@ def qlinear_gemm_w4a8_grouped(x, packed_w, scales, packed_zeros, group_size, n, 
         _need(packed_w, n * k // 2, "packed_w")
         _need(scales, 2 * n * (k // group_size), "scales")
         _need(packed_zeros, n * (k // group_size) // 2, "packed_zeros")
+    _bias(bias, n, out_dtype)
     out = _empty((m, n), out_dtype, x) if out is None else _gpu(out, "out", out_dtype)
     _need(out, m * n * out.element_size(), "out")
     _check("qlinear_gemm_w4a8_grouped", lib().qlinear_gemm_w4a8_grouped(

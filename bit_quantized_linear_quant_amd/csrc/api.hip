@@ -123,61 +123,63 @@ static ql_status gemm_out_kind(ql_dtype d, int *kind) {
 }
 
 ql_status qlinear_gemm_w8a8(const int8_t *x, const int8_t *w, ql_wlayout layout, const float *deq_scale,
-                            const float *per_token_scale, int64_t m, int64_t n, int64_t k,
+                            const float *per_token_scale, const float *bias, int64_t m, int64_t n, int64_t k,
                             ql_dtype out_dtype, void *out, void *stream) {
     int ok;
     if (!x || !w || !out) return QL_ERR_NULL;
     const ql_status ds = gemm_out_kind(out_dtype, &ok);
     if (ds != QL_OK) return ds;
     if (ok != ql::OUT_I32 && (!deq_scale || !per_token_scale)) return QL_ERR_NULL;
+    if (ok == ql::OUT_I32 && bias) return QL_ERR_UNSUPPORTED;
     if (layout != QL_W_KN && layout != QL_W_NK) return QL_ERR_UNSUPPORTED;
     if (m < 1 || n < 1 || k < 1 || k > kMaxK || n > 0x7fffffff) return QL_ERR_SHAPE;
-    if (!aligned16(x) || !aligned16(w) || !aligned16(out)) return QL_ERR_ALIGN;
+    if (!aligned16(x) || !aligned16(w) || !aligned16(out) || !aligned16(bias)) return QL_ERR_ALIGN;
     if (ok != ql::OUT_I32 && (!aligned16(deq_scale) || !aligned16(per_token_scale))) return QL_ERR_ALIGN;
     ql::GemmI8Args a{x, w, layout == QL_W_NK, ql::EPI_ROWCOL, per_token_scale, deq_scale, nullptr,
-                     nullptr, 0.0f, m, n, k, ok, out};
+                     nullptr, 0.0f, m, n, k, ok, out, bias};
     return hip_status(ql::launch_gemm_i8(a, as_stream(stream)));
 }
 
 ql_status qlinear_gemm_w2a8(const int8_t *xq, const float *per_token_scale, const int32_t *rowsum,
-                            const uint32_t *packed, const double *gamma, int64_t m, int64_t n, int64_t k,
-                            ql_dtype out_dtype, void *out, void *stream) {
+                            const uint32_t *packed, const double *gamma, const float *bias, int64_t m, int64_t n,
+                            int64_t k, ql_dtype out_dtype, void *out, void *stream) {
     int ok;
     if (!xq || !rowsum || !packed || !out) return QL_ERR_NULL;
     const ql_status ds = gemm_out_kind(out_dtype, &ok);
     if (ds != QL_OK) return ds;
     if (ok != ql::OUT_I32 && (!per_token_scale || !gamma)) return QL_ERR_NULL;
+    if (ok == ql::OUT_I32 && bias) return QL_ERR_UNSUPPORTED;
     if (m < 1 || n < 16 || k < 256 || n % 16 || k % 256 || k > kMaxK) return QL_ERR_SHAPE;
-    if (!aligned16(xq) || !aligned16(rowsum) || !aligned16(packed) || !aligned16(out)) return QL_ERR_ALIGN;
+    if (!aligned16(xq) || !aligned16(rowsum) || !aligned16(packed) || !aligned16(out) || !aligned16(bias))
+        return QL_ERR_ALIGN;
     if (ok != ql::OUT_I32 && (!aligned16(per_token_scale) || !aligned16(gamma))) return QL_ERR_ALIGN;
-    return hip_status(ql::launch_gemm_w2a8(xq, per_token_scale, rowsum, packed, gamma, m, n, k, ok, out,
+    return hip_status(ql::launch_gemm_w2a8(xq, per_token_scale, rowsum, packed, gamma, bias, m, n, k, ok, out,
                                            as_stream(stream)));
 }
 
 ql_status qlinear_gemm_w4a8_grouped(const void *x, ql_dtype x_dtype, const float *per_token_scale,
                                     const uint32_t *packed_w, const uint16_t *scales,
                                     const uint32_t *packed_zeros, int64_t group_size, int64_t m, int64_t n,
-                                    int64_t k, const void *bias, ql_dtype out_dtype, void *out,
+                                    int64_t k, const float *bias, ql_dtype out_dtype, void *out,
                                     void *stream) {
     if (!x || !packed_w || !scales || !packed_zeros || !out) return QL_ERR_NULL;
     if (x_dtype != QL_F16 && x_dtype != QL_I8) return QL_ERR_DTYPE;
     if (x_dtype == QL_I8 && !per_token_scale) return QL_ERR_NULL;
     if (out_dtype != QL_F16 && out_dtype != QL_F32 && !(x_dtype == QL_I8 && out_dtype == QL_BF16))
         return QL_ERR_DTYPE;
-    if (bias) return QL_ERR_UNSUPPORTED;
     if (m < 1 || n < 16 || k < 128 || n % 16 || k % 128 || group_size < 128 || group_size % 128 ||
         k % group_size)
         return QL_ERR_SHAPE;
     if (!aligned16(x) || !aligned16(packed_w) || !aligned16(scales) || !aligned16(packed_zeros) ||
-        !aligned16(out) || (per_token_scale && !aligned16(per_token_scale)))
+        !aligned16(out) || !aligned16(bias) || (per_token_scale && !aligned16(per_token_scale)))
         return QL_ERR_ALIGN;
     const int ok = out_dtype == QL_F32 ? ql::OUT_F32 : out_dtype == QL_BF16 ? ql::OUT_BF16 : ql::OUT_F16;
     if (x_dtype == QL_I8)
         return hip_status(ql::launch_gemm_int4_grouped_i8(static_cast<const int8_t *>(x), per_token_scale,
-                                                          packed_w, scales, packed_zeros, group_size, m, n, k, ok,
-                                                          out, as_stream(stream)));
+                                                          packed_w, scales, packed_zeros, bias, group_size, m, n,
+                                                          k, ok, out, as_stream(stream)));
     return hip_status(ql::launch_gemm_int4_grouped(static_cast<const uint16_t *>(x), packed_w, scales,
-                                                   packed_zeros, group_size, m, n, k, ok, out,
+                                                   packed_zeros, bias, group_size, m, n, k, ok, out,
                                                    as_stream(stream)));
 }
 

@@ -46,6 +46,7 @@ struct Params {
     float eps;
     int64_t m, n, k;
     void *out;
+    const float *bias;   // [n] or NULL
 };
 
 // Per-row and per-column epilogue factors: (acc * row) * col, rounded once
@@ -80,11 +81,20 @@ struct Epilogue {
         if (OUT == OUT_I32) return 0.f;
         return EPI == EPI_ROWCOL ? rowf[local] : sa;
     }
+    // bias of a column (0 when there is none; value() adds it only if p.bias)
+    __device__ __forceinline__ float col_bias(const Params &p, int64_t col) const {
+        return (OUT == OUT_I32 || !p.bias) ? 0.f : p.bias[col < p.n ? col : p.n - 1];
+    }
+    // fl32(fl32(acc * row) * col), then + bias in fp32
+    __device__ __forceinline__ float value(const Params &p, int32_t v, float rf, float cf, float cb) const {
+        const float y = __fmul_rn(__fmul_rn((float)v, rf), cf);
+        return p.bias ? __fadd_rn(y, cb) : y;
+    }
     __device__ __forceinline__ void store(const Params &p, int64_t row, int64_t col, int32_t v, float rf,
-                                          float cf) const {
+                                          float cf, float cb) const {
         const int64_t idx = row * p.n + col;
         if (OUT == OUT_I32) static_cast<int32_t *>(p.out)[idx] = v;
-        else store_out<OUT>(p.out, idx, __fmul_rn(__fmul_rn((float)v, rf), cf));
+        else store_out<OUT>(p.out, idx, value(p, v, rf, cf, cb));
     }
 };
 
@@ -238,9 +248,12 @@ __global__ __launch_bounds__(LThreads, 1) void gemm_i8_big_kernel(Params p, int 
     ep.init(p);
     ep.stage_rows(p, m0, LB, reinterpret_cast<float *>(smem));
     __syncthreads();
-    float cf[4];
+    float cf[4], cb[4];
 #pragma unroll
-    for (int j = 0; j < 4; j++) cf[j] = ep.col_factor(p, n0 + wn * 128 + 32 * j + fr);
+    for (int j = 0; j < 4; j++) {
+        cf[j] = ep.col_factor(p, n0 + wn * 128 + 32 * j + fr);
+        cb[j] = ep.col_bias(p, n0 + wn * 128 + 32 * j + fr);
+    }
     if constexpr (OUT == OUT_F16 || OUT == OUT_BF16) {
         // Through LDS: the wave rounds its 128 x 128 sub-tile into a padded
         // LDS tile (the two row groups of one write land 16 banks apart), then
@@ -254,7 +267,7 @@ __global__ __launch_bounds__(LThreads, 1) void gemm_i8_big_kernel(Params p, int 
                 const float rf = ep.row_factor(wm * 128 + lr);
 #pragma unroll
                 for (int j = 0; j < 4; j++) {
-                    const float y = __fmul_rn(__fmul_rn((float)acc[i][j][r], rf), cf[j]);
+                    const float y = ep.value(p, acc[i][j][r], rf, cf[j], cb[j]);
                     *reinterpret_cast<uint16_t *>(tile + lr * EPITCH + 2 * (32 * j + fr)) =
                         OUT == OUT_F16 ? f32_to_f16_rne(y) : f32_to_bf16_rne(y);
                 }
@@ -291,7 +304,7 @@ __global__ __launch_bounds__(LThreads, 1) void gemm_i8_big_kernel(Params p, int 
 #pragma unroll
             for (int r = 0; r < 16; r++) {
                 const int local = wm * 128 + 32 * i + 8 * (r / 4) + 4 * (lane / 32) + (r % 4);
-                if (m0 + local < p.m) ep.store(p, m0 + local, col, acc[i][j][r], ep.row_factor(local), cf[j]);
+                if (m0 + local < p.m) ep.store(p, m0 + local, col, acc[i][j][r], ep.row_factor(local), cf[j], cb[j]);
             }
     }
 }
@@ -434,9 +447,12 @@ __global__ __launch_bounds__(kThreads) void gemm_i8_kernel(Params p) {
     ep.init(p);
     ep.stage_rows(p, m0, BM, reinterpret_cast<float *>(As));
     __syncthreads();
-    float cf[TN];
+    float cf[TN], cb[TN];
 #pragma unroll
-    for (int j = 0; j < TN; j++) cf[j] = ep.col_factor(p, n0 + wn * WN + j * 16 + fr);
+    for (int j = 0; j < TN; j++) {
+        cf[j] = ep.col_factor(p, n0 + wn * WN + j * 16 + fr);
+        cb[j] = ep.col_bias(p, n0 + wn * WN + j * 16 + fr);
+    }
 #pragma unroll
     for (int j = 0; j < TN; j++) {
         const int64_t col = n0 + wn * WN + j * 16 + fr;
@@ -446,7 +462,7 @@ __global__ __launch_bounds__(kThreads) void gemm_i8_kernel(Params p) {
 #pragma unroll
             for (int r = 0; r < 4; r++) {
                 const int local = wm * WM + i * 16 + 4 * (lane / 16) + r;
-                if (m0 + local < p.m) ep.store(p, m0 + local, col, acc[i][j][r], ep.row_factor(local), cf[j]);
+                if (m0 + local < p.m) ep.store(p, m0 + local, col, acc[i][j][r], ep.row_factor(local), cf[j], cb[j]);
             }
     }
 }
@@ -501,7 +517,7 @@ bool gemm_i8_uses_big_tiles(bool w_nk, int64_t m, int64_t n, int64_t k) {
 }
 
 hipError_t launch_gemm_i8(const GemmI8Args &a, hipStream_t st) {
-    Params p{a.x, a.w, a.pts, a.deq, a.sa, a.sw, a.eps, a.m, a.n, a.k, a.out};
+    Params p{a.x, a.w, a.pts, a.deq, a.sa, a.sw, a.eps, a.m, a.n, a.k, a.out, a.bias};
     if (gemm_i8_uses_big_tiles(a.w_nk, a.m, a.n, a.k))
         return a.epi == EPI_ROWCOL ? launch_big_out<EPI_ROWCOL>(a.out_kind, p, st)
                                    : launch_big_out<EPI_SCALARS>(a.out_kind, p, st);

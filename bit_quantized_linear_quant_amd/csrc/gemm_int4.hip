@@ -112,6 +112,7 @@ __global__ __launch_bounds__(WAVES * 64) void int4_grouped_kernel(const uint16_t
                                                                   const uint32_t *__restrict__ packed_w,
                                                                   const uint16_t *__restrict__ scales,
                                                                   const uint32_t *__restrict__ packed_z,
+                                                                  const float *__restrict__ bias,
                                                                   int64_t group_size, int64_t m,
                                                                   int64_t n, int64_t k,
                                                                   void *__restrict__ out) {
@@ -170,33 +171,34 @@ __global__ __launch_bounds__(WAVES * 64) void int4_grouped_kernel(const uint16_t
 #pragma unroll
         for (int w = 1; w < WAVES; w++) s += red[w][e][lane];
         const int64_t col = nb * 16 + fr;
+        const float cb = bias ? bias[col] : 0.0f;
 #pragma unroll
         for (int r = 0; r < 4; r++) {
             const int64_t row = row0 + b * 16 + 4 * (lane / 16) + r;
-            if (row < m) store_out<OUT>(out, row * n + col, s[r]);
+            if (row < m) store_out<OUT>(out, row * n + col, bias ? __fadd_rn(s[r], cb) : s[r]);
         }
     }
 }
 
 template <int NBLK, int WAVES, int RB, int OUT>
 hipError_t launch_cfg(const uint16_t *x, const uint32_t *packed_w, const uint16_t *scales,
-                      const uint32_t *packed_z, int64_t group_size, int64_t m, int64_t n, int64_t k,
+                      const uint32_t *packed_z, const float *bias, int64_t group_size, int64_t m, int64_t n, int64_t k,
                       void *out, hipStream_t st) {
     const int64_t nblocks = n / 16;
     dim3 grid((unsigned)((nblocks + NBLK - 1) / NBLK), (unsigned)((m + 16 * RB - 1) / (16 * RB)));
     hipLaunchKernelGGL((int4_grouped_kernel<NBLK, WAVES, RB, OUT>), grid, dim3(WAVES * 64), 0, st, x,
-                       packed_w, scales, packed_z, group_size, m, n, k, out);
+                       packed_w, scales, packed_z, bias, group_size, m, n, k, out);
     return hipGetLastError();
 }
 
 template <int OUT>
 hipError_t launch_t(const uint16_t *x, const uint32_t *packed_w, const uint16_t *scales,
-                    const uint32_t *packed_z, int64_t group_size, int64_t m, int64_t n, int64_t k,
+                    const uint32_t *packed_z, const float *bias, int64_t group_size, int64_t m, int64_t n, int64_t k,
                     void *out, hipStream_t st) {
     // m <= 16 needs one 16-row MFMA block; larger m takes 32-row slices so
     // every unpacked weight fragment serves two row blocks.
-    if (m <= 16) return launch_cfg<3, 8, 1, OUT>(x, packed_w, scales, packed_z, group_size, m, n, k, out, st);
-    return launch_cfg<3, 8, 2, OUT>(x, packed_w, scales, packed_z, group_size, m, n, k, out, st);
+    if (m <= 16) return launch_cfg<3, 8, 1, OUT>(x, packed_w, scales, packed_z, bias, group_size, m, n, k, out, st);
+    return launch_cfg<3, 8, 2, OUT>(x, packed_w, scales, packed_z, bias, group_size, m, n, k, out, st);
 }
 
 // ---------------------------------------------------------------------------
@@ -287,6 +289,7 @@ __global__ __launch_bounds__(WAVES * 64) void int4_grouped_i8_kernel(const int8_
                                                                      const uint32_t *__restrict__ packed_w,
                                                                      const uint16_t *__restrict__ scales,
                                                                      const uint32_t *__restrict__ packed_z,
+                                                                     const float *__restrict__ bias,
                                                                      int64_t group_size, int64_t m, int64_t n,
                                                                      int64_t k, void *__restrict__ out) {
     __shared__ v4f red[WAVES][RB * NBLK][kWave];
@@ -346,43 +349,45 @@ __global__ __launch_bounds__(WAVES * 64) void int4_grouped_i8_kernel(const int8_
 #pragma unroll
         for (int w = 1; w < WAVES; w++) s += red[w][e][lane];
         const int64_t col = nb * 16 + fr;
+        const float cb = bias ? bias[col] : 0.0f;
 #pragma unroll
         for (int r = 0; r < 4; r++) {
             const int64_t row = row0 + b * 16 + 4 * (lane / 16) + r;
-            if (row < m) store_out<OUT>(out, row * n + col, __fmul_rn(s[r], prow[b][r]));
+            const float y = __fmul_rn(s[r], prow[b][r]);
+            if (row < m) store_out<OUT>(out, row * n + col, bias ? __fadd_rn(y, cb) : y);
         }
     }
 }
 
 template <int NBLK, int WAVES, int RB, int OUT>
 hipError_t launch_cfg_i8(const int8_t *xq, const float *pts, const uint32_t *packed_w, const uint16_t *scales,
-                         const uint32_t *packed_z, int64_t group_size, int64_t m, int64_t n, int64_t k, void *out,
+                         const uint32_t *packed_z, const float *bias, int64_t group_size, int64_t m, int64_t n, int64_t k, void *out,
                          hipStream_t st) {
     const int64_t nblocks = n / 16;
     dim3 grid((unsigned)((nblocks + NBLK - 1) / NBLK), (unsigned)((m + 16 * RB - 1) / (16 * RB)));
     hipLaunchKernelGGL((int4_grouped_i8_kernel<NBLK, WAVES, RB, OUT>), grid, dim3(WAVES * 64), 0, st, xq, pts,
-                       packed_w, scales, packed_z, group_size, m, n, k, out);
+                       packed_w, scales, packed_z, bias, group_size, m, n, k, out);
     return hipGetLastError();
 }
 
 template <int OUT>
 hipError_t launch_i8_t(const int8_t *xq, const float *pts, const uint32_t *packed_w, const uint16_t *scales,
-                       const uint32_t *packed_z, int64_t group_size, int64_t m, int64_t n, int64_t k, void *out,
+                       const uint32_t *packed_z, const float *bias, int64_t group_size, int64_t m, int64_t n, int64_t k, void *out,
                        hipStream_t st) {
     if (m <= 16)
-        return launch_cfg_i8<3, 8, 1, OUT>(xq, pts, packed_w, scales, packed_z, group_size, m, n, k, out, st);
-    return launch_cfg_i8<3, 8, 2, OUT>(xq, pts, packed_w, scales, packed_z, group_size, m, n, k, out, st);
+        return launch_cfg_i8<3, 8, 1, OUT>(xq, pts, packed_w, scales, packed_z, bias, group_size, m, n, k, out, st);
+    return launch_cfg_i8<3, 8, 2, OUT>(xq, pts, packed_w, scales, packed_z, bias, group_size, m, n, k, out, st);
 }
 
 }  // namespace
 
 hipError_t launch_gemm_int4_grouped(const uint16_t *x, const uint32_t *packed_w, const uint16_t *scales,
-                                    const uint32_t *packed_zeros, int64_t group_size, int64_t m,
-                                    int64_t n, int64_t k, int out_kind, void *out, hipStream_t st) {
+                                    const uint32_t *packed_zeros, const float *bias, int64_t group_size,
+                                    int64_t m, int64_t n, int64_t k, int out_kind, void *out, hipStream_t st) {
     if ((m + 31) / 32 > 65535) return hipErrorInvalidValue;
     if (out_kind == OUT_F32)
-        return launch_t<OUT_F32>(x, packed_w, scales, packed_zeros, group_size, m, n, k, out, st);
-    return launch_t<OUT_F16>(x, packed_w, scales, packed_zeros, group_size, m, n, k, out, st);
+        return launch_t<OUT_F32>(x, packed_w, scales, packed_zeros, bias, group_size, m, n, k, out, st);
+    return launch_t<OUT_F16>(x, packed_w, scales, packed_zeros, bias, group_size, m, n, k, out, st);
 }
 
 }  // namespace ql
@@ -390,13 +395,14 @@ hipError_t launch_gemm_int4_grouped(const uint16_t *x, const uint32_t *packed_w,
 namespace ql {
 
 hipError_t launch_gemm_int4_grouped_i8(const int8_t *xq, const float *pts, const uint32_t *packed_w,
-                                       const uint16_t *scales, const uint32_t *packed_zeros, int64_t group_size,
-                                       int64_t m, int64_t n, int64_t k, int out_kind, void *out, hipStream_t st) {
+                                       const uint16_t *scales, const uint32_t *packed_zeros, const float *bias,
+                                       int64_t group_size, int64_t m, int64_t n, int64_t k, int out_kind, void *out,
+                                       hipStream_t st) {
     if ((m + 31) / 32 > 65535) return hipErrorInvalidValue;
     switch (out_kind) {
-        case OUT_F32: return launch_i8_t<OUT_F32>(xq, pts, packed_w, scales, packed_zeros, group_size, m, n, k, out, st);
-        case OUT_BF16: return launch_i8_t<OUT_BF16>(xq, pts, packed_w, scales, packed_zeros, group_size, m, n, k, out, st);
-        default: return launch_i8_t<OUT_F16>(xq, pts, packed_w, scales, packed_zeros, group_size, m, n, k, out, st);
+        case OUT_F32: return launch_i8_t<OUT_F32>(xq, pts, packed_w, scales, packed_zeros, bias, group_size, m, n, k, out, st);
+        case OUT_BF16: return launch_i8_t<OUT_BF16>(xq, pts, packed_w, scales, packed_zeros, bias, group_size, m, n, k, out, st);
+        default: return launch_i8_t<OUT_F16>(xq, pts, packed_w, scales, packed_zeros, bias, group_size, m, n, k, out, st);
     }
 }
 

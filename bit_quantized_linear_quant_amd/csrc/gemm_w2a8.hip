@@ -37,12 +37,17 @@ __device__ __forceinline__ uint32_t word_of(const uint4 &v, int t) {
     return t == 0 ? v.x : (t == 1 ? v.y : (t == 2 ? v.z : v.w));
 }
 
+__device__ __forceinline__ float dequant_value(int32_t v, float pts, float g, const float *bias, float cb) {
+    const float y = __fmul_rn(__fmul_rn((float)v, pts), g);
+    return bias ? __fadd_rn(y, cb) : y;   // the bias (if any) is added after the dequant
+}
+
 template <int OUT>
 __device__ __forceinline__ void epilogue_store(void *out, int64_t idx, int32_t acc, int32_t rs,
-                                               float pts, float g) {
+                                               float pts, float g, const float *bias, float cb) {
     const int32_t v = acc - rs;
     if (OUT == OUT_I32) static_cast<int32_t *>(out)[idx] = v;
-    else store_out<OUT>(out, idx, __fmul_rn(__fmul_rn((float)v, pts), g));
+    else store_out<OUT>(out, idx, dequant_value(v, pts, g, bias, cb));
 }
 
 // Code sums and per-token scales of a tile's rows, staged in LDS after the
@@ -71,6 +76,7 @@ __global__ __launch_bounds__(kGThreads) void w2a8_gemm_kernel(const int8_t *__re
                                                               const int32_t *__restrict__ rowsum,
                                                               const uint32_t *__restrict__ packed,
                                                               const double *__restrict__ gamma,
+                                                              const float *__restrict__ bias,
                                                               int64_t m, int64_t n, int64_t k,
                                                               void *__restrict__ out) {
     __shared__ __attribute__((aligned(16))) int8_t As[GBM * kGRow];
@@ -154,6 +160,7 @@ __global__ __launch_bounds__(kGThreads) void w2a8_gemm_kernel(const int8_t *__re
         const int64_t nb = nbase + j;
         if (nb >= nblocks) continue;
         const int64_t col = nb * 16 + fr;
+        const float colb = (OUT != OUT_I32 && bias) ? bias[col] : 0.0f;
 #pragma unroll
         for (int i = 0; i < 4; i++)
 #pragma unroll
@@ -161,7 +168,7 @@ __global__ __launch_bounds__(kGThreads) void w2a8_gemm_kernel(const int8_t *__re
                 const int local = wm * 64 + i * 16 + 4 * (lane / 16) + r;
                 if (m0 + local < m)
                     epilogue_store<OUT>(out, (m0 + local) * n + col, acc[i][j][r], rs_lds[local],
-                                        OUT == OUT_I32 ? 0.0f : pts_lds[local], g);
+                                        OUT == OUT_I32 ? 0.0f : pts_lds[local], g, bias, colb);
             }
     }
 }
@@ -230,6 +237,7 @@ __global__ __launch_bounds__(kXThreads, 1) void w2a8_big_kernel(const int8_t *__
                                                                 const int32_t *__restrict__ rowsum,
                                                                 const uint32_t *__restrict__ packed,
                                                                 const double *__restrict__ gamma,
+                                                                const float *__restrict__ bias,
                                                                 int64_t m, int64_t n, int64_t k,
                                                                 void *__restrict__ out, int tiles_m,
                                                                 int tiles_n) {
@@ -301,6 +309,12 @@ __global__ __launch_bounds__(kXThreads, 1) void w2a8_big_kernel(const int8_t *__
     constexpr int PITCH = ROWB + 16;
     int8_t *tile = smem + 2 * XBM * 4 + wave * 128 * PITCH;
     const float g = OUT == OUT_I32 ? 0.0f : (float)gamma[0];  // gamma may be NULL for int32 output
+    float cbj[4];
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+        const int64_t col = n0 + 64 * wn + 16 * j + lane % 16;
+        cbj[j] = (OUT != OUT_I32 && bias) ? bias[col < n ? col : n - 1] : 0.0f;
+    }
     // Lane l holds column l % 16 and rows 4(l/16) + r of each 16 x 16 block.
 #pragma unroll
     for (int i = 0; i < 8; i++)
@@ -316,9 +330,9 @@ __global__ __launch_bounds__(kXThreads, 1) void w2a8_big_kernel(const int8_t *__
                 const int32_t v = acc[i][j][r] - rsv;
                 int8_t *dst = tile + lr * PITCH + c * ES;
                 if constexpr (OUT == OUT_I32) *reinterpret_cast<int32_t *>(dst) = v;
-                else if constexpr (OUT == OUT_F32) *reinterpret_cast<float *>(dst) = __fmul_rn(__fmul_rn((float)v, rf), g);
-                else if constexpr (OUT == OUT_F16) *reinterpret_cast<uint16_t *>(dst) = f32_to_f16_rne(__fmul_rn(__fmul_rn((float)v, rf), g));
-                else *reinterpret_cast<uint16_t *>(dst) = f32_to_bf16_rne(__fmul_rn(__fmul_rn((float)v, rf), g));
+                else if constexpr (OUT == OUT_F32) *reinterpret_cast<float *>(dst) = dequant_value(v, rf, g, bias, cbj[j]);
+                else if constexpr (OUT == OUT_F16) *reinterpret_cast<uint16_t *>(dst) = f32_to_f16_rne(dequant_value(v, rf, g, bias, cbj[j]));
+                else *reinterpret_cast<uint16_t *>(dst) = f32_to_bf16_rne(dequant_value(v, rf, g, bias, cbj[j]));
             }
         }
     // the wave reads back only its own sub-tile: a wave-local LDS ordering
@@ -395,6 +409,7 @@ __global__ __launch_bounds__(WAVES * 64) void w2a8_gemv_kernel(const int8_t *__r
                                                                const int32_t *__restrict__ rowsum,
                                                                const uint32_t *__restrict__ packed,
                                                                const double *__restrict__ gamma,
+                                                               const float *__restrict__ bias,
                                                                int64_t m, int64_t n, int64_t k,
                                                                void *__restrict__ out) {
     __shared__ v4i red[WAVES][NBLK][kWave];
@@ -449,56 +464,59 @@ __global__ __launch_bounds__(WAVES * 64) void w2a8_gemv_kernel(const int8_t *__r
 #pragma unroll
         for (int w = 1; w < WAVES; w++) s += red[w][j][lane];
         const int64_t col = nb * 16 + fr;
+        const float cb = (OUT != OUT_I32 && bias) ? bias[col] : 0.0f;
 #pragma unroll
         for (int r = 0; r < 4; r++) {
             const int64_t row = 4 * (lane / 16) + r;
-            if (row < m) epilogue_store<OUT>(out, row * n + col, s[r], rsr[r], ptr[r], g);
+            if (row < m) epilogue_store<OUT>(out, row * n + col, s[r], rsr[r], ptr[r], g, bias, cb);
         }
     }
 }
 
 template <int NBLK, int WAVES, int U, int OUT>
 hipError_t launch_gemv(const int8_t *xq, const float *pts, const int32_t *rowsum, const uint32_t *packed,
-                       const double *gamma, int64_t m, int64_t n, int64_t k, void *out, hipStream_t st) {
+                       const double *gamma, const float *bias, int64_t m, int64_t n, int64_t k, void *out,
+                       hipStream_t st) {
     const int64_t nblocks = n / 16;
     const unsigned grid = (unsigned)((nblocks + NBLK - 1) / NBLK);
     hipLaunchKernelGGL((w2a8_gemv_kernel<NBLK, WAVES, U, OUT>), dim3(grid), dim3(WAVES * 64), 0, st, xq,
-                       pts, rowsum, packed, gamma, m, n, k, out);
+                       pts, rowsum, packed, gamma, bias, m, n, k, out);
     return hipGetLastError();
 }
 
 template <int OUT>
 hipError_t launch_out(const int8_t *xq, const float *pts, const int32_t *rowsum, const uint32_t *packed,
-                      const double *gamma, int64_t m, int64_t n, int64_t k, void *out, hipStream_t st) {
+                      const double *gamma, const float *bias, int64_t m, int64_t n, int64_t k, void *out,
+                      hipStream_t st) {
     if (m <= 16) {
         // Measured on MI355X at k=8192, n=28672 with the weights streamed from
         // HBM, 8 waves and one k block per register stage: 4 column blocks per
         // workgroup up to m = 4, 7 above (1792 column blocks = 256 workgroups).
-        if (m <= 4) return launch_gemv<4, 8, 1, OUT>(xq, pts, rowsum, packed, gamma, m, n, k, out, st);
-        return launch_gemv<7, 8, 1, OUT>(xq, pts, rowsum, packed, gamma, m, n, k, out, st);
+        if (m <= 4) return launch_gemv<4, 8, 1, OUT>(xq, pts, rowsum, packed, gamma, bias, m, n, k, out, st);
+        return launch_gemv<7, 8, 1, OUT>(xq, pts, rowsum, packed, gamma, bias, m, n, k, out, st);
     }
     if (m >= XBM) {
         const int tiles_m = (int)((m + XBM - 1) / XBM), tiles_n = (int)((n + XBN - 1) / XBN);
         hipLaunchKernelGGL((w2a8_big_kernel<OUT>), dim3((unsigned)(tiles_m * tiles_n)), dim3(kXThreads), 0, st, xq,
-                           pts, rowsum, packed, gamma, m, n, k, out, tiles_m, tiles_n);
+                           pts, rowsum, packed, gamma, bias, m, n, k, out, tiles_m, tiles_n);
         return hipGetLastError();
     }
     dim3 grid((unsigned)((n + GBN - 1) / GBN), (unsigned)((m + GBM - 1) / GBM));
     hipLaunchKernelGGL((w2a8_gemm_kernel<OUT>), grid, dim3(kGThreads), 0, st, xq, pts, rowsum, packed,
-                       gamma, m, n, k, out);
+                       gamma, bias, m, n, k, out);
     return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_gemm_w2a8(const int8_t *xq, const float *pts, const int32_t *rowsum,
-                            const uint32_t *packed, const double *gamma, int64_t m, int64_t n,
-                            int64_t k, int out_kind, void *out, hipStream_t st) {
+                            const uint32_t *packed, const double *gamma, const float *bias, int64_t m,
+                            int64_t n, int64_t k, int out_kind, void *out, hipStream_t st) {
     if (m > (int64_t)GBM * 65535) return hipErrorInvalidValue;
     switch (out_kind) {
-        case OUT_F16: return launch_out<OUT_F16>(xq, pts, rowsum, packed, gamma, m, n, k, out, st);
-        case OUT_BF16: return launch_out<OUT_BF16>(xq, pts, rowsum, packed, gamma, m, n, k, out, st);
-        default: return launch_out<OUT_I32>(xq, pts, rowsum, packed, gamma, m, n, k, out, st);
+        case OUT_F16: return launch_out<OUT_F16>(xq, pts, rowsum, packed, gamma, bias, m, n, k, out, st);
+        case OUT_BF16: return launch_out<OUT_BF16>(xq, pts, rowsum, packed, gamma, bias, m, n, k, out, st);
+        default: return launch_out<OUT_I32>(xq, pts, rowsum, packed, gamma, bias, m, n, k, out, st);
     }
 }
 

@@ -40,6 +40,7 @@ struct GemmI8Args {
     int64_t m, n, k;
     int out_kind;        // OutKind
     void *out;           // [m, n]
+    const float *bias;   // [n] added after the dequant, or NULL
 };
 hipError_t launch_gemm_i8(const GemmI8Args &a, hipStream_t st);
 // True when the product runs on the 256 x 256 direct-to-LDS kernel.
@@ -47,16 +48,17 @@ bool gemm_i8_uses_big_tiles(bool w_nk, int64_t m, int64_t n, int64_t k);
 
 // gemm_w2a8.hip: packed ternary weights.
 hipError_t launch_gemm_w2a8(const int8_t *xq, const float *pts, const int32_t *rowsum,
-                            const uint32_t *packed, const double *gamma, int64_t m, int64_t n,
-                            int64_t k, int out_kind, void *out, hipStream_t st);
+                            const uint32_t *packed, const double *gamma, const float *bias, int64_t m,
+                            int64_t n, int64_t k, int out_kind, void *out, hipStream_t st);
 
 // gemm_int4.hip: grouped affine INT4 with fp16 activations.
 hipError_t launch_gemm_int4_grouped(const uint16_t *x, const uint32_t *packed_w,
-                                    const uint16_t *scales, const uint32_t *packed_zeros,
+                                    const uint16_t *scales, const uint32_t *packed_zeros, const float *bias,
                                     int64_t group_size, int64_t m, int64_t n, int64_t k,
                                     int out_kind, void *out, hipStream_t st);
 hipError_t launch_gemm_int4_grouped_i8(const int8_t *xq, const float *pts, const uint32_t *packed_w,
-                                       const uint16_t *scales, const uint32_t *packed_zeros, int64_t group_size,
-                                       int64_t m, int64_t n, int64_t k, int out_kind, void *out, hipStream_t st);
+                                       const uint16_t *scales, const uint32_t *packed_zeros, const float *bias,
+                                       int64_t group_size, int64_t m, int64_t n, int64_t k, int out_kind, void *out,
+                                       hipStream_t st);
 
 }  // namespace ql

@@ -47,7 +47,7 @@
 extern "C" {
 #endif
 
-#define QL_ABI_VERSION 1
+#define QL_ABI_VERSION 2
 /* Version of the 2-bit ternary weight layout written by qlinear_pack_ternary. */
 #define QL_TERNARY_PACK_V1 1
 /* Version of the 4-bit weight layout written by qlinear_pack_int4. */
@@ -178,6 +178,19 @@ ql_status qlinear_pack_int4(const uint8_t *codes, int64_t rows, int64_t cols,
                             ql_int4_what what, uint32_t *packed, void *stream);
 
 /*
+ * QL_BIAS - the optional bias of the three GEMM entry points below.
+ * [PT] Parameters lists hasBias (accepted value: false only), [BL] forward
+ * hands its (normally absent) bias to the linear call, and [L4]
+ * QuantizedLinear4BitPlannerEvidence counts bias bytes.  These entry points
+ * take the ordinary linear-layer meaning y = dequant(acc) + b: bias [n] fp32,
+ * added once in fp32 to the dequantized fp32 value, before the rounding to
+ * the output type.  NULL means no bias and gives exactly the bias-free
+ * result.  (Read literally, [BL] forward would add the bias before the
+ * rescale and so scale it by both quantization scales; that reading is not
+ * taken.)
+ */
+
+/*
  * Per-token W8A8 linear ([PT] Input, Parameters, Output, Example):
  *   out[m][n] = (sum_k x[m][k] * w[k][n]) * per_token_scale[m] * deq_scale[n]
  * computed as an exact int32 accumulation, then fl32(fl32(acc * pts) * deq),
@@ -186,13 +199,16 @@ ql_status qlinear_pack_int4(const uint8_t *codes, int64_t rows, int64_t cols,
  *   deq_scale [n] fp32; per_token_scale [m] fp32;
  *   out [m, n] QL_F16 / QL_BF16, or QL_I32 for the raw accumulator (the
  *   scale pointers may then be NULL).
+ *   bias [n] fp32 or NULL: when given, out = fl32(dequantized value + bias[n])
+ *   before the output rounding (see QL_BIAS below); QL_I32 with a bias is
+ *   QL_ERR_UNSUPPORTED.
  * m, n, k >= 1 (any sizes; edge tiles are masked); k <= 131071 so the int32
  * accumulator cannot overflow.
  */
 ql_status qlinear_gemm_w8a8(const int8_t *x, const int8_t *w, ql_wlayout layout,
                             const float *deq_scale, const float *per_token_scale,
-                            int64_t m, int64_t n, int64_t k, ql_dtype out_dtype, void *out,
-                            void *stream);
+                            const float *bias, int64_t m, int64_t n, int64_t k,
+                            ql_dtype out_dtype, void *out, void *stream);
 
 /*
  * BitLinear product on packed ternary weights ([BL] forward steps 4-5):
@@ -201,14 +217,16 @@ ql_status qlinear_gemm_w8a8(const int8_t *x, const int8_t *w, ql_wlayout layout,
  *   xq [m, k] int8 codes and rowsum [m] from qlinear_quant_act;
  *   packed / gamma from qlinear_pack_ternary;
  *   out [m, n] QL_BF16 / QL_F16, or QL_I32 for acc.
+ *   bias [n] fp32 or NULL, added as in qlinear_gemm_w8a8 (QL_BIAS below);
+ *   QL_I32 with a bias is QL_ERR_UNSUPPORTED.
  * The kernel multiplies by code+1 in {0, 1, 2} and subtracts rowsum.
  * m <= 16 takes the split-K decode GEMV path, larger m the tiled GEMM path.
  * n % 16 == 0, k % 256 == 0, k <= 131071.
  */
 ql_status qlinear_gemm_w2a8(const int8_t *xq, const float *per_token_scale,
                             const int32_t *rowsum, const uint32_t *packed,
-                            const double *gamma, int64_t m, int64_t n, int64_t k,
-                            ql_dtype out_dtype, void *out, void *stream);
+                            const double *gamma, const float *bias, int64_t m, int64_t n,
+                            int64_t k, ql_dtype out_dtype, void *out, void *stream);
 
 /*
  * Grouped affine INT4 linear ([L4] module doc: the packed u32 weight is
@@ -228,14 +246,15 @@ ql_status qlinear_gemm_w2a8(const int8_t *xq, const float *per_token_scale,
  *   packed_w from qlinear_pack_int4(QL_INT4_WEIGHT);
  *   scales [n, k/group_size] fp16 (row-major, one per column and group);
  *   packed_zeros from qlinear_pack_int4(QL_INT4_ZEROS) of z [n, groups];
- *   bias must be NULL (not implemented: QL_ERR_UNSUPPORTED).
+ *   bias [n] fp32 or NULL, added to the fp32 value before the output
+ *   rounding (QL_BIAS below).
  * n % 16 == 0, k % 128 == 0, group_size % 128 == 0, k % group_size == 0.
  */
 ql_status qlinear_gemm_w4a8_grouped(const void *x, ql_dtype x_dtype,
                                     const float *per_token_scale,
                                     const uint32_t *packed_w, const uint16_t *scales,
                                     const uint32_t *packed_zeros, int64_t group_size,
-                                    int64_t m, int64_t n, int64_t k, const void *bias,
+                                    int64_t m, int64_t n, int64_t k, const float *bias,
                                     ql_dtype out_dtype, void *out, void *stream);
 
 /*

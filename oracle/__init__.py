@@ -278,6 +278,17 @@ def w2a8(xq, pts, codes, gamma: float):
     return acc, dequant(acc, pts, deq)
 
 
+def add_bias(y, bias):
+    """fp64 ``y[m,n] + bias[n]``: the bias of a linear layer, added to the
+    dequantized product ("Per-token Quantization for Matmul" Parameters
+    hasBias; "linear_4bit/mod.rs" planner evidence bias bytes).  Not scaled
+    by the quantization scales."""
+    y = _c(y, np.float64)
+    b = _c(bias, np.float32).astype(np.float64)
+    assert b.shape == (y.shape[1],)
+    return y + b[None, :]
+
+
 # --------------------------------------------------------------------------
 # O5: A4W4 per-tensor int4 quantization and product.
 # --------------------------------------------------------------------------

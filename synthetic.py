@@ -20,6 +20,9 @@ benchmark or dataset exists for them, so these synthetic draws stand in):
 5. A4W4: fp16 x[8192,8192] N(0,1), fp16 w[8192,8192] N(0, 0.02^2), scale_a
    and scale_w fp32 scalars set to max|t| / 7 of each tensor (the caller's
    per-tensor calibration), eps=1e-5.
+
+An optional bias of any product is fp32 [n] drawn N(0, scale^2), scale
+chosen by the caller near the output's magnitude (``bias``).
 """
 from __future__ import annotations
 
@@ -115,3 +118,8 @@ def a4w4(m: int = 8192, n: int = 8192, k: int = 8192, seed: int = 1005, eps: flo
     sa = np.float32(x.abs().max().float().item()) / np.float32(scale_div)
     sw = np.float32(w.abs().max().float().item()) / np.float32(scale_div)
     return {"x": x, "w": w, "scale_a": float(sa), "scale_w": float(sw), "eps": eps}
+
+
+def bias(n: int, scale: float, seed: int) -> torch.Tensor:
+    """fp32 bias [n], N(0, scale^2)."""
+    return torch.from_numpy(rng(seed).normal(0.0, scale, n).astype(np.float32))

@@ -4,6 +4,8 @@ Tolerances (relative to the oracle's fp64 value y):
   bf16 output: |gpu - y| <= 2^-7 |y| + 1e-6
   fp16 output: |gpu - y| <= 2^-10 |y| + 1e-6
   grouped INT4 (fp16 activations): |gpu - y| <= 1e-3 * sum_k |x_k * w_k|
+  with a bias b, y is the oracle's y0 + b and the bound gains the fp32
+  roundings of the dequant and the add: 2^-22 (|y0| + |b|)
 Integer results (codes, packed words, int32 accumulators) must be identical.
 """
 import numpy as np
@@ -41,12 +43,13 @@ def words(t: torch.Tensor) -> np.ndarray:
     return t.detach().cpu().numpy().view(np.uint32)
 
 
-def assert_float_close(gpu: torch.Tensor, y: np.ndarray, what: str = "out") -> None:
+def assert_float_close(gpu: torch.Tensor, y: np.ndarray, what: str = "out", extra=None) -> None:
+    """``extra`` (array or scalar) widens the bound by an absolute amount per element."""
     rel = TOL_REL[gpu.dtype]
     g = to_np(gpu).astype(np.float64)
     assert g.shape == y.shape, (g.shape, y.shape)
     err = np.abs(g - y)
-    tol = rel * np.abs(y) + TOL_ABS
+    tol = rel * np.abs(y) + TOL_ABS + (0.0 if extra is None else extra)
     bad = ~(err <= tol)  # NaN counts as bad
     if bad.any():
         idx = np.unravel_index(np.argmax(np.where(bad, err / tol, -1)), y.shape)

@@ -39,7 +39,7 @@ def test_exports_every_declared_symbol(L):
 
 
 def test_abi_version_and_status_strings(L):
-    assert ql.qlinear_abi_version() == 1
+    assert ql.qlinear_abi_version() == ql.ABI_VERSION == 2
     for code, name in ql.STATUS.items():
         s = ql.qlinear_status_string(code)
         assert isinstance(s, str) and s
@@ -92,17 +92,21 @@ def test_pack_validation(L):
 
 def test_gemm_validation(L):
     w8 = L.qlinear_gemm_w8a8
-    assert w8(A, A, ql.QL_W_KN, A, A, 2, 3, 2, ql.QL_BF16, NULL, NULL) == -1
-    assert w8(A, A, ql.QL_W_KN, NULL, A, 2, 3, 2, ql.QL_F16, A, NULL) == -1   # scales needed
-    assert w8(A, A, ql.QL_W_KN, A, A, 2, 3, 131072, ql.QL_F16, A, NULL) == -2  # int32 could overflow
-    assert w8(A, A, ql.QL_W_KN, A, A, 0, 3, 2, ql.QL_F16, A, NULL) == -2
-    assert w8(A, A, ql.QL_W_KN, A, A, 2, 3, 2, ql.QL_U8, A, NULL) == -3
-    assert w8(A, A, 3, A, A, 2, 3, 2, ql.QL_F16, A, NULL) == -6
+    assert w8(A, A, ql.QL_W_KN, A, A, NULL, 2, 3, 2, ql.QL_BF16, NULL, NULL) == -1
+    assert w8(A, A, ql.QL_W_KN, NULL, A, NULL, 2, 3, 2, ql.QL_F16, A, NULL) == -1   # scales needed
+    assert w8(A, A, ql.QL_W_KN, A, A, NULL, 2, 3, 131072, ql.QL_F16, A, NULL) == -2  # int32 could overflow
+    assert w8(A, A, ql.QL_W_KN, A, A, NULL, 0, 3, 2, ql.QL_F16, A, NULL) == -2
+    assert w8(A, A, ql.QL_W_KN, A, A, NULL, 2, 3, 2, ql.QL_U8, A, NULL) == -3
+    assert w8(A, A, 3, A, A, NULL, 2, 3, 2, ql.QL_F16, A, NULL) == -6
+    assert w8(A, A, ql.QL_W_KN, A, A, A, 2, 3, 2, ql.QL_I32, A, NULL) == -6  # bias on the raw accumulator
+    assert w8(A, A, ql.QL_W_KN, A, A, U, 2, 3, 2, ql.QL_F16, A, NULL) == -4
     w2 = L.qlinear_gemm_w2a8
-    assert w2(A, A, NULL, A, A, 1, 16, 256, ql.QL_BF16, A, NULL) == -1
-    assert w2(A, A, A, A, A, 1, 24, 256, ql.QL_BF16, A, NULL) == -2
-    assert w2(A, A, A, A, A, 1, 16, 128, ql.QL_BF16, A, NULL) == -2
-    assert w2(A, A, A, U, A, 1, 16, 256, ql.QL_BF16, A, NULL) == -4
+    assert w2(A, A, NULL, A, A, NULL, 1, 16, 256, ql.QL_BF16, A, NULL) == -1
+    assert w2(A, A, A, A, A, NULL, 1, 24, 256, ql.QL_BF16, A, NULL) == -2
+    assert w2(A, A, A, A, A, NULL, 1, 16, 128, ql.QL_BF16, A, NULL) == -2
+    assert w2(A, A, A, U, A, NULL, 1, 16, 256, ql.QL_BF16, A, NULL) == -4
+    assert w2(A, A, A, A, A, A, 1, 16, 256, ql.QL_I32, A, NULL) == -6
+    assert w2(A, A, A, A, A, U, 1, 16, 256, ql.QL_BF16, A, NULL) == -4
     g4 = L.qlinear_gemm_w4a8_grouped
     assert g4(A, ql.QL_I8, NULL, A, A, A, 128, 1, 16, 128, NULL, ql.QL_F16, A, NULL) == -1  # needs pts
     assert g4(A, ql.QL_I8, U, A, A, A, 128, 1, 16, 128, NULL, ql.QL_F16, A, NULL) == -4
@@ -110,7 +114,7 @@ def test_gemm_validation(L):
     assert g4(A, ql.QL_U8, A, A, A, A, 128, 1, 16, 128, NULL, ql.QL_F16, A, NULL) == -3
     assert g4(A, ql.QL_F16, NULL, A, A, A, 64, 1, 16, 128, NULL, ql.QL_F16, A, NULL) == -2
     assert g4(A, ql.QL_F16, NULL, A, A, A, 256, 1, 16, 384, NULL, ql.QL_F16, A, NULL) == -2
-    assert g4(A, ql.QL_F16, NULL, A, A, A, 128, 1, 16, 128, A, ql.QL_F16, A, NULL) == -6  # bias
+    assert g4(A, ql.QL_F16, NULL, A, A, A, 128, 1, 16, 128, U, ql.QL_F16, A, NULL) == -4  # bias alignment
     assert g4(A, ql.QL_F16, NULL, A, A, A, 128, 1, 16, 128, NULL, ql.QL_BF16, A, NULL) == -3
     a4 = L.qlinear_gemm_a4w4
     assert a4(A, A, ql.QL_F16, A, A, 1e-5, 4, 4, 4, ql.QL_F16, A, NULL, 0, NULL) == -5

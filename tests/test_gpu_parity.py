@@ -14,7 +14,7 @@ import torch
 import bit_quantized_linear_quant_amd as ql
 import oracle
 import synthetic
-from parity_util import absmean_rel_tol, assert_equal, assert_float_close, poison, to_np, words
+from parity_util import TOL_REL, absmean_rel_tol, assert_equal, assert_float_close, poison, to_np, words
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
@@ -341,6 +341,101 @@ def test_grouped_int4_i8_extreme_codes():
     _sync()
     # every term is an integer and the sums stay below 2^24: exact in fp32
     assert np.array_equal(to_np(o).astype(np.float64), y)
+
+
+# ---------------------------------------------------------------------------
+# Optional bias: fp32 [n] added to the dequantized fp32 value, then rounded
+# ---------------------------------------------------------------------------
+def _bias_tol(y, b):
+    """Extra bound of a biased output: two fp32 roundings of the dequant and one of the add."""
+    return 2.0 ** -22 * (np.abs(y) + np.abs(b.astype(np.float64))[None, :])
+
+
+@pytest.mark.parametrize("m,n,k,nk", [(300, 270, 200, True), (77, 45, 77, True), (129, 257, 1000, False),
+                                      (520, 777, 192, True), (1024, 768, 1024, True), (1, 1, 1, False)])
+def test_w8a8_bias_parity(m, n, k, nk):
+    d = synthetic.w8a8(m, n, k, nk, seed=1200 + m + n + k)
+    x, w, deq, pts = (d[key] for key in ("x", "w", "deq", "pts"))
+    b = synthetic.bias(n, 1.0, seed=1300 + n)
+    _, y = oracle.w8a8(x.numpy(), w.numpy(), nk, pts.numpy(), deq.numpy())
+    yb = oracle.add_bias(y, b.numpy())
+    layout = ql.QL_W_NK if nk else ql.QL_W_KN
+    args = (_cuda(x), _cuda(w), layout, _cuda(deq), _cuda(pts))
+    for dt in (torch.float16, torch.bfloat16):
+        o = poison((m, n), dt)
+        ql.qlinear_gemm_w8a8(*args, out_dtype=dt, out=o, bias=_cuda(b))
+        o0 = ql.qlinear_gemm_w8a8(*args, out_dtype=dt, bias=torch.zeros(n, dtype=torch.float32, device=DEV))
+        onb = ql.qlinear_gemm_w8a8(*args, out_dtype=dt)
+        _sync()
+        assert_float_close(o, yb, f"w8a8+bias {dt}", extra=_bias_tol(y, b.numpy()))
+        assert torch.equal(o0, onb), "a zero bias must leave the result unchanged"
+
+
+@pytest.mark.parametrize("m,n,k", [(1, 400, 512), (16, 400, 768), (130, 256, 768), (300, 400, 512)])
+def test_w2a8_bias_parity(m, n, k):
+    d = synthetic.bitlinear(m, n, k, seed=1400 + m + n)
+    xq_ref, pts_ref, _ = oracle.quant_act(d["x"].float().numpy(), rmsnorm=True)
+    codes, gamma = oracle.ternary_quant(d["w"].numpy())
+    _, y = oracle.w2a8(xq_ref, pts_ref, codes, gamma)
+    b = synthetic.bias(n, 1.0, seed=1500 + n)
+    yb = oracle.add_bias(y, b.numpy())
+    xq, pts, rs = ql.qlinear_quant_act(_cuda(d["x"]), rmsnorm=True)
+    packed, g = ql.qlinear_pack_ternary(_cuda(d["w"]), ql.QL_W_NK)
+    for dt in (torch.bfloat16, torch.float16):
+        o = poison((m, n), dt)
+        ql.qlinear_gemm_w2a8(xq, pts, rs, packed, g, n, out_dtype=dt, out=o, bias=_cuda(b))
+        o0 = ql.qlinear_gemm_w2a8(xq, pts, rs, packed, g, n, out_dtype=dt,
+                                  bias=torch.zeros(n, dtype=torch.float32, device=DEV))
+        onb = ql.qlinear_gemm_w2a8(xq, pts, rs, packed, g, n, out_dtype=dt)
+        _sync()
+        assert_equal(xq, xq_ref, "activation codes")
+        assert_float_close(o, yb, f"w2a8+bias {dt}", extra=_bias_tol(y, b.numpy()))
+        assert torch.equal(o0, onb), "a zero bias must leave the result unchanged"
+
+
+@pytest.mark.parametrize("m,n,k,g", [(1, 48, 256, 128), (17, 400, 512, 256), (40, 64, 384, 128)])
+def test_grouped_int4_bias_parity(m, n, k, g):
+    d = synthetic.grouped_int4(m, n, k, g, seed=1600 + m + n + k)
+    x, q, s, z = d["x"], d["q"], d["s"], d["z"]
+    b = synthetic.bias(n, 1.0, seed=1700 + n)
+    pw = ql.qlinear_pack_int4(_cuda(q), ql.QL_INT4_WEIGHT)
+    pz = ql.qlinear_pack_int4(_cuda(z), ql.QL_INT4_ZEROS)
+    ab = np.abs(b.numpy().astype(np.float64))[None, :]
+    # fp16 activations
+    y, bound = oracle.grouped_int4(x.float().numpy(), q.numpy(), s.float().numpy(), z.numpy(), g)
+    yb = oracle.add_bias(y, b.numpy())
+    o32 = ql.qlinear_gemm_w4a8_grouped(_cuda(x), pw, _cuda(s), pz, g, n, out_dtype=torch.float32, bias=_cuda(b))
+    o16 = ql.qlinear_gemm_w4a8_grouped(_cuda(x), pw, _cuda(s), pz, g, n, out_dtype=torch.float16, bias=_cuda(b))
+    _sync()
+    # the grouped bar on the product, plus the fp32 add, plus (fp16) one rounding of y + b
+    for o, rel in ((o32, 2.0 ** -23), (o16, 2.0 ** -10)):
+        err = np.abs(to_np(o).astype(np.float64) - yb)
+        tol = 1e-3 * bound + rel * np.abs(yb) + 2.0 ** -23 * ab
+        assert np.all(err <= tol), f"grouped+bias {o.dtype}: max err/tol {np.max(err / tol)}"
+    assert torch.equal(o16, o32.to(torch.float16))
+    # int8 activation codes
+    xq, pts, _, _, _ = _grouped_i8_inputs(m, n, k, g, seed=1800 + m)
+    y, bound = oracle.grouped_int4_i8(xq.numpy(), pts.numpy(), q.numpy(), s.float().numpy(), z.numpy(), g)
+    yb = oracle.add_bias(y, b.numpy())
+    outs = {dt: ql.qlinear_gemm_w4a8_grouped(_cuda(xq), pw, _cuda(s), pz, g, n, out_dtype=dt,
+                                             per_token_scale=_cuda(pts), bias=_cuda(b))
+            for dt in (torch.float32, torch.float16, torch.bfloat16)}
+    _sync()
+    err32 = np.abs(to_np(outs[torch.float32]).astype(np.float64) - yb)
+    assert np.all(err32 <= 2.0 ** -18 * bound + 2.0 ** -23 * (np.abs(y) + ab) + 1e-30), "grouped i8+bias fp32"
+    # 16-bit outputs: the fp32 value rounded once to nearest even
+    for dt in (torch.float16, torch.bfloat16):
+        err = np.abs(to_np(outs[dt]).astype(np.float64) - yb)
+        tol = 1e-3 * bound + TOL_REL[dt] * np.abs(yb) + 2.0 ** -23 * ab
+        assert np.all(err <= tol), f"grouped i8+bias {dt}: max err/tol {np.max(err / tol)}"
+        assert torch.equal(outs[dt], outs[torch.float32].to(dt))
+
+
+def test_bias_with_int32_output_is_rejected():
+    d = synthetic.w8a8(4, 8, 16, True, seed=3)
+    with pytest.raises(ValueError):
+        ql.qlinear_gemm_w8a8(_cuda(d["x"]), _cuda(d["w"]), ql.QL_W_NK, None, None, out_dtype=torch.int32,
+                             bias=torch.zeros(8, dtype=torch.float32, device=DEV))
 
 
 # ---------------------------------------------------------------------------

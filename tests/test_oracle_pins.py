@@ -71,6 +71,27 @@ def test_dequant_brute_force_fp64(layout_nk):
     np.testing.assert_allclose(y, ref, rtol=1e-12, atol=1e-300)
 
 
+def test_bias_is_added_per_output_column_unscaled():
+    """x = identity, pts = 2, deq = 1/4: y + b = w / 2 + b[n] exactly, and the
+    whole product equals torch's fp64 ``F.linear(x * pts, w * deq, b)``."""
+    k = n = 24
+    x = np.eye(k, dtype=np.int8)
+    w = synthetic.w8a8(k, n, k, True, seed=31)["w"].numpy()  # [n, k]
+    b = synthetic.bias(n, 3.0, seed=32).numpy()
+    pts, deq = np.full(k, 2.0, np.float32), np.full(n, 0.25, np.float32)
+    _, y = oracle.w8a8(x, w, True, pts, deq)
+    yb = oracle.add_bias(y, b)
+    assert np.array_equal(yb, w.T.astype(np.float64) / 2 + b.astype(np.float64)[None, :])
+    d = synthetic.w8a8(9, 13, 40, True, seed=33)
+    x, w, pts, deq = (d[key].numpy() for key in ("x", "w", "pts", "deq"))
+    b = synthetic.bias(13, 0.1, seed=34).numpy()
+    _, y = oracle.w8a8(x, w, True, pts, deq)
+    ref = torch.nn.functional.linear(torch.from_numpy(x.astype(np.float64) * pts.astype(np.float64)[:, None]),
+                                     torch.from_numpy(w.astype(np.float64) * deq.astype(np.float64)[:, None]),
+                                     torch.from_numpy(b.astype(np.float64))).numpy()
+    np.testing.assert_allclose(oracle.add_bias(y, b), ref, rtol=1e-12, atol=1e-12)
+
+
 def test_gemm_int32_overflow_is_reported():
     """The definition asserts the accumulator fits int32: (-128)^2 * 2^17 = 2^31 does not."""
     k = 1 << 17
