@@ -75,6 +75,7 @@ def lib() -> ctypes.CDLL:
             "qlinear_pack_ternary": (i32, [vp, i32, i64, i64, f64, vp, vp, vp, sz, vp]),
             "qlinear_pack_int4": (i32, [vp, i64, i64, i32, vp, vp]),
             "qlinear_gemm_w8a8": (i32, [vp, vp, i32, vp, vp, vp, i64, i64, i64, i32, vp, vp]),
+            "qlinear_gemm_w8a8_batched": (i32, [vp, vp, i32, vp, i64, vp, vp, i64, i64, i64, i64, i32, vp, vp]),
             "qlinear_gemm_w2a8": (i32, [vp, vp, vp, vp, vp, vp, i64, i64, i64, i32, vp, vp]),
             "qlinear_gemm_w4a8_grouped": (i32, [vp, i32, vp, vp, vp, vp, i64, i64, i64, i64, vp, i32, vp,
                                                 vp]),
@@ -219,6 +220,33 @@ def qlinear_gemm_w8a8(x, w, layout, deq_scale, per_token_scale, out_dtype=torch.
     _need(out, m * n * out.element_size(), "out")
     _check("qlinear_gemm_w8a8", lib().qlinear_gemm_w8a8(
         _ptr(x), _ptr(w), layout, _ptr(deq_scale), _ptr(per_token_scale), _ptr(bias), m, n, k,
+        _TORCH_TO_QL[out_dtype], _ptr(out), _stream(x)))
+    return out
+
+
+def qlinear_gemm_w8a8_batched(x, w, layout, deq_scale, per_token_scale, out_dtype=torch.float16, out=None,
+                              bias=None):
+    """``batch`` independent W8A8 products: ``x[batch,m,k]``, ``w[batch,k,n]`` or ``[batch,n,k]``,
+    ``per_token_scale[batch,m]``, ``deq_scale[n]`` (shared) or ``[batch,n]``, optional ``bias[n]``."""
+    _gpu(x, "x", torch.int8)
+    _gpu(w, "w", torch.int8)
+    if x.dim() != 3 or w.dim() != 3 or w.shape[0] != x.shape[0]:
+        raise ValueError(f"x {tuple(x.shape)} and w {tuple(w.shape)} must be [batch, ., .] of one batch")
+    batch, m, k = x.shape
+    n = w.shape[2] if layout == QL_W_KN else w.shape[1]
+    if (w.shape[1] if layout == QL_W_KN else w.shape[2]) != k:
+        raise ValueError(f"w {tuple(w.shape)} does not match x {tuple(x.shape)}")
+    deq_stride = 0
+    if out_dtype != torch.int32:
+        _gpu(deq_scale, "deq_scale", torch.float32)
+        deq_stride = n if deq_scale.dim() == 2 else 0
+        _need(deq_scale, 4 * n * (batch if deq_stride else 1), "deq_scale")
+        _need(_gpu(per_token_scale, "per_token_scale", torch.float32), 4 * batch * m, "per_token_scale")
+    _bias(bias, n, out_dtype)
+    out = _empty((batch, m, n), out_dtype, x) if out is None else _gpu(out, "out", out_dtype)
+    _need(out, batch * m * n * out.element_size(), "out")
+    _check("qlinear_gemm_w8a8_batched", lib().qlinear_gemm_w8a8_batched(
+        _ptr(x), _ptr(w), layout, _ptr(deq_scale), deq_stride, _ptr(per_token_scale), _ptr(bias), batch, m, n, k,
         _TORCH_TO_QL[out_dtype], _ptr(out), _stream(x)))
     return out
 

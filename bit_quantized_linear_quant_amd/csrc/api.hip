@@ -140,6 +140,26 @@ ql_status qlinear_gemm_w8a8(const int8_t *x, const int8_t *w, ql_wlayout layout,
     return hip_status(ql::launch_gemm_i8(a, as_stream(stream)));
 }
 
+ql_status qlinear_gemm_w8a8_batched(const int8_t *x, const int8_t *w, ql_wlayout layout, const float *deq_scale,
+                                    int64_t deq_batch_stride, const float *per_token_scale, const float *bias,
+                                    int64_t batch, int64_t m, int64_t n, int64_t k, ql_dtype out_dtype, void *out,
+                                    void *stream) {
+    if (batch < 1 || batch > 65535 || (deq_batch_stride != 0 && deq_batch_stride != n)) return QL_ERR_SHAPE;
+    int ok;
+    if (!x || !w || !out) return QL_ERR_NULL;
+    const ql_status ds = gemm_out_kind(out_dtype, &ok);
+    if (ds != QL_OK) return ds;
+    if (ok != ql::OUT_I32 && (!deq_scale || !per_token_scale)) return QL_ERR_NULL;
+    if (ok == ql::OUT_I32 && bias) return QL_ERR_UNSUPPORTED;
+    if (layout != QL_W_KN && layout != QL_W_NK) return QL_ERR_UNSUPPORTED;
+    if (m < 1 || n < 1 || k < 1 || k > kMaxK || n > 0x7fffffff) return QL_ERR_SHAPE;
+    if (!aligned16(x) || !aligned16(w) || !aligned16(out) || !aligned16(bias)) return QL_ERR_ALIGN;
+    if (ok != ql::OUT_I32 && (!aligned16(deq_scale) || !aligned16(per_token_scale))) return QL_ERR_ALIGN;
+    ql::GemmI8Args a{x, w, layout == QL_W_NK, ql::EPI_ROWCOL, per_token_scale, deq_scale, nullptr,
+                     nullptr, 0.0f, m, n, k, ok, out, bias, batch, deq_batch_stride};
+    return hip_status(ql::launch_gemm_i8(a, as_stream(stream)));
+}
+
 ql_status qlinear_gemm_w2a8(const int8_t *xq, const float *per_token_scale, const int32_t *rowsum,
                             const uint32_t *packed, const double *gamma, const float *bias, int64_t m, int64_t n,
                             int64_t k, ql_dtype out_dtype, void *out, void *stream) {

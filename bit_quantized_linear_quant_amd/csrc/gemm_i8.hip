@@ -47,7 +47,20 @@ struct Params {
     int64_t m, n, k;
     void *out;
     const float *bias;   // [n] or NULL
+    // element strides between batches (blockIdx.z); out's in bytes
+    int64_t bx, bw, bpts, bdeq, bout;
 };
+
+// Move the operand pointers to this workgroup's batch (grid z).  A
+// non-batched launch has one z and leaves them as they are.
+__device__ __forceinline__ void to_batch(Params &p) {
+    const int64_t b = blockIdx.z;
+    p.x += b * p.bx;
+    p.w += b * p.bw;
+    if (p.pts) p.pts += b * p.bpts;
+    if (p.deq) p.deq += b * p.bdeq;
+    p.out = static_cast<char *>(p.out) + b * p.bout;
+}
 
 // Per-row and per-column epilogue factors: (acc * row) * col, rounded once
 // per multiply in fp32, then to the output type.  Per-row factors of a tile
@@ -176,6 +189,7 @@ __global__ __launch_bounds__(LThreads, 1) void gemm_i8_big_kernel(Params p, int 
     constexpr int SMEM = NBUF * STAGE > 1024 + 4 * 128 * EPITCH ? NBUF * STAGE : 1024 + 4 * 128 * EPITCH;
     __shared__ __attribute__((aligned(1024))) int8_t smem[SMEM];
 
+    to_batch(p);
     const int lane = threadIdx.x % kWave, wave = wave_id();
     const int wm = wave / 2, wn = wave % 2;
     int tm, tn;
@@ -364,6 +378,7 @@ __global__ __launch_bounds__(kThreads) void gemm_i8_kernel(Params p) {
     __shared__ __attribute__((aligned(16))) int8_t As[BM * kLdsRow];
     __shared__ __attribute__((aligned(16))) int8_t Bs[BN * kLdsRow];
 
+    to_batch(p);
     const int tid = threadIdx.x;
     const int lane = tid % kWave;
     const int wave = tid / kWave;
@@ -468,8 +483,8 @@ __global__ __launch_bounds__(kThreads) void gemm_i8_kernel(Params p) {
 }
 
 template <bool NK, bool VEC, int EPI, int OUT>
-hipError_t launch_t(const Params &p, hipStream_t st) {
-    dim3 grid((unsigned)((p.n + BN - 1) / BN), (unsigned)((p.m + BM - 1) / BM));
+hipError_t launch_t(const Params &p, int64_t batch, hipStream_t st) {
+    dim3 grid((unsigned)((p.n + BN - 1) / BN), (unsigned)((p.m + BM - 1) / BM), (unsigned)batch);
     hipLaunchKernelGGL((gemm_i8_kernel<NK, VEC, EPI, OUT>), grid, dim3(kThreads), 0, st, p);
     return hipGetLastError();
 }
@@ -478,35 +493,36 @@ constexpr int kBigBK = 64;     // k bytes per slice
 constexpr int kBigBuf = 3;     // slices in the LDS ring (two in flight ahead)
 
 template <int EPI, int OUT>
-hipError_t launch_big(const Params &p, hipStream_t st) {
+hipError_t launch_big(const Params &p, int64_t batch, hipStream_t st) {
     const int tiles_m = (int)((p.m + LB - 1) / LB), tiles_n = (int)((p.n + LB - 1) / LB);
-    hipLaunchKernelGGL((gemm_i8_big_kernel<kBigBK, kBigBuf, EPI, OUT>), dim3((unsigned)(tiles_m * tiles_n)),
-                       dim3(LThreads), 0, st, p, tiles_m, tiles_n);
+    hipLaunchKernelGGL((gemm_i8_big_kernel<kBigBK, kBigBuf, EPI, OUT>),
+                       dim3((unsigned)(tiles_m * tiles_n), 1, (unsigned)batch), dim3(LThreads), 0, st, p, tiles_m,
+                       tiles_n);
     return hipGetLastError();
 }
 
 template <bool NK, bool VEC, int EPI>
-hipError_t launch_out(int out_kind, const Params &p, hipStream_t st) {
+hipError_t launch_out(int out_kind, const Params &p, int64_t batch, hipStream_t st) {
     switch (out_kind) {
-        case OUT_F16: return launch_t<NK, VEC, EPI, OUT_F16>(p, st);
-        case OUT_BF16: return launch_t<NK, VEC, EPI, OUT_BF16>(p, st);
-        default: return launch_t<NK, VEC, EPI, OUT_I32>(p, st);
+        case OUT_F16: return launch_t<NK, VEC, EPI, OUT_F16>(p, batch, st);
+        case OUT_BF16: return launch_t<NK, VEC, EPI, OUT_BF16>(p, batch, st);
+        default: return launch_t<NK, VEC, EPI, OUT_I32>(p, batch, st);
     }
 }
 
 template <int EPI>
-hipError_t launch_big_out(int out_kind, const Params &p, hipStream_t st) {
+hipError_t launch_big_out(int out_kind, const Params &p, int64_t batch, hipStream_t st) {
     switch (out_kind) {
-        case OUT_F16: return launch_big<EPI, OUT_F16>(p, st);
-        case OUT_BF16: return launch_big<EPI, OUT_BF16>(p, st);
-        default: return launch_big<EPI, OUT_I32>(p, st);
+        case OUT_F16: return launch_big<EPI, OUT_F16>(p, batch, st);
+        case OUT_BF16: return launch_big<EPI, OUT_BF16>(p, batch, st);
+        default: return launch_big<EPI, OUT_I32>(p, batch, st);
     }
 }
 
 template <bool NK, bool VEC>
-hipError_t launch_epi(int epi, int out_kind, const Params &p, hipStream_t st) {
-    return epi == EPI_ROWCOL ? launch_out<NK, VEC, EPI_ROWCOL>(out_kind, p, st)
-                             : launch_out<NK, VEC, EPI_SCALARS>(out_kind, p, st);
+hipError_t launch_epi(int epi, int out_kind, const Params &p, int64_t batch, hipStream_t st) {
+    return epi == EPI_ROWCOL ? launch_out<NK, VEC, EPI_ROWCOL>(out_kind, p, batch, st)
+                             : launch_out<NK, VEC, EPI_SCALARS>(out_kind, p, batch, st);
 }
 
 }  // namespace
@@ -517,17 +533,21 @@ bool gemm_i8_uses_big_tiles(bool w_nk, int64_t m, int64_t n, int64_t k) {
 }
 
 hipError_t launch_gemm_i8(const GemmI8Args &a, hipStream_t st) {
-    Params p{a.x, a.w, a.pts, a.deq, a.sa, a.sw, a.eps, a.m, a.n, a.k, a.out, a.bias};
+    const int64_t batch = a.batch < 1 ? 1 : a.batch;
+    if (batch > 65535) return hipErrorInvalidValue;
+    const int64_t es = a.out_kind == OUT_I32 ? 4 : 2;
+    Params p{a.x, a.w, a.pts, a.deq, a.sa, a.sw, a.eps, a.m, a.n, a.k, a.out, a.bias,
+             a.m * a.k, a.n * a.k, a.m, a.deq_stride, a.m * a.n * es};
     if (gemm_i8_uses_big_tiles(a.w_nk, a.m, a.n, a.k))
-        return a.epi == EPI_ROWCOL ? launch_big_out<EPI_ROWCOL>(a.out_kind, p, st)
-                                   : launch_big_out<EPI_SCALARS>(a.out_kind, p, st);
+        return a.epi == EPI_ROWCOL ? launch_big_out<EPI_ROWCOL>(a.out_kind, p, batch, st)
+                                   : launch_big_out<EPI_SCALARS>(a.out_kind, p, batch, st);
     if (a.m > (int64_t)BM * 65535) return hipErrorInvalidValue;
     const bool vec = (a.k % 16) == 0;
     if (a.w_nk)
-        return vec ? launch_epi<true, true>(a.epi, a.out_kind, p, st)
-                   : launch_epi<true, false>(a.epi, a.out_kind, p, st);
-    return vec ? launch_epi<false, true>(a.epi, a.out_kind, p, st)
-               : launch_epi<false, false>(a.epi, a.out_kind, p, st);
+        return vec ? launch_epi<true, true>(a.epi, a.out_kind, p, batch, st)
+                   : launch_epi<true, false>(a.epi, a.out_kind, p, batch, st);
+    return vec ? launch_epi<false, true>(a.epi, a.out_kind, p, batch, st)
+               : launch_epi<false, false>(a.epi, a.out_kind, p, batch, st);
 }
 
 }  // namespace ql

@@ -41,6 +41,11 @@ struct GemmI8Args {
     int out_kind;        // OutKind
     void *out;           // [m, n]
     const float *bias;   // [n] added after the dequant, or NULL
+    // Independent products over grid z: batch b reads x + b*m*k, w + b*n*k,
+    // pts + b*m, deq + b*deq_stride (0: one [n] for every batch) and writes
+    // out + b*m*n.  batch 0 is read as 1.
+    int64_t batch;
+    int64_t deq_stride;
 };
 hipError_t launch_gemm_i8(const GemmI8Args &a, hipStream_t st);
 // True when the product runs on the 256 x 256 direct-to-LDS kernel.

@@ -211,6 +211,28 @@ ql_status qlinear_gemm_w8a8(const int8_t *x, const int8_t *w, ql_wlayout layout,
                             ql_dtype out_dtype, void *out, void *stream);
 
 /*
+ * Batched per-token W8A8 linear ([PT] Input and Output: x [batch,m,k],
+ * weight [batch,k,n], output [batch,m,n]): `batch` independent products,
+ * each exactly qlinear_gemm_w8a8 on its own slice:
+ *   out[b] = qlinear_gemm_w8a8(x[b], w[b], deq_scale + b*deq_batch_stride,
+ *                              per_token_scale + b*m, bias)
+ *   x [batch, m, k] int8; w [batch, k, n] (QL_W_KN) or [batch, n, k] (QL_W_NK);
+ *   per_token_scale [batch, m] fp32 (one per token row);
+ *   deq_scale fp32 [n] shared by every batch (deq_batch_stride 0, [PT] Input
+ *   gives deqScale as [n]) or [batch, n] (deq_batch_stride n); other strides
+ *   are QL_ERR_SHAPE;
+ *   bias [n] fp32 or NULL, shared by every batch (QL_BIAS);
+ *   out [batch, m, n] QL_F16 / QL_BF16 / QL_I32.
+ * 1 <= batch <= 65535; m, n, k as for qlinear_gemm_w8a8.  One launch covers
+ * every batch.
+ */
+ql_status qlinear_gemm_w8a8_batched(const int8_t *x, const int8_t *w, ql_wlayout layout,
+                                    const float *deq_scale, int64_t deq_batch_stride,
+                                    const float *per_token_scale, const float *bias,
+                                    int64_t batch, int64_t m, int64_t n, int64_t k,
+                                    ql_dtype out_dtype, void *out, void *stream);
+
+/*
  * BitLinear product on packed ternary weights ([BL] forward steps 4-5):
  *   acc[m][n] = sum_k xq[m][k] * code[n][k]
  *   out[m][n] = fl32(fl32(acc * per_token_scale[m]) * fp32(*gamma))

@@ -267,6 +267,21 @@ def w8a8(x, w, layout_nk: bool, pts, deq):
     return acc, dequant(acc, pts, deq)
 
 
+def w8a8_batched(x, w, layout_nk: bool, pts, deq):
+    """``batch`` independent per-token W8A8 products ("Per-token Quantization
+    for Matmul" Input / Output with a leading batch dimension): ``(acc, y)``
+    of shapes ``[batch, m, n]``.  ``deq`` is ``[n]`` (every batch) or
+    ``[batch, n]``; ``pts`` is ``[batch, m]``."""
+    x, w = np.asarray(x), np.asarray(w)
+    deq = np.asarray(deq)
+    accs, ys = [], []
+    for b in range(x.shape[0]):
+        acc, y = w8a8(x[b], w[b], layout_nk, np.asarray(pts)[b], deq[b] if deq.ndim == 2 else deq)
+        accs.append(acc)
+        ys.append(y)
+    return np.stack(accs), np.stack(ys)
+
+
 def w2a8(xq, pts, codes, gamma: float):
     """BitLinear product on int8 activation codes and ternary codes ``[n,k]``.
 

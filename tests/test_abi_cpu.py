@@ -100,6 +100,13 @@ def test_gemm_validation(L):
     assert w8(A, A, 3, A, A, NULL, 2, 3, 2, ql.QL_F16, A, NULL) == -6
     assert w8(A, A, ql.QL_W_KN, A, A, A, 2, 3, 2, ql.QL_I32, A, NULL) == -6  # bias on the raw accumulator
     assert w8(A, A, ql.QL_W_KN, A, A, U, 2, 3, 2, ql.QL_F16, A, NULL) == -4
+    wb = L.qlinear_gemm_w8a8_batched
+    assert wb(A, A, ql.QL_W_NK, A, 0, A, NULL, 0, 2, 3, 2, ql.QL_F16, A, NULL) == -2      # batch 0
+    assert wb(A, A, ql.QL_W_NK, A, 0, A, NULL, 65536, 2, 3, 2, ql.QL_F16, A, NULL) == -2  # grid z limit
+    assert wb(A, A, ql.QL_W_NK, A, 5, A, NULL, 2, 2, 3, 2, ql.QL_F16, A, NULL) == -2      # deq stride not 0 or n
+    assert wb(A, A, ql.QL_W_NK, NULL, 0, A, NULL, 2, 2, 3, 2, ql.QL_F16, A, NULL) == -1
+    assert wb(A, A, ql.QL_W_NK, A, 3, A, A, 2, 2, 3, 2, ql.QL_I32, A, NULL) == -6
+    assert wb(U, A, ql.QL_W_NK, A, 3, A, NULL, 2, 2, 3, 2, ql.QL_F16, A, NULL) == -4
     w2 = L.qlinear_gemm_w2a8
     assert w2(A, A, NULL, A, A, NULL, 1, 16, 256, ql.QL_BF16, A, NULL) == -1
     assert w2(A, A, A, A, A, NULL, 1, 24, 256, ql.QL_BF16, A, NULL) == -2

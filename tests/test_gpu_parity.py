@@ -105,6 +105,41 @@ def test_w8a8_deterministic():
     assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
 
 
+@pytest.mark.parametrize("batch,m,n,k,nk,per_batch_deq", [
+    (3, 16, 128, 256, False, False),    # the per-token W8A8 workload, batched
+    (4, 300, 270, 200, True, True),
+    (2, 520, 777, 192, True, False),    # 256 x 256 direct-to-LDS tiles
+    (3, 512, 512, 128, True, True),
+    (5, 77, 45, 77, True, True),        # byte loads
+    (2, 33, 50, 77, False, False),
+    (2, 1, 1, 1, False, True),
+])
+def test_w8a8_batched_parity(batch, m, n, k, nk, per_batch_deq):
+    ds = [synthetic.w8a8(m, n, k, nk, seed=1900 + 10 * b + m + n + k) for b in range(batch)]
+    x = torch.stack([d["x"] for d in ds])
+    w = torch.stack([d["w"] for d in ds])
+    pts = torch.stack([d["pts"] for d in ds])
+    deq = torch.stack([d["deq"] for d in ds]) if per_batch_deq else ds[0]["deq"]
+    b = synthetic.bias(n, 1.0, seed=2000 + n)
+    acc, y = oracle.w8a8_batched(x.numpy(), w.numpy(), nk, pts.numpy(), deq.numpy())
+    layout = ql.QL_W_NK if nk else ql.QL_W_KN
+    args = (_cuda(x), _cuda(w), layout, _cuda(deq), _cuda(pts))
+    oi = poison((batch, m, n), torch.int32)
+    ql.qlinear_gemm_w8a8_batched(args[0], args[1], layout, None, None, out_dtype=torch.int32, out=oi)
+    outs = {}
+    for dt in (torch.float16, torch.bfloat16):
+        outs[dt] = poison((batch, m, n), dt)
+        ql.qlinear_gemm_w8a8_batched(*args, out_dtype=dt, out=outs[dt])
+    ob = poison((batch, m, n), torch.float16)
+    ql.qlinear_gemm_w8a8_batched(*args, out_dtype=torch.float16, out=ob, bias=_cuda(b))
+    _sync()
+    assert_equal(oi, acc, "batched int32 accumulator")
+    for dt, o in outs.items():
+        assert_float_close(o, y, f"batched {dt}")
+    yb = np.stack([oracle.add_bias(y[i], b.numpy()) for i in range(batch)])
+    assert_float_close(ob, yb, "batched + bias", extra=np.stack([_bias_tol(y[i], b.numpy()) for i in range(batch)]))
+
+
 # ---------------------------------------------------------------------------
 # Per-token activation quantization
 # ---------------------------------------------------------------------------

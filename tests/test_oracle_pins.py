@@ -92,6 +92,25 @@ def test_bias_is_added_per_output_column_unscaled():
     np.testing.assert_allclose(oracle.add_bias(y, b), ref, rtol=1e-12, atol=1e-12)
 
 
+@pytest.mark.parametrize("layout_nk,per_batch_deq", [(False, False), (True, True)])
+def test_batched_is_independent_products(layout_nk, per_batch_deq):
+    """Each batch is its own product: numpy int64 ``einsum`` for the
+    accumulators, fp64 dequant of each batch's slices for y."""
+    batch, m, n, k = 3, 5, 7, 40
+    ds = [synthetic.w8a8(m, n, k, layout_nk, seed=40 + b) for b in range(batch)]
+    x = np.stack([d["x"].numpy() for d in ds])
+    w = np.stack([d["w"].numpy() for d in ds])
+    pts = np.stack([d["pts"].numpy() for d in ds])
+    deq = np.stack([d["deq"].numpy() for d in ds]) if per_batch_deq else ds[0]["deq"].numpy()
+    acc, y = oracle.w8a8_batched(x, w, layout_nk, pts, deq)
+    wk = np.swapaxes(w, 1, 2) if layout_nk else w  # [batch, k, n]
+    ref = np.einsum("bmk,bkn->bmn", x.astype(np.int64), wk.astype(np.int64))
+    assert np.array_equal(acc.astype(np.int64), ref)
+    d2 = deq if per_batch_deq else np.broadcast_to(deq, (batch, n))
+    yref = ref.astype(np.float64) * pts.astype(np.float64)[:, :, None] * d2.astype(np.float64)[:, None, :]
+    np.testing.assert_allclose(y, yref, rtol=1e-15, atol=0)
+
+
 def test_gemm_int32_overflow_is_reported():
     """The definition asserts the accumulator fits int32: (-128)^2 * 2^17 = 2^31 does not."""
     k = 1 << 17
