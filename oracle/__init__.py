@@ -17,9 +17,10 @@ Sources (web pages, cited by title and section):
 * docs.rs vyre-libs 0.7.2, "linear_4bit/mod.rs" -- module doc comment,
   QuantizedLinear4BitPlannerEvidence.
 
-Every function here is pinned by ``tests/test_oracle_pins.py`` except the two
-pack layouts, which are this project's own definitions: "parity unpinned"
-beyond their round trip and the end-to-end products that consume them.
+Every function here is pinned by ``tests/test_oracle_pins.py`` except the
+three pack layouts (ternary words, 4-bit words, FP6 operand tiles), which are
+this project's own definitions: "parity unpinned" beyond their round trip and
+the end-to-end products that consume them.
 """
 from __future__ import annotations
 
@@ -72,6 +73,8 @@ def _load():
             "oracle_gemm_i8": (i32, [vp, vp, i32, i64, i64, i64, vp]),
             "oracle_dequant": (i32, [vp, vp, vp, i64, i64, vp]),
             "oracle_quant_int4_tensor": (i32, [vp, i64, f32, f32, vp]),
+            "oracle_a4w4_operand_bytes": (i64, [i64, i64]),
+            "oracle_pack_a4w4_fp6": (i32, [vp, i64, i64, vp]),
             "oracle_round_f16": (None, [vp, i64, vp]),
             "oracle_round_bf16": (None, [vp, i64, vp]),
         }
@@ -330,6 +333,21 @@ def a4w4(x, w, scale_a: float, scale_w: float, eps: float):
     sa, sw = effective_scale(scale_a, eps), effective_scale(scale_w, eps)
     y = acc.astype(np.float64) * float(sa) * float(sw)
     return qa, qw, acc, y
+
+
+def a4w4_operand_bytes(rows: int, k: int) -> int:
+    return int(_load().oracle_a4w4_operand_bytes(rows, k))
+
+
+def pack_a4w4_fp6(codes):
+    """4-bit codes ``[rows, k]`` (int8, in [-8, 7]) as the packed FP6 E3M2
+    operand tiles of the 4-bit product (this project's layout, defined in
+    ``qlinear_oracle.c``).  Returns uint8 bytes."""
+    codes = _c(codes, np.int8)
+    rows, k = codes.shape
+    out = np.zeros(a4w4_operand_bytes(rows, k), np.uint8)
+    _check(_load().oracle_pack_a4w4_fp6(_p(codes), rows, k, _p(out)), "pack_a4w4_fp6")
+    return out
 
 
 # --------------------------------------------------------------------------

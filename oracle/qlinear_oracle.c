@@ -462,6 +462,65 @@ int oracle_quant_int4_tensor(const float *x, int64_t count, float scale,
 }
 
 /* ------------------------------------------------------------------ */
+/* A4W4 operand tiles: 4-bit codes written as FP6 E3M2 values.          */
+/* ------------------------------------------------------------------ */
+/*
+ * Not a format of the pages: this project's packed operand for the 4-bit
+ * product ("Q4LinearFunction" forward multiplies 4-bit codes in [-8, 7]).
+ * Each code is written as the FP6 E3M2 number of the same value (OCP
+ * Microscaling Formats v1.0: 1 sign bit, 3 exponent bits with bias 3, 2
+ * mantissa bits; every integer in [-8, 7] is exact).  Rows are padded with
+ * zero codes to a multiple of 32 and k to a multiple of 128.  Tile (rb, ks)
+ * covers rows 32rb .. 32rb+31 and k 64ks .. 64ks+63 and occupies 1536 bytes
+ * at (rb * (kp / 64) + ks) * 1536.  Slot l (0..63) of a tile holds row
+ * 32rb + l % 32 and k 64ks + 32(l / 32) + j for j = 0..31 as a 192-bit
+ * little-endian string with element j in bits 6j .. 6j+5; its bytes 0..15
+ * sit at tile byte 16l and bytes 16..23 at tile byte 1024 + 8l.
+ * Parity unpinned beyond its definition: tests decode it and compare codes.
+ */
+static unsigned e3m2_of_code(int c)
+{
+    unsigned sign = c < 0 ? 1u : 0u;
+    unsigned a = (unsigned)(c < 0 ? -c : c);
+    unsigned e = 0, m;
+    if (a == 0) return 0u;
+    /* a = 2^p * (1 + m/4) with p = floor(log2 a); biased exponent p + 3 */
+    while ((2u << e) <= a) e++;
+    m = (a * 4u) / (1u << e) - 4u;
+    return (sign << 5) | ((e + 3u) << 2) | m;
+}
+
+int64_t oracle_a4w4_operand_bytes(int64_t rows, int64_t k)
+{
+    int64_t rp = (rows + 31) / 32 * 32, kp = (k + 127) / 128 * 128;
+    return rp * kp * 3 / 4;
+}
+
+int oracle_pack_a4w4_fp6(const int8_t *codes, int64_t rows, int64_t k, uint8_t *out)
+{
+    int64_t rp = (rows + 31) / 32 * 32, kp = (k + 127) / 128 * 128;
+    int64_t kt = kp / 64;
+    for (int64_t rb = 0; rb < rp / 32; rb++)
+        for (int64_t ks = 0; ks < kt; ks++) {
+            uint8_t *tile = out + (rb * kt + ks) * 1536;
+            for (int l = 0; l < 64; l++) {
+                uint8_t img[24] = {0};
+                int64_t row = 32 * rb + l % 32;
+                for (int j = 0; j < 32; j++) {
+                    int64_t kk = 64 * ks + 32 * (l / 32) + j;
+                    int c = (row < rows && kk < k) ? codes[row * k + kk] : 0;
+                    unsigned v = e3m2_of_code(c);
+                    for (int b = 0; b < 6; b++)
+                        if ((v >> b) & 1u) img[(6 * j + b) / 8] |= (uint8_t)(1u << ((6 * j + b) % 8));
+                }
+                for (int b = 0; b < 16; b++) tile[16 * l + b] = img[b];
+                for (int b = 0; b < 8; b++) tile[1024 + 8 * l + b] = img[16 + b];
+            }
+        }
+    return 0;
+}
+
+/* ------------------------------------------------------------------ */
 /* Output rounding: fp64 -> fp16 / bf16, round to nearest, ties to even. */
 /* ------------------------------------------------------------------ */
 /*

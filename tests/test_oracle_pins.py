@@ -457,6 +457,48 @@ def test_a4w4_dequant_brute_force():
 # ---------------------------------------------------------------------------
 # Output rounding
 # ---------------------------------------------------------------------------
+def _e3m2_value(c: int) -> float:
+    """OCP MX FP6 E3M2: (-1)^s 2^(e-3) (1 + m/4), or 2^-2 (m/4) when e = 0."""
+    s, e, m = (c >> 5) & 1, (c >> 2) & 7, c & 3
+    v = (m / 4) * 2.0 ** -2 if e == 0 else (1 + m / 4) * 2.0 ** (e - 3)
+    return -v if s else v
+
+
+def _unpack_a4w4_fp6(buf: np.ndarray, rows: int, k: int) -> np.ndarray:
+    """Decode the operand tiles by their written definition (slot l of tile
+    (rb, ks): row 32rb + l%32, k 64ks + 32(l//32) + j, 6 bits per element,
+    bytes 0..15 at 16l and 16..23 at 1024 + 8l)."""
+    rp, kp = -(-rows // 32) * 32, -(-k // 128) * 128
+    out = np.full((rp, kp), np.nan)
+    for rb in range(rp // 32):
+        for ks in range(kp // 64):
+            t = (rb * (kp // 64) + ks) * 1536
+            for l in range(64):
+                img = bytes(buf[t + 16 * l:t + 16 * l + 16]) + bytes(buf[t + 1024 + 8 * l:t + 1024 + 8 * l + 8])
+                bits = int.from_bytes(img, "little")
+                for j in range(32):
+                    out[32 * rb + l % 32, 64 * ks + 32 * (l // 32) + j] = _e3m2_value((bits >> (6 * j)) & 63)
+    return out
+
+
+def test_a4w4_fp6_operand_encodes_every_code_exactly():
+    """Every 4-bit code is its own FP6 E3M2 value; padding rows and k hold 0."""
+    codes = np.arange(-8, 8, dtype=np.int8).reshape(1, 16)
+    buf = oracle.pack_a4w4_fp6(codes)
+    assert buf.size == oracle.a4w4_operand_bytes(1, 16) == 32 * 128 * 3 // 4
+    dec = _unpack_a4w4_fp6(buf, 1, 16)
+    assert dec[0, :16].tolist() == list(range(-8, 8))
+    assert np.all(dec[1:, :] == 0) and np.all(dec[0, 16:] == 0)
+
+
+@pytest.mark.parametrize("rows,k", [(45, 200), (32, 128), (64, 256)])
+def test_a4w4_fp6_operand_round_trip(rows, k):
+    codes = synthetic.rng(50 + rows).integers(-8, 8, (rows, k), dtype=np.int8)
+    dec = _unpack_a4w4_fp6(oracle.pack_a4w4_fp6(codes), rows, k)
+    assert np.array_equal(dec[:rows, :k], codes.astype(np.float64))
+    assert np.all(dec[rows:, :] == 0) and np.all(dec[:, k:] == 0)
+
+
 def test_round_f16_matches_numpy():
     g = synthetic.rng(51)
     v = np.concatenate([g.standard_normal(20000) * 10.0 ** g.integers(-9, 6, 20000),
