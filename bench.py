@@ -1,18 +1,20 @@
 """Benchmark of the quantized linear layer on one MI355X.
 
 Step: one Q4Linear (A4W4) forward on the 8192^3 workload -- per-tensor 4-bit
-quantization of x[8192,8192] and w[8192,8192] (fp16), then the int8 matrix-
-core product with the fused fp16 epilogue -- the large-M GEMM that the
-metric's int8 TOPS figure is quoted on.  Inputs are resident in HBM before the
-timed region; W untimed warm-up steps precede exactly K timed steps bracketed
-by device synchronization.
+quantization of x[8192,8192] and w[8192,8192] (fp16) into packed FP6 E3M2
+operands (every 4-bit code is exact in E3M2), then the FP6 matrix-core product
+with exact fp32 accumulation and the fused fp16 epilogue -- the large-M GEMM
+that the metric's integer TOPS figure is quoted on.  Inputs are resident in
+HBM before the timed region; W untimed warm-up steps precede exactly K timed
+steps bracketed by device synchronization.
 
 The same JSON line carries:
-  roofline      the int8 GEMM kernel: algorithmic ops per launch / its mean
+  roofline      the FP6 GEMM kernel: algorithmic ops per launch / its mean
                 duration from HIP events recorded around it in the timed
-                region, against the 5.0 POP/s dense int8 peak; `traffic` is
-                the HBM bytes per launch measured by rocprofv3 counters for
-                the current kernel source, else null.
+                region, against the 10.1 PFLOP/s dense FP6 matrix-core peak
+                (the dtype it computes in); `traffic` is the HBM bytes per
+                launch measured by rocprofv3 counters for the current kernel
+                source, else null.
   cpu_baseline  the CPU oracle timed on this host on a bounded row sample of
                 the same forward, scaled to TOPS.
   decode_gemv   the metric's second figure: packed-ternary-weight HBM GB/s of
@@ -36,6 +38,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "int8 TOPS (large-M GEMM) + packed-weight HBM GB/s (M≤16 GEMV), % roofline"
 PEAK_INT8_TOPS = 5000.0      # MI355X dense int8 MFMA, 5.0 POP/s
+PEAK_FP6_TOPS = 10100.0      # MI355X dense FP6 / FP4 MFMA, 10.1 PFLOP/s
 PEAK_HBM_GBS = 8000.0        # MI355X HBM3E, 8 TB/s
 GEMM_KERNEL_SOURCES = ["gemm_i8.hip", "ql_device.hpp"]
 GEMV_KERNEL_SOURCES = ["gemm_w2a8.hip", "ql_device.hpp"]
@@ -108,7 +111,7 @@ def bench_a4w4(args, ql, torch, synthetic):
     eps = d["eps"]
     out = torch.empty((m, n), dtype=torch.float16, device=dev)
     ws = torch.empty((ql.qlinear_workspace_bytes(ql.QL_OP_GEMM_A4W4, m, n, k),), dtype=torch.uint8, device=dev)
-    xq, wq = ql.a4w4_codes_from_workspace(ws, m, n, k)
+    xa, wb = ql.a4w4_operands_from_workspace(ws, m, n, k)
 
     # A plain device copy of known size: the byte counters' calibration kernel.
     cal_src = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
@@ -119,13 +122,13 @@ def bench_a4w4(args, ql, torch, synthetic):
         # the three launches of qlinear_gemm_a4w4, with events between them
         if ev is not None:
             ev[0].record()
-        ql.qlinear_quant_int4_tensor(x.view(-1), sa, eps, q=xq.view(-1))
+        ql.qlinear_quant_a4w4_operand(x, sa, eps, operand=xa)
         if ev is not None:
             ev[1].record()
-        ql.qlinear_quant_int4_tensor(w.view(-1), sw, eps, q=wq.view(-1))
+        ql.qlinear_quant_a4w4_operand(w, sw, eps, operand=wb)
         if ev is not None:
             ev[2].record()
-        ql.qlinear_gemm_a4w4_codes(xq, wq, sa, sw, eps, out_dtype=torch.float16, out=out)
+        ql.qlinear_gemm_a4w4_operands(xa, wb, m, n, k, sa, sw, eps, out_dtype=torch.float16, out=out)
         if ev is not None:
             ev[3].record()
 
@@ -143,9 +146,26 @@ def bench_a4w4(args, ql, torch, synthetic):
     gm = sum(e[2].elapsed_time(e[3]) for e in evs) / args.steps
     ops = 2.0 * m * n * k
     ms_per_step = wall * 1e3 / args.steps
+    # the int8-code product of the same codes (qlinear_gemm_a4w4_codes), for comparison
+    xq = ql.qlinear_quant_int4_tensor(x.view(-1), sa, eps).view(m, k)
+    wq = ql.qlinear_quant_int4_tensor(w.view(-1), sw, eps).view(n, k)
+    ql.qlinear_gemm_a4w4_codes(xq, wq, sa, sw, eps, out_dtype=torch.float16, out=out)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(10):
+        ql.qlinear_gemm_a4w4_codes(xq, wq, sa, sw, eps, out_dtype=torch.float16, out=out)
+    e1.record()
+    torch.cuda.synchronize()
+    i8 = e0.elapsed_time(e1) / 10
+    del xq, wq
     res = {"m": m, "n": n, "k": k, "ops": ops, "ms_per_step": ms_per_step,
            "value": ops / (ms_per_step * 1e-3) / 1e12,
-           "kernel_ms": {"quant_x": qx, "quant_w": qw, "gemm": gm}, "gemm_tops": ops / (gm * 1e-3) / 1e12}
+           "kernel_ms": {"quant_x": qx, "quant_w": qw, "gemm": gm},
+           "gemm_tops": ops / (gm * 1e-3) / 1e12,
+           "int8_codes_gemm": {"ms": round(i8, 4), "TOPS": round(ops / (i8 * 1e-3) / 1e12, 1),
+                               "frac_int8_peak": round(ops / (i8 * 1e-3) / 1e12 / PEAK_INT8_TOPS, 4),
+                               "kernel": "gemm_i8_big_kernel (qlinear_gemm_a4w4_codes), same codes held in int8"}}
     return res, d
 
 
@@ -387,7 +407,7 @@ def main():
                        ("16", "w2a8_gemv_m16_28672x8192")):
         gemv["by_m"][m_str]["traffic"] = recorded_traffic(key, gemv_src)
     gemm_src = kernel_source_hash(GEMM_KERNEL_SOURCES)
-    traffic = recorded_traffic("gemm_i8_a4w4_8192", gemm_src)
+    traffic = recorded_traffic("gemm_a4w4_f6_8192", gemm_src)
     achieved = res["gemm_tops"]
     line = {
         "metric": METRIC,
@@ -400,18 +420,19 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "int8",
+        "dtype": "fp6",
         "data": "synthetic",
         "config": {"workload": "A4W4 Q4Linear forward: fp16 x[8192,8192] N(0,1), fp16 w[8192,8192] "
-                               "N(0,0.02^2), per-tensor scales max|t|/7, eps 1e-5, 4-bit codes in int8, "
-                               "int8 MFMA product, fp16 out",
+                               "N(0,0.02^2), per-tensor scales max|t|/7, eps 1e-5, 4-bit codes packed as "
+                               "FP6 E3M2 operands, FP6 MFMA product with exact fp32 accumulation, fp16 out",
                    "m": res["m"], "n": res["n"], "k": res["k"], "global_batch": res["m"],
                    "parallelism": "single GPU"},
         "kernel_ms": {key: round(v, 4) for key, v in res["kernel_ms"].items()},
-        "roofline": {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_INT8_TOPS, "unit": "TOPS",
-                     "frac": round(achieved / PEAK_INT8_TOPS, 4), "traffic": traffic,
-                     "kernel": "gemm_i8_big_kernel (qlinear_gemm_a4w4_codes)",
-                     "work_per_launch": f"2*m*n*k = {int(res['ops'])} int8 ops"},
+        "int8_codes_gemm": res["int8_codes_gemm"],
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_FP6_TOPS, "unit": "TOPS",
+                     "frac": round(achieved / PEAK_FP6_TOPS, 4), "traffic": traffic,
+                     "kernel": "gemm_a4w4_f6_kernel (qlinear_gemm_a4w4_operands)",
+                     "work_per_launch": f"2*m*n*k = {int(res['ops'])} ops on 4-bit codes"},
         "decode_gemv": gemv,
     }
     line["path_rows"] = bench_rows(ql, torch, synthetic)

@@ -56,7 +56,9 @@ size_t qlinear_workspace_bytes(ql_op op, int64_t m, int64_t n, int64_t k) {
         case QL_OP_PACK_TERNARY:
             return round256(ql::absmean_partial_count(n * k) * sizeof(double));
         case QL_OP_GEMM_A4W4:
-            return round256((size_t)(m * k)) + round256((size_t)(n * k));
+            return round256(ql::a4w4_operand_bytes(m, k)) + round256(ql::a4w4_operand_bytes(n, k));
+        case QL_OP_A4W4_OPERAND:
+            return ql::a4w4_operand_bytes(m, k);
         default: return 0;
     }
 }
@@ -217,6 +219,31 @@ ql_status qlinear_gemm_a4w4_codes(const int8_t *xq, const int8_t *wq, const floa
     return hip_status(ql::launch_gemm_i8(a, as_stream(stream)));
 }
 
+ql_status qlinear_quant_a4w4_operand(const void *x, ql_dtype x_dtype, int64_t rows, int64_t k, const float *scale,
+                                     float eps, void *operand, void *stream) {
+    if (!x || !scale || !operand) return QL_ERR_NULL;
+    const int kind = in_kind(x_dtype);
+    if (kind < 0) return QL_ERR_DTYPE;
+    if (rows < 1 || k < 1 || k > kMaxK) return QL_ERR_SHAPE;
+    if (!aligned16(x) || !aligned16(operand)) return QL_ERR_ALIGN;
+    return hip_status(ql::launch_quant_a4w4_tiles(kind, x, rows, k, scale, eps, static_cast<uint8_t *>(operand),
+                                                  as_stream(stream)));
+}
+
+ql_status qlinear_gemm_a4w4_operands(const void *xa, const void *wb, const float *scale_a, const float *scale_w,
+                                     float eps, int64_t m, int64_t n, int64_t k, ql_dtype out_dtype, void *out,
+                                     void *stream) {
+    int ok;
+    if (!xa || !wb || !out) return QL_ERR_NULL;
+    const ql_status ds = gemm_out_kind(out_dtype, &ok);
+    if (ds != QL_OK) return ds;
+    if (ok != ql::OUT_I32 && (!scale_a || !scale_w)) return QL_ERR_NULL;
+    if (m < 1 || n < 1 || k < 1 || k > kMaxK || n > 0x7fffffff) return QL_ERR_SHAPE;
+    if (!aligned16(xa) || !aligned16(wb) || !aligned16(out)) return QL_ERR_ALIGN;
+    return hip_status(ql::launch_gemm_a4w4_tiles(static_cast<const uint8_t *>(xa), static_cast<const uint8_t *>(wb),
+                                                 scale_a, scale_w, eps, m, n, k, ok, out, as_stream(stream)));
+}
+
 ql_status qlinear_gemm_a4w4(const void *x, const void *w, ql_dtype in_dtype, const float *scale_a,
                             const float *scale_w, float eps, int64_t m, int64_t n, int64_t k,
                             ql_dtype out_dtype, void *out, void *workspace, size_t ws_bytes, void *stream) {
@@ -230,15 +257,14 @@ ql_status qlinear_gemm_a4w4(const void *x, const void *w, ql_dtype in_dtype, con
     if (!aligned16(x) || !aligned16(w) || !aligned16(out)) return QL_ERR_ALIGN;
     if (!workspace || ws_bytes < qlinear_workspace_bytes(QL_OP_GEMM_A4W4, m, n, k)) return QL_ERR_WORKSPACE;
     if (!aligned16(workspace)) return QL_ERR_ALIGN;
-    int8_t *xq = static_cast<int8_t *>(workspace);
-    int8_t *wq = xq + round256((size_t)(m * k));
+    uint8_t *xa = static_cast<uint8_t *>(workspace);
+    uint8_t *wb = xa + round256(ql::a4w4_operand_bytes(m, k));
     hipStream_t st = as_stream(stream);
-    hipError_t e = ql::launch_quant_int4_tensor(kind, x, m * k, scale_a, eps, xq, st);
+    hipError_t e = ql::launch_quant_a4w4_tiles(kind, x, m, k, scale_a, eps, xa, st);
     if (e != hipSuccess) return QL_ERR_HIP;
-    e = ql::launch_quant_int4_tensor(kind, w, n * k, scale_w, eps, wq, st);
+    e = ql::launch_quant_a4w4_tiles(kind, w, n, k, scale_w, eps, wb, st);
     if (e != hipSuccess) return QL_ERR_HIP;
-    ql::GemmI8Args a{xq, wq, true, ql::EPI_SCALARS, nullptr, nullptr, scale_a, scale_w, eps, m, n, k, ok, out};
-    return hip_status(ql::launch_gemm_i8(a, st));
+    return hip_status(ql::launch_gemm_a4w4_tiles(xa, wb, scale_a, scale_w, eps, m, n, k, ok, out, st));
 }
 
 }  // extern "C"

@@ -178,6 +178,82 @@ __device__ __forceinline__ void big_slice(v16i (&acc)[4][4], const int8_t *__res
     }
 }
 
+// Epilogue of the 256 x 256 tile kernels: lane holds column lane%32 of each
+// 32x32 block and rows 8*(r/4) + 4*(lane/32) + r%4 of register r.  The
+// accumulators are int32, or fp32 holding integers below 2^24 (exact).
+__device__ __forceinline__ int32_t acc_i32(int32_t v) { return v; }
+__device__ __forceinline__ int32_t acc_i32(float v) { return (int32_t)v; }
+
+template <int EPI, int OUT, typename ACC>
+__device__ __forceinline__ void big_epilogue(const Params &p, const ACC (&acc)[4][4], int8_t *smem, int64_t m0,
+                                             int64_t n0, int wm, int wn, int wave, int lane) {
+    constexpr int EPITCH = 128 * 2 + 16;
+    const int fr = lane % 32;
+    Epilogue<EPI, OUT> ep;
+    ep.init(p);
+    ep.stage_rows(p, m0, LB, reinterpret_cast<float *>(smem));
+    __syncthreads();
+    float cf[4], cb[4];
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+        cf[j] = ep.col_factor(p, n0 + wn * 128 + 32 * j + fr);
+        cb[j] = ep.col_bias(p, n0 + wn * 128 + 32 * j + fr);
+    }
+    if constexpr (OUT == OUT_F16 || OUT == OUT_BF16) {
+        // Through LDS: the wave rounds its 128 x 128 sub-tile into a padded
+        // LDS tile (the two row groups of one write land 16 banks apart), then
+        // writes whole 256-byte row segments, 16 bytes per lane.
+        int8_t *tile = smem + 1024 + wave * 128 * EPITCH;
+#pragma unroll
+        for (int i = 0; i < 4; i++)
+#pragma unroll
+            for (int r = 0; r < 16; r++) {
+                const int lr = 32 * i + 8 * (r / 4) + 4 * (lane / 32) + (r % 4);
+                const float rf = ep.row_factor(wm * 128 + lr);
+#pragma unroll
+                for (int j = 0; j < 4; j++) {
+                    const float y = ep.value(p, acc_i32(acc[i][j][r]), rf, cf[j], cb[j]);
+                    *reinterpret_cast<uint16_t *>(tile + lr * EPITCH + 2 * (32 * j + fr)) =
+                        OUT == OUT_F16 ? f32_to_f16_rne(y) : f32_to_bf16_rne(y);
+                }
+            }
+        // each wave reads back only its own sub-tile
+        __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0)
+        __builtin_amdgcn_wave_barrier();
+#pragma unroll
+        for (int q = 0; q < 32; q++) {
+            const int lr = 4 * q + lane / 16, piece = lane % 16;
+            const uint4 v = *reinterpret_cast<const uint4 *>(tile + lr * EPITCH + 16 * piece);
+            const int64_t row = m0 + wm * 128 + lr, col = n0 + wn * 128 + 8 * piece;
+            if (row < p.m) {
+                uint16_t *dst = static_cast<uint16_t *>(p.out) + row * p.n + col;
+                if (col + 8 <= p.n && (p.n % 8) == 0) {
+                    *reinterpret_cast<uint4 *>(dst) = v;
+                } else {
+                    const uint16_t h[8] = {(uint16_t)v.x, (uint16_t)(v.x >> 16), (uint16_t)v.y, (uint16_t)(v.y >> 16),
+                                           (uint16_t)v.z, (uint16_t)(v.z >> 16), (uint16_t)v.w, (uint16_t)(v.w >> 16)};
+#pragma unroll
+                    for (int e = 0; e < 8; e++)
+                        if (col + e < p.n) dst[e] = h[e];
+                }
+            }
+        }
+        return;
+    }
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+        const int64_t col = n0 + wn * 128 + 32 * j + fr;
+        if (col >= p.n) continue;
+#pragma unroll
+        for (int i = 0; i < 4; i++)
+#pragma unroll
+            for (int r = 0; r < 16; r++) {
+                const int local = wm * 128 + 32 * i + 8 * (r / 4) + 4 * (lane / 32) + (r % 4);
+                if (m0 + local < p.m) ep.store(p, m0 + local, col, acc_i32(acc[i][j][r]), ep.row_factor(local), cf[j], cb[j]);
+            }
+    }
+}
+
 template <int BK, int NBUF, int EPI, int OUT>
 __global__ __launch_bounds__(LThreads, 1) void gemm_i8_big_kernel(Params p, int tiles_m, int tiles_n) {
     constexpr int CH = BigTile<BK>::CH, TILE = BigTile<BK>::TILE, PER_WAVE = BigTile<BK>::PER_WAVE;
@@ -256,71 +332,139 @@ __global__ __launch_bounds__(LThreads, 1) void gemm_i8_big_kernel(Params p, int 
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
 
-    // Epilogue: lane holds column lane%32 of each 32x32 block and rows
-    // 8*(r/4) + 4*(lane/32) + r%4 of register r.
-    Epilogue<EPI, OUT> ep;
-    ep.init(p);
-    ep.stage_rows(p, m0, LB, reinterpret_cast<float *>(smem));
-    __syncthreads();
-    float cf[4], cb[4];
+    big_epilogue<EPI, OUT>(p, acc, smem, m0, n0, wm, wn, wave, lane);
+}
+
+// ---------------------------------------------------------------------------
+// 4-bit product on FP6 E3M2 operand tiles
+// ---------------------------------------------------------------------------
+// The tile, ring and epilogue of the large-tile kernel, on
+// v_mfma_scale_f32_32x32x64_f8f6f4 with both operands E3M2 and unit block
+// scales: twice the int8 matrix-core rate per instruction.  Codes are
+// integers in [-8, 7], so every product and partial sum is an integer of
+// magnitude at most 64 k < 2^23 (k <= 131071): the fp32 accumulation is
+// exact and equals the int32 one.  Operand tiles (quant_a4w4_tiles_kernel):
+// 32 rows x 64 k in 1536 bytes, lane l's register image at 16l (16 bytes)
+// and 1024 + 8l (8 bytes); a 128-k slice of a 32-row block is two adjacent
+// tiles, so slices copy to LDS unchanged and every fragment is one 16-byte
+// and one 8-byte read by consecutive lanes.
+constexpr int kF6Tile = 1536;
+constexpr int kF6Op = 8 * 2 * kF6Tile;        // one operand's 256-row x 128-k slice
+constexpr int kF6Buf = 3;
+constexpr int kF6Loads = kF6Op / 1024 / 4;    // 1 KB direct loads per wave and operand
+constexpr int kF6Scale = 0x7f7f7f7f;          // E8M0 127 (2^0) in every byte
+
+__device__ __forceinline__ v8i f6_frag(const int8_t *tile, int lane) {
+    const uint4 a = *reinterpret_cast<const uint4 *>(tile + 16 * lane);
+    const uint2 b = *reinterpret_cast<const uint2 *>(tile + 1024 + 8 * lane);
+    return v8i{(int)a.x, (int)a.y, (int)a.z, (int)a.w, (int)b.x, (int)b.y, 0, 0};
+}
+
+// One 128-k slice: the direct loads of a later slice into `nxt`, then two
+// 64-k MFMA steps on `cur`, the second step's fragments read while the first
+// step's MFMAs issue (distinct restrict pointers, as in big_slice).
+__device__ __forceinline__ void f6_slice(v16f (&acc)[4][4], const int8_t *__restrict__ cur,
+                                         int8_t *__restrict__ nxt, const int8_t *const (&srcA)[kF6Loads],
+                                         const int8_t *const (&srcB)[kF6Loads], int64_t nxt_off, int wm, int wn,
+                                         int lane, int wave) {
 #pragma unroll
-    for (int j = 0; j < 4; j++) {
-        cf[j] = ep.col_factor(p, n0 + wn * 128 + 32 * j + fr);
-        cb[j] = ep.col_bias(p, n0 + wn * 128 + 32 * j + fr);
+    for (int ii = 0; ii < kF6Loads; ii++) {
+        const int inst = wave * kF6Loads + ii;
+        lds_load16(srcA[ii] + nxt_off, nxt + 1024 * inst);
+        lds_load16(srcB[ii] + nxt_off, nxt + kF6Op + 1024 * inst);
     }
-    if constexpr (OUT == OUT_F16 || OUT == OUT_BF16) {
-        // Through LDS: the wave rounds its 128 x 128 sub-tile into a padded
-        // LDS tile (the two row groups of one write land 16 banks apart), then
-        // writes whole 256-byte row segments, 16 bytes per lane.
-        int8_t *tile = smem + 1024 + wave * 128 * EPITCH;
+    v8i fa[2][4], fb[2][4];
+    auto frags = [&](int s) {
+#pragma unroll
+        for (int i = 0; i < 4; i++) fa[s][i] = f6_frag(cur + ((wm * 4 + i) * 2 + s) * kF6Tile, lane);
+#pragma unroll
+        for (int j = 0; j < 4; j++) fb[s][j] = f6_frag(cur + kF6Op + ((wn * 4 + j) * 2 + s) * kF6Tile, lane);
+    };
+    frags(0);
+#pragma unroll
+    for (int s = 0; s < 2; s++) {
+        if (s == 0) frags(1);
 #pragma unroll
         for (int i = 0; i < 4; i++)
 #pragma unroll
-            for (int r = 0; r < 16; r++) {
-                const int lr = 32 * i + 8 * (r / 4) + 4 * (lane / 32) + (r % 4);
-                const float rf = ep.row_factor(wm * 128 + lr);
+            for (int j = 0; j < 4; j++)
+                acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa[s][i], fb[s][j], acc[i][j], 3, 3, 0,
+                                                                            kF6Scale, 0, kF6Scale);
+        if (s == 0) {
 #pragma unroll
-                for (int j = 0; j < 4; j++) {
-                    const float y = ep.value(p, acc[i][j][r], rf, cf[j], cb[j]);
-                    *reinterpret_cast<uint16_t *>(tile + lr * EPITCH + 2 * (32 * j + fr)) =
-                        OUT == OUT_F16 ? f32_to_f16_rne(y) : f32_to_bf16_rne(y);
-                }
-            }
-        // each wave reads back only its own sub-tile
-        __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0)
-        __builtin_amdgcn_wave_barrier();
-#pragma unroll
-        for (int q = 0; q < 32; q++) {
-            const int lr = 4 * q + lane / 16, piece = lane % 16;
-            const uint4 v = *reinterpret_cast<const uint4 *>(tile + lr * EPITCH + 16 * piece);
-            const int64_t row = m0 + wm * 128 + lr, col = n0 + wn * 128 + 8 * piece;
-            if (row < p.m) {
-                uint16_t *dst = static_cast<uint16_t *>(p.out) + row * p.n + col;
-                if (col + 8 <= p.n && (p.n % 8) == 0) {
-                    *reinterpret_cast<uint4 *>(dst) = v;
-                } else {
-                    const uint16_t h[8] = {(uint16_t)v.x, (uint16_t)(v.x >> 16), (uint16_t)v.y, (uint16_t)(v.y >> 16),
-                                           (uint16_t)v.z, (uint16_t)(v.z >> 16), (uint16_t)v.w, (uint16_t)(v.w >> 16)};
-#pragma unroll
-                    for (int e = 0; e < 8; e++)
-                        if (col + e < p.n) dst[e] = h[e];
-                }
+            for (int q = 0; q < 16; q++) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
             }
         }
-        return;
     }
+}
+
+template <int OUT>
+__global__ __launch_bounds__(LThreads, 1) void gemm_a4w4_f6_kernel(Params p, int tiles_m, int tiles_n) {
+    constexpr int STAGE = 2 * kF6Op;
+    constexpr int EPITCH = 128 * 2 + 16;
+    constexpr int SMEM = kF6Buf * STAGE > 1024 + 4 * 128 * EPITCH ? kF6Buf * STAGE : 1024 + 4 * 128 * EPITCH;
+    __shared__ __attribute__((aligned(1024))) int8_t smem[SMEM];
+
+    const int lane = threadIdx.x % kWave, wave = wave_id();
+    const int wm = wave / 2, wn = wave % 2;
+    int tm, tn;
+    xcd_tile(blockIdx.x, tiles_m, tiles_n, kGroupM, tm, tn);
+    const int64_t m0 = (int64_t)tm * LB, n0 = (int64_t)tn * LB;
+    const int64_t ktiles = (p.k + 127) / 128 * 2;   // 64-k tiles per 32-row block
+    const int64_t nk = ktiles / 2;                   // 128-k slices
+    const int64_t rows_a = (p.m + 31) / 32, rows_b = (p.n + 31) / 32;
+
+    // Direct load `inst` of a slice copies 1 KB: 32-row block inst / 3 of
+    // the tile, piece inst % 3 of its two adjacent 64-k tiles.  Blocks past
+    // the operand re-read its last block; those rows are never stored.
+    const int8_t *srcA[kF6Loads];
+    const int8_t *srcB[kF6Loads];
 #pragma unroll
-    for (int j = 0; j < 4; j++) {
-        const int64_t col = n0 + wn * 128 + 32 * j + fr;
-        if (col >= p.n) continue;
-#pragma unroll
-        for (int i = 0; i < 4; i++)
-#pragma unroll
-            for (int r = 0; r < 16; r++) {
-                const int local = wm * 128 + 32 * i + 8 * (r / 4) + 4 * (lane / 32) + (r % 4);
-                if (m0 + local < p.m) ep.store(p, m0 + local, col, acc[i][j][r], ep.row_factor(local), cf[j], cb[j]);
-            }
+    for (int ii = 0; ii < kF6Loads; ii++) {
+        const int inst = wave * kF6Loads + ii;
+        const int rt = inst / 3, piece = inst % 3;
+        const int64_t ra = min(m0 / 32 + rt, rows_a - 1), rb = min(n0 / 32 + rt, rows_b - 1);
+        srcA[ii] = p.x + ra * ktiles * kF6Tile + 1024 * piece + 16 * lane;
+        srcB[ii] = p.w + rb * ktiles * kF6Tile + 1024 * piece + 16 * lane;
     }
+
+    v16f acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; i++)
+#pragma unroll
+        for (int j = 0; j < 4; j++) acc[i][j] = v16f{};
+
+#pragma unroll
+    for (int b = 0; b < kF6Buf - 1; b++) {
+        const int64_t off = (int64_t)(b < nk ? b : nk - 1) * 2 * kF6Tile;
+#pragma unroll
+        for (int ii = 0; ii < kF6Loads; ii++) {
+            const int inst = wave * kF6Loads + ii;
+            lds_load16(srcA[ii] + off, smem + b * STAGE + 1024 * inst);
+            lds_load16(srcB[ii] + off, smem + b * STAGE + kF6Op + 1024 * inst);
+        }
+    }
+    for (int64_t kt = 0; kt < nk; kt++) {
+        wait_vmcnt<(kF6Buf - 2) * 2 * kF6Loads>();
+        barrier_only();
+        const int cur = (int)(kt % kF6Buf), nxt = (int)((kt + kF6Buf - 1) % kF6Buf);
+        const int64_t nxt_off = (kt + kF6Buf - 1 < nk ? kt + kF6Buf - 1 : nk - 1) * 2 * kF6Tile;
+        f6_slice(acc, smem + cur * STAGE, smem + nxt * STAGE, srcA, srcB, nxt_off, wm, wn, lane, wave);
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    big_epilogue<EPI_SCALARS, OUT>(p, acc, smem, m0, n0, wm, wn, wave, lane);
+}
+
+template <int OUT>
+hipError_t launch_f6(const Params &p, hipStream_t st) {
+    const int64_t tm = (p.m + LB - 1) / LB, tn = (p.n + LB - 1) / LB;
+    if (tm * tn > 0x7fffffff) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((gemm_a4w4_f6_kernel<OUT>), dim3((unsigned)(tm * tn)), dim3(LThreads), 0, st, p, (int)tm,
+                       (int)tn);
+    return hipGetLastError();
 }
 
 // ---------------------------------------------------------------------------
@@ -526,6 +670,17 @@ hipError_t launch_epi(int epi, int out_kind, const Params &p, int64_t batch, hip
 }
 
 }  // namespace
+
+hipError_t launch_gemm_a4w4_tiles(const uint8_t *xa, const uint8_t *wb, const float *sa, const float *sw, float eps,
+                                  int64_t m, int64_t n, int64_t k, int out_kind, void *out, hipStream_t st) {
+    Params p{reinterpret_cast<const int8_t *>(xa), reinterpret_cast<const int8_t *>(wb), nullptr, nullptr, sa, sw,
+             eps, m, n, k, out, nullptr, 0, 0, 0, 0, 0};
+    switch (out_kind) {
+        case OUT_F16: return launch_f6<OUT_F16>(p, st);
+        case OUT_BF16: return launch_f6<OUT_BF16>(p, st);
+        default: return launch_f6<OUT_I32>(p, st);
+    }
+}
 
 bool gemm_i8_uses_big_tiles(bool w_nk, int64_t m, int64_t n, int64_t k) {
     return w_nk && (k % kBigBK) == 0 && m >= 2 * LB && n >= 2 * LB &&

@@ -16,6 +16,9 @@ typedef _Float16 h2 __attribute__((ext_vector_type(2)));
 constexpr int kWave = 64;
 
 typedef unsigned v4u __attribute__((ext_vector_type(4)));
+typedef unsigned v6u __attribute__((ext_vector_type(6)));
+typedef float v16f __attribute__((ext_vector_type(16)));
+typedef int v8i __attribute__((ext_vector_type(8)));
 
 // 16 bytes per lane from global memory straight into LDS
 // (global_load_lds_dwordx4): lane l of the wave writes lds_base + 16 l.

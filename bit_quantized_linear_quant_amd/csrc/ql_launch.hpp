@@ -15,6 +15,11 @@ hipError_t launch_quant_act(int in_kind, const void *x, int64_t m, int64_t k, bo
                             hipStream_t st);
 hipError_t launch_quant_int4_tensor(int in_kind, const void *x, int64_t count, const float *scale,
                                     float eps, int8_t *q, hipStream_t st);
+// quant.hip: 4-bit codes of a [rows, k] tensor as FP6 E3M2 operand tiles
+// (rows padded to 32 and k to 128 with zero codes; a4w4_operand_bytes).
+size_t a4w4_operand_bytes(int64_t rows, int64_t k);
+hipError_t launch_quant_a4w4_tiles(int in_kind, const void *x, int64_t rows, int64_t k, const float *scale,
+                                   float eps, uint8_t *tiles, hipStream_t st);
 
 // pack.hip
 size_t absmean_partial_count(int64_t count);
@@ -48,6 +53,10 @@ struct GemmI8Args {
     int64_t deq_stride;
 };
 hipError_t launch_gemm_i8(const GemmI8Args &a, hipStream_t st);
+// 4-bit product on FP6 E3M2 operand tiles (launch_quant_a4w4_tiles):
+// out = fl32(fl32(acc * max(*sa, eps)) * max(*sw, eps)), acc exact.
+hipError_t launch_gemm_a4w4_tiles(const uint8_t *xa, const uint8_t *wb, const float *sa, const float *sw, float eps,
+                                  int64_t m, int64_t n, int64_t k, int out_kind, void *out, hipStream_t st);
 // True when the product runs on the 256 x 256 direct-to-LDS kernel.
 bool gemm_i8_uses_big_tiles(bool w_nk, int64_t m, int64_t n, int64_t k);
 

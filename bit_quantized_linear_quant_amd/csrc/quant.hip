@@ -254,10 +254,24 @@ bool try_wave_rows(hipError_t &err, bool rms, const void *x, int64_t m, int64_t 
 
 constexpr int kI4Threads = 256;
 
-__device__ __forceinline__ uint32_t code_i4(float v, float sp) {
-    float t = __builtin_rintf(__fdiv_rn(v, sp));
-    t = fminf(fmaxf(t, -8.0f), 7.0f);
-    return (uint32_t)((int)t) & 0xffu;
+// The 4-bit code clamp(rne(fl32(v / sp)), -8, 7) as a float, from the
+// reciprocal r = fl32(1 / sp) in three operations instead of a full IEEE
+// division: y = fl32(v * r) is within an ulp of v / sp, e = v - y * sp is
+// exact in one FMA, and fl32(y + e * r) is the correctly rounded quotient
+// (Markstein's correction; the reciprocal must itself be correctly rounded).
+// Where |y| > 16 the code saturates whatever the last bits, so y is used
+// as it is: this keeps an overflowing y from turning into inf - inf.
+__device__ __forceinline__ float code_i4_f(float v, float sp, float r) {
+    const float y = __fmul_rn(v, r);
+    const float e = __builtin_fmaf(-y, sp, v);
+    const float q = __builtin_fmaf(e, r, y);
+    const float t = __builtin_rintf(fabsf(y) <= 16.0f ? q : y);
+    // + 0 turns the -0 of a small negative quotient into +0, the code 0
+    return fminf(fmaxf(t, -8.0f), 7.0f) + 0.0f;
+}
+
+__device__ __forceinline__ uint32_t code_i4(float v, float sp, float r) {
+    return (uint32_t)((int)code_i4_f(v, sp, r)) & 0xffu;
 }
 
 template <int K, bool VEC>
@@ -268,6 +282,7 @@ __global__ __launch_bounds__(kI4Threads) void quant_int4_tensor_kernel(const voi
                                                                        int8_t *__restrict__ q) {
     const float sc = *scale;
     const float sp = sc > eps ? sc : eps;
+    const float r = __fdiv_rn(1.0f, sp);
     const int64_t nchunk = (count + 7) / 8;
     const int64_t stride = (int64_t)gridDim.x * kI4Threads;
     for (int64_t ch = (int64_t)blockIdx.x * kI4Threads + threadIdx.x; ch < nchunk; ch += stride) {
@@ -278,15 +293,58 @@ __global__ __launch_bounds__(kI4Threads) void quant_int4_tensor_kernel(const voi
             uint32_t lo = 0, hi = 0;
 #pragma unroll
             for (int j = 0; j < 4; j++) {
-                lo |= code_i4(v[j], sp) << (8 * j);
-                hi |= code_i4(v[j + 4], sp) << (8 * j);
+                lo |= code_i4(v[j], sp, r) << (8 * j);
+                hi |= code_i4(v[j + 4], sp, r) << (8 * j);
             }
             *reinterpret_cast<uint2 *>(q + base) = make_uint2(lo, hi);
         } else {
             for (int j = 0; j < 8 && base + j < count; j++)
-                q[base + j] = (int8_t)code_i4(load_elem<K>(x, base + j), sp);
+                q[base + j] = (int8_t)code_i4(load_elem<K>(x, base + j), sp, r);
         }
     }
+}
+
+// 4-bit codes as FP6 E3M2 operand tiles of the 4-bit product.  One thread
+// per slot: slot l of tile (rb, ks) holds row 32rb + l%32, k 64ks + 32(l/32)
+// .. +31; rows and k past the tensor are zero codes.  Every code in [-8, 7]
+// is exact in E3M2, so the hardware conversion packs them without rounding;
+// it interleaves its two 16-value sources (even element from the first), so
+// the even and odd elements are passed apart.  The 6-dword image is written
+// as 16 bytes at tile byte 16l and 8 bytes at 1024 + 8l: both stores of a
+// wave are contiguous.
+template <int K, bool VEC>
+__global__ __launch_bounds__(kI4Threads) void quant_a4w4_tiles_kernel(const void *__restrict__ x, int64_t rows,
+                                                                      int64_t k, const float *__restrict__ scale,
+                                                                      float eps, int64_t ktiles, int64_t slots,
+                                                                      uint8_t *__restrict__ tiles) {
+    const int64_t t = (int64_t)blockIdx.x * kI4Threads + threadIdx.x;
+    if (t >= slots) return;
+    const float sc = *scale;
+    const float sp = sc > eps ? sc : eps;
+    const float r = __fdiv_rn(1.0f, sp);
+    const int64_t tile = t / 64;
+    const int l = (int)(t % 64);
+    const int64_t row = 32 * (tile / ktiles) + l % 32;
+    const int64_t k0 = 64 * (tile % ktiles) + 32 * (l / 32);
+    float v[32];
+    if (VEC && row < rows && k0 + 32 <= k) {
+        const int64_t base = row * k + k0;
+#pragma unroll
+        for (int c = 0; c < 4; c++) load8_vec<K>(x, base + 8 * c, v + 8 * c);
+    } else {
+#pragma unroll
+        for (int j = 0; j < 32; j++) v[j] = (row < rows && k0 + j < k) ? load_elem<K>(x, row * k + k0 + j) : 0.0f;
+    }
+    v16f ev, od;
+#pragma unroll
+    for (int j = 0; j < 16; j++) {
+        ev[j] = code_i4_f(v[2 * j], sp, r);
+        od[j] = code_i4_f(v[2 * j + 1], sp, r);
+    }
+    const v6u img = __builtin_amdgcn_cvt_scalef32_2xpk16_bf6_f32(ev, od, 1.0f);
+    uint8_t *dst = tiles + tile * 1536;
+    *reinterpret_cast<uint4 *>(dst + 16 * l) = make_uint4(img[0], img[1], img[2], img[3]);
+    *reinterpret_cast<uint2 *>(dst + 1024 + 8 * l) = make_uint2(img[4], img[5]);
 }
 
 template <int K, bool VEC, bool RMS>
@@ -327,7 +385,37 @@ hipError_t launch_i4_v(bool vec, const void *x, int64_t count, const float *scal
     return hipGetLastError();
 }
 
+template <int K>
+hipError_t launch_a4w4_tiles_k(bool vec, const void *x, int64_t rows, int64_t k, const float *scale, float eps,
+                               uint8_t *tiles, hipStream_t st) {
+    const int64_t ktiles = (k + 127) / 128 * 2, slots = (rows + 31) / 32 * ktiles * 64;
+    const int64_t blocks = (slots + kI4Threads - 1) / kI4Threads;
+    if (blocks > 0x7fffffff) return hipErrorInvalidValue;
+    if (vec)
+        hipLaunchKernelGGL((quant_a4w4_tiles_kernel<K, true>), dim3((unsigned)blocks), dim3(kI4Threads), 0, st, x,
+                           rows, k, scale, eps, ktiles, slots, tiles);
+    else
+        hipLaunchKernelGGL((quant_a4w4_tiles_kernel<K, false>), dim3((unsigned)blocks), dim3(kI4Threads), 0, st, x,
+                           rows, k, scale, eps, ktiles, slots, tiles);
+    return hipGetLastError();
+}
+
 }  // namespace
+
+size_t a4w4_operand_bytes(int64_t rows, int64_t k) {
+    return (size_t)((rows + 31) / 32 * 32) * (size_t)((k + 127) / 128 * 128) * 3 / 4;
+}
+
+hipError_t launch_quant_a4w4_tiles(int in_kind, const void *x, int64_t rows, int64_t k, const float *scale,
+                                   float eps, uint8_t *tiles, hipStream_t st) {
+    // whole 8-element vector loads need every row 16-byte aligned
+    const bool vec = (k % 8) == 0;
+    switch (in_kind) {
+        case IN_F32: return launch_a4w4_tiles_k<IN_F32>(vec, x, rows, k, scale, eps, tiles, st);
+        case IN_F16: return launch_a4w4_tiles_k<IN_F16>(vec, x, rows, k, scale, eps, tiles, st);
+        default: return launch_a4w4_tiles_k<IN_BF16>(vec, x, rows, k, scale, eps, tiles, st);
+    }
+}
 
 hipError_t launch_quant_act(int in_kind, const void *x, int64_t m, int64_t k, bool rmsnorm,
                             float eps_norm, float eps_q, int8_t *q, float *pts, int32_t *rowsum,

@@ -47,7 +47,7 @@
 extern "C" {
 #endif
 
-#define QL_ABI_VERSION 2
+#define QL_ABI_VERSION 3
 /* Version of the 2-bit ternary weight layout written by qlinear_pack_ternary. */
 #define QL_TERNARY_PACK_V1 1
 /* Version of the 4-bit weight layout written by qlinear_pack_int4. */
@@ -94,7 +94,8 @@ typedef enum ql_int4_what {
 /* Operations that take a workspace (qlinear_workspace_bytes). */
 typedef enum ql_op {
     QL_OP_PACK_TERNARY = 0,
-    QL_OP_GEMM_A4W4 = 1
+    QL_OP_GEMM_A4W4 = 1,
+    QL_OP_A4W4_OPERAND = 2
 } ql_op;
 
 /* Returns QL_ABI_VERSION of the built library. */
@@ -105,8 +106,10 @@ const char *qlinear_status_string(ql_status s);
 
 /* Bytes of workspace the operation needs for these sizes (0 if none).
  *   QL_OP_PACK_TERNARY: fp64 partial sums of the absmean; m is ignored.
- *   QL_OP_GEMM_A4W4:    int8 codes of x [m,k] then w [n,k], m*k + n*k bytes
- *                       rounded up to 256-byte boundaries. */
+ *   QL_OP_GEMM_A4W4:    the FP6 operand tiles of x [m,k] then of w [n,k]
+ *                       (QL_OP_A4W4_OPERAND of each, rounded up to 256 bytes).
+ *   QL_OP_A4W4_OPERAND: bytes of one FP6 operand of m rows and k columns:
+ *                       roundup(m, 32) * roundup(k, 128) * 3 / 4; n is ignored. */
 size_t qlinear_workspace_bytes(ql_op op, int64_t m, int64_t n, int64_t k);
 
 /*
@@ -293,12 +296,53 @@ ql_status qlinear_gemm_a4w4_codes(const int8_t *xq, const int8_t *wq,
                                   void *out, void *stream);
 
 /*
+ * QL_A4W4_OPERAND - the packed operand of the 4-bit product (this library's
+ * own layout, not one of the pages').  Each 4-bit code c in [-8, 7] is stored
+ * as the FP6 E3M2 number of value c (OCP Microscaling Formats v1.0: sign,
+ * 3 exponent bits with bias 3, 2 mantissa bits; all 16 codes are exact), 6
+ * bits per element, laid out as the register images the gfx950 32x32x64 FP6
+ * matrix-core product reads.  A [rows, k] operand is padded with zero codes
+ * to rows_p = roundup(rows, 32) and k_p = roundup(k, 128) and holds
+ * (rows_p / 32) * (k_p / 64) tiles of 1536 bytes; tile (rb, ks) sits at byte
+ * (rb * k_p/64 + ks) * 1536.  Slot l (0..63) of a tile is row 32rb + l%32,
+ * k = 64ks + 32(l/32) + j for j = 0..31, as a 192-bit little-endian string
+ * with element j in bits 6j..6j+5; its first 16 bytes are at tile byte 16l
+ * and its last 8 at tile byte 1024 + 8l.  Size:
+ * qlinear_workspace_bytes(QL_OP_A4W4_OPERAND, rows, 0, k).
+ */
+
+/*
+ * Per-tensor 4-bit quantization of x [rows, k] ([Q4] forward, first half)
+ * straight into a QL_A4W4_OPERAND: the codes are those of
+ * qlinear_quant_int4_tensor, clamp(rne(fl32(x / max(*scale, eps))), -8, 7).
+ * x_dtype QL_F16 / QL_BF16 / QL_F32; k <= 131071.  A weight can be
+ * quantized once and its operand reused by every later product.
+ */
+ql_status qlinear_quant_a4w4_operand(const void *x, ql_dtype x_dtype, int64_t rows, int64_t k,
+                                     const float *scale, float eps, void *operand, void *stream);
+
+/*
+ * A4W4 product on two QL_A4W4_OPERANDs ([Q4] forward, second half):
+ *   out[m][n] = fl32(fl32(acc * s'_a) * s'_w),  acc = sum_k xq[m][k] * wq[n][k],
+ *   s'_a = max(*scale_a, eps), s'_w = max(*scale_w, eps) (device fp32 scalars)
+ * with xa the operand of x [m, k] and wb that of w [n, k].  acc is exact (an
+ * integer below 2^23 accumulated in fp32), so the result equals
+ * qlinear_gemm_a4w4_codes on the same codes bit for bit.  out QL_F16 /
+ * QL_BF16 / QL_I32 (acc; the scale pointers may then be NULL).
+ * m, n, k >= 1; k <= 131071.
+ */
+ql_status qlinear_gemm_a4w4_operands(const void *xa, const void *wb, const float *scale_a,
+                                     const float *scale_w, float eps, int64_t m, int64_t n,
+                                     int64_t k, ql_dtype out_dtype, void *out, void *stream);
+
+/*
  * Q4Linear forward ([Q4] forward): quantizes x [m, k] and w [n, k] (both
  * in_dtype: QL_F16, QL_BF16 or QL_F32) per tensor to 4 bits with
- * qlinear_quant_int4_tensor into the workspace (xq at offset 0, wq at
- * offset round_up(m*k, 256)), then runs qlinear_gemm_a4w4_codes.
+ * qlinear_quant_a4w4_operand into the workspace (x's operand at offset 0,
+ * w's at offset roundup(QL_OP_A4W4_OPERAND bytes of x, 256)), then runs
+ * qlinear_gemm_a4w4_operands.
  * workspace >= qlinear_workspace_bytes(QL_OP_GEMM_A4W4, m, n, k); on return
- * it holds the codes.
+ * it holds the two operands.
  */
 ql_status qlinear_gemm_a4w4(const void *x, const void *w, ql_dtype in_dtype,
                             const float *scale_a, const float *scale_w, float eps,

@@ -12,6 +12,7 @@ import subprocess
 import pytest
 
 import bit_quantized_linear_quant_amd as ql
+import oracle
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 A = 0x10000      # aligned fake device address (never dereferenced)
@@ -39,7 +40,7 @@ def test_exports_every_declared_symbol(L):
 
 
 def test_abi_version_and_status_strings(L):
-    assert ql.qlinear_abi_version() == ql.ABI_VERSION == 2
+    assert ql.qlinear_abi_version() == ql.ABI_VERSION == 3
     for code, name in ql.STATUS.items():
         s = ql.qlinear_status_string(code)
         assert isinstance(s, str) and s
@@ -48,8 +49,11 @@ def test_abi_version_and_status_strings(L):
 
 def test_workspace_bytes():
     # a4w4: codes of x then w, each rounded to 256 bytes
-    assert ql.qlinear_workspace_bytes(ql.QL_OP_GEMM_A4W4, 8192, 8192, 8192) == 2 * 8192 * 8192
-    assert ql.qlinear_workspace_bytes(ql.QL_OP_GEMM_A4W4, 3, 5, 7) == 256 + 256
+    assert ql.qlinear_workspace_bytes(ql.QL_OP_GEMM_A4W4, 8192, 8192, 8192) == 2 * 8192 * 8192 * 3 // 4
+    # 3 and 5 rows pad to 32, k = 7 to 128: 32 * 128 * 3/4 = 3072 bytes each
+    assert ql.qlinear_workspace_bytes(ql.QL_OP_GEMM_A4W4, 3, 5, 7) == 3072 + 3072
+    for rows, k in [(1, 1), (45, 200), (8192, 8192), (33, 129)]:
+        assert ql.qlinear_workspace_bytes(ql.QL_OP_A4W4_OPERAND, rows, 0, k) == oracle.a4w4_operand_bytes(rows, k)
     # ternary: one fp64 partial per 16384-element chunk, rounded to 256 bytes
     assert ql.qlinear_workspace_bytes(ql.QL_OP_PACK_TERNARY, 0, 16, 256) == 256
     chunks = (28672 * 8192 + 16383) // 16384
@@ -123,6 +127,17 @@ def test_gemm_validation(L):
     assert g4(A, ql.QL_F16, NULL, A, A, A, 256, 1, 16, 384, NULL, ql.QL_F16, A, NULL) == -2
     assert g4(A, ql.QL_F16, NULL, A, A, A, 128, 1, 16, 128, U, ql.QL_F16, A, NULL) == -4  # bias alignment
     assert g4(A, ql.QL_F16, NULL, A, A, A, 128, 1, 16, 128, NULL, ql.QL_BF16, A, NULL) == -3
+    qo = L.qlinear_quant_a4w4_operand
+    assert qo(A, ql.QL_F16, 4, 8, NULL, 1e-5, A, NULL) == -1
+    assert qo(A, ql.QL_I8, 4, 8, A, 1e-5, A, NULL) == -3
+    assert qo(A, ql.QL_F16, 0, 8, A, 1e-5, A, NULL) == -2
+    assert qo(A, ql.QL_F16, 4, 131072, A, 1e-5, A, NULL) == -2
+    assert qo(A, ql.QL_F16, 4, 8, A, 1e-5, U, NULL) == -4
+    go = L.qlinear_gemm_a4w4_operands
+    assert go(A, A, NULL, A, 1e-5, 4, 4, 4, ql.QL_F16, A, NULL) == -1
+    assert go(A, A, A, A, 1e-5, 4, 4, 4, ql.QL_F32, A, NULL) == -3
+    assert go(A, A, A, A, 1e-5, 4, 0, 4, ql.QL_F16, A, NULL) == -2
+    assert go(U, A, A, A, 1e-5, 4, 4, 4, ql.QL_F16, A, NULL) == -4
     a4 = L.qlinear_gemm_a4w4
     assert a4(A, A, ql.QL_F16, A, A, 1e-5, 4, 4, 4, ql.QL_F16, A, NULL, 0, NULL) == -5
     assert a4(A, A, ql.QL_F16, A, A, 1e-5, 4, 4, 4, ql.QL_F16, A, A, 100, NULL) == -5

@@ -165,12 +165,12 @@ def test_a4w4_full_workload():
     swg = torch.tensor([d["scale_w"]], dtype=torch.float32, device=DEV)
     out = poison((m, n), torch.float16)
     out, ws = ql.qlinear_gemm_a4w4(_cuda(d["x"]), _cuda(d["w"]), sag, swg, eps, out=out)
-    xq, wq = ql.a4w4_codes_from_workspace(ws, m, n, k)
+    xa, wb = ql.a4w4_operands_from_workspace(ws, m, n, k)
     oi = poison((m, n), torch.int32)
-    ql.qlinear_gemm_a4w4_codes(xq, wq, sag, swg, eps, out_dtype=torch.int32, out=oi)
+    ql.qlinear_gemm_a4w4_operands(xa, wb, m, n, k, None, None, out_dtype=torch.int32, out=oi)
     torch.cuda.synchronize()
-    assert_equal(xq, qa, "x codes")
-    assert_equal(wq, qw, "w codes")
+    assert_equal(xa, oracle.pack_a4w4_fp6(qa), "x operand")
+    assert_equal(wb, oracle.pack_a4w4_fp6(qw), "w operand")
     rows = _rows(m, 2005, extra=24)
     acc = oracle.gemm_i8(qa[rows], qw, True)
     sa = oracle.effective_scale(d["scale_a"], eps)

@@ -487,13 +487,73 @@ def test_a4w4_parity(m, n, k, scale_mul):
     swg = torch.tensor([sw], dtype=torch.float32, device=DEV)
     out = poison((m, n), torch.float16)
     out, ws = ql.qlinear_gemm_a4w4(_cuda(d["x"]), _cuda(d["w"]), sag, swg, d["eps"], out=out)
-    xq, wq = ql.a4w4_codes_from_workspace(ws, m, n, k)
+    xa, wb = ql.a4w4_operands_from_workspace(ws, m, n, k)
     oi = poison((m, n), torch.int32)
-    ql.qlinear_gemm_a4w4_codes(xq, wq, sag, swg, d["eps"], out_dtype=torch.int32, out=oi)
-    ob = ql.qlinear_gemm_a4w4_codes(xq, wq, sag, swg, d["eps"], out_dtype=torch.bfloat16)
+    ql.qlinear_gemm_a4w4_operands(xa, wb, m, n, k, None, None, out_dtype=torch.int32, out=oi)
+    ob = ql.qlinear_gemm_a4w4_operands(xa, wb, m, n, k, sag, swg, d["eps"], out_dtype=torch.bfloat16)
+    # the int8-code product on the oracle's codes
+    oi8 = poison((m, n), torch.int32)
+    ql.qlinear_gemm_a4w4_codes(_cuda(torch.from_numpy(qa)), _cuda(torch.from_numpy(qw)), sag, swg, d["eps"],
+                               out_dtype=torch.int32, out=oi8)
+    o16 = ql.qlinear_gemm_a4w4_codes(_cuda(torch.from_numpy(qa)), _cuda(torch.from_numpy(qw)), sag, swg, d["eps"])
     _sync()
-    assert_equal(xq, qa, "x codes")
-    assert_equal(wq, qw, "w codes")
-    assert_equal(oi, acc, "a4w4 accumulator")
+    assert_equal(xa, oracle.pack_a4w4_fp6(qa), "x operand")
+    assert_equal(wb, oracle.pack_a4w4_fp6(qw), "w operand")
+    assert_equal(oi, acc, "a4w4 accumulator (fp6 operands)")
+    assert_equal(oi8, acc, "a4w4 accumulator (int8 codes)")
     assert_float_close(out, y, "a4w4 fp16")
     assert_float_close(ob, y, "a4w4 bf16")
+    assert_float_close(o16, y, "a4w4 codes fp16")
+
+
+@pytest.mark.parametrize("dt", [torch.bfloat16, torch.float32, torch.float16])
+@pytest.mark.parametrize("rows,k", [(45, 200), (32, 128), (70, 77), (300, 1000)])
+def test_a4w4_operand_quant_parity(dt, rows, k):
+    """Codes of every input type and ragged shape (k % 8 != 0 takes element loads) packed bit for bit."""
+    r = synthetic.rng(3000 + rows + k)
+    x = torch.from_numpy(r.normal(0, 1, (rows, k)).astype(np.float32)).to(dt)
+    scale = 0.3
+    q = oracle.quant_int4_tensor(x.float().numpy(), scale, 1e-5)
+    op = ql.qlinear_quant_a4w4_operand(_cuda(x), torch.tensor([scale], dtype=torch.float32, device=DEV))
+    _sync()
+    assert_equal(op, oracle.pack_a4w4_fp6(q), f"operand {dt}")
+
+
+def test_a4w4_operands_max_k_extremes():
+    """k = 131071 with every code -8: acc = 64 k = 8388544, exact in the fp32 accumulator."""
+    m, n, k = 3, 5, 131071
+    x = torch.full((m, k), -8.0, dtype=torch.float16)
+    w = torch.full((n, k), -8.0, dtype=torch.float16)
+    w[1, ::2] = 7.0
+    one = torch.ones(1, dtype=torch.float32, device=DEV)
+    qa = oracle.quant_int4_tensor(x.float().numpy(), 1.0, 1e-5)
+    qw = oracle.quant_int4_tensor(w.float().numpy(), 1.0, 1e-5)
+    acc = oracle.gemm_i8(qa, qw, True)
+    assert int(acc[0, 0]) == 64 * k
+    xa = ql.qlinear_quant_a4w4_operand(_cuda(x), one)
+    wb = ql.qlinear_quant_a4w4_operand(_cuda(w), one)
+    o = poison((m, n), torch.int32)
+    ql.qlinear_gemm_a4w4_operands(xa, wb, m, n, k, None, None, out_dtype=torch.int32, out=o)
+    _sync()
+    assert_equal(o, acc, "a4w4 max-k accumulator")
+
+
+@pytest.mark.parametrize("m,n,k", [(512, 512, 512), (520, 777, 300), (256, 1024, 8192)])
+def test_a4w4_operands_equal_int8_codes_bit_for_bit(m, n, k):
+    """The FP6 product and the int8 product of the same codes agree exactly in every output type."""
+    d = synthetic.a4w4(m, n, k, seed=3100 + m + k)
+    sag = torch.tensor([d["scale_a"]], dtype=torch.float32, device=DEV)
+    swg = torch.tensor([d["scale_w"]], dtype=torch.float32, device=DEV)
+    xg, wg = _cuda(d["x"]), _cuda(d["w"])
+    xa = ql.qlinear_quant_a4w4_operand(xg, sag, d["eps"])
+    wb = ql.qlinear_quant_a4w4_operand(wg, swg, d["eps"])
+    xq = ql.qlinear_quant_int4_tensor(xg.view(-1), sag, d["eps"]).view(m, k)
+    wq = ql.qlinear_quant_int4_tensor(wg.view(-1), swg, d["eps"]).view(n, k)
+    for dt in (torch.int32, torch.float16, torch.bfloat16):
+        a = ql.qlinear_gemm_a4w4_operands(xa, wb, m, n, k, sag, swg, d["eps"], out_dtype=dt)
+        b = ql.qlinear_gemm_a4w4_codes(xq, wq, sag, swg, d["eps"], out_dtype=dt)
+        _sync()
+        assert torch.equal(a.view(torch.int16) if dt != torch.int32 else a,
+                           b.view(torch.int16) if dt != torch.int32 else b), f"{dt}"
+    qa = oracle.quant_int4_tensor(d["x"].float().numpy(), d["scale_a"], d["eps"])
+    assert_equal(xq, qa, "x codes")
