@@ -74,6 +74,7 @@ def _load():
             "oracle_dequant": (i32, [vp, vp, vp, i64, i64, vp]),
             "oracle_quant_int4_tensor": (i32, [vp, i64, f32, f32, vp]),
             "oracle_a4w4_operand_bytes": (i64, [i64, i64]),
+            "oracle_q4_backward": (i32, [vp, vp, vp, f32, f32, f32, i64, i64, i64, vp, vp, vp, vp, vp, vp]),
             "oracle_pack_a4w4_fp6": (i32, [vp, i64, i64, vp]),
             "oracle_round_f16": (None, [vp, i64, vp]),
             "oracle_round_bf16": (None, [vp, i64, vp]),
@@ -333,6 +334,29 @@ def a4w4(x, w, scale_a: float, scale_w: float, eps: float):
     sa, sw = effective_scale(scale_a, eps), effective_scale(scale_w, eps)
     y = acc.astype(np.float64) * float(sa) * float(sw)
     return qa, qw, acc, y
+
+
+def q4_backward(g, x, w, scale_a: float, scale_w: float, eps: float):
+    """Q4Linear backward ("Q4LinearFunction" backward, straight-through with
+    the clip range and the learned step size term; see qlinear_oracle.c).
+
+    ``g[m,n]`` output gradient, ``x[m,k]``, ``w[n,k]`` (fp32 copies of the
+    16-bit tensors).  Returns ``(grad_x, grad_w, grad_scale_a, bx, bw, bs)``
+    in fp64, the last three being the absolute-value sums the tolerances
+    use.
+    """
+    g = _c(g, np.float64)
+    x = _c(x, np.float32)
+    w = _c(w, np.float32)
+    m, n = g.shape
+    k = x.shape[1]
+    assert x.shape == (m, k) and w.shape == (n, k)
+    gx = np.empty((m, k)); gw = np.empty((n, k)); bx = np.empty((m, k)); bw = np.empty((n, k))
+    gs = np.zeros(1); bs = np.zeros(1)
+    _check(_load().oracle_q4_backward(_p(g), _p(x), _p(w), float(np.float32(scale_a)), float(np.float32(scale_w)),
+                                      float(np.float32(eps)), m, n, k, _p(gx), _p(gw), _p(gs), _p(bx), _p(bw),
+                                      _p(bs)), "q4_backward")
+    return gx, gw, float(gs[0]), bx, bw, float(bs[0])
 
 
 def a4w4_operand_bytes(rows: int, k: int) -> int:

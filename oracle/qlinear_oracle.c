@@ -462,6 +462,85 @@ int oracle_quant_int4_tensor(const float *x, int64_t count, float scale,
 }
 
 /* ------------------------------------------------------------------ */
+/* Q4Linear backward.                                                   */
+/* ------------------------------------------------------------------ */
+/*
+ * [Q4] backward: gradients for the input, the weight and the activation
+ * scale from the output gradient, "adjusted to the quantization ranges";
+ * none for scale_w and eps.  The page states it only in words; this is
+ * the straight-through reading with the clipping range and the learned
+ * step size term for the scale:
+ *   forward  y = Xh Wh^T, Xh = s'_a q_a, Wh = s'_w q_w (the codes of
+ *            oracle_quant_int4_tensor), v = fl32(X / s') the quotient the
+ *            code rounds
+ *   dXh = G Wh       [m, n] x [n, k]          (fp64)
+ *   dWh = G^T Xh     [n, m] x [m, k]          (fp64)
+ *   in  = (-8 <= v <= 7)                      (the clip range)
+ *   grad_x = dXh * in_a,  grad_w = dWh * in_w (round passes the gradient)
+ *   grad_scale_a = sum dXh * (q_a - v_a * in_a) when scale_a > eps, else 0
+ *                  (d(s round(x/s))/ds = round(v) - v inside the range,
+ *                  the clamp bound outside; s' = eps does not depend on s)
+ * G [m, n] fp64 (exact copies of the fp16 / bf16 gradient), X [m, k],
+ * W [n, k] fp32 (exact copies).  Also returns, for tolerances,
+ *   bx = s'_w sum_n |G q_w|, bw = s'_a sum_m |G q_a|,
+ *   bs = sum |dXh (q_a - v_a in_a)|.
+ */
+static float q4_quotient(float x, float sp) { return x / sp; }
+
+int oracle_q4_backward(const double *g, const float *x, const float *w, float scale_a, float scale_w,
+                       float eps, int64_t m, int64_t n, int64_t k, double *grad_x, double *grad_w,
+                       double *grad_sa, double *bx, double *bw, double *bs)
+{
+    float spa = scale_a > eps ? scale_a : eps, spw = scale_w > eps ? scale_w : eps;
+    int8_t *qa = malloc((size_t)(m * k)), *qw = malloc((size_t)(n * k));
+    unsigned char *ina = malloc((size_t)(m * k)), *inw = malloc((size_t)(n * k));
+    float *va = malloc(sizeof(float) * (size_t)(m * k));
+    double total = 0.0, abs_total = 0.0;
+    if (!qa || !qw || !ina || !inw || !va) return -2;
+    oracle_quant_int4_tensor(x, m * k, scale_a, eps, qa);
+    oracle_quant_int4_tensor(w, n * k, scale_w, eps, qw);
+    for (int64_t i = 0; i < m * k; i++) {
+        va[i] = q4_quotient(x[i], spa);
+        ina[i] = (va[i] >= -8.0f && va[i] <= 7.0f);
+    }
+    for (int64_t i = 0; i < n * k; i++) {
+        float v = q4_quotient(w[i], spw);
+        inw[i] = (v >= -8.0f && v <= 7.0f);
+    }
+#pragma omp parallel for schedule(static) reduction(+ : total, abs_total)
+    for (int64_t i = 0; i < m; i++)
+        for (int64_t c = 0; c < k; c++) {
+            double d = 0.0, a = 0.0;
+            for (int64_t j = 0; j < n; j++) {
+                d += g[i * n + j] * (double)qw[j * k + c];
+                a += fabs(g[i * n + j] * (double)qw[j * k + c]);
+            }
+            d *= (double)spw;
+            bx[i * k + c] = a * (double)spw;
+            grad_x[i * k + c] = ina[i * k + c] ? d : 0.0;
+            double t = (double)qa[i * k + c] - (ina[i * k + c] ? (double)va[i * k + c] : 0.0);
+            total += d * t;
+            abs_total += fabs(d * t);
+        }
+#pragma omp parallel for schedule(static)
+    for (int64_t j = 0; j < n; j++)
+        for (int64_t c = 0; c < k; c++) {
+            double d = 0.0, a = 0.0;
+            for (int64_t i = 0; i < m; i++) {
+                d += g[i * n + j] * (double)qa[i * k + c];
+                a += fabs(g[i * n + j] * (double)qa[i * k + c]);
+            }
+            d *= (double)spa;
+            bw[j * k + c] = a * (double)spa;
+            grad_w[j * k + c] = inw[j * k + c] ? d : 0.0;
+        }
+    *grad_sa = scale_a > eps ? total : 0.0;
+    *bs = abs_total;
+    free(qa); free(qw); free(ina); free(inw); free(va);
+    return 0;
+}
+
+/* ------------------------------------------------------------------ */
 /* A4W4 operand tiles: 4-bit codes written as FP6 E3M2 values.          */
 /* ------------------------------------------------------------------ */
 /*

@@ -499,6 +499,59 @@ def test_a4w4_fp6_operand_round_trip(rows, k):
     assert np.all(dec[rows:, :] == 0) and np.all(dec[:, k:] == 0)
 
 
+def _q4_autograd(g, x, w, sa, sw, eps):
+    """Straight-through fake quantization in torch fp64 autograd: clamp passes
+    the gradient inside [-8, 7] only, round passes it unchanged."""
+    f64 = torch.float64
+    sa_t = torch.tensor(float(np.float32(sa)), dtype=f64, requires_grad=True)
+    x_t = torch.tensor(x, dtype=f64, requires_grad=True)
+    w_t = torch.tensor(w, dtype=f64, requires_grad=True)
+    e = torch.tensor(float(np.float32(eps)), dtype=f64)
+
+    def fake(t, s):
+        v = torch.clamp(t / s, -8.0, 7.0)
+        return (v + (torch.round(v) - v).detach()) * s
+
+    y = fake(x_t, torch.maximum(sa_t, e)) @ fake(w_t, torch.maximum(torch.tensor(float(np.float32(sw)), dtype=f64), e)).T
+    y.backward(torch.tensor(g, dtype=f64))
+    return x_t.grad.numpy(), w_t.grad.numpy(), float(sa_t.grad)
+
+
+@pytest.mark.parametrize("m,n,k,clip", [(5, 7, 9, 0.5), (16, 12, 40, 1.0), (33, 17, 64, 0.3)])
+def test_q4_backward_matches_autograd(m, n, k, clip):
+    """torch autograd of the straight-through fake-quantized linear layer."""
+    r = synthetic.rng(60 + m)
+    x = r.normal(0, 1, (m, k)).astype(np.float16).astype(np.float32)
+    w = (0.02 * r.normal(0, 1, (n, k))).astype(np.float16).astype(np.float32)
+    g = r.normal(0, 1, (m, n)).astype(np.float16).astype(np.float64)
+    sa = float(np.abs(x).max() / 7 * clip)
+    sw = float(np.abs(w).max() / 7 * clip)
+    gx, gw, gs, bx, bw, bs = oracle.q4_backward(g, x, w, sa, sw, 1e-5)
+    ax, aw, asa = _q4_autograd(g, x, w, sa, sw, 1e-5)
+    np.testing.assert_allclose(gx, ax, rtol=1e-12, atol=1e-12 * bx.max())
+    np.testing.assert_allclose(gw, aw, rtol=1e-12, atol=1e-12 * bw.max())
+    # the oracle's quotient is fl32(x / s'), autograd's the fp64 one: relative 2^-24 per term
+    assert abs(gs - asa) <= 2.0 ** -23 * bs + 1e-12
+    if clip < 1.0:
+        assert np.count_nonzero(gx == 0) > 0 and np.count_nonzero(gw == 0) > 0
+
+
+def test_q4_backward_special_cases():
+    """Scale below eps: no scale gradient.  Inputs on the code grid inside the
+    range: the step size term vanishes and grad_x is the plain G Wh."""
+    r = synthetic.rng(70)
+    m, n, k = 6, 5, 8
+    g = r.normal(0, 1, (m, n))
+    x = r.integers(-8, 8, (m, k)).astype(np.float32) * 0.25
+    w = r.integers(-8, 8, (n, k)).astype(np.float32) * 0.5
+    gx, gw, gs, _, _, _ = oracle.q4_backward(g, x, w, 0.25, 0.5, 1e-5)
+    assert gs == 0.0
+    np.testing.assert_allclose(gx, g @ w, rtol=1e-13, atol=1e-13)
+    np.testing.assert_allclose(gw, g.T @ x, rtol=1e-13, atol=1e-13)
+    _, _, gs0, _, _, _ = oracle.q4_backward(g, x * 1e-9, w, 1e-7, 0.5, 1e-5)
+    assert gs0 == 0.0
+
+
 def test_round_f16_matches_numpy():
     g = synthetic.rng(51)
     v = np.concatenate([g.standard_normal(20000) * 10.0 ** g.integers(-9, 6, 20000),
