@@ -343,7 +343,8 @@ def q4_backward(g, x, w, scale_a: float, scale_w: float, eps: float):
     ``g[m,n]`` output gradient, ``x[m,k]``, ``w[n,k]`` (fp32 copies of the
     16-bit tensors).  Returns ``(grad_x, grad_w, grad_scale_a, bx, bw, bs)``
     in fp64, the last three being the absolute-value sums the tolerances
-    use.
+    use: ``bx = s'_w sum_n |g q_w|``, ``bw = s'_a sum_m |g q_a|`` and
+    ``bs = sum bx |q_a - v_a [in range]|``.
     """
     g = _c(g, np.float64)
     x = _c(x, np.float32)

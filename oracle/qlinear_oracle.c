@@ -483,7 +483,7 @@ int oracle_quant_int4_tensor(const float *x, int64_t count, float scale,
  * G [m, n] fp64 (exact copies of the fp16 / bf16 gradient), X [m, k],
  * W [n, k] fp32 (exact copies).  Also returns, for tolerances,
  *   bx = s'_w sum_n |G q_w|, bw = s'_a sum_m |G q_a|,
- *   bs = sum |dXh (q_a - v_a in_a)|.
+ *   bs = sum |bx (q_a - v_a in_a)|.
  */
 static float q4_quotient(float x, float sp) { return x / sp; }
 
@@ -520,7 +520,7 @@ int oracle_q4_backward(const double *g, const float *x, const float *w, float sc
             grad_x[i * k + c] = ina[i * k + c] ? d : 0.0;
             double t = (double)qa[i * k + c] - (ina[i * k + c] ? (double)va[i * k + c] : 0.0);
             total += d * t;
-            abs_total += fabs(d * t);
+            abs_total += a * (double)spw * fabs(t);
         }
 #pragma omp parallel for schedule(static)
     for (int64_t j = 0; j < n; j++)
