@@ -39,8 +39,9 @@ sys.path.insert(0, ROOT)
 METRIC = "int8 TOPS (large-M GEMM) + packed-weight HBM GB/s (M≤16 GEMV), % roofline"
 PEAK_INT8_TOPS = 5000.0      # MI355X dense int8 MFMA, 5.0 POP/s
 PEAK_FP6_TOPS = 10100.0      # MI355X dense FP6 / FP4 MFMA, 10.1 PFLOP/s
+PEAK_FP16_TFLOPS = 2500.0    # MI355X dense fp16 / bf16 MFMA, 2.5 PFLOP/s
 PEAK_HBM_GBS = 8000.0        # MI355X HBM3E, 8 TB/s
-GEMM_KERNEL_SOURCES = ["gemm_i8.hip", "ql_device.hpp"]
+GEMM_KERNEL_SOURCES = ["gemm_i8.hip", "gemm_ring.hpp", "ql_device.hpp"]
 GEMV_KERNEL_SOURCES = ["gemm_w2a8.hip", "ql_device.hpp"]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.txt")
 
@@ -380,7 +381,33 @@ def bench_rows(ql, torch, synthetic):
         us, gbytes8, "GB/s", PEAK_HBM_GBS, "hbm",
         f"{gbytes8} B (packed weight, fp16 scales, packed zeros, int8 x codes and scales, fp16 out)",
         (512 * k // 2 + 512 * (k // gs) * 2.5 + m * k + m * 512 * 2) / t / 1e9, f"512 of {n} columns")
-    del pws
+    del pws, xg, outg
+
+    # next-4: Q4Linear backward, 8192^3 fp16 (grad_x, grad_w, grad_scale_a);
+    # two fp16 matrix-core products of 2*m*n*k flops each plus the operand
+    # transposes and the range-masked epilogues
+    m = n = k = 8192
+    r = np.random.Generator(np.random.PCG64(1007))
+    xb = torch.from_numpy(r.normal(0, 1, (m, k)).astype(np.float16)).to(dev)
+    wb = torch.from_numpy((0.02 * r.normal(0, 1, (n, k))).astype(np.float16)).to(dev)
+    gb = torch.from_numpy(r.normal(0, 1, (m, n)).astype(np.float16)).to(dev)
+    sab = (xb.abs().max().float() / 7).reshape(1)
+    swb = (wb.abs().max().float() / 7).reshape(1)
+    gxb = torch.empty((m, k), dtype=torch.float32, device=dev)
+    gwb = torch.empty((n, k), dtype=torch.float32, device=dev)
+    gsb = torch.empty((1,), dtype=torch.float32, device=dev)
+    wsb = torch.empty((ql.qlinear_workspace_bytes(ql.QL_OP_Q4_BACKWARD, m, n, k),), dtype=torch.uint8, device=dev)
+    us = time_eager(torch, lambda i: ql.qlinear_q4_backward(gb, xb, wb, sab, swb, 1e-5, grad_x=gxb, grad_w=gwb,
+                                                            grad_scale_a=gsb, workspace=wsb), 5)
+    flops = 2 * 2.0 * m * n * k
+    gn, xn, wn = gb[:8].float().cpu().numpy(), xb[:8].float().cpu().numpy(), wb.float().cpu().numpy()
+    t = time_cpu(lambda: oracle.q4_backward(gn, xn, wn, float(sab.item()), float(swb.item()), 1e-5), min_s=0.5)
+    rows["next4_q4_backward_8192x8192x8192_fp16"] = _row(
+        us, flops, "TFLOP/s", PEAK_FP16_TFLOPS, "mfma",
+        "2 x 2*m*n*k fp16 flops (grad_x = G Wh, grad_w = G^T Xh) with transposes and masked epilogues; "
+        "one qlinear_q4_backward call, eager, mean of 5",
+        2 * 2.0 * 8 * n * k / t / 1e12, "8 of 8192 token rows (their grad_x and their share of grad_w)")
+    del xb, wb, gb, gxb, gwb, wsb
     return {"threads_oracle": threads, "rows": rows}
 
 

@@ -28,7 +28,7 @@ QL_F32, QL_F16, QL_BF16, QL_I8, QL_U8, QL_I32 = range(6)
 QL_W_KN, QL_W_NK = 0, 1
 QL_RMSNORM = 1
 QL_INT4_WEIGHT, QL_INT4_ZEROS = 0, 1
-QL_OP_PACK_TERNARY, QL_OP_GEMM_A4W4, QL_OP_A4W4_OPERAND = 0, 1, 2
+QL_OP_PACK_TERNARY, QL_OP_GEMM_A4W4, QL_OP_A4W4_OPERAND, QL_OP_Q4_BACKWARD = 0, 1, 2, 3
 STATUS = {0: "QL_OK", -1: "QL_ERR_NULL", -2: "QL_ERR_SHAPE", -3: "QL_ERR_DTYPE", -4: "QL_ERR_ALIGN",
           -5: "QL_ERR_WORKSPACE", -6: "QL_ERR_UNSUPPORTED", -7: "QL_ERR_HIP"}
 
@@ -40,7 +40,7 @@ _lib = None
 
 
 # QL_ABI_VERSION of include/qlinear.h that the argument lists below follow.
-ABI_VERSION = 3
+ABI_VERSION = 4
 
 
 class QLinearError(RuntimeError):
@@ -83,6 +83,8 @@ def lib() -> ctypes.CDLL:
             "qlinear_gemm_a4w4": (i32, [vp, vp, i32, vp, vp, f32, i64, i64, i64, i32, vp, vp, sz, vp]),
             "qlinear_quant_a4w4_operand": (i32, [vp, i32, i64, i64, vp, f32, vp, vp]),
             "qlinear_gemm_a4w4_operands": (i32, [vp, vp, vp, vp, f32, i64, i64, i64, i32, vp, vp]),
+            "qlinear_q4_backward": (i32, [vp, vp, vp, i32, vp, vp, f32, i64, i64, i64, i32, vp, vp, vp, vp, sz,
+                                          vp]),
         }
         for name, (res, args) in sigs.items():
             fn = getattr(L, name)
@@ -379,3 +381,34 @@ def qlinear_gemm_a4w4_operands(xa, wb, m, n, k, scale_a, scale_w, eps=1e-5, out_
         _ptr(xa), _ptr(wb), _ptr(scale_a), _ptr(scale_w), float(eps), m, n, k, _TORCH_TO_QL[out_dtype],
         _ptr(out), _stream(xa)))
     return out
+
+
+def qlinear_q4_backward(grad_out, x, w, scale_a, scale_w, eps=1e-5, grad_dtype=torch.float32, grad_x=None,
+                        grad_w=None, grad_scale_a=None, workspace=None):
+    """Q4Linear backward: ``(grad_x[m,k], grad_w[n,k], grad_scale_a[1])`` from ``grad_out[m,n]``.
+
+    ``grad_out``, ``x`` and ``w`` share one dtype (fp16 or bf16); the scales
+    are the forward's 1-element fp32 GPU tensors.
+    """
+    _gpu(grad_out, "grad_out")
+    _gpu(x, "x", grad_out.dtype)
+    _gpu(w, "w", grad_out.dtype)
+    _gpu(scale_a, "scale_a", torch.float32)
+    _gpu(scale_w, "scale_w", torch.float32)
+    m, n = grad_out.shape
+    k = x.shape[1]
+    if x.shape[0] != m or w.shape != (n, k):
+        raise ValueError(f"grad_out {tuple(grad_out.shape)}, x {tuple(x.shape)}, w {tuple(w.shape)} do not match")
+    grad_x = _empty((m, k), grad_dtype, x) if grad_x is None else _gpu(grad_x, "grad_x", grad_dtype)
+    grad_w = _empty((n, k), grad_dtype, x) if grad_w is None else _gpu(grad_w, "grad_w", grad_dtype)
+    _need(grad_x, m * k * grad_x.element_size(), "grad_x")
+    _need(grad_w, n * k * grad_w.element_size(), "grad_w")
+    grad_scale_a = _empty((1,), torch.float32, x) if grad_scale_a is None else _gpu(grad_scale_a, "grad_scale_a",
+                                                                                     torch.float32)
+    ws_bytes = qlinear_workspace_bytes(QL_OP_Q4_BACKWARD, m, n, k)
+    workspace = _empty((ws_bytes,), torch.uint8, x) if workspace is None else _gpu(workspace, "workspace")
+    _check("qlinear_q4_backward", lib().qlinear_q4_backward(
+        _ptr(grad_out), _ptr(x), _ptr(w), _TORCH_TO_QL[grad_out.dtype], _ptr(scale_a), _ptr(scale_w), float(eps),
+        m, n, k, _TORCH_TO_QL[grad_dtype], _ptr(grad_x), _ptr(grad_w), _ptr(grad_scale_a), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _stream(x)))
+    return grad_x, grad_w, grad_scale_a

@@ -18,7 +18,7 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libqlinear.so")
-SOURCES = ["api.hip", "quant.hip", "pack.hip", "gemm_i8.hip", "gemm_w2a8.hip", "gemm_int4.hip"]
+SOURCES = ["api.hip", "quant.hip", "pack.hip", "gemm_i8.hip", "gemm_w2a8.hip", "gemm_int4.hip", "q4_backward.hip"]
 ARCH = "gfx950"
 
 

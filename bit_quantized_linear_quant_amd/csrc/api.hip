@@ -59,6 +59,8 @@ size_t qlinear_workspace_bytes(ql_op op, int64_t m, int64_t n, int64_t k) {
             return round256(ql::a4w4_operand_bytes(m, k)) + round256(ql::a4w4_operand_bytes(n, k));
         case QL_OP_A4W4_OPERAND:
             return ql::a4w4_operand_bytes(m, k);
+        case QL_OP_Q4_BACKWARD:
+            return ql::q4_backward_workspace(m, n, k);
         default: return 0;
     }
 }
@@ -265,6 +267,29 @@ ql_status qlinear_gemm_a4w4(const void *x, const void *w, ql_dtype in_dtype, con
     e = ql::launch_quant_a4w4_tiles(kind, w, n, k, scale_w, eps, wb, st);
     if (e != hipSuccess) return QL_ERR_HIP;
     return hip_status(ql::launch_gemm_a4w4_tiles(xa, wb, scale_a, scale_w, eps, m, n, k, ok, out, st));
+}
+
+ql_status qlinear_q4_backward(const void *grad_out, const void *x, const void *w, ql_dtype dtype,
+                              const float *scale_a, const float *scale_w, float eps, int64_t m, int64_t n,
+                              int64_t k, ql_dtype grad_dtype, void *grad_x, void *grad_w, float *grad_scale_a,
+                              void *workspace, size_t ws_bytes, void *stream) {
+    if (!grad_out || !x || !w || !scale_a || !scale_w || !grad_x || !grad_w || !grad_scale_a) return QL_ERR_NULL;
+    if (dtype != QL_F16 && dtype != QL_BF16) return QL_ERR_DTYPE;
+    int ok;
+    switch (grad_dtype) {
+        case QL_F32: ok = ql::OUT_F32; break;
+        case QL_F16: ok = ql::OUT_F16; break;
+        case QL_BF16: ok = ql::OUT_BF16; break;
+        default: return QL_ERR_DTYPE;
+    }
+    if (m < 1 || n < 1 || k < 1 || m > 0x7fffffff || n > 0x7fffffff || k > 0x7fffffff) return QL_ERR_SHAPE;
+    if (!aligned16(grad_out) || !aligned16(x) || !aligned16(w) || !aligned16(grad_x) || !aligned16(grad_w))
+        return QL_ERR_ALIGN;
+    if (!workspace || ws_bytes < qlinear_workspace_bytes(QL_OP_Q4_BACKWARD, m, n, k)) return QL_ERR_WORKSPACE;
+    if (!aligned16(workspace)) return QL_ERR_ALIGN;
+    ql::Q4BackwardArgs a{grad_out, x, w, dtype == QL_BF16, scale_a, scale_w, eps, m, n, k, ok,
+                         grad_x, grad_w, grad_scale_a, workspace};
+    return hip_status(ql::launch_q4_backward(a, as_stream(stream)));
 }
 
 }  // extern "C"

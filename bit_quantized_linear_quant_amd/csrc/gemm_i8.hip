@@ -27,12 +27,12 @@
 //   registers on their way into LDS.
 #include "ql_device.hpp"
 #include "ql_launch.hpp"
+#include "gemm_ring.hpp"
 
 namespace ql {
 
 namespace {
 
-typedef int v16i __attribute__((ext_vector_type(16)));
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(1))) void glb_void;
 
@@ -114,70 +114,6 @@ struct Epilogue {
 // ---------------------------------------------------------------------------
 // Large-tile kernel
 // ---------------------------------------------------------------------------
-constexpr int LB = 256;        // tile rows and columns
-constexpr int LThreads = 256;
-constexpr int kGroupM = 4;     // tile rows walked together per XCD
-
-template <int CH>
-__device__ __forceinline__ int swz(int r) {
-    if constexpr (CH == 4) return ((r >> 1) ^ (r >> 2)) & 3;
-    else return (r & 7) ^ ((r >> 3) & 3);
-}
-
-template <int BK>
-struct BigTile {
-    static constexpr int CH = BK / 16;                // 16-byte chunks per LDS row
-    static constexpr int TILE = LB * BK;              // bytes of one A or B slice
-    static constexpr int PER_WAVE = TILE / 1024 / 4;  // 1 KB direct loads per wave per slice and operand
-    static constexpr int S = BK / 32;                 // 32-k MFMA steps per slice
-};
-
-// One k-slice: the direct loads of a later slice into `nxt`, then the MFMAs of
-// `cur`, each step's fragments read from LDS while the previous step's
-// MFMAs issue.  `cur` and `nxt` are distinct restrict pointers, so the
-// compiler does not make the LDS reads of `cur` wait for the loads into `nxt`.
-template <int BK>
-__device__ __forceinline__ void big_slice(v16i (&acc)[4][4], const int8_t *__restrict__ cur,
-                                          int8_t *__restrict__ nxt, const int8_t *const (&srcA)[BigTile<BK>::PER_WAVE],
-                                          const int8_t *const (&srcB)[BigTile<BK>::PER_WAVE], int64_t nxt_k0,
-                                          const int (&offA)[BigTile<BK>::S], const int (&offB)[BigTile<BK>::S],
-                                          int wave) {
-    constexpr int CH = BigTile<BK>::CH, TILE = BigTile<BK>::TILE, PER_WAVE = BigTile<BK>::PER_WAVE;
-    constexpr int S = BigTile<BK>::S;
-#pragma unroll
-    for (int ii = 0; ii < PER_WAVE; ii++) {
-        const int inst = wave * PER_WAVE + ii;
-        lds_load16(srcA[ii] + nxt_k0, nxt + 1024 * inst);
-        lds_load16(srcB[ii] + nxt_k0, nxt + TILE + 1024 * inst);
-    }
-    v4i fa[2][4], fb[2][4];
-    auto frags = [&](int s) {
-#pragma unroll
-        for (int i = 0; i < 4; i++) fa[s & 1][i] = *reinterpret_cast<const v4i *>(cur + offA[s] + i * 32 * CH * 16);
-#pragma unroll
-        for (int j = 0; j < 4; j++) fb[s & 1][j] = *reinterpret_cast<const v4i *>(cur + TILE + offB[s] + j * 32 * CH * 16);
-    };
-    frags(0);
-#pragma unroll
-    for (int s = 0; s < S; s++) {
-        if (s + 1 < S) frags(s + 1);
-#pragma unroll
-        for (int i = 0; i < 4; i++)
-#pragma unroll
-            for (int j = 0; j < 4; j++)
-                acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fa[s & 1][i], fb[s & 1][j], acc[i][j], 0, 0, 0);
-        // matrix-core issue interleaved with the next step's LDS reads
-        if (s + 1 < S) {
-#pragma unroll
-            for (int q = 0; q < 8; q++) {
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-            }
-            __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
-        }
-    }
-}
-
 // Epilogue of the 256 x 256 tile kernels: lane holds column lane%32 of each
 // 32x32 block and rows 8*(r/4) + 4*(lane/32) + r%4 of register r.  The
 // accumulators are int32, or fp32 holding integers below 2^24 (exact).
@@ -256,9 +192,7 @@ __device__ __forceinline__ void big_epilogue(const Params &p, const ACC (&acc)[4
 
 template <int BK, int NBUF, int EPI, int OUT>
 __global__ __launch_bounds__(LThreads, 1) void gemm_i8_big_kernel(Params p, int tiles_m, int tiles_n) {
-    constexpr int CH = BigTile<BK>::CH, TILE = BigTile<BK>::TILE, PER_WAVE = BigTile<BK>::PER_WAVE;
-    constexpr int S = BigTile<BK>::S;
-    constexpr int STAGE = 2 * TILE;
+    constexpr int STAGE = 2 * BigTile<BK>::TILE;
     // main loop: a ring of NBUF (A, B) slices; epilogue: 1 KB of row factors,
     // then one padded 128 x 128 output sub-tile per wave (2-byte outputs)
     constexpr int EPITCH = 128 * 2 + 16;
@@ -271,67 +205,8 @@ __global__ __launch_bounds__(LThreads, 1) void gemm_i8_big_kernel(Params p, int 
     int tm, tn;
     xcd_tile(blockIdx.x, tiles_m, tiles_n, kGroupM, tm, tn);
     const int64_t m0 = (int64_t)tm * LB, n0 = (int64_t)tn * LB;
-    const int64_t K = p.k;
-    const int64_t nk = K / BK;
-
-    // Global source of each direct load issued by this lane (for k = 0).
-    const int8_t *srcA[PER_WAVE];
-    const int8_t *srcB[PER_WAVE];
-#pragma unroll
-    for (int ii = 0; ii < PER_WAVE; ii++) {
-        const int pos = 64 * (wave * PER_WAVE + ii) + lane;   // chunk position in the slice
-        const int row = pos / CH;
-        const int c = (pos % CH) ^ swz<CH>(row);
-        const int64_t ra = min(m0 + row, p.m - 1), rb = min(n0 + row, p.n - 1);
-        srcA[ii] = p.x + ra * K + 16 * c;
-        srcB[ii] = p.w + rb * K + 16 * c;
-    }
-    // LDS byte offsets of this lane's fragments: block row 32i + lane%32,
-    // chunk 2s + lane/32.  swz depends only on the low 5 row bits, so the
-    // offset of block i is that of block 0 plus 32 rows.
-    const int fr = lane % 32;
-    int offA[S], offB[S];
-#pragma unroll
-    for (int s = 0; s < S; s++) {
-        const int c = 2 * s + lane / 32;
-        const int ra = wm * 128 + fr, rb = wn * 128 + fr;
-        offA[s] = 16 * (CH * ra + (c ^ swz<CH>(ra)));
-        offB[s] = 16 * (CH * rb + (c ^ swz<CH>(rb)));
-    }
-
     v16i acc[4][4];
-#pragma unroll
-    for (int i = 0; i < 4; i++)
-#pragma unroll
-        for (int j = 0; j < 4; j++) acc[i][j] = v16i{};
-
-    // Slices 0 .. NBUF-2 in flight before the loop; iteration kt consumes
-    // slice kt and starts slice kt + NBUF - 1 (clamped: the last iterations
-    // reload the final slice, keeping the loop body free of branches) into
-    // the buffer that iteration kt - 1 consumed.
-#pragma unroll
-    for (int b = 0; b < NBUF - 1; b++) {
-        const int64_t k0 = (int64_t)(b < nk ? b : nk - 1) * BK;
-#pragma unroll
-        for (int ii = 0; ii < PER_WAVE; ii++) {
-            const int inst = wave * PER_WAVE + ii;
-            lds_load16(srcA[ii] + k0, smem + b * STAGE + 1024 * inst);
-            lds_load16(srcB[ii] + k0, smem + b * STAGE + TILE + 1024 * inst);
-        }
-    }
-    for (int64_t kt = 0; kt < nk; kt++) {
-        // this wave's loads of slice kt are done (the NBUF - 2 newer slices
-        // may still be in flight); after the barrier every wave's are, and
-        // every wave has finished reading the buffer refilled below
-        wait_vmcnt<(NBUF - 2) * 2 * PER_WAVE>();
-        barrier_only();
-        const int cur = (int)(kt % NBUF), nxt = (int)((kt + NBUF - 1) % NBUF);
-        const int64_t nxt_k0 = (kt + NBUF - 1 < nk ? kt + NBUF - 1 : nk - 1) * BK;
-        big_slice<BK>(acc, smem + cur * STAGE, smem + nxt * STAGE, srcA, srcB, nxt_k0, offA, offB, wave);
-    }
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-
+    ring_gemm<BK, NBUF, MK_I8>(acc, smem, p.x, p.w, p.m, p.n, p.k, m0, n0, wm, wn, lane, wave);
     big_epilogue<EPI, OUT>(p, acc, smem, m0, n0, wm, wn, wave, lane);
 }
 

@@ -168,4 +168,26 @@ __device__ __forceinline__ void store_out(void *out, int64_t idx, float y) {
     else static_cast<float *>(out)[idx] = y;
 }
 
+// fl32(v / sp) from the reciprocal r = fl32(1 / sp) in three operations
+// instead of a full IEEE division: y = fl32(v * r) is within an ulp of v / sp,
+// e = v - y * sp is exact in one FMA, and fl32(y + e * r) is the correctly
+// rounded quotient (Markstein's correction; r must itself be correctly
+// rounded).  Where |y| > 16 the 4-bit code saturates whatever the last bits
+// are, so y is returned as it is: this keeps an overflowing y from turning
+// into inf - inf.
+__device__ __forceinline__ float q4_quotient(float v, float sp, float r) {
+    const float y = __fmul_rn(v, r);
+    const float e = __builtin_fmaf(-y, sp, v);
+    const float q = __builtin_fmaf(e, r, y);
+    return fabsf(y) <= 16.0f ? q : y;
+}
+
+// The 4-bit code clamp(rne(q), -8, 7) of a quotient, as a float.  + 0 turns
+// the -0 of a small negative quotient into +0, the code 0.
+__device__ __forceinline__ float q4_code(float q) {
+    return fminf(fmaxf(__builtin_rintf(q), -8.0f), 7.0f) + 0.0f;
+}
+
+__device__ __forceinline__ float code_i4_f(float v, float sp, float r) { return q4_code(q4_quotient(v, sp, r)); }
+
 }  // namespace ql

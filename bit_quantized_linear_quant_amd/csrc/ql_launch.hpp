@@ -60,6 +60,25 @@ hipError_t launch_gemm_a4w4_tiles(const uint8_t *xa, const uint8_t *wb, const fl
 // True when the product runs on the 256 x 256 direct-to-LDS kernel.
 bool gemm_i8_uses_big_tiles(bool w_nk, int64_t m, int64_t n, int64_t k);
 
+// q4_backward.hip: Q4Linear backward (grad_x, grad_w, grad of scale_a).
+struct Q4BackwardArgs {
+    const void *grad_out;  // [m][n]
+    const void *x;         // [m][k]
+    const void *w;         // [n][k]; all three fp16, or all three bf16
+    bool bf16;
+    const float *scale_a, *scale_w;
+    float eps;
+    int64_t m, n, k;
+    int out_kind;          // OUT_F32 / OUT_F16 / OUT_BF16 for grad_x and grad_w
+    void *grad_x;          // [m][k]
+    void *grad_w;          // [n][k]
+    float *grad_scale_a;   // device scalar
+    void *workspace;       // q4_backward_workspace(m, n, k) bytes
+};
+size_t q4_backward_partials(int64_t m, int64_t k);
+size_t q4_backward_workspace(int64_t m, int64_t n, int64_t k);
+hipError_t launch_q4_backward(const Q4BackwardArgs &a, hipStream_t st);
+
 // gemm_w2a8.hip: packed ternary weights.
 hipError_t launch_gemm_w2a8(const int8_t *xq, const float *pts, const int32_t *rowsum,
                             const uint32_t *packed, const double *gamma, const float *bias, int64_t m,

@@ -254,22 +254,6 @@ bool try_wave_rows(hipError_t &err, bool rms, const void *x, int64_t m, int64_t 
 
 constexpr int kI4Threads = 256;
 
-// The 4-bit code clamp(rne(fl32(v / sp)), -8, 7) as a float, from the
-// reciprocal r = fl32(1 / sp) in three operations instead of a full IEEE
-// division: y = fl32(v * r) is within an ulp of v / sp, e = v - y * sp is
-// exact in one FMA, and fl32(y + e * r) is the correctly rounded quotient
-// (Markstein's correction; the reciprocal must itself be correctly rounded).
-// Where |y| > 16 the code saturates whatever the last bits, so y is used
-// as it is: this keeps an overflowing y from turning into inf - inf.
-__device__ __forceinline__ float code_i4_f(float v, float sp, float r) {
-    const float y = __fmul_rn(v, r);
-    const float e = __builtin_fmaf(-y, sp, v);
-    const float q = __builtin_fmaf(e, r, y);
-    const float t = __builtin_rintf(fabsf(y) <= 16.0f ? q : y);
-    // + 0 turns the -0 of a small negative quotient into +0, the code 0
-    return fminf(fmaxf(t, -8.0f), 7.0f) + 0.0f;
-}
-
 __device__ __forceinline__ uint32_t code_i4(float v, float sp, float r) {
     return (uint32_t)((int)code_i4_f(v, sp, r)) & 0xffu;
 }

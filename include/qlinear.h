@@ -47,7 +47,7 @@
 extern "C" {
 #endif
 
-#define QL_ABI_VERSION 3
+#define QL_ABI_VERSION 4
 /* Version of the 2-bit ternary weight layout written by qlinear_pack_ternary. */
 #define QL_TERNARY_PACK_V1 1
 /* Version of the 4-bit weight layout written by qlinear_pack_int4. */
@@ -95,7 +95,8 @@ typedef enum ql_int4_what {
 typedef enum ql_op {
     QL_OP_PACK_TERNARY = 0,
     QL_OP_GEMM_A4W4 = 1,
-    QL_OP_A4W4_OPERAND = 2
+    QL_OP_A4W4_OPERAND = 2,
+    QL_OP_Q4_BACKWARD = 3
 } ql_op;
 
 /* Returns QL_ABI_VERSION of the built library. */
@@ -109,7 +110,10 @@ const char *qlinear_status_string(ql_status s);
  *   QL_OP_GEMM_A4W4:    the FP6 operand tiles of x [m,k] then of w [n,k]
  *                       (QL_OP_A4W4_OPERAND of each, rounded up to 256 bytes).
  *   QL_OP_A4W4_OPERAND: bytes of one FP6 operand of m rows and k columns:
- *                       roundup(m, 32) * roundup(k, 128) * 3 / 4; n is ignored. */
+ *                       roundup(m, 32) * roundup(k, 128) * 3 / 4; n is ignored.
+ *   QL_OP_Q4_BACKWARD:  the transposed, zero-padded 16-bit operands of the
+ *                       two backward products and the scale-gradient
+ *                       partials of qlinear_q4_backward. */
 size_t qlinear_workspace_bytes(ql_op op, int64_t m, int64_t n, int64_t k);
 
 /*
@@ -348,6 +352,32 @@ ql_status qlinear_gemm_a4w4(const void *x, const void *w, ql_dtype in_dtype,
                             const float *scale_a, const float *scale_w, float eps,
                             int64_t m, int64_t n, int64_t k, ql_dtype out_dtype, void *out,
                             void *workspace, size_t ws_bytes, void *stream);
+
+/*
+ * Q4Linear backward ([Q4] backward): gradients for the input, the weight
+ * and the activation scale from the output gradient, adjusted to the
+ * quantization range; scale_w and eps get none.  The page gives it only in
+ * words; this is the straight-through reading, with v = fl32(t / s') the
+ * quotient the forward code rounds and q its 4-bit code:
+ *   dXh = G (s'_w q_w),  dWh = G^T (s'_a q_a)     (fp32 accumulation)
+ *   grad_x = dXh where -8 <= v_a <= 7, else 0
+ *   grad_w = dWh where -8 <= v_w <= 7, else 0
+ *   *grad_scale_a = sum dXh * (q_a - v_a if inside the range, q_a outside),
+ *                   0 when *scale_a <= eps  (learned step-size term)
+ *   grad_out G [m, n], x [m, k], w [n, k]: all dtype QL_F16 or all QL_BF16
+ *   (the products run on the fp16 or bf16 matrix cores; the codes are exact
+ *   in both); scale_a, scale_w device fp32 scalars of the forward;
+ *   grad_x [m, k] and grad_w [n, k] of grad_dtype QL_F32 / QL_F16 / QL_BF16;
+ *   grad_scale_a a device fp32 scalar, summed in a fixed order
+ *   (deterministic).
+ * workspace >= qlinear_workspace_bytes(QL_OP_Q4_BACKWARD, m, n, k).
+ * m, n, k >= 1.
+ */
+ql_status qlinear_q4_backward(const void *grad_out, const void *x, const void *w, ql_dtype dtype,
+                              const float *scale_a, const float *scale_w, float eps,
+                              int64_t m, int64_t n, int64_t k, ql_dtype grad_dtype,
+                              void *grad_x, void *grad_w, float *grad_scale_a,
+                              void *workspace, size_t ws_bytes, void *stream);
 
 #ifdef __cplusplus
 }

@@ -40,7 +40,7 @@ def test_exports_every_declared_symbol(L):
 
 
 def test_abi_version_and_status_strings(L):
-    assert ql.qlinear_abi_version() == ql.ABI_VERSION == 3
+    assert ql.qlinear_abi_version() == ql.ABI_VERSION == 4
     for code, name in ql.STATUS.items():
         s = ql.qlinear_status_string(code)
         assert isinstance(s, str) and s
@@ -138,6 +138,13 @@ def test_gemm_validation(L):
     assert go(A, A, A, A, 1e-5, 4, 4, 4, ql.QL_F32, A, NULL) == -3
     assert go(A, A, A, A, 1e-5, 4, 0, 4, ql.QL_F16, A, NULL) == -2
     assert go(U, A, A, A, 1e-5, 4, 4, 4, ql.QL_F16, A, NULL) == -4
+    qb = L.qlinear_q4_backward
+    assert qb(A, A, A, ql.QL_F16, A, A, 1e-5, 4, 4, 4, ql.QL_F32, A, A, NULL, A, 1 << 20, NULL) == -1
+    assert qb(A, A, A, ql.QL_F32, A, A, 1e-5, 4, 4, 4, ql.QL_F32, A, A, A, A, 1 << 20, NULL) == -3
+    assert qb(A, A, A, ql.QL_F16, A, A, 1e-5, 4, 4, 4, ql.QL_I32, A, A, A, A, 1 << 20, NULL) == -3
+    assert qb(A, A, A, ql.QL_F16, A, A, 1e-5, 0, 4, 4, ql.QL_F32, A, A, A, A, 1 << 20, NULL) == -2
+    assert qb(A, A, A, ql.QL_F16, A, A, 1e-5, 4, 4, 4, ql.QL_F32, A, A, A, A, 10, NULL) == -5
+    assert qb(A, U, A, ql.QL_F16, A, A, 1e-5, 4, 4, 4, ql.QL_F32, A, A, A, A, 1 << 20, NULL) == -4
     a4 = L.qlinear_gemm_a4w4
     assert a4(A, A, ql.QL_F16, A, A, 1e-5, 4, 4, 4, ql.QL_F16, A, NULL, 0, NULL) == -5
     assert a4(A, A, ql.QL_F16, A, A, 1e-5, 4, 4, 4, ql.QL_F16, A, A, 100, NULL) == -5

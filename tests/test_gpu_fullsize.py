@@ -179,3 +179,26 @@ def test_a4w4_full_workload():
     ridx = torch.from_numpy(rows).to(DEV)
     assert_equal(oi[ridx], acc, "a4w4 accumulator (sampled rows)")
     assert_float_close(out[ridx], y, "a4w4 fp16 (sampled rows)")
+
+
+def test_q4_backward_full_workload():
+    """8192^3 backward of the A4W4 workload: sampled rows of grad_x and grad_w against the oracle."""
+    m = n = k = 8192
+    d = synthetic.a4w4(m, n, k)
+    g = torch.from_numpy(synthetic.rng(1006).normal(0, 1, (m, n)).astype(np.float32)).to(torch.float16)
+    sag = torch.tensor([d["scale_a"]], dtype=torch.float32, device=DEV)
+    swg = torch.tensor([d["scale_w"]], dtype=torch.float32, device=DEV)
+    gx, gw, gs = ql.qlinear_q4_backward(_cuda(g), _cuda(d["x"]), _cuda(d["w"]), sag, swg, d["eps"])
+    torch.cuda.synchronize()
+    x, w, gn = d["x"].float().numpy(), d["w"].float().numpy(), g.float().numpy()
+    rows = _rows(m, 2007, extra=8)
+    rx = oracle.q4_backward(gn[rows], x[rows], w, d["scale_a"], d["scale_w"], d["eps"])
+    cols = _rows(n, 2008, extra=8)
+    rw = oracle.q4_backward(gn[:, cols], x, w[cols], d["scale_a"], d["scale_w"], d["eps"])
+    u = 2.0 ** -24
+    got_x = to_np(gx[torch.from_numpy(rows).to(DEV)]).astype(np.float64)
+    assert np.all(np.abs(got_x - rx[0]) <= n * u * rx[3] + 3 * u * np.abs(rx[0]) + 1e-30), "grad_x rows"
+    got_w = to_np(gw[torch.from_numpy(cols).to(DEV)]).astype(np.float64)
+    assert np.all(np.abs(got_w - rw[1]) <= m * u * rw[4] + 3 * u * np.abs(rw[1]) + 1e-30), "grad_w rows"
+    assert np.isfinite(gs.item())
+

@@ -557,3 +557,83 @@ def test_a4w4_operands_equal_int8_codes_bit_for_bit(m, n, k):
                            b.view(torch.int16) if dt != torch.int32 else b), f"{dt}"
     qa = oracle.quant_int4_tensor(d["x"].float().numpy(), d["scale_a"], d["eps"])
     assert_equal(xq, qa, "x codes")
+
+
+# ---------------------------------------------------------------------------
+# Q4Linear backward
+# ---------------------------------------------------------------------------
+U24 = 2.0 ** -24
+
+
+def _q4_bwd_inputs(m, n, k, dt, seed, clip=0.6):
+    r = synthetic.rng(seed)
+    x = torch.from_numpy(r.normal(0, 1, (m, k)).astype(np.float32)).to(dt)
+    w = torch.from_numpy((0.02 * r.normal(0, 1, (n, k))).astype(np.float32)).to(dt)
+    g = torch.from_numpy(r.normal(0, 1, (m, n)).astype(np.float32)).to(dt)
+    sa = float(np.float32(x.float().abs().max().item() / 7 * clip))
+    sw = float(np.float32(w.float().abs().max().item() / 7 * clip))
+    return g, x, w, sa, sw
+
+
+def _q4_bwd_check(gx, gw, gs, ref, n, m, what):
+    """fp32 accumulation over a sum of n (grad_x) or m (grad_w) exact products,
+    then one fp32 multiply and the output rounding; the scale gradient adds
+    each term's error, at most (n + 1) u bx |t|, and is rounded to fp32 once."""
+    rx, rw, rs, bx, bw, bs = ref
+    for got, want, b, depth, name in ((gx, rx, bx, n, "grad_x"), (gw, rw, bw, m, "grad_w")):
+        rel = {torch.float32: U24, torch.float16: 2.0 ** -11, torch.bfloat16: 2.0 ** -8}[got.dtype]
+        g = to_np(got).astype(np.float64)
+        tol = depth * U24 * b + 2 * U24 * np.abs(want) + rel * np.abs(want) + 1e-30
+        err = np.abs(g - want)
+        assert np.all(err <= tol), f"{what} {name}: max err/tol {np.max(err / tol)}"
+        assert np.array_equal(g == 0, want == 0) or np.all(g[want == 0] == 0), f"{what} {name}: range mask"
+    # + one fp32 multiply per term and the fp32 rounding of the fp64 sum
+    assert abs(float(gs) - rs) <= (n + 1) * U24 * bs + U24 * abs(rs) + 1e-30, f"{what} grad_scale_a {float(gs)} vs {rs}"
+
+
+@pytest.mark.parametrize("dt", [torch.float16, torch.bfloat16])
+@pytest.mark.parametrize("m,n,k", [(64, 48, 40), (300, 270, 200), (512, 512, 512), (520, 777, 300), (1, 1, 1),
+                                   (33, 64, 1000)])
+def test_q4_backward_parity(dt, m, n, k):
+    g, x, w, sa, sw = _q4_bwd_inputs(m, n, k, dt, seed=4000 + m + n + k)
+    ref = oracle.q4_backward(g.float().numpy(), x.float().numpy(), w.float().numpy(), sa, sw, 1e-5)
+    sag = torch.tensor([sa], dtype=torch.float32, device=DEV)
+    swg = torch.tensor([sw], dtype=torch.float32, device=DEV)
+    gx = poison((m, k), torch.float32)
+    gw = poison((n, k), torch.float32)
+    gx, gw, gs = ql.qlinear_q4_backward(_cuda(g), _cuda(x), _cuda(w), sag, swg, 1e-5, grad_x=gx, grad_w=gw)
+    _sync()
+    _q4_bwd_check(gx, gw, gs.item(), ref, n, m, f"{dt} {m}x{n}x{k}")
+
+
+@pytest.mark.parametrize("gdt", [torch.float16, torch.bfloat16])
+def test_q4_backward_16bit_grads(gdt):
+    m, n, k = 300, 256, 320
+    g, x, w, sa, sw = _q4_bwd_inputs(m, n, k, torch.float16, seed=4100)
+    ref = oracle.q4_backward(g.float().numpy(), x.float().numpy(), w.float().numpy(), sa, sw, 1e-5)
+    sag = torch.tensor([sa], dtype=torch.float32, device=DEV)
+    swg = torch.tensor([sw], dtype=torch.float32, device=DEV)
+    gx, gw, gs = ql.qlinear_q4_backward(_cuda(g), _cuda(x), _cuda(w), sag, swg, 1e-5, grad_dtype=gdt)
+    gx32, gw32, gs32 = ql.qlinear_q4_backward(_cuda(g), _cuda(x), _cuda(w), sag, swg, 1e-5)
+    _sync()
+    _q4_bwd_check(gx, gw, gs.item(), ref, n, m, f"grads {gdt}")
+    # the 16-bit gradients are the fp32 ones rounded once
+    assert torch.equal(gx, gx32.to(gdt)) and torch.equal(gw, gw32.to(gdt))
+    assert gs.item() == gs32.item()
+
+
+def test_q4_backward_deterministic_and_eps():
+    m, n, k = 520, 300, 260
+    g, x, w, sa, sw = _q4_bwd_inputs(m, n, k, torch.float16, seed=4200)
+    sag = torch.tensor([sa], dtype=torch.float32, device=DEV)
+    swg = torch.tensor([sw], dtype=torch.float32, device=DEV)
+    a = ql.qlinear_q4_backward(_cuda(g), _cuda(x), _cuda(w), sag, swg, 1e-5)
+    b = ql.qlinear_q4_backward(_cuda(g), _cuda(x), _cuda(w), sag, swg, 1e-5)
+    # a scale below eps: no scale gradient
+    tiny = torch.tensor([1e-9], dtype=torch.float32, device=DEV)
+    c = ql.qlinear_q4_backward(_cuda(g), _cuda(x), _cuda(w), tiny, swg, 1e-5)
+    _sync()
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+    assert a[2].item() == b[2].item()
+    assert c[2].item() == 0.0
+
