@@ -345,9 +345,9 @@ hipError_t backward_t(const Q4BackwardArgs &a, hipStream_t st) {
     hipError_t e;
     if (n % 32 != 0) {
         uint16_t *pad = reinterpret_cast<uint16_t *>(ws);
-        const int64_t total = m * np;
-        hipLaunchKernelGGL(bwd_pad_kernel, dim3((unsigned)((total + kTThreads - 1) / kTThreads)), dim3(kTThreads), 0,
-                           st, gp, m, n, np, pad);
+        const int64_t blocks = (m * np + kTThreads - 1) / kTThreads;
+        if (blocks > 0x7fffffff) return hipErrorInvalidValue;
+        hipLaunchKernelGGL(bwd_pad_kernel, dim3((unsigned)blocks), dim3(kTThreads), 0, st, gp, m, n, np, pad);
         if ((e = hipGetLastError()) != hipSuccess) return e;
         gp = pad;
     }
