@@ -18,8 +18,9 @@
 // feeds two MFMA row blocks; m <= 16 uses RB = 1).  Each wave keeps two
 // register stages: while the matrix cores consume one k block, the weight
 // fragments (non-temporal: read once), scales, zero-points and x fragments
-// of its next k block are in flight.  The fp32 partials of the waves are
-// added in LDS in a fixed wave order.
+// of its next k block are in flight; when a wave has at most four k blocks
+// (k <= 4096 with 8 waves) it issues all of their loads at once instead.
+// The fp32 partials of the waves are added in LDS in a fixed wave order.
 #include "ql_device.hpp"
 #include "ql_launch.hpp"
 
@@ -107,7 +108,7 @@ __device__ __forceinline__ void compute_stage(const Stage<NBLK, RB> &st, v4f (&a
     }
 }
 
-template <int NBLK, int WAVES, int RB, int OUT>
+template <int NBLK, int WAVES, int RB, int OUT, int NST>
 __global__ __launch_bounds__(WAVES * 64) void int4_grouped_kernel(const uint16_t *__restrict__ x,
                                                                   const uint32_t *__restrict__ packed_w,
                                                                   const uint16_t *__restrict__ scales,
@@ -137,25 +138,40 @@ __global__ __launch_bounds__(WAVES * 64) void int4_grouped_kernel(const uint16_t
 #pragma unroll
         for (int j = 0; j < NBLK; j++) acc[b][j] = v4f{0.f, 0.f, 0.f, 0.f};
 
-    // The wave owns k blocks wave, wave + WAVES, ...  Two register stages:
-    // the loads of the next k block are in flight while the matrix cores
-    // work on the current one.
-    Stage<NBLK, RB> s0, s1;
-    int64_t kb = wave;
-    load_stage(s0, xrow, packed_w, scales, packed_z, kb, nb0, nblocks, kblocks, group_size, groups, n, lane);
-    while (kb < kblocks) {
-        const int64_t kb1 = kb + WAVES;
-        if (kb1 < kblocks)
-            load_stage(s1, xrow, packed_w, scales, packed_z, kb1, nb0, nblocks, kblocks, group_size, groups, n,
-                       lane);
-        compute_stage(s0, acc, true, nb0, nblocks);
-        if (kb1 >= kblocks) break;
-        const int64_t kb2 = kb1 + WAVES;
-        if (kb2 < kblocks)
-            load_stage(s0, xrow, packed_w, scales, packed_z, kb2, nb0, nblocks, kblocks, group_size, groups, n,
-                       lane);
-        compute_stage(s1, acc, true, nb0, nblocks);
-        kb = kb2;
+    // The wave owns k blocks wave, wave + WAVES, ...  NST > 0: the loads of
+    // NST of them are issued together, then consumed in k order (one memory
+    // round trip when the wave has at most NST blocks).  NST = 0: two
+    // register stages, the loads of the next k block in flight while the
+    // matrix cores work on the current one.  Both add the blocks in the same
+    // order, so both give the same bits.
+    if constexpr (NST > 0) {
+        for (int64_t kb0 = wave; kb0 < kblocks; kb0 += (int64_t)WAVES * NST) {
+            Stage<NBLK, RB> st[NST];
+#pragma unroll
+            for (int u = 0; u < NST; u++)
+                load_stage(st[u], xrow, packed_w, scales, packed_z, kb0 + (int64_t)u * WAVES, nb0, nblocks, kblocks,
+                           group_size, groups, n, lane);
+#pragma unroll
+            for (int u = 0; u < NST; u++) compute_stage(st[u], acc, kb0 + (int64_t)u * WAVES < kblocks, nb0, nblocks);
+        }
+    } else {
+        Stage<NBLK, RB> s0, s1;
+        int64_t kb = wave;
+        load_stage(s0, xrow, packed_w, scales, packed_z, kb, nb0, nblocks, kblocks, group_size, groups, n, lane);
+        while (kb < kblocks) {
+            const int64_t kb1 = kb + WAVES;
+            if (kb1 < kblocks)
+                load_stage(s1, xrow, packed_w, scales, packed_z, kb1, nb0, nblocks, kblocks, group_size, groups, n,
+                           lane);
+            compute_stage(s0, acc, true, nb0, nblocks);
+            if (kb1 >= kblocks) break;
+            const int64_t kb2 = kb1 + WAVES;
+            if (kb2 < kblocks)
+                load_stage(s0, xrow, packed_w, scales, packed_z, kb2, nb0, nblocks, kblocks, group_size, groups, n,
+                           lane);
+            compute_stage(s1, acc, true, nb0, nblocks);
+            kb = kb2;
+        }
     }
 
 #pragma unroll
@@ -180,14 +196,21 @@ __global__ __launch_bounds__(WAVES * 64) void int4_grouped_kernel(const uint16_t
     }
 }
 
+// Waves with at most this many k blocks issue all their loads at once.
+constexpr int kAllIn = 4;
+
 template <int NBLK, int WAVES, int RB, int OUT>
 hipError_t launch_cfg(const uint16_t *x, const uint32_t *packed_w, const uint16_t *scales,
                       const uint32_t *packed_z, const float *bias, int64_t group_size, int64_t m, int64_t n, int64_t k,
                       void *out, hipStream_t st) {
     const int64_t nblocks = n / 16;
     dim3 grid((unsigned)((nblocks + NBLK - 1) / NBLK), (unsigned)((m + 16 * RB - 1) / (16 * RB)));
-    hipLaunchKernelGGL((int4_grouped_kernel<NBLK, WAVES, RB, OUT>), grid, dim3(WAVES * 64), 0, st, x,
-                       packed_w, scales, packed_z, bias, group_size, m, n, k, out);
+    if (k / 128 <= (int64_t)WAVES * kAllIn)
+        hipLaunchKernelGGL((int4_grouped_kernel<NBLK, WAVES, RB, OUT, kAllIn>), grid, dim3(WAVES * 64), 0, st, x,
+                           packed_w, scales, packed_z, bias, group_size, m, n, k, out);
+    else
+        hipLaunchKernelGGL((int4_grouped_kernel<NBLK, WAVES, RB, OUT, 0>), grid, dim3(WAVES * 64), 0, st, x,
+                           packed_w, scales, packed_z, bias, group_size, m, n, k, out);
     return hipGetLastError();
 }
 
@@ -283,7 +306,7 @@ __device__ __forceinline__ void compute_stage_i8(const StageI8<NBLK, RB> &st, v4
     }
 }
 
-template <int NBLK, int WAVES, int RB, int OUT>
+template <int NBLK, int WAVES, int RB, int OUT, int NST>
 __global__ __launch_bounds__(WAVES * 64) void int4_grouped_i8_kernel(const int8_t *__restrict__ xq,
                                                                      const float *__restrict__ pts,
                                                                      const uint32_t *__restrict__ packed_w,
@@ -318,22 +341,37 @@ __global__ __launch_bounds__(WAVES * 64) void int4_grouped_i8_kernel(const int8_
 #pragma unroll
         for (int j = 0; j < NBLK; j++) acc[b][j] = v4f{0.f, 0.f, 0.f, 0.f};
 
-    StageI8<NBLK, RB> s0, s1;
-    int64_t kb = wave;
-    load_stage_i8(s0, xrow, packed_w, scales, packed_z, kb, nb0, nblocks, kblocks, group_size, groups, n, lane);
-    while (kb < kblocks) {
-        const int64_t kb1 = kb + WAVES;
-        if (kb1 < kblocks)
-            load_stage_i8(s1, xrow, packed_w, scales, packed_z, kb1, nb0, nblocks, kblocks, group_size, groups,
-                          n, lane);
-        compute_stage_i8(s0, acc, nb0, nblocks);
-        if (kb1 >= kblocks) break;
-        const int64_t kb2 = kb1 + WAVES;
-        if (kb2 < kblocks)
-            load_stage_i8(s0, xrow, packed_w, scales, packed_z, kb2, nb0, nblocks, kblocks, group_size, groups,
-                          n, lane);
-        compute_stage_i8(s1, acc, nb0, nblocks);
-        kb = kb2;
+    // As in the fp16 kernel: NST > 0 issues the loads of NST k blocks
+    // together; NST = 0 pipelines two register stages.  Same order, same bits.
+    if constexpr (NST > 0) {
+        for (int64_t kb0 = wave; kb0 < kblocks; kb0 += (int64_t)WAVES * NST) {
+            StageI8<NBLK, RB> st[NST];
+#pragma unroll
+            for (int u = 0; u < NST; u++)
+                load_stage_i8(st[u], xrow, packed_w, scales, packed_z, kb0 + (int64_t)u * WAVES, nb0, nblocks,
+                              kblocks, group_size, groups, n, lane);
+#pragma unroll
+            for (int u = 0; u < NST; u++)
+                if (kb0 + (int64_t)u * WAVES < kblocks) compute_stage_i8(st[u], acc, nb0, nblocks);
+        }
+    } else {
+        StageI8<NBLK, RB> s0, s1;
+        int64_t kb = wave;
+        load_stage_i8(s0, xrow, packed_w, scales, packed_z, kb, nb0, nblocks, kblocks, group_size, groups, n, lane);
+        while (kb < kblocks) {
+            const int64_t kb1 = kb + WAVES;
+            if (kb1 < kblocks)
+                load_stage_i8(s1, xrow, packed_w, scales, packed_z, kb1, nb0, nblocks, kblocks, group_size, groups,
+                              n, lane);
+            compute_stage_i8(s0, acc, nb0, nblocks);
+            if (kb1 >= kblocks) break;
+            const int64_t kb2 = kb1 + WAVES;
+            if (kb2 < kblocks)
+                load_stage_i8(s0, xrow, packed_w, scales, packed_z, kb2, nb0, nblocks, kblocks, group_size, groups,
+                              n, lane);
+            compute_stage_i8(s1, acc, nb0, nblocks);
+            kb = kb2;
+        }
     }
 
 #pragma unroll
@@ -365,8 +403,12 @@ hipError_t launch_cfg_i8(const int8_t *xq, const float *pts, const uint32_t *pac
                          hipStream_t st) {
     const int64_t nblocks = n / 16;
     dim3 grid((unsigned)((nblocks + NBLK - 1) / NBLK), (unsigned)((m + 16 * RB - 1) / (16 * RB)));
-    hipLaunchKernelGGL((int4_grouped_i8_kernel<NBLK, WAVES, RB, OUT>), grid, dim3(WAVES * 64), 0, st, xq, pts,
-                       packed_w, scales, packed_z, bias, group_size, m, n, k, out);
+    if (k / 128 <= (int64_t)WAVES * kAllIn)
+        hipLaunchKernelGGL((int4_grouped_i8_kernel<NBLK, WAVES, RB, OUT, kAllIn>), grid, dim3(WAVES * 64), 0, st, xq,
+                           pts, packed_w, scales, packed_z, bias, group_size, m, n, k, out);
+    else
+        hipLaunchKernelGGL((int4_grouped_i8_kernel<NBLK, WAVES, RB, OUT, 0>), grid, dim3(WAVES * 64), 0, st, xq,
+                           pts, packed_w, scales, packed_z, bias, group_size, m, n, k, out);
     return hipGetLastError();
 }
 

@@ -282,7 +282,8 @@ def test_w2a8_gemv_deterministic():
 # Grouped affine INT4
 # ---------------------------------------------------------------------------
 @pytest.mark.parametrize("m,n,k,g", [(1, 48, 256, 128), (5, 400, 512, 128), (32, 400, 512, 256),
-                                     (40, 64, 384, 128), (32, 16, 128, 128), (3, 32, 1024, 1024)])
+                                     (40, 64, 384, 128), (32, 16, 128, 128), (3, 32, 1024, 1024),
+                                     (5, 64, 8192, 256)])   # more than 4 k blocks per wave: pipelined stages
 def test_grouped_int4_parity(m, n, k, g):
     d = synthetic.grouped_int4(m, n, k, g, seed=700 + m + n + k)
     x, q, s, z = d["x"], d["q"], d["s"], d["z"]
@@ -323,7 +324,7 @@ def _grouped_i8_inputs(m, n, k, g, seed):
 
 @pytest.mark.parametrize("m,n,k,g", [(1, 48, 256, 128), (5, 400, 512, 128), (16, 64, 256, 128),
                                      (17, 400, 512, 256), (32, 400, 512, 128), (40, 64, 384, 128),
-                                     (3, 32, 1024, 1024)])
+                                     (3, 32, 1024, 1024), (17, 64, 8192, 128)])
 def test_grouped_int4_i8_parity(m, n, k, g):
     """int8 activation codes: fp32 output within the arithmetic's bound, 16-bit outputs
     within the grouped bar and equal to the fp32 output rounded once."""
