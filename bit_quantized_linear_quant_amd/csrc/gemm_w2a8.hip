@@ -12,7 +12,11 @@
 // core sums matching terms.  The accumulator holds sum x*(code+1); the
 // epilogue subtracts the token's code sum: acc = sum x*code exactly.
 //
-// m > 16: 128 x 128 tiles, 2 x 2 waves of 64 x 64, A staged in LDS per
+// m >= 256: 256 x 128 tiles on v_mfma_i32_32x32x32_i8, activation codes
+//         and packed weights streamed into LDS through a ring of 128-k
+//         slices; each lane takes its weight words from LDS in the order the
+//         32x32x32 operand needs.
+// 16 < m < 256: 128 x 128 tiles, 2 x 2 waves of 64 x 64, A staged in LDS per
 //         256-k step (rows padded to 272 bytes), B loaded per wave.
 // m <= 16: decode GEMV.  The m rows fill one 16-row MFMA block (rows past m
 //         repeat row 0 and are never stored); each workgroup owns NBLK
@@ -177,56 +181,66 @@ __global__ __launch_bounds__(kGThreads) void w2a8_gemm_kernel(const int8_t *__re
 // m >= 256: large-tile GEMM
 // ---------------------------------------------------------------------------
 // A 256-thread workgroup owns a 256 x 128 output tile; wave (wm, wn) owns
-// 128 x 64 as 8 x 4 blocks of v_mfma_i32_16x16x64_i8.  Per 256-k block:
-//   * the A slice (256 token rows x 256 code bytes, 64 KB) goes HBM -> LDS
-//     with global_load_lds_dwordx4, double-buffered; 16-byte chunk c of row r
-//     is stored at chunk position c ^ (r & 15), so the 16 rows read by one
-//     fragment load sit in distinct bank groups;
-//   * the tile's eight packed weight fragment blocks (1 KB each, already in
-//     lane order) go HBM -> LDS the same way; each wave reads its four and
-//     unpacks them in registers.
-// Step t of a block uses, for lane l, k = 64(l/16) + 16t: chunk 4(l/16) + t
-// of the A row and word t of the weight fragment.
-constexpr int XBM = 256, XBN = 128, XBK = 256;
+// 128 x 64 as 4 x 2 blocks of v_mfma_i32_32x32x32_i8 (the 16x16x64 form
+// sustains about 60% of the 32x32x32 rate on gfx950).  The k loop runs over
+// 128-k slices through a ring of four LDS stages: three slices stream in while
+// the matrix cores consume the fourth, with one vmcnt wait and one barrier
+// per slice.  Slice sl = 2 kb + hh holds half hh of k block kb:
+//   * the activation codes of k 128 sl .. +127 (256 rows x 128 bytes, 32 KB)
+//     go HBM -> LDS with global_load_lds_dwordx4; 16-byte chunk c of row r
+//     sits at chunk position c ^ (r & 7), so the 8 rows read together by a
+//     fragment load fall in distinct bank groups;
+//   * packed lanes 32 hh .. 32 hh + 31 of each of the tile's eight fragment
+//     blocks (the k groups 2 hh and 2 hh + 1, 512 contiguous bytes each).
+// Step t (0..3) of a slice gives lane half h = lane / 32 the k group
+// g = 2 hh + h and the weight word t: for the A operand, the 16 codes of
+// chunk 4 h + t of its slice row (k = 256 kb + 64 g + 16 t); for B, word t of
+// packed lane (column % 16) + 16 g, unpacked in registers.  Both operands
+// take the same 16 k, so the matrix core sums matching terms.
+constexpr int XBM = 256, XBN = 128, XBK = 128;
 constexpr int kXThreads = 256;
 constexpr int kXGroupM = 4;
-constexpr int kXSlice = XBM * XBK;                     // bytes of one A slice
-constexpr int kXBSlice = XBN / 16 * 1024;              // bytes of one B slice (8 fragment blocks)
-constexpr int kXStage = kXSlice + kXBSlice;
-constexpr int kXLoads = kXSlice / 1024 / (kXThreads / kWave);   // 1 KB A loads per wave per slice
-constexpr int kXBLoads = kXBSlice / 1024 / (kXThreads / kWave); // 1 KB B loads per wave per slice
+constexpr int kXBuf = 4;                               // ring stages
+constexpr int kXASlice = XBM * XBK;                    // bytes of activation codes per slice
+constexpr int kXBSlice = XBN / 16 * 512;               // bytes of packed weights per slice
+constexpr int kXStage = kXASlice + kXBSlice;
+constexpr int kXLoads = kXASlice / 1024 / (kXThreads / kWave);  // 1 KB A loads per wave per slice
+static_assert(kXBSlice == 1024 * (kXThreads / kWave), "one 1 KB weight load per wave per slice");
 
-__device__ __forceinline__ void xs_wait_all() { __builtin_amdgcn_s_waitcnt(0); }
+typedef int v16i __attribute__((ext_vector_type(16)));
 
-// One 256-k block: the loads of the next block go to `nxt` while the matrix
-// cores consume `cur`.  The two slices are distinct restrict pointers, so the
-// compiler knows the LDS reads of `cur` do not depend on the loads into `nxt`
-// and does not make them wait for those loads.
-__device__ __forceinline__ void w2a8_big_step(v4i (&acc)[8][4], const int8_t *__restrict__ cur,
-                                              int8_t *__restrict__ nxt, const int8_t *const (&srca)[kXLoads],
-                                              const uint32_t *const (&srcb)[kXBLoads], int64_t koff_a,
-                                              int64_t koff_b, int wave, int wn, int lane, int aoff0) {
+// Bytes of LDS the epilogue of a 256 x 128 tile uses: the rows' code sums
+// and scales, then a padded 128 x 64 output tile per wave.
+template <int OUT>
+constexpr int xepi_bytes() {
+    return 2 * XBM * 4 + 4 * 128 * (64 * (OUT == OUT_I32 || OUT == OUT_F32 ? 4 : 2) + 16);
+}
+
+// One slice: the direct loads of slice nxt_sl into `nxt`, then the four
+// MFMA steps on `cur`.  `cur` and `nxt` are distinct restrict pointers, so
+// the compiler does not make the fragment reads of `cur` wait for the loads
+// into `nxt`.
+__device__ __forceinline__ void w2a8_big_slice(v16i (&acc)[4][2], const int8_t *__restrict__ cur,
+                                               int8_t *__restrict__ nxt, const int8_t *const (&srca)[kXLoads],
+                                               const int8_t *srcb, int64_t nxt_sl, int aoff, int boff, int wave) {
 #pragma unroll
-    for (int ii = 0; ii < kXLoads; ii++) lds_load16(srca[ii] + koff_a, nxt + 1024 * (kXLoads * wave + ii));
+    for (int ii = 0; ii < kXLoads; ii++) lds_load16(srca[ii] + nxt_sl * XBK, nxt + 1024 * (kXLoads * wave + ii));
+    lds_load16(srcb + nxt_sl * 512, nxt + kXASlice + 1024 * wave);
+    uint4 bw[2];
 #pragma unroll
-    for (int jj = 0; jj < kXBLoads; jj++)
-        lds_load16(srcb[jj] + koff_b, nxt + kXSlice + 1024 * (kXBLoads * wave + jj));
-    uint4 bw[4];
-#pragma unroll
-    for (int j = 0; j < 4; j++) bw[j] = *reinterpret_cast<const uint4 *>(cur + kXSlice + 1024 * (4 * wn + j) + 16 * lane);
-    const int fr = lane % 16, g4 = 4 * (lane / 16);
-    v4i fa[2][8];
+    for (int j = 0; j < 2; j++) bw[j] = *reinterpret_cast<const uint4 *>(cur + boff + 1024 * j);
+    v4i fa[2][4];
 #pragma unroll
     for (int t = 0; t < 4; t++) {
-        const int off = aoff0 + 16 * ((g4 + t) ^ fr);
+        // chunk 4h + t is at position (4h + t) ^ (row & 7) = (4h ^ (row & 7)) ^ t
 #pragma unroll
-        for (int i = 0; i < 8; i++) fa[t & 1][i] = *reinterpret_cast<const v4i *>(cur + off + i * 16 * XBK);
+        for (int i = 0; i < 4; i++) fa[t & 1][i] = *reinterpret_cast<const v4i *>(cur + (aoff ^ (16 * t)) + i * 32 * XBK);
 #pragma unroll
-        for (int j = 0; j < 4; j++) {
+        for (int j = 0; j < 2; j++) {
             const v4i b = unpack_tern(word_of(bw[j], t));
 #pragma unroll
-            for (int i = 0; i < 8; i++)
-                acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(fa[t & 1][i], b, acc[i][j], 0, 0, 0);
+            for (int i = 0; i < 4; i++)
+                acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fa[t & 1][i], b, acc[i][j], 0, 0, 0);
         }
     }
 }
@@ -241,60 +255,71 @@ __global__ __launch_bounds__(kXThreads, 1) void w2a8_big_kernel(const int8_t *__
                                                                 int64_t m, int64_t n, int64_t k,
                                                                 void *__restrict__ out, int tiles_m,
                                                                 int tiles_n) {
-    __shared__ __attribute__((aligned(1024))) int8_t smem[2 * kXStage];
+    constexpr int SMEM = kXBuf * kXStage > xepi_bytes<OUT>() ? kXBuf * kXStage : xepi_bytes<OUT>();
+    __shared__ __attribute__((aligned(1024))) int8_t smem[SMEM];
     const int lane = threadIdx.x % kWave, wave = wave_id();
     const int wm = wave / 2, wn = wave % 2;
     int tm, tn;
     xcd_tile(blockIdx.x, tiles_m, tiles_n, kXGroupM, tm, tn);
     const int64_t m0 = (int64_t)tm * XBM, n0 = (int64_t)tn * XBN;
-    const int64_t kblocks = k / XBK, nblocks = n / 16;
+    const int64_t nsl = k / XBK, nblocks = n / 16;
 
-    // A load ii of this wave fills LDS bytes [1024 (16 wave + ii), +1024) of
-    // the slice: chunk position lane % 16 of row 64 wave + 4 ii + lane / 16.
-    // B load jj fills fragment block 2 wave + jj of the tile's 8 column
-    // blocks, which is 1 KB of the packed weight in lane order.  Sources are
-    // given for k block 0; block kb adds kb * 256 bytes (A) or kb * 256 words (B).
+    // A load ii of this wave fills LDS bytes [1024 (8 wave + ii), +1024) of
+    // the slice: row 8 (8 wave + ii) + lane / 8, chunk position lane % 8.
+    // Sources are given for slice 0; slice sl adds 128 sl bytes.
     const int8_t *srca[kXLoads];
 #pragma unroll
     for (int ii = 0; ii < kXLoads; ii++) {
-        const int row = 64 * wave + 4 * ii + lane / 16;
-        const int c = (lane % 16) ^ (row & 15);
+        const int row = 8 * (kXLoads * wave + ii) + lane / 8;
+        const int c = (lane % 8) ^ (row & 7);
         const int64_t r = m0 + row < m ? m0 + row : m - 1;
         srca[ii] = xq + r * k + 16 * c;
     }
-    const uint32_t *srcb[kXBLoads];
-#pragma unroll
-    for (int jj = 0; jj < kXBLoads; jj++) {
-        const int blk = kXBLoads * wave + jj;
+    // The weight load of this wave: 32 lanes each in fragment blocks 2 wave
+    // and 2 wave + 1 of the tile.  The half hh of k block kb (1 KB per block)
+    // starts at byte 1024 kb + 512 hh = 512 sl.
+    const int8_t *srcb;
+    {
+        const int blk = 2 * wave + lane / 32;
         const int64_t nb = n0 / 16 + blk < nblocks ? n0 / 16 + blk : nblocks - 1;
-        srcb[jj] = packed + nb * kblocks * 256 + 4 * lane;
+        srcb = reinterpret_cast<const int8_t *>(packed) + nb * (k / 256) * 1024 + 16 * (lane % 32);
     }
-    // A fragment of step t, row block i: row 128 wm + 16 i + lane % 16,
-    // chunk 4 (lane / 16) + t, stored at chunk position ^ (lane % 16).
-    const int aoff0 = (128 * wm + lane % 16) * XBK;
+    // Fragment offsets: A row 128 wm + 32 i + lane % 32 (block i adds 32
+    // rows); B column block j of the wave is fragment block 4 wn + 2 j +
+    // (lane % 32) / 16, stored lane (lane % 16) + 16 h.
+    const int h = lane / 32, fr = lane % 32;
+    const int aoff = (128 * wm + fr) * XBK + 16 * ((4 * h) ^ (fr & 7));
+    const int boff = kXASlice + 512 * (4 * wn + fr / 16) + 16 * (fr % 16 + 16 * h);
 
-    v4i acc[8][4];
+    v16i acc[4][2];
 #pragma unroll
-    for (int i = 0; i < 8; i++)
+    for (int i = 0; i < 4; i++)
 #pragma unroll
-        for (int j = 0; j < 4; j++) acc[i][j] = v4i{0, 0, 0, 0};
+        for (int j = 0; j < 2; j++) acc[i][j] = v16i{};
 
+    // Slices 0 .. kXBuf-2 in flight before the loop; iteration sl consumes
+    // slice sl and starts slice sl + kXBuf - 1 (clamped: the last iterations
+    // reload the final slice, keeping the loop body free of branches) into
+    // the stage that iteration sl - 1 consumed.
 #pragma unroll
-    for (int ii = 0; ii < kXLoads; ii++) lds_load16(srca[ii], smem + 1024 * (kXLoads * wave + ii));
+    for (int b = 0; b < kXBuf - 1; b++) {
+        const int64_t sl = b < nsl ? b : nsl - 1;
 #pragma unroll
-    for (int jj = 0; jj < kXBLoads; jj++) lds_load16(srcb[jj], smem + kXSlice + 1024 * (kXBLoads * wave + jj));
-    xs_wait_all();
+        for (int ii = 0; ii < kXLoads; ii++)
+            lds_load16(srca[ii] + sl * XBK, smem + b * kXStage + 1024 * (kXLoads * wave + ii));
+        lds_load16(srcb + sl * 512, smem + b * kXStage + kXASlice + 1024 * wave);
+    }
+    for (int64_t sl = 0; sl < nsl; sl++) {
+        // this wave's loads of slice sl are done; after the barrier every
+        // wave's are, and every wave has finished reading the stage refilled
+        wait_vmcnt<(kXBuf - 2) * (kXLoads + 1)>();
+        barrier_only();
+        const int cur = (int)(sl % kXBuf), nxt = (int)((sl + kXBuf - 1) % kXBuf);
+        const int64_t nxt_sl = sl + kXBuf - 1 < nsl ? sl + kXBuf - 1 : nsl - 1;
+        w2a8_big_slice(acc, smem + cur * kXStage, smem + nxt * kXStage, srca, srcb, nxt_sl, aoff, boff, wave);
+    }
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    for (int64_t kb = 0; kb < kblocks; kb++) {
-        const int cur = (int)(kb & 1);
-        // block kb + 1 streams into the other buffer (the last block reloads
-        // its own slice there, keeping the loop body free of branches)
-        const int64_t nxt = kb + 1 < kblocks ? kb + 1 : kb;
-        w2a8_big_step(acc, smem + cur * kXStage, smem + (cur ^ 1) * kXStage, srca, srcb, nxt * XBK, nxt * 256,
-                      wave, wn, lane, aoff0);
-        xs_wait_all();
-        __syncthreads();
-    }
 
     // Epilogue through LDS: each wave converts its 128 x 64 sub-tile into an
     // LDS tile (rows padded by 16 bytes, so the four row groups of one write
@@ -309,24 +334,25 @@ __global__ __launch_bounds__(kXThreads, 1) void w2a8_big_kernel(const int8_t *__
     constexpr int PITCH = ROWB + 16;
     int8_t *tile = smem + 2 * XBM * 4 + wave * 128 * PITCH;
     const float g = OUT == OUT_I32 ? 0.0f : (float)gamma[0];  // gamma may be NULL for int32 output
-    float cbj[4];
+    float cbj[2];
 #pragma unroll
-    for (int j = 0; j < 4; j++) {
-        const int64_t col = n0 + 64 * wn + 16 * j + lane % 16;
+    for (int j = 0; j < 2; j++) {
+        const int64_t col = n0 + 64 * wn + 32 * j + fr;
         cbj[j] = (OUT != OUT_I32 && bias) ? bias[col < n ? col : n - 1] : 0.0f;
     }
-    // Lane l holds column l % 16 and rows 4(l/16) + r of each 16 x 16 block.
+    // Lane l holds column l % 32 of each 32 x 32 block and rows
+    // 8 (r / 4) + 4 (l / 32) + r % 4 of register r.
 #pragma unroll
-    for (int i = 0; i < 8; i++)
+    for (int i = 0; i < 4; i++)
 #pragma unroll
-        for (int r = 0; r < 4; r++) {
-            const int lr = 16 * i + 4 * (lane / 16) + r;          // row within the sub-tile
+        for (int r = 0; r < 16; r++) {
+            const int lr = 32 * i + 8 * (r / 4) + 4 * h + r % 4;      // row within the sub-tile
             const int local = 128 * wm + lr;
             const float rf = OUT == OUT_I32 ? 0.0f : pts_lds[local];
             const int32_t rsv = rs_lds[local];
 #pragma unroll
-            for (int j = 0; j < 4; j++) {
-                const int c = 16 * j + lane % 16;
+            for (int j = 0; j < 2; j++) {
+                const int c = 32 * j + fr;
                 const int32_t v = acc[i][j][r] - rsv;
                 int8_t *dst = tile + lr * PITCH + c * ES;
                 if constexpr (OUT == OUT_I32) *reinterpret_cast<int32_t *>(dst) = v;

@@ -241,8 +241,10 @@ def test_pack_int4_parity(n, k):
 # ---------------------------------------------------------------------------
 # BitLinear: quant_act -> pack_ternary -> w2a8
 # ---------------------------------------------------------------------------
+# m >= 256 takes the large-tile kernel: one exact tile with fewer 128-k
+# slices than ring stages, ragged m and n over several tiles, a longer k.
 W2A8_SHAPES = [(1, 400, 512), (2, 256, 768), (4, 400, 512), (5, 64, 256), (16, 400, 768), (17, 400, 512),
-               (130, 256, 768), (300, 400, 512)]
+               (130, 256, 768), (300, 400, 512), (256, 128, 256), (513, 272, 1280), (600, 528, 2304)]
 
 
 @pytest.mark.parametrize("m,n,k", W2A8_SHAPES)
