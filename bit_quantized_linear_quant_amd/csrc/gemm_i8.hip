@@ -21,7 +21,7 @@
 //   tile as whole row segments.
 //
 // gemm_i8_kernel -- everything else (any m, n, k >= 1, weights [k][n] or
-//   [n][k]): 128 x 128 tiles, 2 x 2 waves of 64 x 64 in 16x16x64 MFMA blocks,
+//   [n][k]): 128 x 128 tiles, 2 x 2 waves of 64 x 64 in 32x32x32 MFMA blocks,
 //   register-staged loads with zero fill at the edges, LDS rows padded to
 //   80 bytes; [k][n] weights are transposed 4 x 4 bytes at a time in
 //   registers on their way into LDS.
@@ -349,7 +349,7 @@ constexpr int BM = 128, BN = 128, BK = 64;
 constexpr int kLdsRow = BK + 16;  // padded row stride in bytes
 constexpr int kThreads = 256;
 constexpr int WM = 64, WN = 64;   // wave sub-tile
-constexpr int TM = WM / 16, TN = WN / 16;
+constexpr int TM = WM / 32, TN = WN / 32;   // 32 x 32 blocks per wave sub-tile
 
 // 16 bytes of row `row` of a [rows][k] int8 matrix at column kk, zero-filled
 // outside [0, rows) x [0, k).
@@ -443,32 +443,38 @@ __global__ __launch_bounds__(kThreads) void gemm_i8_kernel(Params p) {
         }
     };
 
-    v4i acc[TM][TN];
+    v16i acc[TM][TN];
 #pragma unroll
     for (int i = 0; i < TM; i++)
 #pragma unroll
-        for (int j = 0; j < TN; j++) acc[i][j] = v4i{0, 0, 0, 0};
+        for (int j = 0; j < TN; j++) acc[i][j] = v16i{};
 
     gload(0);
     sstore();
     __syncthreads();
 
-    const int fr = lane % 16;           // fragment row / column
-    const int fk = 16 * (lane / 16);    // fragment k offset (bytes)
+    // v_mfma_i32_32x32x32_i8 (the 16x16x64 form sustains about 60% of its
+    // rate): lane l supplies row / column l % 32 and the 16 k bytes at
+    // 16 (l / 32) of each 32-byte step.  Row pitch 80 bytes: the 8 rows read
+    // together fall in distinct bank groups.
+    const int fr = lane % 32;           // fragment row / column
+    const int fk = 16 * (lane / 32);    // fragment k offset (bytes)
     for (int64_t kt = 0; kt < nk; kt++) {
         if (kt + 1 < nk) gload((kt + 1) * BK);
-        v4i a[TM], b[TN];
 #pragma unroll
-        for (int i = 0; i < TM; i++)
-            a[i] = *reinterpret_cast<const v4i *>(As + (wm * WM + i * 16 + fr) * kLdsRow + fk);
+        for (int s = 0; s < BK / 32; s++) {
+            v4i a[TM], b[TN];
 #pragma unroll
-        for (int j = 0; j < TN; j++)
-            b[j] = *reinterpret_cast<const v4i *>(Bs + (wn * WN + j * 16 + fr) * kLdsRow + fk);
-#pragma unroll
-        for (int i = 0; i < TM; i++)
+            for (int i = 0; i < TM; i++)
+                a[i] = *reinterpret_cast<const v4i *>(As + (wm * WM + i * 32 + fr) * kLdsRow + fk + 32 * s);
 #pragma unroll
             for (int j = 0; j < TN; j++)
-                acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[i], b[j], acc[i][j], 0, 0, 0);
+                b[j] = *reinterpret_cast<const v4i *>(Bs + (wn * WN + j * 32 + fr) * kLdsRow + fk + 32 * s);
+#pragma unroll
+            for (int i = 0; i < TM; i++)
+#pragma unroll
+                for (int j = 0; j < TN; j++) acc[i][j] = mfma32(a[i], b[j], acc[i][j]);
+        }
         __syncthreads();
         if (kt + 1 < nk) {
             sstore();
@@ -476,7 +482,8 @@ __global__ __launch_bounds__(kThreads) void gemm_i8_kernel(Params p) {
         }
     }
 
-    // Epilogue: lane holds column fr of each 16x16 block and rows 4*(lane/16)+r.
+    // Epilogue: lane holds column fr of each 32x32 block and rows
+    // 8 (r / 4) + 4 (lane / 32) + r % 4 of register r.
     Epilogue<EPI, OUT> ep;
     ep.init(p);
     ep.stage_rows(p, m0, BM, reinterpret_cast<float *>(As));
@@ -484,18 +491,18 @@ __global__ __launch_bounds__(kThreads) void gemm_i8_kernel(Params p) {
     float cf[TN], cb[TN];
 #pragma unroll
     for (int j = 0; j < TN; j++) {
-        cf[j] = ep.col_factor(p, n0 + wn * WN + j * 16 + fr);
-        cb[j] = ep.col_bias(p, n0 + wn * WN + j * 16 + fr);
+        cf[j] = ep.col_factor(p, n0 + wn * WN + j * 32 + fr);
+        cb[j] = ep.col_bias(p, n0 + wn * WN + j * 32 + fr);
     }
 #pragma unroll
     for (int j = 0; j < TN; j++) {
-        const int64_t col = n0 + wn * WN + j * 16 + fr;
+        const int64_t col = n0 + wn * WN + j * 32 + fr;
         if (col >= p.n) continue;
 #pragma unroll
         for (int i = 0; i < TM; i++)
 #pragma unroll
-            for (int r = 0; r < 4; r++) {
-                const int local = wm * WM + i * 16 + 4 * (lane / 16) + r;
+            for (int r = 0; r < 16; r++) {
+                const int local = wm * WM + i * 32 + 8 * (r / 4) + 4 * (lane / 32) + r % 4;
                 if (m0 + local < p.m) ep.store(p, m0 + local, col, acc[i][j][r], ep.row_factor(local), cf[j], cb[j]);
             }
     }

@@ -16,8 +16,10 @@
 //         and packed weights streamed into LDS through a ring of 128-k
 //         slices; each lane takes its weight words from LDS in the order the
 //         32x32x32 operand needs.
-// 16 < m < 256: 128 x 128 tiles, 2 x 2 waves of 64 x 64, A staged in LDS per
-//         256-k step (rows padded to 272 bytes), B loaded per wave.
+// 16 < m < 256: 128 x 128 tiles, 2 x 2 waves of 64 x 64 on 32x32x32, A
+//         staged in LDS per 256-k step (rows padded to 272 bytes), B loaded
+//         per wave straight into registers in the lane order that operand
+//         needs.
 // m <= 16: decode GEMV.  The m rows fill one 16-row MFMA block (rows past m
 //         repeat row 0 and are never stored); each workgroup owns NBLK
 //         column blocks and its waves split k, each wave keeping two
@@ -31,6 +33,8 @@
 namespace ql {
 
 namespace {
+
+typedef int v16i __attribute__((ext_vector_type(16)));
 
 __device__ __forceinline__ v4i unpack_tern(uint32_t w) {
     return v4i{(int)(w & 0x03030303u), (int)((w >> 2) & 0x03030303u), (int)((w >> 4) & 0x03030303u),
@@ -74,6 +78,11 @@ constexpr int GBM = 128, GBN = 128, GBK = 256;
 constexpr int kGRow = GBK + 16;  // LDS row stride (bytes)
 constexpr int kGThreads = 256;
 
+// Wave (wm, wn) owns 64 x 64 as 2 x 2 blocks of v_mfma_i32_32x32x32_i8.
+// Step s = 4q + t of a 256-k block gives lane half h = lane / 32 the k group
+// g = 2q + h and word t: A chunk 4g + t of its row, and for B the 16 bytes
+// each lane loads from HBM are those of packed lane (column % 16) + 16 g of
+// the column's fragment block, whose word t is the matching operand.
 template <int OUT>
 __global__ __launch_bounds__(kGThreads) void w2a8_gemm_kernel(const int8_t *__restrict__ xq,
                                                               const float *__restrict__ pts,
@@ -86,12 +95,13 @@ __global__ __launch_bounds__(kGThreads) void w2a8_gemm_kernel(const int8_t *__re
     __shared__ __attribute__((aligned(16))) int8_t As[GBM * kGRow];
     const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
     const int wm = wave / 2, wn = wave % 2;
+    const int h = lane / 32, fr = lane % 32;
     const int64_t m0 = (int64_t)blockIdx.y * GBM;
     const int64_t nbase = (int64_t)blockIdx.x * (GBN / 16) + wn * 4;  // first column block of the wave
     const int64_t nblocks = n / 16, kblocks = k / GBK;
 
     uint4 ra[8];
-    uint4 rb[4];
+    uint4 rb[2][2];   // [32-column block j][k-group pair q]
     auto gload = [&](int64_t kb) {
 #pragma unroll
         for (int c = 0; c < 8; c++) {
@@ -102,11 +112,13 @@ __global__ __launch_bounds__(kGThreads) void w2a8_gemm_kernel(const int8_t *__re
                            : make_uint4(0, 0, 0, 0);
         }
 #pragma unroll
-        for (int j = 0; j < 4; j++) {
-            const int64_t nb = nbase + j;
-            rb[j] = nb < nblocks
-                        ? *reinterpret_cast<const uint4 *>(packed + (nb * kblocks + kb) * 256 + 4 * lane)
-                        : make_uint4(0x55555555u, 0x55555555u, 0x55555555u, 0x55555555u);
+        for (int j = 0; j < 2; j++) {
+            const int64_t nb = nbase + 2 * j + fr / 16;
+#pragma unroll
+            for (int q = 0; q < 2; q++)
+                rb[j][q] = nb < nblocks ? *reinterpret_cast<const uint4 *>(packed + (nb * kblocks + kb) * 256 +
+                                                                           4 * (fr % 16 + 16 * (2 * q + h)))
+                                        : make_uint4(0x55555555u, 0x55555555u, 0x55555555u, 0x55555555u);
         }
     };
     auto sstore = [&]() {
@@ -118,35 +130,39 @@ __global__ __launch_bounds__(kGThreads) void w2a8_gemm_kernel(const int8_t *__re
         }
     };
 
-    v4i acc[4][4];
+    v16i acc[2][2];
 #pragma unroll
-    for (int i = 0; i < 4; i++)
+    for (int i = 0; i < 2; i++)
 #pragma unroll
-        for (int j = 0; j < 4; j++) acc[i][j] = v4i{0, 0, 0, 0};
+        for (int j = 0; j < 2; j++) acc[i][j] = v16i{};
 
     gload(0);
     sstore();
     __syncthreads();
-    const int fr = lane % 16, fk = 64 * (lane / 16);
     for (int64_t kb = 0; kb < kblocks; kb++) {
-        uint4 cb[4];
+        uint4 cb[2][2];
 #pragma unroll
-        for (int j = 0; j < 4; j++) cb[j] = rb[j];
+        for (int j = 0; j < 2; j++)
+#pragma unroll
+            for (int q = 0; q < 2; q++) cb[j][q] = rb[j][q];
         if (kb + 1 < kblocks) gload(kb + 1);
 #pragma unroll
-        for (int t = 0; t < 4; t++) {
-            v4i a[4];
+        for (int q = 0; q < 2; q++)
 #pragma unroll
-            for (int i = 0; i < 4; i++)
-                a[i] = *reinterpret_cast<const v4i *>(As + (wm * 64 + i * 16 + fr) * kGRow + fk + 16 * t);
+            for (int t = 0; t < 4; t++) {
+                v4i a[2];
 #pragma unroll
-            for (int j = 0; j < 4; j++) {
-                const v4i b = unpack_tern(word_of(cb[j], t));
+                for (int i = 0; i < 2; i++)
+                    a[i] = *reinterpret_cast<const v4i *>(As + (wm * 64 + i * 32 + fr) * kGRow +
+                                                          16 * (4 * (2 * q + h) + t));
 #pragma unroll
-                for (int i = 0; i < 4; i++)
-                    acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[i], b, acc[i][j], 0, 0, 0);
+                for (int j = 0; j < 2; j++) {
+                    const v4i b = unpack_tern(word_of(cb[j][q], t));
+#pragma unroll
+                    for (int i = 0; i < 2; i++)
+                        acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[i], b, acc[i][j], 0, 0, 0);
+                }
             }
-        }
         __syncthreads();
         if (kb + 1 < kblocks) {
             sstore();
@@ -159,17 +175,18 @@ __global__ __launch_bounds__(kGThreads) void w2a8_gemm_kernel(const int8_t *__re
     stage_rows<OUT>(pts, rowsum, m, m0, GBM, rs_lds, pts_lds);
     __syncthreads();
     const float g = OUT == OUT_I32 ? 0.0f : (float)gamma[0];  // gamma may be NULL for int32 output
+    // Lane l holds column l % 32 of each 32 x 32 block and rows
+    // 8 (r / 4) + 4 (l / 32) + r % 4 of register r.
 #pragma unroll
-    for (int j = 0; j < 4; j++) {
-        const int64_t nb = nbase + j;
-        if (nb >= nblocks) continue;
-        const int64_t col = nb * 16 + fr;
+    for (int j = 0; j < 2; j++) {
+        const int64_t col = (nbase + 2 * j) * 16 + fr;
+        if (col >= n) continue;
         const float colb = (OUT != OUT_I32 && bias) ? bias[col] : 0.0f;
 #pragma unroll
-        for (int i = 0; i < 4; i++)
+        for (int i = 0; i < 2; i++)
 #pragma unroll
-            for (int r = 0; r < 4; r++) {
-                const int local = wm * 64 + i * 16 + 4 * (lane / 16) + r;
+            for (int r = 0; r < 16; r++) {
+                const int local = wm * 64 + i * 32 + 8 * (r / 4) + 4 * h + r % 4;
                 if (m0 + local < m)
                     epilogue_store<OUT>(out, (m0 + local) * n + col, acc[i][j][r], rs_lds[local],
                                         OUT == OUT_I32 ? 0.0f : pts_lds[local], g, bias, colb);
@@ -207,7 +224,6 @@ constexpr int kXStage = kXASlice + kXBSlice;
 constexpr int kXLoads = kXASlice / 1024 / (kXThreads / kWave);  // 1 KB A loads per wave per slice
 static_assert(kXBSlice == 1024 * (kXThreads / kWave), "one 1 KB weight load per wave per slice");
 
-typedef int v16i __attribute__((ext_vector_type(16)));
 
 // Bytes of LDS the epilogue of a 256 x 128 tile uses: the rows' code sums
 // and scales, then a padded 128 x 64 output tile per wave.
