@@ -62,6 +62,12 @@ W8A8_SHAPES = [
     (520, 777, 192, True),     # ragged m and n
     (1024, 768, 1024, True),
     (700, 600, 120, True),     # k % 64 != 0: general kernel at large m, n
+    (1, 400, 512, True),       # decode kernel from here on (m <= 16, [n][k], k % 64 == 0)
+    (5, 270, 320, True),       # k blocks cut short, n % 16 != 0
+    (16, 1000, 768, True),
+    (4, 6400, 256, True),      # 2 column blocks per workgroup
+    (2, 13000, 128, True),     # 4 column blocks per workgroup, n % 16 != 0
+    (3, 28672, 64, True),      # 7 column blocks per workgroup, a single k step
 ]
 
 
@@ -96,6 +102,21 @@ def test_w8a8_max_k_extremes():
     assert_equal(o, acc, "w8a8 max-k accumulator")
 
 
+def test_w8a8_decode_max_k():
+    """The decode kernel at k = 131008 (the largest multiple of 64 the ABI allows), operands at -128."""
+    m, n, k = 3, 5, 131008
+    x = torch.full((m, k), -128, dtype=torch.int8)
+    w = torch.full((n, k), -128, dtype=torch.int8)
+    w[1, ::2] = 127
+    x[2, 1::3] = 5
+    acc = oracle.gemm_i8(x.numpy(), w.numpy(), True)
+    assert int(acc[0, 0]) == 128 * 128 * k
+    o = poison((m, n), torch.int32)
+    ql.qlinear_gemm_w8a8(_cuda(x), _cuda(w), ql.QL_W_NK, None, None, out_dtype=torch.int32, out=o)
+    _sync()
+    assert_equal(o, acc, "w8a8 decode max-k accumulator")
+
+
 def test_w8a8_deterministic():
     d = synthetic.w8a8(200, 300, 512, True, seed=5)
     args = [_cuda(d[key]) for key in ("x", "w")]
@@ -113,6 +134,7 @@ def test_w8a8_deterministic():
     (5, 77, 45, 77, True, True),        # byte loads
     (2, 33, 50, 77, False, False),
     (2, 1, 1, 1, False, True),
+    (3, 16, 270, 320, True, True),      # decode kernel
 ])
 def test_w8a8_batched_parity(batch, m, n, k, nk, per_batch_deq):
     ds = [synthetic.w8a8(m, n, k, nk, seed=1900 + 10 * b + m + n + k) for b in range(batch)]
@@ -480,7 +502,7 @@ def test_bias_with_int32_output_is_rejected():
 # A4W4
 # ---------------------------------------------------------------------------
 @pytest.mark.parametrize("m,n,k", [(33, 20, 130), (256, 256, 512), (129, 65, 1000), (1, 1, 1), (600, 520, 640),
-                                   (1024, 1024, 256)])
+                                   (1024, 1024, 256), (16, 300, 512)])
 @pytest.mark.parametrize("scale_mul", [1.0, 0.25])
 def test_a4w4_parity(m, n, k, scale_mul):
     d = synthetic.a4w4(m, n, k, seed=800 + m + n + k)
