@@ -519,9 +519,9 @@ __global__ __launch_bounds__(kThreads) void gemm_i8_kernel(Params p) {
 // The m token rows fill one 16-row block of v_mfma_i32_16x16x64_i8 (rows past
 // m repeat row 0 and are never stored; the kernel is bound by the weight
 // bytes, so the idle rows cost nothing).  A workgroup owns NBLK blocks of 16
-// output columns; its kGvWaves waves take turns over k blocks of 64 SPS
-// bytes, each wave holding two register stages so the next block's weights
-// are in flight while the current one is multiplied.  Lane l supplies row /
+// output columns (one, as launched); its kGvWaves waves take turns over k
+// blocks of 64 SPS bytes, each wave holding two register stages so the next
+// block's weights are in flight while the current one is multiplied.  Lane l supplies row /
 // column l % 16 and the 16 bytes at k 64 t + 16 (l / 16) of step t, read
 // straight from the row-major operands (weights with non-temporal loads:
 // each byte is used once).  The waves' int32 partials are summed in LDS in a
@@ -634,16 +634,17 @@ hipError_t launch_gemv_t(const Params &p, int64_t batch, hipStream_t st) {
     return hipGetLastError();
 }
 
-// Column blocks per workgroup: enough workgroups to cover the chip (256
-// CUs) once the columns allow, and at most 8 x 16 bytes of weights in
-// flight per lane and register stage.
+// One column block per workgroup; 256-k register stages while the columns
+// give at most about 1.5 workgroups per CU, 128-k stages above.  Measured on
+// MI355X with the weights streamed from HBM (HIP-graph replays rotating
+// copies), against 2, 4 and 7 column blocks per workgroup and 64-k stages:
+// best or within 6% of best at n x k = 4096 x 4096, 11008 x 4096,
+// 4096 x 11008 and 28672 x 8192 (m = 1, 4, 16).
 template <int EPI, int OUT>
 hipError_t launch_gemv_n(const Params &p, int64_t batch, hipStream_t st) {
     const int64_t nblocks = (p.n + 15) / 16;
     if (nblocks <= 384) return launch_gemv_t<1, 4, EPI, OUT>(p, batch, st);
-    if (nblocks <= 768) return launch_gemv_t<2, 4, EPI, OUT>(p, batch, st);
-    if (nblocks <= 1536) return launch_gemv_t<4, 2, EPI, OUT>(p, batch, st);
-    return launch_gemv_t<7, 1, EPI, OUT>(p, batch, st);
+    return launch_gemv_t<1, 2, EPI, OUT>(p, batch, st);
 }
 
 template <int EPI>

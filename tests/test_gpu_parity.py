@@ -65,9 +65,9 @@ W8A8_SHAPES = [
     (1, 400, 512, True),       # decode kernel from here on (m <= 16, [n][k], k % 64 == 0)
     (5, 270, 320, True),       # k blocks cut short, n % 16 != 0
     (16, 1000, 768, True),
-    (4, 6400, 256, True),      # 2 column blocks per workgroup
-    (2, 13000, 128, True),     # 4 column blocks per workgroup, n % 16 != 0
-    (3, 28672, 64, True),      # 7 column blocks per workgroup, a single k step
+    (4, 6400, 256, True),      # 128-k register stages (more than 384 column blocks)
+    (2, 13000, 128, True),     # n % 16 != 0 with 128-k stages
+    (3, 28672, 64, True),      # a single k step
 ]
 
 
