@@ -34,6 +34,8 @@
 #include "ql_launch.hpp"
 #include "gemm_ring.hpp"
 
+#include <type_traits>
+
 namespace ql {
 
 namespace {
@@ -351,34 +353,54 @@ hipError_t launch_f6(const Params &p, hipStream_t st) {
 // General kernel
 // ---------------------------------------------------------------------------
 constexpr int BM = 128, BN = 128, BK = 64;
-constexpr int kLdsRow = BK + 16;  // padded row stride in bytes
 constexpr int kThreads = 256;
 constexpr int WM = 64, WN = 64;   // wave sub-tile
 constexpr int TM = WM / 32, TN = WN / 32;   // 32 x 32 blocks per wave sub-tile
 
-// 16 bytes of row `row` of a [rows][k] int8 matrix at column kk, zero-filled
-// outside [0, rows) x [0, k).
-template <bool VEC>
+// Operand loads of the general kernel.  Rows past the matrix (m for x, n
+// for w) are read clamped to its last row: their products only reach output
+// rows or columns that are never stored.  Only k past the end must add
+// nothing, so only x's chunks in the last, partial k-step are zeroed (MASK);
+// w's bytes beside them may be any finite values.  With VEC (k % 16 == 0,
+// and n % 4 == 0 for [k][n] weights) every load is one unconditional vector
+// load from a clamped in-bounds address, with no branch around it, so the
+// loads stay in flight across the products that follow.  Otherwise byte
+// loads with zero fill.
+
+// 16 bytes of row `row` of a [rows][k] int8 matrix at column kk.
+template <bool VEC, bool MASK>
 __device__ __forceinline__ uint4 load_row16(const int8_t *base, int64_t rows, int64_t k, int64_t row,
                                             int64_t kk) {
-    if (row >= rows) return make_uint4(0, 0, 0, 0);
-    const int8_t *p = base + row * k + kk;
-    if (VEC && kk + 16 <= k) return *reinterpret_cast<const uint4 *>(p);
-    uint32_t v[4] = {0, 0, 0, 0};
-    for (int j = 0; j < 16; j++)
-        if (kk + j < k) v[j / 4] |= (uint32_t)(uint8_t)p[j] << (8 * (j % 4));
-    return make_uint4(v[0], v[1], v[2], v[3]);
+    if constexpr (VEC) {
+        const int64_t r = row < rows ? row : rows - 1;
+        if constexpr (!MASK) {
+            return *reinterpret_cast<const uint4 *>(base + r * k + kk);
+        } else {
+            const uint4 v = *reinterpret_cast<const uint4 *>(base + r * k + (kk < k ? kk : k - 16));
+            return kk < k ? v : make_uint4(0, 0, 0, 0);
+        }
+    } else {
+        if (row >= rows) return make_uint4(0, 0, 0, 0);
+        const int8_t *p = base + row * k + kk;
+        uint32_t v[4] = {0, 0, 0, 0};
+        for (int j = 0; j < 16; j++)
+            if (kk + j < k) v[j / 4] |= (uint32_t)(uint8_t)p[j] << (8 * (j % 4));
+        return make_uint4(v[0], v[1], v[2], v[3]);
+    }
 }
 
-// 4 k-rows x 4 n-columns of a [k][n] int8 matrix, returned as 4 words, one
-// per column, each holding the 4 consecutive k of that column.
+// 4 k-rows x 4 n-columns of a [k][n] int8 matrix as 4 row words (byte j of
+// word i: k-row kk + i, column nn + j).
+template <bool VEC, bool MASK>
 __device__ __forceinline__ void load_kn_4x4(const int8_t *w, int64_t n, int64_t k, int64_t kk,
-                                            int64_t nn, uint32_t col[4]) {
-    uint32_t rowv[4];
-    const bool full = (nn + 4 <= n) && (kk + 4 <= k) && ((n & 3) == 0);
-    if (full) {
+                                            int64_t nn, uint32_t rowv[4]) {
+    if constexpr (VEC) {
+        const int64_t nc = nn < n ? nn : n - 4;
 #pragma unroll
-        for (int i = 0; i < 4; i++) rowv[i] = *reinterpret_cast<const uint32_t *>(w + (kk + i) * n + nn);
+        for (int i = 0; i < 4; i++) {
+            const int64_t kr = MASK && kk + i >= k ? k - 1 : kk + i;
+            rowv[i] = *reinterpret_cast<const uint32_t *>(w + kr * n + nc);
+        }
     } else {
 #pragma unroll
         for (int i = 0; i < 4; i++) {
@@ -388,19 +410,28 @@ __device__ __forceinline__ void load_kn_4x4(const int8_t *w, int64_t n, int64_t 
             rowv[i] = r;
         }
     }
-#pragma unroll
-    for (int j = 0; j < 4; j++) {
-        uint32_t c = 0;
-#pragma unroll
-        for (int i = 0; i < 4; i++) c |= ((rowv[i] >> (8 * j)) & 0xffu) << (8 * i);
-        col[j] = c;
-    }
 }
 
-template <bool NK, bool VEC, int EPI, int OUT>
+// The 4 x 4 byte transpose of load_kn_4x4's row words: word j holds the 4
+// consecutive k of column nn + j.  Done when the words are stored, so the
+// loads stay in flight until then.
+__device__ __forceinline__ uint32_t kn_column(const uint32_t rowv[4], int j) {
+    uint32_t c = 0;
+#pragma unroll
+    for (int i = 0; i < 4; i++) c |= ((rowv[i] >> (8 * j)) & 0xffu) << (8 * i);
+    return c;
+}
+
+// KALL = 1: one 64-byte k-step staged at a time, the next step's loads in
+// flight while the current one is multiplied.  KALL > 1 (k <= 64 KALL): every
+// k-step's loads are issued at once and the whole k range is staged in LDS
+// before any product, so a short-k product pays one memory latency instead
+// of one per step.
+template <bool NK, bool VEC, int EPI, int OUT, int KALL>
 __global__ __launch_bounds__(kThreads) void gemm_i8_kernel(Params p) {
-    __shared__ __attribute__((aligned(16))) int8_t As[BM * kLdsRow];
-    __shared__ __attribute__((aligned(16))) int8_t Bs[BN * kLdsRow];
+    constexpr int PITCH = KALL * BK + 16;   // LDS row stride in bytes
+    __shared__ __attribute__((aligned(16))) int8_t As[BM * PITCH];
+    __shared__ __attribute__((aligned(16))) int8_t Bs[BN * PITCH];
 
     to_batch(p);
     const int tid = threadIdx.x;
@@ -411,39 +442,48 @@ __global__ __launch_bounds__(kThreads) void gemm_i8_kernel(Params p) {
     const int64_t n0 = (int64_t)blockIdx.x * BN;
     const int64_t nk = (p.k + BK - 1) / BK;
 
-    // Register staging of one k-step: A as 2 x 16 bytes, B likewise ([n][k])
-    // or two 4x4 transposed blocks ([k][n]).
-    uint4 ra[2];
-    uint4 rb[2];
-    uint32_t rbt[2][4];
+    // Register staging of k-step slots: A as 2 x 16 bytes, B likewise
+    // ([n][k]) or two 4 x 4 byte blocks as row words ([k][n]).
+    uint4 ra[KALL][2];
+    uint4 rb[KALL][2];
+    uint32_t rbt[KALL][2][4];
 
-    auto gload = [&](int64_t k0) {
+    // `mask` (std::true_type / false_type): the k-step runs past k
+    auto gload = [&](int slot, int64_t k0, auto mask) {
+        constexpr bool MASK = decltype(mask)::value;
 #pragma unroll
         for (int c = 0; c < 2; c++) {
             const int chunk = tid + c * kThreads;
             const int row = chunk / 4, c16 = chunk % 4;
-            ra[c] = load_row16<VEC>(p.x, p.m, p.k, m0 + row, k0 + 16 * c16);
+            ra[slot][c] = load_row16<VEC, MASK>(p.x, p.m, p.k, m0 + row, k0 + 16 * c16);
             if (NK) {
-                rb[c] = load_row16<VEC>(p.w, p.n, p.k, n0 + row, k0 + 16 * c16);
+                rb[slot][c] = load_row16<VEC, MASK>(p.w, p.n, p.k, n0 + row, k0 + 16 * c16);
             } else {
                 const int n4 = chunk % 32, k4 = chunk / 32;
-                load_kn_4x4(p.w, p.n, p.k, k0 + 4 * k4, n0 + 4 * n4, rbt[c]);
+                load_kn_4x4<VEC, MASK>(p.w, p.n, p.k, k0 + 4 * k4, n0 + 4 * n4, rbt[slot][c]);
             }
         }
     };
-    auto sstore = [&]() {
+    // the branch is uniform (scalar): either path keeps its loads in flight
+    auto gload_step = [&](int slot, int64_t kt) {
+        if ((kt + 1) * BK > p.k) gload(slot, kt * BK, std::true_type{});
+        else gload(slot, kt * BK, std::false_type{});
+    };
+    // slot s goes to LDS columns [64 s, 64 s + 64) of each row
+    auto sstore = [&](int slot, int col0) {
 #pragma unroll
         for (int c = 0; c < 2; c++) {
             const int chunk = tid + c * kThreads;
             const int row = chunk / 4, c16 = chunk % 4;
-            *reinterpret_cast<uint4 *>(As + row * kLdsRow + 16 * c16) = ra[c];
+            *reinterpret_cast<uint4 *>(As + row * PITCH + col0 + 16 * c16) = ra[slot][c];
             if (NK) {
-                *reinterpret_cast<uint4 *>(Bs + row * kLdsRow + 16 * c16) = rb[c];
+                *reinterpret_cast<uint4 *>(Bs + row * PITCH + col0 + 16 * c16) = rb[slot][c];
             } else {
                 const int n4 = chunk % 32, k4 = chunk / 32;
 #pragma unroll
                 for (int j = 0; j < 4; j++)
-                    *reinterpret_cast<uint32_t *>(Bs + (4 * n4 + j) * kLdsRow + 4 * k4) = rbt[c][j];
+                    *reinterpret_cast<uint32_t *>(Bs + (4 * n4 + j) * PITCH + col0 + 4 * k4) =
+                        kn_column(rbt[slot][c], j);
             }
         }
     };
@@ -454,37 +494,54 @@ __global__ __launch_bounds__(kThreads) void gemm_i8_kernel(Params p) {
 #pragma unroll
         for (int j = 0; j < TN; j++) acc[i][j] = v16i{};
 
-    gload(0);
-    sstore();
-    __syncthreads();
-
     // v_mfma_i32_32x32x32_i8 (the 16x16x64 form sustains about 60% of its
     // rate): lane l supplies row / column l % 32 and the 16 k bytes at
-    // 16 (l / 32) of each 32-byte step.  Row pitch 80 bytes: the 8 rows read
-    // together fall in distinct bank groups.
+    // 16 (l / 32) of each 32-byte step.  Row pitch 16 mod 64 bytes: the 8
+    // rows read together fall in distinct bank groups.
     const int fr = lane % 32;           // fragment row / column
     const int fk = 16 * (lane / 32);    // fragment k offset (bytes)
-    for (int64_t kt = 0; kt < nk; kt++) {
-        if (kt + 1 < nk) gload((kt + 1) * BK);
+    auto compute = [&](int col0) {
 #pragma unroll
         for (int s = 0; s < BK / 32; s++) {
             v4i a[TM], b[TN];
 #pragma unroll
             for (int i = 0; i < TM; i++)
-                a[i] = *reinterpret_cast<const v4i *>(As + (wm * WM + i * 32 + fr) * kLdsRow + fk + 32 * s);
+                a[i] = *reinterpret_cast<const v4i *>(As + (wm * WM + i * 32 + fr) * PITCH + col0 + fk + 32 * s);
 #pragma unroll
             for (int j = 0; j < TN; j++)
-                b[j] = *reinterpret_cast<const v4i *>(Bs + (wn * WN + j * 32 + fr) * kLdsRow + fk + 32 * s);
+                b[j] = *reinterpret_cast<const v4i *>(Bs + (wn * WN + j * 32 + fr) * PITCH + col0 + fk + 32 * s);
 #pragma unroll
             for (int i = 0; i < TM; i++)
 #pragma unroll
                 for (int j = 0; j < TN; j++) acc[i][j] = mfma32(a[i], b[j], acc[i][j]);
         }
+    };
+
+    if constexpr (KALL == 1) {
+        gload_step(0, 0);
+        sstore(0, 0);
         __syncthreads();
-        if (kt + 1 < nk) {
-            sstore();
+        for (int64_t kt = 0; kt < nk; kt++) {
+            if (kt + 1 < nk) gload_step(0, kt + 1);
+            compute(0);
             __syncthreads();
+            if (kt + 1 < nk) {
+                sstore(0, 0);
+                __syncthreads();
+            }
         }
+    } else {
+#pragma unroll
+        for (int s = 0; s < KALL; s++)
+            if (s < nk) gload_step(s, s);
+#pragma unroll
+        for (int s = 0; s < KALL; s++)
+            if (s < nk) sstore(s, s * BK);
+        __syncthreads();
+#pragma unroll
+        for (int s = 0; s < KALL; s++)
+            if (s < nk) compute(s * BK);
+        __syncthreads();
     }
 
     // Epilogue: lane holds column fr of each 32x32 block and rows
@@ -656,10 +713,15 @@ hipError_t launch_gemv_out(int out_kind, const Params &p, int64_t batch, hipStre
     }
 }
 
+constexpr int kShortSteps = 4;   // k <= 256: the whole k range staged at once
+
 template <bool NK, bool VEC, int EPI, int OUT>
 hipError_t launch_t(const Params &p, int64_t batch, hipStream_t st) {
     dim3 grid((unsigned)((p.n + BN - 1) / BN), (unsigned)((p.m + BM - 1) / BM), (unsigned)batch);
-    hipLaunchKernelGGL((gemm_i8_kernel<NK, VEC, EPI, OUT>), grid, dim3(kThreads), 0, st, p);
+    if (p.k <= (int64_t)kShortSteps * BK)
+        hipLaunchKernelGGL((gemm_i8_kernel<NK, VEC, EPI, OUT, kShortSteps>), grid, dim3(kThreads), 0, st, p);
+    else
+        hipLaunchKernelGGL((gemm_i8_kernel<NK, VEC, EPI, OUT, 1>), grid, dim3(kThreads), 0, st, p);
     return hipGetLastError();
 }
 
@@ -732,7 +794,8 @@ hipError_t launch_gemm_i8(const GemmI8Args &a, hipStream_t st) {
         return a.epi == EPI_ROWCOL ? launch_big_out<EPI_ROWCOL>(a.out_kind, p, batch, st)
                                    : launch_big_out<EPI_SCALARS>(a.out_kind, p, batch, st);
     if (a.m > (int64_t)BM * 65535) return hipErrorInvalidValue;
-    const bool vec = (a.k % 16) == 0;
+    // whole 16-byte rows of x and w ([n][k]), whole 4-column words of w ([k][n])
+    const bool vec = (a.k % 16) == 0 && (a.w_nk || (a.n % 4) == 0);
     if (a.w_nk)
         return vec ? launch_epi<true, true>(a.epi, a.out_kind, p, batch, st)
                    : launch_epi<true, false>(a.epi, a.out_kind, p, batch, st);
