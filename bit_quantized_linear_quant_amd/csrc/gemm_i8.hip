@@ -20,10 +20,10 @@
 //   clamped and never stored.  16-bit outputs leave through a padded LDS
 //   tile as whole row segments.
 //
-// gemv_i8_kernel -- decode shapes: m <= 16 with [n][k] weights and
-//   k % 64 == 0.  The token rows fill one 16-row matrix-core block; waves
-//   split k over a few 16-column blocks per workgroup, reading the weights
-//   once with streaming loads, and sum their partials in LDS.
+// gemv_i8_kernel -- decode shapes: m <= 64 with [n][k] weights and
+//   k % 64 == 0.  The token rows fill up to four 16-row matrix-core blocks;
+//   waves split k over a few 16-column blocks per workgroup, reading the
+//   weights once with streaming loads, and sum their partials in LDS.
 //
 // gemm_i8_kernel -- everything else (any m, n, k >= 1, weights [k][n] or
 //   [n][k]): 128 x 128 tiles, 2 x 2 waves of 64 x 64 in 32x32x32 MFMA blocks,
@@ -571,36 +571,37 @@ __global__ __launch_bounds__(kThreads) void gemm_i8_kernel(Params p) {
 }
 
 // ---------------------------------------------------------------------------
-// Decode kernel: m <= 16, [n][k] weights, k % 64 == 0
+// Decode kernel: m <= 64, [n][k] weights, k % 64 == 0
 // ---------------------------------------------------------------------------
-// The m token rows fill one 16-row block of v_mfma_i32_16x16x64_i8 (rows past
+// The m token rows fill RB 16-row blocks of v_mfma_i32_16x16x64_i8 (rows past
 // m repeat row 0 and are never stored; the kernel is bound by the weight
 // bytes, so the idle rows cost nothing).  A workgroup owns NBLK blocks of 16
-// output columns (one, as launched); its kGvWaves waves take turns over k
-// blocks of 64 SPS bytes, each wave holding two register stages so the next
-// block's weights are in flight while the current one is multiplied.  Lane l supplies row /
+// output columns; its kGvWaves waves take turns over k blocks of 64 SPS
+// bytes, each wave holding two register stages so the next block's weights
+// are in flight while the current one is multiplied.  Lane l supplies row /
 // column l % 16 and the 16 bytes at k 64 t + 16 (l / 16) of step t, read
 // straight from the row-major operands (weights with non-temporal loads:
 // each byte is used once).  The waves' int32 partials are summed in LDS in a
 // fixed order: exact, hence deterministic.
 constexpr int kGvWaves = 8;
 
-template <int NBLK, int SPS>
+template <int NBLK, int SPS, int RB>
 struct GemvStage {
     v4i w[SPS][NBLK];
-    v4i a[SPS];
+    v4i a[SPS][RB];
 };
 
 // All loads of k block kb from clamped, in-bounds addresses; a step past
 // the end is masked at compute time.
-template <int NBLK, int SPS>
-__device__ __forceinline__ void gemv_load(GemvStage<NBLK, SPS> &st, const int8_t *xrow,
+template <int NBLK, int SPS, int RB>
+__device__ __forceinline__ void gemv_load(GemvStage<NBLK, SPS, RB> &st, const int8_t *const (&xrow)[RB],
                                           const int8_t *const (&wrow)[NBLK], int64_t kb, int64_t nsteps) {
 #pragma unroll
     for (int t = 0; t < SPS; t++) {
         const int64_t s = kb * SPS + t;
         const int64_t off = (s < nsteps ? s : nsteps - 1) * 64;
-        st.a[t] = *reinterpret_cast<const v4i *>(xrow + off);
+#pragma unroll
+        for (int b = 0; b < RB; b++) st.a[t][b] = *reinterpret_cast<const v4i *>(xrow[b] + off);
 #pragma unroll
         for (int j = 0; j < NBLK; j++) {
             const uint4 v = load16_stream(wrow[j] + off);
@@ -609,27 +610,37 @@ __device__ __forceinline__ void gemv_load(GemvStage<NBLK, SPS> &st, const int8_t
     }
 }
 
-template <int NBLK, int SPS>
-__device__ __forceinline__ void gemv_compute(const GemvStage<NBLK, SPS> &st, v4i (&acc)[NBLK], int64_t kb,
+template <int NBLK, int SPS, int RB>
+__device__ __forceinline__ void gemv_compute(const GemvStage<NBLK, SPS, RB> &st, v4i (&acc)[RB][NBLK], int64_t kb,
                                              int64_t nsteps) {
 #pragma unroll
     for (int t = 0; t < SPS; t++) {
         // a zero activation fragment removes a step past the end exactly
-        const v4i a = kb * SPS + t < nsteps ? st.a[t] : v4i{0, 0, 0, 0};
+        const bool ok = kb * SPS + t < nsteps;
 #pragma unroll
-        for (int j = 0; j < NBLK; j++) acc[j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, st.w[t][j], acc[j], 0, 0, 0);
+        for (int b = 0; b < RB; b++) {
+            const v4i a = ok ? st.a[t][b] : v4i{0, 0, 0, 0};
+#pragma unroll
+            for (int j = 0; j < NBLK; j++)
+                acc[b][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, st.w[t][j], acc[b][j], 0, 0, 0);
+        }
     }
 }
 
-template <int NBLK, int SPS, int EPI, int OUT>
+template <int NBLK, int SPS, int RB, int EPI, int OUT>
 __global__ __launch_bounds__(kGvWaves * 64) void gemv_i8_kernel(Params p) {
-    __shared__ v4i red[kGvWaves][NBLK][kWave];
+    __shared__ v4i red[kGvWaves][RB * NBLK][kWave];
     to_batch(p);
     const int lane = threadIdx.x % kWave, wave = wave_id();
     const int fr = lane % 16;
     const int64_t nb0 = (int64_t)blockIdx.x * NBLK;
     const int64_t nsteps = p.k / 64, kblocks = (nsteps + SPS - 1) / SPS;
-    const int8_t *xrow = p.x + (int64_t)(fr < p.m ? fr : 0) * p.k + 16 * (lane / 16);
+    const int8_t *xrow[RB];
+#pragma unroll
+    for (int b = 0; b < RB; b++) {
+        const int64_t row = 16 * b + fr;
+        xrow[b] = p.x + (row < p.m ? row : 0) * p.k + 16 * (lane / 16);
+    }
     // columns past n repeat the last one; they are never stored
     const int8_t *wrow[NBLK];
 #pragma unroll
@@ -637,79 +648,111 @@ __global__ __launch_bounds__(kGvWaves * 64) void gemv_i8_kernel(Params p) {
         const int64_t col = (nb0 + j) * 16 + fr;
         wrow[j] = p.w + (col < p.n ? col : p.n - 1) * p.k + 16 * (lane / 16);
     }
-    // row factors of this lane's output rows 4 (lane / 16) + r, loaded now so
-    // their latency hides behind the k loop
+    // row factors of this lane's output rows 16 b + 4 (lane / 16) + r, loaded
+    // now so their latency hides behind the k loop
     Epilogue<EPI, OUT> ep;
     ep.init(p);
-    float rf[4];
+    float rf[RB][4];
 #pragma unroll
-    for (int r = 0; r < 4; r++) {
-        const int64_t row = 4 * (lane / 16) + r < p.m ? 4 * (lane / 16) + r : p.m - 1;
-        rf[r] = OUT == OUT_I32 ? 0.0f : (EPI == EPI_ROWCOL ? p.pts[row] : ep.sa);
-    }
+    for (int b = 0; b < RB; b++)
+#pragma unroll
+        for (int r = 0; r < 4; r++) {
+            const int64_t row = 16 * b + 4 * (lane / 16) + r < p.m ? 16 * b + 4 * (lane / 16) + r : p.m - 1;
+            rf[b][r] = OUT == OUT_I32 ? 0.0f : (EPI == EPI_ROWCOL ? p.pts[row] : ep.sa);
+        }
 
-    v4i acc[NBLK];
+    v4i acc[RB][NBLK];
 #pragma unroll
-    for (int j = 0; j < NBLK; j++) acc[j] = v4i{0, 0, 0, 0};
-    GemvStage<NBLK, SPS> s0, s1;
+    for (int b = 0; b < RB; b++)
+#pragma unroll
+        for (int j = 0; j < NBLK; j++) acc[b][j] = v4i{0, 0, 0, 0};
+    GemvStage<NBLK, SPS, RB> s0, s1;
     int64_t kb = wave;
-    if (kb < kblocks) gemv_load<NBLK, SPS>(s0, xrow, wrow, kb, nsteps);
+    if (kb < kblocks) gemv_load<NBLK, SPS, RB>(s0, xrow, wrow, kb, nsteps);
     while (kb < kblocks) {
         const int64_t kb1 = kb + kGvWaves;
-        if (kb1 < kblocks) gemv_load<NBLK, SPS>(s1, xrow, wrow, kb1, nsteps);
-        gemv_compute<NBLK, SPS>(s0, acc, kb, nsteps);
+        if (kb1 < kblocks) gemv_load<NBLK, SPS, RB>(s1, xrow, wrow, kb1, nsteps);
+        gemv_compute<NBLK, SPS, RB>(s0, acc, kb, nsteps);
         if (kb1 >= kblocks) break;
         const int64_t kb2 = kb1 + kGvWaves;
-        if (kb2 < kblocks) gemv_load<NBLK, SPS>(s0, xrow, wrow, kb2, nsteps);
-        gemv_compute<NBLK, SPS>(s1, acc, kb1, nsteps);
+        if (kb2 < kblocks) gemv_load<NBLK, SPS, RB>(s0, xrow, wrow, kb2, nsteps);
+        gemv_compute<NBLK, SPS, RB>(s1, acc, kb1, nsteps);
         kb = kb2;
     }
 
 #pragma unroll
-    for (int j = 0; j < NBLK; j++) red[wave][j][lane] = acc[j];
+    for (int b = 0; b < RB; b++)
+#pragma unroll
+        for (int j = 0; j < NBLK; j++) red[wave][b * NBLK + j][lane] = acc[b][j];
     __syncthreads();
-    for (int j = wave; j < NBLK; j += kGvWaves) {
+    for (int e = wave; e < RB * NBLK; e += kGvWaves) {
+        const int b = e / NBLK, j = e % NBLK;
         const int64_t col = (nb0 + j) * 16 + fr;
         if (col >= p.n) continue;
-        v4i sum = red[0][j][lane];
+        v4i sum = red[0][e][lane];
 #pragma unroll
-        for (int w = 1; w < kGvWaves; w++) sum += red[w][j][lane];
+        for (int w = 1; w < kGvWaves; w++) sum += red[w][e][lane];
         const float cf = ep.col_factor(p, col), cb = ep.col_bias(p, col);
+        float rfe[4];
+#pragma unroll
+        for (int r = 0; r < 4; r++) rfe[r] = rf[0][r];
+#pragma unroll
+        for (int bb = 1; bb < RB; bb++)
+            if (bb == b)
+#pragma unroll
+                for (int r = 0; r < 4; r++) rfe[r] = rf[bb][r];
 #pragma unroll
         for (int r = 0; r < 4; r++) {
-            const int64_t row = 4 * (lane / 16) + r;
-            if (row < p.m) ep.store(p, row, col, sum[r], rf[r], cf, cb);
+            const int64_t row = 16 * b + 4 * (lane / 16) + r;
+            if (row < p.m) ep.store(p, row, col, sum[r], rfe[r], cf, cb);
         }
     }
 }
 
-template <int NBLK, int SPS, int EPI, int OUT>
+template <int NBLK, int SPS, int RB, int EPI, int OUT>
 hipError_t launch_gemv_t(const Params &p, int64_t batch, hipStream_t st) {
     const int64_t nblocks = (p.n + 15) / 16;
-    hipLaunchKernelGGL((gemv_i8_kernel<NBLK, SPS, EPI, OUT>), dim3((unsigned)((nblocks + NBLK - 1) / NBLK), 1,
+    hipLaunchKernelGGL((gemv_i8_kernel<NBLK, SPS, RB, EPI, OUT>), dim3((unsigned)((nblocks + NBLK - 1) / NBLK), 1,
                        (unsigned)batch), dim3(kGvWaves * 64), 0, st, p);
     return hipGetLastError();
 }
 
-// One column block per workgroup; 256-k register stages while the columns
-// give at most about 1.5 workgroups per CU, 128-k stages above.  Measured on
-// MI355X with the weights streamed from HBM (HIP-graph replays rotating
-// copies), against 2, 4 and 7 column blocks per workgroup and 64-k stages:
-// best or within 6% of best at n x k = 4096 x 4096, 11008 x 4096,
-// 4096 x 11008 and 28672 x 8192 (m = 1, 4, 16).
-template <int EPI, int OUT>
+// Launch shapes measured on MI355X with the weights streamed from HBM
+// (HIP-graph replays rotating copies) against 1, 2, 4 and 7 column blocks per
+// workgroup and 64-, 128- and 256-k stages, at n x k = 4096 x 4096,
+// 11008 x 4096, 4096 x 11008 and 28672 x 8192.  One row block (m <= 16): one
+// column block per workgroup, 256-k stages up to 384 column blocks, 128-k
+// above (best or within 6% of best).  More row blocks re-read x for every
+// column block a workgroup owns, so past 384 column blocks four of them
+// share each x fragment (64-k stages keep the registers in bounds): the best
+// measured shape at m = 32, 48 and 64.
+template <int RB, int EPI, int OUT>
 hipError_t launch_gemv_n(const Params &p, int64_t batch, hipStream_t st) {
     const int64_t nblocks = (p.n + 15) / 16;
-    if (nblocks <= 384) return launch_gemv_t<1, 4, EPI, OUT>(p, batch, st);
-    return launch_gemv_t<1, 2, EPI, OUT>(p, batch, st);
+    if (RB == 1) {
+        if (nblocks <= 384) return launch_gemv_t<1, 4, RB, EPI, OUT>(p, batch, st);
+        return launch_gemv_t<1, 2, RB, EPI, OUT>(p, batch, st);
+    }
+    if (nblocks <= 384) return launch_gemv_t<1, 2, RB, EPI, OUT>(p, batch, st);
+    return launch_gemv_t<4, 1, RB, EPI, OUT>(p, batch, st);
+}
+
+template <int EPI, int OUT>
+hipError_t launch_gemv_rb(const Params &p, int64_t batch, hipStream_t st) {
+    switch ((p.m + 15) / 16) {
+        case 1: return launch_gemv_n<1, EPI, OUT>(p, batch, st);
+        case 2: return launch_gemv_n<2, EPI, OUT>(p, batch, st);
+        case 3: return launch_gemv_n<3, EPI, OUT>(p, batch, st);
+        default: return launch_gemv_n<4, EPI, OUT>(p, batch, st);
+    }
 }
 
 template <int EPI>
 hipError_t launch_gemv_out(int out_kind, const Params &p, int64_t batch, hipStream_t st) {
     switch (out_kind) {
-        case OUT_F16: return launch_gemv_n<EPI, OUT_F16>(p, batch, st);
-        case OUT_BF16: return launch_gemv_n<EPI, OUT_BF16>(p, batch, st);
-        default: return launch_gemv_n<EPI, OUT_I32>(p, batch, st);
+        case OUT_F16: return launch_gemv_rb<EPI, OUT_F16>(p, batch, st);
+        case OUT_BF16: return launch_gemv_rb<EPI, OUT_BF16>(p, batch, st);
+        default: return launch_gemv_rb<EPI, OUT_I32>(p, batch, st);
     }
 }
 
@@ -785,7 +828,7 @@ hipError_t launch_gemm_i8(const GemmI8Args &a, hipStream_t st) {
     const int64_t es = a.out_kind == OUT_I32 ? 4 : 2;
     Params p{a.x, a.w, a.pts, a.deq, a.sa, a.sw, a.eps, a.m, a.n, a.k, a.out, a.bias,
              a.m * a.k, a.n * a.k, a.m, a.deq_stride, a.m * a.n * es};
-    if (a.w_nk && a.m <= 16 && a.k % 64 == 0) {
+    if (a.w_nk && a.m <= 64 && a.k % 64 == 0) {
         if ((a.n + 15) / 16 > 0x7fffffff) return hipErrorInvalidValue;
         return a.epi == EPI_ROWCOL ? launch_gemv_out<EPI_ROWCOL>(a.out_kind, p, batch, st)
                                    : launch_gemv_out<EPI_SCALARS>(a.out_kind, p, batch, st);

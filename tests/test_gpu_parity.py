@@ -68,6 +68,10 @@ W8A8_SHAPES = [
     (4, 6400, 256, True),      # 128-k register stages (more than 384 column blocks)
     (2, 13000, 128, True),     # n % 16 != 0 with 128-k stages
     (3, 28672, 64, True),      # a single k step
+    (17, 400, 512, True),      # decode kernel with two to four 16-row blocks
+    (33, 1000, 768, True),
+    (64, 6400, 256, True),     # four column blocks per workgroup
+    (48, 13000, 128, True),    # four column blocks per workgroup, the last one past n
 ]
 
 
@@ -135,6 +139,7 @@ def test_w8a8_deterministic():
     (2, 33, 50, 77, False, False),
     (2, 1, 1, 1, False, True),
     (3, 16, 270, 320, True, True),      # decode kernel
+    (2, 40, 900, 192, True, False),     # decode kernel, three row blocks
 ])
 def test_w8a8_batched_parity(batch, m, n, k, nk, per_batch_deq):
     ds = [synthetic.w8a8(m, n, k, nk, seed=1900 + 10 * b + m + n + k) for b in range(batch)]
