@@ -16,13 +16,13 @@
 //         and packed weights streamed into LDS through a ring of 128-k
 //         slices; each lane takes its weight words from LDS in the order the
 //         32x32x32 operand needs.
-// 16 < m < 256: 128 x 128 tiles, 2 x 2 waves of 64 x 64 on 32x32x32, A
+// 64 < m < 256: 128 x 128 tiles, 2 x 2 waves of 64 x 64 on 32x32x32, A
 //         staged in LDS per 256-k step (rows padded to 272 bytes), B loaded
 //         per wave straight into registers in the lane order that operand
 //         needs.
-// m <= 16: decode GEMV.  The m rows fill one 16-row MFMA block (rows past m
-//         repeat row 0 and are never stored); each workgroup owns NBLK
-//         column blocks and its waves split k, each wave keeping two
+// m <= 64: decode GEMV.  The m rows fill one to four 16-row MFMA blocks
+//         (rows past m repeat row 0 and are never stored); each workgroup
+//         owns NBLK column blocks and its waves split k, each wave keeping two
 //         register stages so the next k block's weights are in flight while
 //         the current one is multiplied; int32 partials are summed in LDS in
 //         a fixed order (exact, hence deterministic).  Weights are read with
@@ -397,20 +397,21 @@ __global__ __launch_bounds__(kXThreads, 1) void w2a8_big_kernel(const int8_t *__
 // ---------------------------------------------------------------------------
 // m <= 16: split-K decode GEMV
 // ---------------------------------------------------------------------------
-// U k blocks of operands for the NBLK column blocks of one wave.
-template <int NBLK, int U>
+// U k blocks of operands for the NBLK column blocks and RB row blocks of one
+// wave.
+template <int NBLK, int U, int RB>
 struct GemvStage {
     uint4 w[U][NBLK];
-    v4i a[U][4];
+    v4i a[U][RB][4];
 };
 
 // Issue every load of the k blocks kb0, kb0 + WAVES, ... (U of them) from
 // clamped, in-bounds addresses; nothing is conditional, so no load waits for
 // another.  A k block past the end is masked at compute time.
-template <int NBLK, int WAVES, int U>
-__device__ __forceinline__ void gemv_load(GemvStage<NBLK, U> &st, const int8_t *xrow,
+template <int NBLK, int WAVES, int U, int RB>
+__device__ __forceinline__ void gemv_load(GemvStage<NBLK, U, RB> &st, const int8_t *const (&xrow)[RB],
                                           const uint32_t *__restrict__ packed, int64_t kb0, int64_t nb0,
-                                          int64_t nblocks, int64_t kblocks, int lane, bool row_live) {
+                                          int64_t nblocks, int64_t kblocks, int lane, const bool (&row_live)[RB]) {
 #pragma unroll
     for (int u = 0; u < U; u++) {
         const int64_t kb = kb0 + (int64_t)u * WAVES;
@@ -421,31 +422,37 @@ __device__ __forceinline__ void gemv_load(GemvStage<NBLK, U> &st, const int8_t *
             st.w[u][j] = load16_stream(packed + (nbc * kblocks + kbc) * 256 + 4 * lane);
         }
 #pragma unroll
-        // lanes of rows past m load nothing (their rows are never stored)
-        for (int t = 0; t < 4; t++)
-            st.a[u][t] = row_live ? *reinterpret_cast<const v4i *>(xrow + kbc * 256 + 16 * t) : v4i{0, 0, 0, 0};
+        for (int b = 0; b < RB; b++)
+#pragma unroll
+            // lanes of rows past m load nothing (their rows are never stored)
+            for (int t = 0; t < 4; t++)
+                st.a[u][b][t] = row_live[b] ? *reinterpret_cast<const v4i *>(xrow[b] + kbc * 256 + 16 * t)
+                                            : v4i{0, 0, 0, 0};
     }
 }
 
-template <int NBLK, int WAVES, int U>
-__device__ __forceinline__ void gemv_compute(const GemvStage<NBLK, U> &st, v4i (&acc)[NBLK], int64_t kb0,
+template <int NBLK, int WAVES, int U, int RB>
+__device__ __forceinline__ void gemv_compute(const GemvStage<NBLK, U, RB> &st, v4i (&acc)[RB][NBLK], int64_t kb0,
                                              int64_t kblocks) {
 #pragma unroll
     for (int u = 0; u < U; u++) {
         // a zero activation fragment removes a k block past the end exactly
         const bool ok = kb0 + (int64_t)u * WAVES < kblocks;
 #pragma unroll
-        for (int t = 0; t < 4; t++) {
-            const v4i a = ok ? st.a[u][t] : v4i{0, 0, 0, 0};
+        for (int t = 0; t < 4; t++)
 #pragma unroll
-            for (int j = 0; j < NBLK; j++)
-                acc[j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, unpack_tern(word_of(st.w[u][j], t)), acc[j], 0,
-                                                               0, 0);
-        }
+            for (int j = 0; j < NBLK; j++) {
+                const v4i w = unpack_tern(word_of(st.w[u][j], t));
+#pragma unroll
+                for (int b = 0; b < RB; b++) {
+                    const v4i a = ok ? st.a[u][b][t] : v4i{0, 0, 0, 0};
+                    acc[b][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, w, acc[b][j], 0, 0, 0);
+                }
+            }
     }
 }
 
-template <int NBLK, int WAVES, int U, int OUT>
+template <int NBLK, int WAVES, int U, int RB, int OUT>
 __global__ __launch_bounds__(WAVES * 64) void w2a8_gemv_kernel(const int8_t *__restrict__ xq,
                                                                const float *__restrict__ pts,
                                                                const int32_t *__restrict__ rowsum,
@@ -454,88 +461,140 @@ __global__ __launch_bounds__(WAVES * 64) void w2a8_gemv_kernel(const int8_t *__r
                                                                const float *__restrict__ bias,
                                                                int64_t m, int64_t n, int64_t k,
                                                                void *__restrict__ out) {
-    __shared__ v4i red[WAVES][NBLK][kWave];
+    __shared__ v4i red[WAVES][RB * NBLK][kWave];
     const int lane = threadIdx.x % kWave, wave = wave_id();
     const int64_t nb0 = (int64_t)blockIdx.x * NBLK;
     const int64_t nblocks = n / 16, kblocks = k / 256;
     const int fr = lane % 16;
     // Rows past m read row 0: an MFMA row only feeds its own output row,
     // which is never stored.  Column blocks past n likewise repeat the last.
-    const int8_t *xrow = xq + (int64_t)(fr < m ? fr : 0) * k + 64 * (lane / 16);
-    // this lane's output rows 4(lane/16) + r: their code sums and scales are
-    // loaded now, so their latency hides behind the k loop
+    const int8_t *xrow[RB];
+    bool row_live[RB];
+#pragma unroll
+    for (int b = 0; b < RB; b++) {
+        row_live[b] = 16 * b + fr < m;
+        xrow[b] = xq + (int64_t)(row_live[b] ? 16 * b + fr : 0) * k + 64 * (lane / 16);
+    }
+    // With one row block, this lane's output rows 4(lane/16) + r have their
+    // code sums and scales loaded now, so their latency hides behind the k
+    // loop; more row blocks load them in the epilogue, keeping the registers
+    // for the operand stages.
     int32_t rsr[4];
     float ptr[4];
+    if constexpr (RB == 1) {
 #pragma unroll
-    for (int r = 0; r < 4; r++) {
-        const int64_t row = 4 * (lane / 16) + r < m ? 4 * (lane / 16) + r : m - 1;
-        rsr[r] = rowsum[row];
-        ptr[r] = OUT == OUT_I32 ? 0.0f : pts[row];
+        for (int r = 0; r < 4; r++) {
+            const int64_t row = 4 * (lane / 16) + r < m ? 4 * (lane / 16) + r : m - 1;
+            rsr[r] = rowsum[row];
+            ptr[r] = OUT == OUT_I32 ? 0.0f : pts[row];
+        }
     }
 
-    v4i acc[NBLK];
+    v4i acc[RB][NBLK];
 #pragma unroll
-    for (int j = 0; j < NBLK; j++) acc[j] = v4i{0, 0, 0, 0};
+    for (int b = 0; b < RB; b++)
+#pragma unroll
+        for (int j = 0; j < NBLK; j++) acc[b][j] = v4i{0, 0, 0, 0};
 
     // Two register stages of U k blocks each: the loads of the next stage are
     // in flight while the matrix cores consume the current one.
     constexpr int64_t step = (int64_t)WAVES * U;
-    GemvStage<NBLK, U> s0, s1;
+    GemvStage<NBLK, U, RB> s0, s1;
     int64_t kb = wave;
-    gemv_load<NBLK, WAVES, U>(s0, xrow, packed, kb, nb0, nblocks, kblocks, lane, fr < m);
+    gemv_load<NBLK, WAVES, U, RB>(s0, xrow, packed, kb, nb0, nblocks, kblocks, lane, row_live);
     while (true) {
         const int64_t kb1 = kb + step;
-        if (kb1 < kblocks) gemv_load<NBLK, WAVES, U>(s1, xrow, packed, kb1, nb0, nblocks, kblocks, lane, fr < m);
-        gemv_compute<NBLK, WAVES, U>(s0, acc, kb, kblocks);
+        if (kb1 < kblocks) gemv_load<NBLK, WAVES, U, RB>(s1, xrow, packed, kb1, nb0, nblocks, kblocks, lane, row_live);
+        gemv_compute<NBLK, WAVES, U, RB>(s0, acc, kb, kblocks);
         if (kb1 >= kblocks) break;
         const int64_t kb2 = kb1 + step;
-        if (kb2 < kblocks) gemv_load<NBLK, WAVES, U>(s0, xrow, packed, kb2, nb0, nblocks, kblocks, lane, fr < m);
-        gemv_compute<NBLK, WAVES, U>(s1, acc, kb1, kblocks);
+        if (kb2 < kblocks) gemv_load<NBLK, WAVES, U, RB>(s0, xrow, packed, kb2, nb0, nblocks, kblocks, lane, row_live);
+        gemv_compute<NBLK, WAVES, U, RB>(s1, acc, kb1, kblocks);
         if (kb2 >= kblocks) break;
         kb = kb2;
     }
 
 #pragma unroll
-    for (int j = 0; j < NBLK; j++) red[wave][j][lane] = acc[j];
+    for (int b = 0; b < RB; b++)
+#pragma unroll
+        for (int j = 0; j < NBLK; j++) red[wave][b * NBLK + j][lane] = acc[b][j];
     __syncthreads();
     const float g = OUT == OUT_I32 ? 0.0f : (float)gamma[0];  // gamma may be NULL for int32 output
-    for (int j = wave; j < NBLK; j += WAVES) {
+    for (int e = wave; e < RB * NBLK; e += WAVES) {
+        const int b = e / NBLK, j = e % NBLK;
         const int64_t nb = nb0 + j;
         if (nb >= nblocks) continue;
-        v4i s = red[0][j][lane];
+        v4i s = red[0][e][lane];
 #pragma unroll
-        for (int w = 1; w < WAVES; w++) s += red[w][j][lane];
+        for (int w = 1; w < WAVES; w++) s += red[w][e][lane];
         const int64_t col = nb * 16 + fr;
         const float cb = (OUT != OUT_I32 && bias) ? bias[col] : 0.0f;
+        int32_t rs[4];
+        float pt[4];
 #pragma unroll
         for (int r = 0; r < 4; r++) {
-            const int64_t row = 4 * (lane / 16) + r;
-            if (row < m) epilogue_store<OUT>(out, row * n + col, s[r], rsr[r], ptr[r], g, bias, cb);
+            if constexpr (RB == 1) {
+                rs[r] = rsr[r];
+                pt[r] = ptr[r];
+            } else {
+                const int64_t row = 16 * b + 4 * (lane / 16) + r < m ? 16 * b + 4 * (lane / 16) + r : m - 1;
+                rs[r] = rowsum[row];
+                pt[r] = OUT == OUT_I32 ? 0.0f : pts[row];
+            }
+        }
+#pragma unroll
+        for (int r = 0; r < 4; r++) {
+            const int64_t row = 16 * b + 4 * (lane / 16) + r;
+            if (row < m) epilogue_store<OUT>(out, row * n + col, s[r], rs[r], pt[r], g, bias, cb);
         }
     }
 }
 
-template <int NBLK, int WAVES, int U, int OUT>
+template <int NBLK, int WAVES, int U, int RB, int OUT>
 hipError_t launch_gemv(const int8_t *xq, const float *pts, const int32_t *rowsum, const uint32_t *packed,
                        const double *gamma, const float *bias, int64_t m, int64_t n, int64_t k, void *out,
                        hipStream_t st) {
     const int64_t nblocks = n / 16;
     const unsigned grid = (unsigned)((nblocks + NBLK - 1) / NBLK);
-    hipLaunchKernelGGL((w2a8_gemv_kernel<NBLK, WAVES, U, OUT>), dim3(grid), dim3(WAVES * 64), 0, st, xq,
+    hipLaunchKernelGGL((w2a8_gemv_kernel<NBLK, WAVES, U, RB, OUT>), dim3(grid), dim3(WAVES * 64), 0, st, xq,
                        pts, rowsum, packed, gamma, bias, m, n, k, out);
     return hipGetLastError();
+}
+
+// 16 < m <= 64: two to four 16-row blocks.  Every column block a workgroup
+// owns re-reads x, so wide products give each workgroup several.  Measured
+// on MI355X with the weights streamed from HBM (HIP-graph replays rotating
+// copies) at n x k = 4096 x 4096, 11008 x 4096 and 28672 x 8192, m = 17, 32,
+// 48, 64, against 1-4 column blocks with 8 waves and 4 with 4 waves: one
+// column block up to 384 column blocks, three up to 1024, four with 4 waves
+// above (whose larger register budget holds four row blocks' stages).
+template <int RB, int OUT>
+hipError_t launch_gemv_rows(const int8_t *xq, const float *pts, const int32_t *rowsum, const uint32_t *packed,
+                            const double *gamma, const float *bias, int64_t m, int64_t n, int64_t k, void *out,
+                            hipStream_t st) {
+    const int64_t nblocks = n / 16;
+    if (nblocks <= 384) return launch_gemv<1, 8, 1, RB, OUT>(xq, pts, rowsum, packed, gamma, bias, m, n, k, out, st);
+    if (nblocks <= 1024) return launch_gemv<3, 8, 1, RB, OUT>(xq, pts, rowsum, packed, gamma, bias, m, n, k, out, st);
+    return launch_gemv<4, 4, 1, RB, OUT>(xq, pts, rowsum, packed, gamma, bias, m, n, k, out, st);
 }
 
 template <int OUT>
 hipError_t launch_out(const int8_t *xq, const float *pts, const int32_t *rowsum, const uint32_t *packed,
                       const double *gamma, const float *bias, int64_t m, int64_t n, int64_t k, void *out,
                       hipStream_t st) {
+    if (m > 16 && m <= 64) {
+        switch ((m + 15) / 16) {
+            case 2: return launch_gemv_rows<2, OUT>(xq, pts, rowsum, packed, gamma, bias, m, n, k, out, st);
+            case 3: return launch_gemv_rows<3, OUT>(xq, pts, rowsum, packed, gamma, bias, m, n, k, out, st);
+            default: return launch_gemv_rows<4, OUT>(xq, pts, rowsum, packed, gamma, bias, m, n, k, out, st);
+        }
+    }
     if (m <= 16) {
         // Measured on MI355X at k=8192, n=28672 with the weights streamed from
         // HBM, 8 waves and one k block per register stage: 4 column blocks per
         // workgroup up to m = 4, 7 above (1792 column blocks = 256 workgroups).
-        if (m <= 4) return launch_gemv<4, 8, 1, OUT>(xq, pts, rowsum, packed, gamma, bias, m, n, k, out, st);
-        return launch_gemv<7, 8, 1, OUT>(xq, pts, rowsum, packed, gamma, bias, m, n, k, out, st);
+        if (m <= 4) return launch_gemv<4, 8, 1, 1, OUT>(xq, pts, rowsum, packed, gamma, bias, m, n, k, out, st);
+        return launch_gemv<7, 8, 1, 1, OUT>(xq, pts, rowsum, packed, gamma, bias, m, n, k, out, st);
     }
     if (m >= XBM) {
         const int tiles_m = (int)((m + XBM - 1) / XBM), tiles_n = (int)((n + XBN - 1) / XBN);

@@ -270,7 +270,10 @@ def test_pack_int4_parity(n, k):
 # ---------------------------------------------------------------------------
 # m >= 256 takes the large-tile kernel: one exact tile with fewer 128-k
 # slices than ring stages, ragged m and n over several tiles, a longer k.
+# m <= 64 takes the decode kernel with one to four 16-row blocks and one,
+# three or four column blocks per workgroup (the last past n).
 W2A8_SHAPES = [(1, 400, 512), (2, 256, 768), (4, 400, 512), (5, 64, 256), (16, 400, 768), (17, 400, 512),
+               (33, 400, 768), (64, 6400, 512), (40, 20000, 256), (64, 16400, 256),
                (130, 256, 768), (300, 400, 512), (256, 128, 256), (513, 272, 1280), (600, 528, 2304)]
 
 
@@ -436,7 +439,7 @@ def test_w8a8_bias_parity(m, n, k, nk):
         assert torch.equal(o0, onb), "a zero bias must leave the result unchanged"
 
 
-@pytest.mark.parametrize("m,n,k", [(1, 400, 512), (16, 400, 768), (130, 256, 768), (300, 400, 512)])
+@pytest.mark.parametrize("m,n,k", [(1, 400, 512), (16, 400, 768), (40, 400, 512), (130, 256, 768), (300, 400, 512)])
 def test_w2a8_bias_parity(m, n, k):
     d = synthetic.bitlinear(m, n, k, seed=1400 + m + n)
     xq_ref, pts_ref, _ = oracle.quant_act(d["x"].float().numpy(), rmsnorm=True)
