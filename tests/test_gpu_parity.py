@@ -510,7 +510,7 @@ def test_bias_with_int32_output_is_rejected():
 # A4W4
 # ---------------------------------------------------------------------------
 @pytest.mark.parametrize("m,n,k", [(33, 20, 130), (256, 256, 512), (129, 65, 1000), (1, 1, 1), (600, 520, 640),
-                                   (1024, 1024, 256), (16, 300, 512)])
+                                   (1024, 1024, 256), (16, 300, 512), (48, 200, 256)])
 @pytest.mark.parametrize("scale_mul", [1.0, 0.25])
 def test_a4w4_parity(m, n, k, scale_mul):
     d = synthetic.a4w4(m, n, k, seed=800 + m + n + k)
