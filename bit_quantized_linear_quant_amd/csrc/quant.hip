@@ -197,21 +197,33 @@ __global__ __launch_bounds__(kQWaveRows * kWave) void quant_act_wave_kernel(cons
 
     const float ap = amax > eps_q ? amax : eps_q;
     const float s = __fdiv_rn(127.0f, ap);
-    int rs = 0;
+    // The code of v is clamp(rint(fl(v * s)), -128, 127).  Clamping first
+    // (the bounds are integers) and adding 1.5 * 2^23 rounds the value to an
+    // integer, ties to even, in the low mantissa bits: the word is
+    // 0x4B400000 + code, whose low byte is the code's byte.  Sums of these
+    // words wrap mod 2^32; subtracting the count times 0x4B400000 leaves the
+    // exact code sum.
+    constexpr float kRound = 12582912.0f;
+    constexpr uint32_t kRoundBits = 0x4B400000u;
+    uint32_t rsw = 0;
 #pragma unroll
     for (int c = 0; c < NCH; c++) {
         const int64_t ch = (int64_t)c * kWave + lane;
-        uint32_t lo = 0, hi = 0;
+        uint32_t y[8];
 #pragma unroll
-        for (int j = 0; j < 4; j++) {
-            const int c0 = code_i8(v[c][j], s), c1 = code_i8(v[c][j + 4], s);
-            rs += c0 + c1;
-            lo |= (uint32_t)(c0 & 0xff) << (8 * j);
-            hi |= (uint32_t)(c1 & 0xff) << (8 * j);
+        for (int j = 0; j < 8; j++) {
+            const float t = fminf(fmaxf(__fmul_rn(v[c][j], s), -128.0f), 127.0f);
+            y[j] = __float_as_uint(__fadd_rn(t, kRound));
+            rsw += y[j];
         }
+        // bytes 0 of y[0..3] and y[4..7]
+        const uint32_t lo = __builtin_amdgcn_perm(__builtin_amdgcn_perm(y[3], y[2], 0x0c0c0400u),
+                                                  __builtin_amdgcn_perm(y[1], y[0], 0x0c0c0400u), 0x05040100u);
+        const uint32_t hi = __builtin_amdgcn_perm(__builtin_amdgcn_perm(y[7], y[6], 0x0c0c0400u),
+                                                  __builtin_amdgcn_perm(y[5], y[4], 0x0c0c0400u), 0x05040100u);
         if (ch < nchunk) *reinterpret_cast<uint2 *>(qr + ch * 8) = make_uint2(lo, hi);
     }
-    rs = wave_sum(rs);
+    rsw = wave_sum(rsw);
     if (lane == 0) {
         float p;
         if (RMS) {
@@ -221,7 +233,8 @@ __global__ __launch_bounds__(kQWaveRows * kWave) void quant_act_wave_kernel(cons
             p = __fdiv_rn(ap, 127.0f);
         }
         pts[row] = p;
-        if (rowsum) rowsum[row] = rs;
+        // NCH * 64 * 8 words were summed (masked chunks as code 0)
+        if (rowsum) rowsum[row] = (int32_t)(rsw - (uint32_t)(NCH * kWave * 8) * kRoundBits);
     }
 }
 
