@@ -420,7 +420,8 @@ def _bias_tol(y, b):
 
 
 @pytest.mark.parametrize("m,n,k,nk", [(300, 270, 200, True), (77, 45, 77, True), (129, 257, 1000, False),
-                                      (520, 777, 192, True), (1024, 768, 1024, True), (1, 1, 1, False)])
+                                      (520, 777, 192, True), (1024, 768, 1024, True), (1, 1, 1, False),
+                                      (5, 300, 256, True), (40, 300, 256, True)])
 def test_w8a8_bias_parity(m, n, k, nk):
     d = synthetic.w8a8(m, n, k, nk, seed=1200 + m + n + k)
     x, w, deq, pts = (d[key] for key in ("x", "w", "deq", "pts"))
