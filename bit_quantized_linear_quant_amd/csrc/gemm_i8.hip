@@ -20,8 +20,9 @@
 //   clamped and never stored.  16-bit outputs leave through a padded LDS
 //   tile as whole row segments.
 //
-// gemv_i8_kernel -- decode shapes: m <= 64 with [n][k] weights and
-//   k % 64 == 0.  The token rows fill up to four 16-row matrix-core blocks;
+// gemv_i8_kernel -- decode shapes: m <= 64 (or m <= 128 with at most 6144
+//   columns) with [n][k] weights and k % 64 == 0.  The token rows fill up
+//   to eight 16-row matrix-core blocks;
 //   waves split k over a few 16-column blocks per workgroup, reading the
 //   weights once with streaming loads, and sum their partials in LDS.
 //
@@ -383,6 +384,8 @@ __device__ __forceinline__ uint4 load_row16(const int8_t *base, int64_t rows, in
         if (row >= rows) return make_uint4(0, 0, 0, 0);
         const int8_t *p = base + row * k + kk;
         uint32_t v[4] = {0, 0, 0, 0};
+        // unrolled, so v stays in registers (a run-time index would put it in scratch)
+#pragma unroll
         for (int j = 0; j < 16; j++)
             if (kk + j < k) v[j / 4] |= (uint32_t)(uint8_t)p[j] << (8 * (j % 4));
         return make_uint4(v[0], v[1], v[2], v[3]);
@@ -405,6 +408,7 @@ __device__ __forceinline__ void load_kn_4x4(const int8_t *w, int64_t n, int64_t 
 #pragma unroll
         for (int i = 0; i < 4; i++) {
             uint32_t r = 0;
+#pragma unroll
             for (int j = 0; j < 4; j++)
                 if (kk + i < k && nn + j < n) r |= (uint32_t)(uint8_t)w[(kk + i) * n + nn + j] << (8 * j);
             rowv[i] = r;
@@ -449,7 +453,8 @@ __global__ __launch_bounds__(kThreads) void gemm_i8_kernel(Params p) {
     uint32_t rbt[KALL][2][4];
 
     // `mask` (std::true_type / false_type): the k-step runs past k
-    auto gload = [&](int slot, int64_t k0, auto mask) {
+    // the lambdas are inlined so the slot arrays stay in registers
+    auto gload = [&](int slot, int64_t k0, auto mask) __attribute__((always_inline)) {
         constexpr bool MASK = decltype(mask)::value;
 #pragma unroll
         for (int c = 0; c < 2; c++) {
@@ -465,12 +470,12 @@ __global__ __launch_bounds__(kThreads) void gemm_i8_kernel(Params p) {
         }
     };
     // the branch is uniform (scalar): either path keeps its loads in flight
-    auto gload_step = [&](int slot, int64_t kt) {
+    auto gload_step = [&](int slot, int64_t kt) __attribute__((always_inline)) {
         if ((kt + 1) * BK > p.k) gload(slot, kt * BK, std::true_type{});
         else gload(slot, kt * BK, std::false_type{});
     };
     // slot s goes to LDS columns [64 s, 64 s + 64) of each row
-    auto sstore = [&](int slot, int col0) {
+    auto sstore = [&](int slot, int col0) __attribute__((always_inline)) {
 #pragma unroll
         for (int c = 0; c < 2; c++) {
             const int chunk = tid + c * kThreads;
@@ -500,7 +505,7 @@ __global__ __launch_bounds__(kThreads) void gemm_i8_kernel(Params p) {
     // rows read together fall in distinct bank groups.
     const int fr = lane % 32;           // fragment row / column
     const int fk = 16 * (lane / 32);    // fragment k offset (bytes)
-    auto compute = [&](int col0) {
+    auto compute = [&](int col0) __attribute__((always_inline)) {
 #pragma unroll
         for (int s = 0; s < BK / 32; s++) {
             v4i a[TM], b[TN];
@@ -571,7 +576,7 @@ __global__ __launch_bounds__(kThreads) void gemm_i8_kernel(Params p) {
 }
 
 // ---------------------------------------------------------------------------
-// Decode kernel: m <= 64, [n][k] weights, k % 64 == 0
+// Decode kernel: m <= 128 (see gemv_fits), [n][k] weights, k % 64 == 0
 // ---------------------------------------------------------------------------
 // The m token rows fill RB 16-row blocks of v_mfma_i32_16x16x64_i8 (rows past
 // m repeat row 0 and are never stored; the kernel is bound by the weight
@@ -743,8 +748,21 @@ hipError_t launch_gemv_rb(const Params &p, int64_t batch, hipStream_t st) {
         case 1: return launch_gemv_n<1, EPI, OUT>(p, batch, st);
         case 2: return launch_gemv_n<2, EPI, OUT>(p, batch, st);
         case 3: return launch_gemv_n<3, EPI, OUT>(p, batch, st);
-        default: return launch_gemv_n<4, EPI, OUT>(p, batch, st);
+        case 4: return launch_gemv_n<4, EPI, OUT>(p, batch, st);
+        // 64 < m <= 128, at most 384 column blocks (gemv_fits): 64-k stages
+        // keep six or eight row blocks' operands in registers
+        case 5: case 6: return launch_gemv_t<1, 1, 6, EPI, OUT>(p, batch, st);
+        default: return launch_gemv_t<1, 1, 8, EPI, OUT>(p, batch, st);
     }
+}
+
+// Products the decode kernel takes: m <= 64, or m <= 128 when the columns
+// are few.  Past 64 rows every column block re-reads eight 16-row blocks of
+// x; measured with the weights streamed from HBM, that beats the 128x128
+// tiles only up to 384 column blocks (128x4096x4096 21.8 against 50.9 us;
+// at n = 11008 the two tie, at 28672 the tiles win).
+bool gemv_fits(int64_t m, int64_t n) {
+    return m <= 64 || (m <= 128 && (n + 15) / 16 <= 384);
 }
 
 template <int EPI>
@@ -761,10 +779,15 @@ constexpr int kShortSteps = 4;   // k <= 256: the whole k range staged at once
 template <bool NK, bool VEC, int EPI, int OUT>
 hipError_t launch_t(const Params &p, int64_t batch, hipStream_t st) {
     dim3 grid((unsigned)((p.n + BN - 1) / BN), (unsigned)((p.m + BM - 1) / BM), (unsigned)batch);
-    if (p.k <= (int64_t)kShortSteps * BK)
-        hipLaunchKernelGGL((gemm_i8_kernel<NK, VEC, EPI, OUT, kShortSteps>), grid, dim3(kThreads), 0, st, p);
-    else
-        hipLaunchKernelGGL((gemm_i8_kernel<NK, VEC, EPI, OUT, 1>), grid, dim3(kThreads), 0, st, p);
+    // (the byte-load form stages one k-step at a time: its staging registers
+    // for the whole k range would not fit)
+    if constexpr (VEC) {
+        if (p.k <= (int64_t)kShortSteps * BK) {
+            hipLaunchKernelGGL((gemm_i8_kernel<NK, VEC, EPI, OUT, kShortSteps>), grid, dim3(kThreads), 0, st, p);
+            return hipGetLastError();
+        }
+    }
+    hipLaunchKernelGGL((gemm_i8_kernel<NK, VEC, EPI, OUT, 1>), grid, dim3(kThreads), 0, st, p);
     return hipGetLastError();
 }
 
@@ -828,7 +851,7 @@ hipError_t launch_gemm_i8(const GemmI8Args &a, hipStream_t st) {
     const int64_t es = a.out_kind == OUT_I32 ? 4 : 2;
     Params p{a.x, a.w, a.pts, a.deq, a.sa, a.sw, a.eps, a.m, a.n, a.k, a.out, a.bias,
              a.m * a.k, a.n * a.k, a.m, a.deq_stride, a.m * a.n * es};
-    if (a.w_nk && a.m <= 64 && a.k % 64 == 0) {
+    if (a.w_nk && gemv_fits(a.m, a.n) && a.k % 64 == 0) {
         if ((a.n + 15) / 16 > 0x7fffffff) return hipErrorInvalidValue;
         return a.epi == EPI_ROWCOL ? launch_gemv_out<EPI_ROWCOL>(a.out_kind, p, batch, st)
                                    : launch_gemv_out<EPI_SCALARS>(a.out_kind, p, batch, st);

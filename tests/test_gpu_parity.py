@@ -72,6 +72,9 @@ W8A8_SHAPES = [
     (33, 1000, 768, True),
     (64, 6400, 256, True),     # four column blocks per workgroup
     (48, 13000, 128, True),    # four column blocks per workgroup, the last one past n
+    (96, 400, 512, True),      # six and eight row blocks (m <= 128, few columns)
+    (128, 1000, 768, True),
+    (100, 6400, 128, True),    # many columns: back to the 128x128 tiles
 ]
 
 
