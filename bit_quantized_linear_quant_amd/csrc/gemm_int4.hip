@@ -13,13 +13,18 @@
 // One 128-k block is four MFMA steps; its fp32 partial sum is closed before
 // the group scale multiplies it once (group_size is a multiple of 128).
 //
+// x fragments reach the lanes through the wave's own LDS block
+// (rows256_to_fragments): x is loaded in whole cache lines, lane (r, q) taking
+// the 8 halves at k offset 8r of row 4t + q in load t.
+//
 // Workgroup: WAVES waves split the k blocks of NBLK column blocks for one
 // slice of RB 16-row blocks of x (with RB = 2 every unpacked weight fragment
 // feeds two MFMA row blocks; m <= 16 uses RB = 1).  Each wave keeps two
 // register stages: while the matrix cores consume one k block, the weight
 // fragments (non-temporal: read once), scales, zero-points and x fragments
-// of its next k block are in flight; when a wave has at most four k blocks
-// (k <= 4096 with 8 waves) it issues all of their loads at once instead.
+// of its next k block are in flight; with one row block, a wave with at most
+// four k blocks (k <= 4096 with 8 waves) issues all of their loads at once
+// instead.
 // The fp32 partials of the waves are added in LDS in a fixed wave order.
 #include "ql_device.hpp"
 #include "ql_launch.hpp"
@@ -59,7 +64,8 @@ struct Stage {
 // block past the end).  All loads are unconditional, so none of them waits
 // for another.
 template <int NBLK, int RB>
-__device__ __forceinline__ void load_stage(Stage<NBLK, RB> &st, const uint16_t *const xrow[RB],
+__device__ __forceinline__ void load_stage(Stage<NBLK, RB> &st, const uint16_t *__restrict__ x, int64_t row0, int64_t m,
+                                           int64_t k,
                                            const uint32_t *__restrict__ packed_w,
                                            const uint16_t *__restrict__ scales,
                                            const uint32_t *__restrict__ packed_z, int64_t kb,
@@ -79,14 +85,22 @@ __device__ __forceinline__ void load_stage(Stage<NBLK, RB> &st, const uint16_t *
 #pragma unroll
     for (int b = 0; b < RB; b++)
 #pragma unroll
-        for (int t = 0; t < 4; t++) st.a[b][t] = *reinterpret_cast<const v8h *>(xrow[b] + kbc * 128 + 8 * t);
+        for (int t = 0; t < 4; t++) {
+            // Load t of row block b covers rows 16b + 4t + lane/16.  Rows
+            // past m read row 0: an MFMA row only feeds its own output row,
+            // which is never stored.
+            const int64_t r = row0 + 16 * b + 4 * t + lane / 16;
+            st.a[b][t] = *reinterpret_cast<const v8h *>(x + (r < m ? r : 0) * k + kbc * 128 + 8 * fr);
+        }
 }
 
 // Accumulate one k block: per column block, four MFMA steps per row block
 // into a fresh fp32 partial, then one multiply by the group scale.
 template <int NBLK, int RB>
 __device__ __forceinline__ void compute_stage(const Stage<NBLK, RB> &st, v4f (&acc)[RB][NBLK], bool kb_ok,
-                                              int64_t nb0, int64_t nblocks) {
+                                              int64_t nb0, int64_t nblocks, uint8_t *xb, int lane) {
+    v8h a[RB][4];
+    rows256_to_fragments<RB>(st.a, a, xb, lane);
 #pragma unroll
     for (int j = 0; j < NBLK; j++) {
         const bool ok = kb_ok && nb0 + j < nblocks;
@@ -99,7 +113,7 @@ __device__ __forceinline__ void compute_stage(const Stage<NBLK, RB> &st, v4f (&a
         for (int t = 0; t < 4; t++) {
             const v8h wv = unpack_int4(word_of(st.w[j], t), zz);
 #pragma unroll
-            for (int b = 0; b < RB; b++) p[b] = __builtin_amdgcn_mfma_f32_16x16x32_f16(st.a[b][t], wv, p[b], 0, 0, 0);
+            for (int b = 0; b < RB; b++) p[b] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[b][t], wv, p[b], 0, 0, 0);
         }
 #pragma unroll
         for (int b = 0; b < RB; b++)
@@ -118,19 +132,13 @@ __global__ __launch_bounds__(WAVES * 64) void int4_grouped_kernel(const uint16_t
                                                                   int64_t n, int64_t k,
                                                                   void *__restrict__ out) {
     __shared__ v4f red[WAVES][RB * NBLK][kWave];
+    __shared__ __attribute__((aligned(16))) uint8_t xlds[WAVES][16 * RB * kRow256Pitch];
     const int lane = threadIdx.x % kWave, wave = wave_id();
     const int64_t nb0 = (int64_t)blockIdx.x * NBLK;
     const int64_t row0 = (int64_t)blockIdx.y * 16 * RB;
     const int64_t nblocks = n / 16, kblocks = k / 128, groups = k / group_size;
     const int fr = lane % 16;
-    // Rows past m read row 0: an MFMA row only feeds its own output row,
-    // which is never stored.
-    const uint16_t *xrow[RB];
-#pragma unroll
-    for (int b = 0; b < RB; b++) {
-        const int64_t r = row0 + 16 * b + fr;
-        xrow[b] = x + (r < m ? r : 0) * k + 32 * (lane / 16);
-    }
+    uint8_t *xb = xlds[wave];
 
     v4f acc[RB][NBLK];
 #pragma unroll
@@ -149,27 +157,28 @@ __global__ __launch_bounds__(WAVES * 64) void int4_grouped_kernel(const uint16_t
             Stage<NBLK, RB> st[NST];
 #pragma unroll
             for (int u = 0; u < NST; u++)
-                load_stage(st[u], xrow, packed_w, scales, packed_z, kb0 + (int64_t)u * WAVES, nb0, nblocks, kblocks,
+                load_stage(st[u], x, row0, m, k, packed_w, scales, packed_z, kb0 + (int64_t)u * WAVES, nb0, nblocks, kblocks,
                            group_size, groups, n, lane);
 #pragma unroll
-            for (int u = 0; u < NST; u++) compute_stage(st[u], acc, kb0 + (int64_t)u * WAVES < kblocks, nb0, nblocks);
+            for (int u = 0; u < NST; u++)
+                compute_stage(st[u], acc, kb0 + (int64_t)u * WAVES < kblocks, nb0, nblocks, xb, lane);
         }
     } else {
         Stage<NBLK, RB> s0, s1;
         int64_t kb = wave;
-        load_stage(s0, xrow, packed_w, scales, packed_z, kb, nb0, nblocks, kblocks, group_size, groups, n, lane);
+        load_stage(s0, x, row0, m, k, packed_w, scales, packed_z, kb, nb0, nblocks, kblocks, group_size, groups, n, lane);
         while (kb < kblocks) {
             const int64_t kb1 = kb + WAVES;
             if (kb1 < kblocks)
-                load_stage(s1, xrow, packed_w, scales, packed_z, kb1, nb0, nblocks, kblocks, group_size, groups, n,
+                load_stage(s1, x, row0, m, k, packed_w, scales, packed_z, kb1, nb0, nblocks, kblocks, group_size, groups, n,
                            lane);
-            compute_stage(s0, acc, true, nb0, nblocks);
+            compute_stage(s0, acc, true, nb0, nblocks, xb, lane);
             if (kb1 >= kblocks) break;
             const int64_t kb2 = kb1 + WAVES;
             if (kb2 < kblocks)
-                load_stage(s0, xrow, packed_w, scales, packed_z, kb2, nb0, nblocks, kblocks, group_size, groups, n,
+                load_stage(s0, x, row0, m, k, packed_w, scales, packed_z, kb2, nb0, nblocks, kblocks, group_size, groups, n,
                            lane);
-            compute_stage(s1, acc, true, nb0, nblocks);
+            compute_stage(s1, acc, true, nb0, nblocks, xb, lane);
             kb = kb2;
         }
     }
@@ -205,12 +214,17 @@ hipError_t launch_cfg(const uint16_t *x, const uint32_t *packed_w, const uint16_
                       void *out, hipStream_t st) {
     const int64_t nblocks = n / 16;
     dim3 grid((unsigned)((nblocks + NBLK - 1) / NBLK), (unsigned)((m + 16 * RB - 1) / (16 * RB)));
-    if (k / 128 <= (int64_t)WAVES * kAllIn)
-        hipLaunchKernelGGL((int4_grouped_kernel<NBLK, WAVES, RB, OUT, kAllIn>), grid, dim3(WAVES * 64), 0, st, x,
-                           packed_w, scales, packed_z, bias, group_size, m, n, k, out);
-    else
-        hipLaunchKernelGGL((int4_grouped_kernel<NBLK, WAVES, RB, OUT, 0>), grid, dim3(WAVES * 64), 0, st, x,
-                           packed_w, scales, packed_z, bias, group_size, m, n, k, out);
+    // With two row blocks, four stages of x fragments do not fit beside the
+    // weights in registers: those launches keep the two-stage pipeline.
+    if constexpr (RB == 1) {
+        if (k / 128 <= (int64_t)WAVES * kAllIn) {
+            hipLaunchKernelGGL((int4_grouped_kernel<NBLK, WAVES, RB, OUT, kAllIn>), grid, dim3(WAVES * 64), 0, st, x,
+                               packed_w, scales, packed_z, bias, group_size, m, n, k, out);
+            return hipGetLastError();
+        }
+    }
+    hipLaunchKernelGGL((int4_grouped_kernel<NBLK, WAVES, RB, OUT, 0>), grid, dim3(WAVES * 64), 0, st, x, packed_w,
+                       scales, packed_z, bias, group_size, m, n, k, out);
     return hipGetLastError();
 }
 
@@ -258,7 +272,8 @@ struct StageI8 {
 };
 
 template <int NBLK, int RB>
-__device__ __forceinline__ void load_stage_i8(StageI8<NBLK, RB> &st, const int8_t *const xrow[RB],
+__device__ __forceinline__ void load_stage_i8(StageI8<NBLK, RB> &st, const int8_t *__restrict__ xq, int64_t row0,
+                                              int64_t m, int64_t k,
                                               const uint32_t *__restrict__ packed_w,
                                               const uint16_t *__restrict__ scales,
                                               const uint32_t *__restrict__ packed_z, int64_t kb, int64_t nb0,
@@ -278,18 +293,50 @@ __device__ __forceinline__ void load_stage_i8(StageI8<NBLK, RB> &st, const int8_
 #pragma unroll
     for (int b = 0; b < RB; b++)
 #pragma unroll
-        for (int s = 0; s < 2; s++) st.a[b][s] = *reinterpret_cast<const v4i *>(xrow[b] + kbc * 128 + 16 * s);
+        for (int s = 0; s < 2; s++) {
+            // Load s of row block b covers rows 16b + 8s + lane/8; rows past
+            // m read row 0 (their outputs are never stored).
+            const int64_t r = row0 + 16 * b + 8 * s + lane / 8;
+            st.a[b][s] = *reinterpret_cast<const v4i *>(xq + (r < m ? r : 0) * k + kbc * 128 + 16 * (lane % 8));
+        }
+}
+
+// As x_fragments for int8 codes: 128-byte rows, load s of row block b
+// covers rows 16b + 8s + lane/8.
+constexpr int kXPitchI8 = 144;
+
+template <int RB>
+__device__ __forceinline__ void x_fragments_i8(const v4i (&in)[RB][2], v4i (&frag)[RB][2], uint8_t *xb, int lane) {
+    const int fr = lane % 16, q = lane / 16;
+#pragma unroll
+    for (int b = 0; b < RB; b++)
+#pragma unroll
+        for (int s = 0; s < 2; s++)
+            *reinterpret_cast<v4i *>(xb + (16 * b + 8 * s + lane / 8) * kXPitchI8 + 16 * (lane % 8)) = in[b][s];
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+    for (int b = 0; b < RB; b++)
+#pragma unroll
+        for (int s = 0; s < 2; s++)
+            frag[b][s] = *reinterpret_cast<const v4i *>(xb + (16 * b + fr) * kXPitchI8 + 32 * q + 16 * s);
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
 template <int NBLK, int RB>
 __device__ __forceinline__ void compute_stage_i8(const StageI8<NBLK, RB> &st, v4f (&acc)[RB][NBLK], int64_t nb0,
-                                                 int64_t nblocks) {
+                                                 int64_t nblocks, uint8_t *xb, int lane) {
     const v4i ones = v4i{0x01010101, 0x01010101, 0x01010101, 0x01010101};
+    v4i a[RB][2];
+    x_fragments_i8<RB>(st.a, a, xb, lane);
     v4i sx[RB];
 #pragma unroll
     for (int b = 0; b < RB; b++) {
-        sx[b] = __builtin_amdgcn_mfma_i32_16x16x64_i8(st.a[b][0], ones, v4i{0, 0, 0, 0}, 0, 0, 0);
-        sx[b] = __builtin_amdgcn_mfma_i32_16x16x64_i8(st.a[b][1], ones, sx[b], 0, 0, 0);
+        sx[b] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[b][0], ones, v4i{0, 0, 0, 0}, 0, 0, 0);
+        sx[b] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[b][1], ones, sx[b], 0, 0, 0);
     }
 #pragma unroll
     for (int j = 0; j < NBLK; j++) {
@@ -298,8 +345,8 @@ __device__ __forceinline__ void compute_stage_i8(const StageI8<NBLK, RB> &st, v4
         const v4i w0 = weight_step(st.w[j], 0), w1 = weight_step(st.w[j], 1);
 #pragma unroll
         for (int b = 0; b < RB; b++) {
-            v4i p = __builtin_amdgcn_mfma_i32_16x16x64_i8(st.a[b][0], w0, v4i{0, 0, 0, 0}, 0, 0, 0);
-            p = __builtin_amdgcn_mfma_i32_16x16x64_i8(st.a[b][1], w1, p, 0, 0, 0);
+            v4i p = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[b][0], w0, v4i{0, 0, 0, 0}, 0, 0, 0);
+            p = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[b][1], w1, p, 0, 0, 0);
 #pragma unroll
             for (int r = 0; r < 4; r++) acc[b][j][r] = __builtin_fmaf(sc, (float)(p[r] - z * sx[b][r]), acc[b][j][r]);
         }
@@ -316,18 +363,16 @@ __global__ __launch_bounds__(WAVES * 64) void int4_grouped_i8_kernel(const int8_
                                                                      int64_t group_size, int64_t m, int64_t n,
                                                                      int64_t k, void *__restrict__ out) {
     __shared__ v4f red[WAVES][RB * NBLK][kWave];
+    __shared__ __attribute__((aligned(16))) uint8_t xlds[WAVES][16 * RB * kXPitchI8];
     const int lane = threadIdx.x % kWave, wave = wave_id();
     const int64_t nb0 = (int64_t)blockIdx.x * NBLK;
     const int64_t row0 = (int64_t)blockIdx.y * 16 * RB;
     const int64_t nblocks = n / 16, kblocks = k / 128, groups = k / group_size;
     const int fr = lane % 16;
-    // Rows past m read row 0: an MFMA row only feeds its own output row.
-    const int8_t *xrow[RB];
+    uint8_t *xb = xlds[wave];
     float prow[RB][4];
 #pragma unroll
     for (int b = 0; b < RB; b++) {
-        const int64_t r = row0 + 16 * b + fr;
-        xrow[b] = xq + (r < m ? r : 0) * k + 32 * (lane / 16);
 #pragma unroll
         for (int q = 0; q < 4; q++) {
             const int64_t orow = row0 + 16 * b + 4 * (lane / 16) + q;
@@ -348,28 +393,28 @@ __global__ __launch_bounds__(WAVES * 64) void int4_grouped_i8_kernel(const int8_
             StageI8<NBLK, RB> st[NST];
 #pragma unroll
             for (int u = 0; u < NST; u++)
-                load_stage_i8(st[u], xrow, packed_w, scales, packed_z, kb0 + (int64_t)u * WAVES, nb0, nblocks,
+                load_stage_i8(st[u], xq, row0, m, k, packed_w, scales, packed_z, kb0 + (int64_t)u * WAVES, nb0, nblocks,
                               kblocks, group_size, groups, n, lane);
 #pragma unroll
             for (int u = 0; u < NST; u++)
-                if (kb0 + (int64_t)u * WAVES < kblocks) compute_stage_i8(st[u], acc, nb0, nblocks);
+                if (kb0 + (int64_t)u * WAVES < kblocks) compute_stage_i8(st[u], acc, nb0, nblocks, xb, lane);
         }
     } else {
         StageI8<NBLK, RB> s0, s1;
         int64_t kb = wave;
-        load_stage_i8(s0, xrow, packed_w, scales, packed_z, kb, nb0, nblocks, kblocks, group_size, groups, n, lane);
+        load_stage_i8(s0, xq, row0, m, k, packed_w, scales, packed_z, kb, nb0, nblocks, kblocks, group_size, groups, n, lane);
         while (kb < kblocks) {
             const int64_t kb1 = kb + WAVES;
             if (kb1 < kblocks)
-                load_stage_i8(s1, xrow, packed_w, scales, packed_z, kb1, nb0, nblocks, kblocks, group_size, groups,
+                load_stage_i8(s1, xq, row0, m, k, packed_w, scales, packed_z, kb1, nb0, nblocks, kblocks, group_size, groups,
                               n, lane);
-            compute_stage_i8(s0, acc, nb0, nblocks);
+            compute_stage_i8(s0, acc, nb0, nblocks, xb, lane);
             if (kb1 >= kblocks) break;
             const int64_t kb2 = kb1 + WAVES;
             if (kb2 < kblocks)
-                load_stage_i8(s0, xrow, packed_w, scales, packed_z, kb2, nb0, nblocks, kblocks, group_size, groups,
+                load_stage_i8(s0, xq, row0, m, k, packed_w, scales, packed_z, kb2, nb0, nblocks, kblocks, group_size, groups,
                               n, lane);
-            compute_stage_i8(s1, acc, nb0, nblocks);
+            compute_stage_i8(s1, acc, nb0, nblocks, xb, lane);
             kb = kb2;
         }
     }

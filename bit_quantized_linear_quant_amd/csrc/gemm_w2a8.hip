@@ -408,10 +408,11 @@ struct GemvStage {
 // Issue every load of the k blocks kb0, kb0 + WAVES, ... (U of them) from
 // clamped, in-bounds addresses; nothing is conditional, so no load waits for
 // another.  A k block past the end is masked at compute time.
-template <int NBLK, int WAVES, int U, int RB>
+template <int NBLK, int WAVES, int U, int RB, bool XT>
 __device__ __forceinline__ void gemv_load(GemvStage<NBLK, U, RB> &st, const int8_t *const (&xrow)[RB],
                                           const uint32_t *__restrict__ packed, int64_t kb0, int64_t nb0,
-                                          int64_t nblocks, int64_t kblocks, int lane, const bool (&row_live)[RB]) {
+                                          int64_t nblocks, int64_t kblocks, int lane, const bool (&row_live)[RB],
+                                          const int8_t *__restrict__ xq, int64_t m, int64_t k) {
 #pragma unroll
     for (int u = 0; u < U; u++) {
         const int64_t kb = kb0 + (int64_t)u * WAVES;
@@ -424,20 +425,38 @@ __device__ __forceinline__ void gemv_load(GemvStage<NBLK, U, RB> &st, const int8
 #pragma unroll
         for (int b = 0; b < RB; b++)
 #pragma unroll
-            // lanes of rows past m load nothing (their rows are never stored)
-            for (int t = 0; t < 4; t++)
-                st.a[u][b][t] = row_live[b] ? *reinterpret_cast<const v4i *>(xrow[b] + kbc * 256 + 16 * t)
-                                            : v4i{0, 0, 0, 0};
+            for (int t = 0; t < 4; t++) {
+                if constexpr (XT) {
+                    // whole-line loads for rows256_to_fragments; rows past m
+                    // read row 0 (their outputs are never stored)
+                    const int64_t r = 16 * b + 4 * t + lane / 16;
+                    st.a[u][b][t] =
+                        *reinterpret_cast<const v4i *>(xq + (r < m ? r : 0) * k + kbc * 256 + 16 * (lane % 16));
+                } else {
+                    // lanes of rows past m load nothing (their rows are never stored)
+                    st.a[u][b][t] = row_live[b] ? *reinterpret_cast<const v4i *>(xrow[b] + kbc * 256 + 16 * t)
+                                                : v4i{0, 0, 0, 0};
+                }
+            }
     }
 }
 
-template <int NBLK, int WAVES, int U, int RB>
+template <int NBLK, int WAVES, int U, int RB, bool XT>
 __device__ __forceinline__ void gemv_compute(const GemvStage<NBLK, U, RB> &st, v4i (&acc)[RB][NBLK], int64_t kb0,
-                                             int64_t kblocks) {
+                                             int64_t kblocks, uint8_t *xb, int lane) {
 #pragma unroll
     for (int u = 0; u < U; u++) {
         // a zero activation fragment removes a k block past the end exactly
         const bool ok = kb0 + (int64_t)u * WAVES < kblocks;
+        v4i xa[RB][4];
+        if constexpr (XT) {
+            rows256_to_fragments<RB>(st.a[u], xa, xb, lane);
+        } else {
+#pragma unroll
+            for (int b = 0; b < RB; b++)
+#pragma unroll
+                for (int t = 0; t < 4; t++) xa[b][t] = st.a[u][b][t];
+        }
 #pragma unroll
         for (int t = 0; t < 4; t++)
 #pragma unroll
@@ -445,14 +464,14 @@ __device__ __forceinline__ void gemv_compute(const GemvStage<NBLK, U, RB> &st, v
                 const v4i w = unpack_tern(word_of(st.w[u][j], t));
 #pragma unroll
                 for (int b = 0; b < RB; b++) {
-                    const v4i a = ok ? st.a[u][b][t] : v4i{0, 0, 0, 0};
+                    const v4i a = ok ? xa[b][t] : v4i{0, 0, 0, 0};
                     acc[b][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, w, acc[b][j], 0, 0, 0);
                 }
             }
     }
 }
 
-template <int NBLK, int WAVES, int U, int RB, int OUT>
+template <int NBLK, int WAVES, int U, int RB, int OUT, bool XT>
 __global__ __launch_bounds__(WAVES * 64) void w2a8_gemv_kernel(const int8_t *__restrict__ xq,
                                                                const float *__restrict__ pts,
                                                                const int32_t *__restrict__ rowsum,
@@ -462,7 +481,10 @@ __global__ __launch_bounds__(WAVES * 64) void w2a8_gemv_kernel(const int8_t *__r
                                                                int64_t m, int64_t n, int64_t k,
                                                                void *__restrict__ out) {
     __shared__ v4i red[WAVES][RB * NBLK][kWave];
+    // XT: x reaches the lanes through each wave's LDS block (whole-line loads)
+    __shared__ __attribute__((aligned(16))) uint8_t xlds[XT ? WAVES : 1][XT ? 16 * RB * kRow256Pitch : 16];
     const int lane = threadIdx.x % kWave, wave = wave_id();
+    uint8_t *xb = xlds[XT ? wave : 0];
     const int64_t nb0 = (int64_t)blockIdx.x * NBLK;
     const int64_t nblocks = n / 16, kblocks = k / 256;
     const int fr = lane % 16;
@@ -501,15 +523,17 @@ __global__ __launch_bounds__(WAVES * 64) void w2a8_gemv_kernel(const int8_t *__r
     constexpr int64_t step = (int64_t)WAVES * U;
     GemvStage<NBLK, U, RB> s0, s1;
     int64_t kb = wave;
-    gemv_load<NBLK, WAVES, U, RB>(s0, xrow, packed, kb, nb0, nblocks, kblocks, lane, row_live);
+    gemv_load<NBLK, WAVES, U, RB, XT>(s0, xrow, packed, kb, nb0, nblocks, kblocks, lane, row_live, xq, m, k);
     while (true) {
         const int64_t kb1 = kb + step;
-        if (kb1 < kblocks) gemv_load<NBLK, WAVES, U, RB>(s1, xrow, packed, kb1, nb0, nblocks, kblocks, lane, row_live);
-        gemv_compute<NBLK, WAVES, U, RB>(s0, acc, kb, kblocks);
+        if (kb1 < kblocks)
+            gemv_load<NBLK, WAVES, U, RB, XT>(s1, xrow, packed, kb1, nb0, nblocks, kblocks, lane, row_live, xq, m, k);
+        gemv_compute<NBLK, WAVES, U, RB, XT>(s0, acc, kb, kblocks, xb, lane);
         if (kb1 >= kblocks) break;
         const int64_t kb2 = kb1 + step;
-        if (kb2 < kblocks) gemv_load<NBLK, WAVES, U, RB>(s0, xrow, packed, kb2, nb0, nblocks, kblocks, lane, row_live);
-        gemv_compute<NBLK, WAVES, U, RB>(s1, acc, kb1, kblocks);
+        if (kb2 < kblocks)
+            gemv_load<NBLK, WAVES, U, RB, XT>(s0, xrow, packed, kb2, nb0, nblocks, kblocks, lane, row_live, xq, m, k);
+        gemv_compute<NBLK, WAVES, U, RB, XT>(s1, acc, kb1, kblocks, xb, lane);
         if (kb2 >= kblocks) break;
         kb = kb2;
     }
@@ -550,13 +574,13 @@ __global__ __launch_bounds__(WAVES * 64) void w2a8_gemv_kernel(const int8_t *__r
     }
 }
 
-template <int NBLK, int WAVES, int U, int RB, int OUT>
+template <int NBLK, int WAVES, int U, int RB, int OUT, bool XT = false>
 hipError_t launch_gemv(const int8_t *xq, const float *pts, const int32_t *rowsum, const uint32_t *packed,
                        const double *gamma, const float *bias, int64_t m, int64_t n, int64_t k, void *out,
                        hipStream_t st) {
     const int64_t nblocks = n / 16;
     const unsigned grid = (unsigned)((nblocks + NBLK - 1) / NBLK);
-    hipLaunchKernelGGL((w2a8_gemv_kernel<NBLK, WAVES, U, RB, OUT>), dim3(grid), dim3(WAVES * 64), 0, st, xq,
+    hipLaunchKernelGGL((w2a8_gemv_kernel<NBLK, WAVES, U, RB, OUT, XT>), dim3(grid), dim3(WAVES * 64), 0, st, xq,
                        pts, rowsum, packed, gamma, bias, m, n, k, out);
     return hipGetLastError();
 }
@@ -593,8 +617,9 @@ hipError_t launch_out(const int8_t *xq, const float *pts, const int32_t *rowsum,
         // Measured on MI355X at k=8192, n=28672 with the weights streamed from
         // HBM, 8 waves and one k block per register stage: 4 column blocks per
         // workgroup up to m = 4, 7 above (1792 column blocks = 256 workgroups).
+        // Above m = 4, x moves in whole cache lines through LDS.
         if (m <= 4) return launch_gemv<4, 8, 1, 1, OUT>(xq, pts, rowsum, packed, gamma, bias, m, n, k, out, st);
-        return launch_gemv<7, 8, 1, 1, OUT>(xq, pts, rowsum, packed, gamma, bias, m, n, k, out, st);
+        return launch_gemv<7, 8, 1, 1, OUT, true>(xq, pts, rowsum, packed, gamma, bias, m, n, k, out, st);
     }
     if (m >= XBM) {
         const int tiles_m = (int)((m + XBM - 1) / XBM), tiles_n = (int)((n + XBN - 1) / XBN);

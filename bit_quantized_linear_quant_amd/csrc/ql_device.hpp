@@ -59,6 +59,42 @@ __device__ __forceinline__ uint4 load16_stream(const void *p) {
     return make_uint4(t[0], t[1], t[2], t[3]);
 }
 
+// Operand rows of 256 bytes (one k block), 16 bytes per lane per load.  A
+// matrix-core fragment gives lane (r, q) = (lane % 16, lane / 16) the 16-byte
+// pieces 4q + t (t = 0..3) of row r, so loading fragments directly makes one
+// load instruction touch 32 cache lines and use a quarter of each.  Instead
+// load t of row block b gives lane (r, q) piece r of row 16b + 4t + q (whole
+// lines), and this turns those pieces into fragments through the wave's own
+// LDS block xb (16 RB rows at kRow256Pitch bytes, 16 more than a row so that
+// the fragment reads of 16 rows fall in distinct banks).  Only the wave
+// touches its block and LDS operations of one wave complete in issue order,
+// so wave-scope fences (which keep the compiler from moving the reads above
+// the writes, or the next call's writes above these reads) are all the
+// ordering needed.
+constexpr int kRow256Pitch = 272;
+
+template <int RB, typename T>
+__device__ __forceinline__ void rows256_to_fragments(const T (&in)[RB][4], T (&frag)[RB][4], uint8_t *xb, int lane) {
+    static_assert(sizeof(T) == 16, "16-byte pieces");
+    const int fr = lane % 16, q = lane / 16;
+#pragma unroll
+    for (int b = 0; b < RB; b++)
+#pragma unroll
+        for (int t = 0; t < 4; t++)
+            *reinterpret_cast<T *>(xb + (16 * b + 4 * t + q) * kRow256Pitch + 16 * fr) = in[b][t];
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+    for (int b = 0; b < RB; b++)
+#pragma unroll
+        for (int t = 0; t < 4; t++)
+            frag[b][t] = *reinterpret_cast<const T *>(xb + (16 * b + fr) * kRow256Pitch + 64 * q + 16 * t);
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
 // Workgroup id -> (tile row, tile column) for a grid of tiles_m x tiles_n
 // output tiles.  The hardware hands consecutive workgroup ids to the 8 XCDs in
 // turn; ids are first regrouped so each XCD receives a contiguous range of
