@@ -40,7 +40,7 @@ _lib = None
 
 
 # QL_ABI_VERSION of include/qlinear.h that the argument lists below follow.
-ABI_VERSION = 4
+ABI_VERSION = 5
 
 
 class QLinearError(RuntimeError):
@@ -79,6 +79,8 @@ def lib() -> ctypes.CDLL:
             "qlinear_gemm_w2a8": (i32, [vp, vp, vp, vp, vp, vp, i64, i64, i64, i32, vp, vp]),
             "qlinear_gemm_w4a8_grouped": (i32, [vp, i32, vp, vp, vp, vp, i64, i64, i64, i64, vp, i32, vp,
                                                 vp]),
+            "qlinear_gemm_w4a8_grouped_batched": (i32, [i64, vp, i32, vp, vp, vp, vp, i64, i64, i64, i64, vp,
+                                                        i32, vp, vp]),
             "qlinear_gemm_a4w4_codes": (i32, [vp, vp, vp, vp, f32, i64, i64, i64, i32, vp, vp]),
             "qlinear_gemm_a4w4": (i32, [vp, vp, i32, vp, vp, f32, i64, i64, i64, i32, vp, vp, sz, vp]),
             "qlinear_quant_a4w4_operand": (i32, [vp, i32, i64, i64, vp, f32, vp, vp]),
@@ -302,6 +304,35 @@ def qlinear_gemm_w4a8_grouped(x, packed_w, scales, packed_zeros, group_size, n, 
         _ptr(x), _TORCH_TO_QL[x.dtype], _ptr(per_token_scale), _ptr(packed_w), _ptr(scales),
         _ptr(packed_zeros), group_size, m, n, k, _ptr(bias), _TORCH_TO_QL[out_dtype], _ptr(out),
         _stream(x)))
+    return out
+
+
+def qlinear_gemm_w4a8_grouped_batched(x, packed_w, scales, packed_zeros, group_size, n,
+                                      out_dtype=torch.float16, out=None, per_token_scale=None, bias=None):
+    """``batch`` independent grouped INT4 products: ``x[batch,m,k]`` (fp16, or
+    int8 codes with ``per_token_scale[batch,m]``), each slice with its own
+    packed weights ``[batch, n*k/8]`` words, fp16 scales ``[batch, n,
+    k/group_size]``, packed zero-points and optional fp32 ``bias[batch,n]``;
+    returns ``out[batch,m,n]``.
+    """
+    _gpu(x, "x")
+    batch, m, k = x.shape
+    if x.dtype == torch.int8:
+        _need(_gpu(per_token_scale, "per_token_scale", torch.float32), 4 * batch * m, "per_token_scale")
+    _gpu(packed_w, "packed_w")
+    _gpu(scales, "scales", torch.float16)
+    _gpu(packed_zeros, "packed_zeros")
+    if group_size > 0 and k % group_size == 0:
+        _need(packed_w, batch * n * k // 2, "packed_w")
+        _need(scales, 2 * batch * n * (k // group_size), "scales")
+        _need(packed_zeros, batch * n * (k // group_size) // 2, "packed_zeros")
+    if bias is not None:
+        _need(_gpu(bias, "bias", torch.float32), 4 * batch * n, "bias")
+    out = _empty((batch, m, n), out_dtype, x) if out is None else _gpu(out, "out", out_dtype)
+    _need(out, batch * m * n * out.element_size(), "out")
+    _check("qlinear_gemm_w4a8_grouped_batched", lib().qlinear_gemm_w4a8_grouped_batched(
+        batch, _ptr(x), _TORCH_TO_QL[x.dtype], _ptr(per_token_scale), _ptr(packed_w), _ptr(scales),
+        _ptr(packed_zeros), group_size, m, n, k, _ptr(bias), _TORCH_TO_QL[out_dtype], _ptr(out), _stream(x)))
     return out
 
 

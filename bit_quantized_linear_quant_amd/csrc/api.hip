@@ -181,18 +181,17 @@ ql_status qlinear_gemm_w2a8(const int8_t *xq, const float *per_token_scale, cons
                                            as_stream(stream)));
 }
 
-ql_status qlinear_gemm_w4a8_grouped(const void *x, ql_dtype x_dtype, const float *per_token_scale,
-                                    const uint32_t *packed_w, const uint16_t *scales,
-                                    const uint32_t *packed_zeros, int64_t group_size, int64_t m, int64_t n,
-                                    int64_t k, const float *bias, ql_dtype out_dtype, void *out,
-                                    void *stream) {
+static ql_status grouped_int4(int64_t batch, const void *x, ql_dtype x_dtype, const float *per_token_scale,
+                              const uint32_t *packed_w, const uint16_t *scales, const uint32_t *packed_zeros,
+                              int64_t group_size, int64_t m, int64_t n, int64_t k, const float *bias,
+                              ql_dtype out_dtype, void *out, void *stream) {
     if (!x || !packed_w || !scales || !packed_zeros || !out) return QL_ERR_NULL;
     if (x_dtype != QL_F16 && x_dtype != QL_I8) return QL_ERR_DTYPE;
     if (x_dtype == QL_I8 && !per_token_scale) return QL_ERR_NULL;
     if (out_dtype != QL_F16 && out_dtype != QL_F32 && !(x_dtype == QL_I8 && out_dtype == QL_BF16))
         return QL_ERR_DTYPE;
     if (m < 1 || n < 16 || k < 128 || n % 16 || k % 128 || group_size < 128 || group_size % 128 ||
-        k % group_size)
+        k % group_size || batch < 1 || batch > 65535)
         return QL_ERR_SHAPE;
     if (!aligned16(x) || !aligned16(packed_w) || !aligned16(scales) || !aligned16(packed_zeros) ||
         !aligned16(out) || !aligned16(bias) || (per_token_scale && !aligned16(per_token_scale)))
@@ -201,10 +200,28 @@ ql_status qlinear_gemm_w4a8_grouped(const void *x, ql_dtype x_dtype, const float
     if (x_dtype == QL_I8)
         return hip_status(ql::launch_gemm_int4_grouped_i8(static_cast<const int8_t *>(x), per_token_scale,
                                                           packed_w, scales, packed_zeros, bias, group_size, m, n,
-                                                          k, ok, out, as_stream(stream)));
+                                                          k, ok, out, as_stream(stream), batch));
     return hip_status(ql::launch_gemm_int4_grouped(static_cast<const uint16_t *>(x), packed_w, scales,
                                                    packed_zeros, bias, group_size, m, n, k, ok, out,
-                                                   as_stream(stream)));
+                                                   as_stream(stream), batch));
+}
+
+ql_status qlinear_gemm_w4a8_grouped(const void *x, ql_dtype x_dtype, const float *per_token_scale,
+                                    const uint32_t *packed_w, const uint16_t *scales,
+                                    const uint32_t *packed_zeros, int64_t group_size, int64_t m, int64_t n,
+                                    int64_t k, const float *bias, ql_dtype out_dtype, void *out,
+                                    void *stream) {
+    return grouped_int4(1, x, x_dtype, per_token_scale, packed_w, scales, packed_zeros, group_size, m, n, k, bias,
+                        out_dtype, out, stream);
+}
+
+ql_status qlinear_gemm_w4a8_grouped_batched(int64_t batch, const void *x, ql_dtype x_dtype,
+                                            const float *per_token_scale, const uint32_t *packed_w,
+                                            const uint16_t *scales, const uint32_t *packed_zeros,
+                                            int64_t group_size, int64_t m, int64_t n, int64_t k,
+                                            const float *bias, ql_dtype out_dtype, void *out, void *stream) {
+    return grouped_int4(batch, x, x_dtype, per_token_scale, packed_w, scales, packed_zeros, group_size, m, n, k,
+                        bias, out_dtype, out, stream);
 }
 
 ql_status qlinear_gemm_a4w4_codes(const int8_t *xq, const int8_t *wq, const float *scale_a,

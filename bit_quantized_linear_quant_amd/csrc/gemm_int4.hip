@@ -139,6 +139,14 @@ __global__ __launch_bounds__(WAVES * 64) void int4_grouped_kernel(const uint16_t
     const int64_t nblocks = n / 16, kblocks = k / 128, groups = k / group_size;
     const int fr = lane % 16;
     uint8_t *xb = xlds[wave];
+    // Batched launches: blockIdx.z selects one independent product.
+    const int64_t z = blockIdx.z;
+    x += z * m * k;
+    packed_w += z * (n * k / 8);
+    scales += z * n * groups;
+    packed_z += z * groups * (n / 8);
+    if (bias) bias += z * n;
+    const int64_t obase = z * m * n;
 
     v4f acc[RB][NBLK];
 #pragma unroll
@@ -200,7 +208,7 @@ __global__ __launch_bounds__(WAVES * 64) void int4_grouped_kernel(const uint16_t
 #pragma unroll
         for (int r = 0; r < 4; r++) {
             const int64_t row = row0 + b * 16 + 4 * (lane / 16) + r;
-            if (row < m) store_out<OUT>(out, row * n + col, bias ? __fadd_rn(s[r], cb) : s[r]);
+            if (row < m) store_out<OUT>(out, obase + row * n + col, bias ? __fadd_rn(s[r], cb) : s[r]);
         }
     }
 }
@@ -211,9 +219,9 @@ constexpr int kAllIn = 4;
 template <int NBLK, int WAVES, int RB, int OUT>
 hipError_t launch_cfg(const uint16_t *x, const uint32_t *packed_w, const uint16_t *scales,
                       const uint32_t *packed_z, const float *bias, int64_t group_size, int64_t m, int64_t n, int64_t k,
-                      void *out, hipStream_t st) {
+                      void *out, hipStream_t st, int64_t batch) {
     const int64_t nblocks = n / 16;
-    dim3 grid((unsigned)((nblocks + NBLK - 1) / NBLK), (unsigned)((m + 16 * RB - 1) / (16 * RB)));
+    dim3 grid((unsigned)((nblocks + NBLK - 1) / NBLK), (unsigned)((m + 16 * RB - 1) / (16 * RB)), (unsigned)batch);
     // With two row blocks, four stages of x fragments do not fit beside the
     // weights in registers: those launches keep the two-stage pipeline.
     if constexpr (RB == 1) {
@@ -231,11 +239,11 @@ hipError_t launch_cfg(const uint16_t *x, const uint32_t *packed_w, const uint16_
 template <int OUT>
 hipError_t launch_t(const uint16_t *x, const uint32_t *packed_w, const uint16_t *scales,
                     const uint32_t *packed_z, const float *bias, int64_t group_size, int64_t m, int64_t n, int64_t k,
-                    void *out, hipStream_t st) {
+                    void *out, hipStream_t st, int64_t batch) {
     // m <= 16 needs one 16-row MFMA block; larger m takes 32-row slices so
     // every unpacked weight fragment serves two row blocks.
-    if (m <= 16) return launch_cfg<3, 8, 1, OUT>(x, packed_w, scales, packed_z, bias, group_size, m, n, k, out, st);
-    return launch_cfg<3, 8, 2, OUT>(x, packed_w, scales, packed_z, bias, group_size, m, n, k, out, st);
+    if (m <= 16) return launch_cfg<3, 8, 1, OUT>(x, packed_w, scales, packed_z, bias, group_size, m, n, k, out, st, batch);
+    return launch_cfg<3, 8, 2, OUT>(x, packed_w, scales, packed_z, bias, group_size, m, n, k, out, st, batch);
 }
 
 // ---------------------------------------------------------------------------
@@ -370,6 +378,15 @@ __global__ __launch_bounds__(WAVES * 64) void int4_grouped_i8_kernel(const int8_
     const int64_t nblocks = n / 16, kblocks = k / 128, groups = k / group_size;
     const int fr = lane % 16;
     uint8_t *xb = xlds[wave];
+    // Batched launches: blockIdx.z selects one independent product.
+    const int64_t z = blockIdx.z;
+    xq += z * m * k;
+    pts += z * m;
+    packed_w += z * (n * k / 8);
+    scales += z * n * groups;
+    packed_z += z * groups * (n / 8);
+    if (bias) bias += z * n;
+    const int64_t obase = z * m * n;
     float prow[RB][4];
 #pragma unroll
     for (int b = 0; b < RB; b++) {
@@ -437,7 +454,7 @@ __global__ __launch_bounds__(WAVES * 64) void int4_grouped_i8_kernel(const int8_
         for (int r = 0; r < 4; r++) {
             const int64_t row = row0 + b * 16 + 4 * (lane / 16) + r;
             const float y = __fmul_rn(s[r], prow[b][r]);
-            if (row < m) store_out<OUT>(out, row * n + col, bias ? __fadd_rn(y, cb) : y);
+            if (row < m) store_out<OUT>(out, obase + row * n + col, bias ? __fadd_rn(y, cb) : y);
         }
     }
 }
@@ -445,9 +462,9 @@ __global__ __launch_bounds__(WAVES * 64) void int4_grouped_i8_kernel(const int8_
 template <int NBLK, int WAVES, int RB, int OUT>
 hipError_t launch_cfg_i8(const int8_t *xq, const float *pts, const uint32_t *packed_w, const uint16_t *scales,
                          const uint32_t *packed_z, const float *bias, int64_t group_size, int64_t m, int64_t n, int64_t k, void *out,
-                         hipStream_t st) {
+                         hipStream_t st, int64_t batch) {
     const int64_t nblocks = n / 16;
-    dim3 grid((unsigned)((nblocks + NBLK - 1) / NBLK), (unsigned)((m + 16 * RB - 1) / (16 * RB)));
+    dim3 grid((unsigned)((nblocks + NBLK - 1) / NBLK), (unsigned)((m + 16 * RB - 1) / (16 * RB)), (unsigned)batch);
     if (k / 128 <= (int64_t)WAVES * kAllIn)
         hipLaunchKernelGGL((int4_grouped_i8_kernel<NBLK, WAVES, RB, OUT, kAllIn>), grid, dim3(WAVES * 64), 0, st, xq,
                            pts, packed_w, scales, packed_z, bias, group_size, m, n, k, out);
@@ -460,21 +477,21 @@ hipError_t launch_cfg_i8(const int8_t *xq, const float *pts, const uint32_t *pac
 template <int OUT>
 hipError_t launch_i8_t(const int8_t *xq, const float *pts, const uint32_t *packed_w, const uint16_t *scales,
                        const uint32_t *packed_z, const float *bias, int64_t group_size, int64_t m, int64_t n, int64_t k, void *out,
-                       hipStream_t st) {
+                       hipStream_t st, int64_t batch) {
     if (m <= 16)
-        return launch_cfg_i8<3, 8, 1, OUT>(xq, pts, packed_w, scales, packed_z, bias, group_size, m, n, k, out, st);
-    return launch_cfg_i8<3, 8, 2, OUT>(xq, pts, packed_w, scales, packed_z, bias, group_size, m, n, k, out, st);
+        return launch_cfg_i8<3, 8, 1, OUT>(xq, pts, packed_w, scales, packed_z, bias, group_size, m, n, k, out, st, batch);
+    return launch_cfg_i8<3, 8, 2, OUT>(xq, pts, packed_w, scales, packed_z, bias, group_size, m, n, k, out, st, batch);
 }
 
 }  // namespace
 
 hipError_t launch_gemm_int4_grouped(const uint16_t *x, const uint32_t *packed_w, const uint16_t *scales,
                                     const uint32_t *packed_zeros, const float *bias, int64_t group_size,
-                                    int64_t m, int64_t n, int64_t k, int out_kind, void *out, hipStream_t st) {
-    if ((m + 31) / 32 > 65535) return hipErrorInvalidValue;
+                                    int64_t m, int64_t n, int64_t k, int out_kind, void *out, hipStream_t st, int64_t batch) {
+    if ((m + 31) / 32 > 65535 || batch < 1 || batch > 65535) return hipErrorInvalidValue;
     if (out_kind == OUT_F32)
-        return launch_t<OUT_F32>(x, packed_w, scales, packed_zeros, bias, group_size, m, n, k, out, st);
-    return launch_t<OUT_F16>(x, packed_w, scales, packed_zeros, bias, group_size, m, n, k, out, st);
+        return launch_t<OUT_F32>(x, packed_w, scales, packed_zeros, bias, group_size, m, n, k, out, st, batch);
+    return launch_t<OUT_F16>(x, packed_w, scales, packed_zeros, bias, group_size, m, n, k, out, st, batch);
 }
 
 }  // namespace ql
@@ -484,12 +501,12 @@ namespace ql {
 hipError_t launch_gemm_int4_grouped_i8(const int8_t *xq, const float *pts, const uint32_t *packed_w,
                                        const uint16_t *scales, const uint32_t *packed_zeros, const float *bias,
                                        int64_t group_size, int64_t m, int64_t n, int64_t k, int out_kind, void *out,
-                                       hipStream_t st) {
-    if ((m + 31) / 32 > 65535) return hipErrorInvalidValue;
+                                       hipStream_t st, int64_t batch) {
+    if ((m + 31) / 32 > 65535 || batch < 1 || batch > 65535) return hipErrorInvalidValue;
     switch (out_kind) {
-        case OUT_F32: return launch_i8_t<OUT_F32>(xq, pts, packed_w, scales, packed_zeros, bias, group_size, m, n, k, out, st);
-        case OUT_BF16: return launch_i8_t<OUT_BF16>(xq, pts, packed_w, scales, packed_zeros, bias, group_size, m, n, k, out, st);
-        default: return launch_i8_t<OUT_F16>(xq, pts, packed_w, scales, packed_zeros, bias, group_size, m, n, k, out, st);
+        case OUT_F32: return launch_i8_t<OUT_F32>(xq, pts, packed_w, scales, packed_zeros, bias, group_size, m, n, k, out, st, batch);
+        case OUT_BF16: return launch_i8_t<OUT_BF16>(xq, pts, packed_w, scales, packed_zeros, bias, group_size, m, n, k, out, st, batch);
+        default: return launch_i8_t<OUT_F16>(xq, pts, packed_w, scales, packed_zeros, bias, group_size, m, n, k, out, st, batch);
     }
 }
 

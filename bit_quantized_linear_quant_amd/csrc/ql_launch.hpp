@@ -84,14 +84,15 @@ hipError_t launch_gemm_w2a8(const int8_t *xq, const float *pts, const int32_t *r
                             const uint32_t *packed, const double *gamma, const float *bias, int64_t m,
                             int64_t n, int64_t k, int out_kind, void *out, hipStream_t st);
 
-// gemm_int4.hip: grouped affine INT4 with fp16 activations.
+// gemm_int4.hip: grouped affine INT4 with fp16 activations or int8 codes;
+// batch independent products laid out back to back (grid z).
 hipError_t launch_gemm_int4_grouped(const uint16_t *x, const uint32_t *packed_w,
                                     const uint16_t *scales, const uint32_t *packed_zeros, const float *bias,
                                     int64_t group_size, int64_t m, int64_t n, int64_t k,
-                                    int out_kind, void *out, hipStream_t st);
+                                    int out_kind, void *out, hipStream_t st, int64_t batch = 1);
 hipError_t launch_gemm_int4_grouped_i8(const int8_t *xq, const float *pts, const uint32_t *packed_w,
                                        const uint16_t *scales, const uint32_t *packed_zeros, const float *bias,
                                        int64_t group_size, int64_t m, int64_t n, int64_t k, int out_kind, void *out,
-                                       hipStream_t st);
+                                       hipStream_t st, int64_t batch = 1);
 
 }  // namespace ql

@@ -47,7 +47,7 @@
 extern "C" {
 #endif
 
-#define QL_ABI_VERSION 4
+#define QL_ABI_VERSION 5
 /* Version of the 2-bit ternary weight layout written by qlinear_pack_ternary. */
 #define QL_TERNARY_PACK_V1 1
 /* Version of the 4-bit weight layout written by qlinear_pack_int4. */
@@ -285,6 +285,27 @@ ql_status qlinear_gemm_w4a8_grouped(const void *x, ql_dtype x_dtype,
                                     const uint32_t *packed_zeros, int64_t group_size,
                                     int64_t m, int64_t n, int64_t k, const float *bias,
                                     ql_dtype out_dtype, void *out, void *stream);
+
+/*
+ * Batched grouped affine INT4 linear ([L4] lists a batched form of the grouped
+ * linear among the module's exports, by name only; read here as batch
+ * independent products of qlinear_gemm_w4a8_grouped, one per slice):
+ *   for b in [0, batch): the qlinear_gemm_w4a8_grouped product of
+ *     x + b*m*k elements ([batch, m, k]), per_token_scale + b*m (QL_I8),
+ *     packed_w + b*n*k/8 words, scales + b*n*(k/group_size),
+ *     packed_zeros + b*(k/group_size)*n/8 words, bias + b*n (if not NULL),
+ *     written to out + b*m*n elements ([batch, m, n]).
+ * Every slice holds its own weights; the argument rules are those of
+ * qlinear_gemm_w4a8_grouped, plus 1 <= batch <= 65535 (else QL_ERR_SHAPE).
+ * Each slice's result equals a separate qlinear_gemm_w4a8_grouped call on
+ * that slice, bit for bit.
+ */
+ql_status qlinear_gemm_w4a8_grouped_batched(int64_t batch, const void *x, ql_dtype x_dtype,
+                                            const float *per_token_scale,
+                                            const uint32_t *packed_w, const uint16_t *scales,
+                                            const uint32_t *packed_zeros, int64_t group_size,
+                                            int64_t m, int64_t n, int64_t k, const float *bias,
+                                            ql_dtype out_dtype, void *out, void *stream);
 
 /*
  * A4W4 product on 4-bit codes held in int8 ([Q4] forward, second half):

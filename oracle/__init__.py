@@ -286,6 +286,23 @@ def w8a8_batched(x, w, layout_nk: bool, pts, deq):
     return np.stack(accs), np.stack(ys)
 
 
+def grouped_int4_batched(x, q, s, z, group_size: int, pts=None):
+    """``batch`` independent grouped INT4 products ("linear_4bit/mod.rs" lists
+    a batched grouped linear by name only; each slice has its own weights):
+    ``grouped_int4`` of every slice, or ``grouped_int4_i8`` when the per-token
+    scales ``pts[batch, m]`` of int8 codes are given.  Returns ``(y, bound)``
+    of shape ``[batch, m, n]``."""
+    ys, bs = [], []
+    for b in range(len(x)):
+        if pts is None:
+            y, bd = grouped_int4(x[b], q[b], s[b], z[b], group_size)
+        else:
+            y, bd = grouped_int4_i8(x[b], pts[b], q[b], s[b], z[b], group_size)
+        ys.append(y)
+        bs.append(bd)
+    return np.stack(ys), np.stack(bs)
+
+
 def w2a8(xq, pts, codes, gamma: float):
     """BitLinear product on int8 activation codes and ternary codes ``[n,k]``.
 

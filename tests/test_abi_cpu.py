@@ -40,7 +40,7 @@ def test_exports_every_declared_symbol(L):
 
 
 def test_abi_version_and_status_strings(L):
-    assert ql.qlinear_abi_version() == ql.ABI_VERSION == 4
+    assert ql.qlinear_abi_version() == ql.ABI_VERSION == 5
     for code, name in ql.STATUS.items():
         s = ql.qlinear_status_string(code)
         assert isinstance(s, str) and s
@@ -123,6 +123,12 @@ def test_gemm_validation(L):
     assert g4(A, ql.QL_I8, U, A, A, A, 128, 1, 16, 128, NULL, ql.QL_F16, A, NULL) == -4
     assert g4(A, ql.QL_I8, A, A, A, A, 128, 1, 16, 128, NULL, ql.QL_I32, A, NULL) == -3
     assert g4(A, ql.QL_U8, A, A, A, A, 128, 1, 16, 128, NULL, ql.QL_F16, A, NULL) == -3
+    gb = L.qlinear_gemm_w4a8_grouped_batched
+    assert gb(0, A, ql.QL_F16, NULL, A, A, A, 128, 1, 16, 128, NULL, ql.QL_F16, A, NULL) == -2      # batch 0
+    assert gb(65536, A, ql.QL_F16, NULL, A, A, A, 128, 1, 16, 128, NULL, ql.QL_F16, A, NULL) == -2  # grid z limit
+    assert gb(2, A, ql.QL_I8, NULL, A, A, A, 128, 1, 16, 128, NULL, ql.QL_F16, A, NULL) == -1       # needs pts
+    assert gb(2, A, ql.QL_F16, NULL, A, A, A, 128, 1, 24, 128, NULL, ql.QL_F16, A, NULL) == -2      # n % 16
+    assert gb(2, A, ql.QL_F16, NULL, A, A, A, 128, 1, 16, 128, U, ql.QL_F16, A, NULL) == -4         # bias alignment
     assert g4(A, ql.QL_F16, NULL, A, A, A, 64, 1, 16, 128, NULL, ql.QL_F16, A, NULL) == -2
     assert g4(A, ql.QL_F16, NULL, A, A, A, 256, 1, 16, 384, NULL, ql.QL_F16, A, NULL) == -2
     assert g4(A, ql.QL_F16, NULL, A, A, A, 128, 1, 16, 128, U, ql.QL_F16, A, NULL) == -4  # bias alignment

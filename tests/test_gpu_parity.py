@@ -383,6 +383,48 @@ def test_grouped_int4_i8_parity(m, n, k, g):
         assert torch.equal(outs[dt], outs[torch.float32].to(dt))
 
 
+@pytest.mark.parametrize("batch,m,n,k,g,int8_codes,with_bias", [
+    (3, 5, 400, 512, 128, False, False), (2, 33, 160, 768, 256, False, True),
+    (3, 16, 128, 256, 128, True, False), (2, 40, 64, 384, 128, True, True)])
+def test_grouped_int4_batched_parity(batch, m, n, k, g, int8_codes, with_bias):
+    """Every slice within the grouped bar of the oracle, and bit-equal to a separate
+    non-batched call on that slice."""
+    ds = [synthetic.grouped_int4(m, n, k, g, seed=1100 + 7 * b + m) for b in range(batch)]
+    q = torch.stack([d["q"] for d in ds])
+    s = torch.stack([d["s"] for d in ds])
+    z = torch.stack([d["z"] for d in ds])
+    if int8_codes:
+        r = synthetic.rng(1200 + m)
+        x = torch.from_numpy(r.integers(-127, 128, (batch, m, k), dtype=np.int8))
+        pts = torch.from_numpy(r.uniform(1e-3, 1e-2, (batch, m)).astype(np.float32))
+        y, bound = oracle.grouped_int4_batched(x.numpy(), q.numpy(), s.float().numpy(), z.numpy(), g,
+                                               pts=pts.numpy())
+    else:
+        x = torch.stack([d["x"] for d in ds])
+        pts = None
+        y, bound = oracle.grouped_int4_batched(x.float().numpy(), q.numpy(), s.float().numpy(), z.numpy(), g)
+    bias = torch.from_numpy(synthetic.rng(1300 + m).uniform(-1, 1, (batch, n)).astype(np.float32)) \
+        if with_bias else None
+    pw = torch.stack([ql.qlinear_pack_int4(_cuda(q[b]), ql.QL_INT4_WEIGHT) for b in range(batch)])
+    pz = torch.stack([ql.qlinear_pack_int4(_cuda(z[b]), ql.QL_INT4_ZEROS) for b in range(batch)])
+    cp = _cuda(pts) if int8_codes else None
+    cb = _cuda(bias) if with_bias else None
+    o = poison((batch, m, n), torch.float32)
+    ql.qlinear_gemm_w4a8_grouped_batched(_cuda(x), pw, _cuda(s), pz, g, n, out_dtype=torch.float32, out=o,
+                                         per_token_scale=cp, bias=cb)
+    singles = [ql.qlinear_gemm_w4a8_grouped(_cuda(x[b]), pw[b], _cuda(s[b]), pz[b], g, n,
+                                            out_dtype=torch.float32,
+                                            per_token_scale=None if cp is None else cp[b],
+                                            bias=None if cb is None else cb[b]) for b in range(batch)]
+    _sync()
+    for b in range(batch):
+        assert torch.equal(o[b], singles[b]), f"slice {b} differs from its separate call"
+    ref = y + (bias.numpy().astype(np.float64)[:, None, :] if with_bias else 0.0)
+    err = np.abs(to_np(o).astype(np.float64) - ref)
+    tol = 1e-3 * bound + (2.0 ** -23 * np.abs(ref) if with_bias else 0.0)
+    assert np.all(err <= tol), f"batched grouped: max err/bound {np.max(err / bound)}"
+
+
 def test_grouped_int4_i8_zero_point_equals_code_gives_zero():
     m, n, k, g = 4, 32, 256, 128
     xq, pts, _, s, z = _grouped_i8_inputs(m, n, k, g, seed=19)

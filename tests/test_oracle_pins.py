@@ -111,6 +111,30 @@ def test_batched_is_independent_products(layout_nk, per_batch_deq):
     np.testing.assert_allclose(y, yref, rtol=1e-15, atol=0)
 
 
+@pytest.mark.parametrize("int8_codes", [False, True])
+def test_grouped_batched_is_independent_products(int8_codes):
+    """Each slice is its own product: fp64 dequantize-then-matmul per slice
+    with numpy einsum, the per-token scale applied to the int8 codes' rows."""
+    batch, m, n, k, g = 3, 4, 16, 256, 128
+    ds = [synthetic.grouped_int4(m, n, k, g, seed=60 + b) for b in range(batch)]
+    q = np.stack([d["q"].numpy() for d in ds])
+    s = np.stack([d["s"].float().numpy() for d in ds]).astype(np.float64)
+    z = np.stack([d["z"].numpy() for d in ds])
+    if int8_codes:
+        r = synthetic.rng(66)
+        x = r.integers(-127, 128, (batch, m, k), dtype=np.int8)
+        pts = r.uniform(1e-3, 1e-2, (batch, m)).astype(np.float32)
+        y, _ = oracle.grouped_int4_batched(x, q, s, z, g, pts=pts)
+        xd = x.astype(np.float64) * pts.astype(np.float64)[:, :, None]
+    else:
+        x = np.stack([d["x"].float().numpy() for d in ds])
+        y, _ = oracle.grouped_int4_batched(x, q, s, z, g)
+        xd = x.astype(np.float64)
+    w = (q.astype(np.float64) - np.repeat(z, g, axis=2)) * np.repeat(s, g, axis=2)  # [batch, n, k]
+    ref = np.einsum("bmk,bnk->bmn", xd, w)
+    np.testing.assert_allclose(y, ref, rtol=1e-12, atol=1e-12)
+
+
 def test_gemm_int32_overflow_is_reported():
     """The definition asserts the accumulator fits int32: (-128)^2 * 2^17 = 2^31 does not."""
     k = 1 << 17
