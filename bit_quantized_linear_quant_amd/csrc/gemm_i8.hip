@@ -598,15 +598,32 @@ struct GemvStage {
 
 // All loads of k block kb from clamped, in-bounds addresses; a step past
 // the end is masked at compute time.
-template <int NBLK, int SPS, int RB>
+//
+// XT (SPS even, k % 128 == 0): x moves in whole cache lines.  Steps 2i and
+// 2i + 1 cover 128 bytes of each row; their loads give lane l piece l % 8 of
+// row 16b + 8u + l / 8 (u = 0, 1), and gemv_compute turns them into
+// fragments through the wave's LDS block (x_pair_fragments).
+template <int NBLK, int SPS, int RB, bool XT>
 __device__ __forceinline__ void gemv_load(GemvStage<NBLK, SPS, RB> &st, const int8_t *const (&xrow)[RB],
-                                          const int8_t *const (&wrow)[NBLK], int64_t kb, int64_t nsteps) {
+                                          const int8_t *const (&wrow)[NBLK], int64_t kb, int64_t nsteps,
+                                          const int8_t *__restrict__ x, int64_t m, int64_t k, int lane) {
 #pragma unroll
     for (int t = 0; t < SPS; t++) {
         const int64_t s = kb * SPS + t;
         const int64_t off = (s < nsteps ? s : nsteps - 1) * 64;
+        if constexpr (XT) {
+            // the pair's first step, clamped to the last pair (nsteps is even)
+            const int64_t s0 = kb * SPS + (t & ~1);
+            const int64_t poff = (s0 < nsteps ? s0 : nsteps - 2) * 64;
 #pragma unroll
-        for (int b = 0; b < RB; b++) st.a[t][b] = *reinterpret_cast<const v4i *>(xrow[b] + off);
+            for (int b = 0; b < RB; b++) {
+                const int64_t r = 16 * b + 8 * (t & 1) + lane / 8;
+                st.a[t][b] = *reinterpret_cast<const v4i *>(x + (r < m ? r : 0) * k + poff + 16 * (lane % 8));
+            }
+        } else {
+#pragma unroll
+            for (int b = 0; b < RB; b++) st.a[t][b] = *reinterpret_cast<const v4i *>(xrow[b] + off);
+        }
 #pragma unroll
         for (int j = 0; j < NBLK; j++) {
             const uint4 v = load16_stream(wrow[j] + off);
@@ -615,16 +632,64 @@ __device__ __forceinline__ void gemv_load(GemvStage<NBLK, SPS, RB> &st, const in
     }
 }
 
-template <int NBLK, int SPS, int RB>
+// Row pitch of a wave's LDS block for XT: 128 bytes of x plus 16, so the
+// fragment reads of 16 rows fall in distinct banks.
+constexpr int kRow128Pitch = 144;
+
+// Whole-line pieces of steps 2i, 2i + 1 (as gemv_load leaves them) to the
+// fragments of those steps: lane (r, q) gets bytes 64u + 16q of row 16b + r.
+// Only the wave touches its block and its LDS operations complete in issue
+// order; the fences keep the compiler from reordering them.
+template <int RB>
+__device__ __forceinline__ void x_pair_fragments(const v4i (&in0b)[RB], const v4i (&in1b)[RB], v4i (&frag)[2][RB],
+                                                 uint8_t *xb, int lane) {
+#pragma unroll
+    for (int b = 0; b < RB; b++) {
+        *reinterpret_cast<v4i *>(xb + (16 * b + lane / 8) * kRow128Pitch + 16 * (lane % 8)) = in0b[b];
+        *reinterpret_cast<v4i *>(xb + (16 * b + 8 + lane / 8) * kRow128Pitch + 16 * (lane % 8)) = in1b[b];
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+    for (int u = 0; u < 2; u++)
+#pragma unroll
+        for (int b = 0; b < RB; b++)
+            frag[u][b] = *reinterpret_cast<const v4i *>(xb + (16 * b + lane % 16) * kRow128Pitch + 64 * u +
+                                                         16 * (lane / 16));
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+template <int NBLK, int SPS, int RB, bool XT>
 __device__ __forceinline__ void gemv_compute(const GemvStage<NBLK, SPS, RB> &st, v4i (&acc)[RB][NBLK], int64_t kb,
-                                             int64_t nsteps) {
+                                             int64_t nsteps, uint8_t *xb, int lane) {
+    v4i xa[SPS][RB];
+    if constexpr (XT) {
+#pragma unroll
+        for (int i = 0; i < SPS / 2; i++) {
+            v4i f[2][RB];
+            x_pair_fragments<RB>(st.a[2 * i], st.a[2 * i + 1], f, xb, lane);
+#pragma unroll
+            for (int b = 0; b < RB; b++) {
+                xa[2 * i][b] = f[0][b];
+                xa[2 * i + 1][b] = f[1][b];
+            }
+        }
+    } else {
+#pragma unroll
+        for (int t = 0; t < SPS; t++)
+#pragma unroll
+            for (int b = 0; b < RB; b++) xa[t][b] = st.a[t][b];
+    }
 #pragma unroll
     for (int t = 0; t < SPS; t++) {
         // a zero activation fragment removes a step past the end exactly
         const bool ok = kb * SPS + t < nsteps;
 #pragma unroll
         for (int b = 0; b < RB; b++) {
-            const v4i a = ok ? st.a[t][b] : v4i{0, 0, 0, 0};
+            const v4i a = ok ? xa[t][b] : v4i{0, 0, 0, 0};
 #pragma unroll
             for (int j = 0; j < NBLK; j++)
                 acc[b][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, st.w[t][j], acc[b][j], 0, 0, 0);
@@ -632,11 +697,13 @@ __device__ __forceinline__ void gemv_compute(const GemvStage<NBLK, SPS, RB> &st,
     }
 }
 
-template <int NBLK, int SPS, int RB, int EPI, int OUT>
+template <int NBLK, int SPS, int RB, int EPI, int OUT, bool XT>
 __global__ __launch_bounds__(kGvWaves * 64) void gemv_i8_kernel(Params p) {
     __shared__ v4i red[kGvWaves][RB * NBLK][kWave];
+    __shared__ __attribute__((aligned(16))) int8_t xlds[XT ? kGvWaves : 1][XT ? 16 * RB * kRow128Pitch : 16];
     to_batch(p);
     const int lane = threadIdx.x % kWave, wave = wave_id();
+    uint8_t *xb = reinterpret_cast<uint8_t *>(xlds[XT ? wave : 0]);
     const int fr = lane % 16;
     const int64_t nb0 = (int64_t)blockIdx.x * NBLK;
     const int64_t nsteps = p.k / 64, kblocks = (nsteps + SPS - 1) / SPS;
@@ -673,15 +740,15 @@ __global__ __launch_bounds__(kGvWaves * 64) void gemv_i8_kernel(Params p) {
         for (int j = 0; j < NBLK; j++) acc[b][j] = v4i{0, 0, 0, 0};
     GemvStage<NBLK, SPS, RB> s0, s1;
     int64_t kb = wave;
-    if (kb < kblocks) gemv_load<NBLK, SPS, RB>(s0, xrow, wrow, kb, nsteps);
+    if (kb < kblocks) gemv_load<NBLK, SPS, RB, XT>(s0, xrow, wrow, kb, nsteps, p.x, p.m, p.k, lane);
     while (kb < kblocks) {
         const int64_t kb1 = kb + kGvWaves;
-        if (kb1 < kblocks) gemv_load<NBLK, SPS, RB>(s1, xrow, wrow, kb1, nsteps);
-        gemv_compute<NBLK, SPS, RB>(s0, acc, kb, nsteps);
+        if (kb1 < kblocks) gemv_load<NBLK, SPS, RB, XT>(s1, xrow, wrow, kb1, nsteps, p.x, p.m, p.k, lane);
+        gemv_compute<NBLK, SPS, RB, XT>(s0, acc, kb, nsteps, xb, lane);
         if (kb1 >= kblocks) break;
         const int64_t kb2 = kb1 + kGvWaves;
-        if (kb2 < kblocks) gemv_load<NBLK, SPS, RB>(s0, xrow, wrow, kb2, nsteps);
-        gemv_compute<NBLK, SPS, RB>(s1, acc, kb1, nsteps);
+        if (kb2 < kblocks) gemv_load<NBLK, SPS, RB, XT>(s0, xrow, wrow, kb2, nsteps, p.x, p.m, p.k, lane);
+        gemv_compute<NBLK, SPS, RB, XT>(s1, acc, kb1, nsteps, xb, lane);
         kb = kb2;
     }
 
@@ -717,8 +784,16 @@ __global__ __launch_bounds__(kGvWaves * 64) void gemv_i8_kernel(Params p) {
 template <int NBLK, int SPS, int RB, int EPI, int OUT>
 hipError_t launch_gemv_t(const Params &p, int64_t batch, hipStream_t st) {
     const int64_t nblocks = (p.n + 15) / 16;
-    hipLaunchKernelGGL((gemv_i8_kernel<NBLK, SPS, RB, EPI, OUT>), dim3((unsigned)((nblocks + NBLK - 1) / NBLK), 1,
-                       (unsigned)batch), dim3(kGvWaves * 64), 0, st, p);
+    const dim3 grid((unsigned)((nblocks + NBLK - 1) / NBLK), 1, (unsigned)batch);
+    // Whole-line x loads need pairs of 64-k steps in a stage and in k, and
+    // an LDS block per wave (up to four row blocks).
+    if constexpr (SPS % 2 == 0 && RB <= 4) {
+        if (p.k % 128 == 0) {
+            hipLaunchKernelGGL((gemv_i8_kernel<NBLK, SPS, RB, EPI, OUT, true>), grid, dim3(kGvWaves * 64), 0, st, p);
+            return hipGetLastError();
+        }
+    }
+    hipLaunchKernelGGL((gemv_i8_kernel<NBLK, SPS, RB, EPI, OUT, false>), grid, dim3(kGvWaves * 64), 0, st, p);
     return hipGetLastError();
 }
 
@@ -734,11 +809,14 @@ hipError_t launch_gemv_t(const Params &p, int64_t batch, hipStream_t st) {
 template <int RB, int EPI, int OUT>
 hipError_t launch_gemv_n(const Params &p, int64_t batch, hipStream_t st) {
     const int64_t nblocks = (p.n + 15) / 16;
-    if (RB == 1) {
+    if constexpr (RB == 1) {
         if (nblocks <= 384) return launch_gemv_t<1, 4, RB, EPI, OUT>(p, batch, st);
         return launch_gemv_t<1, 2, RB, EPI, OUT>(p, batch, st);
     }
     if (nblocks <= 384) return launch_gemv_t<1, 2, RB, EPI, OUT>(p, batch, st);
+    // two row blocks: 128-k stages (whole-line x) still fit in registers
+    if constexpr (RB == 2)
+        if (p.k % 128 == 0) return launch_gemv_t<4, 2, RB, EPI, OUT>(p, batch, st);
     return launch_gemv_t<4, 1, RB, EPI, OUT>(p, batch, st);
 }
 

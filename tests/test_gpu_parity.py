@@ -72,6 +72,8 @@ W8A8_SHAPES = [
     (33, 1000, 768, True),
     (64, 6400, 256, True),     # four column blocks per workgroup
     (48, 13000, 128, True),    # four column blocks per workgroup, the last one past n
+    (20, 6400, 384, True),     # two row blocks, 128-k whole-line stages, more than 384 column blocks
+    (27, 5000, 320, True),     # the same shape class with k % 128 != 0 (64-k stages), n % 16 != 0
     (96, 400, 512, True),      # six and eight row blocks (m <= 128, few columns)
     (128, 1000, 768, True),
     (100, 6400, 128, True),    # many columns: back to the 128x128 tiles
