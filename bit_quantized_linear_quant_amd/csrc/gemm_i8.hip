@@ -606,7 +606,8 @@ struct GemvStage {
 template <int NBLK, int SPS, int RB, bool XT>
 __device__ __forceinline__ void gemv_load(GemvStage<NBLK, SPS, RB> &st, const int8_t *const (&xrow)[RB],
                                           const int8_t *const (&wrow)[NBLK], int64_t kb, int64_t nsteps,
-                                          const int8_t *__restrict__ x, int64_t m, int64_t k, int lane) {
+                                          const int8_t *__restrict__ x, int64_t m, int64_t k, int lane,
+                                          const int8_t *const (&wcol)[2 * NBLK]) {
 #pragma unroll
     for (int t = 0; t < SPS; t++) {
         const int64_t s = kb * SPS + t;
@@ -626,8 +627,16 @@ __device__ __forceinline__ void gemv_load(GemvStage<NBLK, SPS, RB> &st, const in
         }
 #pragma unroll
         for (int j = 0; j < NBLK; j++) {
-            const uint4 v = load16_stream(wrow[j] + off);
-            st.w[t][j] = v4i{(int)v.x, (int)v.y, (int)v.z, (int)v.w};
+            if constexpr (XT) {
+                // weights in whole lines too: column 16 j + 8 (t & 1) + lane / 8
+                const int64_t s0 = kb * SPS + (t & ~1);
+                const int64_t poff = (s0 < nsteps ? s0 : nsteps - 2) * 64;
+                const uint4 v = load16_stream(wcol[2 * j + (t & 1)] + poff);
+                st.w[t][j] = v4i{(int)v.x, (int)v.y, (int)v.z, (int)v.w};
+            } else {
+                const uint4 v = load16_stream(wrow[j] + off);
+                st.w[t][j] = v4i{(int)v.x, (int)v.y, (int)v.z, (int)v.w};
+            }
         }
     }
 }
@@ -665,7 +674,7 @@ __device__ __forceinline__ void x_pair_fragments(const v4i (&in0b)[RB], const v4
 template <int NBLK, int SPS, int RB, bool XT>
 __device__ __forceinline__ void gemv_compute(const GemvStage<NBLK, SPS, RB> &st, v4i (&acc)[RB][NBLK], int64_t kb,
                                              int64_t nsteps, uint8_t *xb, int lane) {
-    v4i xa[SPS][RB];
+    v4i xa[SPS][RB], wa[SPS][NBLK];
     if constexpr (XT) {
 #pragma unroll
         for (int i = 0; i < SPS / 2; i++) {
@@ -676,12 +685,22 @@ __device__ __forceinline__ void gemv_compute(const GemvStage<NBLK, SPS, RB> &st,
                 xa[2 * i][b] = f[0][b];
                 xa[2 * i + 1][b] = f[1][b];
             }
+            v4i g[2][NBLK];
+            x_pair_fragments<NBLK>(st.w[2 * i], st.w[2 * i + 1], g, xb, lane);
+#pragma unroll
+            for (int j = 0; j < NBLK; j++) {
+                wa[2 * i][j] = g[0][j];
+                wa[2 * i + 1][j] = g[1][j];
+            }
         }
     } else {
 #pragma unroll
-        for (int t = 0; t < SPS; t++)
+        for (int t = 0; t < SPS; t++) {
 #pragma unroll
             for (int b = 0; b < RB; b++) xa[t][b] = st.a[t][b];
+#pragma unroll
+            for (int j = 0; j < NBLK; j++) wa[t][j] = st.w[t][j];
+        }
     }
 #pragma unroll
     for (int t = 0; t < SPS; t++) {
@@ -692,7 +711,7 @@ __device__ __forceinline__ void gemv_compute(const GemvStage<NBLK, SPS, RB> &st,
             const v4i a = ok ? xa[t][b] : v4i{0, 0, 0, 0};
 #pragma unroll
             for (int j = 0; j < NBLK; j++)
-                acc[b][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, st.w[t][j], acc[b][j], 0, 0, 0);
+                acc[b][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, wa[t][j], acc[b][j], 0, 0, 0);
         }
     }
 }
@@ -700,7 +719,7 @@ __device__ __forceinline__ void gemv_compute(const GemvStage<NBLK, SPS, RB> &st,
 template <int NBLK, int SPS, int RB, int EPI, int OUT, bool XT>
 __global__ __launch_bounds__(kGvWaves * 64) void gemv_i8_kernel(Params p) {
     __shared__ v4i red[kGvWaves][RB * NBLK][kWave];
-    __shared__ __attribute__((aligned(16))) int8_t xlds[XT ? kGvWaves : 1][XT ? 16 * RB * kRow128Pitch : 16];
+    __shared__ __attribute__((aligned(16))) int8_t xlds[XT ? kGvWaves : 1][XT ? 16 * (RB > NBLK ? RB : NBLK) * kRow128Pitch : 16];
     to_batch(p);
     const int lane = threadIdx.x % kWave, wave = wave_id();
     uint8_t *xb = reinterpret_cast<uint8_t *>(xlds[XT ? wave : 0]);
@@ -719,6 +738,13 @@ __global__ __launch_bounds__(kGvWaves * 64) void gemv_i8_kernel(Params p) {
     for (int j = 0; j < NBLK; j++) {
         const int64_t col = (nb0 + j) * 16 + fr;
         wrow[j] = p.w + (col < p.n ? col : p.n - 1) * p.k + 16 * (lane / 16);
+    }
+    // whole-line weight loads (XT): column 16 j + 8 u + lane / 8, clamped
+    const int8_t *wcol[2 * NBLK];
+#pragma unroll
+    for (int i = 0; i < 2 * NBLK; i++) {
+        const int64_t col = (nb0 + i / 2) * 16 + 8 * (i % 2) + lane / 8;
+        wcol[i] = p.w + (col < p.n ? col : p.n - 1) * p.k + 16 * (lane % 8);
     }
     // row factors of this lane's output rows 16 b + 4 (lane / 16) + r, loaded
     // now so their latency hides behind the k loop
@@ -740,14 +766,14 @@ __global__ __launch_bounds__(kGvWaves * 64) void gemv_i8_kernel(Params p) {
         for (int j = 0; j < NBLK; j++) acc[b][j] = v4i{0, 0, 0, 0};
     GemvStage<NBLK, SPS, RB> s0, s1;
     int64_t kb = wave;
-    if (kb < kblocks) gemv_load<NBLK, SPS, RB, XT>(s0, xrow, wrow, kb, nsteps, p.x, p.m, p.k, lane);
+    if (kb < kblocks) gemv_load<NBLK, SPS, RB, XT>(s0, xrow, wrow, kb, nsteps, p.x, p.m, p.k, lane, wcol);
     while (kb < kblocks) {
         const int64_t kb1 = kb + kGvWaves;
-        if (kb1 < kblocks) gemv_load<NBLK, SPS, RB, XT>(s1, xrow, wrow, kb1, nsteps, p.x, p.m, p.k, lane);
+        if (kb1 < kblocks) gemv_load<NBLK, SPS, RB, XT>(s1, xrow, wrow, kb1, nsteps, p.x, p.m, p.k, lane, wcol);
         gemv_compute<NBLK, SPS, RB, XT>(s0, acc, kb, nsteps, xb, lane);
         if (kb1 >= kblocks) break;
         const int64_t kb2 = kb1 + kGvWaves;
-        if (kb2 < kblocks) gemv_load<NBLK, SPS, RB, XT>(s0, xrow, wrow, kb2, nsteps, p.x, p.m, p.k, lane);
+        if (kb2 < kblocks) gemv_load<NBLK, SPS, RB, XT>(s0, xrow, wrow, kb2, nsteps, p.x, p.m, p.k, lane, wcol);
         gemv_compute<NBLK, SPS, RB, XT>(s1, acc, kb1, nsteps, xb, lane);
         kb = kb2;
     }
@@ -815,8 +841,10 @@ hipError_t launch_gemv_n(const Params &p, int64_t batch, hipStream_t st) {
     }
     if (nblocks <= 384) return launch_gemv_t<1, 2, RB, EPI, OUT>(p, batch, st);
     // two row blocks: 128-k stages (whole-line x) still fit in registers
-    if constexpr (RB == 2)
-        if (p.k % 128 == 0) return launch_gemv_t<4, 2, RB, EPI, OUT>(p, batch, st);
+    if (p.k % 128 == 0) {
+        if constexpr (RB == 2) return launch_gemv_t<4, 2, RB, EPI, OUT>(p, batch, st);
+        else return launch_gemv_t<2, 2, RB, EPI, OUT>(p, batch, st);
+    }
     return launch_gemv_t<4, 1, RB, EPI, OUT>(p, batch, st);
 }
 
