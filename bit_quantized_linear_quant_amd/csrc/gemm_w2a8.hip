@@ -450,7 +450,11 @@ __device__ __forceinline__ void gemv_compute(const GemvStage<NBLK, U, RB> &st, v
         const bool ok = kb0 + (int64_t)u * WAVES < kblocks;
         v4i xa[RB][4];
         if constexpr (XT) {
-            rows256_to_fragments<RB>(st.a[u], xa, xb, lane);
+            // one row block at a time through the wave's 16-row LDS block
+#pragma unroll
+            for (int b = 0; b < RB; b++)
+                rows256_to_fragments<1>(reinterpret_cast<const v4i(&)[1][4]>(st.a[u][b]),
+                                        reinterpret_cast<v4i(&)[1][4]>(xa[b]), xb, lane);
         } else {
 #pragma unroll
             for (int b = 0; b < RB; b++)
@@ -482,7 +486,7 @@ __global__ __launch_bounds__(WAVES * 64) void w2a8_gemv_kernel(const int8_t *__r
                                                                void *__restrict__ out) {
     __shared__ v4i red[WAVES][RB * NBLK][kWave];
     // XT: x reaches the lanes through each wave's LDS block (whole-line loads)
-    __shared__ __attribute__((aligned(16))) uint8_t xlds[XT ? WAVES : 1][XT ? 16 * RB * kRow256Pitch : 16];
+    __shared__ __attribute__((aligned(16))) uint8_t xlds[XT ? WAVES : 1][XT ? 16 * kRow256Pitch : 16];
     const int lane = threadIdx.x % kWave, wave = wave_id();
     uint8_t *xb = xlds[XT ? wave : 0];
     const int64_t nb0 = (int64_t)blockIdx.x * NBLK;
@@ -597,6 +601,16 @@ hipError_t launch_gemv_rows(const int8_t *xq, const float *pts, const int32_t *r
                             const double *gamma, const float *bias, int64_t m, int64_t n, int64_t k, void *out,
                             hipStream_t st) {
     const int64_t nblocks = n / 16;
+    // x through LDS in whole lines once every wave has k blocks to stream
+    // (k >= 2048; at k = 256 the LDS round trip only adds latency); four row
+    // blocks of three column blocks have no registers left for it.
+    if (k >= 2048) {
+        if (nblocks <= 384)
+            return launch_gemv<1, 8, 1, RB, OUT, true>(xq, pts, rowsum, packed, gamma, bias, m, n, k, out, st);
+        if (nblocks <= 1024)
+            return launch_gemv<3, 8, 1, RB, OUT, (RB < 4)>(xq, pts, rowsum, packed, gamma, bias, m, n, k, out, st);
+        return launch_gemv<4, 4, 1, RB, OUT, true>(xq, pts, rowsum, packed, gamma, bias, m, n, k, out, st);
+    }
     if (nblocks <= 384) return launch_gemv<1, 8, 1, RB, OUT>(xq, pts, rowsum, packed, gamma, bias, m, n, k, out, st);
     if (nblocks <= 1024) return launch_gemv<3, 8, 1, RB, OUT>(xq, pts, rowsum, packed, gamma, bias, m, n, k, out, st);
     return launch_gemv<4, 4, 1, RB, OUT>(xq, pts, rowsum, packed, gamma, bias, m, n, k, out, st);
