@@ -678,12 +678,24 @@ __device__ __forceinline__ void gemv_compute(const GemvStage<NBLK, SPS, RB> &st,
     if constexpr (XT) {
 #pragma unroll
         for (int i = 0; i < SPS / 2; i++) {
-            v4i f[2][RB];
-            x_pair_fragments<RB>(st.a[2 * i], st.a[2 * i + 1], f, xb, lane);
+            if constexpr (RB <= 4) {
+                v4i f[2][RB];
+                x_pair_fragments<RB>(st.a[2 * i], st.a[2 * i + 1], f, xb, lane);
 #pragma unroll
-            for (int b = 0; b < RB; b++) {
-                xa[2 * i][b] = f[0][b];
-                xa[2 * i + 1][b] = f[1][b];
+                for (int b = 0; b < RB; b++) {
+                    xa[2 * i][b] = f[0][b];
+                    xa[2 * i + 1][b] = f[1][b];
+                }
+            } else {
+                // more row blocks pass through the 16-row block one at a time
+#pragma unroll
+                for (int b = 0; b < RB; b++) {
+                    v4i f[2][1];
+                    x_pair_fragments<1>(reinterpret_cast<const v4i(&)[1]>(st.a[2 * i][b]),
+                                        reinterpret_cast<const v4i(&)[1]>(st.a[2 * i + 1][b]), f, xb, lane);
+                    xa[2 * i][b] = f[0][0];
+                    xa[2 * i + 1][b] = f[1][0];
+                }
             }
             v4i g[2][NBLK];
             x_pair_fragments<NBLK>(st.w[2 * i], st.w[2 * i + 1], g, xb, lane);
@@ -719,7 +731,8 @@ __device__ __forceinline__ void gemv_compute(const GemvStage<NBLK, SPS, RB> &st,
 template <int NBLK, int SPS, int RB, int EPI, int OUT, bool XT>
 __global__ __launch_bounds__(kGvWaves * 64) void gemv_i8_kernel(Params p) {
     __shared__ v4i red[kGvWaves][RB * NBLK][kWave];
-    __shared__ __attribute__((aligned(16))) int8_t xlds[XT ? kGvWaves : 1][XT ? 16 * (RB > NBLK ? RB : NBLK) * kRow128Pitch : 16];
+    constexpr int kXRows = RB <= 4 ? (RB > NBLK ? RB : NBLK) : NBLK;  // 16-row blocks in the wave's LDS block
+    __shared__ __attribute__((aligned(16))) int8_t xlds[XT ? kGvWaves : 1][XT ? 16 * kXRows * kRow128Pitch : 16];
     to_batch(p);
     const int lane = threadIdx.x % kWave, wave = wave_id();
     uint8_t *xb = reinterpret_cast<uint8_t *>(xlds[XT ? wave : 0]);
@@ -813,7 +826,7 @@ hipError_t launch_gemv_t(const Params &p, int64_t batch, hipStream_t st) {
     const dim3 grid((unsigned)((nblocks + NBLK - 1) / NBLK), 1, (unsigned)batch);
     // Whole-line x loads need pairs of 64-k steps in a stage and in k, and
     // an LDS block per wave (up to four row blocks).
-    if constexpr (SPS % 2 == 0 && RB <= 4) {
+    if constexpr (SPS % 2 == 0) {
         if (p.k % 128 == 0) {
             hipLaunchKernelGGL((gemv_i8_kernel<NBLK, SPS, RB, EPI, OUT, true>), grid, dim3(kGvWaves * 64), 0, st, p);
             return hipGetLastError();
@@ -855,9 +868,12 @@ hipError_t launch_gemv_rb(const Params &p, int64_t batch, hipStream_t st) {
         case 2: return launch_gemv_n<2, EPI, OUT>(p, batch, st);
         case 3: return launch_gemv_n<3, EPI, OUT>(p, batch, st);
         case 4: return launch_gemv_n<4, EPI, OUT>(p, batch, st);
-        // 64 < m <= 128, at most 384 column blocks (gemv_fits): 64-k stages
-        // keep six or eight row blocks' operands in registers
-        case 5: case 6: return launch_gemv_t<1, 1, 6, EPI, OUT>(p, batch, st);
+        // 64 < m <= 128, at most 384 column blocks (gemv_fits): six row blocks
+        // take 128-k whole-line stages (k % 128 == 0), else 64-k stages
+        case 5: case 6:
+            if (p.k % 128 == 0) return launch_gemv_t<1, 2, 6, EPI, OUT>(p, batch, st);
+            return launch_gemv_t<1, 1, 6, EPI, OUT>(p, batch, st);
+        // (eight row blocks: 128-k stages no longer fit in registers)
         default: return launch_gemv_t<1, 1, 8, EPI, OUT>(p, batch, st);
     }
 }
