@@ -631,9 +631,12 @@ hipError_t launch_out(const int8_t *xq, const float *pts, const int32_t *rowsum,
         // Measured on MI355X at k=8192, n=28672 with the weights streamed from
         // HBM, 8 waves and one k block per register stage: 4 column blocks per
         // workgroup up to m = 4, 7 above (1792 column blocks = 256 workgroups).
-        // Above m = 4, x moves in whole cache lines through LDS.
+        // Above m = 4 (and k >= 2048, as for more row blocks), x moves in
+        // whole cache lines through LDS.
         if (m <= 4) return launch_gemv<4, 8, 1, 1, OUT>(xq, pts, rowsum, packed, gamma, bias, m, n, k, out, st);
-        return launch_gemv<7, 8, 1, 1, OUT, true>(xq, pts, rowsum, packed, gamma, bias, m, n, k, out, st);
+        if (k >= 2048)
+            return launch_gemv<7, 8, 1, 1, OUT, true>(xq, pts, rowsum, packed, gamma, bias, m, n, k, out, st);
+        return launch_gemv<7, 8, 1, 1, OUT>(xq, pts, rowsum, packed, gamma, bias, m, n, k, out, st);
     }
     if (m >= XBM) {
         const int tiles_m = (int)((m + XBM - 1) / XBM), tiles_n = (int)((n + XBN - 1) / XBN);

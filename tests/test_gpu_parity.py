@@ -280,8 +280,8 @@ def test_pack_int4_parity(n, k):
 W2A8_SHAPES = [(1, 400, 512), (2, 256, 768), (4, 400, 512), (5, 64, 256), (16, 400, 768), (17, 400, 512),
                (33, 400, 768), (64, 6400, 512), (40, 20000, 256), (64, 16400, 256),
                (130, 256, 768), (300, 400, 512), (256, 128, 256), (513, 272, 1280), (600, 528, 2304),
-               # 17 <= m <= 64 with k >= 2048: x through LDS in whole lines, one to four column blocks
-               (20, 400, 2048), (33, 1008, 4096), (48, 6400, 2304), (64, 16400, 2048)]
+               # 4 < m <= 64 with k >= 2048: x through LDS in whole lines, one to four row blocks
+               (12, 400, 2048), (20, 400, 2048), (33, 1008, 4096), (48, 6400, 2304), (64, 16400, 2048)]
 
 
 @pytest.mark.parametrize("m,n,k", W2A8_SHAPES)
