@@ -627,6 +627,22 @@ hipError_t launch_out(const int8_t *xq, const float *pts, const int32_t *rowsum,
             default: return launch_gemv_rows<4, OUT>(xq, pts, rowsum, packed, gamma, bias, m, n, k, out, st);
         }
     }
+    if (m > 96 && m <= 128 && k >= 2048 && n / 16 <= 1024) {
+        // Eight row blocks do not fit the decode kernel's registers; two
+        // decode launches of 64 and m - 64 rows (each streaming the weights
+        // once) beat the 128x128 tiles while the columns are few enough.
+        const hipError_t e = launch_out<OUT>(xq, pts, rowsum, packed, gamma, bias, 64, n, k, out, st);
+        if (e != hipSuccess) return e;
+        const int64_t es = OUT == OUT_I32 || OUT == OUT_F32 ? 4 : 2;   // output element bytes
+        return launch_out<OUT>(xq + 64 * k, pts ? pts + 64 : nullptr, rowsum + 64, packed, gamma, bias, m - 64, n, k,
+                               static_cast<int8_t *>(out) + 64 * n * es, st);
+    }
+    if (m > 64 && m <= 96 && k >= 2048) {
+        // Five or six row blocks: four waves (their register budget holds the
+        // stages), two column blocks per workgroup, x through LDS.  Eight row
+        // blocks spill even with one column block.
+        return launch_gemv<2, 4, 1, 6, OUT, true>(xq, pts, rowsum, packed, gamma, bias, m, n, k, out, st);
+    }
     if (m <= 16) {
         // Measured on MI355X at k=8192, n=28672 with the weights streamed from
         // HBM, 8 waves and one k block per register stage: 4 column blocks per

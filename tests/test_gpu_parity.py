@@ -281,7 +281,11 @@ W2A8_SHAPES = [(1, 400, 512), (2, 256, 768), (4, 400, 512), (5, 64, 256), (16, 4
                (33, 400, 768), (64, 6400, 512), (40, 20000, 256), (64, 16400, 256),
                (130, 256, 768), (300, 400, 512), (256, 128, 256), (513, 272, 1280), (600, 528, 2304),
                # 4 < m <= 64 with k >= 2048: x through LDS in whole lines, one to four row blocks
-               (12, 400, 2048), (20, 400, 2048), (33, 1008, 4096), (48, 6400, 2304), (64, 16400, 2048)]
+               (12, 400, 2048), (20, 400, 2048), (33, 1008, 4096), (48, 6400, 2304), (64, 16400, 2048),
+               # 64 < m <= 96 with k >= 2048: six row blocks on four waves
+               (65, 400, 2048), (96, 1008, 2304),
+               # 96 < m <= 128, k >= 2048, at most 1024 column blocks: two decode launches
+               (100, 400, 2048), (128, 1008, 4096)]
 
 
 @pytest.mark.parametrize("m,n,k", W2A8_SHAPES)
