@@ -19,7 +19,9 @@
 // 64 < m < 256: 128 x 128 tiles, 2 x 2 waves of 64 x 64 on 32x32x32, A
 //         staged in LDS per 256-k step (rows padded to 272 bytes), B loaded
 //         per wave straight into registers in the lane order that operand
-//         needs.
+//         needs; except, for k >= 2048, m <= 96 (the decode kernel with six
+//         row blocks) and m <= 128 with at most 1024 column blocks (two
+//         decode launches of 64 and m - 64 rows).
 // m <= 64: decode GEMV.  The m rows fill one to four 16-row MFMA blocks
 //         (rows past m repeat row 0 and are never stored); each workgroup
 //         owns NBLK column blocks and its waves split k, each wave keeping two

@@ -249,7 +249,8 @@ ql_status qlinear_gemm_w8a8_batched(const int8_t *x, const int8_t *w, ql_wlayout
  *   bias [n] fp32 or NULL, added as in qlinear_gemm_w8a8 (QL_BIAS below);
  *   QL_I32 with a bias is QL_ERR_UNSUPPORTED.
  * The kernel multiplies by code+1 in {0, 1, 2} and subtracts rowsum.
- * m <= 16 takes the split-K decode GEMV path, larger m the tiled GEMM path.
+ * m <= 64 takes the split-k decode kernel (as do 64 < m <= 128 at k >= 2048,
+ * within column limits), larger m the tiled GEMM kernels.
  * n % 16 == 0, k % 256 == 0, k <= 131071.
  */
 ql_status qlinear_gemm_w2a8(const int8_t *xq, const float *per_token_scale,
