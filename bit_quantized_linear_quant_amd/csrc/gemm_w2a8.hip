@@ -19,8 +19,8 @@
 // 64 < m < 256: 128 x 128 tiles, 2 x 2 waves of 64 x 64 on 32x32x32, A
 //         staged in LDS per 256-k step (rows padded to 272 bytes), B loaded
 //         per wave straight into registers in the lane order that operand
-//         needs; except, for k >= 2048, m <= 96 (the decode kernel with six
-//         row blocks) and m <= 128 with at most 1024 column blocks (two
+//         needs; except, for k >= 2048 and at most 1024 column blocks,
+//         m <= 96 (the decode kernel with six row blocks) and m <= 128 (two
 //         decode launches of 64 and m - 64 rows).
 // m <= 64: decode GEMV.  The m rows fill one to four 16-row MFMA blocks
 //         (rows past m repeat row 0 and are never stored); each workgroup
@@ -639,10 +639,11 @@ hipError_t launch_out(const int8_t *xq, const float *pts, const int32_t *rowsum,
         return launch_out<OUT>(xq + 64 * k, pts ? pts + 64 : nullptr, rowsum + 64, packed, gamma, bias, m - 64, n, k,
                                static_cast<int8_t *>(out) + 64 * n * es, st);
     }
-    if (m > 64 && m <= 96 && k >= 2048) {
+    if (m > 64 && m <= 96 && k >= 2048 && n / 16 <= 1024) {
         // Five or six row blocks: four waves (their register budget holds the
         // stages), two column blocks per workgroup, x through LDS.  Eight row
-        // blocks spill even with one column block.
+        // blocks spill even with one column block.  Wider products (x
+        // re-read for every two column blocks) stay on the tiles.
         return launch_gemv<2, 4, 1, 6, OUT, true>(xq, pts, rowsum, packed, gamma, bias, m, n, k, out, st);
     }
     if (m <= 16) {
