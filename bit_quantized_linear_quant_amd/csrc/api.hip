@@ -12,6 +12,9 @@
 namespace {
 
 constexpr int64_t kMaxK = 131071;  // (-128)^2 * k must fit int32
+// Longest row quant_act accepts: the int32 code sum of a row, at most 127 k
+// in magnitude, must fit int32.
+constexpr int64_t kMaxQuantK = 16909320;
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -69,8 +72,12 @@ ql_status qlinear_quant_act(const void *x, ql_dtype x_dtype, int64_t m, int64_t 
                             float eps_norm, float eps_q, int8_t *q, float *per_token_scale,
                             int32_t *rowsum, void *stream) {
     if (!x || !q || !per_token_scale) return QL_ERR_NULL;
-    if (m < 1 || k < 1 || m > 0x7fffffff) return QL_ERR_SHAPE;
+    if (m < 1 || k < 1 || m > 0x7fffffff || k > kMaxQuantK) return QL_ERR_SHAPE;
     if ((flags & ~QL_RMSNORM) != 0) return QL_ERR_UNSUPPORTED;
+    // eps_q guards a division and must be a positive number; eps_norm must
+    // not be negative (NaN fails both comparisons).
+    if (!(eps_q > 0.0f) || !(eps_q <= 3.4e38f) || !(eps_norm >= 0.0f) || !(eps_norm <= 3.4e38f))
+        return QL_ERR_UNSUPPORTED;
     const int kind = in_kind(x_dtype);
     if (kind < 0) return QL_ERR_DTYPE;
     if (!aligned16(x) || !aligned16(q) || !aligned16(per_token_scale) || (rowsum && !aligned16(rowsum)))

@@ -65,6 +65,24 @@ __device__ __forceinline__ int store_chunk(int8_t *qrow, int64_t ch, int64_t k, 
     return sum;
 }
 
+// The RMSNorm factor r = 1 / sqrt(ss / k + eps_norm) (1 without RMSNorm) and
+// the guarded absmax a' = max(a, eps_q / r).  The quantizer sees the
+// normalized row r x, whose absmax r a is guarded by eps_q; in the units of x
+// that guard is eps_q / r = eps_q * sqrt(ss / k + eps_norm).  Without RMSNorm
+// a' = max(a, eps_q) exactly.
+template <bool RMS>
+__device__ __forceinline__ void guarded_absmax(float amax, float ss, int64_t k, float eps_norm, float eps_q,
+                                               float &r, float &ap) {
+    float t = eps_q;
+    r = 1.0f;
+    if (RMS) {
+        const float d = sqrtf(__fadd_rn(__fdiv_rn(ss, (float)k), eps_norm));
+        r = __fdiv_rn(1.0f, d);
+        t = __fmul_rn(eps_q, d);
+    }
+    ap = amax > t ? amax : t;
+}
+
 // Block-wide reduction of one value through LDS after a wave reduction; the
 // four wave results are combined in a fixed order, so the result does not
 // depend on scheduling.
@@ -122,7 +140,8 @@ __global__ __launch_bounds__(kQThreads) void quant_act_kernel(const void *__rest
     amax = block_reduce<float, true>(amax, red_f);
     if (RMS) ss = block_reduce<float, false>(ss, red_f);
 
-    const float ap = amax > eps_q ? amax : eps_q;
+    float r, ap;
+    guarded_absmax<RMS>(amax, ss, k, eps_norm, eps_q, r, ap);
     const float s = __fdiv_rn(127.0f, ap);
 
     int rs = 0;
@@ -139,14 +158,7 @@ __global__ __launch_bounds__(kQThreads) void quant_act_kernel(const void *__rest
     rs = block_reduce<int, false>(rs, red_i);
 
     if (tid == 0) {
-        float p;
-        if (RMS) {
-            const float r = 1.0f / sqrtf(ss / (float)k + eps_norm);
-            p = ap * r / 127.0f;
-        } else {
-            p = __fdiv_rn(ap, 127.0f);
-        }
-        pts[row] = p;
+        pts[row] = RMS ? __fdiv_rn(__fmul_rn(ap, r), 127.0f) : __fdiv_rn(ap, 127.0f);
         if (rowsum) rowsum[row] = rs;
     }
 }
@@ -195,7 +207,8 @@ __global__ __launch_bounds__(kQWaveRows * kWave) void quant_act_wave_kernel(cons
     amax = wave_max(amax);
     if (RMS) ss = wave_sum(ss);
 
-    const float ap = amax > eps_q ? amax : eps_q;
+    float r, ap;
+    guarded_absmax<RMS>(amax, ss, k, eps_norm, eps_q, r, ap);
     const float s = __fdiv_rn(127.0f, ap);
     // The code of v is clamp(rint(fl(v * s)), -128, 127).  Clamping first
     // (the bounds are integers) and adding 1.5 * 2^23 rounds the value to an
@@ -225,14 +238,7 @@ __global__ __launch_bounds__(kQWaveRows * kWave) void quant_act_wave_kernel(cons
     }
     rsw = wave_sum(rsw);
     if (lane == 0) {
-        float p;
-        if (RMS) {
-            const float r = 1.0f / sqrtf(ss / (float)k + eps_norm);
-            p = ap * r / 127.0f;
-        } else {
-            p = __fdiv_rn(ap, 127.0f);
-        }
-        pts[row] = p;
+        pts[row] = RMS ? __fdiv_rn(__fmul_rn(ap, r), 127.0f) : __fdiv_rn(ap, 127.0f);
         // NCH * 64 * 8 words were summed (masked chunks as code 0)
         if (rowsum) rowsum[row] = (int32_t)(rsw - (uint32_t)(NCH * kWave * 8) * kRoundBits);
     }

@@ -124,13 +124,19 @@ size_t qlinear_workspace_bytes(ql_op op, int64_t m, int64_t n, int64_t k);
  *
  *   x       [m, k] QL_BF16, QL_F16 or QL_F32.
  *   flags   0 or QL_RMSNORM.
+ *   r       = 1/sqrt(mean(x^2) + eps_norm) with QL_RMSNORM (fp32), else 1.
  *   q       [m, k] int8 out: clamp(rne(fl32(x * fl32(127 / a'))), -128, 127),
- *           a' = max(max_k |x|, eps_q).  Codes do not depend on the RMSNorm:
- *           it multiplies a row by r > 0 and absmax codes are invariant.
- *   per_token_scale [m] fp32 out: a' * r / 127, r = 1/sqrt(mean(x^2) + eps_norm)
- *           with QL_RMSNORM (computed in fp32), else r = 1 (correctly rounded).
+ *           a' = max(max_k |x|, eps_q / r): the guard applies to the absmax of
+ *           the normalized row r x, which the quantizer sees.  Where
+ *           r max|x| >= eps_q the codes do not depend on the RMSNorm (it
+ *           multiplies the row by r > 0 and absmax codes are invariant).
+ *   per_token_scale [m] fp32 out: a' * r / 127 (without RMSNorm correctly
+ *           rounded; with it, from the fp32 r).
  *   rowsum  [m] int32 out, may be NULL: sum_k q[m, k].
- * m, k >= 1.  Errors: QL_ERR_NULL, QL_ERR_SHAPE, QL_ERR_DTYPE, QL_ERR_ALIGN.
+ * 1 <= m < 2^31, 1 <= k <= 16909320 (the code sum must fit int32); eps_q a
+ * positive finite number, eps_norm a finite number >= 0.
+ * Errors: QL_ERR_NULL, QL_ERR_SHAPE, QL_ERR_UNSUPPORTED (flags or eps),
+ * QL_ERR_DTYPE, QL_ERR_ALIGN.
  */
 ql_status qlinear_quant_act(const void *x, ql_dtype x_dtype, int64_t m, int64_t k,
                             uint32_t flags, float eps_norm, float eps_q,
@@ -138,9 +144,10 @@ ql_status qlinear_quant_act(const void *x, ql_dtype x_dtype, int64_t m, int64_t 
                             void *stream);
 
 /*
- * Per-tensor 4-bit quantization of [Q4] forward ("quantizes inputs and
- * weights to 4-bits using specified scale factors"; eps avoids division by
- * zero):  q = clamp(rne(fl32(x / max(*scale, eps))), -8, 7), stored in int8.
+ * Per-tensor 4-bit quantization of [Q4] forward (activations and weights
+ * both become 4-bit codes under their given scale; eps keeps the divisor
+ * away from zero):  q = clamp(rne(fl32(x / max(*scale, eps))), -8, 7),
+ * stored in int8.
  *   x      [count] QL_F16, QL_BF16 or QL_F32.
  *   scale  device fp32 scalar.
  * count >= 1.  Errors: QL_ERR_NULL, QL_ERR_SHAPE, QL_ERR_DTYPE, QL_ERR_ALIGN.

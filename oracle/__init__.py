@@ -109,8 +109,9 @@ def quant_act(x, rmsnorm: bool = False, eps_norm: float = 1e-6, eps_q: float = 1
     "Class BitLinear" forward steps 1-2 and 5; "Common Attention
     Utilities" activation_quant.  Returns ``(q int8[m,k], pts fp32[m],
     rowsum int32[m])``; ``pts`` is the per-token dequant scale
-    ``max(absmax, eps_q) * r / 127`` with ``r`` the RMSNorm factor (1 when
-    off).
+    ``a' * r / 127`` with ``r`` the RMSNorm factor (1 when off) and
+    ``a' = max(absmax, fl32(eps_q / r))``: the guard applies to the absmax of
+    the normalized row ``r * x``.
     """
     x = _c(x, np.float32)
     m, k = x.shape

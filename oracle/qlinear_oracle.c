@@ -39,17 +39,21 @@
  *
  * For each token row m of X[m, k] (fp32 values, exact copies of the bf16 /
  * fp16 input):
- *   a   = max_k |X|                       (exact)
- *   a'  = max(a, eps_q)                   (division guard)
- *   s   = fl32(127 / a')
- *   q   = clamp(rne(fl32(X * s)), -128, 127)
  *   r   = 1                               without RMSNorm
  *   r   = 1 / sqrt(sum_k X^2 / K + eps_n) with RMSNorm (fp64)
+ *   a   = max_k |X|                       (exact)
+ *   t   = fl32(eps_q / r)                 (t = eps_q exactly without RMSNorm)
+ *   a'  = max(a, t)                       (division guard)
+ *   s   = fl32(127 / a')
+ *   q   = clamp(rne(fl32(X * s)), -128, 127)
  *   pts = fp32(a' * r / 127)              (fp64, one final rounding)
  *   rowsum = sum_k q                      (int32)
  * RMSNorm multiplies the whole row by r > 0 and absmax quantization is
  * invariant under a positive per-row factor, so the codes are those of X
- * and the norm survives only as the factor r in the dequant scale.
+ * and the norm survives as the factor r in the dequant scale.  The guard
+ * belongs to the quantizer, which sees the normalized row Y = r X: it takes
+ * max(max|Y|, eps_q), and max(r a, eps_q) / r = max(a, eps_q / r) = a'.
+ * Only rows with r a < eps_q reach the guard; their codes depend on r.
  */
 int oracle_quant_act(const float *x, int64_t m, int64_t k, int rmsnorm,
                      double eps_norm, float eps_q, int8_t *q, float *pts,
@@ -63,7 +67,14 @@ int oracle_quant_act(const float *x, int64_t m, int64_t k, int rmsnorm,
             float v = fabsf(row[j]);
             if (v > a) a = v;
         }
-        float ap = a > eps_q ? a : eps_q;
+        double rr = 1.0;
+        if (rmsnorm) {
+            double ss = 0.0;
+            for (int64_t j = 0; j < k; j++) ss += (double)row[j] * (double)row[j];
+            rr = 1.0 / sqrt(ss / (double)k + eps_norm);
+        }
+        float t = rmsnorm ? (float)((double)eps_q / rr) : eps_q;
+        float ap = a > t ? a : t;
         float s = 127.0f / ap;
         int64_t sum = 0;
         for (int64_t j = 0; j < k; j++) {
@@ -74,12 +85,6 @@ int oracle_quant_act(const float *x, int64_t m, int64_t k, int rmsnorm,
             int8_t c = (int8_t)r;
             q[i * k + j] = c;
             sum += c;
-        }
-        double rr = 1.0;
-        if (rmsnorm) {
-            double ss = 0.0;
-            for (int64_t j = 0; j < k; j++) ss += (double)row[j] * (double)row[j];
-            rr = 1.0 / sqrt(ss / (double)k + eps_norm);
         }
         pts[i] = (float)((double)ap * rr / 127.0);
         if (rowsum) rowsum[i] = (int32_t)sum;

@@ -31,6 +31,31 @@ def absmean_rel_tol(count: int) -> float:
     return (depth + 2) * 2.0 ** -53
 
 
+def rms_pts_rel_tol(k: int) -> float:
+    """Relative bound on |pts_gpu - pts_oracle| for quant_act with RMSNorm.
+
+    The kernel sums x^2 in fp32 (squares of bf16 / fp16 values are exact,
+    fp32 ones round once) along addition paths of depth d: rows of whole
+    8-element chunks up to k = 8192 run one wave per row, each lane adding
+    8 * NCH terms (NCH the smallest of 2, 4, 8, 16 with 64 * 8 * NCH >= k)
+    then 6 shuffle levels; other rows run 256 threads per row, each adding
+    8 * ceil(k / 2048) terms, then 6 shuffle levels and 3 adds across waves.
+    A sum of non-negative terms along depth d is within (d + 1) u of exact
+    (u = 2^-24).  Then ss / k and + eps_n round once each (the sum of two
+    non-negative terms keeps the relative error), the square root halves the
+    relative error and rounds once, 1 / sqrt and a' * r and / 127 round once
+    each, and the oracle rounds its fp64 value once: (d + 3) / 2 + 5 units.
+    Rows that reach the eps guard have pts = fl(fl(eps * D) / D) / 127 with
+    the same D on both factors, within 7 units, which the bound covers.
+    """
+    if k % 8 == 0 and k <= 8192:
+        nch = next(c for c in (2, 4, 8, 16) if 64 * 8 * c >= k)
+        depth = 8 * nch + 6
+    else:
+        depth = 8 * (-(-k // 2048)) + 6 + 3
+    return ((depth + 3) / 2 + 5) * 2.0 ** -24
+
+
 def to_np(t: torch.Tensor) -> np.ndarray:
     t = t.detach().cpu()
     if t.dtype in (torch.bfloat16, torch.float16):

@@ -69,6 +69,14 @@ def test_quant_act_validation(L):
     assert f(A, ql.QL_I8, 4, 8, 0, 1e-6, 1e-5, A, A, A, NULL) == -3
     assert f(U, ql.QL_BF16, 4, 8, 0, 1e-6, 1e-5, A, A, A, NULL) == -4
     assert f(A, ql.QL_BF16, 4, 8, 0x10, 1e-6, 1e-5, A, A, A, NULL) == -6   # unknown flag
+    # the int32 code sum of a row (at most 127 k in magnitude) must fit int32
+    assert f(A, ql.QL_BF16, 4, 16909321, 0, 1e-6, 1e-5, A, A, A, NULL) == -2
+    assert 127 * 16909320 < 2 ** 31 <= 127 * 16909321
+    # eps_q guards a division: positive and finite; eps_norm finite and >= 0
+    for eq in (0.0, -1e-5, float("nan"), float("inf")):
+        assert f(A, ql.QL_BF16, 4, 8, 0, 1e-6, eq, A, A, A, NULL) == -6
+    for en in (-1e-6, float("nan"), float("inf")):
+        assert f(A, ql.QL_BF16, 4, 8, 1, en, 1e-5, A, A, A, NULL) == -6
 
 
 def test_quant_int4_validation(L):

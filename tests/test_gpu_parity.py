@@ -14,7 +14,8 @@ import torch
 import bit_quantized_linear_quant_amd as ql
 import oracle
 import synthetic
-from parity_util import TOL_REL, absmean_rel_tol, assert_equal, assert_float_close, poison, to_np, words
+from parity_util import (TOL_REL, absmean_rel_tol, assert_equal, assert_float_close, poison, rms_pts_rel_tol,
+                         to_np, words)
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
@@ -193,9 +194,47 @@ def test_quant_act_parity(dtype, rms, m, k):
     assert_equal(q, q_ref, "codes")
     assert_equal(rs, rs_ref, "rowsum")
     if rms:
-        np.testing.assert_allclose(to_np(pts), pts_ref, rtol=1e-5)
+        np.testing.assert_allclose(to_np(pts).astype(np.float64), pts_ref.astype(np.float64),
+                                   rtol=rms_pts_rel_tol(k), atol=0)
     else:
         assert_equal(pts, pts_ref, "per-token scale")
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+@pytest.mark.parametrize("k", [96, 4096, 4097])
+def test_quant_act_rmsnorm_guard_on_tiny_rows(dtype, k):
+    """Rows whose normalized absmax falls below eps_q: the guard acts on r * max|x|.
+
+    Where r * a >= eps_q the codes are those of x (bit-exact).  Below it the
+    codes are rne(x * 127 / (eps_q / r)) and depend on the RMSNorm factor r,
+    which the kernel computes in fp32 and the oracle in fp64: they may differ
+    by one only where x * 127 r / eps_q lies within 1e-4 of a rounding tie.
+    """
+    rng = np.random.default_rng(k)
+    scales = [1.0, 1e-6, 3e-8, 1e-9, 1e-10, 1e-12, 0.0]
+    rows = [rng.standard_normal(k) * s for s in scales]
+    rows.append(np.full(k, 1e-6) * np.sign(rng.standard_normal(k)))
+    x = torch.tensor(np.stack(rows), dtype=torch.float32).to(dtype)
+    xf = x.float().numpy()
+    q_ref, pts_ref, rs_ref = oracle.quant_act(xf, rmsnorm=True, eps_norm=1e-6, eps_q=1e-5)
+    q, pts, rs = ql.qlinear_quant_act(_cuda(x), rmsnorm=True, eps_norm=1e-6, eps_q=1e-5)
+    _sync()
+    xd = xf.astype(np.float64)
+    r = 1.0 / np.sqrt((xd * xd).mean(axis=1) + 1e-6)
+    ar = np.abs(xd).max(axis=1) * r
+    g = q.cpu().numpy()
+    assert np.all(np.abs(g[-1]) == 127)  # the +-1e-6 row is far above the guard after the norm
+    for i in range(x.shape[0]):
+        if ar[i] >= 1e-5 * (1 + 1e-4):
+            assert_equal(g[i], q_ref[i], f"codes of row {i}")
+        else:
+            v = np.abs(xd[i] * 127.0 * r[i] / 1e-5)
+            tie = np.abs(v - np.floor(v) - 0.5) < 1e-4
+            diff = g[i].astype(np.int32) - q_ref[i].astype(np.int32)
+            assert np.all((diff == 0) | (tie & (np.abs(diff) == 1))), f"codes of row {i}"
+    assert_equal(rs, g.astype(np.int64).sum(axis=1).astype(np.int32), "rowsum")
+    np.testing.assert_allclose(to_np(pts).astype(np.float64), pts_ref.astype(np.float64),
+                               rtol=rms_pts_rel_tol(k), atol=0)
 
 
 def test_quant_act_degenerate_rows():

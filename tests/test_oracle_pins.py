@@ -226,6 +226,44 @@ def test_quant_act_degenerate_rows():
     assert np.all(q[2] == 127) and rs[2] == 127 * 40
 
 
+def test_quant_act_guard_applies_to_the_normalized_row():
+    """"Class BitLinear" steps 1-2: the quantizer sees the normalized row r*x.
+
+    The eps guard of the absmax protects the division of the quantizer, so it
+    applies to max|r x|, not to max|x|.  Checked against a literal fp64
+    normalize-then-quantize pipeline on rows from 1e-12 to 1: where r*a is at
+    least eps the codes are those of x itself (127 at the absmax); below, the
+    codes are rne(r x 127 / eps) and pts = eps / 127.
+    """
+    rng = np.random.default_rng(77)
+    eps_q, eps_n = 1e-5, 1e-6
+    rows = []
+    for scale in (1.0, 1e-3, 1e-6, 3e-8, 1e-9, 1e-10, 1e-12):
+        rows.append((rng.standard_normal(96) * scale).astype(np.float32))
+    rows.append(np.full(96, 1e-6, np.float32) * np.sign(rng.standard_normal(96)).astype(np.float32))
+    rows.append(np.zeros(96, np.float32))
+    x = np.stack(rows)
+    q, pts, rs = oracle.quant_act(x, rmsnorm=True, eps_norm=eps_n, eps_q=eps_q)
+    xd = x.astype(np.float64)
+    r = 1.0 / np.sqrt((xd * xd).mean(axis=1) + eps_n)
+    y = xd * r[:, None]
+    ay = np.maximum(np.abs(y).max(axis=1), eps_q)
+    v = y * (127.0 / ay)[:, None]
+    lit = np.clip(np.rint(v), -128, 127)
+    near_tie = np.abs(np.abs(v - np.trunc(v)) - 0.5) < 1e-4
+    assert np.all((lit == q) | near_tie)
+    assert np.count_nonzero(near_tie) < 3
+    # the +-1e-6 row: normalized absmax is about 1e-3, far above eps, so every code is +-127
+    assert np.all(np.abs(q[7]) == 127)
+    # rows whose normalized absmax is below eps use eps: pts = eps / 127, codes below 127
+    small = np.abs(y).max(axis=1) < eps_q
+    assert small[4:7].all() and small[8] and not small[:4].any() and not small[7]
+    np.testing.assert_allclose(pts[small].astype(np.float64), eps_q / 127.0, rtol=2 ** -22)
+    assert np.all(np.abs(q[5]) < 127) and np.all(q[8] == 0)
+    np.testing.assert_allclose(pts.astype(np.float64), ay / 127.0, rtol=2 ** -22)
+    assert np.array_equal(rs, q.astype(np.int64).sum(axis=1).astype(np.int32))
+
+
 # ---------------------------------------------------------------------------
 # O2: absmean ternary
 # ---------------------------------------------------------------------------
