@@ -22,13 +22,18 @@ The same JSON line carries:
                 with the packed weight rotated over copies larger than the
                 256 MB last-level cache, launches replayed from a HIP graph.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--only PART]
+
+--only runs one part by itself and prints its figures (no headline line):
+the rocprofv3 counter runs recorded under profiles/ use it so that a
+counter pass sees only the kernels it is about.
 """
 from __future__ import annotations
 
 import argparse
 import hashlib
 import json
+import math
 import os
 import sys
 import time
@@ -265,12 +270,12 @@ def _row(us, work, unit, peak, bound, what, oracle_rate=None, oracle_sample=None
     if peak is not None:
         r["peak"] = peak
         r["frac"] = round(rate / peak, 4)
-    if oracle_rate is not None:
+    if oracle_rate:
         r["oracle"] = {"value": round(oracle_rate, 4), "unit": unit, "sample": oracle_sample}
     return r
 
 
-def bench_rows(ql, torch, synthetic):
+def bench_rows(ql, torch, synthetic, with_oracle: bool = True):
     """Every step of the path on its own workload, against the roofline that bounds it.
 
     HBM-bound rows rotate enough input copies (>= 384 MB) that no launch finds its
@@ -283,6 +288,8 @@ def bench_rows(ql, torch, synthetic):
     dev = "cuda:0"
     rows = {}
     threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    # without the oracle legs every oracle rate below comes out 0 and is left out
+    tc = time_cpu if with_oracle else (lambda fn, min_s=1.0: math.inf)
 
     # a4: per-token W8A8, 16x256x128, fp16 out (launch-bound; no roofline claim).
     d = synthetic.w8a8()
@@ -291,7 +298,7 @@ def bench_rows(ql, torch, synthetic):
     out = torch.empty((16, 128), dtype=torch.float16, device=dev)
     us = time_graph(torch, lambda i: ql.qlinear_gemm_w8a8(x, w, ql.QL_W_KN, deq, pts, out=out), 100)
     xn, wn, dn, pn = (d[key].numpy() for key in ("x", "w", "deq", "pts"))
-    t = time_cpu(lambda: oracle.w8a8(xn, wn, False, pn, dn))
+    t = tc(lambda: oracle.w8a8(xn, wn, False, pn, dn))
     rows["a4_w8a8_16x256x128"] = _row(us, 2.0 * 16 * 256 * 128, "TOPS", None, "launch",
                                       "2*m*n*k ops; HIP-graph replay of 100 launches",
                                       2.0 * 16 * 256 * 128 / t / 1e12, "the whole product")
@@ -308,7 +315,7 @@ def bench_rows(ql, torch, synthetic):
     qbytes = m * k * 2 + m * k + 8 * m
     xf = d["x"].float().numpy()
     sample = 256
-    t = time_cpu(lambda: oracle.quant_act(xf[:sample], rmsnorm=True))
+    t = tc(lambda: oracle.quant_act(xf[:sample], rmsnorm=True))
     rows["a1_quant_act_2048x4096_bf16_rmsnorm"] = _row(
         us, qbytes, "GB/s", PEAK_HBM_GBS, "hbm", f"{qbytes} B (bf16 read, int8 codes, scale and rowsum)",
         sample * (k * 3 + 8) / t / 1e9, f"{sample} of {m} rows")
@@ -320,7 +327,7 @@ def bench_rows(ql, torch, synthetic):
     ops = 2.0 * m * n * k
     codes, g = oracle.ternary_quant(d["w"].numpy())
     xqn, ptsn, _ = oracle.quant_act(xf[:32], rmsnorm=True)
-    t = time_cpu(lambda: oracle.w2a8(xqn, ptsn, codes, g))
+    t = tc(lambda: oracle.w2a8(xqn, ptsn, codes, g))
     rows["a5_w2a8_gemm_2048x4096x4096"] = _row(us, ops, "TOPS", PEAK_INT8_TOPS, "mfma", "2*m*n*k int8 ops",
                                                2.0 * 32 * n * k / t / 1e12, f"32 of {m} rows")
 
@@ -337,7 +344,7 @@ def bench_rows(ql, torch, synthetic):
     pbytes = 2 * n * k * 4 + n * k // 4
     wn = wd.numpy()
     sample = 2048
-    t = time_cpu(lambda: oracle.pack_ternary(oracle.ternary_quant(wn[:sample])[0]))
+    t = tc(lambda: oracle.pack_ternary(oracle.ternary_quant(wn[:sample])[0]))
     rows["a2_pack_ternary_28672x8192_fp32"] = _row(
         us, pbytes, "GB/s", PEAK_HBM_GBS, "hbm",
         f"{pbytes} B (fp32 weight read twice: absmean, then threshold; 2-bit words written)",
@@ -352,7 +359,7 @@ def bench_rows(ql, torch, synthetic):
     us = time_eager(torch, lambda i: ql.qlinear_pack_int4(qdev, ql.QL_INT4_WEIGHT, packed=pw), 20)
     i4bytes = n * k + n * k // 2
     qn = dg["q"].numpy()
-    t = time_cpu(lambda: oracle.pack_int4(qn[:1024]))
+    t = tc(lambda: oracle.pack_int4(qn[:1024]))
     rows["a3_pack_int4_11008x4096"] = _row(us, i4bytes, "GB/s", PEAK_HBM_GBS, "hbm",
                                            f"{i4bytes} B (one code byte read, half a byte written per weight)",
                                            1024 * k * 1.5 / t / 1e9, f"1024 of {n} rows")
@@ -366,7 +373,7 @@ def bench_rows(ql, torch, synthetic):
     gbytes = n * k // 2 + n * (k // gs) * 2 + n * (k // gs) // 2 + m * k * 2 + m * n * 2
     xgn, sn = dg["x"].float().numpy(), dg["s"].float().numpy()
     zn = dg["z"].numpy()
-    t = time_cpu(lambda: oracle.grouped_int4(xgn, qn[:512], sn[:512], zn[:512], gs))
+    t = tc(lambda: oracle.grouped_int4(xgn, qn[:512], sn[:512], zn[:512], gs))
     rows["a7_grouped_int4_32x4096x11008_g128"] = _row(
         us, gbytes, "GB/s", PEAK_HBM_GBS, "hbm",
         f"{gbytes} B (packed weight, fp16 scales, packed zeros, fp16 x, fp16 out)",
@@ -376,7 +383,7 @@ def bench_rows(ql, torch, synthetic):
                                                                   per_token_scale=ptsg), 48)
     gbytes8 = n * k // 2 + n * (k // gs) * 2 + n * (k // gs) // 2 + m * k + 4 * m + m * n * 2
     xqn, ptsn, _ = oracle.quant_act(xgn)
-    t = time_cpu(lambda: oracle.grouped_int4_i8(xqn, ptsn, qn[:512], sn[:512], zn[:512], gs))
+    t = tc(lambda: oracle.grouped_int4_i8(xqn, ptsn, qn[:512], sn[:512], zn[:512], gs))
     rows["a7i8_grouped_int4_int8_act_32x4096x11008_g128"] = _row(
         us, gbytes8, "GB/s", PEAK_HBM_GBS, "hbm",
         f"{gbytes8} B (packed weight, fp16 scales, packed zeros, int8 x codes and scales, fp16 out)",
@@ -401,7 +408,7 @@ def bench_rows(ql, torch, synthetic):
                                                             grad_scale_a=gsb, workspace=wsb), 5)
     flops = 2 * 2.0 * m * n * k
     gn, xn, wn = gb[:8].float().cpu().numpy(), xb[:8].float().cpu().numpy(), wb.float().cpu().numpy()
-    t = time_cpu(lambda: oracle.q4_backward(gn, xn, wn, float(sab.item()), float(swb.item()), 1e-5), min_s=0.5)
+    t = tc(lambda: oracle.q4_backward(gn, xn, wn, float(sab.item()), float(swb.item()), 1e-5), min_s=0.5)
     rows["next4_q4_backward_8192x8192x8192_fp16"] = _row(
         us, flops, "TFLOP/s", PEAK_FP16_TFLOPS, "mfma",
         "2 x 2*m*n*k fp16 flops (grad_x = G Wh, grad_w = G^T Xh) with transposes and masked epilogues; "
@@ -416,6 +423,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--only", choices=["a4w4", "decode", "rows"], default=None,
+                    help="run one part alone (for counter runs): the A4W4 step, the decode GEMV, or the path rows")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -427,6 +436,16 @@ def main():
     import synthetic
 
     ql.lib()
+    if args.only is not None:
+        if args.only == "a4w4":
+            part = bench_a4w4(args, ql, torch, synthetic)[0]
+        elif args.only == "decode":
+            part = bench_decode(ql, torch, synthetic)
+        else:
+            part = bench_rows(ql, torch, synthetic, with_oracle=False)
+        torch.cuda.synchronize()
+        print(json.dumps({"only": args.only, "result": part}), flush=True)
+        return
     res, d = bench_a4w4(args, ql, torch, synthetic)
     gemv = bench_decode(ql, torch, synthetic)
     gemv_src = kernel_source_hash(GEMV_KERNEL_SOURCES)

@@ -197,8 +197,8 @@ static ql_status grouped_int4(int64_t batch, const void *x, ql_dtype x_dtype, co
     if (x_dtype == QL_I8 && !per_token_scale) return QL_ERR_NULL;
     if (out_dtype != QL_F16 && out_dtype != QL_F32 && !(x_dtype == QL_I8 && out_dtype == QL_BF16))
         return QL_ERR_DTYPE;
-    if (m < 1 || n < 16 || k < 128 || n % 16 || k % 128 || group_size < 128 || group_size % 128 ||
-        k % group_size || batch < 1 || batch > 65535)
+    if (m < 1 || n < 16 || k < 128 || n % 16 || k % 128 || group_size < 32 || group_size % 32 ||
+        k % group_size || k > 0x7fffffff || n > 0x7fffffff || batch < 1 || batch > 65535)
         return QL_ERR_SHAPE;
     if (!aligned16(x) || !aligned16(packed_w) || !aligned16(scales) || !aligned16(packed_zeros) ||
         !aligned16(out) || !aligned16(bias) || (per_token_scale && !aligned16(per_token_scale)))

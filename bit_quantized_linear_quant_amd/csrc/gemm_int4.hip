@@ -10,8 +10,17 @@
 // exactly 1024+q, and subtracting the pair (1024+z, 1024+z) gives (q - z)
 // exactly in fp16.  The x fragment of lane l in step t is the 8 halves of
 // its row at k = 128kb + 32(l/16) + 8t, the same k as the weight fragment.
-// One 128-k block is four MFMA steps; its fp32 partial sum is closed before
-// the group scale multiplies it once (group_size is a multiple of 128).
+// One 128-k block is four MFMA steps; when group_size is a multiple of 128
+// its fp32 partial sum is closed before the group scale multiplies it once.
+//
+// Smaller groups (group_size a multiple of 32): in the packed layout one step
+// takes its 32 k from four different 32-k sub-blocks (8 k from each 16-lane
+// row of the wave), so a per-step scale cannot be applied.  These launches
+// transpose each lane's four words across the four 16-lane rows
+// (quad_transpose), after which step t covers exactly the 32-k sub-block t
+// of the block (k 32t + 8q in row q, and the x fragments are read in the same
+// order), and every step's fp32 partial is scaled by its own group's scale
+// and offset by its own zero-point.
 //
 // x fragments reach the lanes through the wave's own LDS block
 // (rows256_to_fragments): x is loaded in whole cache lines, lane (r, q) taking
@@ -53,19 +62,43 @@ __device__ __forceinline__ v8h unpack_int4(uint32_t w, h2 zz) {
 // One k block's operands for the NBLK column blocks of a wave: packed
 // weight fragments, raw fp16 scales, zero-point words and the x fragments of
 // RB 16-row blocks.
-template <int NBLK, int RB>
+template <int NBLK, int RB, bool SUB>
 struct Stage {
     uint4 w[NBLK];
-    uint32_t s[NBLK], z[NBLK];
+    // SUB: per 32-k step, the scale's fp16 bits | zero-point << 16.
+    uint32_t s[NBLK][SUB ? 4 : 1], z[NBLK];
     v8h a[RB][4];
 };
+
+// Groups of the four 32-k sub-blocks 4 kb + t (t = 0..3) for group_size =
+// 32 * g32: one division, then a running remainder.
+__device__ __forceinline__ void subblock_groups(int64_t kb, int64_t g32, int64_t (&gt)[4]) {
+    const int64_t u0 = kb * 4;
+    int64_t g = u0 / g32, r = u0 - g * g32;
+#pragma unroll
+    for (int t = 0; t < 4; t++) {
+        gt[t] = g;
+        if (++r == g32) {
+            r = 0;
+            g++;
+        }
+    }
+}
+
+// Scale bits | zero-point << 16 of column col in group g.
+__device__ __forceinline__ uint32_t scale_zero(const uint16_t *__restrict__ scales,
+                                               const uint32_t *__restrict__ packed_z, int64_t col, int64_t g,
+                                               int64_t groups, int64_t n) {
+    const uint32_t zw = packed_z[g * (n / 8) + col / 8] >> (4 * (col % 8));
+    return (uint32_t)scales[col * groups + g] | ((zw & 15u) << 16);
+}
 
 // Issue every load of k block kb (clamped into range; the caller masks a
 // block past the end).  All loads are unconditional, so none of them waits
 // for another.
-template <int NBLK, int RB>
-__device__ __forceinline__ void load_stage(Stage<NBLK, RB> &st, const uint16_t *__restrict__ x, int64_t row0, int64_t m,
-                                           int64_t k,
+template <int NBLK, int RB, bool SUB>
+__device__ __forceinline__ void load_stage(Stage<NBLK, RB, SUB> &st, const uint16_t *__restrict__ x, int64_t row0,
+                                           int64_t m, int64_t k,
                                            const uint32_t *__restrict__ packed_w,
                                            const uint16_t *__restrict__ scales,
                                            const uint32_t *__restrict__ packed_z, int64_t kb,
@@ -73,14 +106,27 @@ __device__ __forceinline__ void load_stage(Stage<NBLK, RB> &st, const uint16_t *
                                            int64_t group_size, int64_t groups, int64_t n, int lane) {
     const int fr = lane % 16;
     const int64_t kbc = kb < kblocks ? kb : kblocks - 1;
-    const int64_t g = kbc * 128 / group_size;
+    if constexpr (SUB) {
+        int64_t gt[4];
+        subblock_groups(kbc, group_size / 32, gt);
 #pragma unroll
-    for (int j = 0; j < NBLK; j++) {
-        const int64_t nbc = nb0 + j < nblocks ? nb0 + j : nblocks - 1;
-        const int64_t col = nbc * 16 + fr;
-        st.w[j] = load16_stream(packed_w + (nbc * kblocks + kbc) * 256 + 4 * lane);
-        st.s[j] = scales[col * groups + g];
-        st.z[j] = packed_z[g * (n / 8) + col / 8] >> (4 * (col % 8));
+        for (int j = 0; j < NBLK; j++) {
+            const int64_t nbc = nb0 + j < nblocks ? nb0 + j : nblocks - 1;
+            const int64_t col = nbc * 16 + fr;
+            st.w[j] = load16_stream(packed_w + (nbc * kblocks + kbc) * 256 + 4 * lane);
+#pragma unroll
+            for (int t = 0; t < 4; t++) st.s[j][t] = scale_zero(scales, packed_z, col, gt[t], groups, n);
+        }
+    } else {
+        const int64_t g = kbc * 128 / group_size;
+#pragma unroll
+        for (int j = 0; j < NBLK; j++) {
+            const int64_t nbc = nb0 + j < nblocks ? nb0 + j : nblocks - 1;
+            const int64_t col = nbc * 16 + fr;
+            st.w[j] = load16_stream(packed_w + (nbc * kblocks + kbc) * 256 + 4 * lane);
+            st.s[j][0] = scales[col * groups + g];
+            st.z[j] = packed_z[g * (n / 8) + col / 8] >> (4 * (col % 8));
+        }
     }
 #pragma unroll
     for (int b = 0; b < RB; b++)
@@ -96,15 +142,38 @@ __device__ __forceinline__ void load_stage(Stage<NBLK, RB> &st, const uint16_t *
 
 // Accumulate one k block: per column block, four MFMA steps per row block
 // into a fresh fp32 partial, then one multiply by the group scale.
-template <int NBLK, int RB>
-__device__ __forceinline__ void compute_stage(const Stage<NBLK, RB> &st, v4f (&acc)[RB][NBLK], bool kb_ok,
+template <int NBLK, int RB, bool SUB>
+__device__ __forceinline__ void compute_stage(const Stage<NBLK, RB, SUB> &st, v4f (&acc)[RB][NBLK], bool kb_ok,
                                               int64_t nb0, int64_t nblocks, uint8_t *xb, int lane) {
     v8h a[RB][4];
+    if constexpr (SUB) {
+        // Step t covers the 32-k sub-block t: per-step scale and zero-point.
+        rows256_to_subblock_fragments<RB>(st.a, a, xb, lane);
+#pragma unroll
+        for (int j = 0; j < NBLK; j++) {
+            const bool ok = kb_ok && nb0 + j < nblocks;
+            const uint4 wt = quad_transpose(st.w[j]);
+#pragma unroll
+            for (int t = 0; t < 4; t++) {
+                const uint32_t sz = st.s[j][t];
+                const float sc = ok ? f16_bits_to_f32(sz & 0xffffu) : 0.0f;
+                const h2 zz = __builtin_bit_cast(h2, (0x6400u | ((sz >> 16) & 15u)) * 0x00010001u);
+                const v8h wv = unpack_int4(word_of(wt, t), zz);
+#pragma unroll
+                for (int b = 0; b < RB; b++) {
+                    const v4f p = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[b][t], wv, v4f{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+#pragma unroll
+                    for (int r = 0; r < 4; r++) acc[b][j][r] = __builtin_fmaf(sc, p[r], acc[b][j][r]);
+                }
+            }
+        }
+        return;
+    }
     rows256_to_fragments<RB>(st.a, a, xb, lane);
 #pragma unroll
     for (int j = 0; j < NBLK; j++) {
         const bool ok = kb_ok && nb0 + j < nblocks;
-        const float sc = ok ? f16_bits_to_f32(st.s[j]) : 0.0f;
+        const float sc = ok ? f16_bits_to_f32(st.s[j][0]) : 0.0f;
         const h2 zz = __builtin_bit_cast(h2, (0x6400u | (st.z[j] & 15u)) * 0x00010001u);
         v4f p[RB];
 #pragma unroll
@@ -122,7 +191,7 @@ __device__ __forceinline__ void compute_stage(const Stage<NBLK, RB> &st, v4f (&a
     }
 }
 
-template <int NBLK, int WAVES, int RB, int OUT, int NST>
+template <int NBLK, int WAVES, int RB, int OUT, int NST, bool SUB>
 __global__ __launch_bounds__(WAVES * 64) void int4_grouped_kernel(const uint16_t *__restrict__ x,
                                                                   const uint32_t *__restrict__ packed_w,
                                                                   const uint16_t *__restrict__ scales,
@@ -162,7 +231,7 @@ __global__ __launch_bounds__(WAVES * 64) void int4_grouped_kernel(const uint16_t
     // order, so both give the same bits.
     if constexpr (NST > 0) {
         for (int64_t kb0 = wave; kb0 < kblocks; kb0 += (int64_t)WAVES * NST) {
-            Stage<NBLK, RB> st[NST];
+            Stage<NBLK, RB, SUB> st[NST];
 #pragma unroll
             for (int u = 0; u < NST; u++)
                 load_stage(st[u], x, row0, m, k, packed_w, scales, packed_z, kb0 + (int64_t)u * WAVES, nb0, nblocks, kblocks,
@@ -172,7 +241,7 @@ __global__ __launch_bounds__(WAVES * 64) void int4_grouped_kernel(const uint16_t
                 compute_stage(st[u], acc, kb0 + (int64_t)u * WAVES < kblocks, nb0, nblocks, xb, lane);
         }
     } else {
-        Stage<NBLK, RB> s0, s1;
+        Stage<NBLK, RB, SUB> s0, s1;
         int64_t kb = wave;
         load_stage(s0, x, row0, m, k, packed_w, scales, packed_z, kb, nb0, nblocks, kblocks, group_size, groups, n, lane);
         while (kb < kblocks) {
@@ -216,23 +285,24 @@ __global__ __launch_bounds__(WAVES * 64) void int4_grouped_kernel(const uint16_t
 // Waves with at most this many k blocks issue all their loads at once.
 constexpr int kAllIn = 4;
 
-template <int NBLK, int WAVES, int RB, int OUT>
+template <int NBLK, int WAVES, int RB, int OUT, bool SUB>
 hipError_t launch_cfg(const uint16_t *x, const uint32_t *packed_w, const uint16_t *scales,
                       const uint32_t *packed_z, const float *bias, int64_t group_size, int64_t m, int64_t n, int64_t k,
                       void *out, hipStream_t st, int64_t batch) {
     const int64_t nblocks = n / 16;
     dim3 grid((unsigned)((nblocks + NBLK - 1) / NBLK), (unsigned)((m + 16 * RB - 1) / (16 * RB)), (unsigned)batch);
     // With two row blocks, four stages of x fragments do not fit beside the
-    // weights in registers: those launches keep the two-stage pipeline.
-    if constexpr (RB == 1) {
+    // weights in registers, nor do four stages of per-step scales: those
+    // launches keep the two-stage pipeline.
+    if constexpr (RB == 1 && !SUB) {
         if (k / 128 <= (int64_t)WAVES * kAllIn) {
-            hipLaunchKernelGGL((int4_grouped_kernel<NBLK, WAVES, RB, OUT, kAllIn>), grid, dim3(WAVES * 64), 0, st, x,
-                               packed_w, scales, packed_z, bias, group_size, m, n, k, out);
+            hipLaunchKernelGGL((int4_grouped_kernel<NBLK, WAVES, RB, OUT, kAllIn, SUB>), grid, dim3(WAVES * 64), 0,
+                               st, x, packed_w, scales, packed_z, bias, group_size, m, n, k, out);
             return hipGetLastError();
         }
     }
-    hipLaunchKernelGGL((int4_grouped_kernel<NBLK, WAVES, RB, OUT, 0>), grid, dim3(WAVES * 64), 0, st, x, packed_w,
-                       scales, packed_z, bias, group_size, m, n, k, out);
+    hipLaunchKernelGGL((int4_grouped_kernel<NBLK, WAVES, RB, OUT, 0, SUB>), grid, dim3(WAVES * 64), 0, st, x,
+                       packed_w, scales, packed_z, bias, group_size, m, n, k, out);
     return hipGetLastError();
 }
 
@@ -241,9 +311,18 @@ hipError_t launch_t(const uint16_t *x, const uint32_t *packed_w, const uint16_t 
                     const uint32_t *packed_z, const float *bias, int64_t group_size, int64_t m, int64_t n, int64_t k,
                     void *out, hipStream_t st, int64_t batch) {
     // m <= 16 needs one 16-row MFMA block; larger m takes 32-row slices so
-    // every unpacked weight fragment serves two row blocks.
-    if (m <= 16) return launch_cfg<3, 8, 1, OUT>(x, packed_w, scales, packed_z, bias, group_size, m, n, k, out, st, batch);
-    return launch_cfg<3, 8, 2, OUT>(x, packed_w, scales, packed_z, bias, group_size, m, n, k, out, st, batch);
+    // every unpacked weight fragment serves two row blocks.  Groups smaller
+    // than a 128-k block (or not aligned to one) take the per-step variant.
+    if (group_size % 128 != 0) {
+        if (m <= 16)
+            return launch_cfg<3, 8, 1, OUT, true>(x, packed_w, scales, packed_z, bias, group_size, m, n, k, out, st,
+                                                  batch);
+        return launch_cfg<3, 8, 2, OUT, true>(x, packed_w, scales, packed_z, bias, group_size, m, n, k, out, st,
+                                              batch);
+    }
+    if (m <= 16)
+        return launch_cfg<3, 8, 1, OUT, false>(x, packed_w, scales, packed_z, bias, group_size, m, n, k, out, st, batch);
+    return launch_cfg<3, 8, 2, OUT, false>(x, packed_w, scales, packed_z, bias, group_size, m, n, k, out, st, batch);
 }
 
 // ---------------------------------------------------------------------------
@@ -272,16 +351,17 @@ __device__ __forceinline__ v4i weight_step(const uint4 &w, int s) {
     return v4i{b0, b1, b2, b3};
 }
 
-template <int NBLK, int RB>
+template <int NBLK, int RB, bool SUB>
 struct StageI8 {
     uint4 w[NBLK];
-    uint32_t s[NBLK], z[NBLK];
+    // SUB: per 32-k step, the scale's fp16 bits | zero-point << 16.
+    uint32_t s[NBLK][SUB ? 4 : 1], z[NBLK];
     v4i a[RB][2];
 };
 
-template <int NBLK, int RB>
-__device__ __forceinline__ void load_stage_i8(StageI8<NBLK, RB> &st, const int8_t *__restrict__ xq, int64_t row0,
-                                              int64_t m, int64_t k,
+template <int NBLK, int RB, bool SUB>
+__device__ __forceinline__ void load_stage_i8(StageI8<NBLK, RB, SUB> &st, const int8_t *__restrict__ xq,
+                                              int64_t row0, int64_t m, int64_t k,
                                               const uint32_t *__restrict__ packed_w,
                                               const uint16_t *__restrict__ scales,
                                               const uint32_t *__restrict__ packed_z, int64_t kb, int64_t nb0,
@@ -289,14 +369,27 @@ __device__ __forceinline__ void load_stage_i8(StageI8<NBLK, RB> &st, const int8_
                                               int64_t groups, int64_t n, int lane) {
     const int fr = lane % 16;
     const int64_t kbc = kb < kblocks ? kb : kblocks - 1;
-    const int64_t g = kbc * 128 / group_size;
+    if constexpr (SUB) {
+        int64_t gt[4];
+        subblock_groups(kbc, group_size / 32, gt);
 #pragma unroll
-    for (int j = 0; j < NBLK; j++) {
-        const int64_t nbc = nb0 + j < nblocks ? nb0 + j : nblocks - 1;
-        const int64_t col = nbc * 16 + fr;
-        st.w[j] = load16_stream(packed_w + (nbc * kblocks + kbc) * 256 + 4 * lane);
-        st.s[j] = scales[col * groups + g];
-        st.z[j] = packed_z[g * (n / 8) + col / 8] >> (4 * (col % 8));
+        for (int j = 0; j < NBLK; j++) {
+            const int64_t nbc = nb0 + j < nblocks ? nb0 + j : nblocks - 1;
+            const int64_t col = nbc * 16 + fr;
+            st.w[j] = load16_stream(packed_w + (nbc * kblocks + kbc) * 256 + 4 * lane);
+#pragma unroll
+            for (int t = 0; t < 4; t++) st.s[j][t] = scale_zero(scales, packed_z, col, gt[t], groups, n);
+        }
+    } else {
+        const int64_t g = kbc * 128 / group_size;
+#pragma unroll
+        for (int j = 0; j < NBLK; j++) {
+            const int64_t nbc = nb0 + j < nblocks ? nb0 + j : nblocks - 1;
+            const int64_t col = nbc * 16 + fr;
+            st.w[j] = load16_stream(packed_w + (nbc * kblocks + kbc) * 256 + 4 * lane);
+            st.s[j][0] = scales[col * groups + g];
+            st.z[j] = packed_z[g * (n / 8) + col / 8] >> (4 * (col % 8));
+        }
     }
 #pragma unroll
     for (int b = 0; b < RB; b++)
@@ -334,9 +427,69 @@ __device__ __forceinline__ void x_fragments_i8(const v4i (&in)[RB][2], v4i (&fra
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-template <int NBLK, int RB>
-__device__ __forceinline__ void compute_stage_i8(const StageI8<NBLK, RB> &st, v4f (&acc)[RB][NBLK], int64_t nb0,
+// Sub-block fragments of the int8 codes: fragment t of lane (r, q) is the
+// 8 bytes at k 32t + 8q of row r (the same k as word t of the transposed
+// weight fragment).  Writes as x_fragments_i8; 8-byte reads.
+template <int RB>
+__device__ __forceinline__ void x_subblock_fragments_i8(const v4i (&in)[RB][2], long (&frag)[RB][4], uint8_t *xb,
+                                                        int lane) {
+    const int fr = lane % 16, q = lane / 16;
+#pragma unroll
+    for (int b = 0; b < RB; b++)
+#pragma unroll
+        for (int s = 0; s < 2; s++)
+            *reinterpret_cast<v4i *>(xb + (16 * b + 8 * s + lane / 8) * kXPitchI8 + 16 * (lane % 8)) = in[b][s];
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+    for (int b = 0; b < RB; b++)
+#pragma unroll
+        for (int t = 0; t < 4; t++)
+            frag[b][t] = *reinterpret_cast<const long *>(xb + (16 * b + fr) * kXPitchI8 + 32 * t + 8 * q);
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+template <int NBLK, int RB, bool SUB>
+__device__ __forceinline__ void compute_stage_i8(const StageI8<NBLK, RB, SUB> &st, v4f (&acc)[RB][NBLK], int64_t nb0,
                                                  int64_t nblocks, uint8_t *xb, int lane) {
+    if constexpr (SUB) {
+        // Step t (v_mfma_i32_16x16x32_i8) covers the 32-k sub-block t, whose
+        // exact int32 partial gets its own zero-point and scale.
+        const long ones = 0x0101010101010101l;
+        long a[RB][4];
+        x_subblock_fragments_i8<RB>(st.a, a, xb, lane);
+        v4i sx[RB][4];
+#pragma unroll
+        for (int b = 0; b < RB; b++)
+#pragma unroll
+            for (int t = 0; t < 4; t++)
+                sx[b][t] = __builtin_amdgcn_mfma_i32_16x16x32_i8(a[b][t], ones, v4i{0, 0, 0, 0}, 0, 0, 0);
+#pragma unroll
+        for (int j = 0; j < NBLK; j++) {
+            const bool ok = nb0 + j < nblocks;
+            const uint4 wt = quad_transpose(st.w[j]);
+#pragma unroll
+            for (int t = 0; t < 4; t++) {
+                const uint32_t sz = st.s[j][t];
+                const float sc = ok ? f16_bits_to_f32(sz & 0xffffu) : 0.0f;
+                const int z = (int)((sz >> 16) & 15u);
+                int lo, hi;
+                nibbles_to_bytes(word_of(wt, t), lo, hi);
+                const long wv = (long)(((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo);
+#pragma unroll
+                for (int b = 0; b < RB; b++) {
+                    const v4i p = __builtin_amdgcn_mfma_i32_16x16x32_i8(a[b][t], wv, v4i{0, 0, 0, 0}, 0, 0, 0);
+#pragma unroll
+                    for (int r = 0; r < 4; r++)
+                        acc[b][j][r] = __builtin_fmaf(sc, (float)(p[r] - z * sx[b][t][r]), acc[b][j][r]);
+                }
+            }
+        }
+        return;
+    }
     const v4i ones = v4i{0x01010101, 0x01010101, 0x01010101, 0x01010101};
     v4i a[RB][2];
     x_fragments_i8<RB>(st.a, a, xb, lane);
@@ -348,7 +501,7 @@ __device__ __forceinline__ void compute_stage_i8(const StageI8<NBLK, RB> &st, v4
     }
 #pragma unroll
     for (int j = 0; j < NBLK; j++) {
-        const float sc = nb0 + j < nblocks ? f16_bits_to_f32(st.s[j]) : 0.0f;
+        const float sc = nb0 + j < nblocks ? f16_bits_to_f32(st.s[j][0]) : 0.0f;
         const int z = (int)(st.z[j] & 15u);
         const v4i w0 = weight_step(st.w[j], 0), w1 = weight_step(st.w[j], 1);
 #pragma unroll
@@ -361,7 +514,7 @@ __device__ __forceinline__ void compute_stage_i8(const StageI8<NBLK, RB> &st, v4
     }
 }
 
-template <int NBLK, int WAVES, int RB, int OUT, int NST>
+template <int NBLK, int WAVES, int RB, int OUT, int NST, bool SUB>
 __global__ __launch_bounds__(WAVES * 64) void int4_grouped_i8_kernel(const int8_t *__restrict__ xq,
                                                                      const float *__restrict__ pts,
                                                                      const uint32_t *__restrict__ packed_w,
@@ -407,7 +560,7 @@ __global__ __launch_bounds__(WAVES * 64) void int4_grouped_i8_kernel(const int8_
     // together; NST = 0 pipelines two register stages.  Same order, same bits.
     if constexpr (NST > 0) {
         for (int64_t kb0 = wave; kb0 < kblocks; kb0 += (int64_t)WAVES * NST) {
-            StageI8<NBLK, RB> st[NST];
+            StageI8<NBLK, RB, SUB> st[NST];
 #pragma unroll
             for (int u = 0; u < NST; u++)
                 load_stage_i8(st[u], xq, row0, m, k, packed_w, scales, packed_z, kb0 + (int64_t)u * WAVES, nb0, nblocks,
@@ -417,7 +570,7 @@ __global__ __launch_bounds__(WAVES * 64) void int4_grouped_i8_kernel(const int8_
                 if (kb0 + (int64_t)u * WAVES < kblocks) compute_stage_i8(st[u], acc, nb0, nblocks, xb, lane);
         }
     } else {
-        StageI8<NBLK, RB> s0, s1;
+        StageI8<NBLK, RB, SUB> s0, s1;
         int64_t kb = wave;
         load_stage_i8(s0, xq, row0, m, k, packed_w, scales, packed_z, kb, nb0, nblocks, kblocks, group_size, groups, n, lane);
         while (kb < kblocks) {
@@ -459,17 +612,20 @@ __global__ __launch_bounds__(WAVES * 64) void int4_grouped_i8_kernel(const int8_
     }
 }
 
-template <int NBLK, int WAVES, int RB, int OUT>
+template <int NBLK, int WAVES, int RB, int OUT, bool SUB>
 hipError_t launch_cfg_i8(const int8_t *xq, const float *pts, const uint32_t *packed_w, const uint16_t *scales,
                          const uint32_t *packed_z, const float *bias, int64_t group_size, int64_t m, int64_t n, int64_t k, void *out,
                          hipStream_t st, int64_t batch) {
     const int64_t nblocks = n / 16;
     dim3 grid((unsigned)((nblocks + NBLK - 1) / NBLK), (unsigned)((m + 16 * RB - 1) / (16 * RB)), (unsigned)batch);
-    if (k / 128 <= (int64_t)WAVES * kAllIn)
-        hipLaunchKernelGGL((int4_grouped_i8_kernel<NBLK, WAVES, RB, OUT, kAllIn>), grid, dim3(WAVES * 64), 0, st, xq,
-                           pts, packed_w, scales, packed_z, bias, group_size, m, n, k, out);
+    // Four stages of per-step scales beside two row blocks of codes do not
+    // fit in registers: that launch keeps the two-stage pipeline.
+    if (k / 128 <= (int64_t)WAVES * kAllIn && !(SUB && RB == 2))
+        hipLaunchKernelGGL((int4_grouped_i8_kernel<NBLK, WAVES, RB, OUT, (SUB && RB == 2) ? 0 : kAllIn, SUB>), grid,
+                           dim3(WAVES * 64), 0, st, xq, pts, packed_w, scales, packed_z, bias, group_size, m, n, k,
+                           out);
     else
-        hipLaunchKernelGGL((int4_grouped_i8_kernel<NBLK, WAVES, RB, OUT, 0>), grid, dim3(WAVES * 64), 0, st, xq,
+        hipLaunchKernelGGL((int4_grouped_i8_kernel<NBLK, WAVES, RB, OUT, 0, SUB>), grid, dim3(WAVES * 64), 0, st, xq,
                            pts, packed_w, scales, packed_z, bias, group_size, m, n, k, out);
     return hipGetLastError();
 }
@@ -478,9 +634,18 @@ template <int OUT>
 hipError_t launch_i8_t(const int8_t *xq, const float *pts, const uint32_t *packed_w, const uint16_t *scales,
                        const uint32_t *packed_z, const float *bias, int64_t group_size, int64_t m, int64_t n, int64_t k, void *out,
                        hipStream_t st, int64_t batch) {
+    if (group_size % 128 != 0) {
+        if (m <= 16)
+            return launch_cfg_i8<3, 8, 1, OUT, true>(xq, pts, packed_w, scales, packed_z, bias, group_size, m, n, k, out,
+                                                     st, batch);
+        return launch_cfg_i8<3, 8, 2, OUT, true>(xq, pts, packed_w, scales, packed_z, bias, group_size, m, n, k, out, st,
+                                                 batch);
+    }
     if (m <= 16)
-        return launch_cfg_i8<3, 8, 1, OUT>(xq, pts, packed_w, scales, packed_z, bias, group_size, m, n, k, out, st, batch);
-    return launch_cfg_i8<3, 8, 2, OUT>(xq, pts, packed_w, scales, packed_z, bias, group_size, m, n, k, out, st, batch);
+        return launch_cfg_i8<3, 8, 1, OUT, false>(xq, pts, packed_w, scales, packed_z, bias, group_size, m, n, k, out, st,
+                                                  batch);
+    return launch_cfg_i8<3, 8, 2, OUT, false>(xq, pts, packed_w, scales, packed_z, bias, group_size, m, n, k, out, st,
+                                              batch);
 }
 
 }  // namespace

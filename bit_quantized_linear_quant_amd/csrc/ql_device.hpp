@@ -95,6 +95,45 @@ __device__ __forceinline__ void rows256_to_fragments(const T (&in)[RB][4], T (&f
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
+// As rows256_to_fragments, with the fragments of 32-k sub-blocks: fragment t
+// of lane (r, q) is the 16-byte piece t * 4 + q of row r (k 32t + 8q of the
+// 128-k block for 16-bit elements), so that one matrix-core step covers one
+// contiguous 32-k range.  Same LDS block, same ordering.
+template <int RB, typename T>
+__device__ __forceinline__ void rows256_to_subblock_fragments(const T (&in)[RB][4], T (&frag)[RB][4], uint8_t *xb,
+                                                              int lane) {
+    static_assert(sizeof(T) == 16, "16-byte pieces");
+    const int fr = lane % 16, q = lane / 16;
+#pragma unroll
+    for (int b = 0; b < RB; b++)
+#pragma unroll
+        for (int t = 0; t < 4; t++)
+            *reinterpret_cast<T *>(xb + (16 * b + 4 * t + q) * kRow256Pitch + 16 * fr) = in[b][t];
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+    for (int b = 0; b < RB; b++)
+#pragma unroll
+        for (int t = 0; t < 4; t++)
+            frag[b][t] = *reinterpret_cast<const T *>(xb + (16 * b + fr) * kRow256Pitch + 64 * t + 16 * q);
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// Transpose of four 32-bit words across the four 16-lane rows of a wave: on
+// return, word t of the lane in row q holds what word q of the lane in the
+// same column of row t held.  Two v_permlane32_swap (rows 0-1 with rows 2-3)
+// and two v_permlane16_swap (even rows with odd rows).
+__device__ __forceinline__ uint4 quad_transpose(uint4 v) {
+    const auto a = __builtin_amdgcn_permlane32_swap(v.x, v.z, false, false);
+    const auto b = __builtin_amdgcn_permlane32_swap(v.y, v.w, false, false);
+    const auto c = __builtin_amdgcn_permlane16_swap(a[0], b[0], false, false);
+    const auto d = __builtin_amdgcn_permlane16_swap(a[1], b[1], false, false);
+    return make_uint4(c[0], c[1], d[0], d[1]);
+}
+
 // Workgroup id -> (tile row, tile column) for a grid of tiles_m x tiles_n
 // output tiles.  The hardware hands consecutive workgroup ids to the 8 XCDs in
 // turn; ids are first regrouped so each XCD receives a contiguous range of

@@ -272,20 +272,24 @@ ql_status qlinear_gemm_w2a8(const int8_t *xq, const float *per_token_scale,
  *   x_dtype QL_F16: x [m, k] fp16 activations,
  *     out[m][n] = sum_g s[n][g] * sum_{k in g} x[m][k] * (q[n][k] - z[n][g]);
  *     (q - z) is formed exactly in fp16, products accumulate in fp32 per
- *     128-k block and each block's partial sum is scaled once.
+ *     128-k block (group_size a multiple of 128) or per 32-k step (other
+ *     group sizes) and each partial sum is scaled once by its group's scale.
  *     per_token_scale is ignored.  out QL_F16, or QL_F32 for the value before
  *     rounding.
  *   x_dtype QL_I8: x [m, k] int8 activation codes with per_token_scale [m]
  *     fp32 (qlinear_quant_act; [BL] steps 2 and 5),
  *     out[m][n] = pts[m] * sum_g s[n][g] * sum_{k in g} xq[m][k] * (q[n][k] - z[n][g]);
- *     each 128-k block's integer sum is exact (int32), scaled by s in fp32;
- *     pts multiplies the final sum.  out QL_F16, QL_BF16 or QL_F32.
+ *     each 128-k block's (or, for group sizes that are not multiples of
+ *     128, each 32-k step's) integer sum is exact (int32), scaled by s in
+ *     fp32; pts multiplies the final sum.  out QL_F16, QL_BF16 or QL_F32.
  *   packed_w from qlinear_pack_int4(QL_INT4_WEIGHT);
  *   scales [n, k/group_size] fp16 (row-major, one per column and group);
  *   packed_zeros from qlinear_pack_int4(QL_INT4_ZEROS) of z [n, groups];
  *   bias [n] fp32 or NULL, added to the fp32 value before the output
  *   rounding (QL_BIAS below).
- * n % 16 == 0, k % 128 == 0, group_size % 128 == 0, k % group_size == 0.
+ * n % 16 == 0, k % 128 == 0, group_size >= 32, group_size % 32 == 0 (one
+ * matrix-core step, so no step straddles two groups), k % group_size == 0,
+ * n, k < 2^31.  Errors: QL_ERR_NULL, QL_ERR_SHAPE, QL_ERR_DTYPE, QL_ERR_ALIGN.
  */
 ql_status qlinear_gemm_w4a8_grouped(const void *x, ql_dtype x_dtype,
                                     const float *per_token_scale,

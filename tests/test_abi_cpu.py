@@ -137,8 +137,12 @@ def test_gemm_validation(L):
     assert gb(2, A, ql.QL_I8, NULL, A, A, A, 128, 1, 16, 128, NULL, ql.QL_F16, A, NULL) == -1       # needs pts
     assert gb(2, A, ql.QL_F16, NULL, A, A, A, 128, 1, 24, 128, NULL, ql.QL_F16, A, NULL) == -2      # n % 16
     assert gb(2, A, ql.QL_F16, NULL, A, A, A, 128, 1, 16, 128, U, ql.QL_F16, A, NULL) == -4         # bias alignment
-    assert g4(A, ql.QL_F16, NULL, A, A, A, 64, 1, 16, 128, NULL, ql.QL_F16, A, NULL) == -2
-    assert g4(A, ql.QL_F16, NULL, A, A, A, 256, 1, 16, 384, NULL, ql.QL_F16, A, NULL) == -2
+    assert g4(A, ql.QL_F16, NULL, A, A, A, 48, 1, 16, 128, NULL, ql.QL_F16, A, NULL) == -2   # group % 32
+    assert g4(A, ql.QL_F16, NULL, A, A, A, 16, 1, 16, 128, NULL, ql.QL_F16, A, NULL) == -2
+    assert g4(A, ql.QL_F16, NULL, A, A, A, 0, 1, 16, 128, NULL, ql.QL_F16, A, NULL) == -2
+    assert g4(A, ql.QL_F16, NULL, A, A, A, 256, 1, 16, 384, NULL, ql.QL_F16, A, NULL) == -2  # k % group
+    assert g4(A, ql.QL_F16, NULL, A, A, A, 96, 1, 16, 320, NULL, ql.QL_F16, A, NULL) == -2   # k % 128
+    assert g4(A, ql.QL_F16, NULL, A, A, A, 64, 1, 16, 128, NULL, ql.QL_U8, A, NULL) == -3    # 32 | 64 accepted
     assert g4(A, ql.QL_F16, NULL, A, A, A, 128, 1, 16, 128, U, ql.QL_F16, A, NULL) == -4  # bias alignment
     assert g4(A, ql.QL_F16, NULL, A, A, A, 128, 1, 16, 128, NULL, ql.QL_BF16, A, NULL) == -3
     qo = L.qlinear_quant_a4w4_operand

@@ -5,7 +5,7 @@ benchmark times.
   BitLinear    x bf16 [2048, 4096] (1 % outliers x20), RMSNorm eps 1e-6,
                fp32 weight [4096, 4096] -> ternary, bf16 out
   Decode GEMV  M in {1, 4, 16}, K = 8192, N = 28672, bf16 out
-  Grouped INT4 fp16 x [32, 4096], uint4 weight [11008, 4096], g = 128
+  Grouped INT4 fp16 x [32, 4096], uint4 weight [11008, 4096], g = 128 (and 64, 32)
   A4W4         fp16 x, w [8192, 8192], per-tensor scales max|t| / 7
 
 Codes, packed words and per-token scales are compared in full.  Products are
@@ -118,9 +118,11 @@ def test_decode_gemv_full_workload(decode_case, m):
     assert_float_close(ob, y, "decode bf16")
 
 
-def test_grouped_int4_full_workload():
-    d = synthetic.grouped_int4()
-    m, n, k, gs = 32, 11008, 4096, d["group_size"]
+@pytest.mark.parametrize("gs", [128, 64, 32])
+def test_grouped_int4_full_workload(gs):
+    """32 x 4096 x 11008 at the workload's group size 128 and at 64 and 32 (per-step scales)."""
+    d = synthetic.grouped_int4(group_size=gs)
+    m, n, k = 32, 11008, 4096
     y, bound = oracle.grouped_int4(d["x"].float().numpy(), d["q"].numpy(), d["s"].float().numpy(),
                                    d["z"].numpy(), gs)
     pw = ql.qlinear_pack_int4(_cuda(d["q"]), ql.QL_INT4_WEIGHT)
@@ -137,11 +139,12 @@ def test_grouped_int4_full_workload():
     assert torch.equal(o16, o32.to(torch.float16))
 
 
-def test_grouped_int4_i8_full_shape():
+@pytest.mark.parametrize("gs", [128, 32])
+def test_grouped_int4_i8_full_shape(gs):
     """The grouped INT4 weights with int8 activation codes (quantized from the fp16
-    activations of the same workload) at 32x4096x11008, g = 128."""
-    d = synthetic.grouped_int4()
-    m, n, k, gs = 32, 11008, 4096, d["group_size"]
+    activations of the same workload) at 32x4096x11008, g = 128 and 32."""
+    d = synthetic.grouped_int4(group_size=gs)
+    m, n, k = 32, 11008, 4096
     xq_ref, pts_ref, _ = oracle.quant_act(d["x"].float().numpy())
     y, bound = oracle.grouped_int4_i8(xq_ref, pts_ref, d["q"].numpy(), d["s"].float().numpy(), d["z"].numpy(), gs)
     xq, pts, _ = ql.qlinear_quant_act(_cuda(d["x"]))
