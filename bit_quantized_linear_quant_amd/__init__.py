@@ -40,7 +40,7 @@ _lib = None
 
 
 # QL_ABI_VERSION of include/qlinear.h that the argument lists below follow.
-ABI_VERSION = 5
+ABI_VERSION = 6
 
 
 class QLinearError(RuntimeError):
@@ -73,6 +73,7 @@ def lib() -> ctypes.CDLL:
             "qlinear_quant_act": (i32, [vp, i32, i64, i64, u32, f32, f32, vp, vp, vp, vp]),
             "qlinear_quant_int4_tensor": (i32, [vp, i32, i64, vp, f32, vp, vp]),
             "qlinear_pack_ternary": (i32, [vp, i32, i64, i64, f64, vp, vp, vp, sz, vp]),
+            "qlinear_pack_ternary_noalloc": (i32, [vp, i32, i64, i64, f64, vp, vp, vp]),
             "qlinear_pack_int4": (i32, [vp, i64, i64, i32, vp, vp]),
             "qlinear_gemm_w8a8": (i32, [vp, vp, i32, vp, vp, vp, i64, i64, i64, i32, vp, vp]),
             "qlinear_gemm_w8a8_batched": (i32, [vp, vp, i32, vp, i64, vp, vp, i64, i64, i64, i64, i32, vp, vp]),
@@ -196,6 +197,22 @@ def qlinear_pack_ternary(w, layout=QL_W_NK, eps=1e-5, packed=None, gamma=None, w
     _check("qlinear_pack_ternary", lib().qlinear_pack_ternary(
         _ptr(w), layout, n, k, float(eps), _ptr(packed), _ptr(gamma), _ptr(workspace),
         workspace.numel() * workspace.element_size(), _stream(w)))
+    return packed, gamma
+
+
+def qlinear_pack_ternary_noalloc(w, layout=QL_W_NK, eps=1e-5, packed=None, gamma=None):
+    """As ``qlinear_pack_ternary`` through the entry point that allocates nothing on the device.
+
+    The C function takes no workspace (its scratch is a static array of the library); output
+    tensors are still allocated here when not given.
+    """
+    _gpu(w, "w", torch.float32)
+    n, k = (w.shape if layout == QL_W_NK else (w.shape[1], w.shape[0]))
+    packed = _empty((n * k // 16,), torch.int32, w) if packed is None else _gpu(packed, "packed")
+    gamma = _empty((1,), torch.float64, w) if gamma is None else _gpu(gamma, "gamma", torch.float64)
+    _need(packed, n * k // 4, "packed")
+    _check("qlinear_pack_ternary_noalloc", lib().qlinear_pack_ternary_noalloc(
+        _ptr(w), layout, n, k, float(eps), _ptr(packed), _ptr(gamma), _stream(w)))
     return packed, gamma
 
 

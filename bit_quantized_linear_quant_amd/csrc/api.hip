@@ -109,6 +109,21 @@ ql_status qlinear_pack_ternary(const float *w, ql_wlayout layout, int64_t n, int
                                               static_cast<double *>(workspace), as_stream(stream)));
 }
 
+ql_status qlinear_pack_ternary_noalloc(const float *w, ql_wlayout layout, int64_t n, int64_t k, double eps,
+                                       uint32_t *packed, double *gamma, void *stream) {
+    if (!w || !packed || !gamma) return QL_ERR_NULL;
+    if (layout != QL_W_KN && layout != QL_W_NK) return QL_ERR_UNSUPPORTED;
+    if (n < 16 || k < 256 || n % 16 || k % 256) return QL_ERR_SHAPE;
+    if (!aligned16(w) || !aligned16(packed) || !aligned16(gamma)) return QL_ERR_ALIGN;
+    // The absmean partials must fit the library's static scratch.
+    if (n > ((int64_t)1 << 31) / k || (int64_t)ql::absmean_partial_count(n * k) > ql::kPackScratchPartials)
+        return QL_ERR_WORKSPACE;
+    double *partials = nullptr;
+    if (ql::pack_ternary_scratch(&partials) != hipSuccess) return QL_ERR_HIP;
+    return hip_status(ql::launch_pack_ternary(w, layout == QL_W_NK, n, k, eps, packed, gamma, partials,
+                                              as_stream(stream)));
+}
+
 ql_status qlinear_pack_int4(const uint8_t *codes, int64_t rows, int64_t cols, ql_int4_what what,
                             uint32_t *packed, void *stream) {
     if (!codes || !packed) return QL_ERR_NULL;

@@ -11,12 +11,25 @@
 //
 // 4-bit ("linear_4bit/mod.rs" module doc: eight nibbles per u32): weights
 // into the fragment-ordered layout, zero-points group-major.
+#include <atomic>
+
 #include "ql_device.hpp"
 #include "ql_launch.hpp"
 
 namespace ql {
 
 namespace {
+
+// Scratch of the allocation-free ternary pack: the fp64 chunk partials of
+// the absmean, one per 16384 weights, for at most kPackScratchPartials
+// chunks (1 MiB of device memory per GPU, held until the process ends).  In
+// host code `scratch` is a host-side stand-in, not a device address: host
+// code uses only the per-device pointer from hipGetSymbolAddress below.
+static __device__ __align__(256) double scratch[kPackScratchPartials];
+
+// Per-device address of `scratch`, found once per device.
+constexpr int kMaxDevices = 64;
+std::atomic<double *> g_scratch_ptr[kMaxDevices];
 
 constexpr int kPThreads = 256;
 constexpr int kChunkIters = 16;
@@ -231,6 +244,23 @@ hipError_t launch_pack_ternary(const float *w, bool layout_nk, int64_t n, int64_
         hipLaunchKernelGGL((pack_ternary_kernel<false>), dim3(blocks_for(nslices)), dim3(kPThreads),
                            0, st, w, n, k, gamma, packed, nslices);
     return hipGetLastError();
+}
+
+hipError_t pack_ternary_scratch(double **partials) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    double *p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+    if (p == nullptr) {
+        // Idempotent: threads racing here all store the same address.
+        e = hipGetSymbolAddress(reinterpret_cast<void **>(&p), HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        if (p == nullptr) return hipErrorInvalidSymbol;
+        g_scratch_ptr[dev].store(p, std::memory_order_release);
+    }
+    *partials = p;
+    return hipSuccess;
 }
 
 hipError_t launch_pack_int4_weight(const uint8_t *codes, int64_t n, int64_t k, uint32_t *packed,

@@ -25,6 +25,12 @@ hipError_t launch_quant_a4w4_tiles(int in_kind, const void *x, int64_t rows, int
 size_t absmean_partial_count(int64_t count);
 hipError_t launch_pack_ternary(const float *w, bool layout_nk, int64_t n, int64_t k, double eps,
                                uint32_t *packed, double *gamma, double *partials, hipStream_t st);
+// Capacity of the static scratch of the allocation-free ternary pack, in
+// fp64 chunk partials (absmean_partial_count of at most 2^31 weights).
+constexpr int64_t kPackScratchPartials = 131072;
+// Device address of that scratch on the current device (looked up once per
+// device with hipGetSymbolAddress; allocates nothing).
+hipError_t pack_ternary_scratch(double **partials);
 hipError_t launch_pack_int4_weight(const uint8_t *codes, int64_t n, int64_t k, uint32_t *packed,
                                    hipStream_t st);
 hipError_t launch_pack_int4_zeros(const uint8_t *z, int64_t n, int64_t groups, uint32_t *packed,

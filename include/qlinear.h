@@ -47,7 +47,7 @@
 extern "C" {
 #endif
 
-#define QL_ABI_VERSION 5
+#define QL_ABI_VERSION 6
 /* Version of the 2-bit ternary weight layout written by qlinear_pack_ternary. */
 #define QL_TERNARY_PACK_V1 1
 /* Version of the 4-bit weight layout written by qlinear_pack_int4. */
@@ -175,6 +175,25 @@ ql_status qlinear_quant_int4_tensor(const void *x, ql_dtype x_dtype, int64_t cou
 ql_status qlinear_pack_ternary(const float *w, ql_wlayout layout, int64_t n, int64_t k,
                                double eps, uint32_t *packed, double *gamma,
                                void *workspace, size_t ws_bytes, void *stream);
+
+/*
+ * qlinear_pack_ternary with no workspace argument and no device allocation,
+ * for callers that cannot allocate: code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc.  The absmean's fp64 chunk
+ * partials go to a static device array inside the library (1 MiB per GPU,
+ * held until the process ends), so n * k <= 2^31.  Same kernels, same
+ * gamma' and words as qlinear_pack_ternary.  The caller still owns w,
+ * packed and gamma.  All calls on one GPU share that array: calls that
+ * overlap on one GPU (different streams, or threads without ordering) race,
+ * and the caller must order them.  The device current at the call must be
+ * the stream's device.
+ * Errors: as qlinear_pack_ternary; QL_ERR_WORKSPACE when n * k > 2^31 (the
+ * static array's capacity); QL_ERR_HIP when the array's address cannot be
+ * obtained.
+ */
+ql_status qlinear_pack_ternary_noalloc(const float *w, ql_wlayout layout, int64_t n, int64_t k,
+                                       double eps, uint32_t *packed, double *gamma,
+                                       void *stream);
 
 /*
  * 4-bit pack ([L4] module doc: eight nibbles per u32 word).  Only the low

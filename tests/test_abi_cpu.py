@@ -40,7 +40,7 @@ def test_exports_every_declared_symbol(L):
 
 
 def test_abi_version_and_status_strings(L):
-    assert ql.qlinear_abi_version() == ql.ABI_VERSION == 5
+    assert ql.qlinear_abi_version() == ql.ABI_VERSION == 6
     for code, name in ql.STATUS.items():
         s = ql.qlinear_status_string(code)
         assert isinstance(s, str) and s
@@ -95,6 +95,15 @@ def test_pack_validation(L):
     assert f(A, ql.QL_W_NK, 16, 256, 1e-5, A, A, NULL, 1 << 20, NULL) == -5
     assert f(A, ql.QL_W_NK, 16, 256, 1e-5, A, A, A, 8, NULL) == -5         # too small
     assert f(A, 7, 16, 256, 1e-5, A, A, A, 1 << 20, NULL) == -6
+    nf = L.qlinear_pack_ternary_noalloc
+    assert nf(NULL, ql.QL_W_NK, 16, 256, 1e-5, A, A, NULL) == -1
+    assert nf(A, ql.QL_W_NK, 17, 256, 1e-5, A, A, NULL) == -2
+    assert nf(A, ql.QL_W_NK, 16, 300, 1e-5, A, A, NULL) == -2
+    assert nf(A, 7, 16, 256, 1e-5, A, A, NULL) == -6
+    assert nf(A, ql.QL_W_NK, 16, 256, 1e-5, U, A, NULL) == -4
+    # more than 2^31 weights: beyond the static scratch, rejected before any HIP call
+    assert nf(A, ql.QL_W_NK, 2 ** 23 + 16, 256, 1e-5, A, A, NULL) == -5
+    assert nf(A, ql.QL_W_NK, 1 << 40, 256, 1e-5, A, A, NULL) == -5
     g = L.qlinear_pack_int4
     assert g(A, 16, 100, ql.QL_INT4_WEIGHT, A, NULL) == -2
     assert g(A, 12, 4, ql.QL_INT4_ZEROS, A, NULL) == -2
