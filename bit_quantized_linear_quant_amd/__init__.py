@@ -19,7 +19,9 @@ import re
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libqlinear.so")
+# QLINEAR_LIB names another build of the same library (the sanitizer test
+# loads a host-ASan/UBSan build this way); the default is the in-tree build.
+LIB_PATH = os.environ.get("QLINEAR_LIB") or os.path.join(_HERE, "libqlinear.so")
 HEADER_PATH = os.path.join(os.path.dirname(_HERE), "include", "qlinear.h")
 
 # enums of qlinear.h

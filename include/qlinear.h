@@ -61,7 +61,11 @@ typedef enum ql_status {
     QL_ERR_ALIGN = -4,       /* a pointer is not 16-byte aligned */
     QL_ERR_WORKSPACE = -5,   /* workspace NULL or smaller than qlinear_workspace_bytes */
     QL_ERR_UNSUPPORTED = -6, /* a valid but not implemented combination */
-    QL_ERR_HIP = -7          /* the HIP runtime reported an error */
+    QL_ERR_HIP = -7,         /* the HIP runtime reported an error */
+    /* Range markers, never returned: they make every enum of this header span
+     * all 32-bit values, so any int a C caller passes is a valid value. */
+    QL_STATUS_MIN_ENUM = -0x7fffffff - 1,
+    QL_STATUS_MAX_ENUM = 0x7fffffff
 } ql_status;
 
 /* Element types.  QL_I32 as an output dtype exposes the raw int32
@@ -72,14 +76,18 @@ typedef enum ql_dtype {
     QL_BF16 = 2,
     QL_I8 = 3,
     QL_U8 = 4,
-    QL_I32 = 5
+    QL_I32 = 5,
+    QL_DTYPE_MIN_ENUM = -0x7fffffff - 1,
+    QL_DTYPE_MAX_ENUM = 0x7fffffff
 } ql_dtype;
 
 /* Weight layouts: [PT] Input gives weight [k, n]; [PT] Parameters
  * transposeB=true, and the nn.Linear weight of [BL], give [n, k]. */
 typedef enum ql_wlayout {
     QL_W_KN = 0,
-    QL_W_NK = 1
+    QL_W_NK = 1,
+    QL_WLAYOUT_MIN_ENUM = -0x7fffffff - 1,
+    QL_WLAYOUT_MAX_ENUM = 0x7fffffff
 } ql_wlayout;
 
 /* Flags of qlinear_quant_act. */
@@ -88,7 +96,9 @@ typedef enum ql_wlayout {
 /* What qlinear_pack_int4 packs. */
 typedef enum ql_int4_what {
     QL_INT4_WEIGHT = 0,
-    QL_INT4_ZEROS = 1
+    QL_INT4_ZEROS = 1,
+    QL_INT4_WHAT_MIN_ENUM = -0x7fffffff - 1,
+    QL_INT4_WHAT_MAX_ENUM = 0x7fffffff
 } ql_int4_what;
 
 /* Operations that take a workspace (qlinear_workspace_bytes). */
@@ -96,7 +106,9 @@ typedef enum ql_op {
     QL_OP_PACK_TERNARY = 0,
     QL_OP_GEMM_A4W4 = 1,
     QL_OP_A4W4_OPERAND = 2,
-    QL_OP_Q4_BACKWARD = 3
+    QL_OP_Q4_BACKWARD = 3,
+    QL_OP_MIN_ENUM = -0x7fffffff - 1,
+    QL_OP_MAX_ENUM = 0x7fffffff
 } ql_op;
 
 /* Returns QL_ABI_VERSION of the built library. */

@@ -32,7 +32,10 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "qlinear_oracle.c")
-_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+# QLINEAR_ORACLE_LIB names a prebuilt copy of the oracle to load instead (the
+# sanitizer test builds one with ASan/UBSan); it is never rebuilt from here.
+_LIB_OVERRIDE = os.environ.get("QLINEAR_ORACLE_LIB")
+_LIB_PATH = _LIB_OVERRIDE or os.path.join(_HERE, "liboracle.so")
 _lib = None
 
 # Plain C, no intrinsics, no BLAS.  -ffp-contract=off keeps every fl32 step
@@ -53,8 +56,8 @@ def build(force: bool = True) -> str:
 def _load():
     global _lib
     if _lib is None:
-        if not os.path.exists(_LIB_PATH) or (
-                os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC)):
+        if not _LIB_OVERRIDE and (not os.path.exists(_LIB_PATH) or (
+                os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC))):
             build(force=True)
         _lib = ctypes.CDLL(_LIB_PATH)
         i64, i32, f32, f64, vp = (ctypes.c_int64, ctypes.c_int, ctypes.c_float,
