@@ -79,6 +79,8 @@ def _load():
             "oracle_a4w4_operand_bytes": (i64, [i64, i64]),
             "oracle_q4_backward": (i32, [vp, vp, vp, f32, f32, f32, i64, i64, i64, vp, vp, vp, vp, vp, vp]),
             "oracle_pack_a4w4_fp6": (i32, [vp, i64, i64, vp]),
+            "oracle_a4w4_packed_bytes": (i64, [i64, i64]),
+            "oracle_pack_a4w4_int4": (i32, [vp, i64, i64, vp]),
             "oracle_round_f16": (None, [vp, i64, vp]),
             "oracle_round_bf16": (None, [vp, i64, vp]),
         }
@@ -393,6 +395,21 @@ def pack_a4w4_fp6(codes):
     rows, k = codes.shape
     out = np.zeros(a4w4_operand_bytes(rows, k), np.uint8)
     _check(_load().oracle_pack_a4w4_fp6(_p(codes), rows, k, _p(out)), "pack_a4w4_fp6")
+    return out
+
+
+def a4w4_packed_bytes(rows: int, k: int) -> int:
+    return int(_load().oracle_a4w4_packed_bytes(rows, k))
+
+
+def pack_a4w4_int4(codes):
+    """4-bit codes ``[rows, k]`` (int8, in [-8, 7]) as the packed 4-bit operand of
+    the 4-bit product: two codes per byte, stored as code + 8 (this project's
+    layout, defined in ``qlinear_oracle.c``).  Returns uint8 bytes."""
+    codes = _c(codes, np.int8)
+    rows, k = codes.shape
+    out = np.zeros(a4w4_packed_bytes(rows, k), np.uint8)
+    _check(_load().oracle_pack_a4w4_int4(_p(codes), rows, k, _p(out)), "pack_a4w4_int4")
     return out
 
 

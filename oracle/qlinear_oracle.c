@@ -605,6 +605,53 @@ int oracle_pack_a4w4_fp6(const int8_t *codes, int64_t rows, int64_t k, uint8_t *
 }
 
 /* ------------------------------------------------------------------ */
+/* A4W4 packed operand: two 4-bit codes per byte.                       */
+/* ------------------------------------------------------------------ */
+/*
+ * Not a format of the pages: this project's 4-bit storage of the codes of
+ * "Q4LinearFunction" forward, 0.5 byte per code.  Same tiling as the FP6
+ * operand above (rows padded with zero codes to a multiple of 32, k to a
+ * multiple of 128; tile (rb, ks) = rows 32rb .. 32rb+31, k 64ks .. 64ks+63),
+ * but a tile is 1024 bytes at (rb * (kp / 64) + ks) * 1024 and slot l
+ * (0..63) is the 16 bytes at tile byte 16l: row 32rb + l % 32, k
+ * 64ks + 32(l / 32) + j for j = 0..31.  Element j of a slot is in the
+ * little-endian 32-bit word j / 8 of the slot, in nibble p (bits 4p .. 4p+3)
+ * with p = e / 2 for even e = j % 8 and p = 4 + e / 2 for odd e, stored as
+ * code + 8 (in [0, 15]).
+ * Parity unpinned beyond its definition: tests decode it and compare codes.
+ */
+int64_t oracle_a4w4_packed_bytes(int64_t rows, int64_t k)
+{
+    int64_t rp = (rows + 31) / 32 * 32, kp = (k + 127) / 128 * 128;
+    return rp * kp / 2;
+}
+
+int oracle_pack_a4w4_int4(const int8_t *codes, int64_t rows, int64_t k, uint8_t *out)
+{
+    int64_t rp = (rows + 31) / 32 * 32, kp = (k + 127) / 128 * 128;
+    int64_t kt = kp / 64;
+    for (int64_t rb = 0; rb < rp / 32; rb++)
+        for (int64_t ks = 0; ks < kt; ks++) {
+            uint8_t *tile = out + (rb * kt + ks) * 1024;
+            for (int l = 0; l < 64; l++) {
+                uint32_t word[4] = {0, 0, 0, 0};
+                int64_t row = 32 * rb + l % 32;
+                for (int j = 0; j < 32; j++) {
+                    int64_t kk = 64 * ks + 32 * (l / 32) + j;
+                    int c = (row < rows && kk < k) ? codes[row * k + kk] : 0;
+                    int e = j % 8;
+                    int p = (e % 2 == 0) ? e / 2 : 4 + e / 2;
+                    word[j / 8] |= (uint32_t)(c + 8) << (4 * p);
+                }
+                for (int w = 0; w < 4; w++)
+                    for (int b = 0; b < 4; b++)
+                        tile[16 * l + 4 * w + b] = (uint8_t)(word[w] >> (8 * b));
+            }
+        }
+    return 0;
+}
+
+/* ------------------------------------------------------------------ */
 /* Output rounding: fp64 -> fp16 / bf16, round to nearest, ties to even. */
 /* ------------------------------------------------------------------ */
 /*

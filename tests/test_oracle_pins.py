@@ -561,6 +561,50 @@ def test_a4w4_fp6_operand_round_trip(rows, k):
     assert np.all(dec[rows:, :] == 0) and np.all(dec[:, k:] == 0)
 
 
+def _unpack_a4w4_int4(buf, rows, k):
+    """Decode the packed 4-bit operand by its written definition (tile (rb, ks)
+    of 1024 bytes, slot l at byte 16l: row 32rb + l%32, k 64ks + 32(l//32) + j;
+    element j in little-endian word j//8, nibble j%8//2 for even j%8 and
+    4 + j%8//2 for odd, holding code + 8)."""
+    rp, kp = -(-rows // 32) * 32, -(-k // 128) * 128
+    out = np.full((rp, kp), np.nan)
+    for rb in range(rp // 32):
+        for ks in range(kp // 64):
+            t = (rb * (kp // 64) + ks) * 1024
+            for l in range(64):
+                words = [int.from_bytes(bytes(buf[t + 16 * l + 4 * w:t + 16 * l + 4 * w + 4]), "little")
+                         for w in range(4)]
+                for j in range(32):
+                    e = j % 8
+                    nib = e // 2 if e % 2 == 0 else 4 + e // 2
+                    out[32 * rb + l % 32, 64 * ks + 32 * (l // 32) + j] = ((words[j // 8] >> (4 * nib)) & 15) - 8
+    return out
+
+
+def test_a4w4_int4_operand_encodes_every_code_exactly():
+    """Two codes per byte: every code in [-8, 7] is stored as code + 8; padding holds code 0."""
+    codes = np.arange(-8, 8, dtype=np.int8).reshape(1, 16)
+    buf = oracle.pack_a4w4_int4(codes)
+    assert buf.size == oracle.a4w4_packed_bytes(1, 16) == 32 * 128 // 2
+    assert oracle.a4w4_packed_bytes(8192, 8192) * 3 == oracle.a4w4_operand_bytes(8192, 8192) * 2
+    dec = _unpack_a4w4_int4(buf, 1, 16)
+    assert dec[0, :16].tolist() == list(range(-8, 8))
+    assert np.all(dec[1:, :] == 0) and np.all(dec[0, 16:] == 0)
+    # slot 0's first word holds elements 0..7 as nibbles (0, 2, 4, 6, 1, 3, 5, 7)
+    w0 = int.from_bytes(bytes(buf[0:4]), "little")
+    assert [(w0 >> (4 * p)) & 15 for p in range(8)] == [0, 2, 4, 6, 1, 3, 5, 7]
+
+
+@pytest.mark.parametrize("rows,k", [(45, 200), (32, 128), (64, 256), (1, 1)])
+def test_a4w4_int4_operand_round_trip_and_matches_fp6(rows, k):
+    codes = synthetic.rng(60 + rows).integers(-8, 8, (rows, k), dtype=np.int8)
+    dec = _unpack_a4w4_int4(oracle.pack_a4w4_int4(codes), rows, k)
+    assert np.array_equal(dec[:rows, :k], codes.astype(np.float64))
+    assert np.all(dec[rows:, :] == 0) and np.all(dec[:, k:] == 0)
+    # the same tile grid as the FP6 operand: both decode to the same padded code matrix
+    assert np.array_equal(dec, _unpack_a4w4_fp6(oracle.pack_a4w4_fp6(codes), rows, k))
+
+
 def _q4_autograd(g, x, w, sa, sw, eps):
     """Straight-through fake quantization in torch fp64 autograd: clamp passes
     the gradient inside [-8, 7] only, round passes it unchanged."""
