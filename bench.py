@@ -165,13 +165,36 @@ def bench_a4w4(args, ql, torch, synthetic):
     torch.cuda.synchronize()
     i8 = e0.elapsed_time(e1) / 10
     del xq, wq
+    # the same product on two-codes-per-byte operands (qlinear_gemm_a4w4_packed)
+    xp = ql.qlinear_quant_a4w4_packed(x, sa, eps)
+    wp = ql.qlinear_quant_a4w4_packed(w, sw, eps)
+    ql.qlinear_gemm_a4w4_packed(xp, wp, m, n, k, sa, sw, eps, out_dtype=torch.float16, out=out)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(10):
+        ql.qlinear_gemm_a4w4_packed(xp, wp, m, n, k, sa, sw, eps, out_dtype=torch.float16, out=out)
+    e1.record()
+    torch.cuda.synchronize()
+    pk = e0.elapsed_time(e1) / 10
+    e0.record()
+    for _ in range(5):
+        ql.qlinear_quant_a4w4_packed(x, sa, eps, operand=xp)
+    e1.record()
+    torch.cuda.synchronize()
+    pq = e0.elapsed_time(e1) / 5
+    del xp, wp
     res = {"m": m, "n": n, "k": k, "ops": ops, "ms_per_step": ms_per_step,
            "value": ops / (ms_per_step * 1e-3) / 1e12,
            "kernel_ms": {"quant_x": qx, "quant_w": qw, "gemm": gm},
            "gemm_tops": ops / (gm * 1e-3) / 1e12,
            "int8_codes_gemm": {"ms": round(i8, 4), "TOPS": round(ops / (i8 * 1e-3) / 1e12, 1),
                                "frac_int8_peak": round(ops / (i8 * 1e-3) / 1e12 / PEAK_INT8_TOPS, 4),
-                               "kernel": "gemm_i8_big_kernel (qlinear_gemm_a4w4_codes), same codes held in int8"}}
+                               "kernel": "gemm_i8_big_kernel (qlinear_gemm_a4w4_codes), same codes held in int8"},
+           "packed_operands_gemm": {"ms": round(pk, 4), "TOPS": round(ops / (pk * 1e-3) / 1e12, 1),
+                                    "frac_fp6_peak": round(ops / (pk * 1e-3) / 1e12 / PEAK_FP6_TOPS, 4),
+                                    "quant_ms_per_tensor": round(pq, 4),
+                                    "kernel": "gemm_a4w4_packed_kernel (qlinear_gemm_a4w4_packed): operands "
+                                              "at two 4-bit codes per byte, expanded to FP6 on the way into LDS"}}
     return res, d
 
 
@@ -475,6 +498,7 @@ def main():
                    "parallelism": "single GPU"},
         "kernel_ms": {key: round(v, 4) for key, v in res["kernel_ms"].items()},
         "int8_codes_gemm": res["int8_codes_gemm"],
+        "packed_operands_gemm": res["packed_operands_gemm"],
         "roofline": {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_FP6_TOPS, "unit": "TOPS",
                      "frac": round(achieved / PEAK_FP6_TOPS, 4), "traffic": traffic,
                      "kernel": "gemm_a4w4_f6_kernel (qlinear_gemm_a4w4_operands)",

@@ -30,7 +30,7 @@ QL_F32, QL_F16, QL_BF16, QL_I8, QL_U8, QL_I32 = range(6)
 QL_W_KN, QL_W_NK = 0, 1
 QL_RMSNORM = 1
 QL_INT4_WEIGHT, QL_INT4_ZEROS = 0, 1
-QL_OP_PACK_TERNARY, QL_OP_GEMM_A4W4, QL_OP_A4W4_OPERAND, QL_OP_Q4_BACKWARD = 0, 1, 2, 3
+QL_OP_PACK_TERNARY, QL_OP_GEMM_A4W4, QL_OP_A4W4_OPERAND, QL_OP_Q4_BACKWARD, QL_OP_A4W4_PACKED = 0, 1, 2, 3, 4
 STATUS = {0: "QL_OK", -1: "QL_ERR_NULL", -2: "QL_ERR_SHAPE", -3: "QL_ERR_DTYPE", -4: "QL_ERR_ALIGN",
           -5: "QL_ERR_WORKSPACE", -6: "QL_ERR_UNSUPPORTED", -7: "QL_ERR_HIP"}
 
@@ -42,7 +42,7 @@ _lib = None
 
 
 # QL_ABI_VERSION of include/qlinear.h that the argument lists below follow.
-ABI_VERSION = 6
+ABI_VERSION = 7
 
 
 class QLinearError(RuntimeError):
@@ -88,6 +88,8 @@ def lib() -> ctypes.CDLL:
             "qlinear_gemm_a4w4": (i32, [vp, vp, i32, vp, vp, f32, i64, i64, i64, i32, vp, vp, sz, vp]),
             "qlinear_quant_a4w4_operand": (i32, [vp, i32, i64, i64, vp, f32, vp, vp]),
             "qlinear_gemm_a4w4_operands": (i32, [vp, vp, vp, vp, f32, i64, i64, i64, i32, vp, vp]),
+            "qlinear_quant_a4w4_packed": (i32, [vp, i32, i64, i64, vp, f32, vp, vp]),
+            "qlinear_gemm_a4w4_packed": (i32, [vp, vp, vp, vp, f32, i64, i64, i64, i32, vp, vp]),
             "qlinear_q4_backward": (i32, [vp, vp, vp, i32, vp, vp, f32, i64, i64, i64, i32, vp, vp, vp, vp, sz,
                                           vp]),
         }
@@ -428,6 +430,36 @@ def qlinear_gemm_a4w4_operands(xa, wb, m, n, k, scale_a, scale_w, eps=1e-5, out_
     out = _empty((m, n), out_dtype, xa) if out is None else _gpu(out, "out", out_dtype)
     _need(out, m * n * out.element_size(), "out")
     _check("qlinear_gemm_a4w4_operands", lib().qlinear_gemm_a4w4_operands(
+        _ptr(xa), _ptr(wb), _ptr(scale_a), _ptr(scale_w), float(eps), m, n, k, _TORCH_TO_QL[out_dtype],
+        _ptr(out), _stream(xa)))
+    return out
+
+
+def qlinear_quant_a4w4_packed(x, scale, eps=1e-5, operand=None):
+    """Per-tensor 4-bit codes of ``x[rows,k]`` written two per byte (the packed 4-bit operand, uint8 bytes)."""
+    _gpu(x, "x")
+    _gpu(scale, "scale", torch.float32)
+    rows, k = x.shape
+    nbytes = qlinear_workspace_bytes(QL_OP_A4W4_PACKED, rows, 0, k)
+    operand = _empty((nbytes,), torch.uint8, x) if operand is None else _gpu(operand, "operand")
+    _need(operand, nbytes, "operand")
+    _check("qlinear_quant_a4w4_packed", lib().qlinear_quant_a4w4_packed(
+        _ptr(x), _TORCH_TO_QL[x.dtype], rows, k, _ptr(scale), float(eps), _ptr(operand), _stream(x)))
+    return operand
+
+
+def qlinear_gemm_a4w4_packed(xa, wb, m, n, k, scale_a, scale_w, eps=1e-5, out_dtype=torch.float16, out=None):
+    """A4W4 product of two packed 4-bit operands (of ``x[m,k]`` and ``w[n,k]``), two codes per byte."""
+    _gpu(xa, "xa")
+    _gpu(wb, "wb")
+    _need(xa, qlinear_workspace_bytes(QL_OP_A4W4_PACKED, m, 0, k), "xa")
+    _need(wb, qlinear_workspace_bytes(QL_OP_A4W4_PACKED, n, 0, k), "wb")
+    if out_dtype != torch.int32:
+        _gpu(scale_a, "scale_a", torch.float32)
+        _gpu(scale_w, "scale_w", torch.float32)
+    out = _empty((m, n), out_dtype, xa) if out is None else _gpu(out, "out", out_dtype)
+    _need(out, m * n * out.element_size(), "out")
+    _check("qlinear_gemm_a4w4_packed", lib().qlinear_gemm_a4w4_packed(
         _ptr(xa), _ptr(wb), _ptr(scale_a), _ptr(scale_w), float(eps), m, n, k, _TORCH_TO_QL[out_dtype],
         _ptr(out), _stream(xa)))
     return out

@@ -62,6 +62,8 @@ size_t qlinear_workspace_bytes(ql_op op, int64_t m, int64_t n, int64_t k) {
             return round256(ql::a4w4_operand_bytes(m, k)) + round256(ql::a4w4_operand_bytes(n, k));
         case QL_OP_A4W4_OPERAND:
             return ql::a4w4_operand_bytes(m, k);
+        case QL_OP_A4W4_PACKED:
+            return ql::a4w4_packed_bytes(m, k);
         case QL_OP_Q4_BACKWARD:
             return ql::q4_backward_workspace(m, n, k);
         default: return 0;
@@ -269,6 +271,31 @@ ql_status qlinear_quant_a4w4_operand(const void *x, ql_dtype x_dtype, int64_t ro
     if (!aligned16(x) || !aligned16(operand)) return QL_ERR_ALIGN;
     return hip_status(ql::launch_quant_a4w4_tiles(kind, x, rows, k, scale, eps, static_cast<uint8_t *>(operand),
                                                   as_stream(stream)));
+}
+
+ql_status qlinear_quant_a4w4_packed(const void *x, ql_dtype x_dtype, int64_t rows, int64_t k, const float *scale,
+                                    float eps, void *operand, void *stream) {
+    if (!x || !scale || !operand) return QL_ERR_NULL;
+    const int kind = in_kind(x_dtype);
+    if (kind < 0) return QL_ERR_DTYPE;
+    if (rows < 1 || k < 1 || k > kMaxK || rows > 0x7fffffff) return QL_ERR_SHAPE;
+    if (!aligned16(x) || !aligned16(operand)) return QL_ERR_ALIGN;
+    return hip_status(ql::launch_quant_a4w4_packed(kind, x, rows, k, scale, eps, static_cast<uint8_t *>(operand),
+                                                   as_stream(stream)));
+}
+
+ql_status qlinear_gemm_a4w4_packed(const void *xa, const void *wb, const float *scale_a, const float *scale_w,
+                                   float eps, int64_t m, int64_t n, int64_t k, ql_dtype out_dtype, void *out,
+                                   void *stream) {
+    int ok;
+    if (!xa || !wb || !out) return QL_ERR_NULL;
+    const ql_status ds = gemm_out_kind(out_dtype, &ok);
+    if (ds != QL_OK) return ds;
+    if (ok != ql::OUT_I32 && (!scale_a || !scale_w)) return QL_ERR_NULL;
+    if (m < 1 || n < 1 || k < 1 || k > kMaxK || m > 0x7fffffff || n > 0x7fffffff) return QL_ERR_SHAPE;
+    if (!aligned16(xa) || !aligned16(wb) || !aligned16(out)) return QL_ERR_ALIGN;
+    return hip_status(ql::launch_gemm_a4w4_packed(static_cast<const uint8_t *>(xa), static_cast<const uint8_t *>(wb),
+                                                  scale_a, scale_w, eps, m, n, k, ok, out, as_stream(stream)));
 }
 
 ql_status qlinear_gemm_a4w4_operands(const void *xa, const void *wb, const float *scale_a, const float *scale_w,

@@ -351,6 +351,163 @@ hipError_t launch_f6(const Params &p, hipStream_t st) {
 }
 
 // ---------------------------------------------------------------------------
+// 4-bit product on packed two-per-byte operands
+// ---------------------------------------------------------------------------
+// The operands hold 0.5 byte per code (quant_a4w4_packed_kernel) on the FP6
+// operand's tile grid: a 1024-byte tile per 32 rows x 64 k, slot l (16
+// bytes) holding the 32 codes of lane l's register image.  The 16 KB of each
+// operand that a 128-k slice of the 256 x 256 tile needs move HBM ->
+// registers, one slot (16 bytes) per load; each slot becomes 32 exact fp16
+// values (code + 8 ORed into the mantissa of 1024.0, minus 1032) and then
+// its FP6 E3M2 register image with one v_cvt_scalef32_pk32_bf6_f16 (exact
+// on these integers), stored into the FP6 tile layout in LDS.  From there
+// the slice runs exactly as in the FP6 kernel (same fragments, products and
+// epilogue).  Two LDS stages: while the matrix cores consume one, the next
+// slice is expanded into the other and the slice after it is in flight in
+// registers.  The last iterations reload and re-expand the final slice into
+// the unused stage, so the loop body has no branches around its loads.
+constexpr int kP4Tile = 1024;                          // bytes of one packed 32 x 64 tile
+constexpr int kP4Slots = 2 * (LB / 32) * 64 / LThreads;  // slots per thread, operand and slice
+
+typedef _Float16 v32h __attribute__((ext_vector_type(32)));
+
+// FP6 register image of one packed slot: element 8q + 2i (+1) is nibble i
+// (i + 4) of word q.  lo / hi hold the even / odd nibbles of a word in their
+// bytes; one byte permute against 0x64 bytes forms each fp16 pair
+// (1024 + n, 1024 + n'), one packed subtract of (1032, 1032) the codes.
+__device__ __forceinline__ v6u expand_slot(const uint4 &s) {
+    const uint32_t w[4] = {s.x, s.y, s.z, s.w};
+    const h2 off = __builtin_bit_cast(h2, 0x64086408u);   // (1032, 1032)
+    const uint32_t c64 = 0x64646464u;
+    v32h v;
+#pragma unroll
+    for (int q = 0; q < 4; q++) {
+        const uint32_t lo = w[q] & 0x0F0F0F0Fu, hi = (w[q] >> 4) & 0x0F0F0F0Fu;
+        // pair i: nibbles (i, i + 4) = (lo, hi alternating) bytes (i / 2, i / 2 + 2)
+        const uint32_t pr[4] = {__builtin_amdgcn_perm(c64, lo, 0x04020400u), __builtin_amdgcn_perm(c64, hi, 0x04020400u),
+                                __builtin_amdgcn_perm(c64, lo, 0x04030401u), __builtin_amdgcn_perm(c64, hi, 0x04030401u)};
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            const h2 d = __builtin_bit_cast(h2, pr[i]) - off;
+            v[8 * q + 2 * i] = d[0];
+            v[8 * q + 2 * i + 1] = d[1];
+        }
+    }
+    return __builtin_amdgcn_cvt_scalef32_pk32_bf6_f16(v, 1.0f);
+}
+
+__device__ __forceinline__ void store_image(int8_t *tile, int l, const v6u &img) {
+    *reinterpret_cast<uint4 *>(tile + 16 * l) = make_uint4(img[0], img[1], img[2], img[3]);
+    *reinterpret_cast<uint2 *>(tile + 1024 + 8 * l) = make_uint2(img[4], img[5]);
+}
+
+template <int OUT>
+__global__ __launch_bounds__(LThreads, 1) void gemm_a4w4_packed_kernel(Params p, int tiles_m, int tiles_n) {
+    constexpr int STAGE = 2 * kF6Op;
+    constexpr int EPITCH = 128 * 2 + 16;
+    constexpr int SMEM = 2 * STAGE > 1024 + 4 * 128 * EPITCH ? 2 * STAGE : 1024 + 4 * 128 * EPITCH;
+    __shared__ __attribute__((aligned(1024))) int8_t smem[SMEM];
+
+    const int lane = threadIdx.x % kWave, wave = wave_id();
+    const int wm = wave / 2, wn = wave % 2;
+    int tm, tn;
+    xcd_tile(blockIdx.x, tiles_m, tiles_n, kGroupM, tm, tn);
+    const int64_t m0 = (int64_t)tm * LB, n0 = (int64_t)tn * LB;
+    const int64_t ktiles = (p.k + 127) / 128 * 2;   // 64-k tiles per 32-row block
+    const int64_t nk = ktiles / 2;                   // 128-k slices
+    const int64_t rows_a = (p.m + 31) / 32, rows_b = (p.n + 31) / 32;
+
+    // Slot i of this thread in a slice is s = tid + 256 i: tile s / 64 =
+    // tid / 64 + 4 i of the slice (32-row block tid / 128 + 2 i, 64-k half
+    // (tid / 64) % 2), lane slot tid % 64.  Blocks past the operand re-read
+    // its last block; those rows are never stored.
+    const int tid = (int)threadIdx.x, sl = tid % 64, half = (tid / 64) % 2;
+    const uint8_t *srcA[kP4Slots];
+    const uint8_t *srcB[kP4Slots];
+#pragma unroll
+    for (int i = 0; i < kP4Slots; i++) {
+        const int rt = tid / 128 + 2 * i;
+        const int64_t ra = min(m0 / 32 + rt, rows_a - 1), rb = min(n0 / 32 + rt, rows_b - 1);
+        srcA[i] = reinterpret_cast<const uint8_t *>(p.x) + (ra * ktiles + half) * kP4Tile + 16 * sl;
+        srcB[i] = reinterpret_cast<const uint8_t *>(p.w) + (rb * ktiles + half) * kP4Tile + 16 * sl;
+    }
+    const int dbase = (tid / 64) * kF6Tile;   // LDS tile of slot 0; slot i is 4 i tiles further
+    uint4 la[kP4Slots], lb[kP4Slots];
+    auto load = [&](int64_t kt) {
+        const int64_t off = (kt < nk ? kt : nk - 1) * 2 * kP4Tile;
+#pragma unroll
+        for (int i = 0; i < kP4Slots; i++) {
+            la[i] = load16_stream(srcA[i] + off);
+            lb[i] = load16_stream(srcB[i] + off);
+        }
+    };
+    auto expand = [&](int8_t *stage) {
+#pragma unroll
+        for (int i = 0; i < kP4Slots; i++) {
+            store_image(stage + dbase + 4 * i * kF6Tile, sl, expand_slot(la[i]));
+            store_image(stage + kF6Op + dbase + 4 * i * kF6Tile, sl, expand_slot(lb[i]));
+        }
+    };
+
+    v16f acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; i++)
+#pragma unroll
+        for (int j = 0; j < 4; j++) acc[i][j] = v16f{};
+
+    load(0);
+    expand(smem);
+    load(1);
+    for (int64_t kt = 0; kt < nk; kt++) {
+        // this slice's images are in LDS (every wave's stores done), and every
+        // wave has finished reading the stage expanded into below
+        __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0)
+        barrier_only();
+        const int8_t *__restrict__ cur = smem + (kt & 1) * STAGE;
+        int8_t *__restrict__ nxt = smem + ((kt + 1) & 1) * STAGE;
+        v8i fa[2][4], fb[2][4];
+        auto frags = [&](int st) {
+#pragma unroll
+            for (int i = 0; i < 4; i++) fa[st][i] = f6_frag(cur + ((wm * 4 + i) * 2 + st) * kF6Tile, lane);
+#pragma unroll
+            for (int j = 0; j < 4; j++) fb[st][j] = f6_frag(cur + kF6Op + ((wn * 4 + j) * 2 + st) * kF6Tile, lane);
+        };
+        frags(0);
+        expand(nxt);        // slice kt + 1 (loaded during the previous slice)
+        load(kt + 2);
+#pragma unroll
+        for (int st = 0; st < 2; st++) {
+            if (st == 0) frags(1);
+#pragma unroll
+            for (int i = 0; i < 4; i++)
+#pragma unroll
+                for (int j = 0; j < 4; j++)
+                    acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa[st][i], fb[st][j], acc[i][j], 3, 3,
+                                                                                0, kF6Scale, 0, kF6Scale);
+            if (st == 0) {
+#pragma unroll
+                for (int q = 0; q < 16; q++) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                }
+            }
+        }
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    big_epilogue<EPI_SCALARS, OUT>(p, acc, smem, m0, n0, wm, wn, wave, lane);
+}
+
+template <int OUT>
+hipError_t launch_packed(const Params &p, hipStream_t st) {
+    const int64_t tm = (p.m + LB - 1) / LB, tn = (p.n + LB - 1) / LB;
+    if (tm * tn > 0x7fffffff) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((gemm_a4w4_packed_kernel<OUT>), dim3((unsigned)(tm * tn)), dim3(LThreads), 0, st, p, (int)tm,
+                       (int)tn);
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
 // General kernel
 // ---------------------------------------------------------------------------
 constexpr int BM = 128, BN = 128, BK = 64;
@@ -950,6 +1107,17 @@ hipError_t launch_epi(int epi, int out_kind, const Params &p, int64_t batch, hip
 }
 
 }  // namespace
+
+hipError_t launch_gemm_a4w4_packed(const uint8_t *xa, const uint8_t *wb, const float *sa, const float *sw, float eps,
+                                   int64_t m, int64_t n, int64_t k, int out_kind, void *out, hipStream_t st) {
+    Params p{reinterpret_cast<const int8_t *>(xa), reinterpret_cast<const int8_t *>(wb), nullptr, nullptr, sa, sw,
+             eps, m, n, k, out, nullptr, 0, 0, 0, 0, 0};
+    switch (out_kind) {
+        case OUT_F16: return launch_packed<OUT_F16>(p, st);
+        case OUT_BF16: return launch_packed<OUT_BF16>(p, st);
+        default: return launch_packed<OUT_I32>(p, st);
+    }
+}
 
 hipError_t launch_gemm_a4w4_tiles(const uint8_t *xa, const uint8_t *wb, const float *sa, const float *sw, float eps,
                                   int64_t m, int64_t n, int64_t k, int out_kind, void *out, hipStream_t st) {

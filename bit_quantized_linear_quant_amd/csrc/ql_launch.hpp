@@ -20,6 +20,11 @@ hipError_t launch_quant_int4_tensor(int in_kind, const void *x, int64_t count, c
 size_t a4w4_operand_bytes(int64_t rows, int64_t k);
 hipError_t launch_quant_a4w4_tiles(int in_kind, const void *x, int64_t rows, int64_t k, const float *scale,
                                    float eps, uint8_t *tiles, hipStream_t st);
+// quant.hip: 4-bit codes of a [rows, k] tensor packed two per byte (code + 8)
+// on the same tile grid, 1024 bytes per 32 x 64 tile (a4w4_packed_bytes).
+size_t a4w4_packed_bytes(int64_t rows, int64_t k);
+hipError_t launch_quant_a4w4_packed(int in_kind, const void *x, int64_t rows, int64_t k, const float *scale,
+                                    float eps, uint8_t *tiles, hipStream_t st);
 
 // pack.hip
 size_t absmean_partial_count(int64_t count);
@@ -63,6 +68,10 @@ hipError_t launch_gemm_i8(const GemmI8Args &a, hipStream_t st);
 // out = fl32(fl32(acc * max(*sa, eps)) * max(*sw, eps)), acc exact.
 hipError_t launch_gemm_a4w4_tiles(const uint8_t *xa, const uint8_t *wb, const float *sa, const float *sw, float eps,
                                   int64_t m, int64_t n, int64_t k, int out_kind, void *out, hipStream_t st);
+// The same product on packed two-per-byte operands (launch_quant_a4w4_packed),
+// expanded to FP6 register images on their way into LDS.
+hipError_t launch_gemm_a4w4_packed(const uint8_t *xa, const uint8_t *wb, const float *sa, const float *sw, float eps,
+                                   int64_t m, int64_t n, int64_t k, int out_kind, void *out, hipStream_t st);
 // True when the product runs on the 256 x 256 direct-to-LDS kernel.
 bool gemm_i8_uses_big_tiles(bool w_nk, int64_t m, int64_t n, int64_t k);
 

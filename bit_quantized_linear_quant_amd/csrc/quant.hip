@@ -350,6 +350,49 @@ __global__ __launch_bounds__(kI4Threads) void quant_a4w4_tiles_kernel(const void
     *reinterpret_cast<uint2 *>(dst + 1024 + 8 * l) = make_uint2(img[4], img[5]);
 }
 
+// 4-bit codes as the packed two-per-byte operand: the tile grid of the FP6
+// operand, 1024 bytes per tile, slot l (row 32rb + l%32, k 64ks + 32(l/32)
+// .. +31) the 16 bytes at 16l.  Element j goes to word j/8, nibble j%8/2
+// (even j) or 4 + j%8/2 (odd j), as code + 8, so that
+// (word >> 4i) & 0x000F000F holds the elements 8w + 2i and 8w + 2i + 1 in
+// its two halves.  One thread per slot; a wave writes 1 KB contiguously.
+template <int K, bool VEC>
+__global__ __launch_bounds__(kI4Threads) void quant_a4w4_packed_kernel(const void *__restrict__ x, int64_t rows,
+                                                                       int64_t k, const float *__restrict__ scale,
+                                                                       float eps, int64_t ktiles, int64_t slots,
+                                                                       uint8_t *__restrict__ tiles) {
+    const int64_t t = (int64_t)blockIdx.x * kI4Threads + threadIdx.x;
+    if (t >= slots) return;
+    const float sc = *scale;
+    const float sp = sc > eps ? sc : eps;
+    const float r = __fdiv_rn(1.0f, sp);
+    const int64_t tile = t / 64;
+    const int l = (int)(t % 64);
+    const int64_t row = 32 * (tile / ktiles) + l % 32;
+    const int64_t k0 = 64 * (tile % ktiles) + 32 * (l / 32);
+    float v[32];
+    if (VEC && row < rows && k0 + 32 <= k) {
+        const int64_t base = row * k + k0;
+#pragma unroll
+        for (int c = 0; c < 4; c++) load8_vec<K>(x, base + 8 * c, v + 8 * c);
+    } else {
+#pragma unroll
+        for (int j = 0; j < 32; j++) v[j] = (row < rows && k0 + j < k) ? load_elem<K>(x, row * k + k0 + j) : 0.0f;
+    }
+    uint32_t w[4];
+#pragma unroll
+    for (int q = 0; q < 4; q++) {
+        uint32_t word = 0;
+#pragma unroll
+        for (int e = 0; e < 8; e++) {
+            const uint32_t nib = (uint32_t)((int)code_i4_f(v[8 * q + e], sp, r) + 8);
+            word |= nib << (4 * ((e % 2 == 0) ? e / 2 : 4 + e / 2));
+        }
+        w[q] = word;
+    }
+    *reinterpret_cast<uint4 *>(tiles + tile * 1024 + 16 * l) = make_uint4(w[0], w[1], w[2], w[3]);
+}
+
 template <int K, bool VEC, bool RMS>
 hipError_t launch_quant_act_t(const void *x, int64_t m, int64_t k, float eps_norm, float eps_q,
                               int8_t *q, float *pts, int32_t *rowsum, hipStream_t st) {
@@ -403,7 +446,36 @@ hipError_t launch_a4w4_tiles_k(bool vec, const void *x, int64_t rows, int64_t k,
     return hipGetLastError();
 }
 
+template <int K>
+hipError_t launch_a4w4_packed_k(bool vec, const void *x, int64_t rows, int64_t k, const float *scale, float eps,
+                                uint8_t *tiles, hipStream_t st) {
+    const int64_t ktiles = (k + 127) / 128 * 2, slots = (rows + 31) / 32 * ktiles * 64;
+    const int64_t blocks = (slots + kI4Threads - 1) / kI4Threads;
+    if (blocks > 0x7fffffff) return hipErrorInvalidValue;
+    if (vec)
+        hipLaunchKernelGGL((quant_a4w4_packed_kernel<K, true>), dim3((unsigned)blocks), dim3(kI4Threads), 0, st, x,
+                           rows, k, scale, eps, ktiles, slots, tiles);
+    else
+        hipLaunchKernelGGL((quant_a4w4_packed_kernel<K, false>), dim3((unsigned)blocks), dim3(kI4Threads), 0, st, x,
+                           rows, k, scale, eps, ktiles, slots, tiles);
+    return hipGetLastError();
+}
+
 }  // namespace
+
+size_t a4w4_packed_bytes(int64_t rows, int64_t k) {
+    return (size_t)((rows + 31) / 32 * 32) * (size_t)((k + 127) / 128 * 128) / 2;
+}
+
+hipError_t launch_quant_a4w4_packed(int in_kind, const void *x, int64_t rows, int64_t k, const float *scale,
+                                    float eps, uint8_t *tiles, hipStream_t st) {
+    const bool vec = (k % 8) == 0;
+    switch (in_kind) {
+        case IN_F32: return launch_a4w4_packed_k<IN_F32>(vec, x, rows, k, scale, eps, tiles, st);
+        case IN_F16: return launch_a4w4_packed_k<IN_F16>(vec, x, rows, k, scale, eps, tiles, st);
+        default: return launch_a4w4_packed_k<IN_BF16>(vec, x, rows, k, scale, eps, tiles, st);
+    }
+}
 
 size_t a4w4_operand_bytes(int64_t rows, int64_t k) {
     return (size_t)((rows + 31) / 32 * 32) * (size_t)((k + 127) / 128 * 128) * 3 / 4;

@@ -47,7 +47,7 @@
 extern "C" {
 #endif
 
-#define QL_ABI_VERSION 6
+#define QL_ABI_VERSION 7
 /* Version of the 2-bit ternary weight layout written by qlinear_pack_ternary. */
 #define QL_TERNARY_PACK_V1 1
 /* Version of the 4-bit weight layout written by qlinear_pack_int4. */
@@ -107,6 +107,7 @@ typedef enum ql_op {
     QL_OP_GEMM_A4W4 = 1,
     QL_OP_A4W4_OPERAND = 2,
     QL_OP_Q4_BACKWARD = 3,
+    QL_OP_A4W4_PACKED = 4,
     QL_OP_MIN_ENUM = -0x7fffffff - 1,
     QL_OP_MAX_ENUM = 0x7fffffff
 } ql_op;
@@ -123,6 +124,8 @@ const char *qlinear_status_string(ql_status s);
  *                       (QL_OP_A4W4_OPERAND of each, rounded up to 256 bytes).
  *   QL_OP_A4W4_OPERAND: bytes of one FP6 operand of m rows and k columns:
  *                       roundup(m, 32) * roundup(k, 128) * 3 / 4; n is ignored.
+ *   QL_OP_A4W4_PACKED:  bytes of one two-codes-per-byte operand of m rows and
+ *                       k columns: roundup(m, 32) * roundup(k, 128) / 2.
  *   QL_OP_Q4_BACKWARD:  the transposed, zero-padded 16-bit operands of the
  *                       two backward products and the scale-gradient
  *                       partials of qlinear_q4_backward. */
@@ -402,6 +405,33 @@ ql_status qlinear_quant_a4w4_operand(const void *x, ql_dtype x_dtype, int64_t ro
 ql_status qlinear_gemm_a4w4_operands(const void *xa, const void *wb, const float *scale_a,
                                      const float *scale_w, float eps, int64_t m, int64_t n,
                                      int64_t k, ql_dtype out_dtype, void *out, void *stream);
+
+/*
+ * QL_A4W4_PACKED - the 4-bit operand at two codes per byte (0.5 byte per
+ * code; this library's own layout).  The tile grid of QL_A4W4_OPERAND, but a
+ * tile is 1024 bytes at byte (rb * k_p/64 + ks) * 1024 and slot l is the 16
+ * bytes at tile byte 16l (row 32rb + l%32, k 64ks + 32(l/32) + j, j = 0..31).
+ * Element j is in the little-endian 32-bit word j/8 of the slot, in nibble
+ * (j%8)/2 for even j%8 and 4 + (j%8)/2 for odd, stored as c + 8 in [0, 15].
+ * Size: qlinear_workspace_bytes(QL_OP_A4W4_PACKED, rows, 0, k)
+ * = roundup(rows, 32) * roundup(k, 128) / 2.
+ */
+
+/*
+ * As qlinear_quant_a4w4_operand, writing a QL_A4W4_PACKED operand: the same
+ * codes, two per byte.
+ */
+ql_status qlinear_quant_a4w4_packed(const void *x, ql_dtype x_dtype, int64_t rows, int64_t k,
+                                    const float *scale, float eps, void *operand, void *stream);
+
+/*
+ * As qlinear_gemm_a4w4_operands on two QL_A4W4_PACKED operands: each slot is
+ * expanded to its FP6 E3M2 register image on its way from HBM into LDS, then
+ * multiplied on the FP6 matrix cores.  Same acc, same outputs bit for bit.
+ */
+ql_status qlinear_gemm_a4w4_packed(const void *xa, const void *wb, const float *scale_a,
+                                   const float *scale_w, float eps, int64_t m, int64_t n,
+                                   int64_t k, ql_dtype out_dtype, void *out, void *stream);
 
 /*
  * Q4Linear forward ([Q4] forward): quantizes x [m, k] and w [n, k] (both

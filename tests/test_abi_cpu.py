@@ -40,7 +40,7 @@ def test_exports_every_declared_symbol(L):
 
 
 def test_abi_version_and_status_strings(L):
-    assert ql.qlinear_abi_version() == ql.ABI_VERSION == 6
+    assert ql.qlinear_abi_version() == ql.ABI_VERSION == 7
     for code, name in ql.STATUS.items():
         s = ql.qlinear_status_string(code)
         assert isinstance(s, str) and s
@@ -59,6 +59,10 @@ def test_workspace_bytes():
     chunks = (28672 * 8192 + 16383) // 16384
     assert ql.qlinear_workspace_bytes(ql.QL_OP_PACK_TERNARY, 0, 28672, 8192) == (chunks * 8 + 255) // 256 * 256
     assert ql.qlinear_workspace_bytes(99, 1, 1, 1) == 0
+    # the packed 4-bit operand: half a byte per padded element
+    for rows, k in [(1, 1), (45, 200), (8192, 8192), (33, 129)]:
+        assert ql.qlinear_workspace_bytes(ql.QL_OP_A4W4_PACKED, rows, 0, k) == oracle.a4w4_packed_bytes(rows, k)
+    assert ql.qlinear_workspace_bytes(ql.QL_OP_A4W4_PACKED, 8192, 0, 8192) == 8192 * 8192 // 2
 
 
 def test_quant_act_validation(L):
@@ -160,6 +164,18 @@ def test_gemm_validation(L):
     assert qo(A, ql.QL_F16, 0, 8, A, 1e-5, A, NULL) == -2
     assert qo(A, ql.QL_F16, 4, 131072, A, 1e-5, A, NULL) == -2
     assert qo(A, ql.QL_F16, 4, 8, A, 1e-5, U, NULL) == -4
+    qp = L.qlinear_quant_a4w4_packed
+    assert qp(A, ql.QL_F16, 4, 8, NULL, 1e-5, A, NULL) == -1
+    assert qp(A, ql.QL_I8, 4, 8, A, 1e-5, A, NULL) == -3
+    assert qp(A, ql.QL_F16, 0, 8, A, 1e-5, A, NULL) == -2
+    assert qp(A, ql.QL_F16, 4, 131072, A, 1e-5, A, NULL) == -2
+    assert qp(A, ql.QL_F16, 4, 8, A, 1e-5, U, NULL) == -4
+    gp = L.qlinear_gemm_a4w4_packed
+    assert gp(A, A, NULL, A, 1e-5, 4, 4, 4, ql.QL_F16, A, NULL) == -1
+    assert gp(A, A, A, A, 1e-5, 4, 4, 4, ql.QL_F32, A, NULL) == -3
+    assert gp(A, A, A, A, 1e-5, 4, 0, 4, ql.QL_F16, A, NULL) == -2
+    assert gp(A, A, A, A, 1e-5, 4, 4, 131072, ql.QL_F16, A, NULL) == -2
+    assert gp(U, A, A, A, 1e-5, 4, 4, 4, ql.QL_F16, A, NULL) == -4
     go = L.qlinear_gemm_a4w4_operands
     assert go(A, A, NULL, A, 1e-5, 4, 4, 4, ql.QL_F16, A, NULL) == -1
     assert go(A, A, A, A, 1e-5, 4, 4, 4, ql.QL_F32, A, NULL) == -3

@@ -184,6 +184,38 @@ def test_a4w4_full_workload():
     assert_float_close(out[ridx], y, "a4w4 fp16 (sampled rows)")
 
 
+def test_a4w4_packed_full_workload():
+    """The 8192^3 workload on two-codes-per-byte operands: both operands bit for bit, the
+    whole fp16 output equal to the FP6-operand product's, sampled rows against the oracle."""
+    m = n = k = 8192
+    d = synthetic.a4w4(m, n, k)
+    eps = d["eps"]
+    qa = oracle.quant_int4_tensor(d["x"].float().numpy(), d["scale_a"], eps)
+    qw = oracle.quant_int4_tensor(d["w"].float().numpy(), d["scale_w"], eps)
+    sag = torch.tensor([d["scale_a"]], dtype=torch.float32, device=DEV)
+    swg = torch.tensor([d["scale_w"]], dtype=torch.float32, device=DEV)
+    xg, wg = _cuda(d["x"]), _cuda(d["w"])
+    xp = ql.qlinear_quant_a4w4_packed(xg, sag, eps)
+    wp = ql.qlinear_quant_a4w4_packed(wg, swg, eps)
+    op = poison((m, n), torch.float16)
+    ql.qlinear_gemm_a4w4_packed(xp, wp, m, n, k, sag, swg, eps, out=op)
+    oi = poison((m, n), torch.int32)
+    ql.qlinear_gemm_a4w4_packed(xp, wp, m, n, k, None, None, out_dtype=torch.int32, out=oi)
+    of, _ = ql.qlinear_gemm_a4w4(xg, wg, sag, swg, eps)
+    torch.cuda.synchronize()
+    assert_equal(xp, oracle.pack_a4w4_int4(qa), "x packed operand")
+    assert_equal(wp, oracle.pack_a4w4_int4(qw), "w packed operand")
+    assert torch.equal(op.view(torch.int16), of.view(torch.int16)), "packed vs FP6 operands, whole output"
+    rows = np.unique(np.concatenate([_rows(m, 2009, extra=16), np.arange(13, m, 256)]))   # one row per tile row
+    acc = oracle.gemm_i8(qa[rows], qw, True)
+    sa = oracle.effective_scale(d["scale_a"], eps)
+    sw = oracle.effective_scale(d["scale_w"], eps)
+    y = oracle.dequant(acc, np.full(len(rows), sa, np.float32), np.full(n, sw, np.float32))
+    ridx = torch.from_numpy(rows).to(DEV)
+    assert_equal(oi[ridx], acc, "a4w4 packed accumulator (sampled rows)")
+    assert_float_close(op[ridx], y, "a4w4 packed fp16 (sampled rows)")
+
+
 def test_q4_backward_full_workload():
     """8192^3 backward of the A4W4 workload: sampled rows of grad_x and grad_w against the oracle."""
     m = n = k = 8192

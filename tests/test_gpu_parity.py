@@ -704,6 +704,69 @@ def test_a4w4_operands_equal_int8_codes_bit_for_bit(m, n, k):
     assert_equal(xq, qa, "x codes")
 
 
+@pytest.mark.parametrize("dt", [torch.bfloat16, torch.float32, torch.float16])
+@pytest.mark.parametrize("rows,k", [(45, 200), (32, 128), (70, 77), (300, 1000), (1, 1)])
+def test_a4w4_packed_operand_quant_parity(dt, rows, k):
+    """The two-codes-per-byte operand, bit for bit, for every input type and ragged shape."""
+    r = synthetic.rng(3200 + rows + k)
+    x = torch.from_numpy(r.normal(0, 1, (rows, k)).astype(np.float32)).to(dt)
+    scale = 0.3
+    q = oracle.quant_int4_tensor(x.float().numpy(), scale, 1e-5)
+    op = poison((oracle.a4w4_packed_bytes(rows, k),), torch.uint8)
+    ql.qlinear_quant_a4w4_packed(_cuda(x), torch.tensor([scale], dtype=torch.float32, device=DEV), operand=op)
+    _sync()
+    assert_equal(op, oracle.pack_a4w4_int4(q), f"packed operand {dt}")
+
+
+@pytest.mark.parametrize("m,n,k", [(33, 20, 130), (256, 256, 512), (129, 65, 1000), (1, 1, 1), (600, 520, 640),
+                                   (1024, 1024, 256), (16, 300, 512), (520, 777, 300), (256, 1024, 8192)])
+def test_a4w4_packed_parity(m, n, k):
+    """Packed 4-bit operands: exact accumulators against the oracle, and every output type
+    bit-identical to the FP6-operand product of the same codes."""
+    d = synthetic.a4w4(m, n, k, seed=3300 + m + n + k)
+    sa, sw = d["scale_a"] * 0.5, d["scale_w"] * 0.5     # some codes clamp at -8 / 7
+    qa, qw, acc, y = oracle.a4w4(d["x"].float().numpy(), d["w"].float().numpy(), sa, sw, d["eps"])
+    sag = torch.tensor([sa], dtype=torch.float32, device=DEV)
+    swg = torch.tensor([sw], dtype=torch.float32, device=DEV)
+    xg, wg = _cuda(d["x"]), _cuda(d["w"])
+    xp = ql.qlinear_quant_a4w4_packed(xg, sag, d["eps"])
+    wp = ql.qlinear_quant_a4w4_packed(wg, swg, d["eps"])
+    xa = ql.qlinear_quant_a4w4_operand(xg, sag, d["eps"])
+    wb = ql.qlinear_quant_a4w4_operand(wg, swg, d["eps"])
+    outs = {}
+    for dt in (torch.int32, torch.float16, torch.bfloat16):
+        o = poison((m, n), dt)
+        ql.qlinear_gemm_a4w4_packed(xp, wp, m, n, k, sag, swg, d["eps"], out_dtype=dt, out=o)
+        f = ql.qlinear_gemm_a4w4_operands(xa, wb, m, n, k, sag, swg, d["eps"], out_dtype=dt)
+        outs[dt] = (o, f)
+    _sync()
+    assert_equal(xp, oracle.pack_a4w4_int4(qa), "x packed operand")
+    assert_equal(wp, oracle.pack_a4w4_int4(qw), "w packed operand")
+    assert_equal(outs[torch.int32][0], acc, "a4w4 accumulator (packed operands)")
+    for dt in (torch.float16, torch.bfloat16):
+        o, f = outs[dt]
+        assert torch.equal(o.view(torch.int16), f.view(torch.int16)), f"packed vs FP6 operands {dt}"
+        assert_float_close(o, y, f"a4w4 packed {dt}")
+
+
+def test_a4w4_packed_max_k_extremes():
+    """k = 131071 with every code -8 (and 7 on alternate k of one row): acc = 64 k exactly."""
+    m, n, k = 3, 5, 131071
+    x = torch.full((m, k), -8.0, dtype=torch.float16)
+    w = torch.full((n, k), -8.0, dtype=torch.float16)
+    w[1, ::2] = 7.0
+    one = torch.ones(1, dtype=torch.float32, device=DEV)
+    qa = oracle.quant_int4_tensor(x.float().numpy(), 1.0, 1e-5)
+    qw = oracle.quant_int4_tensor(w.float().numpy(), 1.0, 1e-5)
+    acc = oracle.gemm_i8(qa, qw, True)
+    xp = ql.qlinear_quant_a4w4_packed(_cuda(x), one)
+    wp = ql.qlinear_quant_a4w4_packed(_cuda(w), one)
+    o = poison((m, n), torch.int32)
+    ql.qlinear_gemm_a4w4_packed(xp, wp, m, n, k, None, None, out_dtype=torch.int32, out=o)
+    _sync()
+    assert_equal(o, acc, "a4w4 packed max-k accumulator")
+
+
 # ---------------------------------------------------------------------------
 # Q4Linear backward
 # ---------------------------------------------------------------------------
