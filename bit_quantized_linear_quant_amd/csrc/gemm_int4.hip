@@ -35,6 +35,8 @@
 // four k blocks (k <= 4096 with 8 waves) issues all of their loads at once
 // instead.
 // The fp32 partials of the waves are added in LDS in a fixed wave order.
+#include <type_traits>
+
 #include "ql_device.hpp"
 #include "ql_launch.hpp"
 
@@ -47,12 +49,17 @@ __device__ __forceinline__ uint32_t word_of(const uint4 &v, int t) {
 }
 
 // 8 exact fp16 (q - z) values from one packed word; zz is the pair (1024+z).
+// lo / hi hold the even / odd nibbles in their bytes; one byte permute
+// against 0x64 bytes forms the pair (1024 + q_{2i}, 1024 + q_{2i+1}), i.e.
+// nibbles (i, i + 4) = bytes (i/2, i/2 + 2) of lo (even i) or hi (odd i).
 __device__ __forceinline__ v8h unpack_int4(uint32_t w, h2 zz) {
+    const uint32_t lo = w & 0x0F0F0F0Fu, hi = (w >> 4) & 0x0F0F0F0Fu, c64 = 0x64646464u;
+    const uint32_t pr[4] = {__builtin_amdgcn_perm(c64, lo, 0x04020400u), __builtin_amdgcn_perm(c64, hi, 0x04020400u),
+                            __builtin_amdgcn_perm(c64, lo, 0x04030401u), __builtin_amdgcn_perm(c64, hi, 0x04030401u)};
     v8h r;
 #pragma unroll
     for (int i = 0; i < 4; i++) {
-        const uint32_t pair = ((w >> (4 * i)) & 0x000F000Fu) | 0x64006400u;
-        const h2 d = __builtin_bit_cast(h2, pair) - zz;
+        const h2 d = __builtin_bit_cast(h2, pr[i]) - zz;
         r[2 * i] = d[0];
         r[2 * i + 1] = d[1];
     }
@@ -140,22 +147,21 @@ __device__ __forceinline__ void load_stage(Stage<NBLK, RB, SUB> &st, const uint1
         }
 }
 
-// Accumulate one k block: per column block, four MFMA steps per row block
-// into a fresh fp32 partial, then one multiply by the group scale.
+// Accumulate one k block from its x fragments: per column block, four MFMA
+// steps per row block into a fresh fp32 partial, then one multiply by the
+// group scale (SUB: per step, after the cross-row transpose of the words).
 template <int NBLK, int RB, bool SUB>
-__device__ __forceinline__ void compute_stage(const Stage<NBLK, RB, SUB> &st, v4f (&acc)[RB][NBLK], bool kb_ok,
-                                              int64_t nb0, int64_t nblocks, uint8_t *xb, int lane) {
-    v8h a[RB][4];
+__device__ __forceinline__ void block_mma(const v8h (&a)[RB][4], const uint4 (&w)[NBLK],
+                                          const uint32_t (&s)[NBLK][SUB ? 4 : 1], const uint32_t (&z)[NBLK],
+                                          v4f (&acc)[RB][NBLK], bool kb_ok, int64_t nb0, int64_t nblocks) {
     if constexpr (SUB) {
-        // Step t covers the 32-k sub-block t: per-step scale and zero-point.
-        rows256_to_subblock_fragments<RB>(st.a, a, xb, lane);
 #pragma unroll
         for (int j = 0; j < NBLK; j++) {
             const bool ok = kb_ok && nb0 + j < nblocks;
-            const uint4 wt = quad_transpose(st.w[j]);
+            const uint4 wt = quad_transpose(w[j]);
 #pragma unroll
             for (int t = 0; t < 4; t++) {
-                const uint32_t sz = st.s[j][t];
+                const uint32_t sz = s[j][t];
                 const float sc = ok ? f16_bits_to_f32(sz & 0xffffu) : 0.0f;
                 const h2 zz = __builtin_bit_cast(h2, (0x6400u | ((sz >> 16) & 15u)) * 0x00010001u);
                 const v8h wv = unpack_int4(word_of(wt, t), zz);
@@ -169,18 +175,17 @@ __device__ __forceinline__ void compute_stage(const Stage<NBLK, RB, SUB> &st, v4
         }
         return;
     }
-    rows256_to_fragments<RB>(st.a, a, xb, lane);
 #pragma unroll
     for (int j = 0; j < NBLK; j++) {
         const bool ok = kb_ok && nb0 + j < nblocks;
-        const float sc = ok ? f16_bits_to_f32(st.s[j][0]) : 0.0f;
-        const h2 zz = __builtin_bit_cast(h2, (0x6400u | (st.z[j] & 15u)) * 0x00010001u);
+        const float sc = ok ? f16_bits_to_f32(s[j][0]) : 0.0f;
+        const h2 zz = __builtin_bit_cast(h2, (0x6400u | (z[j] & 15u)) * 0x00010001u);
         v4f p[RB];
 #pragma unroll
         for (int b = 0; b < RB; b++) p[b] = v4f{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int t = 0; t < 4; t++) {
-            const v8h wv = unpack_int4(word_of(st.w[j], t), zz);
+            const v8h wv = unpack_int4(word_of(w[j], t), zz);
 #pragma unroll
             for (int b = 0; b < RB; b++) p[b] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[b][t], wv, p[b], 0, 0, 0);
         }
@@ -189,6 +194,17 @@ __device__ __forceinline__ void compute_stage(const Stage<NBLK, RB, SUB> &st, v4
 #pragma unroll
             for (int r = 0; r < 4; r++) acc[b][j][r] = __builtin_fmaf(sc, p[b][r], acc[b][j][r]);
     }
+}
+
+// One register stage: x pieces to fragments through the wave's LDS block,
+// then block_mma.
+template <int NBLK, int RB, bool SUB>
+__device__ __forceinline__ void compute_stage(const Stage<NBLK, RB, SUB> &st, v4f (&acc)[RB][NBLK], bool kb_ok,
+                                              int64_t nb0, int64_t nblocks, uint8_t *xb, int lane) {
+    v8h a[RB][4];
+    if constexpr (SUB) rows256_to_subblock_fragments<RB>(st.a, a, xb, lane);
+    else rows256_to_fragments<RB>(st.a, a, xb, lane);
+    block_mma<NBLK, RB, SUB>(a, st.w, st.s, st.z, acc, kb_ok, nb0, nblocks);
 }
 
 template <int NBLK, int WAVES, int RB, int OUT, int NST, bool SUB>
@@ -282,6 +298,207 @@ __global__ __launch_bounds__(WAVES * 64) void int4_grouped_kernel(const uint16_t
     }
 }
 
+
+// global_load_lds_dwordx4 issued from inline asm: lane l writes lds_base + 16 l.
+// The compiler does not see it, so its own waits for register loads are not
+// widened to vmcnt(0); the caller waits for it explicitly (s_waitcnt vmcnt).
+__device__ __forceinline__ void lds_load16_hidden(const void *src, const void *lds_base) {
+    const uint32_t m = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds_base);
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(src), "s"(m) : "memory", "m0");
+}
+
+// Compile-time loop: f(std::integral_constant<int, I>) for I in [B, E).
+template <int B, int E, typename F>
+__device__ __forceinline__ void static_for(F &&f) {
+    if constexpr (B < E) {
+        f(std::integral_constant<int, B>{});
+        static_for<B + 1, E>(f);
+    }
+}
+
+// Direct-load form for waves with at most NKB k blocks (k <= 128 * WAVES *
+// NKB).  The two-stage pipeline above issues a k block's weight loads only
+// after the block two earlier has arrived, so the HBM latency is paid once
+// per two blocks.  Here every weight, scale and zero-point load of the wave
+// is issued at the start (NKB * NBLK 16-byte weight fragments in registers),
+// and x moves L2 -> LDS with global_load_lds_dwordx4 into two buffers that
+// belong to the wave alone (no registers, no workgroup barrier): direct load
+// i of a k block writes rows 4i .. 4i + 3 of its RB * 16-row slice, lane l
+// taking 16-byte piece (l % 16) ^ (row % 16) of row 4i + l / 16 to LDS
+// position l % 16, so that the fragment reads of 16 rows (piece 4q + t, or
+// 4t + q for per-step groups, of row r at position piece ^ r) fall in
+// distinct banks.  The wave walks the same k blocks in the same order as the
+// pipelined kernel (kb = wave + u * WAVES), so the sums are the same bits.
+//
+// When the compiler sees a direct load pending it waits for every
+// outstanding load (vmcnt(0)) before the first use of any loaded register,
+// which would hold block 0 back until the wave's last weight arrived.  So
+// the direct loads and the fragment reads are issued from inline asm, in a
+// fixed order (weights of block 0, x(0), x(1), weights of the other blocks,
+// then x(u) after block u - 2, kept by scheduling barriers), the waits for
+// x are explicit vmcnt counts of the loads issued after it, and the
+// compiler's own waits for the register loads stay precise (they may only
+// over-wait, since the hidden loads are not in its count).
+template <int NBLK, int WAVES, int RB, int OUT, int NKB, bool SUB>
+__global__ __launch_bounds__(WAVES * 64) void int4_grouped_dl_kernel(const uint16_t *__restrict__ x,
+                                                                     const uint32_t *__restrict__ packed_w,
+                                                                     const uint16_t *__restrict__ scales,
+                                                                     const uint32_t *__restrict__ packed_z,
+                                                                     const float *__restrict__ bias,
+                                                                     int64_t group_size, int64_t m, int64_t n,
+                                                                     int64_t k, void *__restrict__ out) {
+    constexpr int XBUF = RB * 16 * 256;            // one k block of x for the row slice
+    constexpr int XL = XBUF / 1024;                // direct loads per k block
+    constexpr int NXB = NKB < 2 ? NKB : 2;         // x buffers per wave
+    constexpr int WL = NBLK * (SUB ? 9 : 3);       // weight, scale, zero loads per k block
+    constexpr int XS = WAVES * XBUF;
+    constexpr int RED = WAVES * RB * NBLK * kWave * 16;
+    static_assert(RED <= XS, "the partials reuse the first x buffer");
+    // Two distinct LDS objects, so the compiler's wait before a fragment read
+    // covers only the direct loads into that buffer.
+    __shared__ __attribute__((aligned(1024))) uint8_t xbuf0[XS];
+    __shared__ __attribute__((aligned(1024))) uint8_t xbuf1[NXB > 1 ? XS : 16];
+    const int lane = threadIdx.x % kWave, wave = wave_id();
+    const int64_t nb0 = (int64_t)blockIdx.x * NBLK;
+    const int64_t row0 = (int64_t)blockIdx.y * 16 * RB;
+    const int64_t nblocks = n / 16, kblocks = k / 128, groups = k / group_size;
+    const int fr = lane % 16, q = lane / 16;
+    const int64_t z = blockIdx.z;
+    x += z * m * k;
+    packed_w += z * (n * k / 8);
+    scales += z * n * groups;
+    packed_z += z * groups * (n / 8);
+    if (bias) bias += z * n;
+    const int64_t obase = z * m * n;
+
+    // Global source of each direct load of a k block (k block 0); rows past
+    // m read row 0 (their outputs are never stored).
+    const uint16_t *xsrc[XL];
+#pragma unroll
+    for (int i = 0; i < XL; i++) {
+        const int r = 4 * i + lane / 16;
+        const int64_t row = row0 + r;
+        xsrc[i] = x + (row < m ? row : 0) * k + 8 * ((lane % 16) ^ (r % 16));
+    }
+    auto kb_of = [&](int u) { return (int64_t)wave + (int64_t)u * WAVES; };
+    auto load_x = [&](int u) {
+        const int64_t kb = kb_of(u), kbc = kb < kblocks ? kb : kblocks - 1;
+        uint8_t *buf = (u % 2 == 0 ? xbuf0 : xbuf1) + wave * XBUF;
+#pragma unroll
+        for (int i = 0; i < XL; i++) lds_load16_hidden(xsrc[i] + kbc * 128, buf + 1024 * i);
+    };
+
+    uint4 w[NKB][NBLK];
+    uint32_t sc[NKB][NBLK][SUB ? 4 : 1], zr[NKB][NBLK];
+    auto load_w = [&](int u) {
+        const int64_t kb = kb_of(u), kbc = kb < kblocks ? kb : kblocks - 1;
+#pragma unroll
+        for (int j = 0; j < NBLK; j++) {
+            const int64_t nbc = nb0 + j < nblocks ? nb0 + j : nblocks - 1;
+            const int64_t col = nbc * 16 + fr;
+            w[u][j] = load16_stream(packed_w + (nbc * kblocks + kbc) * 256 + 4 * lane);
+            if constexpr (SUB) {
+                int64_t gt[4];
+                subblock_groups(kbc, group_size / 32, gt);
+#pragma unroll
+                for (int t = 0; t < 4; t++) sc[u][j][t] = scale_zero(scales, packed_z, col, gt[t], groups, n);
+                zr[u][j] = 0;
+            } else {
+                const int64_t g = kbc * 128 / group_size;
+                sc[u][j][0] = scales[col * groups + g];
+                zr[u][j] = packed_z[g * (n / 8) + col / 8] >> (4 * (col % 8));
+            }
+        }
+    };
+    // Issue order: weights of block 0, x(0), x(1), weights of blocks 1 ..
+    // NKB - 1, then x(u) for u >= 2 after block u - 2 (scheduling barriers
+    // keep it).
+    load_w(0);
+    __builtin_amdgcn_sched_barrier(0);
+    load_x(0);
+    if constexpr (NKB > 1) load_x(1);
+    __builtin_amdgcn_sched_barrier(0);
+    static_for<1, NKB>([&](auto uc) {
+        load_w(decltype(uc)::value);
+        __builtin_amdgcn_sched_barrier(0);
+    });
+
+    v4f acc[RB][NBLK];
+#pragma unroll
+    for (int b = 0; b < RB; b++)
+#pragma unroll
+        for (int j = 0; j < NBLK; j++) acc[b][j] = v4f{0.f, 0.f, 0.f, 0.f};
+
+    static_for<0, NKB>([&](auto uc) {
+        constexpr int u = decltype(uc)::value;
+        // Issue order: x(0), x(1), every weight load, then x(u) for u >= 2
+        // after block u - 2.  Wait until x(u) has landed (the weights are
+        // registers: the compiler waits for those itself).
+        // loads after x(0): x(1) and the weights of blocks 1 ..; after x(1):
+        // those weights and x(2)
+        constexpr int after0 = (NKB > 1 ? XL : 0) + (NKB - 1) * WL;
+        constexpr int after1 = (NKB - 1) * WL + (NKB > 2 ? XL : 0);
+        if constexpr (u == 0) wait_vmcnt<after0 < 63 ? after0 : 63>();
+        else if constexpr (u == 1) wait_vmcnt<after1 < 63 ? after1 : 63>();
+        else if constexpr (u + 1 < NKB) wait_vmcnt<XL>();
+        else wait_vmcnt<0>();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        const uint8_t *buf = (u % 2 == 0 ? xbuf0 : xbuf1) + wave * XBUF;
+        v8h a[RB][4];
+#pragma unroll
+        for (int b = 0; b < RB; b++) {
+            uint32_t ad[4];
+#pragma unroll
+            for (int t = 0; t < 4; t++) {
+                const int piece = SUB ? 4 * t + q : 4 * q + t;
+                ad[t] = (uint32_t)(uintptr_t)(buf + (16 * b + fr) * 256 + 16 * (piece ^ fr));
+            }
+            // The compiler cannot tell which direct loads wrote this buffer
+            // and would wait for every outstanding load; the explicit vmcnt
+            // wait above covers them, and the reads wait for themselves.
+            asm volatile(
+                "ds_read_b128 %0, %4\n\t"
+                "ds_read_b128 %1, %5\n\t"
+                "ds_read_b128 %2, %6\n\t"
+                "ds_read_b128 %3, %7\n\t"
+                "s_waitcnt lgkmcnt(0)"
+                : "=v"(a[b][0]), "=v"(a[b][1]), "=v"(a[b][2]), "=v"(a[b][3])
+                : "v"(ad[0]), "v"(ad[1]), "v"(ad[2]), "v"(ad[3])
+                : "memory");
+        }
+        block_mma<NBLK, RB, SUB>(a, w[u], sc[u], zr[u], acc, kb_of(u) < kblocks, nb0, nblocks);
+        if constexpr (u + 2 < NKB) {
+            // every fragment of this buffer was read into registers above
+            __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0)
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            load_x(u + 2);
+        }
+    });
+
+    __syncthreads();   // every wave is done with its x buffers: the same LDS holds the partials
+    v4f *red = reinterpret_cast<v4f *>(xbuf0);
+#pragma unroll
+    for (int b = 0; b < RB; b++)
+#pragma unroll
+        for (int j = 0; j < NBLK; j++) red[(wave * RB * NBLK + b * NBLK + j) * kWave + lane] = acc[b][j];
+    __syncthreads();
+    for (int e = wave; e < RB * NBLK; e += WAVES) {
+        const int b = e / NBLK, j = e % NBLK;
+        const int64_t nb = nb0 + j;
+        if (nb >= nblocks) continue;
+        v4f sum = red[e * kWave + lane];
+#pragma unroll
+        for (int wv = 1; wv < WAVES; wv++) sum += red[(wv * RB * NBLK + e) * kWave + lane];
+        const int64_t col = nb * 16 + fr;
+        const float cb = bias ? bias[col] : 0.0f;
+#pragma unroll
+        for (int r = 0; r < 4; r++) {
+            const int64_t row = row0 + b * 16 + 4 * (lane / 16) + r;
+            if (row < m) store_out<OUT>(out, obase + row * n + col, bias ? __fadd_rn(sum[r], cb) : sum[r]);
+        }
+    }
+}
+
 // Waves with at most this many k blocks issue all their loads at once.
 constexpr int kAllIn = 4;
 
@@ -291,6 +508,21 @@ hipError_t launch_cfg(const uint16_t *x, const uint32_t *packed_w, const uint16_
                       void *out, hipStream_t st, int64_t batch) {
     const int64_t nblocks = n / 16;
     dim3 grid((unsigned)((nblocks + NBLK - 1) / NBLK), (unsigned)((m + 16 * RB - 1) / (16 * RB)), (unsigned)batch);
+    // Two row blocks with at most four k blocks per wave: the direct-load
+    // form (all weight loads at the start, x straight into LDS).
+    if constexpr (RB == 2) {
+        const int64_t per_wave = (k / 128 + WAVES - 1) / WAVES;
+        if (per_wave <= 2) {
+            hipLaunchKernelGGL((int4_grouped_dl_kernel<NBLK, WAVES, RB, OUT, 2, SUB>), grid, dim3(WAVES * 64), 0, st,
+                               x, packed_w, scales, packed_z, bias, group_size, m, n, k, out);
+            return hipGetLastError();
+        }
+        if (per_wave <= 4) {
+            hipLaunchKernelGGL((int4_grouped_dl_kernel<NBLK, WAVES, RB, OUT, 4, SUB>), grid, dim3(WAVES * 64), 0, st,
+                               x, packed_w, scales, packed_z, bias, group_size, m, n, k, out);
+            return hipGetLastError();
+        }
+    }
     // With two row blocks, four stages of x fragments do not fit beside the
     // weights in registers, nor do four stages of per-step scales: those
     // launches keep the two-stage pipeline.
