@@ -525,8 +525,15 @@ __global__ __launch_bounds__(WAVES * 64) void w2a8_gemv_kernel(const int8_t *__r
         for (int j = 0; j < NBLK; j++) acc[b][j] = v4i{0, 0, 0, 0};
 
     // Two register stages of U k blocks each: the loads of the next stage are
-    // in flight while the matrix cores consume the current one.
+    // in flight while the matrix cores consume the current one.  U >= 4: one
+    // stage holds every k block of the wave (the host launches it only when
+    // kblocks <= WAVES * U), all loads issued at the start.
     constexpr int64_t step = (int64_t)WAVES * U;
+    if constexpr (U >= 4) {
+        GemvStage<NBLK, U, RB> s0;
+        gemv_load<NBLK, WAVES, U, RB, XT>(s0, xrow, packed, wave, nb0, nblocks, kblocks, lane, row_live, xq, m, k);
+        gemv_compute<NBLK, WAVES, U, RB, XT>(s0, acc, wave, kblocks, xb, lane);
+    } else {
     GemvStage<NBLK, U, RB> s0, s1;
     int64_t kb = wave;
     gemv_load<NBLK, WAVES, U, RB, XT>(s0, xrow, packed, kb, nb0, nblocks, kblocks, lane, row_live, xq, m, k);
@@ -542,6 +549,7 @@ __global__ __launch_bounds__(WAVES * 64) void w2a8_gemv_kernel(const int8_t *__r
         gemv_compute<NBLK, WAVES, U, RB, XT>(s1, acc, kb1, kblocks, xb, lane);
         if (kb2 >= kblocks) break;
         kb = kb2;
+    }
     }
 
 #pragma unroll
@@ -651,8 +659,12 @@ hipError_t launch_out(const int8_t *xq, const float *pts, const int32_t *rowsum,
         // HBM, 8 waves and one k block per register stage: 4 column blocks per
         // workgroup up to m = 4, 7 above (1792 column blocks = 256 workgroups).
         // Above m = 4 (and k >= 2048, as for more row blocks), x moves in
-        // whole cache lines through LDS.
+        // whole cache lines through LDS, and up to k = 8192 every k block of
+        // a wave is loaded at the start (one stage: 13.7-13.9 against
+        // 14.6-14.7 us at m = 16; slower at m = 1 and 4 with 7 column blocks).
         if (m <= 4) return launch_gemv<4, 8, 1, 1, OUT>(xq, pts, rowsum, packed, gamma, bias, m, n, k, out, st);
+        if (k >= 2048 && k / 256 <= 8 * 4)
+            return launch_gemv<7, 8, 4, 1, OUT, true>(xq, pts, rowsum, packed, gamma, bias, m, n, k, out, st);
         if (k >= 2048)
             return launch_gemv<7, 8, 1, 1, OUT, true>(xq, pts, rowsum, packed, gamma, bias, m, n, k, out, st);
         return launch_gemv<7, 8, 1, 1, OUT>(xq, pts, rowsum, packed, gamma, bias, m, n, k, out, st);

@@ -326,7 +326,9 @@ W2A8_SHAPES = [(1, 400, 512), (2, 256, 768), (4, 400, 512), (5, 64, 256), (16, 4
                # 96 < m <= 128, k >= 2048, at most 1024 column blocks: two decode launches
                (100, 400, 2048), (128, 1008, 4096),
                # 64 < m <= 128, k >= 2048, more than 1024 column blocks: the 128x128 tiles
-               (96, 16400, 2048), (120, 16400, 2048)]
+               (96, 16400, 2048), (120, 16400, 2048),
+               # 4 < m <= 16, 2048 <= k <= 8192: every k block of a wave loaded at the start
+               (9, 1008, 8192), (16, 48, 2304), (5, 400, 4096)]
 
 
 @pytest.mark.parametrize("m,n,k", W2A8_SHAPES)
@@ -551,7 +553,8 @@ def test_w8a8_bias_parity(m, n, k, nk):
 
 
 @pytest.mark.parametrize("m,n,k", [(1, 400, 512), (16, 400, 768), (40, 400, 512), (130, 256, 768), (300, 400, 512),
-                                   (100, 400, 2048)])   # two decode launches (64 and 36 rows)
+                                   (100, 400, 2048),    # two decode launches (64 and 36 rows)
+                                   (16, 400, 4096)])    # one-stage decode kernel
 def test_w2a8_bias_parity(m, n, k):
     d = synthetic.bitlinear(m, n, k, seed=1400 + m + n)
     xq_ref, pts_ref, _ = oracle.quant_act(d["x"].float().numpy(), rmsnorm=True)
