@@ -128,25 +128,32 @@ struct Epilogue {
 __device__ __forceinline__ int32_t acc_i32(int32_t v) { return v; }
 __device__ __forceinline__ int32_t acc_i32(float v) { return (int32_t)v; }
 
-template <int EPI, int OUT, typename ACC>
-__device__ __forceinline__ void big_epilogue(const Params &p, const ACC (&acc)[4][4], int8_t *smem, int64_t m0,
+// The wave's sub-tile is 128 rows (wm) x 32 BJ columns (wn); LDS needs
+// 1024 + waves x 128 x big_epitch(BJ) bytes.
+constexpr int big_epitch(int bj) { return 64 * bj + 16; }
+
+template <int EPI, int OUT, int BJ, typename ACC>
+__device__ __forceinline__ void big_epilogue(const Params &p, const ACC (&acc)[4][BJ], int8_t *smem, int64_t m0,
                                              int64_t n0, int wm, int wn, int wave, int lane) {
-    constexpr int EPITCH = 128 * 2 + 16;
+    constexpr int EPITCH = big_epitch(BJ);
+    constexpr int PIECES = 4 * BJ;        // 16-byte pieces of a sub-tile row
+    constexpr int RPQ = kWave / PIECES;   // rows per store instruction
     const int fr = lane % 32;
+    const int64_t c0 = n0 + wn * 32 * BJ;
     Epilogue<EPI, OUT> ep;
     ep.init(p);
     ep.stage_rows(p, m0, LB, reinterpret_cast<float *>(smem));
     __syncthreads();
-    float cf[4], cb[4];
+    float cf[BJ], cb[BJ];
 #pragma unroll
-    for (int j = 0; j < 4; j++) {
-        cf[j] = ep.col_factor(p, n0 + wn * 128 + 32 * j + fr);
-        cb[j] = ep.col_bias(p, n0 + wn * 128 + 32 * j + fr);
+    for (int j = 0; j < BJ; j++) {
+        cf[j] = ep.col_factor(p, c0 + 32 * j + fr);
+        cb[j] = ep.col_bias(p, c0 + 32 * j + fr);
     }
     if constexpr (OUT == OUT_F16 || OUT == OUT_BF16) {
-        // Through LDS: the wave rounds its 128 x 128 sub-tile into a padded
-        // LDS tile (the two row groups of one write land 16 banks apart), then
-        // writes whole 256-byte row segments, 16 bytes per lane.
+        // Through LDS: the wave rounds its sub-tile into a padded LDS tile
+        // (the two row groups of one write land 16 banks apart), then writes
+        // whole row segments, 16 bytes per lane.
         int8_t *tile = smem + 1024 + wave * 128 * EPITCH;
 #pragma unroll
         for (int i = 0; i < 4; i++)
@@ -155,7 +162,7 @@ __device__ __forceinline__ void big_epilogue(const Params &p, const ACC (&acc)[4
                 const int lr = 32 * i + 8 * (r / 4) + 4 * (lane / 32) + (r % 4);
                 const float rf = ep.row_factor(wm * 128 + lr);
 #pragma unroll
-                for (int j = 0; j < 4; j++) {
+                for (int j = 0; j < BJ; j++) {
                     const float y = ep.value(p, acc_i32(acc[i][j][r]), rf, cf[j], cb[j]);
                     *reinterpret_cast<uint16_t *>(tile + lr * EPITCH + 2 * (32 * j + fr)) =
                         OUT == OUT_F16 ? f32_to_f16_rne(y) : f32_to_bf16_rne(y);
@@ -165,10 +172,10 @@ __device__ __forceinline__ void big_epilogue(const Params &p, const ACC (&acc)[4
         __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0)
         __builtin_amdgcn_wave_barrier();
 #pragma unroll
-        for (int q = 0; q < 32; q++) {
-            const int lr = 4 * q + lane / 16, piece = lane % 16;
+        for (int q = 0; q < 128 / RPQ; q++) {
+            const int lr = RPQ * q + lane / PIECES, piece = lane % PIECES;
             const uint4 v = *reinterpret_cast<const uint4 *>(tile + lr * EPITCH + 16 * piece);
-            const int64_t row = m0 + wm * 128 + lr, col = n0 + wn * 128 + 8 * piece;
+            const int64_t row = m0 + wm * 128 + lr, col = c0 + 8 * piece;
             if (row < p.m) {
                 uint16_t *dst = static_cast<uint16_t *>(p.out) + row * p.n + col;
                 if (col + 8 <= p.n && (p.n % 8) == 0) {
@@ -185,8 +192,8 @@ __device__ __forceinline__ void big_epilogue(const Params &p, const ACC (&acc)[4
         return;
     }
 #pragma unroll
-    for (int j = 0; j < 4; j++) {
-        const int64_t col = n0 + wn * 128 + 32 * j + fr;
+    for (int j = 0; j < BJ; j++) {
+        const int64_t col = c0 + 32 * j + fr;
         if (col >= p.n) continue;
 #pragma unroll
         for (int i = 0; i < 4; i++)
@@ -203,8 +210,8 @@ __global__ __launch_bounds__(LThreads, 1) void gemm_i8_big_kernel(Params p, int 
     constexpr int STAGE = 2 * BigTile<BK>::TILE;
     // main loop: a ring of NBUF (A, B) slices; epilogue: 1 KB of row factors,
     // then one padded 128 x 128 output sub-tile per wave (2-byte outputs)
-    constexpr int EPITCH = 128 * 2 + 16;
-    constexpr int SMEM = NBUF * STAGE > 1024 + 4 * 128 * EPITCH ? NBUF * STAGE : 1024 + 4 * 128 * EPITCH;
+    constexpr int EPI_BYTES = 1024 + 4 * 128 * big_epitch(4);
+    constexpr int SMEM = NBUF * STAGE > EPI_BYTES ? NBUF * STAGE : EPI_BYTES;
     __shared__ __attribute__((aligned(1024))) int8_t smem[SMEM];
 
     to_batch(p);
@@ -221,7 +228,7 @@ __global__ __launch_bounds__(LThreads, 1) void gemm_i8_big_kernel(Params p, int 
 // ---------------------------------------------------------------------------
 // 4-bit product on FP6 E3M2 operand tiles
 // ---------------------------------------------------------------------------
-// The tile, ring and epilogue of the large-tile kernel, on
+// The 256 x 256 tile of the large-tile kernel on
 // v_mfma_scale_f32_32x32x64_f8f6f4 with both operands E3M2 and unit block
 // scales: twice the int8 matrix-core rate per instruction.  Codes are
 // integers in [-8, 7], so every product and partial sum is an integer of
@@ -231,10 +238,24 @@ __global__ __launch_bounds__(LThreads, 1) void gemm_i8_big_kernel(Params p, int 
 // and 1024 + 8l (8 bytes); a 128-k slice of a 32-row block is two adjacent
 // tiles, so slices copy to LDS unchanged and every fragment is one 16-byte
 // and one 8-byte read by consecutive lanes.
+//
+// Eight waves, two per SIMD (waves w and w + 4 share SIMD w % 4), each own a
+// 128 x 64 sub-tile (4 x 2 blocks of 32 x 32).  The two groups of four
+// waves run opposite phases of a slice: while one group issues its 16
+// products, its SIMD partners read their fragments of the slice from LDS
+// and issue their share of the direct global -> LDS loads two slices ahead,
+// so the matrix cores see a ready wave at every phase.  Two workgroup
+// barriers per slice separate the phases; the second group passes one extra
+// barrier at the start and the first group one at the end, which puts them
+// half a slice apart.  Before every barrier a wave waits until at most one
+// slice of its own loads is in flight, so a slice has fully landed (all
+// waves' loads) at the barrier before the first read of it, and a ring of
+// three LDS slices is never overwritten while a partner still reads it.
 constexpr int kF6Tile = 1536;
 constexpr int kF6Op = 8 * 2 * kF6Tile;        // one operand's 256-row x 128-k slice
-constexpr int kF6Buf = 3;
-constexpr int kF6Loads = kF6Op / 1024 / 4;    // 1 KB direct loads per wave and operand
+constexpr int kF6Buf = 3;                     // LDS slices in the ring
+constexpr int kF6Waves = 8;
+constexpr int kF6Loads = kF6Op / 1024 / kF6Waves;   // 1 KB direct loads per wave and operand
 constexpr int kF6Scale = 0x7f7f7f7f;          // E8M0 127 (2^0) in every byte
 
 __device__ __forceinline__ v8i f6_frag(const int8_t *tile, int lane) {
@@ -243,55 +264,16 @@ __device__ __forceinline__ v8i f6_frag(const int8_t *tile, int lane) {
     return v8i{(int)a.x, (int)a.y, (int)a.z, (int)a.w, (int)b.x, (int)b.y, 0, 0};
 }
 
-// One 128-k slice: the direct loads of a later slice into `nxt`, then two
-// 64-k MFMA steps on `cur`, the second step's fragments read while the first
-// step's MFMAs issue (distinct restrict pointers, as in big_slice).
-__device__ __forceinline__ void f6_slice(v16f (&acc)[4][4], const int8_t *__restrict__ cur,
-                                         int8_t *__restrict__ nxt, const int8_t *const (&srcA)[kF6Loads],
-                                         const int8_t *const (&srcB)[kF6Loads], int64_t nxt_off, int wm, int wn,
-                                         int lane, int wave) {
-#pragma unroll
-    for (int ii = 0; ii < kF6Loads; ii++) {
-        const int inst = wave * kF6Loads + ii;
-        lds_load16(srcA[ii] + nxt_off, nxt + 1024 * inst);
-        lds_load16(srcB[ii] + nxt_off, nxt + kF6Op + 1024 * inst);
-    }
-    v8i fa[2][4], fb[2][4];
-    auto frags = [&](int s) {
-#pragma unroll
-        for (int i = 0; i < 4; i++) fa[s][i] = f6_frag(cur + ((wm * 4 + i) * 2 + s) * kF6Tile, lane);
-#pragma unroll
-        for (int j = 0; j < 4; j++) fb[s][j] = f6_frag(cur + kF6Op + ((wn * 4 + j) * 2 + s) * kF6Tile, lane);
-    };
-    frags(0);
-#pragma unroll
-    for (int s = 0; s < 2; s++) {
-        if (s == 0) frags(1);
-#pragma unroll
-        for (int i = 0; i < 4; i++)
-#pragma unroll
-            for (int j = 0; j < 4; j++)
-                acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa[s][i], fb[s][j], acc[i][j], 3, 3, 0,
-                                                                            kF6Scale, 0, kF6Scale);
-        if (s == 0) {
-#pragma unroll
-            for (int q = 0; q < 16; q++) {
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-            }
-        }
-    }
-}
-
 template <int OUT>
-__global__ __launch_bounds__(LThreads, 1) void gemm_a4w4_f6_kernel(Params p, int tiles_m, int tiles_n) {
+__global__ __launch_bounds__(kF6Waves * kWave, 1) void gemm_a4w4_f6_kernel(Params p, int tiles_m, int tiles_n) {
     constexpr int STAGE = 2 * kF6Op;
-    constexpr int EPITCH = 128 * 2 + 16;
-    constexpr int SMEM = kF6Buf * STAGE > 1024 + 4 * 128 * EPITCH ? kF6Buf * STAGE : 1024 + 4 * 128 * EPITCH;
+    constexpr int EPI_BYTES = 1024 + kF6Waves * 128 * big_epitch(2);
+    constexpr int SMEM = kF6Buf * STAGE > EPI_BYTES ? kF6Buf * STAGE : EPI_BYTES;
     __shared__ __attribute__((aligned(1024))) int8_t smem[SMEM];
 
     const int lane = threadIdx.x % kWave, wave = wave_id();
-    const int wm = wave / 2, wn = wave % 2;
+    const int group = wave / 4;
+    const int wm = wave % 2, wn = (wave / 2) % 4;   // 2 x 4 sub-tiles of 128 x 64
     int tm, tn;
     xcd_tile(blockIdx.x, tiles_m, tiles_n, kGroupM, tm, tn);
     const int64_t m0 = (int64_t)tm * LB, n0 = (int64_t)tn * LB;
@@ -312,30 +294,57 @@ __global__ __launch_bounds__(LThreads, 1) void gemm_a4w4_f6_kernel(Params p, int
         srcA[ii] = p.x + ra * ktiles * kF6Tile + 1024 * piece + 16 * lane;
         srcB[ii] = p.w + rb * ktiles * kF6Tile + 1024 * piece + 16 * lane;
     }
-
-    v16f acc[4][4];
-#pragma unroll
-    for (int i = 0; i < 4; i++)
-#pragma unroll
-        for (int j = 0; j < 4; j++) acc[i][j] = v16f{};
-
-#pragma unroll
-    for (int b = 0; b < kF6Buf - 1; b++) {
-        const int64_t off = (int64_t)(b < nk ? b : nk - 1) * 2 * kF6Tile;
+    // slices past the end re-read the last one into the ring's free slot
+    auto issue = [&](int64_t slice, int buf) __attribute__((always_inline)) {
+        const int64_t off = (slice < nk ? slice : nk - 1) * 2 * kF6Tile;
 #pragma unroll
         for (int ii = 0; ii < kF6Loads; ii++) {
             const int inst = wave * kF6Loads + ii;
-            lds_load16(srcA[ii] + off, smem + b * STAGE + 1024 * inst);
-            lds_load16(srcB[ii] + off, smem + b * STAGE + kF6Op + 1024 * inst);
+            lds_load16(srcA[ii] + off, smem + buf * STAGE + 1024 * inst);
+            lds_load16(srcB[ii] + off, smem + buf * STAGE + kF6Op + 1024 * inst);
         }
+    };
+
+    v16f acc[4][2];
+#pragma unroll
+    for (int i = 0; i < 4; i++)
+#pragma unroll
+        for (int j = 0; j < 2; j++) acc[i][j] = v16f{};
+
+    issue(0, 0);
+    issue(1, 1);
+    if (group == 1) {
+        wait_vmcnt<2 * kF6Loads>();
+        barrier_only();
     }
     for (int64_t kt = 0; kt < nk; kt++) {
-        wait_vmcnt<(kF6Buf - 2) * 2 * kF6Loads>();
+        // fragment phase: this slice to registers, slice kt + 2 requested
+        wait_vmcnt<2 * kF6Loads>();
         barrier_only();
-        const int cur = (int)(kt % kF6Buf), nxt = (int)((kt + kF6Buf - 1) % kF6Buf);
-        const int64_t nxt_off = (kt + kF6Buf - 1 < nk ? kt + kF6Buf - 1 : nk - 1) * 2 * kF6Tile;
-        f6_slice(acc, smem + cur * STAGE, smem + nxt * STAGE, srcA, srcB, nxt_off, wm, wn, lane, wave);
+        const int8_t *cur = smem + (int)(kt % kF6Buf) * STAGE;
+        v8i fa[2][4], fb[2][2];
+#pragma unroll
+        for (int st = 0; st < 2; st++) {
+#pragma unroll
+            for (int i = 0; i < 4; i++) fa[st][i] = f6_frag(cur + ((wm * 4 + i) * 2 + st) * kF6Tile, lane);
+#pragma unroll
+            for (int j = 0; j < 2; j++) fb[st][j] = f6_frag(cur + kF6Op + ((wn * 2 + j) * 2 + st) * kF6Tile, lane);
+        }
+        issue(kt + 2, (int)((kt + 2) % kF6Buf));
+        __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0): the fragments are in registers
+        wait_vmcnt<2 * kF6Loads>();
+        barrier_only();
+        // product phase
+#pragma unroll
+        for (int st = 0; st < 2; st++)
+#pragma unroll
+            for (int i = 0; i < 4; i++)
+#pragma unroll
+                for (int j = 0; j < 2; j++)
+                    acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa[st][i], fb[st][j], acc[i][j], 3, 3,
+                                                                                0, kF6Scale, 0, kF6Scale);
     }
+    if (group == 0) barrier_only();
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     big_epilogue<EPI_SCALARS, OUT>(p, acc, smem, m0, n0, wm, wn, wave, lane);
@@ -345,8 +354,8 @@ template <int OUT>
 hipError_t launch_f6(const Params &p, hipStream_t st) {
     const int64_t tm = (p.m + LB - 1) / LB, tn = (p.n + LB - 1) / LB;
     if (tm * tn > 0x7fffffff) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((gemm_a4w4_f6_kernel<OUT>), dim3((unsigned)(tm * tn)), dim3(LThreads), 0, st, p, (int)tm,
-                       (int)tn);
+    hipLaunchKernelGGL((gemm_a4w4_f6_kernel<OUT>), dim3((unsigned)(tm * tn)), dim3(kF6Waves * kWave), 0, st, p,
+                       (int)tm, (int)tn);
     return hipGetLastError();
 }
 
@@ -404,8 +413,8 @@ __device__ __forceinline__ void store_image(int8_t *tile, int l, const v6u &img)
 template <int OUT>
 __global__ __launch_bounds__(LThreads, 1) void gemm_a4w4_packed_kernel(Params p, int tiles_m, int tiles_n) {
     constexpr int STAGE = 2 * kF6Op;
-    constexpr int EPITCH = 128 * 2 + 16;
-    constexpr int SMEM = 2 * STAGE > 1024 + 4 * 128 * EPITCH ? 2 * STAGE : 1024 + 4 * 128 * EPITCH;
+    constexpr int EPI_BYTES = 1024 + 4 * 128 * big_epitch(4);
+    constexpr int SMEM = 2 * STAGE > EPI_BYTES ? 2 * STAGE : EPI_BYTES;
     __shared__ __attribute__((aligned(1024))) int8_t smem[SMEM];
 
     const int lane = threadIdx.x % kWave, wave = wave_id();
@@ -885,6 +894,58 @@ __device__ __forceinline__ void gemv_compute(const GemvStage<NBLK, SPS, RB> &st,
     }
 }
 
+// Row factors of lane's output rows 16 b + 4 (lane / 16) + r of the decode
+// kernels (rows past m repeat the last one; they are never stored).
+template <int RB, int EPI, int OUT>
+__device__ __forceinline__ void gemv_row_factors(const Params &p, const Epilogue<EPI, OUT> &ep, float (&rf)[RB][4],
+                                                 int lane) {
+#pragma unroll
+    for (int b = 0; b < RB; b++)
+#pragma unroll
+        for (int r = 0; r < 4; r++) {
+            const int64_t row = 16 * b + 4 * (lane / 16) + r < p.m ? 16 * b + 4 * (lane / 16) + r : p.m - 1;
+            rf[b][r] = OUT == OUT_I32 ? 0.0f : (EPI == EPI_ROWCOL ? p.pts[row] : ep.sa);
+        }
+}
+
+// The decode kernels' end: every wave's 16x16 int32 partials to LDS, then
+// each output block summed over the WAVES waves in wave order (exact) and
+// stored through the epilogue.  Lane l holds column l % 16 and rows
+// 4 (l / 16) + r of a block; column blocks nb0 .. nb0 + NBLK - 1.
+template <int WAVES, int RB, int NBLK, int EPI, int OUT>
+__device__ __forceinline__ void gemv_reduce_store(const Params &p, const Epilogue<EPI, OUT> &ep,
+                                                  const v4i (&acc)[RB][NBLK], v4i (*red)[RB * NBLK][kWave],
+                                                  const float (&rf)[RB][4], int64_t nb0, int wave, int lane) {
+    const int fr = lane % 16;
+#pragma unroll
+    for (int b = 0; b < RB; b++)
+#pragma unroll
+        for (int j = 0; j < NBLK; j++) red[wave][b * NBLK + j][lane] = acc[b][j];
+    __syncthreads();
+    for (int e = wave; e < RB * NBLK; e += WAVES) {
+        const int b = e / NBLK, j = e % NBLK;
+        const int64_t col = (nb0 + j) * 16 + fr;
+        if (col >= p.n) continue;
+        v4i sum = red[0][e][lane];
+#pragma unroll
+        for (int w = 1; w < WAVES; w++) sum += red[w][e][lane];
+        const float cf = ep.col_factor(p, col), cb = ep.col_bias(p, col);
+        float rfe[4];
+#pragma unroll
+        for (int r = 0; r < 4; r++) rfe[r] = rf[0][r];
+#pragma unroll
+        for (int bb = 1; bb < RB; bb++)
+            if (bb == b)
+#pragma unroll
+                for (int r = 0; r < 4; r++) rfe[r] = rf[bb][r];
+#pragma unroll
+        for (int r = 0; r < 4; r++) {
+            const int64_t row = 16 * b + 4 * (lane / 16) + r;
+            if (row < p.m) ep.store(p, row, col, sum[r], rfe[r], cf, cb);
+        }
+    }
+}
+
 template <int NBLK, int SPS, int RB, int EPI, int OUT, bool XT>
 __global__ __launch_bounds__(kGvWaves * 64) void gemv_i8_kernel(Params p) {
     __shared__ v4i red[kGvWaves][RB * NBLK][kWave];
@@ -916,18 +977,12 @@ __global__ __launch_bounds__(kGvWaves * 64) void gemv_i8_kernel(Params p) {
         const int64_t col = (nb0 + i / 2) * 16 + 8 * (i % 2) + lane / 8;
         wcol[i] = p.w + (col < p.n ? col : p.n - 1) * p.k + 16 * (lane % 8);
     }
-    // row factors of this lane's output rows 16 b + 4 (lane / 16) + r, loaded
-    // now so their latency hides behind the k loop
+    // row factors of this lane's output rows, loaded now so their latency
+    // hides behind the k loop
     Epilogue<EPI, OUT> ep;
     ep.init(p);
     float rf[RB][4];
-#pragma unroll
-    for (int b = 0; b < RB; b++)
-#pragma unroll
-        for (int r = 0; r < 4; r++) {
-            const int64_t row = 16 * b + 4 * (lane / 16) + r < p.m ? 16 * b + 4 * (lane / 16) + r : p.m - 1;
-            rf[b][r] = OUT == OUT_I32 ? 0.0f : (EPI == EPI_ROWCOL ? p.pts[row] : ep.sa);
-        }
+    gemv_row_factors<RB>(p, ep, rf, lane);
 
     v4i acc[RB][NBLK];
 #pragma unroll
@@ -948,33 +1003,7 @@ __global__ __launch_bounds__(kGvWaves * 64) void gemv_i8_kernel(Params p) {
         kb = kb2;
     }
 
-#pragma unroll
-    for (int b = 0; b < RB; b++)
-#pragma unroll
-        for (int j = 0; j < NBLK; j++) red[wave][b * NBLK + j][lane] = acc[b][j];
-    __syncthreads();
-    for (int e = wave; e < RB * NBLK; e += kGvWaves) {
-        const int b = e / NBLK, j = e % NBLK;
-        const int64_t col = (nb0 + j) * 16 + fr;
-        if (col >= p.n) continue;
-        v4i sum = red[0][e][lane];
-#pragma unroll
-        for (int w = 1; w < kGvWaves; w++) sum += red[w][e][lane];
-        const float cf = ep.col_factor(p, col), cb = ep.col_bias(p, col);
-        float rfe[4];
-#pragma unroll
-        for (int r = 0; r < 4; r++) rfe[r] = rf[0][r];
-#pragma unroll
-        for (int bb = 1; bb < RB; bb++)
-            if (bb == b)
-#pragma unroll
-                for (int r = 0; r < 4; r++) rfe[r] = rf[bb][r];
-#pragma unroll
-        for (int r = 0; r < 4; r++) {
-            const int64_t row = 16 * b + 4 * (lane / 16) + r;
-            if (row < p.m) ep.store(p, row, col, sum[r], rfe[r], cf, cb);
-        }
-    }
+    gemv_reduce_store<kGvWaves, RB, NBLK>(p, ep, acc, red, rf, nb0, wave, lane);
 }
 
 template <int NBLK, int SPS, int RB, int EPI, int OUT>
@@ -1033,6 +1062,177 @@ hipError_t launch_gemv_rb(const Params &p, int64_t batch, hipStream_t st) {
         // (eight row blocks: 128-k stages no longer fit in registers)
         default: return launch_gemv_t<1, 1, 8, EPI, OUT>(p, batch, st);
     }
+}
+
+// ---------------------------------------------------------------------------
+// Decode kernel for [k][n] weights: m <= 64, k % 64 == 0, n % 4 == 0
+// ---------------------------------------------------------------------------
+// The matrix cores take the weights as 16 consecutive k of one column per
+// lane, which [k][n] rows do not hold.  A workgroup owns 16 NBLK columns;
+// lane (q, c) of a 64-k step loads NBLK column dwords (4 NBLK columns from
+// 4 NBLK c on) of rows 4 q .. 4 q + 3, transposes each 4 x 4 byte block in
+// registers into 4-k column words, writes them to the wave's LDS block as
+// [column][k] and reads whole 16-byte fragments back.  The x fragments come
+// straight from the row-major activations, as in the [n][k] decode kernel.
+// WAVES waves take turns over the 64-k steps, S steps at a time in flight in
+// registers; their int32 partials are summed in LDS in wave order (exact).
+// Workgroups are laid out so that each XCD (workgroup id mod 8) owns a
+// contiguous run of column groups and its L2 serves neighbouring rows.
+//
+// LDS: column c's 64 k at c * 80 + (c / 16) * 64 bytes.  The 80-byte pitch
+// puts the 16 fragment reads of a step in distinct banks, and the extra 64
+// bytes per 16 columns spread the writes of the NBLK column blocks over
+// distinct bank groups.
+constexpr int kKnPitch = 80;
+constexpr int kKnBlock = 16 * kKnPitch + 64;
+
+__device__ __forceinline__ int kn_lds_col(int c) { return c * kKnPitch + (c / 16) * 64; }
+
+template <int NBLK, int RB>
+struct KnStage {
+    static_assert(NBLK == 1 || NBLK == 4, "one column dword or one 16-byte piece per row and lane");
+    v4i a[RB];
+    uint32_t w[4][NBLK];   // rows 4 q + i, NBLK column dwords
+};
+
+template <int NBLK, int RB>
+__device__ __forceinline__ void kn_load(KnStage<NBLK, RB> &st, const int8_t *const (&xrow)[RB], const int8_t *wblk,
+                                        int64_t step, int64_t n) {
+    const int64_t k0 = step * 64;
+#pragma unroll
+    for (int b = 0; b < RB; b++) st.a[b] = *reinterpret_cast<const v4i *>(xrow[b] + k0);
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+        const int8_t *src = wblk + (k0 + i) * n;
+        if constexpr (NBLK == 4) {
+            const uint4 v = load16_stream(src);
+            st.w[i][0] = v.x; st.w[i][1] = v.y; st.w[i][2] = v.z; st.w[i][3] = v.w;
+        } else {
+            st.w[i][0] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t *>(src));
+        }
+    }
+}
+
+template <int NBLK, int RB, int WAVES, int S, int EPI, int OUT>
+__global__ __launch_bounds__(WAVES * 64) void gemv_kn_i8_kernel(Params p, int groups) {
+    __shared__ v4i red[WAVES][RB * NBLK][kWave];
+    __shared__ __attribute__((aligned(16))) uint8_t wt[WAVES][NBLK * kKnBlock];
+    to_batch(p);
+    const int lane = threadIdx.x % kWave, wave = wave_id();
+    // XCD-contiguous column groups: workgroup b runs on XCD b % 8
+    const int xcd = blockIdx.x % 8, slot = blockIdx.x / 8;
+    const int per = groups / 8, rem = groups % 8;
+    const int64_t nb0 = (int64_t)(xcd * per + min(xcd, rem) + slot) * NBLK;
+    const int64_t nsteps = p.k / 64;
+
+    const int8_t *xrow[RB];
+#pragma unroll
+    for (int b = 0; b < RB; b++) {
+        const int64_t row = 16 * b + lane % 16;
+        xrow[b] = p.x + (row < p.m ? row : 0) * p.k + 16 * (lane / 16);
+    }
+    // lane (q, c): rows 4 q + i of the step, columns 4 NBLK c .. + 4 NBLK - 1
+    // of the group (past n: the last whole dwords, never stored)
+    const int c = lane % 4, q = lane / 4;
+    const int64_t wcol = min(nb0 * 16 + 4 * NBLK * c, p.n - 4 * NBLK);
+    const int8_t *wblk = p.w + (int64_t)(4 * q) * p.n + wcol;
+    uint8_t *wl = wt[wave];
+
+    Epilogue<EPI, OUT> ep;
+    ep.init(p);
+    float rf[RB][4];
+    gemv_row_factors<RB>(p, ep, rf, lane);
+
+    v4i acc[RB][NBLK];
+#pragma unroll
+    for (int b = 0; b < RB; b++)
+#pragma unroll
+        for (int j = 0; j < NBLK; j++) acc[b][j] = v4i{0, 0, 0, 0};
+
+    auto compute = [&](const KnStage<NBLK, RB> &st) __attribute__((always_inline)) {
+#pragma unroll
+        for (int d = 0; d < NBLK; d++) {
+            const uint32_t rowv[4] = {st.w[0][d], st.w[1][d], st.w[2][d], st.w[3][d]};
+#pragma unroll
+            for (int j = 0; j < 4; j++)
+                *reinterpret_cast<uint32_t *>(wl + kn_lds_col(4 * NBLK * c + 4 * d + j) + 4 * q) = kn_column(rowv, j);
+        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        v4i wf[NBLK];
+#pragma unroll
+        for (int j = 0; j < NBLK; j++)
+            wf[j] = *reinterpret_cast<const v4i *>(wl + kn_lds_col(16 * j + lane % 16) + 16 * (lane / 16));
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+        for (int b = 0; b < RB; b++)
+#pragma unroll
+            for (int j = 0; j < NBLK; j++)
+                acc[b][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(st.a[b], wf[j], acc[b][j], 0, 0, 0);
+    };
+
+    // Rounds of S steps (wave + (i + S t) WAVES): all S steps' loads are
+    // issued, then each step is multiplied as its loads land.  Loads are
+    // unconditional (steps past the end re-read the last one and are not
+    // multiplied), so each step's wait is a fixed count and no load is
+    // carried across the loop's back edge.
+    for (int64_t base = wave; base < nsteps; base += (int64_t)S * WAVES) {
+        KnStage<NBLK, RB> st[S];
+        static_for<0, S>([&](auto I) {
+            const int64_t s0 = base + (int64_t)I * WAVES;
+            kn_load<NBLK, RB>(st[I], xrow, wblk, s0 < nsteps ? s0 : nsteps - 1, p.n);
+        });
+        static_for<0, S>([&](auto I) {
+            if (base + (int64_t)I * WAVES < nsteps) compute(st[I]);
+        });
+    }
+    gemv_reduce_store<WAVES, RB, NBLK>(p, ep, acc, red, rf, nb0, wave, lane);
+}
+
+template <int NBLK, int RB, int WAVES, int S, int EPI, int OUT>
+hipError_t launch_gemv_kn_t(const Params &p, int64_t batch, hipStream_t st) {
+    const int64_t groups = ((p.n + 15) / 16 + NBLK - 1) / NBLK;
+    if (groups > 0x7fffffff) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((gemv_kn_i8_kernel<NBLK, RB, WAVES, S, EPI, OUT>), dim3((unsigned)groups, 1, (unsigned)batch),
+                       dim3(WAVES * 64), 0, st, p, (int)groups);
+    return hipGetLastError();
+}
+
+// Four column blocks (64-byte row segments, x read once per 64 columns)
+// once that still makes 256 workgroups and n allows whole 16-byte loads;
+// one column block with eight waves below that.
+template <int RB, int EPI, int OUT>
+hipError_t launch_gemv_kn_n(const Params &p, int64_t batch, hipStream_t st) {
+    if (p.n % 16 == 0 && (p.n / 64) * batch >= 256) return launch_gemv_kn_t<4, RB, 4, 4, EPI, OUT>(p, batch, st);
+    return launch_gemv_kn_t<1, RB, 8, 4, EPI, OUT>(p, batch, st);
+}
+
+template <int EPI, int OUT>
+hipError_t launch_gemv_kn_rb(const Params &p, int64_t batch, hipStream_t st) {
+    switch ((p.m + 15) / 16) {
+        case 1: return launch_gemv_kn_n<1, EPI, OUT>(p, batch, st);
+        case 2: return launch_gemv_kn_n<2, EPI, OUT>(p, batch, st);
+        case 3: return launch_gemv_kn_n<3, EPI, OUT>(p, batch, st);
+        default: return launch_gemv_kn_n<4, EPI, OUT>(p, batch, st);
+    }
+}
+
+template <int EPI>
+hipError_t launch_gemv_kn_out(int out_kind, const Params &p, int64_t batch, hipStream_t st) {
+    switch (out_kind) {
+        case OUT_F16: return launch_gemv_kn_rb<EPI, OUT_F16>(p, batch, st);
+        case OUT_BF16: return launch_gemv_kn_rb<EPI, OUT_BF16>(p, batch, st);
+        default: return launch_gemv_kn_rb<EPI, OUT_I32>(p, batch, st);
+    }
+}
+
+// [k][n] products the decode kernel takes (whole 64-k steps, whole column
+// dwords).
+bool gemv_kn_fits(int64_t m, int64_t n, int64_t k) {
+    return m <= 64 && k % 64 == 0 && n % 4 == 0;
 }
 
 // Products the decode kernel takes: m <= 64, or m <= 128 when the columns
@@ -1145,6 +1345,11 @@ hipError_t launch_gemm_i8(const GemmI8Args &a, hipStream_t st) {
         if ((a.n + 15) / 16 > 0x7fffffff) return hipErrorInvalidValue;
         return a.epi == EPI_ROWCOL ? launch_gemv_out<EPI_ROWCOL>(a.out_kind, p, batch, st)
                                    : launch_gemv_out<EPI_SCALARS>(a.out_kind, p, batch, st);
+    }
+    if (!a.w_nk && gemv_kn_fits(a.m, a.n, a.k)) {
+        if ((a.n + 15) / 16 > 0x7fffffff) return hipErrorInvalidValue;
+        return a.epi == EPI_ROWCOL ? launch_gemv_kn_out<EPI_ROWCOL>(a.out_kind, p, batch, st)
+                                   : launch_gemv_kn_out<EPI_SCALARS>(a.out_kind, p, batch, st);
     }
     if (gemm_i8_uses_big_tiles(a.w_nk, a.m, a.n, a.k))
         return a.epi == EPI_ROWCOL ? launch_big_out<EPI_ROWCOL>(a.out_kind, p, batch, st)

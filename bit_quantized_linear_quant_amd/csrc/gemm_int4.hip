@@ -307,15 +307,6 @@ __device__ __forceinline__ void lds_load16_hidden(const void *src, const void *l
     asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(src), "s"(m) : "memory", "m0");
 }
 
-// Compile-time loop: f(std::integral_constant<int, I>) for I in [B, E).
-template <int B, int E, typename F>
-__device__ __forceinline__ void static_for(F &&f) {
-    if constexpr (B < E) {
-        f(std::integral_constant<int, B>{});
-        static_for<B + 1, E>(f);
-    }
-}
-
 // Direct-load form for waves with at most NKB k blocks (k <= 128 * WAVES *
 // NKB).  The two-stage pipeline above issues a k block's weight loads only
 // after the block two earlier has arrived, so the HBM latency is paid once

@@ -6,6 +6,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace ql {
 
 typedef int v4i __attribute__((ext_vector_type(4)));
@@ -264,5 +266,14 @@ __device__ __forceinline__ float q4_code(float q) {
 }
 
 __device__ __forceinline__ float code_i4_f(float v, float sp, float r) { return q4_code(q4_quotient(v, sp, r)); }
+
+// Compile-time loop: f(std::integral_constant<int, I>) for I in [B, E).
+template <int B, int E, typename F>
+__device__ __forceinline__ void static_for(F &&f) {
+    if constexpr (B < E) {
+        f(std::integral_constant<int, B>{});
+        static_for<B + 1, E>(f);
+    }
+}
 
 }  // namespace ql

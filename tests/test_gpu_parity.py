@@ -78,6 +78,13 @@ W8A8_SHAPES = [
     (96, 400, 512, True),      # six and eight row blocks (m <= 128, few columns)
     (128, 1000, 768, True),
     (100, 6400, 128, True),    # many columns: back to the 128x128 tiles
+    (1, 4, 64, False),         # [k][n] decode kernel from here on (m <= 64, k % 64 == 0, n % 4 == 0)
+    (5, 1004, 320, False),     # n % 16 != 0, k steps not a multiple of the waves, ragged XCD groups
+    (33, 3000, 768, False),    # three row blocks
+    (64, 2048, 4096, False),   # four row blocks, long k
+    (48, 260, 128, False),
+    (16, 128, 200, False),     # k % 64 != 0 and n % 4 != 0: general kernel
+    (9, 130, 256, False),
 ]
 
 
@@ -127,6 +134,21 @@ def test_w8a8_decode_max_k():
     assert_equal(o, acc, "w8a8 decode max-k accumulator")
 
 
+def test_w8a8_decode_kn_max_k():
+    """The [k][n] decode kernel at k = 131008, operands at -128 (and a few larger codes)."""
+    m, n, k = 3, 8, 131008
+    x = torch.full((m, k), -128, dtype=torch.int8)
+    w = torch.full((k, n), -128, dtype=torch.int8)
+    w[::2, 1] = 127
+    x[2, 1::3] = 5
+    acc = oracle.gemm_i8(x.numpy(), w.numpy(), False)
+    assert int(acc[0, 0]) == 128 * 128 * k
+    o = poison((m, n), torch.int32)
+    ql.qlinear_gemm_w8a8(_cuda(x), _cuda(w), ql.QL_W_KN, None, None, out_dtype=torch.int32, out=o)
+    _sync()
+    assert_equal(o, acc, "w8a8 [k][n] decode max-k accumulator")
+
+
 def test_w8a8_deterministic():
     d = synthetic.w8a8(200, 300, 512, True, seed=5)
     args = [_cuda(d[key]) for key in ("x", "w")]
@@ -146,6 +168,7 @@ def test_w8a8_deterministic():
     (2, 1, 1, 1, False, True),
     (3, 16, 270, 320, True, True),      # decode kernel
     (2, 40, 900, 192, True, False),     # decode kernel, three row blocks
+    (2, 40, 900, 192, False, True),     # [k][n] decode kernel, three row blocks
 ])
 def test_w8a8_batched_parity(batch, m, n, k, nk, per_batch_deq):
     ds = [synthetic.w8a8(m, n, k, nk, seed=1900 + 10 * b + m + n + k) for b in range(batch)]
@@ -533,7 +556,8 @@ def _bias_tol(y, b):
 
 @pytest.mark.parametrize("m,n,k,nk", [(300, 270, 200, True), (77, 45, 77, True), (129, 257, 1000, False),
                                       (520, 777, 192, True), (1024, 768, 1024, True), (1, 1, 1, False),
-                                      (5, 300, 256, True), (40, 300, 256, True)])
+                                      (5, 300, 256, True), (40, 300, 256, True), (16, 128, 256, False),
+                                      (40, 300, 256, False)])
 def test_w8a8_bias_parity(m, n, k, nk):
     d = synthetic.w8a8(m, n, k, nk, seed=1200 + m + n + k)
     x, w, deq, pts = (d[key] for key in ("x", "w", "deq", "pts"))
