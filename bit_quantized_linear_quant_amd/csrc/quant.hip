@@ -171,7 +171,7 @@ __global__ __launch_bounds__(kQThreads) void quant_act_kernel(const void *__rest
 // reductions, with no LDS and no barrier.
 constexpr int kQWaveRows = 4;  // rows (waves) per workgroup
 
-template <int K, int NCH, bool RMS>
+template <int K, int NCH, bool RMS, bool FULL>
 __global__ __launch_bounds__(kQWaveRows * kWave) void quant_act_wave_kernel(const void *__restrict__ x,
                                                                             int64_t m, int64_t k,
                                                                             float eps_norm, float eps_q,
@@ -195,7 +195,7 @@ __global__ __launch_bounds__(kQWaveRows * kWave) void quant_act_wave_kernel(cons
     float amax = 0.0f, ss = 0.0f;
 #pragma unroll
     for (int c = 0; c < NCH; c++) {
-        const bool in = (int64_t)c * kWave + lane < nchunk;
+        const bool in = FULL || (int64_t)c * kWave + lane < nchunk;
 #pragma unroll
         for (int j = 0; j < 8; j++) {
             const float e = in ? v[c][j] : 0.0f;
@@ -213,12 +213,10 @@ __global__ __launch_bounds__(kQWaveRows * kWave) void quant_act_wave_kernel(cons
     // The code of v is clamp(rint(fl(v * s)), -128, 127).  Clamping first
     // (the bounds are integers) and adding 1.5 * 2^23 rounds the value to an
     // integer, ties to even, in the low mantissa bits: the word is
-    // 0x4B400000 + code, whose low byte is the code's byte.  Sums of these
-    // words wrap mod 2^32; subtracting the count times 0x4B400000 leaves the
-    // exact code sum.
+    // 0x4B400000 + code, whose low byte is the code's byte.  The code sum is
+    // a 4-way signed byte dot product of the packed codes with ones.
     constexpr float kRound = 12582912.0f;
-    constexpr uint32_t kRoundBits = 0x4B400000u;
-    uint32_t rsw = 0;
+    int rs = 0;
 #pragma unroll
     for (int c = 0; c < NCH; c++) {
         const int64_t ch = (int64_t)c * kWave + lane;
@@ -227,20 +225,20 @@ __global__ __launch_bounds__(kQWaveRows * kWave) void quant_act_wave_kernel(cons
         for (int j = 0; j < 8; j++) {
             const float t = fminf(fmaxf(__fmul_rn(v[c][j], s), -128.0f), 127.0f);
             y[j] = __float_as_uint(__fadd_rn(t, kRound));
-            rsw += y[j];
         }
         // bytes 0 of y[0..3] and y[4..7]
         const uint32_t lo = __builtin_amdgcn_perm(__builtin_amdgcn_perm(y[3], y[2], 0x0c0c0400u),
                                                   __builtin_amdgcn_perm(y[1], y[0], 0x0c0c0400u), 0x05040100u);
         const uint32_t hi = __builtin_amdgcn_perm(__builtin_amdgcn_perm(y[7], y[6], 0x0c0c0400u),
                                                   __builtin_amdgcn_perm(y[5], y[4], 0x0c0c0400u), 0x05040100u);
-        if (ch < nchunk) *reinterpret_cast<uint2 *>(qr + ch * 8) = make_uint2(lo, hi);
+        rs = __builtin_amdgcn_sdot4((int)lo, 0x01010101, rs, false);
+        rs = __builtin_amdgcn_sdot4((int)hi, 0x01010101, rs, false);
+        if (FULL || ch < nchunk) *reinterpret_cast<uint2 *>(qr + ch * 8) = make_uint2(lo, hi);
     }
-    rsw = wave_sum(rsw);
+    rs = wave_sum(rs);
     if (lane == 0) {
         pts[row] = RMS ? __fdiv_rn(__fmul_rn(ap, r), 127.0f) : __fdiv_rn(ap, 127.0f);
-        // NCH * 64 * 8 words were summed (masked chunks as code 0)
-        if (rowsum) rowsum[row] = (int32_t)(rsw - (uint32_t)(NCH * kWave * 8) * kRoundBits);
+        if (rowsum) rowsum[row] = rs;
     }
 }
 
@@ -248,12 +246,14 @@ template <int K, int NCH>
 hipError_t launch_wave_rows(bool rms, const void *x, int64_t m, int64_t k, float eps_norm, float eps_q,
                             int8_t *q, float *pts, int32_t *rowsum, hipStream_t st) {
     const unsigned grid = (unsigned)((m + kQWaveRows - 1) / kQWaveRows);
-    if (rms)
-        hipLaunchKernelGGL((quant_act_wave_kernel<K, NCH, true>), dim3(grid), dim3(kQWaveRows * kWave), 0, st, x,
-                           m, k, eps_norm, eps_q, q, pts, rowsum);
-    else
-        hipLaunchKernelGGL((quant_act_wave_kernel<K, NCH, false>), dim3(grid), dim3(kQWaveRows * kWave), 0, st,
-                           x, m, k, eps_norm, eps_q, q, pts, rowsum);
+    // rows of exactly 64 NCH chunks need no per-lane masking
+    const bool full = k == (int64_t)NCH * kWave * 8;
+    auto go = [&](auto kern) {
+        hipLaunchKernelGGL(kern, dim3(grid), dim3(kQWaveRows * kWave), 0, st, x, m, k, eps_norm, eps_q, q, pts,
+                           rowsum);
+    };
+    if (rms) full ? go(quant_act_wave_kernel<K, NCH, true, true>) : go(quant_act_wave_kernel<K, NCH, true, false>);
+    else full ? go(quant_act_wave_kernel<K, NCH, false, true>) : go(quant_act_wave_kernel<K, NCH, false, false>);
     return hipGetLastError();
 }
 
