@@ -12,10 +12,10 @@
 // core sums matching terms.  The accumulator holds sum x*(code+1); the
 // epilogue subtracts the token's code sum: acc = sum x*code exactly.
 //
-// m >= 256: 256 x 128 tiles on v_mfma_i32_32x32x32_i8, activation codes
-//         and packed weights streamed into LDS through a ring of 128-k
-//         slices; each lane takes its weight words from LDS in the order the
-//         32x32x32 operand needs.
+// m >= 256: 256 x 128 tiles on v_mfma_i32_32x32x32_i8, eight waves in two
+//         phase-alternating groups; activation codes and packed weights
+//         streamed into LDS through a ring of 128-k slices; each lane takes
+//         its weight words from LDS in the order the 32x32x32 operand needs.
 // 64 < m < 256: 128 x 128 tiles, 2 x 2 waves of 64 x 64 on 32x32x32, A
 //         staged in LDS per 256-k step (rows padded to 272 bytes), B loaded
 //         per wave straight into registers in the lane order that operand
@@ -199,16 +199,17 @@ __global__ __launch_bounds__(kGThreads) void w2a8_gemm_kernel(const int8_t *__re
 // ---------------------------------------------------------------------------
 // m >= 256: large-tile GEMM
 // ---------------------------------------------------------------------------
-// A 256-thread workgroup owns a 256 x 128 output tile; wave (wm, wn) owns
-// 128 x 64 as 4 x 2 blocks of v_mfma_i32_32x32x32_i8 (the 16x16x64 form
-// sustains about 60% of the 32x32x32 rate on gfx950).  The k loop runs over
-// 128-k slices through a ring of four LDS stages: three slices stream in while
-// the matrix cores consume the fourth, with one vmcnt wait and one barrier
-// per slice.  Slice sl = 2 kb + hh holds half hh of k block kb:
+// A 512-thread workgroup owns a 256 x 128 output tile: eight waves, two per
+// SIMD (waves w and w + 4 share SIMD w % 4), each owning a 64 x 64 quarter
+// as 2 x 2 blocks of v_mfma_i32_32x32x32_i8 (the 16x16x64 form sustains
+// about 60% of the 32x32x32 rate on gfx950).  The k loop runs over 128-k
+// slices through a ring of four LDS stages.  Slice sl = 2 kb + hh holds
+// half hh of k block kb:
 //   * the activation codes of k 128 sl .. +127 (256 rows x 128 bytes, 32 KB)
 //     go HBM -> LDS with global_load_lds_dwordx4; 16-byte chunk c of row r
-//     sits at chunk position c ^ (r & 7), so the 8 rows read together by a
-//     fragment load fall in distinct bank groups;
+//     sits at chunk position c ^ ((r >> 1) & 7), so each 16 lanes of a
+//     fragment read (16 rows, two per bank group parity) fall in distinct
+//     bank groups;
 //   * packed lanes 32 hh .. 32 hh + 31 of each of the tile's eight fragment
 //     blocks (the k groups 2 hh and 2 hh + 1, 512 contiguous bytes each).
 // Step t (0..3) of a slice gives lane half h = lane / 32 the k group
@@ -216,133 +217,138 @@ __global__ __launch_bounds__(kGThreads) void w2a8_gemm_kernel(const int8_t *__re
 // chunk 4 h + t of its slice row (k = 256 kb + 64 g + 16 t); for B, word t of
 // packed lane (column % 16) + 16 g, unpacked in registers.  Both operands
 // take the same 16 k, so the matrix core sums matching terms.
+//
+// The groups of waves 0-3 and 4-7 run opposite phases of every slice: one
+// reads its fragments of the slice from LDS and issues its share of the
+// direct loads three slices ahead while the other unpacks its weight words
+// and issues its 16 matrix-core products, so the matrix cores of a SIMD
+// see a ready wave at every phase.  Two workgroup barriers per slice keep
+// the phases apart; the second group passes one extra barrier at the start
+// and the first group one at the end.  Before every barrier a wave waits
+// until at most two slices of its own loads are in flight: a slice has
+// landed (every wave's loads) at the barrier before its first read, and
+// the ring is never overwritten while a partner still reads it.
 constexpr int XBM = 256, XBN = 128, XBK = 128;
-constexpr int kXThreads = 256;
 constexpr int kXGroupM = 4;
 constexpr int kXBuf = 4;                               // ring stages
 constexpr int kXASlice = XBM * XBK;                    // bytes of activation codes per slice
 constexpr int kXBSlice = XBN / 16 * 512;               // bytes of packed weights per slice
 constexpr int kXStage = kXASlice + kXBSlice;
-constexpr int kXLoads = kXASlice / 1024 / (kXThreads / kWave);  // 1 KB A loads per wave per slice
-static_assert(kXBSlice == 1024 * (kXThreads / kWave), "one 1 KB weight load per wave per slice");
-
+constexpr int kPThreads = 512;
+constexpr int kPLoads = kXASlice / 1024 / (kPThreads / kWave);   // 1 KB A loads per wave per slice (4)
+static_assert(kXBSlice == 1024 * 4, "one 1 KB weight load for each of waves 0-3 per slice");
 
 // Bytes of LDS the epilogue of a 256 x 128 tile uses: the rows' code sums
-// and scales, then a padded 128 x 64 output tile per wave.
+// and scales, then a padded 64 x 64 output tile per wave.
 template <int OUT>
 constexpr int xepi_bytes() {
-    return 2 * XBM * 4 + 4 * 128 * (64 * (OUT == OUT_I32 || OUT == OUT_F32 ? 4 : 2) + 16);
-}
-
-// One slice: the direct loads of slice nxt_sl into `nxt`, then the four
-// MFMA steps on `cur`.  `cur` and `nxt` are distinct restrict pointers, so
-// the compiler does not make the fragment reads of `cur` wait for the loads
-// into `nxt`.
-__device__ __forceinline__ void w2a8_big_slice(v16i (&acc)[4][2], const int8_t *__restrict__ cur,
-                                               int8_t *__restrict__ nxt, const int8_t *const (&srca)[kXLoads],
-                                               const int8_t *srcb, int64_t nxt_sl, int aoff, int boff, int wave) {
-#pragma unroll
-    for (int ii = 0; ii < kXLoads; ii++) lds_load16(srca[ii] + nxt_sl * XBK, nxt + 1024 * (kXLoads * wave + ii));
-    lds_load16(srcb + nxt_sl * 512, nxt + kXASlice + 1024 * wave);
-    uint4 bw[2];
-#pragma unroll
-    for (int j = 0; j < 2; j++) bw[j] = *reinterpret_cast<const uint4 *>(cur + boff + 1024 * j);
-    v4i fa[2][4];
-#pragma unroll
-    for (int t = 0; t < 4; t++) {
-        // chunk 4h + t is at position (4h + t) ^ (row & 7) = (4h ^ (row & 7)) ^ t
-#pragma unroll
-        for (int i = 0; i < 4; i++) fa[t & 1][i] = *reinterpret_cast<const v4i *>(cur + (aoff ^ (16 * t)) + i * 32 * XBK);
-#pragma unroll
-        for (int j = 0; j < 2; j++) {
-            const v4i b = unpack_tern(word_of(bw[j], t));
-#pragma unroll
-            for (int i = 0; i < 4; i++)
-                acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fa[t & 1][i], b, acc[i][j], 0, 0, 0);
-        }
-    }
+    return 2 * XBM * 4 + 8 * 64 * (64 * (OUT == OUT_I32 || OUT == OUT_F32 ? 4 : 2) + 16);
 }
 
 template <int OUT>
-__global__ __launch_bounds__(kXThreads, 1) void w2a8_big_kernel(const int8_t *__restrict__ xq,
-                                                                const float *__restrict__ pts,
-                                                                const int32_t *__restrict__ rowsum,
-                                                                const uint32_t *__restrict__ packed,
-                                                                const double *__restrict__ gamma,
-                                                                const float *__restrict__ bias,
-                                                                int64_t m, int64_t n, int64_t k,
-                                                                void *__restrict__ out, int tiles_m,
-                                                                int tiles_n) {
+__global__ __launch_bounds__(kPThreads, 1) void w2a8_big_kernel(const int8_t *__restrict__ xq,
+                                                               const float *__restrict__ pts,
+                                                               const int32_t *__restrict__ rowsum,
+                                                               const uint32_t *__restrict__ packed,
+                                                               const double *__restrict__ gamma,
+                                                               const float *__restrict__ bias,
+                                                               int64_t m, int64_t n, int64_t k,
+                                                               void *__restrict__ out, int tiles_m,
+                                                               int tiles_n) {
     constexpr int SMEM = kXBuf * kXStage > xepi_bytes<OUT>() ? kXBuf * kXStage : xepi_bytes<OUT>();
     __shared__ __attribute__((aligned(1024))) int8_t smem[SMEM];
     const int lane = threadIdx.x % kWave, wave = wave_id();
-    const int wm = wave / 2, wn = wave % 2;
+    const int group = wave / 4;
+    const int wm = wave % 4, wn = wave / 4;   // 4 x 2 quarters of 64 x 64
     int tm, tn;
     xcd_tile(blockIdx.x, tiles_m, tiles_n, kXGroupM, tm, tn);
     const int64_t m0 = (int64_t)tm * XBM, n0 = (int64_t)tn * XBN;
     const int64_t nsl = k / XBK, nblocks = n / 16;
 
-    // A load ii of this wave fills LDS bytes [1024 (8 wave + ii), +1024) of
-    // the slice: row 8 (8 wave + ii) + lane / 8, chunk position lane % 8.
-    // Sources are given for slice 0; slice sl adds 128 sl bytes.
-    const int8_t *srca[kXLoads];
+    // A load ii of this wave fills LDS bytes [1024 (4 wave + ii), +1024) of
+    // the slice: row 8 (4 wave + ii) + lane / 8, chunk position lane % 8.
+    const int8_t *srca[kPLoads];
 #pragma unroll
-    for (int ii = 0; ii < kXLoads; ii++) {
-        const int row = 8 * (kXLoads * wave + ii) + lane / 8;
-        const int c = (lane % 8) ^ (row & 7);
+    for (int ii = 0; ii < kPLoads; ii++) {
+        const int row = 8 * (kPLoads * wave + ii) + lane / 8;
+        const int c = (lane % 8) ^ ((row >> 1) & 7);
         const int64_t r = m0 + row < m ? m0 + row : m - 1;
         srca[ii] = xq + r * k + 16 * c;
     }
-    // The weight load of this wave: 32 lanes each in fragment blocks 2 wave
-    // and 2 wave + 1 of the tile.  The half hh of k block kb (1 KB per block)
-    // starts at byte 1024 kb + 512 hh = 512 sl.
+    // Waves 0-3 load the weights: 32 lanes each in fragment blocks 2 wave
+    // and 2 wave + 1 of the tile (half hh of k block kb at byte 512 sl).
     const int8_t *srcb;
     {
-        const int blk = 2 * wave + lane / 32;
+        const int blk = 2 * (wave % 4) + lane / 32;
         const int64_t nb = n0 / 16 + blk < nblocks ? n0 / 16 + blk : nblocks - 1;
         srcb = reinterpret_cast<const int8_t *>(packed) + nb * (k / 256) * 1024 + 16 * (lane % 32);
     }
-    // Fragment offsets: A row 128 wm + 32 i + lane % 32 (block i adds 32
-    // rows); B column block j of the wave is fragment block 4 wn + 2 j +
-    // (lane % 32) / 16, stored lane (lane % 16) + 16 h.
     const int h = lane / 32, fr = lane % 32;
-    const int aoff = (128 * wm + fr) * XBK + 16 * ((4 * h) ^ (fr & 7));
+    const int aoff = (64 * wm + fr) * XBK + 16 * ((4 * h) ^ ((fr >> 1) & 7));
     const int boff = kXASlice + 512 * (4 * wn + fr / 16) + 16 * (fr % 16 + 16 * h);
 
-    v16i acc[4][2];
+    auto issue = [&](int64_t sl, int stage) __attribute__((always_inline)) {
+        const int64_t s = sl < nsl ? sl : nsl - 1;
+        int8_t *dst = smem + stage * kXStage;
 #pragma unroll
-    for (int i = 0; i < 4; i++)
+        for (int ii = 0; ii < kPLoads; ii++) lds_load16(srca[ii] + s * XBK, dst + 1024 * (kPLoads * wave + ii));
+        if (group == 0) lds_load16(srcb + s * 512, dst + kXASlice + 1024 * wave);
+    };
+    // at most two slices of this wave's loads in flight
+    auto wait_two = [&]() __attribute__((always_inline)) {
+        if (group == 0) wait_vmcnt<2 * (kPLoads + 1)>();
+        else wait_vmcnt<2 * kPLoads>();
+    };
+
+    v16i acc[2][2];
+#pragma unroll
+    for (int i = 0; i < 2; i++)
 #pragma unroll
         for (int j = 0; j < 2; j++) acc[i][j] = v16i{};
 
-    // Slices 0 .. kXBuf-2 in flight before the loop; iteration sl consumes
-    // slice sl and starts slice sl + kXBuf - 1 (clamped: the last iterations
-    // reload the final slice, keeping the loop body free of branches) into
-    // the stage that iteration sl - 1 consumed.
-#pragma unroll
-    for (int b = 0; b < kXBuf - 1; b++) {
-        const int64_t sl = b < nsl ? b : nsl - 1;
-#pragma unroll
-        for (int ii = 0; ii < kXLoads; ii++)
-            lds_load16(srca[ii] + sl * XBK, smem + b * kXStage + 1024 * (kXLoads * wave + ii));
-        lds_load16(srcb + sl * 512, smem + b * kXStage + kXASlice + 1024 * wave);
+    issue(0, 0);
+    issue(1, 1);
+    issue(2, 2);
+    if (group == 1) {
+        wait_two();
+        barrier_only();
     }
     for (int64_t sl = 0; sl < nsl; sl++) {
-        // this wave's loads of slice sl are done; after the barrier every
-        // wave's are, and every wave has finished reading the stage refilled
-        wait_vmcnt<(kXBuf - 2) * (kXLoads + 1)>();
+        // fragment phase: this slice to registers, slice sl + 3 requested
+        wait_two();
         barrier_only();
-        const int cur = (int)(sl % kXBuf), nxt = (int)((sl + kXBuf - 1) % kXBuf);
-        const int64_t nxt_sl = sl + kXBuf - 1 < nsl ? sl + kXBuf - 1 : nsl - 1;
-        w2a8_big_slice(acc, smem + cur * kXStage, smem + nxt * kXStage, srca, srcb, nxt_sl, aoff, boff, wave);
+        const int8_t *cur = smem + (int)(sl % kXBuf) * kXStage;
+        v4i fa[4][2];
+        uint4 bw[2];
+#pragma unroll
+        for (int j = 0; j < 2; j++) bw[j] = *reinterpret_cast<const uint4 *>(cur + boff + 1024 * j);
+#pragma unroll
+        for (int t = 0; t < 4; t++)
+#pragma unroll
+            for (int i = 0; i < 2; i++) fa[t][i] = *reinterpret_cast<const v4i *>(cur + (aoff ^ (16 * t)) + i * 32 * XBK);
+        issue(sl + 3, (int)((sl + 3) % kXBuf));
+        __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0): the fragments are in registers
+        wait_two();
+        barrier_only();
+        // product phase
+#pragma unroll
+        for (int t = 0; t < 4; t++)
+#pragma unroll
+            for (int j = 0; j < 2; j++) {
+                const v4i b = unpack_tern(word_of(bw[j], t));
+#pragma unroll
+                for (int i = 0; i < 2; i++)
+                    acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fa[t][i], b, acc[i][j], 0, 0, 0);
+            }
     }
+    if (group == 0) barrier_only();
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
 
-    // Epilogue through LDS: each wave converts its 128 x 64 sub-tile into an
+    // Epilogue through LDS: each wave converts its 64 x 64 sub-tile into an
     // LDS tile (rows padded by 16 bytes, so the four row groups of one write
-    // fall in distinct banks), then writes whole 128- or 256-byte row segments
-    // to global memory, 16 bytes per lane.
+    // fall in distinct banks), then writes whole 128- or 256-byte row
+    // segments to global memory, 16 bytes per lane.
     int32_t *rs_lds = reinterpret_cast<int32_t *>(smem);
     float *pts_lds = reinterpret_cast<float *>(smem) + XBM;
     stage_rows<OUT>(pts, rowsum, m, m0, XBM, rs_lds, pts_lds);
@@ -350,7 +356,7 @@ __global__ __launch_bounds__(kXThreads, 1) void w2a8_big_kernel(const int8_t *__
     constexpr int ES = OUT == OUT_I32 || OUT == OUT_F32 ? 4 : 2;   // output element bytes
     constexpr int ROWB = 64 * ES;                                  // bytes of a sub-tile row
     constexpr int PITCH = ROWB + 16;
-    int8_t *tile = smem + 2 * XBM * 4 + wave * 128 * PITCH;
+    int8_t *tile = smem + 2 * XBM * 4 + wave * 64 * PITCH;
     const float g = OUT == OUT_I32 ? 0.0f : (float)gamma[0];  // gamma may be NULL for int32 output
     float cbj[2];
 #pragma unroll
@@ -361,11 +367,11 @@ __global__ __launch_bounds__(kXThreads, 1) void w2a8_big_kernel(const int8_t *__
     // Lane l holds column l % 32 of each 32 x 32 block and rows
     // 8 (r / 4) + 4 (l / 32) + r % 4 of register r.
 #pragma unroll
-    for (int i = 0; i < 4; i++)
+    for (int i = 0; i < 2; i++)
 #pragma unroll
         for (int r = 0; r < 16; r++) {
             const int lr = 32 * i + 8 * (r / 4) + 4 * h + r % 4;      // row within the sub-tile
-            const int local = 128 * wm + lr;
+            const int local = 64 * wm + lr;
             const float rf = OUT == OUT_I32 ? 0.0f : pts_lds[local];
             const int32_t rsv = rs_lds[local];
 #pragma unroll
@@ -387,10 +393,10 @@ __global__ __launch_bounds__(kXThreads, 1) void w2a8_big_kernel(const int8_t *__
     constexpr int ROWS_PER = 64 / SEG;             // sub-tile rows per wave store
     const int64_t col0 = n0 + 64 * wn;
 #pragma unroll
-    for (int q = 0; q < 128 / ROWS_PER; q++) {
+    for (int q = 0; q < 64 / ROWS_PER; q++) {
         const int lr = q * ROWS_PER + lane / SEG, piece = lane % SEG;
         const uint4 v = *reinterpret_cast<const uint4 *>(tile + lr * PITCH + 16 * piece);
-        const int64_t row = m0 + 128 * wm + lr;
+        const int64_t row = m0 + 64 * wm + lr;
         const int64_t col = col0 + piece * (16 / ES);
         if (row < m && col < n) *reinterpret_cast<uint4 *>(static_cast<int8_t *>(out) + (row * n + col) * ES) = v;
     }
@@ -671,7 +677,7 @@ hipError_t launch_out(const int8_t *xq, const float *pts, const int32_t *rowsum,
     }
     if (m >= XBM) {
         const int tiles_m = (int)((m + XBM - 1) / XBM), tiles_n = (int)((n + XBN - 1) / XBN);
-        hipLaunchKernelGGL((w2a8_big_kernel<OUT>), dim3((unsigned)(tiles_m * tiles_n)), dim3(kXThreads), 0, st, xq,
+        hipLaunchKernelGGL((w2a8_big_kernel<OUT>), dim3((unsigned)(tiles_m * tiles_n)), dim3(kPThreads), 0, st, xq,
                            pts, rowsum, packed, gamma, bias, m, n, k, out, tiles_m, tiles_n);
         return hipGetLastError();
     }
