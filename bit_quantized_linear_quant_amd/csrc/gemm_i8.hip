@@ -5,13 +5,14 @@
 // Three kernels share the epilogue:
 //
 // gemm_i8_big_kernel -- large products with [n][k] weights and k % 64 == 0
-//   (the 8192^3 A4W4 product).  A 256-thread workgroup owns a 256 x 256
-//   output tile, each wave a 128 x 128 quarter held as 4 x 4 blocks of
-//   v_mfma_i32_32x32x32_i8 (256 int32 accumulators per lane, one wave per
-//   SIMD).  64-byte k-slices of A and B move from HBM straight into LDS with
-//   global_load_lds_dwordx4 (no register staging) through a ring of three
-//   slices, so two slices stream in while the matrix cores consume the
-//   third; one explicit vmcnt wait and one barrier per slice.  In LDS each
+//   (the 8192^3 A4W4 product).  A 512-thread workgroup owns a 256 x 256
+//   output tile, each of its eight waves (two per SIMD) a 128 x 64 part
+//   held as 4 x 2 blocks of v_mfma_i32_32x32x32_i8; the two groups of four
+//   waves run opposite phases of every slice (fragment reads and loads
+//   against products).  64-byte k-slices of A and B move from HBM straight
+//   into LDS with global_load_lds_dwordx4 (no register staging) through a
+//   ring of three slices, so two slices stream in while the matrix cores
+//   consume the third; explicit vmcnt waits and two barriers per slice.  In LDS each
 //   16-byte chunk c of row r sits at chunk position c ^ swz(r), which puts
 //   the 16 rows read together by a fragment load in distinct bank groups.
 //   Tiles are ordered so that each XCD (workgroup id mod 8) walks its own
@@ -206,22 +207,22 @@ __device__ __forceinline__ void big_epilogue(const Params &p, const ACC (&acc)[4
 }
 
 template <int BK, int NBUF, int EPI, int OUT>
-__global__ __launch_bounds__(LThreads, 1) void gemm_i8_big_kernel(Params p, int tiles_m, int tiles_n) {
+__global__ __launch_bounds__(2 * LThreads, 1) void gemm_i8_big_kernel(Params p, int tiles_m, int tiles_n) {
     constexpr int STAGE = 2 * BigTile<BK>::TILE;
     // main loop: a ring of NBUF (A, B) slices; epilogue: 1 KB of row factors,
-    // then one padded 128 x 128 output sub-tile per wave (2-byte outputs)
-    constexpr int EPI_BYTES = 1024 + 4 * 128 * big_epitch(4);
+    // then one padded 128 x 64 output sub-tile per wave (2-byte outputs)
+    constexpr int EPI_BYTES = 1024 + 8 * 128 * big_epitch(2);
     constexpr int SMEM = NBUF * STAGE > EPI_BYTES ? NBUF * STAGE : EPI_BYTES;
     __shared__ __attribute__((aligned(1024))) int8_t smem[SMEM];
 
     to_batch(p);
     const int lane = threadIdx.x % kWave, wave = wave_id();
-    const int wm = wave / 2, wn = wave % 2;
+    const int wm = wave % 2, wn = (wave / 2) % 4;
     int tm, tn;
     xcd_tile(blockIdx.x, tiles_m, tiles_n, kGroupM, tm, tn);
     const int64_t m0 = (int64_t)tm * LB, n0 = (int64_t)tn * LB;
-    v16i acc[4][4];
-    ring_gemm<BK, NBUF, MK_I8>(acc, smem, p.x, p.w, p.m, p.n, p.k, m0, n0, wm, wn, lane, wave);
+    v16i acc[4][2];
+    ring_gemm_pp<BK, NBUF, MK_I8>(acc, smem, p.x, p.w, p.m, p.n, p.k, m0, n0, wm, wn, lane, wave);
     big_epilogue<EPI, OUT>(p, acc, smem, m0, n0, wm, wn, wave, lane);
 }
 
@@ -1277,8 +1278,8 @@ template <int EPI, int OUT>
 hipError_t launch_big(const Params &p, int64_t batch, hipStream_t st) {
     const int tiles_m = (int)((p.m + LB - 1) / LB), tiles_n = (int)((p.n + LB - 1) / LB);
     hipLaunchKernelGGL((gemm_i8_big_kernel<kBigBK, kBigBuf, EPI, OUT>),
-                       dim3((unsigned)(tiles_m * tiles_n), 1, (unsigned)batch), dim3(LThreads), 0, st, p, tiles_m,
-                       tiles_n);
+                       dim3((unsigned)(tiles_m * tiles_n), 1, (unsigned)batch), dim3(2 * LThreads), 0, st, p,
+                       tiles_m, tiles_n);
     return hipGetLastError();
 }
 

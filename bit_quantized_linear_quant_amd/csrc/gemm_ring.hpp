@@ -3,10 +3,10 @@
 // backward (q4_backward.hip).
 //
 // Operands are row-major with k contiguous, K bytes per row (K % BK == 0);
-// A has rows_a rows, B rows_b, and out = A B^T.  A 256-thread workgroup owns
-// a 256 x 256 output tile, each wave a 128 x 128 quarter (wm, wn) held as
-// 4 x 4 blocks of a 32 x 32 matrix-core product: 256 accumulators per lane,
-// one wave per SIMD.  Every 32-byte k step gives lane l the 16 bytes
+// A has rows_a rows, B rows_b, and out = A B^T.  A 512-thread workgroup owns
+// a 256 x 256 output tile, each of its eight waves a 128 x 64 part (wm, wn)
+// held as 4 x 2 blocks of a 32 x 32 matrix-core product: 128 accumulators
+// per lane, two waves per SIMD.  Every 32-byte k step gives lane l the 16 bytes
 // 16(l/32) .. +15 of row l%32 of a block, for the int8 32x32x32 product and
 // for the fp16 / bf16 32x32x16 products alike (16 bytes are 16 int8 or 8
 // 16-bit values; A and B take the same k positions, so the products are the
@@ -15,7 +15,7 @@
 // BK-byte k-slices of A and B move from HBM straight into LDS with
 // global_load_lds_dwordx4 (no register staging) through a ring of NBUF
 // slices, so NBUF - 1 slices stream in while the matrix cores consume one;
-// one explicit vmcnt wait and one barrier per slice.  In LDS each 16-byte
+// explicit vmcnt waits and two barriers per slice.  In LDS each 16-byte
 // chunk c of row r sits at chunk position c ^ swz(r), which puts the 16 rows
 // read together by a fragment load in distinct bank groups.  Rows past
 // rows_a or rows_b are loaded clamped; their outputs are never stored.
@@ -45,7 +45,6 @@ template <int BK>
 struct BigTile {
     static constexpr int CH = BK / 16;                // 16-byte chunks per LDS row
     static constexpr int TILE = LB * BK;              // bytes of one A or B slice
-    static constexpr int PER_WAVE = TILE / 1024 / 4;  // 1 KB direct loads per wave per slice and operand
     static constexpr int S = BK / 32;                 // 32-byte MFMA steps per slice
 };
 
@@ -63,123 +62,101 @@ __device__ __forceinline__ v16f mfma32(v4i a, v4i b, v16f c) {
                                                        0, 0, 0);
 }
 
-// One k-slice: the direct loads of a later slice into `nxt`, then the MFMAs of
-// `cur`, each step's fragments read from LDS while the previous step's
-// MFMAs issue.  `cur` and `nxt` are distinct restrict pointers, so the
-// compiler does not make the LDS reads of `cur` wait for the loads into `nxt`.
-template <int BK, int MK, typename ACC>
-__device__ __forceinline__ void big_slice(ACC (&acc)[4][4], const int8_t *__restrict__ cur,
-                                          int8_t *__restrict__ nxt, const int8_t *const (&srcA)[BigTile<BK>::PER_WAVE],
-                                          const int8_t *const (&srcB)[BigTile<BK>::PER_WAVE], int64_t nxt_k0,
-                                          const int (&offA)[BigTile<BK>::S], const int (&offB)[BigTile<BK>::S],
-                                          int wave) {
-    constexpr int CH = BigTile<BK>::CH, TILE = BigTile<BK>::TILE, PER_WAVE = BigTile<BK>::PER_WAVE;
-    constexpr int S = BigTile<BK>::S;
-#pragma unroll
-    for (int ii = 0; ii < PER_WAVE; ii++) {
-        const int inst = wave * PER_WAVE + ii;
-        lds_load16(srcA[ii] + nxt_k0, nxt + 1024 * inst);
-        lds_load16(srcB[ii] + nxt_k0, nxt + TILE + 1024 * inst);
-    }
-    v4i fa[2][4], fb[2][4];
-    auto frags = [&](int s) {
-#pragma unroll
-        for (int i = 0; i < 4; i++) fa[s & 1][i] = *reinterpret_cast<const v4i *>(cur + offA[s] + i * 32 * CH * 16);
-#pragma unroll
-        for (int j = 0; j < 4; j++) fb[s & 1][j] = *reinterpret_cast<const v4i *>(cur + TILE + offB[s] + j * 32 * CH * 16);
-    };
-    frags(0);
-#pragma unroll
-    for (int s = 0; s < S; s++) {
-        if (s + 1 < S) frags(s + 1);
-#pragma unroll
-        for (int i = 0; i < 4; i++)
-#pragma unroll
-            for (int j = 0; j < 4; j++) {
-                if constexpr (MK == MK_I8) acc[i][j] = mfma32(fa[s & 1][i], fb[s & 1][j], acc[i][j]);
-                else acc[i][j] = mfma32<MK>(fa[s & 1][i], fb[s & 1][j], acc[i][j]);
-            }
-        // matrix-core issue interleaved with the next step's LDS reads
-        if (s + 1 < S) {
-#pragma unroll
-            for (int q = 0; q < 8; q++) {
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-            }
-            __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
-        }
-    }
-}
-
-// The whole k loop of one 256 x 256 tile at (m0, n0): zeroes `acc`, runs the
-// ring over K bytes and leaves every load drained and every wave past a
-// barrier, so `smem` may be reused by the epilogue.  `smem` holds NBUF
-// stages of 2 * BigTile<BK>::TILE bytes.
+// The k loop of one 256 x 256 tile at (m0, n0) for a 512-thread workgroup:
+// zeroes `acc` and runs the ring over K bytes (`smem` holds NBUF stages of
+// 2 * BigTile<BK>::TILE bytes).  Eight waves, two per SIMD
+// (waves w and w + 4 share SIMD w % 4), each a 128 x 64 sub-tile (wm in
+// 0..1 selects 128 rows, wn in 0..3 64 columns) held as 4 x 2 blocks.  The
+// groups of waves 0-3 and 4-7 run opposite phases of every slice: one reads
+// its fragments of the slice from LDS and issues its direct loads NBUF - 1
+// slices ahead while the other issues its products, so each SIMD's matrix
+// core has a ready wave in both phases.  Two barriers per slice separate
+// the phases; the second group passes one extra barrier before the loop
+// and the first group one after it.  Before every barrier a wave waits
+// until at most NBUF - 2 slices of its own loads are in flight, so a slice
+// has landed (every wave's loads) at the barrier before its first read and
+// no stage is refilled while a partner still reads it.  Leaves every load
+// drained and every wave past a barrier, so `smem` may be reused by the
+// epilogue.
 template <int BK, int NBUF, int MK, typename ACC>
-__device__ __forceinline__ void ring_gemm(ACC (&acc)[4][4], int8_t *smem, const int8_t *A, const int8_t *B,
-                                          int64_t rows_a, int64_t rows_b, int64_t K, int64_t m0, int64_t n0, int wm,
-                                          int wn, int lane, int wave) {
-    constexpr int CH = BigTile<BK>::CH, TILE = BigTile<BK>::TILE, PER_WAVE = BigTile<BK>::PER_WAVE;
+__device__ __forceinline__ void ring_gemm_pp(ACC (&acc)[4][2], int8_t *smem, const int8_t *A, const int8_t *B,
+                                             int64_t rows_a, int64_t rows_b, int64_t K, int64_t m0, int64_t n0,
+                                             int wm, int wn, int lane, int wave) {
+    constexpr int CH = BigTile<BK>::CH, TILE = BigTile<BK>::TILE;
+    constexpr int PW = TILE / 1024 / 8;     // direct loads per wave, slice and operand
     constexpr int S = BigTile<BK>::S;
     constexpr int STAGE = 2 * TILE;
+    const int group = wave / 4;
     const int64_t nk = K / BK;
-
-    // Global source of each direct load issued by this lane (for k = 0).
-    const int8_t *srcA[PER_WAVE];
-    const int8_t *srcB[PER_WAVE];
+    const int8_t *srcA[PW];
+    const int8_t *srcB[PW];
 #pragma unroll
-    for (int ii = 0; ii < PER_WAVE; ii++) {
-        const int pos = 64 * (wave * PER_WAVE + ii) + lane;   // chunk position in the slice
+    for (int ii = 0; ii < PW; ii++) {
+        const int pos = 64 * (wave * PW + ii) + lane;
         const int row = pos / CH;
         const int c = (pos % CH) ^ swz<CH>(row);
         const int64_t ra = min(m0 + row, rows_a - 1), rb = min(n0 + row, rows_b - 1);
         srcA[ii] = A + ra * K + 16 * c;
         srcB[ii] = B + rb * K + 16 * c;
     }
-    // LDS byte offsets of this lane's fragments: block row 32i + lane%32,
-    // chunk 2s + lane/32.  swz depends only on the low 5 row bits, so the
-    // offset of block i is that of block 0 plus 32 rows.
     const int fr = lane % 32;
     int offA[S], offB[S];
 #pragma unroll
     for (int s = 0; s < S; s++) {
         const int c = 2 * s + lane / 32;
-        const int ra = wm * 128 + fr, rb = wn * 128 + fr;
+        const int ra = wm * 128 + fr, rb = wn * 64 + fr;
         offA[s] = 16 * (CH * ra + (c ^ swz<CH>(ra)));
         offB[s] = 16 * (CH * rb + (c ^ swz<CH>(rb)));
     }
-
 #pragma unroll
     for (int i = 0; i < 4; i++)
 #pragma unroll
-        for (int j = 0; j < 4; j++) acc[i][j] = ACC{};
-
-    // Slices 0 .. NBUF-2 in flight before the loop; iteration kt consumes
-    // slice kt and starts slice kt + NBUF - 1 (clamped: the last iterations
-    // reload the final slice, keeping the loop body free of branches) into
-    // the buffer that iteration kt - 1 consumed.
+        for (int j = 0; j < 2; j++) acc[i][j] = ACC{};
+    auto issue = [&](int64_t slice, int buf) __attribute__((always_inline)) {
+        const int64_t k0 = (slice < nk ? slice : nk - 1) * BK;
 #pragma unroll
-    for (int b = 0; b < NBUF - 1; b++) {
-        const int64_t k0 = (int64_t)(b < nk ? b : nk - 1) * BK;
-#pragma unroll
-        for (int ii = 0; ii < PER_WAVE; ii++) {
-            const int inst = wave * PER_WAVE + ii;
-            lds_load16(srcA[ii] + k0, smem + b * STAGE + 1024 * inst);
-            lds_load16(srcB[ii] + k0, smem + b * STAGE + TILE + 1024 * inst);
+        for (int ii = 0; ii < PW; ii++) {
+            const int inst = wave * PW + ii;
+            lds_load16(srcA[ii] + k0, smem + buf * STAGE + 1024 * inst);
+            lds_load16(srcB[ii] + k0, smem + buf * STAGE + TILE + 1024 * inst);
         }
+    };
+#pragma unroll
+    for (int b = 0; b < NBUF - 1; b++) issue(b, b);
+    if (group == 1) {
+        wait_vmcnt<(NBUF - 2) * 2 * PW>();
+        barrier_only();
     }
     for (int64_t kt = 0; kt < nk; kt++) {
-        // this wave's loads of slice kt are done (the NBUF - 2 newer slices
-        // may still be in flight); after the barrier every wave's are, and
-        // every wave has finished reading the buffer refilled below
-        wait_vmcnt<(NBUF - 2) * 2 * PER_WAVE>();
+        wait_vmcnt<(NBUF - 2) * 2 * PW>();
         barrier_only();
-        const int cur = (int)(kt % NBUF), nxt = (int)((kt + NBUF - 1) % NBUF);
-        const int64_t nxt_k0 = (kt + NBUF - 1 < nk ? kt + NBUF - 1 : nk - 1) * BK;
-        big_slice<BK, MK>(acc, smem + cur * STAGE, smem + nxt * STAGE, srcA, srcB, nxt_k0, offA, offB, wave);
+        const int8_t *cur = smem + (int)(kt % NBUF) * STAGE;
+        v4i fa[S][4], fb[S][2];
+#pragma unroll
+        for (int s = 0; s < S; s++) {
+#pragma unroll
+            for (int i = 0; i < 4; i++) fa[s][i] = *reinterpret_cast<const v4i *>(cur + offA[s] + i * 32 * CH * 16);
+#pragma unroll
+            for (int j = 0; j < 2; j++) fb[s][j] = *reinterpret_cast<const v4i *>(cur + TILE + offB[s] + j * 32 * CH * 16);
+        }
+        issue(kt + NBUF - 1, (int)((kt + NBUF - 1) % NBUF));
+        __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0)
+        wait_vmcnt<(NBUF - 2) * 2 * PW>();
+        barrier_only();
+#pragma unroll
+        for (int s = 0; s < S; s++)
+#pragma unroll
+            for (int i = 0; i < 4; i++)
+#pragma unroll
+                for (int j = 0; j < 2; j++) {
+                    if constexpr (MK == MK_I8) acc[i][j] = mfma32(fa[s][i], fb[s][j], acc[i][j]);
+                    else acc[i][j] = mfma32<MK>(fa[s][i], fb[s][j], acc[i][j]);
+                }
     }
+    if (group == 0) barrier_only();
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
 }
+
 
 }  // namespace ql

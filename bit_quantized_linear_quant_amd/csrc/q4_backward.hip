@@ -130,6 +130,10 @@ __global__ __launch_bounds__(kTThreads) void bwd_pad_kernel(const uint16_t *__re
     dst[i] = c < cols ? src[r * cols + c] : (uint16_t)0;
 }
 
+// Threads of a backward product's workgroup: eight waves on the
+// phase-alternating ring (ring_gemm_pp).
+constexpr int kBwdThreads = 2 * LThreads;
+
 struct BwdParams {
     const int8_t *a;       // [rows_a][kc] 16-bit
     const int8_t *b;       // [rows_b][kc] 16-bit
@@ -142,7 +146,7 @@ struct BwdParams {
     double *partials;      // one per wave (step-size term), or NULL
 };
 
-// One 32-column block J of a wave's 128 x 128 sub-tile of the backward
+// One 32-column block J of a wave's 128 x 64 sub-tile of the backward
 // epilogue: the products d = acc * s'_v go to a padded LDS block (lane
 // holds column lane%32 and rows 8*(r/4) + 4*(lane/32) + r%4 of register r
 // of each 32x32 block), then each lane takes 8 runs of 8 columns of one
@@ -150,7 +154,7 @@ struct BwdParams {
 // used), the mask and step-size term, and 8 outputs written together.  J is
 // a template argument so the accumulators are indexed statically.
 template <int J, int IN, int OUT, bool LSQ>
-__device__ __forceinline__ void bwd_epi_block(const BwdParams &p, const v16f (&acc)[4][4], float *ep, bool vec,
+__device__ __forceinline__ void bwd_epi_block(const BwdParams &p, const v16f (&acc)[4][2], float *ep, bool vec,
                                               int64_t m0, int64_t n0, int wm, int wn, int lane, float sv, float sp,
                                               float rcp, double &part) {
     constexpr int j = J;
@@ -163,7 +167,7 @@ __device__ __forceinline__ void bwd_epi_block(const BwdParams &p, const v16f (&a
         }
     __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0): the block is in LDS
     __builtin_amdgcn_wave_barrier();
-    const int64_t cb = n0 + wn * 128 + 32 * j;
+    const int64_t cb = n0 + wn * 64 + 32 * j;
     if (vec) {
         uint4 raw[8];
 #pragma unroll
@@ -243,20 +247,21 @@ __device__ __forceinline__ void bwd_epi_block(const BwdParams &p, const v16f (&a
     }
 
 template <int MK, int IN, int OUT, bool LSQ>
-__global__ __launch_bounds__(LThreads, 1) void bwd_gemm_kernel(BwdParams p, int tiles_m, int tiles_n) {
+__global__ __launch_bounds__(kBwdThreads, 1) void bwd_gemm_kernel(BwdParams p, int tiles_m, int tiles_n) {
     constexpr int BK = 64, NBUF = 3;
     constexpr int STAGE = 2 * BigTile<BK>::TILE;
     // the ring, then per wave a padded 128 x 32 fp32 block of the epilogue
-    static_assert(4 * 128 * 33 * 4 <= NBUF * STAGE, "epilogue blocks fit in the ring's LDS");
-    __shared__ __attribute__((aligned(1024))) int8_t smem[NBUF * STAGE];
+    constexpr int EPI_BYTES = kBwdThreads / kWave * 128 * 33 * 4;
+    constexpr int SMEM = NBUF * STAGE > EPI_BYTES ? NBUF * STAGE : EPI_BYTES;
+    __shared__ __attribute__((aligned(1024))) int8_t smem[SMEM];
 
     const int lane = threadIdx.x % kWave, wave = wave_id();
-    const int wm = wave / 2, wn = wave % 2;
+    const int wm = wave % 2, wn = (wave / 2) % 4;
     int tm, tn;
     xcd_tile(blockIdx.x, tiles_m, tiles_n, kGroupM, tm, tn);
     const int64_t m0 = (int64_t)tm * LB, n0 = (int64_t)tn * LB;
-    v16f acc[4][4];
-    ring_gemm<BK, NBUF, MK>(acc, smem, p.a, p.b, p.rows_a, p.rows_b, p.kbytes, m0, n0, wm, wn, lane, wave);
+    v16f acc[4][2];
+    ring_gemm_pp<BK, NBUF, MK>(acc, smem, p.a, p.b, p.rows_a, p.rows_b, p.kbytes, m0, n0, wm, wn, lane, wave);
 
     const float ss = *p.src_scale, vs = *p.val_scale;
     const float sp = ss > p.eps ? ss : p.eps, rcp = __fdiv_rn(1.0f, sp);
@@ -266,14 +271,12 @@ __global__ __launch_bounds__(LThreads, 1) void bwd_gemm_kernel(BwdParams p, int 
     const bool vec = (p.rows_b % 8) == 0;
     bwd_epi_block<0, IN, OUT, LSQ>(p, acc, ep, vec, m0, n0, wm, wn, lane, sv, sp, rcp, part);
     bwd_epi_block<1, IN, OUT, LSQ>(p, acc, ep, vec, m0, n0, wm, wn, lane, sv, sp, rcp, part);
-    bwd_epi_block<2, IN, OUT, LSQ>(p, acc, ep, vec, m0, n0, wm, wn, lane, sv, sp, rcp, part);
-    bwd_epi_block<3, IN, OUT, LSQ>(p, acc, ep, vec, m0, n0, wm, wn, lane, sv, sp, rcp, part);
     if constexpr (LSQ) {
         // one partial per wave, no workgroup barrier: a barrier here would
         // make every wave wait for its output stores to drain
 #pragma unroll
         for (int off = 32; off > 0; off >>= 1) part += __shfl_xor(part, off);
-        if (lane == 0) p.partials[(int64_t)blockIdx.x * (LThreads / kWave) + wave] = part;
+        if (lane == 0) p.partials[(int64_t)blockIdx.x * (kBwdThreads / kWave) + wave] = part;
     }
 }
 
@@ -311,7 +314,7 @@ template <int MK, int IN, int OUT, bool LSQ>
 hipError_t launch_bwd_gemm(const BwdParams &p, hipStream_t st) {
     const int64_t tm = (p.rows_a + LB - 1) / LB, tn = (p.rows_b + LB - 1) / LB;
     if (tm * tn > 0x7fffffff) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((bwd_gemm_kernel<MK, IN, OUT, LSQ>), dim3((unsigned)(tm * tn)), dim3(LThreads), 0, st, p,
+    hipLaunchKernelGGL((bwd_gemm_kernel<MK, IN, OUT, LSQ>), dim3((unsigned)(tm * tn)), dim3(kBwdThreads), 0, st, p,
                        (int)tm, (int)tn);
     return hipGetLastError();
 }
@@ -368,7 +371,7 @@ hipError_t backward_t(const Q4BackwardArgs &a, hipStream_t st) {
 }  // namespace
 
 size_t q4_backward_partials(int64_t m, int64_t k) {
-    return (size_t)(((m + LB - 1) / LB) * ((k + LB - 1) / LB)) * (LThreads / kWave);
+    return (size_t)(((m + LB - 1) / LB) * ((k + LB - 1) / LB)) * (kBwdThreads / kWave);
 }
 
 size_t q4_backward_workspace(int64_t m, int64_t n, int64_t k) {
