@@ -367,17 +367,20 @@ hipError_t launch_f6(const Params &p, hipStream_t st) {
 // operand's tile grid: a 1024-byte tile per 32 rows x 64 k, slot l (16
 // bytes) holding the 32 codes of lane l's register image.  The 16 KB of each
 // operand that a 128-k slice of the 256 x 256 tile needs move HBM ->
-// registers, one slot (16 bytes) per load; each slot becomes 32 exact fp16
-// values (code + 8 ORed into the mantissa of 1024.0, minus 1032) and then
-// its FP6 E3M2 register image with one v_cvt_scalef32_pk32_bf6_f16 (exact
-// on these integers), stored into the FP6 tile layout in LDS.  From there
-// the slice runs exactly as in the FP6 kernel (same fragments, products and
-// epilogue).  Two LDS stages: while the matrix cores consume one, the next
-// slice is expanded into the other and the slice after it is in flight in
-// registers.  The last iterations reload and re-expand the final slice into
-// the unused stage, so the loop body has no branches around its loads.
+// registers, one slot (16 bytes) per load, two slices ahead in two register
+// sets; each slot becomes 32 exact fp16 values (code + 8 ORed into the
+// mantissa of 1024.0, minus 1032) and then its FP6 E3M2 register image with
+// one v_cvt_scalef32_pk32_bf6_f16 (exact on these integers), stored into the
+// FP6 tile layout in LDS, one slice ahead, through a ring of three stages.
+// From there the slice runs as in the FP6 kernel (same fragments, products
+// and epilogue) on eight waves of 128 x 64 in two phase-alternating groups:
+// one group reads its first 64-k step's fragments and expands its slots of
+// the next slice while the other issues its products (reading its second
+// step's fragments among them), so the expansion's vector work overlaps the
+// partner's matrix-core work.  The last iterations reload and re-expand the
+// final slice, so the loop body has no branches around its loads; a padded
+// last slice (odd slice counts) is walked but not multiplied.
 constexpr int kP4Tile = 1024;                          // bytes of one packed 32 x 64 tile
-constexpr int kP4Slots = 2 * (LB / 32) * 64 / LThreads;  // slots per thread, operand and slice
 
 typedef _Float16 v32h __attribute__((ext_vector_type(32)));
 
@@ -412,97 +415,109 @@ __device__ __forceinline__ void store_image(int8_t *tile, int l, const v6u &img)
 }
 
 template <int OUT>
-__global__ __launch_bounds__(LThreads, 1) void gemm_a4w4_packed_kernel(Params p, int tiles_m, int tiles_n) {
+__global__ __launch_bounds__(2 * LThreads, 1) void gemm_a4w4_packed_kernel(Params p, int tiles_m, int tiles_n) {
     constexpr int STAGE = 2 * kF6Op;
-    constexpr int EPI_BYTES = 1024 + 4 * 128 * big_epitch(4);
-    constexpr int SMEM = 2 * STAGE > EPI_BYTES ? 2 * STAGE : EPI_BYTES;
+    constexpr int SLOTS = 2 * (LB / 32) * 64 / (2 * LThreads);   // slots per thread, operand and slice (2)
+    constexpr int EPI_BYTES = 1024 + 8 * 128 * big_epitch(2);
+    constexpr int NST = 3;                      // LDS stages of FP6 images
+    constexpr int SMEM = NST * STAGE > EPI_BYTES ? NST * STAGE : EPI_BYTES;
     __shared__ __attribute__((aligned(1024))) int8_t smem[SMEM];
 
     const int lane = threadIdx.x % kWave, wave = wave_id();
-    const int wm = wave / 2, wn = wave % 2;
+    const int group = wave / 4;
+    const int wm = wave % 2, wn = (wave / 2) % 4;
     int tm, tn;
     xcd_tile(blockIdx.x, tiles_m, tiles_n, kGroupM, tm, tn);
     const int64_t m0 = (int64_t)tm * LB, n0 = (int64_t)tn * LB;
-    const int64_t ktiles = (p.k + 127) / 128 * 2;   // 64-k tiles per 32-row block
-    const int64_t nk = ktiles / 2;                   // 128-k slices
+    const int64_t ktiles = (p.k + 127) / 128 * 2;
+    const int64_t nk = ktiles / 2;
+    const int64_t nkp = (nk + 1) / 2 * 2;            // slices walked (a padded last one is not multiplied)
     const int64_t rows_a = (p.m + 31) / 32, rows_b = (p.n + 31) / 32;
 
-    // Slot i of this thread in a slice is s = tid + 256 i: tile s / 64 =
-    // tid / 64 + 4 i of the slice (32-row block tid / 128 + 2 i, 64-k half
-    // (tid / 64) % 2), lane slot tid % 64.  Blocks past the operand re-read
-    // its last block; those rows are never stored.
+    // Slot i of this thread in a slice is s = tid + 512 i: tile s / 64 =
+    // tid / 64 + 8 i (32-row block tid / 128 + 4 i, 64-k half (tid / 64) % 2),
+    // lane slot tid % 64.
     const int tid = (int)threadIdx.x, sl = tid % 64, half = (tid / 64) % 2;
-    const uint8_t *srcA[kP4Slots];
-    const uint8_t *srcB[kP4Slots];
+    const uint8_t *srcA[SLOTS];
+    const uint8_t *srcB[SLOTS];
 #pragma unroll
-    for (int i = 0; i < kP4Slots; i++) {
-        const int rt = tid / 128 + 2 * i;
+    for (int i = 0; i < SLOTS; i++) {
+        const int rt = tid / 128 + 4 * i;
         const int64_t ra = min(m0 / 32 + rt, rows_a - 1), rb = min(n0 / 32 + rt, rows_b - 1);
         srcA[i] = reinterpret_cast<const uint8_t *>(p.x) + (ra * ktiles + half) * kP4Tile + 16 * sl;
         srcB[i] = reinterpret_cast<const uint8_t *>(p.w) + (rb * ktiles + half) * kP4Tile + 16 * sl;
     }
-    const int dbase = (tid / 64) * kF6Tile;   // LDS tile of slot 0; slot i is 4 i tiles further
-    uint4 la[kP4Slots], lb[kP4Slots];
-    auto load = [&](int64_t kt) {
-        const int64_t off = (kt < nk ? kt : nk - 1) * 2 * kP4Tile;
+    const int dbase = (tid / 64) * kF6Tile;   // LDS tile of slot 0; slot i is 8 i tiles further
+    uint4 la[2][SLOTS], lb[2][SLOTS];         // slice s lives in register set s % 2
+    auto load = [&](int64_t slice, auto S) __attribute__((always_inline)) {
+        const int64_t off = (slice < nk ? slice : nk - 1) * 2 * kP4Tile;
 #pragma unroll
-        for (int i = 0; i < kP4Slots; i++) {
-            la[i] = load16_stream(srcA[i] + off);
-            lb[i] = load16_stream(srcB[i] + off);
+        for (int i = 0; i < SLOTS; i++) {
+            la[S][i] = load16_stream(srcA[i] + off);
+            lb[S][i] = load16_stream(srcB[i] + off);
         }
     };
-    auto expand = [&](int8_t *stage) {
+    auto expand = [&](int8_t *stage, auto S) __attribute__((always_inline)) {
 #pragma unroll
-        for (int i = 0; i < kP4Slots; i++) {
-            store_image(stage + dbase + 4 * i * kF6Tile, sl, expand_slot(la[i]));
-            store_image(stage + kF6Op + dbase + 4 * i * kF6Tile, sl, expand_slot(lb[i]));
+        for (int i = 0; i < SLOTS; i++) {
+            store_image(stage + dbase + 8 * i * kF6Tile, sl, expand_slot(la[S][i]));
+            store_image(stage + kF6Op + dbase + 8 * i * kF6Tile, sl, expand_slot(lb[S][i]));
         }
     };
 
-    v16f acc[4][4];
+    v16f acc[4][2];
 #pragma unroll
     for (int i = 0; i < 4; i++)
 #pragma unroll
-        for (int j = 0; j < 4; j++) acc[i][j] = v16f{};
+        for (int j = 0; j < 2; j++) acc[i][j] = v16f{};
 
-    load(0);
-    expand(smem);
-    load(1);
-    for (int64_t kt = 0; kt < nk; kt++) {
-        // this slice's images are in LDS (every wave's stores done), and every
-        // wave has finished reading the stage expanded into below
-        __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0)
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
+    load(0, I0{});
+    load(1, I1{});
+    expand(smem, I0{});
+    load(2, I0{});
+    __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0): this thread's images of slice 0 are stored
+    if (group == 1) barrier_only();
+    // One slice: wait for the barrier (slice kt's images complete, the stage
+    // expanded into below free), read its fragments, expand slice kt + 1 from
+    // its register set into the other stage, load slice kt + 3 into the set
+    // just freed; barrier; the products.
+    auto step = [&](int64_t kt, auto S) __attribute__((always_inline)) {
+        constexpr int SN = 1 - decltype(S)::value;   // register set of slice kt + 1
         barrier_only();
-        const int8_t *__restrict__ cur = smem + (kt & 1) * STAGE;
-        int8_t *__restrict__ nxt = smem + ((kt + 1) & 1) * STAGE;
-        v8i fa[2][4], fb[2][4];
-        auto frags = [&](int st) {
+        const int8_t *cur = smem + (int)(kt % NST) * STAGE;
+        int8_t *nxt = smem + (int)((kt + 1) % NST) * STAGE;
+        v8i fa[4], fb[2];
+        auto frags = [&](int st) __attribute__((always_inline)) {
 #pragma unroll
-            for (int i = 0; i < 4; i++) fa[st][i] = f6_frag(cur + ((wm * 4 + i) * 2 + st) * kF6Tile, lane);
+            for (int i = 0; i < 4; i++) fa[i] = f6_frag(cur + ((wm * 4 + i) * 2 + st) * kF6Tile, lane);
 #pragma unroll
-            for (int j = 0; j < 4; j++) fb[st][j] = f6_frag(cur + kF6Op + ((wn * 4 + j) * 2 + st) * kF6Tile, lane);
+            for (int j = 0; j < 2; j++) fb[j] = f6_frag(cur + kF6Op + ((wn * 2 + j) * 2 + st) * kF6Tile, lane);
         };
         frags(0);
-        expand(nxt);        // slice kt + 1 (loaded during the previous slice)
-        load(kt + 2);
+        expand(nxt, std::integral_constant<int, SN>{});
+        load(kt + 3, std::integral_constant<int, SN>{});
+        __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0): fragments in registers, images stored
+        barrier_only();
+        if (kt < nk) {
 #pragma unroll
-        for (int st = 0; st < 2; st++) {
-            if (st == 0) frags(1);
+            for (int st = 0; st < 2; st++) {
+                if (st == 1) frags(1);
 #pragma unroll
-            for (int i = 0; i < 4; i++)
+                for (int i = 0; i < 4; i++)
 #pragma unroll
-                for (int j = 0; j < 4; j++)
-                    acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa[st][i], fb[st][j], acc[i][j], 3, 3,
-                                                                                0, kF6Scale, 0, kF6Scale);
-            if (st == 0) {
-#pragma unroll
-                for (int q = 0; q < 16; q++) {
-                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-                }
+                    for (int j = 0; j < 2; j++)
+                        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa[i], fb[j], acc[i][j], 3, 3, 0,
+                                                                                    kF6Scale, 0, kF6Scale);
             }
         }
+    };
+    for (int64_t kt = 0; kt < nkp; kt += 2) {
+        step(kt, I0{});
+        step(kt + 1, I1{});
     }
+    if (group == 0) barrier_only();
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     big_epilogue<EPI_SCALARS, OUT>(p, acc, smem, m0, n0, wm, wn, wave, lane);
@@ -512,8 +527,8 @@ template <int OUT>
 hipError_t launch_packed(const Params &p, hipStream_t st) {
     const int64_t tm = (p.m + LB - 1) / LB, tn = (p.n + LB - 1) / LB;
     if (tm * tn > 0x7fffffff) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((gemm_a4w4_packed_kernel<OUT>), dim3((unsigned)(tm * tn)), dim3(LThreads), 0, st, p, (int)tm,
-                       (int)tn);
+    hipLaunchKernelGGL((gemm_a4w4_packed_kernel<OUT>), dim3((unsigned)(tm * tn)), dim3(2 * LThreads), 0, st, p,
+                       (int)tm, (int)tn);
     return hipGetLastError();
 }
 
