@@ -20,7 +20,12 @@ The same JSON line carries:
   decode_gemv   the metric's second figure: packed-ternary-weight HBM GB/s of
                 the M<=16 decode GEMV (K=8192, N=28672) for M in {1,4,16},
                 with the packed weight rotated over copies larger than the
-                256 MB last-level cache, launches replayed from a HIP graph.
+                256 MB last-level cache, launches replayed from a HIP graph;
+                each M also with its single-launch latency (one eager launch
+                timed alone) and its share of the stream floor: the same
+                weight bytes read by a plain HBM read stream
+                (qlinear_hbm_read_stream), per launch in the same graph
+                rotation, and once over all copies in one launch.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--only PART]
 
@@ -228,17 +233,64 @@ def bench_decode(ql, torch, synthetic, reps: int = 10):
         torch.cuda.synchronize()
         us = e0.elapsed_time(e1) * 1e3 / (reps * launches)
         gbs = packed_bytes / (us * 1e-6) / 1e9
+        single = time_single(torch, lambda i: ql.qlinear_gemm_w2a8(xq, pts, rs, copies[i % len(copies)], gamma, n,
+                                                                   out=out))
         res[str(m)] = {"us_per_launch": round(us, 3), "packed_weight_GBps": round(gbs, 1),
-                       "frac_hbm": round(gbs / PEAK_HBM_GBS, 4)}
+                       "frac_hbm": round(gbs / PEAK_HBM_GBS, 4), "single_launch_us": round(single, 3)}
         del g
+    floor = stream_floor(ql, torch, copies, packed_bytes, reps)
+    for m in res:
+        res[m]["frac_of_stream_floor"] = round(floor["per_launch_us"] / res[m]["us_per_launch"], 4)
     return {"unit": "GB/s", "n": n, "k": k, "packed_weight_bytes": packed_bytes,
             "timing": "per launch, mean over HIP-graph replays of 24 back-to-back launches rotating 6 "
-                      "copies of the packed weight (352 MB)",
-            "by_m": res}
+                      "copies of the packed weight (352 MB); single_launch_us: median of 24 eager launches "
+                      "each timed alone (events around it, device idle before it)",
+            "by_m": res, "stream_floor": floor}
+
+
+def stream_floor(ql, torch, copies, nbytes: int, reps: int = 10):
+    """The HBM read ceiling of the decode weight stream (qlinear_hbm_read_stream).
+
+    One launch over a 6x larger buffer gives the sustained read rate; the same
+    HIP-graph rotation as the GEMV, one copy per launch, gives the per-launch
+    floor that includes the launch's ramp-up and drain.
+    """
+    big = torch.empty((len(copies) * nbytes,), dtype=torch.uint8, device=copies[0].device)
+    for i, c in enumerate(copies):
+        big[i * nbytes:(i + 1) * nbytes].copy_(c.view(torch.uint8))
+    sink = torch.zeros((ql.QL_HBM_STREAM_SINK_WORDS,), dtype=torch.int64, device=big.device)
+    one = time_single(torch, lambda i: ql.qlinear_hbm_read_stream(big, sink), 9)
+    per = time_graph(torch, lambda i: ql.qlinear_hbm_read_stream(copies[i % len(copies)], sink),
+                     4 * len(copies), reps)
+    del big
+    return {"kernel": "hbm_read_stream_kernel (qlinear_hbm_read_stream): 16-byte non-temporal loads",
+            "one_launch_bytes": len(copies) * nbytes, "one_launch_us": round(one, 3),
+            "one_launch_GBps": round(len(copies) * nbytes / (one * 1e-6) / 1e9, 1),
+            "per_launch_us": round(per, 3),
+            "per_launch_GBps": round(nbytes / (per * 1e-6) / 1e9, 1)}
 
 
 def _events(torch):
     return torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+
+def time_single(torch, launch, count: int = 24) -> float:
+    """Median us of one eager launch timed alone: events around it, the device idle before it.
+
+    ``launch(i)`` rotates its inputs, so a launch does not find them in the last-level cache.
+    """
+    launch(0)
+    torch.cuda.synchronize()
+    t = []
+    for i in range(count):
+        e0, e1 = _events(torch)
+        e0.record()
+        launch(i)
+        e1.record()
+        torch.cuda.synchronize()
+        t.append(e0.elapsed_time(e1) * 1e3)
+    t.sort()
+    return t[len(t) // 2]
 
 
 def time_graph(torch, launch, count: int, reps: int = 10) -> float:
@@ -401,6 +453,8 @@ def bench_rows(ql, torch, synthetic, with_oracle: bool = True):
         us, gbytes, "GB/s", PEAK_HBM_GBS, "hbm",
         f"{gbytes} B (packed weight, fp16 scales, packed zeros, fp16 x, fp16 out)",
         (512 * k // 2 + 512 * (k // gs) * 2.5 + m * k * 2 + m * 512 * 2) / t / 1e9, f"512 of {n} columns")
+    rows["a7_grouped_int4_32x4096x11008_g128"]["single_launch_us"] = round(time_single(
+        torch, lambda i: ql.qlinear_gemm_w4a8_grouped(xg, pws[i % len(pws)], sc, pz, gs, n, out=outg)), 3)
     xqg, ptsg, _ = ql.qlinear_quant_act(xg)
     us = time_graph(torch, lambda i: ql.qlinear_gemm_w4a8_grouped(xqg, pws[i % len(pws)], sc, pz, gs, n, out=outg,
                                                                   per_token_scale=ptsg), 48)

@@ -42,7 +42,9 @@ _lib = None
 
 
 # QL_ABI_VERSION of include/qlinear.h that the argument lists below follow.
-ABI_VERSION = 7
+ABI_VERSION = 8
+# Words of the sink array of qlinear_hbm_read_stream (QL_HBM_STREAM_SINK_WORDS).
+QL_HBM_STREAM_SINK_WORDS = 16384
 
 
 class QLinearError(RuntimeError):
@@ -77,6 +79,7 @@ def lib() -> ctypes.CDLL:
             "qlinear_pack_ternary": (i32, [vp, i32, i64, i64, f64, vp, vp, vp, sz, vp]),
             "qlinear_pack_ternary_noalloc": (i32, [vp, i32, i64, i64, f64, vp, vp, vp]),
             "qlinear_pack_int4": (i32, [vp, i64, i64, i32, vp, vp]),
+            "qlinear_hbm_read_stream": (i32, [vp, sz, vp, vp]),
             "qlinear_gemm_w8a8": (i32, [vp, vp, i32, vp, vp, vp, i64, i64, i64, i32, vp, vp]),
             "qlinear_gemm_w8a8_batched": (i32, [vp, vp, i32, vp, i64, vp, vp, i64, i64, i64, i64, i32, vp, vp]),
             "qlinear_gemm_w2a8": (i32, [vp, vp, vp, vp, vp, vp, i64, i64, i64, i32, vp, vp]),
@@ -218,6 +221,23 @@ def qlinear_pack_ternary_noalloc(w, layout=QL_W_NK, eps=1e-5, packed=None, gamma
     _check("qlinear_pack_ternary_noalloc", lib().qlinear_pack_ternary_noalloc(
         _ptr(w), layout, n, k, float(eps), _ptr(packed), _ptr(gamma), _stream(w)))
     return packed, gamma
+
+
+def qlinear_hbm_read_stream(buf, sink=None):
+    """Read every byte of the device tensor ``buf`` once (HBM read-rate measurement aid).
+
+    ``sink`` is a device int64 tensor of ``QL_HBM_STREAM_SINK_WORDS`` elements, XOR-accumulated
+    word by word (not cleared); returns it.
+    """
+    _gpu(buf, "buf")
+    if sink is None:
+        sink = torch.zeros((QL_HBM_STREAM_SINK_WORDS,), dtype=torch.int64, device=buf.device)
+    else:
+        _gpu(sink, "sink", torch.int64)
+        _need(sink, QL_HBM_STREAM_SINK_WORDS * 8, "sink")
+    nbytes = buf.numel() * buf.element_size()
+    _check("qlinear_hbm_read_stream", lib().qlinear_hbm_read_stream(_ptr(buf), nbytes, _ptr(sink), _stream(buf)))
+    return sink
 
 
 def qlinear_pack_int4(codes, what=QL_INT4_WEIGHT, packed=None):

@@ -141,6 +141,13 @@ ql_status qlinear_pack_int4(const uint8_t *codes, int64_t rows, int64_t cols, ql
     return QL_ERR_UNSUPPORTED;
 }
 
+ql_status qlinear_hbm_read_stream(const void *buf, size_t bytes, uint64_t *sink, void *stream) {
+    if (!buf || !sink) return QL_ERR_NULL;
+    if (bytes == 0 || bytes % 16 || bytes > (size_t)INT64_MAX) return QL_ERR_SHAPE;
+    if (!aligned16(buf) || !aligned16(sink)) return QL_ERR_ALIGN;
+    return hip_status(ql::launch_hbm_read_stream(buf, (int64_t)bytes, sink, as_stream(stream)));
+}
+
 static ql_status gemm_out_kind(ql_dtype d, int *kind) {
     switch (d) {
         case QL_F16: *kind = ql::OUT_F16; return QL_OK;

@@ -10,6 +10,9 @@
 namespace ql {
 
 // quant.hip
+// stream.hip: reads bytes (a multiple of 16) at buf once, XOR into *sink.
+hipError_t launch_hbm_read_stream(const void *buf, int64_t bytes, uint64_t *sink, hipStream_t st);
+
 hipError_t launch_quant_act(int in_kind, const void *x, int64_t m, int64_t k, bool rmsnorm,
                             float eps_norm, float eps_q, int8_t *q, float *pts, int32_t *rowsum,
                             hipStream_t st);

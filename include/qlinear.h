@@ -47,7 +47,7 @@
 extern "C" {
 #endif
 
-#define QL_ABI_VERSION 7
+#define QL_ABI_VERSION 8
 /* Version of the 2-bit ternary weight layout written by qlinear_pack_ternary. */
 #define QL_TERNARY_PACK_V1 1
 /* Version of the 4-bit weight layout written by qlinear_pack_int4. */
@@ -472,6 +472,24 @@ ql_status qlinear_q4_backward(const void *grad_out, const void *x, const void *w
                               int64_t m, int64_t n, int64_t k, ql_dtype grad_dtype,
                               void *grad_x, void *grad_w, float *grad_scale_a,
                               void *workspace, size_t ws_bytes, void *stream);
+
+/* Words of the sink array of qlinear_hbm_read_stream. */
+#define QL_HBM_STREAM_SINK_WORDS 16384
+
+/*
+ * Measurement aid (no page defines it): reads the `bytes` bytes at `buf`
+ * once with 16-byte non-temporal loads spread over the whole device.  Each
+ * wave XORs the 32-bit words it read into its own word of `sink`, a device
+ * array of QL_HBM_STREAM_SINK_WORDS uint64 that the call does not clear;
+ * the XOR of the whole array then changes by the XOR of every word of the
+ * buffer.  Its time is the ceiling of any kernel that must stream as many
+ * bytes from HBM once, such as the decode product's packed weight, measured
+ * with the same load form.  buf and sink are device memory, 16-byte
+ * aligned; bytes is a positive multiple of 16 (QL_ERR_SHAPE otherwise).
+ * Asynchronous on `stream`; calls that overlap on one sink race on its
+ * words.
+ */
+ql_status qlinear_hbm_read_stream(const void *buf, size_t bytes, uint64_t *sink, void *stream);
 
 #ifdef __cplusplus
 }

@@ -40,7 +40,7 @@ def test_exports_every_declared_symbol(L):
 
 
 def test_abi_version_and_status_strings(L):
-    assert ql.qlinear_abi_version() == ql.ABI_VERSION == 7
+    assert ql.qlinear_abi_version() == ql.ABI_VERSION == 8
     for code, name in ql.STATUS.items():
         s = ql.qlinear_status_string(code)
         assert isinstance(s, str) and s
@@ -215,3 +215,19 @@ def test_product_path_does_not_touch_the_oracle():
                 assert "qlinear_oracle" not in text and "liboracle" not in text, fn
     out = subprocess.run(["nm", "-D", ql.LIB_PATH], capture_output=True, text=True, check=True).stdout
     assert "oracle_" not in out
+
+
+def test_hbm_read_stream_validation(L):
+    f = L.qlinear_hbm_read_stream
+    assert f(NULL, 16, A, NULL) == -1
+    assert f(A, 16, NULL, NULL) == -1
+    assert f(A, 0, A, NULL) == -2          # empty
+    assert f(A, 24, A, NULL) == -2         # not whole 16-byte chunks
+    assert f(U, 16, A, NULL) == -4
+    assert f(A, 16, U, NULL) == -4
+
+
+def test_hbm_stream_sink_words_match_header():
+    with open(os.path.join(ROOT, "include", "qlinear.h")) as f:
+        words = int(re.search(r"#define QL_HBM_STREAM_SINK_WORDS (\d+)", f.read()).group(1))
+    assert words == ql.QL_HBM_STREAM_SINK_WORDS

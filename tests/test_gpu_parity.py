@@ -872,3 +872,20 @@ def test_q4_backward_deterministic_and_eps():
     assert a[2].item() == b[2].item()
     assert c[2].item() == 0.0
 
+
+
+# ---------------------------------------------------------------------------
+# HBM read-stream measurement aid: every 32-bit word is read exactly once
+# (a word read twice cancels in the XOR, a word skipped is missing)
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("nbytes", [16, 48, 4096 * 16 + 16, 2048 * 128 + 32, 8 << 20, (64 << 20) + 16 * 3])
+def test_hbm_read_stream_reads_every_word_once(nbytes):
+    g = torch.Generator().manual_seed(nbytes % 1000003)
+    words = torch.randint(-2 ** 31, 2 ** 31 - 1, (nbytes // 4,), dtype=torch.int64, generator=g).to(torch.int32)
+    want = int(np.bitwise_xor.reduce(words.numpy().view(np.uint32)))
+    sink = ql.qlinear_hbm_read_stream(_cuda(words))
+    _sync()
+    assert int(np.bitwise_xor.reduce(sink.cpu().numpy().view(np.uint64))) == want
+    ql.qlinear_hbm_read_stream(_cuda(words), sink=sink)   # a second pass cancels the first
+    _sync()
+    assert not sink.cpu().numpy().any()
