@@ -350,6 +350,14 @@ def _row(us, work, unit, peak, bound, what, oracle_rate=None, oracle_sample=None
     return r
 
 
+def _with_floor(row, ql, torch, bufs, count, what):
+    """Add the HBM read-stream floor of a row: the same buffers read once each, same rotation."""
+    sink = torch.zeros((ql.QL_HBM_STREAM_SINK_WORDS,), dtype=torch.int64, device=bufs[0].device)
+    us = time_graph(torch, lambda i: ql.qlinear_hbm_read_stream(bufs[i % len(bufs)], sink), count)
+    row["stream_floor"] = {"us_per_launch": round(us, 3), "what": what}
+    row["frac_of_stream_floor"] = round(us / row["us_per_launch"], 4)
+
+
 def bench_rows(ql, torch, synthetic, with_oracle: bool = True):
     """Every step of the path on its own workload, against the roofline that bounds it.
 
@@ -394,6 +402,8 @@ def bench_rows(ql, torch, synthetic, with_oracle: bool = True):
     rows["a1_quant_act_2048x4096_bf16_rmsnorm"] = _row(
         us, qbytes, "GB/s", PEAK_HBM_GBS, "hbm", f"{qbytes} B (bf16 read, int8 codes, scale and rowsum)",
         sample * (k * 3 + 8) / t / 1e9, f"{sample} of {m} rows")
+    _with_floor(rows["a1_quant_act_2048x4096_bf16_rmsnorm"], ql, torch, xs, 48,
+                "plain read of the same bf16 inputs in the same rotation (the codes' writes not included)")
     del xs
     packed, gamma = ql.qlinear_pack_ternary(d["w"].to(dev), ql.QL_W_NK)
     xq, pts, rs = ql.qlinear_quant_act(d["x"].to(dev), rmsnorm=True)
@@ -455,6 +465,9 @@ def bench_rows(ql, torch, synthetic, with_oracle: bool = True):
         (512 * k // 2 + 512 * (k // gs) * 2.5 + m * k * 2 + m * 512 * 2) / t / 1e9, f"512 of {n} columns")
     rows["a7_grouped_int4_32x4096x11008_g128"]["single_launch_us"] = round(time_single(
         torch, lambda i: ql.qlinear_gemm_w4a8_grouped(xg, pws[i % len(pws)], sc, pz, gs, n, out=outg)), 3)
+    _with_floor(rows["a7_grouped_int4_32x4096x11008_g128"], ql, torch, pws, 48,
+                "plain read of the same packed weight copies in the same rotation (scales, zero-points, x "
+                "and out not included)")
     xqg, ptsg, _ = ql.qlinear_quant_act(xg)
     us = time_graph(torch, lambda i: ql.qlinear_gemm_w4a8_grouped(xqg, pws[i % len(pws)], sc, pz, gs, n, out=outg,
                                                                   per_token_scale=ptsg), 48)

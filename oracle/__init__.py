@@ -260,6 +260,25 @@ def gemm_i8(x, w, layout_nk: bool):
     return acc
 
 
+def gemm_exact(x, w, layout_nk: bool):
+    """``gemm_i8`` by a float64 matrix product (a library matmul as one step):
+    every product of two int8 values and every partial sum of a k <= 2^37
+    product is an integer below 2^53 in magnitude (127 * 128 * k), so the
+    float64 result is exact whatever order the library sums in.  For
+    products too large for the plain loops of ``gemm_i8``.
+
+    "Per-token Quantization for Matmul" Input / Example.
+    """
+    x = np.asarray(x)
+    w = np.asarray(w)
+    assert x.dtype == np.int8 and w.dtype == np.int8
+    k = x.shape[1]
+    assert (w.shape[1] if layout_nk else w.shape[0]) == k and 127 * 128 * k < 2 ** 53
+    wf = w.astype(np.float64)
+    acc = x.astype(np.float64) @ (wf.T if layout_nk else wf)
+    return acc.astype(np.int32)
+
+
 def dequant(acc, pts, deq):
     """fp64 ``y[m,n] = acc[m,n] * pts[m] * deq[n]`` ("Per-token ... Example")."""
     acc = _c(acc, np.int32)

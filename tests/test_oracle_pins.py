@@ -135,6 +135,25 @@ def test_grouped_batched_is_independent_products(int8_codes):
     np.testing.assert_allclose(y, ref, rtol=1e-12, atol=1e-12)
 
 
+@pytest.mark.parametrize("m,n,k,layout_nk", [(1, 1, 1, True), (7, 5, 300, True), (33, 17, 1000, False),
+                                              (64, 48, 4096, True)])
+def test_gemm_exact_equals_the_loop_product(m, n, k, layout_nk):
+    """The float64 library product of integer codes is the int32 loop product exactly,
+    including the extreme codes (-128 * -128 summed over the whole k)."""
+    r = synthetic.rng(m * 1000 + n + k)
+    x = r.integers(-128, 128, (m, k), dtype=np.int8)
+    w = r.integers(-128, 128, (n, k) if layout_nk else (k, n), dtype=np.int8)
+    x[0, :] = -128
+    if layout_nk:
+        w[0, :] = -128
+    else:
+        w[:, 0] = -128
+    got = oracle.gemm_exact(x, w, layout_nk)
+    assert got.dtype == np.int32
+    assert np.array_equal(got, oracle.gemm_i8(x, w, layout_nk))
+    assert int(got[0, 0]) == 128 * 128 * k
+
+
 def test_gemm_int32_overflow_is_reported():
     """The definition asserts the accumulator fits int32: (-128)^2 * 2^17 = 2^31 does not."""
     k = 1 << 17
