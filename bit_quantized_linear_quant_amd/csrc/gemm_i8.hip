@@ -2,7 +2,7 @@
 // epilogue fused ("Per-token Quantization for Matmul": Input, Output and
 // Example; "Q4LinearFunction" forward for the per-tensor scale pair).
 //
-// Three kernels share the epilogue:
+// The int8 kernels share the epilogue:
 //
 // gemm_i8_big_kernel -- large products with [n][k] weights and k % 64 == 0
 //   (the 8192^3 A4W4 product).  A 512-thread workgroup owns a 256 x 256
@@ -27,11 +27,20 @@
 //   waves split k over a few 16-column blocks per workgroup, reading the
 //   weights once with streaming loads, and sum their partials in LDS.
 //
+// gemv_kn_i8_kernel -- the same shapes with [k][n] weights (m <= 64,
+//   k % 64 == 0, n % 4 == 0): 4 x 4 byte blocks of the weight rows are
+//   transposed in registers and turned into fragments through a per-wave
+//   LDS block.
+//
 // gemm_i8_kernel -- everything else (any m, n, k >= 1, weights [k][n] or
 //   [n][k]): 128 x 128 tiles, 2 x 2 waves of 64 x 64 in 32x32x32 MFMA blocks,
 //   register-staged loads with zero fill at the edges, LDS rows padded to
 //   80 bytes; [k][n] weights are transposed 4 x 4 bytes at a time in
 //   registers on their way into LDS.
+//
+// The 4-bit A4W4 products of the same file run on the FP6 matrix cores
+// (gemm_a4w4_f6_kernel on FP6 operand tiles, gemm_a4w4_packed_kernel on
+// operands of two 4-bit codes per byte) with the large-tile epilogue.
 #include "ql_device.hpp"
 #include "ql_launch.hpp"
 #include "gemm_ring.hpp"
