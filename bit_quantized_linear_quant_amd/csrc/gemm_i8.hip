@@ -1228,10 +1228,12 @@ hipError_t launch_gemv_kn_t(const Params &p, int64_t batch, hipStream_t st) {
 
 // Four column blocks (64-byte row segments, x read once per 64 columns)
 // once that still makes 256 workgroups and n allows whole 16-byte loads;
-// one column block with eight waves below that.
+// one column block with eight waves below that; at most four 64-k steps
+// (a launch-bound product): four waves, one step each.
 template <int RB, int EPI, int OUT>
 hipError_t launch_gemv_kn_n(const Params &p, int64_t batch, hipStream_t st) {
     if (p.n % 16 == 0 && (p.n / 64) * batch >= 256) return launch_gemv_kn_t<4, RB, 4, 4, EPI, OUT>(p, batch, st);
+    if (p.k / 64 <= 4) return launch_gemv_kn_t<1, RB, 4, 1, EPI, OUT>(p, batch, st);
     return launch_gemv_kn_t<1, RB, 8, 4, EPI, OUT>(p, batch, st);
 }
 
