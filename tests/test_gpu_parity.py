@@ -83,6 +83,9 @@ W8A8_SHAPES = [
     (33, 3000, 768, False),    # three row blocks
     (64, 2048, 4096, False),   # four row blocks, long k
     (48, 260, 128, False),
+    (16, 16384, 256, False),   # 64-column groups with 16-byte row loads (n / 64 >= 256)
+    (33, 16400, 128, False),   # the same, last column group partly past n
+    (64, 16384, 320, False),   # the same with four row blocks, k steps not a multiple of the waves
     (16, 128, 200, False),     # k % 64 != 0 and n % 4 != 0: general kernel
     (9, 130, 256, False),
 ]
