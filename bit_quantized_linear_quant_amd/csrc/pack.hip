@@ -6,8 +6,10 @@
 // per-thread order and a fixed shuffle tree), then one 1024-thread workgroup
 // sums the chunk partials in a fixed order, so gamma' is identical on every
 // call.
-// The pack kernel compares |W| with gamma'/2 exactly in fp64 and writes one
-// 16-byte lane slice (four words) of the 2-bit layout per thread.
+// The pack kernels compare |W| with gamma'/2 exactly in fp64.  For [n][k]
+// weights one wave builds a 1 KB block of the 2-bit layout from 16 whole
+// 1 KB row segments (coalesced loads); for [k][n] weights one thread builds
+// one 16-byte lane slice (four words) from four-byte column gathers.
 //
 // 4-bit ("linear_4bit/mod.rs" module doc: eight nibbles per u32): weights
 // into the fragment-ordered layout, zero-points group-major.
@@ -132,10 +134,9 @@ __device__ __forceinline__ uint32_t tern_field(float v, double half) {
     return a > half ? (v > 0.0f ? 2u : 0u) : 1u;
 }
 
-// One thread = one lane slice (4 words, 64 consecutive k of one column) of a
-// 16-column x 256-k block.
-template <bool NK>
-__global__ __launch_bounds__(kPThreads) void pack_ternary_kernel(const float *__restrict__ w,
+// [k][n] weights: one thread = one lane slice (4 words, 64 consecutive k of
+// one column) of a 16-column x 256-k block.
+__global__ __launch_bounds__(kPThreads) void pack_ternary_kn_kernel(const float *__restrict__ w,
                                                                  int64_t n, int64_t k,
                                                                  const double *__restrict__ gamma,
                                                                  uint32_t *__restrict__ packed,
@@ -156,13 +157,8 @@ __global__ __launch_bounds__(kPThreads) void pack_ternary_kernel(const float *__
         for (int q4 = 0; q4 < 4; q4++) {
             float v[4];
             const int64_t k0 = kbase + 16 * t + 4 * q4;
-            if (NK) {
-                const float4 f = *reinterpret_cast<const float4 *>(w + col * k + k0);
-                v[0] = f.x; v[1] = f.y; v[2] = f.z; v[3] = f.w;
-            } else {
 #pragma unroll
-                for (int j = 0; j < 4; j++) v[j] = w[(k0 + j) * n + col];
-            }
+            for (int j = 0; j < 4; j++) v[j] = w[(k0 + j) * n + col];
             // element e = 4*q4 + j of the word: a = q4, b = j -> bits 8b + 2a
 #pragma unroll
             for (int j = 0; j < 4; j++) words[t] |= tern_field(v[j], half) << (8 * j + 2 * q4);
@@ -170,6 +166,57 @@ __global__ __launch_bounds__(kPThreads) void pack_ternary_kernel(const float *__
     }
     *reinterpret_cast<uint4 *>(packed + bi * 256 + 4 * l) =
         make_uint4(words[0], words[1], words[2], words[3]);
+}
+
+// [n][k] weights: one wave per 16-column x 256-k block (1 KB of output).
+// Lane l loads the floats 4 l .. 4 l + 3 of each of the block's 16 weight
+// rows (one coalesced 1 KB load per row), so it holds element e = 4 (l % 4)
+// + j of word (l % 16) / 4 of k group l / 16 of every column; its four 2-bit
+// fields go to bits 8 j + 2 (l % 4), the four lanes of a quad OR their
+// parts into the whole word, and the words go through a wave-private LDS
+// block to one 16-byte store per lane.  Same comparison as the [k][n] form.
+constexpr int kTWaves = kPThreads / kWave;
+
+__global__ __launch_bounds__(kPThreads) void pack_ternary_rows_kernel(const float *__restrict__ w, int64_t k,
+                                                                      const double *__restrict__ gamma,
+                                                                      uint32_t *__restrict__ packed,
+                                                                      int64_t nblocks) {
+    __shared__ uint32_t blk[kTWaves][256];
+    const int lane = threadIdx.x % kWave, wave = wave_id();
+    const int64_t bi = (int64_t)blockIdx.x * kTWaves + wave;
+    if (bi >= nblocks) return;
+    const int64_t kblocks = k / 256;
+    const int64_t nb = bi / kblocks, kb = bi % kblocks;
+    const float *src = w + nb * 16 * k + kb * 256 + 4 * lane;
+    uint4 v[16];
+#pragma unroll
+    for (int r = 0; r < 16; r++) v[r] = load16_stream(src + r * k);
+    const double half = gamma[0] * 0.5;
+    const int q4 = lane % 4;
+    uint32_t word[16];
+#pragma unroll
+    for (int r = 0; r < 16; r++) {
+        const float e[4] = {__uint_as_float(v[r].x), __uint_as_float(v[r].y), __uint_as_float(v[r].z),
+                            __uint_as_float(v[r].w)};
+        uint32_t part = 0;
+#pragma unroll
+        for (int j = 0; j < 4; j++) part |= tern_field(e[j], half) << (8 * j + 2 * q4);
+        part |= (uint32_t)__shfl_xor((int)part, 1);
+        part |= (uint32_t)__shfl_xor((int)part, 2);
+        word[r] = part;
+    }
+    // lane 4 m (m = 4 g + t) holds word t of packed lane r + 16 g for every row r
+    uint32_t *b = blk[wave];
+    if (q4 == 0) {
+        const int g = lane / 16, t = (lane % 16) / 4;
+#pragma unroll
+        for (int r = 0; r < 16; r++) b[4 * (r + 16 * g) + t] = word[r];
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    const uint4 o = *reinterpret_cast<const uint4 *>(b + 4 * lane);
+    *reinterpret_cast<uint4 *>(packed + bi * 256 + 4 * lane) = o;
 }
 
 // One thread = one lane slice (4 words, 32 consecutive k of one column) of a
@@ -237,12 +284,13 @@ hipError_t launch_pack_ternary(const float *w, bool layout_nk, int64_t n, int64_
     hipLaunchKernelGGL(absmean_final_kernel, dim3(1), dim3(kFThreads), 0, st, partials, nparts,
                        count, eps, gamma);
     const int64_t nslices = (n / 16) * (k / 256) * 64;
-    if (layout_nk)
-        hipLaunchKernelGGL((pack_ternary_kernel<true>), dim3(blocks_for(nslices)), dim3(kPThreads),
-                           0, st, w, n, k, gamma, packed, nslices);
-    else
-        hipLaunchKernelGGL((pack_ternary_kernel<false>), dim3(blocks_for(nslices)), dim3(kPThreads),
-                           0, st, w, n, k, gamma, packed, nslices);
+    if (layout_nk) {
+        const int64_t nblocks = nslices / 64;
+        hipLaunchKernelGGL(pack_ternary_rows_kernel, dim3((unsigned)((nblocks + kTWaves - 1) / kTWaves)),
+                           dim3(kPThreads), 0, st, w, k, gamma, packed, nblocks);
+    } else
+        hipLaunchKernelGGL(pack_ternary_kn_kernel, dim3(blocks_for(nslices)), dim3(kPThreads), 0, st, w, n,
+                           k, gamma, packed, nslices);
     return hipGetLastError();
 }
 
