@@ -72,8 +72,9 @@ __device__ __forceinline__ v8h unpack_int4(uint32_t w, h2 zz) {
 template <int NBLK, int RB, bool SUB>
 struct Stage {
     uint4 w[NBLK];
-    // SUB: per 32-k step, the scale's fp16 bits | zero-point << 16.
-    uint32_t s[NBLK][SUB ? 4 : 1], z[NBLK];
+    // SUB: the scale's fp16 bits | zero-point << 16 of this lane's 32-k
+    // step lane / 16 (sub_scale_zero hands each lane the other steps').
+    uint32_t s[NBLK][1], z[NBLK];
     v8h a[RB][4];
 };
 
@@ -100,6 +101,21 @@ __device__ __forceinline__ uint32_t scale_zero(const uint16_t *__restrict__ scal
     return (uint32_t)scales[col * groups + g] | ((zw & 15u) << 16);
 }
 
+// Per-step scales of k block kbc, one load pair per lane: lane (fr, q)
+// loads the word of its column's 32-k step q (group gt[q]); at use, the
+// word of step t comes from lane fr + 16 t of the same column.
+__device__ __forceinline__ uint32_t lane_scale_zero(const uint16_t *__restrict__ scales,
+                                                    const uint32_t *__restrict__ packed_z, int64_t col,
+                                                    const int64_t (&gt)[4], int64_t groups, int64_t n, int lane) {
+    const int q = lane / 16;
+    const int64_t g = q == 0 ? gt[0] : q == 1 ? gt[1] : q == 2 ? gt[2] : gt[3];
+    return scale_zero(scales, packed_z, col, g, groups, n);
+}
+
+__device__ __forceinline__ uint32_t sub_scale_zero(uint32_t own, int t, int lane) {
+    return (uint32_t)__builtin_amdgcn_ds_bpermute(4 * (lane % 16 + 16 * t), (int)own);
+}
+
 // Issue every load of k block kb (clamped into range; the caller masks a
 // block past the end).  All loads are unconditional, so none of them waits
 // for another.
@@ -121,8 +137,7 @@ __device__ __forceinline__ void load_stage(Stage<NBLK, RB, SUB> &st, const uint1
             const int64_t nbc = nb0 + j < nblocks ? nb0 + j : nblocks - 1;
             const int64_t col = nbc * 16 + fr;
             st.w[j] = load16_stream(packed_w + (nbc * kblocks + kbc) * 256 + 4 * lane);
-#pragma unroll
-            for (int t = 0; t < 4; t++) st.s[j][t] = scale_zero(scales, packed_z, col, gt[t], groups, n);
+            st.s[j][0] = lane_scale_zero(scales, packed_z, col, gt, groups, n, lane);
         }
     } else {
         const int64_t g = kbc * 128 / group_size;
@@ -152,8 +167,8 @@ __device__ __forceinline__ void load_stage(Stage<NBLK, RB, SUB> &st, const uint1
 // group scale (SUB: per step, after the cross-row transpose of the words).
 template <int NBLK, int RB, bool SUB>
 __device__ __forceinline__ void block_mma(const v8h (&a)[RB][4], const uint4 (&w)[NBLK],
-                                          const uint32_t (&s)[NBLK][SUB ? 4 : 1], const uint32_t (&z)[NBLK],
-                                          v4f (&acc)[RB][NBLK], bool kb_ok, int64_t nb0, int64_t nblocks) {
+                                          const uint32_t (&s)[NBLK][1], const uint32_t (&z)[NBLK],
+                                          v4f (&acc)[RB][NBLK], bool kb_ok, int64_t nb0, int64_t nblocks, int lane) {
     if constexpr (SUB) {
 #pragma unroll
         for (int j = 0; j < NBLK; j++) {
@@ -161,7 +176,7 @@ __device__ __forceinline__ void block_mma(const v8h (&a)[RB][4], const uint4 (&w
             const uint4 wt = quad_transpose(w[j]);
 #pragma unroll
             for (int t = 0; t < 4; t++) {
-                const uint32_t sz = s[j][t];
+                const uint32_t sz = sub_scale_zero(s[j][0], t, lane);
                 const float sc = ok ? f16_bits_to_f32(sz & 0xffffu) : 0.0f;
                 const h2 zz = __builtin_bit_cast(h2, (0x6400u | ((sz >> 16) & 15u)) * 0x00010001u);
                 const v8h wv = unpack_int4(word_of(wt, t), zz);
@@ -204,7 +219,7 @@ __device__ __forceinline__ void compute_stage(const Stage<NBLK, RB, SUB> &st, v4
     v8h a[RB][4];
     if constexpr (SUB) rows256_to_subblock_fragments<RB>(st.a, a, xb, lane);
     else rows256_to_fragments<RB>(st.a, a, xb, lane);
-    block_mma<NBLK, RB, SUB>(a, st.w, st.s, st.z, acc, kb_ok, nb0, nblocks);
+    block_mma<NBLK, RB, SUB>(a, st.w, st.s, st.z, acc, kb_ok, nb0, nblocks, lane);
 }
 
 template <int NBLK, int WAVES, int RB, int OUT, int NST, bool SUB>
@@ -380,7 +395,7 @@ __global__ __launch_bounds__(WAVES * 64) void int4_grouped_dl_kernel(const uint1
     };
 
     uint4 w[NKB][NBLK];
-    uint32_t sc[NKB][NBLK][SUB ? 4 : 1], zr[NKB][NBLK];
+    uint32_t sc[NKB][NBLK][1], zr[NKB][NBLK];
     auto load_w = [&](int u) {
         const int64_t kb = kb_of(u), kbc = kb < kblocks ? kb : kblocks - 1;
 #pragma unroll
@@ -391,8 +406,7 @@ __global__ __launch_bounds__(WAVES * 64) void int4_grouped_dl_kernel(const uint1
             if constexpr (SUB) {
                 int64_t gt[4];
                 subblock_groups(kbc, group_size / 32, gt);
-#pragma unroll
-                for (int t = 0; t < 4; t++) sc[u][j][t] = scale_zero(scales, packed_z, col, gt[t], groups, n);
+                sc[u][j][0] = lane_scale_zero(scales, packed_z, col, gt, groups, n, lane);
                 zr[u][j] = 0;
             } else {
                 const int64_t g = kbc * 128 / group_size;
@@ -457,7 +471,7 @@ __global__ __launch_bounds__(WAVES * 64) void int4_grouped_dl_kernel(const uint1
                 : "v"(ad[0]), "v"(ad[1]), "v"(ad[2]), "v"(ad[3])
                 : "memory");
         }
-        block_mma<NBLK, RB, SUB>(a, w[u], sc[u], zr[u], acc, kb_of(u) < kblocks, nb0, nblocks);
+        block_mma<NBLK, RB, SUB>(a, w[u], sc[u], zr[u], acc, kb_of(u) < kblocks, nb0, nblocks, lane);
         if constexpr (u + 2 < NKB) {
             // every fragment of this buffer was read into registers above
             __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0)
@@ -515,7 +529,8 @@ hipError_t launch_cfg(const uint16_t *x, const uint32_t *packed_w, const uint16_
         }
     }
     // With two row blocks, four stages of x fragments do not fit beside the
-    // weights in registers, nor do four stages of per-step scales: those
+    // weights in registers; with per-step groups the all-in form fits but
+    // measured slower (m = 16, g = 32: 13.9 against 12.9 us).  Those
     // launches keep the two-stage pipeline.
     if constexpr (RB == 1 && !SUB) {
         if (k / 128 <= (int64_t)WAVES * kAllIn) {
@@ -577,8 +592,9 @@ __device__ __forceinline__ v4i weight_step(const uint4 &w, int s) {
 template <int NBLK, int RB, bool SUB>
 struct StageI8 {
     uint4 w[NBLK];
-    // SUB: per 32-k step, the scale's fp16 bits | zero-point << 16.
-    uint32_t s[NBLK][SUB ? 4 : 1], z[NBLK];
+    // SUB: the scale's fp16 bits | zero-point << 16 of this lane's 32-k
+    // step lane / 16 (sub_scale_zero hands each lane the other steps').
+    uint32_t s[NBLK][1], z[NBLK];
     v4i a[RB][2];
 };
 
@@ -600,8 +616,7 @@ __device__ __forceinline__ void load_stage_i8(StageI8<NBLK, RB, SUB> &st, const 
             const int64_t nbc = nb0 + j < nblocks ? nb0 + j : nblocks - 1;
             const int64_t col = nbc * 16 + fr;
             st.w[j] = load16_stream(packed_w + (nbc * kblocks + kbc) * 256 + 4 * lane);
-#pragma unroll
-            for (int t = 0; t < 4; t++) st.s[j][t] = scale_zero(scales, packed_z, col, gt[t], groups, n);
+            st.s[j][0] = lane_scale_zero(scales, packed_z, col, gt, groups, n, lane);
         }
     } else {
         const int64_t g = kbc * 128 / group_size;
@@ -696,7 +711,7 @@ __device__ __forceinline__ void compute_stage_i8(const StageI8<NBLK, RB, SUB> &s
             const uint4 wt = quad_transpose(st.w[j]);
 #pragma unroll
             for (int t = 0; t < 4; t++) {
-                const uint32_t sz = st.s[j][t];
+                const uint32_t sz = sub_scale_zero(st.s[j][0], t, lane);
                 const float sc = ok ? f16_bits_to_f32(sz & 0xffffu) : 0.0f;
                 const int z = (int)((sz >> 16) & 15u);
                 int lo, hi;
@@ -841,8 +856,8 @@ hipError_t launch_cfg_i8(const int8_t *xq, const float *pts, const uint32_t *pac
                          hipStream_t st, int64_t batch) {
     const int64_t nblocks = n / 16;
     dim3 grid((unsigned)((nblocks + NBLK - 1) / NBLK), (unsigned)((m + 16 * RB - 1) / (16 * RB)), (unsigned)batch);
-    // Four stages of per-step scales beside two row blocks of codes do not
-    // fit in registers: that launch keeps the two-stage pipeline.
+    // Per-step groups with two row blocks keep the two-stage pipeline: the
+    // all-in form fits (248 registers) but measured no faster.
     if (k / 128 <= (int64_t)WAVES * kAllIn && !(SUB && RB == 2))
         hipLaunchKernelGGL((int4_grouped_i8_kernel<NBLK, WAVES, RB, OUT, (SUB && RB == 2) ? 0 : kAllIn, SUB>), grid,
                            dim3(WAVES * 64), 0, st, xq, pts, packed_w, scales, packed_z, bias, group_size, m, n, k,
