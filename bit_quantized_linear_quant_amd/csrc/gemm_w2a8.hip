@@ -12,7 +12,7 @@
 // core sums matching terms.  The accumulator holds sum x*(code+1); the
 // epilogue subtracts the token's code sum: acc = sum x*code exactly.
 //
-// m >= 256: 256 x 128 tiles on v_mfma_i32_32x32x32_i8, eight waves in two
+// m >= 256: 128 x 256 tiles on v_mfma_i32_32x32x32_i8, eight waves in two
 //         phase-alternating groups; activation codes and packed weights
 //         streamed into LDS through a ring of 128-k slices; each lane takes
 //         its weight words from LDS in the order the 32x32x32 operand needs.
@@ -199,19 +199,23 @@ __global__ __launch_bounds__(kGThreads) void w2a8_gemm_kernel(const int8_t *__re
 // ---------------------------------------------------------------------------
 // m >= 256: large-tile GEMM
 // ---------------------------------------------------------------------------
-// A 512-thread workgroup owns a 256 x 128 output tile: eight waves, two per
-// SIMD (waves w and w + 4 share SIMD w % 4), each owning a 64 x 64 quarter
-// as 2 x 2 blocks of v_mfma_i32_32x32x32_i8 (the 16x16x64 form sustains
-// about 60% of the 32x32x32 rate on gfx950).  The k loop runs over 128-k
-// slices through a ring of four LDS stages.  Slice sl = 2 kb + hh holds
-// half hh of k block kb:
-//   * the activation codes of k 128 sl .. +127 (256 rows x 128 bytes, 32 KB)
+// A 512-thread workgroup owns a 128 x 256 output tile: eight waves, two per
+// SIMD (waves w and w + 4 share SIMD w % 4), each owning a 64 x 64 part
+// (2 x 4 of them) as 2 x 2 blocks of v_mfma_i32_32x32x32_i8 (the 16x16x64
+// form sustains about 60% of the 32x32x32 rate on gfx950).  The tile is
+// wide in n because the activation codes are the heavy operand: every
+// tile column re-reads them, while the 2-bit weights cost a quarter of a
+// byte per element.  The k loop runs over 128-k slices through a ring of
+// six LDS stages of 24 KB.  Slice sl = 2 kb + hh holds half hh of k block
+// kb:
+//   * the activation codes of k 128 sl .. +127 (128 rows x 128 bytes, 16 KB)
 //     go HBM -> LDS with global_load_lds_dwordx4; 16-byte chunk c of row r
 //     sits at chunk position c ^ ((r >> 1) & 7), so each 16 lanes of a
 //     fragment read (16 rows, two per bank group parity) fall in distinct
 //     bank groups;
-//   * packed lanes 32 hh .. 32 hh + 31 of each of the tile's eight fragment
-//     blocks (the k groups 2 hh and 2 hh + 1, 512 contiguous bytes each).
+//   * packed lanes 32 hh .. 32 hh + 31 of each of the tile's sixteen
+//     fragment blocks (the k groups 2 hh and 2 hh + 1, 512 contiguous bytes
+//     each), one 1 KB direct load per wave.
 // Step t (0..3) of a slice gives lane half h = lane / 32 the k group
 // g = 2 hh + h and the weight word t: for the A operand, the 16 codes of
 // chunk 4 h + t of its slice row (k = 256 kb + 64 g + 16 t); for B, word t of
@@ -220,25 +224,25 @@ __global__ __launch_bounds__(kGThreads) void w2a8_gemm_kernel(const int8_t *__re
 //
 // The groups of waves 0-3 and 4-7 run opposite phases of every slice: one
 // reads its fragments of the slice from LDS and issues its share of the
-// direct loads three slices ahead while the other unpacks its weight words
+// direct loads five slices ahead while the other unpacks its weight words
 // and issues its 16 matrix-core products, so the matrix cores of a SIMD
 // see a ready wave at every phase.  Two workgroup barriers per slice keep
 // the phases apart; the second group passes one extra barrier at the start
 // and the first group one at the end.  Before every barrier a wave waits
-// until at most two slices of its own loads are in flight: a slice has
+// until at most four slices of its own loads are in flight: a slice has
 // landed (every wave's loads) at the barrier before its first read, and
 // the ring is never overwritten while a partner still reads it.
-constexpr int XBM = 256, XBN = 128, XBK = 128;
+constexpr int XBM = 128, XBN = 256, XBK = 128;
 constexpr int kXGroupM = 4;
-constexpr int kXBuf = 4;                               // ring stages
+constexpr int kXBuf = 6;                               // ring stages
 constexpr int kXASlice = XBM * XBK;                    // bytes of activation codes per slice
 constexpr int kXBSlice = XBN / 16 * 512;               // bytes of packed weights per slice
 constexpr int kXStage = kXASlice + kXBSlice;
 constexpr int kPThreads = 512;
 constexpr int kPLoads = kXASlice / 1024 / (kPThreads / kWave);   // 1 KB A loads per wave per slice (4)
-static_assert(kXBSlice == 1024 * 4, "one 1 KB weight load for each of waves 0-3 per slice");
+static_assert(kXBSlice == 1024 * 8, "one 1 KB weight load for each wave per slice");
 
-// Bytes of LDS the epilogue of a 256 x 128 tile uses: the rows' code sums
+// Bytes of LDS the epilogue of a 128 x 256 tile uses: the rows' code sums
 // and scales, then a padded 64 x 64 output tile per wave.
 template <int OUT>
 constexpr int xepi_bytes() {
@@ -259,7 +263,7 @@ __global__ __launch_bounds__(kPThreads, 1) void w2a8_big_kernel(const int8_t *__
     __shared__ __attribute__((aligned(1024))) int8_t smem[SMEM];
     const int lane = threadIdx.x % kWave, wave = wave_id();
     const int group = wave / 4;
-    const int wm = wave % 4, wn = wave / 4;   // 4 x 2 quarters of 64 x 64
+    const int wm = wave % 2, wn = wave / 2;   // 2 x 4 quarters of 64 x 64
     int tm, tn;
     xcd_tile(blockIdx.x, tiles_m, tiles_n, kXGroupM, tm, tn);
     const int64_t m0 = (int64_t)tm * XBM, n0 = (int64_t)tn * XBN;
@@ -275,11 +279,11 @@ __global__ __launch_bounds__(kPThreads, 1) void w2a8_big_kernel(const int8_t *__
         const int64_t r = m0 + row < m ? m0 + row : m - 1;
         srca[ii] = xq + r * k + 16 * c;
     }
-    // Waves 0-3 load the weights: 32 lanes each in fragment blocks 2 wave
-    // and 2 wave + 1 of the tile (half hh of k block kb at byte 512 sl).
+    // Every wave loads weights: 32 lanes each in fragment blocks 2 wave and
+    // 2 wave + 1 of the tile (half hh of k block kb at byte 512 sl).
     const int8_t *srcb;
     {
-        const int blk = 2 * (wave % 4) + lane / 32;
+        const int blk = 2 * wave + lane / 32;
         const int64_t nb = n0 / 16 + blk < nblocks ? n0 / 16 + blk : nblocks - 1;
         srcb = reinterpret_cast<const int8_t *>(packed) + nb * (k / 256) * 1024 + 16 * (lane % 32);
     }
@@ -292,13 +296,10 @@ __global__ __launch_bounds__(kPThreads, 1) void w2a8_big_kernel(const int8_t *__
         int8_t *dst = smem + stage * kXStage;
 #pragma unroll
         for (int ii = 0; ii < kPLoads; ii++) lds_load16(srca[ii] + s * XBK, dst + 1024 * (kPLoads * wave + ii));
-        if (group == 0) lds_load16(srcb + s * 512, dst + kXASlice + 1024 * wave);
+        lds_load16(srcb + s * 512, dst + kXASlice + 1024 * wave);
     };
-    // at most two slices of this wave's loads in flight
-    auto wait_two = [&]() __attribute__((always_inline)) {
-        if (group == 0) wait_vmcnt<2 * (kPLoads + 1)>();
-        else wait_vmcnt<2 * kPLoads>();
-    };
+    // at most four slices of this wave's loads in flight
+    auto wait_two = [&]() __attribute__((always_inline)) { wait_vmcnt<(kXBuf - 2) * (kPLoads + 1)>(); };
 
     v16i acc[2][2];
 #pragma unroll
@@ -306,15 +307,14 @@ __global__ __launch_bounds__(kPThreads, 1) void w2a8_big_kernel(const int8_t *__
 #pragma unroll
         for (int j = 0; j < 2; j++) acc[i][j] = v16i{};
 
-    issue(0, 0);
-    issue(1, 1);
-    issue(2, 2);
+#pragma unroll
+    for (int i = 0; i < kXBuf - 1; i++) issue(i, i);
     if (group == 1) {
         wait_two();
         barrier_only();
     }
     for (int64_t sl = 0; sl < nsl; sl++) {
-        // fragment phase: this slice to registers, slice sl + 3 requested
+        // fragment phase: this slice to registers, slice sl + 5 requested
         wait_two();
         barrier_only();
         const int8_t *cur = smem + (int)(sl % kXBuf) * kXStage;
@@ -326,7 +326,7 @@ __global__ __launch_bounds__(kPThreads, 1) void w2a8_big_kernel(const int8_t *__
         for (int t = 0; t < 4; t++)
 #pragma unroll
             for (int i = 0; i < 2; i++) fa[t][i] = *reinterpret_cast<const v4i *>(cur + (aoff ^ (16 * t)) + i * 32 * XBK);
-        issue(sl + 3, (int)((sl + 3) % kXBuf));
+        issue(sl + kXBuf - 1, (int)((sl + kXBuf - 1) % kXBuf));
         __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0): the fragments are in registers
         wait_two();
         barrier_only();
@@ -675,7 +675,7 @@ hipError_t launch_out(const int8_t *xq, const float *pts, const int32_t *rowsum,
             return launch_gemv<7, 8, 1, 1, OUT, true>(xq, pts, rowsum, packed, gamma, bias, m, n, k, out, st);
         return launch_gemv<7, 8, 1, 1, OUT>(xq, pts, rowsum, packed, gamma, bias, m, n, k, out, st);
     }
-    if (m >= XBM) {
+    if (m >= 256) {
         const int tiles_m = (int)((m + XBM - 1) / XBM), tiles_n = (int)((n + XBN - 1) / XBN);
         hipLaunchKernelGGL((w2a8_big_kernel<OUT>), dim3((unsigned)(tiles_m * tiles_n)), dim3(kPThreads), 0, st, xq,
                            pts, rowsum, packed, gamma, bias, m, n, k, out, tiles_m, tiles_n);
