@@ -12,16 +12,13 @@
 // core sums matching terms.  The accumulator holds sum x*(code+1); the
 // epilogue subtracts the token's code sum: acc = sum x*code exactly.
 //
-// m >= 256: 128 x 256 tiles on v_mfma_i32_32x32x32_i8, eight waves in two
+// m > 64: 128 x 256 tiles on v_mfma_i32_32x32x32_i8, eight waves in two
 //         phase-alternating groups; activation codes and packed weights
 //         streamed into LDS through a ring of 128-k slices; each lane takes
 //         its weight words from LDS in the order the 32x32x32 operand needs.
-// 64 < m < 256: 128 x 128 tiles, 2 x 2 waves of 64 x 64 on 32x32x32, A
-//         staged in LDS per 256-k step (rows padded to 272 bytes), B loaded
-//         per wave straight into registers in the lane order that operand
-//         needs; except, for k >= 2048 and at most 1024 column blocks,
-//         m <= 96 (the decode kernel with six row blocks) and m <= 128 (two
-//         decode launches of 64 and m - 64 rows).
+//         Except, for k >= 2048 and at most 1024 column blocks, m <= 96 (the
+//         decode kernel with six row blocks) and m <= 128 (two decode
+//         launches of 64 and m - 64 rows).
 // m <= 64: decode GEMV.  The m rows fill one to four 16-row MFMA blocks
 //         (rows past m repeat row 0 and are never stored); each workgroup
 //         owns NBLK column blocks and its waves split k, each wave keeping two
@@ -74,130 +71,7 @@ __device__ __forceinline__ void stage_rows(const float *__restrict__ pts, const 
 }
 
 // ---------------------------------------------------------------------------
-// m > 16: tiled GEMM
-// ---------------------------------------------------------------------------
-constexpr int GBM = 128, GBN = 128, GBK = 256;
-constexpr int kGRow = GBK + 16;  // LDS row stride (bytes)
-constexpr int kGThreads = 256;
-
-// Wave (wm, wn) owns 64 x 64 as 2 x 2 blocks of v_mfma_i32_32x32x32_i8.
-// Step s = 4q + t of a 256-k block gives lane half h = lane / 32 the k group
-// g = 2q + h and word t: A chunk 4g + t of its row, and for B the 16 bytes
-// each lane loads from HBM are those of packed lane (column % 16) + 16 g of
-// the column's fragment block, whose word t is the matching operand.
-template <int OUT>
-__global__ __launch_bounds__(kGThreads) void w2a8_gemm_kernel(const int8_t *__restrict__ xq,
-                                                              const float *__restrict__ pts,
-                                                              const int32_t *__restrict__ rowsum,
-                                                              const uint32_t *__restrict__ packed,
-                                                              const double *__restrict__ gamma,
-                                                              const float *__restrict__ bias,
-                                                              int64_t m, int64_t n, int64_t k,
-                                                              void *__restrict__ out) {
-    __shared__ __attribute__((aligned(16))) int8_t As[GBM * kGRow];
-    const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
-    const int wm = wave / 2, wn = wave % 2;
-    const int h = lane / 32, fr = lane % 32;
-    const int64_t m0 = (int64_t)blockIdx.y * GBM;
-    const int64_t nbase = (int64_t)blockIdx.x * (GBN / 16) + wn * 4;  // first column block of the wave
-    const int64_t nblocks = n / 16, kblocks = k / GBK;
-
-    uint4 ra[8];
-    uint4 rb[2][2];   // [32-column block j][k-group pair q]
-    auto gload = [&](int64_t kb) {
-#pragma unroll
-        for (int c = 0; c < 8; c++) {
-            const int chunk = tid + c * kGThreads;
-            const int row = chunk / 16, c16 = chunk % 16;
-            const int64_t gr = m0 + row;
-            ra[c] = gr < m ? *reinterpret_cast<const uint4 *>(xq + gr * k + kb * GBK + 16 * c16)
-                           : make_uint4(0, 0, 0, 0);
-        }
-#pragma unroll
-        for (int j = 0; j < 2; j++) {
-            const int64_t nb = nbase + 2 * j + fr / 16;
-#pragma unroll
-            for (int q = 0; q < 2; q++)
-                rb[j][q] = nb < nblocks ? *reinterpret_cast<const uint4 *>(packed + (nb * kblocks + kb) * 256 +
-                                                                           4 * (fr % 16 + 16 * (2 * q + h)))
-                                        : make_uint4(0x55555555u, 0x55555555u, 0x55555555u, 0x55555555u);
-        }
-    };
-    auto sstore = [&]() {
-#pragma unroll
-        for (int c = 0; c < 8; c++) {
-            const int chunk = tid + c * kGThreads;
-            const int row = chunk / 16, c16 = chunk % 16;
-            *reinterpret_cast<uint4 *>(As + row * kGRow + 16 * c16) = ra[c];
-        }
-    };
-
-    v16i acc[2][2];
-#pragma unroll
-    for (int i = 0; i < 2; i++)
-#pragma unroll
-        for (int j = 0; j < 2; j++) acc[i][j] = v16i{};
-
-    gload(0);
-    sstore();
-    __syncthreads();
-    for (int64_t kb = 0; kb < kblocks; kb++) {
-        uint4 cb[2][2];
-#pragma unroll
-        for (int j = 0; j < 2; j++)
-#pragma unroll
-            for (int q = 0; q < 2; q++) cb[j][q] = rb[j][q];
-        if (kb + 1 < kblocks) gload(kb + 1);
-#pragma unroll
-        for (int q = 0; q < 2; q++)
-#pragma unroll
-            for (int t = 0; t < 4; t++) {
-                v4i a[2];
-#pragma unroll
-                for (int i = 0; i < 2; i++)
-                    a[i] = *reinterpret_cast<const v4i *>(As + (wm * 64 + i * 32 + fr) * kGRow +
-                                                          16 * (4 * (2 * q + h) + t));
-#pragma unroll
-                for (int j = 0; j < 2; j++) {
-                    const v4i b = unpack_tern(word_of(cb[j][q], t));
-#pragma unroll
-                    for (int i = 0; i < 2; i++)
-                        acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[i], b, acc[i][j], 0, 0, 0);
-                }
-            }
-        __syncthreads();
-        if (kb + 1 < kblocks) {
-            sstore();
-            __syncthreads();
-        }
-    }
-
-    int32_t *rs_lds = reinterpret_cast<int32_t *>(As);
-    float *pts_lds = reinterpret_cast<float *>(As) + GBM;
-    stage_rows<OUT>(pts, rowsum, m, m0, GBM, rs_lds, pts_lds);
-    __syncthreads();
-    const float g = OUT == OUT_I32 ? 0.0f : (float)gamma[0];  // gamma may be NULL for int32 output
-    // Lane l holds column l % 32 of each 32 x 32 block and rows
-    // 8 (r / 4) + 4 (l / 32) + r % 4 of register r.
-#pragma unroll
-    for (int j = 0; j < 2; j++) {
-        const int64_t col = (nbase + 2 * j) * 16 + fr;
-        if (col >= n) continue;
-        const float colb = (OUT != OUT_I32 && bias) ? bias[col] : 0.0f;
-#pragma unroll
-        for (int i = 0; i < 2; i++)
-#pragma unroll
-            for (int r = 0; r < 16; r++) {
-                const int local = wm * 64 + i * 32 + 8 * (r / 4) + 4 * h + r % 4;
-                if (m0 + local < m)
-                    epilogue_store<OUT>(out, (m0 + local) * n + col, acc[i][j][r], rs_lds[local],
-                                        OUT == OUT_I32 ? 0.0f : pts_lds[local], g, bias, colb);
-            }
-    }
-}
-
-// ---------------------------------------------------------------------------
-// m >= 256: large-tile GEMM
+// m > 64: large-tile GEMM
 // ---------------------------------------------------------------------------
 // A 512-thread workgroup owns a 128 x 256 output tile: eight waves, two per
 // SIMD (waves w and w + 4 share SIMD w % 4), each owning a 64 x 64 part
@@ -643,10 +517,14 @@ hipError_t launch_out(const int8_t *xq, const float *pts, const int32_t *rowsum,
             default: return launch_gemv_rows<4, OUT>(xq, pts, rowsum, packed, gamma, bias, m, n, k, out, st);
         }
     }
-    if (m > 96 && m <= 128 && k >= 2048 && n / 16 <= 1024) {
+    if (m > 96 && m <= 128 && k >= 2048 && n / 16 <= 768) {
         // Eight row blocks do not fit the decode kernel's registers; two
         // decode launches of 64 and m - 64 rows (each streaming the weights
-        // once) beat the 128x128 tiles while the columns are few enough.
+        // once) beat the 128 x 256 tiles while each launch's grid fits one
+        // round on the CUs (three column blocks per workgroup up to 768
+        // column blocks).  Measured at m = 112, k = 2048 / 4096 / 8192: n =
+        // 11008 13.9 / 20.5 / 34.0 us against 18.6 / 28.9 / 50.1 on the
+        // tiles; n = 16384 24.9 / 37.6 / 64.2 against 18.7 / 29.2 / 50.5.
         const hipError_t e = launch_out<OUT>(xq, pts, rowsum, packed, gamma, bias, 64, n, k, out, st);
         if (e != hipSuccess) return e;
         const int64_t es = OUT == OUT_I32 || OUT == OUT_F32 ? 4 : 2;   // output element bytes
@@ -657,7 +535,9 @@ hipError_t launch_out(const int8_t *xq, const float *pts, const int32_t *rowsum,
         // Five or six row blocks: four waves (their register budget holds the
         // stages), two column blocks per workgroup, x through LDS.  Eight row
         // blocks spill even with one column block.  Wider products (x
-        // re-read for every two column blocks) stay on the tiles.
+        // re-read for every two column blocks) stay on the tiles, although
+        // at m = 80 the decode kernel still led at 1024 column blocks (16.0
+        // against 18.6 us at k = 2048, 37.7-38.1 against 50.3 at k = 8192).
         return launch_gemv<2, 4, 1, 6, OUT, true>(xq, pts, rowsum, packed, gamma, bias, m, n, k, out, st);
     }
     if (m <= 16) {
@@ -675,15 +555,13 @@ hipError_t launch_out(const int8_t *xq, const float *pts, const int32_t *rowsum,
             return launch_gemv<7, 8, 1, 1, OUT, true>(xq, pts, rowsum, packed, gamma, bias, m, n, k, out, st);
         return launch_gemv<7, 8, 1, 1, OUT>(xq, pts, rowsum, packed, gamma, bias, m, n, k, out, st);
     }
-    if (m >= 256) {
-        const int tiles_m = (int)((m + XBM - 1) / XBM), tiles_n = (int)((n + XBN - 1) / XBN);
-        hipLaunchKernelGGL((w2a8_big_kernel<OUT>), dim3((unsigned)(tiles_m * tiles_n)), dim3(kPThreads), 0, st, xq,
-                           pts, rowsum, packed, gamma, bias, m, n, k, out, tiles_m, tiles_n);
-        return hipGetLastError();
-    }
-    dim3 grid((unsigned)((n + GBN - 1) / GBN), (unsigned)((m + GBM - 1) / GBM));
-    hipLaunchKernelGGL((w2a8_gemm_kernel<OUT>), grid, dim3(kGThreads), 0, st, xq, pts, rowsum, packed,
-                       gamma, bias, m, n, k, out);
+    // Everything else above 64 rows: the large tiles, also for 64 < m < 256
+    // (one or two tile rows), where they beat 128 x 128 tiles on four waves
+    // at every measured shape.
+    const int64_t tiles_m = (m + XBM - 1) / XBM, tiles_n = (n + XBN - 1) / XBN;
+    if (tiles_m * tiles_n > 0x7fffffff) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((w2a8_big_kernel<OUT>), dim3((unsigned)(tiles_m * tiles_n)), dim3(kPThreads), 0, st, xq, pts,
+                       rowsum, packed, gamma, bias, m, n, k, out, (int)tiles_m, (int)tiles_n);
     return hipGetLastError();
 }
 
@@ -692,7 +570,6 @@ hipError_t launch_out(const int8_t *xq, const float *pts, const int32_t *rowsum,
 hipError_t launch_gemm_w2a8(const int8_t *xq, const float *pts, const int32_t *rowsum,
                             const uint32_t *packed, const double *gamma, const float *bias, int64_t m,
                             int64_t n, int64_t k, int out_kind, void *out, hipStream_t st) {
-    if (m > (int64_t)GBM * 65535) return hipErrorInvalidValue;
     switch (out_kind) {
         case OUT_F16: return launch_out<OUT_F16>(xq, pts, rowsum, packed, gamma, bias, m, n, k, out, st);
         case OUT_BF16: return launch_out<OUT_BF16>(xq, pts, rowsum, packed, gamma, bias, m, n, k, out, st);

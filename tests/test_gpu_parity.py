@@ -349,10 +349,12 @@ W2A8_SHAPES = [(1, 400, 512), (2, 256, 768), (4, 400, 512), (5, 64, 256), (16, 4
                (12, 400, 2048), (20, 400, 2048), (33, 1008, 4096), (48, 6400, 2304), (64, 16400, 2048),
                # 64 < m <= 96 with k >= 2048: six row blocks on four waves
                (65, 400, 2048), (96, 1008, 2304),
-               # 96 < m <= 128, k >= 2048, at most 1024 column blocks: two decode launches
+               # 96 < m <= 128, k >= 2048, at most 768 column blocks: two decode launches
                (100, 400, 2048), (128, 1008, 4096),
-               # 64 < m <= 128, k >= 2048, more than 1024 column blocks: the 128x128 tiles
-               (96, 16400, 2048), (120, 16400, 2048),
+               # 64 < m <= 128 with more than 1024 column blocks or k < 2048: the 128x256 tiles
+               # (one tile row, ragged), also 128 < m < 256 (two tile rows)
+               (96, 16400, 2048), (120, 16400, 2048), (80, 400, 1024), (128, 272, 256), (65, 64, 512),
+               (200, 528, 768), (112, 13312, 2048),
                # 4 < m <= 16, 2048 <= k <= 8192: every k block of a wave loaded at the start
                (9, 1008, 8192), (16, 48, 2304), (5, 400, 4096)]
 
