@@ -113,8 +113,9 @@ constexpr int kXASlice = XBM * XBK;                    // bytes of activation co
 constexpr int kXBSlice = XBN / 16 * 512;               // bytes of packed weights per slice
 constexpr int kXStage = kXASlice + kXBSlice;
 constexpr int kPThreads = 512;
-constexpr int kPLoads = kXASlice / 1024 / (kPThreads / kWave);   // 1 KB A loads per wave per slice (4)
+constexpr int kPLoads = kXASlice / 1024 / (kPThreads / kWave);   // 1 KB A loads per wave per slice (2)
 static_assert(kXBSlice == 1024 * 8, "one 1 KB weight load for each wave per slice");
+static_assert(kPLoads == 2, "the A load layout below assumes two 1 KB loads per wave and slice");
 
 // Bytes of LDS the epilogue of a 128 x 256 tile uses: the rows' code sums
 // and scales, then a padded 64 x 64 output tile per wave.
@@ -143,8 +144,8 @@ __global__ __launch_bounds__(kPThreads, 1) void w2a8_big_kernel(const int8_t *__
     const int64_t m0 = (int64_t)tm * XBM, n0 = (int64_t)tn * XBN;
     const int64_t nsl = k / XBK, nblocks = n / 16;
 
-    // A load ii of this wave fills LDS bytes [1024 (4 wave + ii), +1024) of
-    // the slice: row 8 (4 wave + ii) + lane / 8, chunk position lane % 8.
+    // A load ii of this wave fills LDS bytes [1024 (2 wave + ii), +1024) of
+    // the slice: row 8 (2 wave + ii) + lane / 8, chunk position lane % 8.
     const int8_t *srca[kPLoads];
 #pragma unroll
     for (int ii = 0; ii < kPLoads; ii++) {
@@ -173,7 +174,7 @@ __global__ __launch_bounds__(kPThreads, 1) void w2a8_big_kernel(const int8_t *__
         lds_load16(srcb + s * 512, dst + kXASlice + 1024 * wave);
     };
     // at most four slices of this wave's loads in flight
-    auto wait_two = [&]() __attribute__((always_inline)) { wait_vmcnt<(kXBuf - 2) * (kPLoads + 1)>(); };
+    auto wait_ring = [&]() __attribute__((always_inline)) { wait_vmcnt<(kXBuf - 2) * (kPLoads + 1)>(); };
 
     v16i acc[2][2];
 #pragma unroll
@@ -184,12 +185,12 @@ __global__ __launch_bounds__(kPThreads, 1) void w2a8_big_kernel(const int8_t *__
 #pragma unroll
     for (int i = 0; i < kXBuf - 1; i++) issue(i, i);
     if (group == 1) {
-        wait_two();
+        wait_ring();
         barrier_only();
     }
     for (int64_t sl = 0; sl < nsl; sl++) {
         // fragment phase: this slice to registers, slice sl + 5 requested
-        wait_two();
+        wait_ring();
         barrier_only();
         const int8_t *cur = smem + (int)(sl % kXBuf) * kXStage;
         v4i fa[4][2];
@@ -202,7 +203,7 @@ __global__ __launch_bounds__(kPThreads, 1) void w2a8_big_kernel(const int8_t *__
             for (int i = 0; i < 2; i++) fa[t][i] = *reinterpret_cast<const v4i *>(cur + (aoff ^ (16 * t)) + i * 32 * XBK);
         issue(sl + kXBuf - 1, (int)((sl + kXBuf - 1) % kXBuf));
         __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0): the fragments are in registers
-        wait_two();
+        wait_ring();
         barrier_only();
         // product phase
 #pragma unroll
