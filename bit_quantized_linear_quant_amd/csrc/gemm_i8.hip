@@ -5,7 +5,9 @@
 // The int8 kernels share the epilogue:
 //
 // gemm_i8_big_kernel -- large products with [n][k] weights and k % 64 == 0
-//   (the 8192^3 A4W4 product).  A 512-thread workgroup owns a 256 x 256
+//   whose 256 x 256 tiles number at least 128 per launch (the 8192^3 A4W4
+//   product; fewer tiles leave compute units idle and the 128 x 128 kernel
+//   below is faster).  A 512-thread workgroup owns a 256 x 256
 //   output tile, each of its eight waves (two per SIMD) a 128 x 64 part
 //   held as 4 x 2 blocks of v_mfma_i32_32x32x32_i8; the two groups of four
 //   waves run opposite phases of every slice (fragment reads and loads
@@ -1357,9 +1359,14 @@ hipError_t launch_gemm_a4w4_tiles(const uint8_t *xa, const uint8_t *wb, const fl
     }
 }
 
-bool gemm_i8_uses_big_tiles(bool w_nk, int64_t m, int64_t n, int64_t k) {
-    return w_nk && (k % kBigBK) == 0 && m >= 2 * LB && n >= 2 * LB &&
-           ((m + LB - 1) / LB) * ((n + LB - 1) / LB) <= 0x7fffffff;
+// The large tiles need at least 128 of them per launch: measured with
+// [n][k] weights at k = 4096, us, 256 x 256 against 128 x 128 tiles:
+// 512x4096 56.5 / 40.6, 1024x4096 57.9 / 44.5, 2048x4096 62.2-63.2 /
+// 61.2 (128 tiles), 1024x11008 71.2-72.0 / 86.4 (172 tiles), 4096x4096
+// 84.4 / 120 (256 tiles).
+bool gemm_i8_uses_big_tiles(bool w_nk, int64_t m, int64_t n, int64_t k, int64_t batch) {
+    const int64_t tiles = ((m + LB - 1) / LB) * ((n + LB - 1) / LB);
+    return w_nk && (k % kBigBK) == 0 && m >= 2 * LB && n >= 2 * LB && tiles <= 0x7fffffff && tiles * batch >= 128;
 }
 
 hipError_t launch_gemm_i8(const GemmI8Args &a, hipStream_t st) {
@@ -1378,7 +1385,7 @@ hipError_t launch_gemm_i8(const GemmI8Args &a, hipStream_t st) {
         return a.epi == EPI_ROWCOL ? launch_gemv_kn_out<EPI_ROWCOL>(a.out_kind, p, batch, st)
                                    : launch_gemv_kn_out<EPI_SCALARS>(a.out_kind, p, batch, st);
     }
-    if (gemm_i8_uses_big_tiles(a.w_nk, a.m, a.n, a.k))
+    if (gemm_i8_uses_big_tiles(a.w_nk, a.m, a.n, a.k, batch))
         return a.epi == EPI_ROWCOL ? launch_big_out<EPI_ROWCOL>(a.out_kind, p, batch, st)
                                    : launch_big_out<EPI_SCALARS>(a.out_kind, p, batch, st);
     if (a.m > (int64_t)BM * 65535) return hipErrorInvalidValue;

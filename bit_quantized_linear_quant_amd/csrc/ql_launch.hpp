@@ -76,7 +76,7 @@ hipError_t launch_gemm_a4w4_tiles(const uint8_t *xa, const uint8_t *wb, const fl
 hipError_t launch_gemm_a4w4_packed(const uint8_t *xa, const uint8_t *wb, const float *sa, const float *sw, float eps,
                                    int64_t m, int64_t n, int64_t k, int out_kind, void *out, hipStream_t st);
 // True when the product runs on the 256 x 256 direct-to-LDS kernel.
-bool gemm_i8_uses_big_tiles(bool w_nk, int64_t m, int64_t n, int64_t k);
+bool gemm_i8_uses_big_tiles(bool w_nk, int64_t m, int64_t n, int64_t k, int64_t batch);
 
 // q4_backward.hip: Q4Linear backward (grad_x, grad_w, grad of scale_a).
 struct Q4BackwardArgs {

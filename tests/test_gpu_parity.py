@@ -59,9 +59,11 @@ W8A8_SHAPES = [
     (33, 50, 77, False),
     (256, 256, 64, True),
     (130, 131, 4096, True),
-    (512, 512, 64, True),      # 256 x 256 direct-to-LDS tiles from here on
+    (512, 512, 64, True),      # m, n >= 512 but fewer than 128 tiles of 256 x 256: 128 x 128 kernel
     (520, 777, 192, True),     # ragged m and n
     (1024, 768, 1024, True),
+    (2048, 4096, 64, True),    # at least 128 tiles of 256 x 256: the direct-to-LDS kernel
+    (2100, 4000, 128, True),   # the same, ragged m and n
     (700, 600, 120, True),     # k % 64 != 0: general kernel at large m, n
     (1, 400, 512, True),       # decode kernel from here on (m <= 16, [n][k], k % 64 == 0)
     (5, 270, 320, True),       # k blocks cut short, n % 16 != 0
@@ -164,7 +166,8 @@ def test_w8a8_deterministic():
 @pytest.mark.parametrize("batch,m,n,k,nk,per_batch_deq", [
     (3, 16, 128, 256, False, False),    # the per-token W8A8 workload, batched
     (4, 300, 270, 200, True, True),
-    (2, 520, 777, 192, True, False),    # 256 x 256 direct-to-LDS tiles
+    (2, 520, 777, 192, True, False),
+    (2, 2048, 2080, 64, True, True),    # 2 x 72 tiles of 256 x 256: the direct-to-LDS kernel
     (3, 512, 512, 128, True, True),
     (5, 77, 45, 77, True, True),        # byte loads
     (2, 33, 50, 77, False, False),
