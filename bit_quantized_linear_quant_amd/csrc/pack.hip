@@ -219,37 +219,51 @@ __global__ __launch_bounds__(kPThreads) void pack_ternary_rows_kernel(const floa
     *reinterpret_cast<uint4 *>(packed + bi * 256 + 4 * lane) = o;
 }
 
-// One thread = one lane slice (4 words, 32 consecutive k of one column) of a
-// 16-column x 128-k block.  Nibble p holds k-offset 2p (p < 4) or 2(p-4)+1.
+// One wave per 16-column x 128-k block (2 KB of codes, 1 KB of words).
+// Lane L loads 16 codes of column 8 i + L / 8 (i = 0, 1) at k 16 (L % 8)
+// of the block, so each load takes whole 128-byte row segments; those 16
+// codes are exactly words 2 (q % 2) and 2 (q % 2) + 1 (q = L % 8) of lane
+// slice column + 16 (q / 2), whose nibble p holds k-offset 2p (p < 4) or
+// 2(p-4)+1 within its 8 codes.  The words go through a wave-private LDS
+// block to one 16-byte store per lane.
 __global__ __launch_bounds__(kPThreads) void pack_int4_weight_kernel(const uint8_t *__restrict__ codes,
                                                                      int64_t k,
                                                                      uint32_t *__restrict__ packed,
-                                                                     int64_t nslices) {
-    const int64_t g = (int64_t)blockIdx.x * kPThreads + threadIdx.x;
-    if (g >= nslices) return;
-    const int64_t bi = g / 64;
-    const int l = (int)(g % 64);
+                                                                     int64_t nblocks) {
+    __shared__ uint32_t blk[kPThreads / kWave][256];
+    const int lane = threadIdx.x % kWave, wave = wave_id();
+    const int64_t bi = (int64_t)blockIdx.x * (kPThreads / kWave) + wave;
+    if (bi >= nblocks) return;
     const int64_t kblocks = k / 128;
     const int64_t nb = bi / kblocks, kb = bi % kblocks;
-    const int64_t col = nb * 16 + (l % 16);
-    const int64_t kbase = kb * 128 + 32 * (l / 16);
-    const uint4 *src = reinterpret_cast<const uint4 *>(codes + col * k + kbase);
-    const uint4 a = src[0], b = src[1];
-    const uint32_t in[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
-    uint32_t words[4];
+    const int q = lane % 8;
+    uint4 v[2];
 #pragma unroll
-    for (int t = 0; t < 4; t++) {
-        uint32_t wd = 0;
+    for (int i = 0; i < 2; i++)
+        v[i] = *reinterpret_cast<const uint4 *>(codes + (nb * 16 + 8 * i + lane / 8) * k + kb * 128 + 16 * q);
+    uint32_t *b = blk[wave];
 #pragma unroll
-        for (int off = 0; off < 8; off++) {
-            const uint32_t c = (in[2 * t + off / 4] >> (8 * (off % 4))) & 15u;
-            const int p = (off % 2 == 0) ? off / 2 : off / 2 + 4;
-            wd |= c << (4 * p);
+    for (int i = 0; i < 2; i++) {
+        const uint32_t in[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
+        uint32_t words[2];
+#pragma unroll
+        for (int h = 0; h < 2; h++) {
+            uint32_t wd = 0;
+#pragma unroll
+            for (int off = 0; off < 8; off++) {
+                const uint32_t c = (in[2 * h + off / 4] >> (8 * (off % 4))) & 15u;
+                const int p = (off % 2 == 0) ? off / 2 : off / 2 + 4;
+                wd |= c << (4 * p);
+            }
+            words[h] = wd;
         }
-        words[t] = wd;
+        const int col = 8 * i + lane / 8;
+        *reinterpret_cast<uint2 *>(b + 4 * (col + 16 * (q / 2)) + 2 * (q % 2)) = make_uint2(words[0], words[1]);
     }
-    *reinterpret_cast<uint4 *>(packed + bi * 256 + 4 * l) =
-        make_uint4(words[0], words[1], words[2], words[3]);
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    *reinterpret_cast<uint4 *>(packed + bi * 256 + 4 * lane) = *reinterpret_cast<const uint4 *>(b + 4 * lane);
 }
 
 __global__ __launch_bounds__(kPThreads) void pack_int4_zeros_kernel(const uint8_t *__restrict__ z,
@@ -313,9 +327,10 @@ hipError_t pack_ternary_scratch(double **partials) {
 
 hipError_t launch_pack_int4_weight(const uint8_t *codes, int64_t n, int64_t k, uint32_t *packed,
                                    hipStream_t st) {
-    const int64_t nslices = (n / 16) * (k / 128) * 64;
-    hipLaunchKernelGGL(pack_int4_weight_kernel, dim3(blocks_for(nslices)), dim3(kPThreads), 0, st,
-                       codes, k, packed, nslices);
+    const int64_t nblocks = (n / 16) * (k / 128);
+    constexpr int64_t per = kPThreads / kWave;
+    hipLaunchKernelGGL(pack_int4_weight_kernel, dim3((unsigned)((nblocks + per - 1) / per)), dim3(kPThreads), 0,
+                       st, codes, k, packed, nblocks);
     return hipGetLastError();
 }
 
