@@ -356,7 +356,7 @@ __global__ __launch_bounds__(WAVES * 64) void int4_grouped_dl_kernel(const uint1
     constexpr int XBUF = RB * 16 * 256;            // one k block of x for the row slice
     constexpr int XL = XBUF / 1024;                // direct loads per k block
     constexpr int NXB = NKB < 2 ? NKB : 2;         // x buffers per wave
-    constexpr int WL = NBLK * (SUB ? 9 : 3);       // weight, scale, zero loads per k block
+    constexpr int WL = NBLK * 3;                   // weight, scale and zero-point loads per k block
     constexpr int XS = WAVES * XBUF;
     constexpr int RED = WAVES * RB * NBLK * kWave * 16;
     static_assert(RED <= XS, "the partials reuse the first x buffer");
