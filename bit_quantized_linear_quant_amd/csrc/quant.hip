@@ -3,11 +3,13 @@
 // quant_act: per-token absmax int8 codes with an optional parameter-free
 // RMSNorm folded into the per-token scale ("Class BitLinear" forward steps
 // 1-2 and 5; "Common Attention Utilities" activation_quant).  Rows of up to
-// 8192 elements in whole 8-element chunks: one wave per row, the row held in
-// registers, all of a lane's loads in flight at once, wave64 shuffle
-// reductions only.  Other rows: one 256-thread workgroup per row, the row
-// read from HBM once and kept in registers (up to 8192 elements), wave
-// reductions combined through LDS.  Codes are written with 8-byte stores.
+// 8192 elements in whole 8-element chunks: two or four waves per row while
+// a launch has at most 16384 waves, else one, the row held in registers, all
+// of a lane's loads in flight at once, wave64 shuffle reductions (the wave
+// results of a split row combined through LDS).  Other rows: one 256-thread
+// workgroup per row, the row read from HBM once and kept in registers (up
+// to 8192 elements), wave reductions combined through LDS.  Codes are
+// written with 8-byte stores.
 //
 // quant_int4_tensor: per-tensor 4-bit codes of "Q4LinearFunction" forward,
 // q = clamp(rne(x / max(scale, eps)), -8, 7) with IEEE division.
@@ -163,6 +165,61 @@ __global__ __launch_bounds__(kQThreads) void quant_act_kernel(const void *__rest
     }
 }
 
+// One 8-element chunk as raw words (16 bytes for 16-bit kinds, 32 for fp32)
+// and its conversion to fp32, apart, so that a kernel can issue every chunk
+// load before it converts any: the scheduler would otherwise place the
+// first conversions, and the wait for their load, among the later loads.
+template <int K>
+__device__ __forceinline__ void load_chunk_raw(const void *row, int64_t ch, uint4 (&r)[2]) {
+    const uint4 *p = reinterpret_cast<const uint4 *>(static_cast<const char *>(row) + ch * 8 * (K == IN_F32 ? 4 : 2));
+    r[0] = p[0];
+    if constexpr (K == IN_F32) r[1] = p[1];
+}
+
+template <int K>
+__device__ __forceinline__ void chunk_to_f32(const uint4 (&r)[2], float v[8]) {
+    if constexpr (K == IN_F32) {
+        const uint32_t w[8] = {r[0].x, r[0].y, r[0].z, r[0].w, r[1].x, r[1].y, r[1].z, r[1].w};
+#pragma unroll
+        for (int j = 0; j < 8; j++) v[j] = __uint_as_float(w[j]);
+    } else {
+        const uint32_t w[4] = {r[0].x, r[0].y, r[0].z, r[0].w};
+#pragma unroll
+        for (int j = 0; j < 4; j++) {
+            if constexpr (K == IN_F16) {
+                v[2 * j] = f16_bits_to_f32(w[j] & 0xffffu);
+                v[2 * j + 1] = f16_bits_to_f32(w[j] >> 16);
+            } else {
+                v[2 * j] = __uint_as_float(w[j] << 16);
+                v[2 * j + 1] = __uint_as_float(w[j] & 0xffff0000u);
+            }
+        }
+    }
+}
+
+// The int8 codes of eight values packed into two words (element j in byte
+// j % 4 of lo (j < 4) or hi), and rs plus their sum.  The code of v is
+// clamp(rint(fl(v * s)), -128, 127): clamping first (the bounds are
+// integers) and adding 1.5 * 2^23 rounds the value to an integer, ties to
+// even, in the low mantissa bits, so the word is 0x4B400000 + code, whose low
+// byte is the code's byte.  The sum is a 4-way signed byte dot product of the
+// packed codes with ones.
+__device__ __forceinline__ int pack_codes8(const float (&v)[8], float s, int rs, uint32_t &lo, uint32_t &hi) {
+    constexpr float kRound = 12582912.0f;
+    uint32_t y[8];
+#pragma unroll
+    for (int j = 0; j < 8; j++) {
+        const float t = fminf(fmaxf(__fmul_rn(v[j], s), -128.0f), 127.0f);
+        y[j] = __float_as_uint(__fadd_rn(t, kRound));
+    }
+    lo = __builtin_amdgcn_perm(__builtin_amdgcn_perm(y[3], y[2], 0x0c0c0400u),
+                               __builtin_amdgcn_perm(y[1], y[0], 0x0c0c0400u), 0x05040100u);
+    hi = __builtin_amdgcn_perm(__builtin_amdgcn_perm(y[7], y[6], 0x0c0c0400u),
+                               __builtin_amdgcn_perm(y[5], y[4], 0x0c0c0400u), 0x05040100u);
+    rs = __builtin_amdgcn_sdot4((int)lo, 0x01010101, rs, false);
+    return __builtin_amdgcn_sdot4((int)hi, 0x01010101, rs, false);
+}
+
 // One wave per token row for rows of at most 64 * NCH whole 8-element
 // chunks: lane l holds chunks l, l + 64, ... in registers.  Every load is
 // unconditional (a chunk index past the row is clamped to the last chunk and
@@ -186,12 +243,16 @@ __global__ __launch_bounds__(kQWaveRows * kWave) void quant_act_wave_kernel(cons
     int8_t *qr = q + row * k;
     const int64_t nchunk = k / 8;
 
-    float v[NCH][8];
+    uint4 raw[NCH][2];
 #pragma unroll
     for (int c = 0; c < NCH; c++) {
         const int64_t ch = (int64_t)c * kWave + lane;
-        load8_vec<K>(xr, (ch < nchunk ? ch : nchunk - 1) * 8, v[c]);
+        load_chunk_raw<K>(xr, FULL || ch < nchunk ? ch : nchunk - 1, raw[c]);
     }
+    __builtin_amdgcn_sched_barrier(0);
+    float v[NCH][8];
+#pragma unroll
+    for (int c = 0; c < NCH; c++) chunk_to_f32<K>(raw[c], v[c]);
     float amax = 0.0f, ss = 0.0f;
 #pragma unroll
     for (int c = 0; c < NCH; c++) {
@@ -210,35 +271,101 @@ __global__ __launch_bounds__(kQWaveRows * kWave) void quant_act_wave_kernel(cons
     float r, ap;
     guarded_absmax<RMS>(amax, ss, k, eps_norm, eps_q, r, ap);
     const float s = __fdiv_rn(127.0f, ap);
-    // The code of v is clamp(rint(fl(v * s)), -128, 127).  Clamping first
-    // (the bounds are integers) and adding 1.5 * 2^23 rounds the value to an
-    // integer, ties to even, in the low mantissa bits: the word is
-    // 0x4B400000 + code, whose low byte is the code's byte.  The code sum is
-    // a 4-way signed byte dot product of the packed codes with ones.
-    constexpr float kRound = 12582912.0f;
     int rs = 0;
 #pragma unroll
     for (int c = 0; c < NCH; c++) {
         const int64_t ch = (int64_t)c * kWave + lane;
-        uint32_t y[8];
-#pragma unroll
-        for (int j = 0; j < 8; j++) {
-            const float t = fminf(fmaxf(__fmul_rn(v[c][j], s), -128.0f), 127.0f);
-            y[j] = __float_as_uint(__fadd_rn(t, kRound));
-        }
-        // bytes 0 of y[0..3] and y[4..7]
-        const uint32_t lo = __builtin_amdgcn_perm(__builtin_amdgcn_perm(y[3], y[2], 0x0c0c0400u),
-                                                  __builtin_amdgcn_perm(y[1], y[0], 0x0c0c0400u), 0x05040100u);
-        const uint32_t hi = __builtin_amdgcn_perm(__builtin_amdgcn_perm(y[7], y[6], 0x0c0c0400u),
-                                                  __builtin_amdgcn_perm(y[5], y[4], 0x0c0c0400u), 0x05040100u);
-        rs = __builtin_amdgcn_sdot4((int)lo, 0x01010101, rs, false);
-        rs = __builtin_amdgcn_sdot4((int)hi, 0x01010101, rs, false);
+        uint32_t lo, hi;
+        rs = pack_codes8(v[c], s, rs, lo, hi);
         if (FULL || ch < nchunk) *reinterpret_cast<uint2 *>(qr + ch * 8) = make_uint2(lo, hi);
     }
     rs = wave_sum(rs);
     if (lane == 0) {
         pts[row] = RMS ? __fdiv_rn(__fmul_rn(ap, r), 127.0f) : __fdiv_rn(ap, 127.0f);
         if (rowsum) rowsum[row] = rs;
+    }
+}
+
+// W waves per token row (W = 2 or 4), for the same rows as the wave kernel
+// when a launch leaves room for more waves: wave w holds chunks
+// 64 (w NCH + c) + l, c < NCH, so a row's loads are spread over W waves and
+// each wave's share of the code step, which follows the last of its loads,
+// is 1 / W of the row's.  The W wave results of absmax and the sum of
+// squares are combined through LDS in wave order, the code sums likewise;
+// codes and code sums are those of the one-wave kernel (absmax is exact),
+// the sum of squares is added in another order.
+template <int K, int NCH, int W, bool RMS, bool FULL>
+__global__ __launch_bounds__(W * kWave) void quant_act_split_kernel(const void *__restrict__ x, int64_t k,
+                                                                    float eps_norm, float eps_q,
+                                                                    int8_t *__restrict__ q,
+                                                                    float *__restrict__ pts,
+                                                                    int32_t *__restrict__ rowsum) {
+    __shared__ float red_a[W], red_s[W];
+    __shared__ int red_r[W];
+    const int lane = threadIdx.x % kWave, w = wave_id();
+    const int64_t row = blockIdx.x;
+    const int esz = K == IN_F32 ? 4 : 2;
+    const void *xr = static_cast<const char *>(x) + row * k * esz;
+    int8_t *qr = q + row * k;
+    const int64_t nchunk = k / 8;
+
+    uint4 raw[NCH][2];
+#pragma unroll
+    for (int c = 0; c < NCH; c++) {
+        const int64_t ch = (int64_t)(w * NCH + c) * kWave + lane;
+        load_chunk_raw<K>(xr, FULL || ch < nchunk ? ch : nchunk - 1, raw[c]);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    float v[NCH][8];
+#pragma unroll
+    for (int c = 0; c < NCH; c++) chunk_to_f32<K>(raw[c], v[c]);
+    float amax = 0.0f, ss = 0.0f;
+#pragma unroll
+    for (int c = 0; c < NCH; c++) {
+        const bool in = FULL || (int64_t)(w * NCH + c) * kWave + lane < nchunk;
+#pragma unroll
+        for (int j = 0; j < 8; j++) {
+            const float e = in ? v[c][j] : 0.0f;
+            v[c][j] = e;
+            amax = fmaxf(amax, fabsf(e));
+            if (RMS) ss += e * e;
+        }
+    }
+    amax = wave_max(amax);
+    if (RMS) ss = wave_sum(ss);
+    if (lane == 0) {
+        red_a[w] = amax;
+        red_s[w] = ss;
+    }
+    __syncthreads();
+    amax = red_a[0];
+    ss = red_s[0];
+#pragma unroll
+    for (int i = 1; i < W; i++) {
+        amax = fmaxf(amax, red_a[i]);
+        ss += red_s[i];
+    }
+
+    float r, ap;
+    guarded_absmax<RMS>(amax, ss, k, eps_norm, eps_q, r, ap);
+    const float s = __fdiv_rn(127.0f, ap);
+    int rs = 0;
+#pragma unroll
+    for (int c = 0; c < NCH; c++) {
+        const int64_t ch = (int64_t)(w * NCH + c) * kWave + lane;
+        uint32_t lo, hi;
+        rs = pack_codes8(v[c], s, rs, lo, hi);
+        if (FULL || ch < nchunk) *reinterpret_cast<uint2 *>(qr + ch * 8) = make_uint2(lo, hi);
+    }
+    rs = wave_sum(rs);
+    if (lane == 0) red_r[w] = rs;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        int t = red_r[0];
+#pragma unroll
+        for (int i = 1; i < W; i++) t += red_r[i];
+        pts[row] = RMS ? __fdiv_rn(__fmul_rn(ap, r), 127.0f) : __fdiv_rn(ap, 127.0f);
+        if (rowsum) rowsum[row] = t;
     }
 }
 
@@ -259,11 +386,46 @@ hipError_t launch_wave_rows(bool rms, const void *x, int64_t m, int64_t k, float
 
 // Rows of whole 8-element chunks up to 8192 elements take the wave-per-row
 // kernel, sized to the row; anything else the workgroup-per-row kernel.
+template <int K, int W, int NCH>
+hipError_t launch_split_rows(bool rms, const void *x, int64_t m, int64_t k, float eps_norm, float eps_q,
+                             int8_t *q, float *pts, int32_t *rowsum, hipStream_t st) {
+    const bool full = k == (int64_t)W * NCH * kWave * 8;
+    auto go = [&](auto kern) {
+        hipLaunchKernelGGL(kern, dim3((unsigned)m), dim3(W * kWave), 0, st, x, k, eps_norm, eps_q, q, pts, rowsum);
+    };
+    if (rms) full ? go(quant_act_split_kernel<K, NCH, W, true, true>) : go(quant_act_split_kernel<K, NCH, W, true, false>);
+    else full ? go(quant_act_split_kernel<K, NCH, W, false, true>) : go(quant_act_split_kernel<K, NCH, W, false, false>);
+    return hipGetLastError();
+}
+
+// W waves per row while the launch has at most 16384 waves (16 per SIMD).
+// Measured on MI355X, bf16 rows of 4096 with RMSNorm, us per graph-replayed
+// launch for W = 1 / 2 / 4 / 8: 512 rows 4.12 / 3.91 / 3.69 / 3.95, 2048
+// rows 7.60-7.64 / 7.18-7.27 / 7.07-7.09 / 9.33, 8192 rows 19.1-19.3 /
+// 18.6-18.8 / 19.8-20.1 / 27.7-28.0.
+template <int K, int W>
+hipError_t launch_split_w(int64_t per_lane, bool rms, const void *x, int64_t m, int64_t k, float eps_norm,
+                          float eps_q, int8_t *q, float *pts, int32_t *rowsum, hipStream_t st) {
+    const int64_t nch = (per_lane + W - 1) / W;
+    if (nch <= 1) return launch_split_rows<K, W, 1>(rms, x, m, k, eps_norm, eps_q, q, pts, rowsum, st);
+    if (nch <= 2) return launch_split_rows<K, W, 2>(rms, x, m, k, eps_norm, eps_q, q, pts, rowsum, st);
+    if (nch <= 4) return launch_split_rows<K, W, 4>(rms, x, m, k, eps_norm, eps_q, q, pts, rowsum, st);
+    return launch_split_rows<K, W, 8>(rms, x, m, k, eps_norm, eps_q, q, pts, rowsum, st);
+}
+
 template <int K>
 bool try_wave_rows(hipError_t &err, bool rms, const void *x, int64_t m, int64_t k, float eps_norm,
                    float eps_q, int8_t *q, float *pts, int32_t *rowsum, hipStream_t st) {
     if (k % 8 != 0 || k > 8192) return false;
     const int64_t per_lane = (k / 8 + kWave - 1) / kWave;
+    if (per_lane >= 4 && m <= 16384 / 4) {
+        err = launch_split_w<K, 4>(per_lane, rms, x, m, k, eps_norm, eps_q, q, pts, rowsum, st);
+        return true;
+    }
+    if (per_lane >= 2 && m <= 16384 / 2) {
+        err = launch_split_w<K, 2>(per_lane, rms, x, m, k, eps_norm, eps_q, q, pts, rowsum, st);
+        return true;
+    }
     if (per_lane <= 2) err = launch_wave_rows<K, 2>(rms, x, m, k, eps_norm, eps_q, q, pts, rowsum, st);
     else if (per_lane <= 4) err = launch_wave_rows<K, 4>(rms, x, m, k, eps_norm, eps_q, q, pts, rowsum, st);
     else if (per_lane <= 8) err = launch_wave_rows<K, 8>(rms, x, m, k, eps_norm, eps_q, q, pts, rowsum, st);

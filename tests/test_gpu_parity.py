@@ -205,7 +205,11 @@ def test_w8a8_batched_parity(batch, m, n, k, nk, per_batch_deq):
 # ---------------------------------------------------------------------------
 # Per-token activation quantization
 # ---------------------------------------------------------------------------
-QUANT_SHAPES = [(1, 8192), (16, 8192), (7, 4097), (33, 77), (5, 1), (3, 20000), (64, 4096), (2, 8)]
+# (rows of whole 8-element chunks up to 8192 run W = 4, 2 or 1 waves per row
+# by the launch's size; the ragged ones leave a split row's last waves
+# partly or wholly past the row)
+QUANT_SHAPES = [(1, 8192), (16, 8192), (7, 4097), (33, 77), (5, 1), (3, 20000), (64, 4096), (2, 8),
+                (40, 1000), (9, 2056), (3, 6144)]
 
 
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16, torch.float32])
@@ -219,6 +223,23 @@ def test_quant_act_parity(dtype, rms, m, k):
     rs = poison((m,), torch.int32)
     ql.qlinear_quant_act(_cuda(x), rmsnorm=rms, eps_norm=1e-6, eps_q=1e-5, q=q, per_token_scale=pts,
                          rowsum=rs)
+    _sync()
+    assert_equal(q, q_ref, "codes")
+    assert_equal(rs, rs_ref, "rowsum")
+    if rms:
+        np.testing.assert_allclose(to_np(pts).astype(np.float64), pts_ref.astype(np.float64),
+                                   rtol=rms_pts_rel_tol(k), atol=0)
+    else:
+        assert_equal(pts, pts_ref, "per-token scale")
+
+
+@pytest.mark.parametrize("rms", [False, True])
+@pytest.mark.parametrize("m,k", [(4096, 4096), (4097, 4096), (5000, 2048), (8193, 1024), (8192, 1024)])
+def test_quant_act_split_routes(rms, m, k):
+    """Launch sizes around the switch from four to two to one waves per row."""
+    x = synthetic.activations(m, k, seed=250 + m + k, outliers=0.01, dtype=torch.bfloat16)
+    q_ref, pts_ref, rs_ref = oracle.quant_act(x.float().numpy(), rmsnorm=rms, eps_norm=1e-6, eps_q=1e-5)
+    q, pts, rs = ql.qlinear_quant_act(_cuda(x), rmsnorm=rms, eps_norm=1e-6, eps_q=1e-5)
     _sync()
     assert_equal(q, q_ref, "codes")
     assert_equal(rs, rs_ref, "rowsum")
