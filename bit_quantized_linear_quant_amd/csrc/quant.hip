@@ -3,8 +3,9 @@
 // quant_act: per-token absmax int8 codes with an optional parameter-free
 // RMSNorm folded into the per-token scale ("Class BitLinear" forward steps
 // 1-2 and 5; "Common Attention Utilities" activation_quant).  Rows of up to
-// 8192 elements in whole 8-element chunks: two or four waves per row while
-// a launch has at most 16384 waves, else one, the row held in registers, all
+// 8192 elements in whole 8-element chunks: rows of more than 3584 elements
+// take two or four waves per row while a launch has at most 16384 waves,
+// others one, the row held in registers, all
 // of a lane's loads in flight at once, wave64 shuffle reductions (the wave
 // results of a split row combined through LDS).  Other rows: one 256-thread
 // workgroup per row, the row read from HBM once and kept in registers (up
@@ -243,16 +244,12 @@ __global__ __launch_bounds__(kQWaveRows * kWave) void quant_act_wave_kernel(cons
     int8_t *qr = q + row * k;
     const int64_t nchunk = k / 8;
 
-    uint4 raw[NCH][2];
+    float v[NCH][8];
 #pragma unroll
     for (int c = 0; c < NCH; c++) {
         const int64_t ch = (int64_t)c * kWave + lane;
-        load_chunk_raw<K>(xr, FULL || ch < nchunk ? ch : nchunk - 1, raw[c]);
+        load8_vec<K>(xr, (ch < nchunk ? ch : nchunk - 1) * 8, v[c]);
     }
-    __builtin_amdgcn_sched_barrier(0);
-    float v[NCH][8];
-#pragma unroll
-    for (int c = 0; c < NCH; c++) chunk_to_f32<K>(raw[c], v[c]);
     float amax = 0.0f, ss = 0.0f;
 #pragma unroll
     for (int c = 0; c < NCH; c++) {
@@ -398,11 +395,16 @@ hipError_t launch_split_rows(bool rms, const void *x, int64_t m, int64_t k, floa
     return hipGetLastError();
 }
 
-// W waves per row while the launch has at most 16384 waves (16 per SIMD).
-// Measured on MI355X, bf16 rows of 4096 with RMSNorm, us per graph-replayed
-// launch for W = 1 / 2 / 4 / 8: 512 rows 4.12 / 3.91 / 3.69 / 3.95, 2048
-// rows 7.60-7.64 / 7.18-7.27 / 7.07-7.09 / 9.33, 8192 rows 19.1-19.3 /
-// 18.6-18.8 / 19.8-20.1 / 27.7-28.0.
+// W waves per row for rows of more than 3584 elements (at least eight chunks
+// per lane with one wave) while the launch has at most 16384 waves (16 per
+// SIMD).  Measured on MI355X, bf16 with RMSNorm, us per graph-replayed
+// launch for W = 1 / 2 / 4 / 8: rows of 4096: 512 rows 4.12 / 3.91 / 3.69
+// / 3.95, 2048 rows 7.60-7.64 / 7.18-7.27 / 7.07-7.09 / 9.33, 8192 rows
+// 19.1-19.3 / 18.6-18.8 / 19.8-20.1 / 27.7-28.0; rows of 8192 (W = 4): 1 /
+// 16 / 256 / 2048 rows 3.6 / 4.1 / 5.2 / 12.4 -> 2.5 / 2.8 / 3.8 / 11.0.
+// Shorter rows stay on one wave: 4096 rows of 2048 6.85 with W = 1 against
+// 7.26 with W = 2 and 9.0 with W = 4; 1024 rows of 1024 2.99 against 3.27
+// with W = 2.
 template <int K, int W>
 hipError_t launch_split_w(int64_t per_lane, bool rms, const void *x, int64_t m, int64_t k, float eps_norm,
                           float eps_q, int8_t *q, float *pts, int32_t *rowsum, hipStream_t st) {
@@ -418,11 +420,11 @@ bool try_wave_rows(hipError_t &err, bool rms, const void *x, int64_t m, int64_t 
                    float eps_q, int8_t *q, float *pts, int32_t *rowsum, hipStream_t st) {
     if (k % 8 != 0 || k > 8192) return false;
     const int64_t per_lane = (k / 8 + kWave - 1) / kWave;
-    if (per_lane >= 4 && m <= 16384 / 4) {
+    if (per_lane >= 8 && m <= 16384 / 4) {
         err = launch_split_w<K, 4>(per_lane, rms, x, m, k, eps_norm, eps_q, q, pts, rowsum, st);
         return true;
     }
-    if (per_lane >= 2 && m <= 16384 / 2) {
+    if (per_lane >= 8 && m <= 16384 / 2) {
         err = launch_split_w<K, 2>(per_lane, rms, x, m, k, eps_norm, eps_q, q, pts, rowsum, st);
         return true;
     }

@@ -234,7 +234,7 @@ def test_quant_act_parity(dtype, rms, m, k):
 
 
 @pytest.mark.parametrize("rms", [False, True])
-@pytest.mark.parametrize("m,k", [(4096, 4096), (4097, 4096), (5000, 2048), (8193, 1024), (8192, 1024)])
+@pytest.mark.parametrize("m,k", [(4096, 4096), (4097, 4096), (4096, 3592), (8192, 4096), (8193, 4096), (4096, 3584), (5000, 8192)])
 def test_quant_act_split_routes(rms, m, k):
     """Launch sizes around the switch from four to two to one waves per row."""
     x = synthetic.activations(m, k, seed=250 + m + k, outliers=0.01, dtype=torch.bfloat16)
