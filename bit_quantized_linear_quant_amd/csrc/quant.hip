@@ -283,8 +283,9 @@ __global__ __launch_bounds__(kQWaveRows * kWave) void quant_act_wave_kernel(cons
     }
 }
 
-// W waves per token row (W = 2 or 4), for the same rows as the wave kernel
-// when a launch leaves room for more waves: wave w holds chunks
+// W waves per token row (W = 2 or 4), for rows the wave kernel would hold
+// as at least eight chunks per lane when a launch leaves room for more
+// waves: wave w holds chunks
 // 64 (w NCH + c) + l, c < NCH, so a row's loads are spread over W waves and
 // each wave's share of the code step, which follows the last of its loads,
 // is 1 / W of the row's.  The W wave results of absmax and the sum of
