@@ -356,7 +356,10 @@ __global__ __launch_bounds__(WAVES * 64) void int4_grouped_dl_kernel(const uint1
     constexpr int XBUF = RB * 16 * 256;            // one k block of x for the row slice
     constexpr int XL = XBUF / 1024;                // direct loads per k block
     constexpr int NXB = NKB < 2 ? NKB : 2;         // x buffers per wave
-    constexpr int WL = NBLK * 3;                   // weight, scale and zero-point loads per k block
+    // loads per k block after the first: the weights, and with per-step
+    // groups a scale and zero-point pair per column block (block 0 also
+    // loads the pairs of the other blocks' groups of 128 k or more)
+    constexpr int WL = SUB ? NBLK * 3 : NBLK;
     constexpr int XS = WAVES * XBUF;
     constexpr int RED = WAVES * RB * NBLK * kWave * 16;
     static_assert(RED <= XS, "the partials reuse the first x buffer");
@@ -396,6 +399,11 @@ __global__ __launch_bounds__(WAVES * 64) void int4_grouped_dl_kernel(const uint1
 
     uint4 w[NKB][NBLK];
     uint32_t sc[NKB][NBLK][1], zr[NKB][NBLK];
+    // Groups of 128 k or more: lane (fr, q) loads, with block 0's weights,
+    // the scale and zero-point of its column for the wave's k block q (one
+    // load pair per column block instead of one per k block); block u takes
+    // them from lane fr + 16 u of the same column.
+    uint32_t szl[NBLK];
     auto load_w = [&](int u) {
         const int64_t kb = kb_of(u), kbc = kb < kblocks ? kb : kblocks - 1;
 #pragma unroll
@@ -408,10 +416,10 @@ __global__ __launch_bounds__(WAVES * 64) void int4_grouped_dl_kernel(const uint1
                 subblock_groups(kbc, group_size / 32, gt);
                 sc[u][j][0] = lane_scale_zero(scales, packed_z, col, gt, groups, n, lane);
                 zr[u][j] = 0;
-            } else {
-                const int64_t g = kbc * 128 / group_size;
-                sc[u][j][0] = scales[col * groups + g];
-                zr[u][j] = packed_z[g * (n / 8) + col / 8] >> (4 * (col % 8));
+            } else if (u == 0) {
+                const int uq = q < NKB ? q : NKB - 1;
+                const int64_t kq = kb_of(uq), kqc = kq < kblocks ? kq : kblocks - 1;
+                szl[j] = scale_zero(scales, packed_z, col, kqc * 128 / group_size, groups, n);
             }
         }
     };
@@ -470,6 +478,14 @@ __global__ __launch_bounds__(WAVES * 64) void int4_grouped_dl_kernel(const uint1
                 : "=v"(a[b][0]), "=v"(a[b][1]), "=v"(a[b][2]), "=v"(a[b][3])
                 : "v"(ad[0]), "v"(ad[1]), "v"(ad[2]), "v"(ad[3])
                 : "memory");
+        }
+        if constexpr (!SUB) {
+#pragma unroll
+            for (int j = 0; j < NBLK; j++) {
+                const uint32_t sz = sub_scale_zero(szl[j], u, lane);
+                sc[u][j][0] = sz & 0xffffu;
+                zr[u][j] = sz >> 16;
+            }
         }
         block_mma<NBLK, RB, SUB>(a, w[u], sc[u], zr[u], acc, kb_of(u) < kblocks, nb0, nblocks, lane);
         if constexpr (u + 2 < NKB) {
