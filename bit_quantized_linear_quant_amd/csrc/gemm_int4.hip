@@ -614,7 +614,9 @@ struct StageI8 {
     v4i a[RB][2];
 };
 
-template <int NBLK, int RB, bool SUB>
+// SZ = false: the scales and zero-points of groups of 128 k or more are not
+// loaded here (the caller shares one pair per column block and lane).
+template <int NBLK, int RB, bool SUB, bool SZ = true>
 __device__ __forceinline__ void load_stage_i8(StageI8<NBLK, RB, SUB> &st, const int8_t *__restrict__ xq,
                                               int64_t row0, int64_t m, int64_t k,
                                               const uint32_t *__restrict__ packed_w,
@@ -641,8 +643,10 @@ __device__ __forceinline__ void load_stage_i8(StageI8<NBLK, RB, SUB> &st, const 
             const int64_t nbc = nb0 + j < nblocks ? nb0 + j : nblocks - 1;
             const int64_t col = nbc * 16 + fr;
             st.w[j] = load16_stream(packed_w + (nbc * kblocks + kbc) * 256 + 4 * lane);
-            st.s[j][0] = scales[col * groups + g];
-            st.z[j] = packed_z[g * (n / 8) + col / 8] >> (4 * (col % 8));
+            if constexpr (SZ) {
+                st.s[j][0] = scales[col * groups + g];
+                st.z[j] = packed_z[g * (n / 8) + col / 8] >> (4 * (col % 8));
+            }
         }
     }
 #pragma unroll
@@ -813,15 +817,40 @@ __global__ __launch_bounds__(WAVES * 64) void int4_grouped_i8_kernel(const int8_
     // As in the fp16 kernel: NST > 0 issues the loads of NST k blocks
     // together; NST = 0 pipelines two register stages.  Same order, same bits.
     if constexpr (NST > 0) {
+        // Groups of 128 k or more with four blocks per round: lane (fr, q)
+        // loads its column's scale and zero-point for k block kb0 + q WAVES
+        // (one load pair per column block instead of one per k block), and
+        // block u takes them from lane fr + 16 u of the same column.
+        constexpr bool SHARED = !SUB && NST == 4;
         for (int64_t kb0 = wave; kb0 < kblocks; kb0 += (int64_t)WAVES * NST) {
             StageI8<NBLK, RB, SUB> st[NST];
+            uint32_t szl[NBLK];
+            if constexpr (SHARED) {
+                const int64_t kq = kb0 + (int64_t)(lane / 16) * WAVES, kqc = kq < kblocks ? kq : kblocks - 1;
+#pragma unroll
+                for (int j = 0; j < NBLK; j++) {
+                    const int64_t nbc = nb0 + j < nblocks ? nb0 + j : nblocks - 1;
+                    szl[j] = scale_zero(scales, packed_z, nbc * 16 + fr, kqc * 128 / group_size, groups, n);
+                }
+            }
 #pragma unroll
             for (int u = 0; u < NST; u++)
-                load_stage_i8(st[u], xq, row0, m, k, packed_w, scales, packed_z, kb0 + (int64_t)u * WAVES, nb0, nblocks,
-                              kblocks, group_size, groups, n, lane);
+                load_stage_i8<NBLK, RB, SUB, !SHARED>(st[u], xq, row0, m, k, packed_w, scales, packed_z,
+                                                      kb0 + (int64_t)u * WAVES, nb0, nblocks, kblocks, group_size,
+                                                      groups, n, lane);
 #pragma unroll
             for (int u = 0; u < NST; u++)
-                if (kb0 + (int64_t)u * WAVES < kblocks) compute_stage_i8(st[u], acc, nb0, nblocks, xb, lane);
+                if (kb0 + (int64_t)u * WAVES < kblocks) {
+                    if constexpr (SHARED) {
+#pragma unroll
+                        for (int j = 0; j < NBLK; j++) {
+                            const uint32_t sz = sub_scale_zero(szl[j], u, lane);
+                            st[u].s[j][0] = sz & 0xffffu;
+                            st[u].z[j] = sz >> 16;
+                        }
+                    }
+                    compute_stage_i8(st[u], acc, nb0, nblocks, xb, lane);
+                }
         }
     } else {
         StageI8<NBLK, RB, SUB> s0, s1;
