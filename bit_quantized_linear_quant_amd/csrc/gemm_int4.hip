@@ -119,7 +119,9 @@ __device__ __forceinline__ uint32_t sub_scale_zero(uint32_t own, int t, int lane
 // Issue every load of k block kb (clamped into range; the caller masks a
 // block past the end).  All loads are unconditional, so none of them waits
 // for another.
-template <int NBLK, int RB, bool SUB>
+// SZ = false: the scales and zero-points of groups of 128 k or more are not
+// loaded here (the caller shares one pair per column block and lane).
+template <int NBLK, int RB, bool SUB, bool SZ = true>
 __device__ __forceinline__ void load_stage(Stage<NBLK, RB, SUB> &st, const uint16_t *__restrict__ x, int64_t row0,
                                            int64_t m, int64_t k,
                                            const uint32_t *__restrict__ packed_w,
@@ -146,8 +148,10 @@ __device__ __forceinline__ void load_stage(Stage<NBLK, RB, SUB> &st, const uint1
             const int64_t nbc = nb0 + j < nblocks ? nb0 + j : nblocks - 1;
             const int64_t col = nbc * 16 + fr;
             st.w[j] = load16_stream(packed_w + (nbc * kblocks + kbc) * 256 + 4 * lane);
-            st.s[j][0] = scales[col * groups + g];
-            st.z[j] = packed_z[g * (n / 8) + col / 8] >> (4 * (col % 8));
+            if constexpr (SZ) {
+                st.s[j][0] = scales[col * groups + g];
+                st.z[j] = packed_z[g * (n / 8) + col / 8] >> (4 * (col % 8));
+            }
         }
     }
 #pragma unroll
@@ -261,15 +265,39 @@ __global__ __launch_bounds__(WAVES * 64) void int4_grouped_kernel(const uint16_t
     // matrix cores work on the current one.  Both add the blocks in the same
     // order, so both give the same bits.
     if constexpr (NST > 0) {
+        // Groups of 128 k or more with four blocks per round: lane (fr, q)
+        // loads its column's scale and zero-point for k block kb0 + q WAVES
+        // (one load pair per column block instead of one per k block), and
+        // block u takes them from lane fr + 16 u of the same column.
+        constexpr bool SHARED = !SUB && NST == 4;
         for (int64_t kb0 = wave; kb0 < kblocks; kb0 += (int64_t)WAVES * NST) {
             Stage<NBLK, RB, SUB> st[NST];
+            uint32_t szl[NBLK];
+            if constexpr (SHARED) {
+                const int64_t kq = kb0 + (int64_t)(lane / 16) * WAVES, kqc = kq < kblocks ? kq : kblocks - 1;
+#pragma unroll
+                for (int j = 0; j < NBLK; j++) {
+                    const int64_t nbc = nb0 + j < nblocks ? nb0 + j : nblocks - 1;
+                    szl[j] = scale_zero(scales, packed_z, nbc * 16 + fr, kqc * 128 / group_size, groups, n);
+                }
+            }
 #pragma unroll
             for (int u = 0; u < NST; u++)
-                load_stage(st[u], x, row0, m, k, packed_w, scales, packed_z, kb0 + (int64_t)u * WAVES, nb0, nblocks, kblocks,
-                           group_size, groups, n, lane);
+                load_stage<NBLK, RB, SUB, !SHARED>(st[u], x, row0, m, k, packed_w, scales, packed_z,
+                                                   kb0 + (int64_t)u * WAVES, nb0, nblocks, kblocks, group_size,
+                                                   groups, n, lane);
 #pragma unroll
-            for (int u = 0; u < NST; u++)
+            for (int u = 0; u < NST; u++) {
+                if constexpr (SHARED) {
+#pragma unroll
+                    for (int j = 0; j < NBLK; j++) {
+                        const uint32_t sz = sub_scale_zero(szl[j], u, lane);
+                        st[u].s[j][0] = sz & 0xffffu;
+                        st[u].z[j] = sz >> 16;
+                    }
+                }
                 compute_stage(st[u], acc, kb0 + (int64_t)u * WAVES < kblocks, nb0, nblocks, xb, lane);
+            }
         }
     } else {
         Stage<NBLK, RB, SUB> s0, s1;
