@@ -33,7 +33,12 @@
 // fragments (non-temporal: read once), scales, zero-points and x fragments
 // of its next k block are in flight; with one row block, a wave with at most
 // four k blocks (k <= 4096 with 8 waves) issues all of their loads at once
-// instead.
+// instead.  In those all-at-once forms, with groups of 128 k or more, a lane
+// loads the scale and zero-point of its column for one of the wave's k
+// blocks (lane (fr, q): block q) and the other lanes of the column read it
+// with ds_bpermute, so a column block costs two small loads per wave rather
+// than two per k block: each such gather touches 16 columns 64 bytes apart,
+// and issuing them, not their bytes, was a large part of the load phase.
 // The fp32 partials of the waves are added in LDS in a fixed wave order.
 #include <type_traits>
 
