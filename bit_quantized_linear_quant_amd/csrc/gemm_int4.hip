@@ -33,12 +33,7 @@
 // fragments (non-temporal: read once), scales, zero-points and x fragments
 // of its next k block are in flight; with one row block, a wave with at most
 // four k blocks (k <= 4096 with 8 waves) issues all of their loads at once
-// instead.  In those all-at-once forms, with groups of 128 k or more, a lane
-// loads the scale and zero-point of its column for one of the wave's k
-// blocks (lane (fr, q): block q) and the other lanes of the column read it
-// with ds_bpermute, so a column block costs two small loads per wave rather
-// than two per k block: each such gather touches 16 columns 64 bytes apart,
-// and issuing them, not their bytes, was a large part of the load phase.
+// instead.
 // The fp32 partials of the waves are added in LDS in a fixed wave order.
 #include <type_traits>
 
@@ -124,9 +119,7 @@ __device__ __forceinline__ uint32_t sub_scale_zero(uint32_t own, int t, int lane
 // Issue every load of k block kb (clamped into range; the caller masks a
 // block past the end).  All loads are unconditional, so none of them waits
 // for another.
-// SZ = false: the scales and zero-points of groups of 128 k or more are not
-// loaded here (the caller shares one pair per column block and lane).
-template <int NBLK, int RB, bool SUB, bool SZ = true>
+template <int NBLK, int RB, bool SUB>
 __device__ __forceinline__ void load_stage(Stage<NBLK, RB, SUB> &st, const uint16_t *__restrict__ x, int64_t row0,
                                            int64_t m, int64_t k,
                                            const uint32_t *__restrict__ packed_w,
@@ -153,10 +146,8 @@ __device__ __forceinline__ void load_stage(Stage<NBLK, RB, SUB> &st, const uint1
             const int64_t nbc = nb0 + j < nblocks ? nb0 + j : nblocks - 1;
             const int64_t col = nbc * 16 + fr;
             st.w[j] = load16_stream(packed_w + (nbc * kblocks + kbc) * 256 + 4 * lane);
-            if constexpr (SZ) {
-                st.s[j][0] = scales[col * groups + g];
-                st.z[j] = packed_z[g * (n / 8) + col / 8] >> (4 * (col % 8));
-            }
+            st.s[j][0] = scales[col * groups + g];
+            st.z[j] = packed_z[g * (n / 8) + col / 8] >> (4 * (col % 8));
         }
     }
 #pragma unroll
@@ -270,39 +261,15 @@ __global__ __launch_bounds__(WAVES * 64) void int4_grouped_kernel(const uint16_t
     // matrix cores work on the current one.  Both add the blocks in the same
     // order, so both give the same bits.
     if constexpr (NST > 0) {
-        // Groups of 128 k or more with four blocks per round: lane (fr, q)
-        // loads its column's scale and zero-point for k block kb0 + q WAVES
-        // (one load pair per column block instead of one per k block), and
-        // block u takes them from lane fr + 16 u of the same column.
-        constexpr bool SHARED = !SUB && NST == 4;
         for (int64_t kb0 = wave; kb0 < kblocks; kb0 += (int64_t)WAVES * NST) {
             Stage<NBLK, RB, SUB> st[NST];
-            uint32_t szl[NBLK];
-            if constexpr (SHARED) {
-                const int64_t kq = kb0 + (int64_t)(lane / 16) * WAVES, kqc = kq < kblocks ? kq : kblocks - 1;
-#pragma unroll
-                for (int j = 0; j < NBLK; j++) {
-                    const int64_t nbc = nb0 + j < nblocks ? nb0 + j : nblocks - 1;
-                    szl[j] = scale_zero(scales, packed_z, nbc * 16 + fr, kqc * 128 / group_size, groups, n);
-                }
-            }
 #pragma unroll
             for (int u = 0; u < NST; u++)
-                load_stage<NBLK, RB, SUB, !SHARED>(st[u], x, row0, m, k, packed_w, scales, packed_z,
-                                                   kb0 + (int64_t)u * WAVES, nb0, nblocks, kblocks, group_size,
-                                                   groups, n, lane);
+                load_stage(st[u], x, row0, m, k, packed_w, scales, packed_z, kb0 + (int64_t)u * WAVES, nb0, nblocks, kblocks,
+                           group_size, groups, n, lane);
 #pragma unroll
-            for (int u = 0; u < NST; u++) {
-                if constexpr (SHARED) {
-#pragma unroll
-                    for (int j = 0; j < NBLK; j++) {
-                        const uint32_t sz = sub_scale_zero(szl[j], u, lane);
-                        st[u].s[j][0] = sz & 0xffffu;
-                        st[u].z[j] = sz >> 16;
-                    }
-                }
+            for (int u = 0; u < NST; u++)
                 compute_stage(st[u], acc, kb0 + (int64_t)u * WAVES < kblocks, nb0, nblocks, xb, lane);
-            }
         }
     } else {
         Stage<NBLK, RB, SUB> s0, s1;
@@ -389,10 +356,7 @@ __global__ __launch_bounds__(WAVES * 64) void int4_grouped_dl_kernel(const uint1
     constexpr int XBUF = RB * 16 * 256;            // one k block of x for the row slice
     constexpr int XL = XBUF / 1024;                // direct loads per k block
     constexpr int NXB = NKB < 2 ? NKB : 2;         // x buffers per wave
-    // loads per k block after the first: the weights, and with per-step
-    // groups a scale and zero-point pair per column block (block 0 also
-    // loads the pairs of the other blocks' groups of 128 k or more)
-    constexpr int WL = SUB ? NBLK * 3 : NBLK;
+    constexpr int WL = NBLK * 3;                   // weight, scale and zero-point loads per k block
     constexpr int XS = WAVES * XBUF;
     constexpr int RED = WAVES * RB * NBLK * kWave * 16;
     static_assert(RED <= XS, "the partials reuse the first x buffer");
@@ -432,11 +396,6 @@ __global__ __launch_bounds__(WAVES * 64) void int4_grouped_dl_kernel(const uint1
 
     uint4 w[NKB][NBLK];
     uint32_t sc[NKB][NBLK][1], zr[NKB][NBLK];
-    // Groups of 128 k or more: lane (fr, q) loads, with block 0's weights,
-    // the scale and zero-point of its column for the wave's k block q (one
-    // load pair per column block instead of one per k block); block u takes
-    // them from lane fr + 16 u of the same column.
-    uint32_t szl[NBLK];
     auto load_w = [&](int u) {
         const int64_t kb = kb_of(u), kbc = kb < kblocks ? kb : kblocks - 1;
 #pragma unroll
@@ -449,10 +408,10 @@ __global__ __launch_bounds__(WAVES * 64) void int4_grouped_dl_kernel(const uint1
                 subblock_groups(kbc, group_size / 32, gt);
                 sc[u][j][0] = lane_scale_zero(scales, packed_z, col, gt, groups, n, lane);
                 zr[u][j] = 0;
-            } else if (u == 0) {
-                const int uq = q < NKB ? q : NKB - 1;
-                const int64_t kq = kb_of(uq), kqc = kq < kblocks ? kq : kblocks - 1;
-                szl[j] = scale_zero(scales, packed_z, col, kqc * 128 / group_size, groups, n);
+            } else {
+                const int64_t g = kbc * 128 / group_size;
+                sc[u][j][0] = scales[col * groups + g];
+                zr[u][j] = packed_z[g * (n / 8) + col / 8] >> (4 * (col % 8));
             }
         }
     };
@@ -511,14 +470,6 @@ __global__ __launch_bounds__(WAVES * 64) void int4_grouped_dl_kernel(const uint1
                 : "=v"(a[b][0]), "=v"(a[b][1]), "=v"(a[b][2]), "=v"(a[b][3])
                 : "v"(ad[0]), "v"(ad[1]), "v"(ad[2]), "v"(ad[3])
                 : "memory");
-        }
-        if constexpr (!SUB) {
-#pragma unroll
-            for (int j = 0; j < NBLK; j++) {
-                const uint32_t sz = sub_scale_zero(szl[j], u, lane);
-                sc[u][j][0] = sz & 0xffffu;
-                zr[u][j] = sz >> 16;
-            }
         }
         block_mma<NBLK, RB, SUB>(a, w[u], sc[u], zr[u], acc, kb_of(u) < kblocks, nb0, nblocks, lane);
         if constexpr (u + 2 < NKB) {
@@ -647,9 +598,7 @@ struct StageI8 {
     v4i a[RB][2];
 };
 
-// SZ = false: the scales and zero-points of groups of 128 k or more are not
-// loaded here (the caller shares one pair per column block and lane).
-template <int NBLK, int RB, bool SUB, bool SZ = true>
+template <int NBLK, int RB, bool SUB>
 __device__ __forceinline__ void load_stage_i8(StageI8<NBLK, RB, SUB> &st, const int8_t *__restrict__ xq,
                                               int64_t row0, int64_t m, int64_t k,
                                               const uint32_t *__restrict__ packed_w,
@@ -676,10 +625,8 @@ __device__ __forceinline__ void load_stage_i8(StageI8<NBLK, RB, SUB> &st, const 
             const int64_t nbc = nb0 + j < nblocks ? nb0 + j : nblocks - 1;
             const int64_t col = nbc * 16 + fr;
             st.w[j] = load16_stream(packed_w + (nbc * kblocks + kbc) * 256 + 4 * lane);
-            if constexpr (SZ) {
-                st.s[j][0] = scales[col * groups + g];
-                st.z[j] = packed_z[g * (n / 8) + col / 8] >> (4 * (col % 8));
-            }
+            st.s[j][0] = scales[col * groups + g];
+            st.z[j] = packed_z[g * (n / 8) + col / 8] >> (4 * (col % 8));
         }
     }
 #pragma unroll
@@ -850,40 +797,15 @@ __global__ __launch_bounds__(WAVES * 64) void int4_grouped_i8_kernel(const int8_
     // As in the fp16 kernel: NST > 0 issues the loads of NST k blocks
     // together; NST = 0 pipelines two register stages.  Same order, same bits.
     if constexpr (NST > 0) {
-        // Groups of 128 k or more with four blocks per round: lane (fr, q)
-        // loads its column's scale and zero-point for k block kb0 + q WAVES
-        // (one load pair per column block instead of one per k block), and
-        // block u takes them from lane fr + 16 u of the same column.
-        constexpr bool SHARED = !SUB && NST == 4;
         for (int64_t kb0 = wave; kb0 < kblocks; kb0 += (int64_t)WAVES * NST) {
             StageI8<NBLK, RB, SUB> st[NST];
-            uint32_t szl[NBLK];
-            if constexpr (SHARED) {
-                const int64_t kq = kb0 + (int64_t)(lane / 16) * WAVES, kqc = kq < kblocks ? kq : kblocks - 1;
-#pragma unroll
-                for (int j = 0; j < NBLK; j++) {
-                    const int64_t nbc = nb0 + j < nblocks ? nb0 + j : nblocks - 1;
-                    szl[j] = scale_zero(scales, packed_z, nbc * 16 + fr, kqc * 128 / group_size, groups, n);
-                }
-            }
 #pragma unroll
             for (int u = 0; u < NST; u++)
-                load_stage_i8<NBLK, RB, SUB, !SHARED>(st[u], xq, row0, m, k, packed_w, scales, packed_z,
-                                                      kb0 + (int64_t)u * WAVES, nb0, nblocks, kblocks, group_size,
-                                                      groups, n, lane);
+                load_stage_i8(st[u], xq, row0, m, k, packed_w, scales, packed_z, kb0 + (int64_t)u * WAVES, nb0, nblocks,
+                              kblocks, group_size, groups, n, lane);
 #pragma unroll
             for (int u = 0; u < NST; u++)
-                if (kb0 + (int64_t)u * WAVES < kblocks) {
-                    if constexpr (SHARED) {
-#pragma unroll
-                        for (int j = 0; j < NBLK; j++) {
-                            const uint32_t sz = sub_scale_zero(szl[j], u, lane);
-                            st[u].s[j][0] = sz & 0xffffu;
-                            st[u].z[j] = sz >> 16;
-                        }
-                    }
-                    compute_stage_i8(st[u], acc, nb0, nblocks, xb, lane);
-                }
+                if (kb0 + (int64_t)u * WAVES < kblocks) compute_stage_i8(st[u], acc, nb0, nblocks, xb, lane);
         }
     } else {
         StageI8<NBLK, RB, SUB> s0, s1;

@@ -424,7 +424,11 @@ GROUPED_SHAPES = [(1, 48, 256, 128), (5, 400, 512, 128), (32, 400, 512, 256),
                   (5, 64, 8192, 256),    # more than 4 k blocks per wave: pipelined stages
                   # groups smaller than a 128-k block: per-step scales after the cross-row transpose
                   (1, 48, 256, 32), (5, 400, 512, 32), (32, 400, 512, 64), (17, 64, 384, 96),
-                  (3, 32, 1024, 64), (40, 64, 8192, 32), (16, 48, 128, 32), (33, 160, 640, 160)]
+                  (3, 32, 1024, 64), (40, 64, 8192, 32), (16, 48, 128, 32), (33, 160, 640, 160),
+                  # four k blocks per wave with one scale and zero-point pair per column block and
+                  # lane: whole rounds, and a last round whose blocks past k are clamped and masked
+                  (32, 400, 4096, 128), (48, 160, 2560, 256), (7, 96, 2816, 128), (16, 400, 4096, 512),
+                  (32, 48, 2304, 2304)]
 
 
 @pytest.mark.parametrize("m,n,k,g", GROUPED_SHAPES)
@@ -471,7 +475,10 @@ def _grouped_i8_inputs(m, n, k, g, seed):
                                      (17, 400, 512, 256), (32, 400, 512, 128), (40, 64, 384, 128),
                                      (3, 32, 1024, 1024), (17, 64, 8192, 128),
                                      (1, 48, 256, 32), (17, 400, 512, 64), (32, 400, 512, 32),
-                                     (5, 64, 384, 96), (17, 64, 8192, 32), (16, 48, 1024, 64)])
+                                     (5, 64, 384, 96), (17, 64, 8192, 32), (16, 48, 1024, 64),
+                                     # four k blocks per wave, shared scale and zero-point pairs
+                                     (32, 400, 4096, 128), (48, 160, 2560, 256), (7, 96, 2816, 128),
+                                     (16, 400, 4096, 512)])
 def test_grouped_int4_i8_parity(m, n, k, g):
     """int8 activation codes: fp32 output within the arithmetic's bound, 16-bit outputs
     within the grouped bar and equal to the fp32 output rounded once."""
